@@ -1,0 +1,240 @@
+/*
+ * libqe -- the inference hot path of a Quant Experts (QE) linear layer on AMD
+ * Instinct MI355X (gfx950), as a C ABI.
+ *
+ * What a QE linear computes (sources cited by page title and section):
+ *   y = Q(x / s) . Q(W_f diag(s))^T            quantized main product
+ *     + (x . A_s) . B_s                         shared expert (every token)
+ *     + (x . A_e) . B_e,  e = argmin_j (x . R)_j  one routed expert per token
+ *   - MCISLAB DeepRead summary "Quant Experts: Token-aware Adaptive Error
+ *     Reconstruction with Mixture of Experts for Large Vision-Language Models
+ *     Quantization", section "Method": shared low-rank expert for the global error,
+ *     routed low-rank experts for token-specific error, a lightweight router that
+ *     predicts each expert's remaining error and picks the smallest, channel-wise
+ *     scaling before activation quantization, and the per-token statistic
+ *     Top-k(|x_t| * Mean_row(|W_f|)).
+ *   - thelatestinai.com listing of arXiv 2602.24059, Table 7: a QE linear costs
+ *     s*d^2 + s*d*(2r + N_r) multiply-adds (dense adapters, one routed expert per
+ *     token, one d x N_r router map); bit settings W4A6 / W4A8 / W3A16 (Tables 1-3).
+ *
+ * Conventions shared by every entry point
+ *   - Return value: a qe_status (0 = QE_OK).  Arguments are validated on the host
+ *     before anything is enqueued; on failure nothing is launched.  A failed HIP
+ *     launch returns QE_ERR_HIP and its hipError_t is kept in qe_last_hip_error()
+ *     (thread-local).  Faults inside kernels surface at the caller's next
+ *     synchronisation.  No C++ exception crosses this ABI.  T == 0 is a no-op.
+ *   - Memory: every pointer marked "device" is device memory allocated and owned
+ *     by the caller; the library never allocates or frees memory and keeps no
+ *     pointer after returning.  Buffers must stay valid until the work enqueued
+ *     on `stream` has finished.
+ *   - Streams: `stream` is a hipStream_t passed as void* (NULL = the default
+ *     stream).  Device entry points only enqueue work; none synchronises.
+ *   - Layouts are row-major and dense.  bf16 tensors are passed as uint16_t bit
+ *     patterns.  Device pointers must be 16-byte aligned (QE_ERR_ALIGNMENT).
+ *   - Inputs must be finite; results for non-finite inputs are undefined.
+ *   - The library holds no global mutable state except the thread-local error;
+ *     calls on different streams may run concurrently as long as they do not
+ *     share output or workspace buffers.
+ */
+#ifndef QE_H
+#define QE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QE_OK = 0,
+    QE_ERR_INVALID_ARG = 1,  /* bad shape, bit width, NULL required pointer, k > d_in ... */
+    QE_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. W3 with A6/A8, d_in % 128 != 0) */
+    QE_ERR_ALIGNMENT = 3,    /* a device pointer is not 16-byte aligned */
+    QE_ERR_WORKSPACE = 4,    /* workspace / prepared buffer smaller than required */
+    QE_ERR_HIP = 5           /* a HIP call failed; see qe_last_hip_error() */
+} qe_status;
+
+typedef enum { QE_F32 = 0, QE_BF16 = 1 } qe_dtype;
+
+/* Shape and bit widths of one QE linear, plus its prepared parameter buffer.
+ *   d_in, d_out  input / output channels (d_in > 0, d_out > 0)
+ *   w_bits       4 (int4, per-output-channel symmetric) or 3 (3-bit, weight-only)
+ *   a_bits       6 or 8 (per-token symmetric activation codes) with w_bits 4;
+ *                16 (bf16 activations, no activation quantization) with w_bits 3 or 4
+ *   r_shared     shared-expert rank, 0..64 (0 = no shared expert)
+ *   n_routed     number of routed experts N_r, 0..16 (0 = no router, no routed expert)
+ *   r_routed     routed-expert rank, 1..64 when n_routed > 0, else 0
+ *   prep         device buffer written by qe_prepare() (qe_prepared_bytes() bytes)
+ * Kernel-path constraints: d_out % 16 == 0 and d_in % 128 == 0 (else QE_ERR_UNSUPPORTED).
+ */
+typedef struct qe_linear {
+    int32_t d_in;
+    int32_t d_out;
+    int32_t w_bits;
+    int32_t a_bits;
+    int32_t r_shared;
+    int32_t n_routed;
+    int32_t r_routed;
+    int32_t reserved;
+    const void* prep;
+} qe_linear;
+
+/* Human-readable name of a status code (static storage). */
+const char* qe_status_string(int status);
+
+/* hipError_t of the last QE_ERR_HIP returned on this thread (0 if none). */
+int qe_last_hip_error(void);
+
+/* Library version string (static storage). */
+const char* qe_version(void);
+
+/* ---------------------------------------------------------------- weights ----
+ * Quantize and pack one full-precision weight matrix (host memory, synchronous).
+ * Follows the DeepRead summary, "Method" (weights amplified by the smoothing
+ * factors) with per-output-channel symmetric round-to-nearest-even:
+ *   W'[i][j] = W_f[i][j] * s[j]           (float32; s == NULL means s = 1)
+ *   w_scale[i] = max_j |W'[i][j]| / qmax    (qmax = 7 for w_bits 4, 3 for w_bits 3)
+ *   q[i][j] = clamp(rint(W'[i][j] / w_scale[i]), -qmax, qmax); all-zero rows -> 0
+ * Packed layouts (canonical, two's complement):
+ *   w_bits 4: uint8 [d_out][d_in/2]; byte m holds code 2m in bits 0-3, 2m+1 in bits 4-7.
+ *   w_bits 3: uint32 [d_out][d_in/32][3]; 32 codes per 96-bit little-endian group,
+ *             code c at bits 3c..3c+2.
+ * W_f_host: float32 [d_out][d_in]; s_host: float32 [d_in] or NULL;
+ * packed_host: d_out*d_in/2 bytes (W4) or d_out*d_in*3/8 bytes (W3);
+ * w_scale_host: float32 [d_out].  Requires d_in even (W4) or d_in % 32 == 0 (W3).
+ */
+int qe_pack_weights(const float* W_f_host, const float* s_host, int32_t d_out, int32_t d_in,
+                    int32_t w_bits, void* packed_host, float* w_scale_host);
+
+/* Bytes of the prepared parameter buffer for this linear (lin->prep ignored). */
+size_t qe_prepared_bytes(const qe_linear* lin);
+
+/* Lay out one linear's parameters for the kernels (load-time step, enqueued on
+ * `stream`).  All inputs are device pointers in the canonical layouts:
+ *   w_packed  W4/W3 packed codes as produced by qe_pack_weights
+ *   w_scale   float32 [d_out]
+ *   smooth    float32 [d_in], entries > 0, or NULL (identity); must be NULL when a_bits == 16
+ *   A_s [d_in][r_shared], B_s [r_shared][d_out]          bf16 (NULL iff r_shared == 0)
+ *   A_r [n_routed][d_in][r_routed], B_r [n_routed][r_routed][d_out]  bf16
+ *   R   [d_in][n_routed]                                  bf16 (NULL iff n_routed == 0)
+ * prep: device output buffer of qe_prepared_bytes(lin) bytes; it becomes lin->prep.
+ * The inputs may be freed once the enqueued work has finished.
+ */
+int qe_prepare(const qe_linear* lin, const void* w_packed, const float* w_scale, const float* smooth,
+               const uint16_t* A_s, const uint16_t* B_s, const uint16_t* A_r, const uint16_t* B_r,
+               const uint16_t* R, void* prep, void* stream);
+
+/* Workspace bytes needed by qe_linear_forward / qe_route / qe_adapter_inputs /
+ * qe_wq_gemm / qe_routed_lora for T tokens (the largest of them). */
+size_t qe_workspace_bytes(const qe_linear* lin, int32_t T);
+
+/* ------------------------------------------------------------ hot-path steps -- */
+
+/* (a1) Smoothing and per-token symmetric RTN of the activations.
+ * DeepRead summary, "Method": channel-wise scaling divides the activations before
+ * activation quantization; A6/A8 from the listing's Tables 1-3.  In float32 with
+ * IEEE division and round-half-to-even:
+ *   x'[t][j] = x[t][j] / s[j];  s_x[t] = max_j |x'[t][j]| / qmax  (qmax 31 or 127)
+ *   codes[t][j] = clamp(rint(x'[t][j] / s_x[t]), -qmax, qmax); all-zero token -> 0
+ * x: device [T][d_in] (x_dtype); smooth: device [d_in] or NULL (identity);
+ * codes: device int8 [T][d_in]; s_x: device float32 [T].  a_bits 6 or 8.
+ */
+int qe_quant_act(const void* x, int32_t x_dtype, const float* smooth, int32_t T, int32_t d_in,
+                 int32_t a_bits, int8_t* codes, float* s_x, void* stream);
+
+/* (a5) Router and token bucketing.
+ * DeepRead summary, "Method" (router picks the routed expert with the smallest
+ * predicted error) and the listing's Table 7 (one d x N_r map per token):
+ *   scores[t][e] = sum_j bf16(x)[t][j] * R[j][e]  (float32 accumulation of exact products)
+ *   expert[t] = argmin_e scores[t][e], lowest e on ties
+ *   counts[e] = #tokens routed to e; offsets = exclusive prefix sum (offsets[N_r] = T);
+ *   perm = token indices sorted by (expert, token index)
+ * x: device [T][d_in]; scores: device float32 [T][n_routed] or NULL;
+ * expert, perm: device int32 [T]; counts: int32 [n_routed]; offsets: int32 [n_routed+1].
+ * Requires lin->n_routed > 0.  ws: workspace of ws_bytes >= qe_workspace_bytes(lin, T).
+ */
+int qe_route(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* scores,
+             int32_t* expert, int32_t* counts, int32_t* offsets, int32_t* perm,
+             void* ws, size_t ws_bytes, void* stream);
+
+/* (a4/a6, first half) Adapter inputs: u = bf16(x) . A_s and v[t] = bf16(x)[t] . A_{expert[t]},
+ * accumulated in float32 and stored as bf16 (round to nearest even).
+ * u: device bf16 [T][r_shared] (NULL iff r_shared == 0); v: device bf16 [T][r_routed]
+ * (NULL iff n_routed == 0); expert: device int32 [T] in [0, n_routed) (NULL iff n_routed == 0).
+ */
+int qe_adapter_inputs(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T,
+                      const int32_t* expert, uint16_t* u, uint16_t* v,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* (a3, plus the second halves of a4/a6; a7 when a_bits == 16) Quantized main
+ * product with a float32 dequantization epilogue into which the shared and the
+ * selected routed low-rank terms are fused (listing, Table 7: the s*d^2 term):
+ *   a_bits 6/8: acc[t][i] = sum_j codes[t][j] * q_w[i][j]   (exact int32)
+ *               y[t][i] = acc * s_x[t] * w_scale[i] + u[t].B_s[:,i] + v[t].B_{expert[t]}[:,i]
+ *   a_bits 16:  y[t][i] = w_scale[i] * sum_j bf16(x)[t][j] * q_w[i][j] + (same adapter terms)
+ * codes/s_x: from qe_quant_act (a_bits 6/8; NULL for 16); x: device [T][d_in] (a_bits 16 only,
+ * else ignored); u, v, expert as produced by qe_adapter_inputs / qe_route (each NULL => that
+ * term is skipped); y: device float32 [T][d_out], overwritten;
+ * acc_debug: device int32 [T][d_out] or NULL (a_bits 6/8 only).
+ */
+int qe_wq_gemm(const qe_linear* lin, const int8_t* codes, const float* s_x, const void* x,
+               int32_t x_dtype, int32_t T, const uint16_t* u, const uint16_t* v,
+               const int32_t* expert, float* y, int32_t* acc_debug,
+               void* ws, size_t ws_bytes, void* stream);
+
+/* (a6, unfused form) Routed experts as a grouped low-rank product over the
+ * expert buckets: for each expert e and each token t in perm[offsets[e]..offsets[e+1]):
+ *   y[t] += (bf16(x)[t] . A_e) . B_e      (y is ADDED to, not overwritten)
+ * expert/offsets/perm as produced by qe_route.
+ */
+int qe_routed_lora(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T,
+                   const int32_t* expert, const int32_t* offsets, const int32_t* perm, float* y,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/* The whole QE linear: a1 + a5 + a4 + a6 + a3 (or a7 for a_bits 16), fused as
+ * above.  y: device float32 [T][d_out] (overwritten); expert_out: device int32 [T]
+ * or NULL (the routed expert of each token).  ws: qe_workspace_bytes(lin, T) bytes.
+ */
+int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* y,
+                      int32_t* expert_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------- channel-importance statistic --
+ * (a8 helper) w[j] = (sum_i |W[i][j]|) / d_out: the column mean of |W_f|, one value
+ * per input channel (DeepRead summary, "Method", first paragraph: Mean_row(|W_f|)).
+ * Summed in float64 and rounded once to float32.  W: device [d_out][d_in] (dtype);
+ * w: device float32 [d_in].
+ */
+int qe_colmean_abs(const void* W, int32_t dtype, int32_t d_out, int32_t d_in, float* w, void* stream);
+
+/* (a8) Per-token important channels and their frequency (DeepRead summary,
+ * "Method": S_t = Top-k(|x_t| * w); the listing's Figure 3 counts how often each
+ * channel is selected):
+ *   sc[t][j] = |x[t][j]| * w[j]  (float32, x at its stored precision)
+ *   topk[t][0..k) = the k channels first in the order (sc descending, j ascending)
+ *   hist[j] += #{t : j in topk[t]}   (hist is ACCUMULATED; the caller zeroes it)
+ * x: device [T][d_in]; w: device float32 [d_in] (entries >= 0);
+ * topk: device int32 [T][k] or NULL; hist: device uint32 [d_in].  1 <= k <= min(d_in, 1024),
+ * d_in <= 32768.
+ */
+int qe_channel_topk(const void* x, int32_t x_dtype, const float* w, int32_t T, int32_t d_in,
+                    int32_t k, int32_t* topk, uint32_t* hist, void* stream);
+
+/* ----------------------------------------------------------------- accounting --
+ * Algorithmic work of one QE linear over T tokens (listing, Table 7, generalised
+ * to d_in != d_out):
+ *   int_macs      = T * d_in * d_out                        (the quantized product)
+ *   adapter_macs  = T * (d_in + d_out) * (r_shared + r_routed) + T * d_in * n_routed
+ *   alg_bytes     = minimum HBM traffic: x read once, packed weights, scales, y written
+ *                   once (float32), A_s, B_s, R and the A_e, B_e of n_distinct_experts
+ *                   distinct routed experts actually selected.
+ * Host-only; x_bytes_per_elt is 2 (bf16) or 4 (float32).
+ */
+int qe_linear_cost(const qe_linear* lin, int32_t T, int32_t n_distinct_experts, int32_t x_bytes_per_elt,
+                   double* int_macs, double* adapter_macs, double* alg_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QE_H */

@@ -1,0 +1,215 @@
+"""ctypes binding of libqe (include/qe.h).  Argument marshalling only.
+
+Every function here has the name of the C entry point it wraps, takes torch
+tensors (device memory) or numpy arrays (host memory) where the C function takes
+pointers, passes torch's current HIP stream, and raises QEError on a non-zero
+status.  No computation of the hot path happens in Python: if the shared library
+is missing, importing this module fails.
+"""
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqe.so")
+
+QE_OK, QE_ERR_INVALID_ARG, QE_ERR_UNSUPPORTED, QE_ERR_ALIGNMENT, QE_ERR_WORKSPACE, QE_ERR_HIP = range(6)
+QE_F32, QE_BF16 = 0, 1
+
+
+class QEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = f"{where}: {_lib.qe_status_string(status).decode()}"
+        if status == QE_ERR_HIP:
+            msg += f" (hipError {_lib.qe_last_hip_error()})"
+        super().__init__(msg)
+
+
+class qe_linear(ctypes.Structure):
+    _fields_ = [
+        ("d_in", ctypes.c_int32),
+        ("d_out", ctypes.c_int32),
+        ("w_bits", ctypes.c_int32),
+        ("a_bits", ctypes.c_int32),
+        ("r_shared", ctypes.c_int32),
+        ("n_routed", ctypes.c_int32),
+        ("r_routed", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("prep", ctypes.c_void_p),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"libqe.so not found at {LIB_PATH}; build it with `python -m quantized_linear_moe_amd.build` "
+            "(hipcc, gfx950). There is no fallback implementation.")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, Z, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.POINTER(ctypes.c_double)
+    LP = ctypes.POINTER(qe_linear)
+    sig = {
+        "qe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "qe_last_hip_error": (ctypes.c_int, []),
+        "qe_version": (ctypes.c_char_p, []),
+        "qe_pack_weights": (ctypes.c_int, [P, P, I, I, I, P, P]),
+        "qe_prepared_bytes": (Z, [LP]),
+        "qe_prepare": (ctypes.c_int, [LP, P, P, P, P, P, P, P, P, P, P]),
+        "qe_workspace_bytes": (Z, [LP, I]),
+        "qe_quant_act": (ctypes.c_int, [P, I, P, I, I, I, P, P, P]),
+        "qe_route": (ctypes.c_int, [LP, P, I, I, P, P, P, P, P, P, Z, P]),
+        "qe_adapter_inputs": (ctypes.c_int, [LP, P, I, I, P, P, P, P, Z, P]),
+        "qe_wq_gemm": (ctypes.c_int, [LP, P, P, P, I, I, P, P, P, P, P, P, Z, P]),
+        "qe_routed_lora": (ctypes.c_int, [LP, P, I, I, P, P, P, P, P, Z, P]),
+        "qe_linear_forward": (ctypes.c_int, [LP, P, I, I, P, P, P, Z, P]),
+        "qe_colmean_abs": (ctypes.c_int, [P, I, I, I, P, P]),
+        "qe_channel_topk": (ctypes.c_int, [P, I, P, I, I, I, P, P, P]),
+        "qe_linear_cost": (ctypes.c_int, [LP, I, I, I, D, D, D]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTED = (
+    "qe_status_string", "qe_last_hip_error", "qe_version", "qe_pack_weights", "qe_prepared_bytes", "qe_prepare",
+    "qe_workspace_bytes", "qe_quant_act", "qe_route", "qe_adapter_inputs", "qe_wq_gemm", "qe_routed_lora",
+    "qe_linear_forward", "qe_colmean_abs", "qe_channel_topk", "qe_linear_cost",
+)
+
+
+# ----------------------------------------------------------------- marshalling
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, np.ndarray):
+        return t.ctypes.data
+    return t.data_ptr()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return QE_BF16
+    if t.dtype == torch.float32:
+        return QE_F32
+    raise TypeError(f"activations must be bf16 or float32, got {t.dtype}")
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(st: int, where: str):
+    if st != QE_OK:
+        raise QEError(st, where)
+
+
+def make_linear(d_in, d_out, w_bits, a_bits, r_shared, n_routed, r_routed, prep=None) -> qe_linear:
+    return qe_linear(d_in, d_out, w_bits, a_bits, r_shared, n_routed, r_routed, 0, _ptr(prep))
+
+
+def qe_status_string(status: int) -> str:
+    return _lib.qe_status_string(status).decode()
+
+
+def qe_last_hip_error() -> int:
+    return _lib.qe_last_hip_error()
+
+
+def qe_version() -> str:
+    return _lib.qe_version().decode()
+
+
+def qe_pack_weights(W_f: np.ndarray, s: Optional[np.ndarray], w_bits: int):
+    """Host quantize + pack; returns (packed bytes as uint8 ndarray, w_scale float32 ndarray)."""
+    W_f = np.ascontiguousarray(W_f, dtype=np.float32)
+    d_out, d_in = W_f.shape
+    s_arr = None if s is None else np.ascontiguousarray(s, dtype=np.float32)
+    nbytes = d_out * d_in // 2 if w_bits == 4 else d_out * d_in * 3 // 8
+    packed = np.empty(nbytes, dtype=np.uint8)
+    w_scale = np.empty(d_out, dtype=np.float32)
+    _check(_lib.qe_pack_weights(_ptr(W_f), _ptr(s_arr), d_out, d_in, w_bits, _ptr(packed), _ptr(w_scale)),
+           "qe_pack_weights")
+    return packed, w_scale
+
+
+def qe_prepared_bytes(lin: qe_linear) -> int:
+    return _lib.qe_prepared_bytes(ctypes.byref(lin))
+
+
+def qe_prepare(lin: qe_linear, w_packed, w_scale, smooth, A_s, B_s, A_r, B_r, R, prep, stream=None):
+    _check(_lib.qe_prepare(ctypes.byref(lin), _ptr(w_packed), _ptr(w_scale), _ptr(smooth), _ptr(A_s), _ptr(B_s),
+                           _ptr(A_r), _ptr(B_r), _ptr(R), _ptr(prep), _stream(stream)), "qe_prepare")
+
+
+def qe_workspace_bytes(lin: qe_linear, T: int) -> int:
+    return _lib.qe_workspace_bytes(ctypes.byref(lin), T)
+
+
+def qe_quant_act(x, smooth, a_bits, codes, s_x, stream=None):
+    T, d_in = x.shape
+    _check(_lib.qe_quant_act(_ptr(x), _dtype_code(x), _ptr(smooth), T, d_in, a_bits, _ptr(codes), _ptr(s_x),
+                             _stream(stream)), "qe_quant_act")
+
+
+def qe_route(lin, x, scores, expert, counts, offsets, perm, ws, stream=None):
+    _check(_lib.qe_route(ctypes.byref(lin), _ptr(x), _dtype_code(x), x.shape[0], _ptr(scores), _ptr(expert),
+                         _ptr(counts), _ptr(offsets), _ptr(perm), _ptr(ws), ws.numel() * ws.element_size(),
+                         _stream(stream)), "qe_route")
+
+
+def qe_adapter_inputs(lin, x, expert, u, v, ws, stream=None):
+    _check(_lib.qe_adapter_inputs(ctypes.byref(lin), _ptr(x), _dtype_code(x), x.shape[0], _ptr(expert), _ptr(u),
+                                  _ptr(v), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "qe_adapter_inputs")
+
+
+def qe_wq_gemm(lin, codes, s_x, x, T, u, v, expert, y, acc_debug, ws, stream=None):
+    xd = _dtype_code(x) if x is not None else QE_BF16
+    _check(_lib.qe_wq_gemm(ctypes.byref(lin), _ptr(codes), _ptr(s_x), _ptr(x), xd, T, _ptr(u), _ptr(v), _ptr(expert),
+                           _ptr(y), _ptr(acc_debug), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "qe_wq_gemm")
+
+
+def qe_routed_lora(lin, x, expert, offsets, perm, y, ws, stream=None):
+    _check(_lib.qe_routed_lora(ctypes.byref(lin), _ptr(x), _dtype_code(x), x.shape[0], _ptr(expert), _ptr(offsets),
+                               _ptr(perm), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "qe_routed_lora")
+
+
+def qe_linear_forward(lin, x, y, expert_out, ws, stream=None):
+    _check(_lib.qe_linear_forward(ctypes.byref(lin), _ptr(x), _dtype_code(x), x.shape[0], _ptr(y), _ptr(expert_out),
+                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "qe_linear_forward")
+
+
+def qe_colmean_abs(W, w, stream=None):
+    d_out, d_in = W.shape
+    _check(_lib.qe_colmean_abs(_ptr(W), _dtype_code(W), d_out, d_in, _ptr(w), _stream(stream)), "qe_colmean_abs")
+
+
+def qe_channel_topk(x, w, k, topk, hist, stream=None):
+    T, d_in = x.shape
+    _check(_lib.qe_channel_topk(_ptr(x), _dtype_code(x), _ptr(w), T, d_in, k, _ptr(topk), _ptr(hist),
+                                _stream(stream)), "qe_channel_topk")
+
+
+def qe_linear_cost(lin, T, n_distinct, x_bytes):
+    a, b, c = ctypes.c_double(), ctypes.c_double(), ctypes.c_double()
+    _check(_lib.qe_linear_cost(ctypes.byref(lin), T, n_distinct, x_bytes, ctypes.byref(a), ctypes.byref(b),
+                               ctypes.byref(c)), "qe_linear_cost")
+    return a.value, b.value, c.value
+
+
+def raw_library():
+    """The ctypes CDLL handle (for tests that call entry points with raw pointers)."""
+    return _lib

@@ -1,0 +1,377 @@
+// Activation-side kernels of the QE linear:
+//   * smoothing + per-token symmetric RTN quantization (step a1),
+//   * the x-projection  P = bf16(x) . [A_s | A_1..A_N | R]  on bf16 MFMA
+//     (inputs of the shared expert, the routed experts and the router),
+//   * its reduction, the argmin router and the bf16 adapter inputs (a5, a4/a6),
+//   * token bucketing by routed expert (counts, offsets, stable permutation).
+//
+// Method sources: MCISLAB DeepRead summary of Quant Experts, "Method" (scaling
+// before activation quantization; shared expert on every token; router choosing
+// the routed expert with the smallest predicted error); thelatestinai.com
+// listing, Table 7 (dense adapters, one d x N_r router map per token).
+
+#include "qe_internal.h"
+
+namespace qe {
+
+// ---------------------------------------------------------------- helpers
+__device__ inline float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// float32 -> bf16 bits, round to nearest even (inputs finite)
+__device__ inline uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// a / b correctly rounded, given inv_b = RN(1/b).  One multiply and two fused
+// multiply-adds (Markstein's correction).  Exact for |a| in [2^-100, 2^100] and b
+// in [2^-90, 2^90] with quotients of magnitude >= 2^-3; callers fall back to the
+// IEEE division outside that domain.
+__device__ inline float div_markstein(float a, float b, float inv_b) {
+    float q0 = a * inv_b;
+    float r = __builtin_fmaf(-b, q0, a);
+    return __builtin_fmaf(r, inv_b, q0);
+}
+
+__device__ inline bool in_markstein_range(float a) {
+    float m = __builtin_fabsf(a);
+    return (m >= 0x1p-100f && m <= 0x1p100f) || m == 0.0f;
+}
+
+// x / s exactly as IEEE float32 division
+__device__ inline float smooth_div(float x, float s, float inv_s) {
+    return in_markstein_range(x) ? div_markstein(x, s, inv_s) : x / s;
+}
+
+// load 8 consecutive activations as float
+__device__ inline void load8(const void* x, int x_dtype, size_t idx, float out[8]) {
+    if (x_dtype == QE_BF16) {
+        v4u p = *reinterpret_cast<const v4u*>(reinterpret_cast<const uint16_t*>(x) + idx);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(p[i] << 16);
+            out[2 * i + 1] = __uint_as_float(p[i] & 0xFFFF0000u);
+        }
+    } else {
+        const v4f* p = reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(x) + idx);
+        v4f a = p[0], b = p[1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[i] = a[i];
+            out[4 + i] = b[i];
+        }
+    }
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+// ---------------------------------------------------------------- a1: quant
+// One workgroup per token.  Pass 1: x' = x / s and the token's max |x'|.
+// Pass 2: codes = clamp(rint(x' / s_x), +-qmax) with s_x = amax / qmax.
+// All float32, IEEE division semantics, round half to even.
+template <int kThreads>
+__global__ __launch_bounds__(kThreads) void quant_act_kernel(const void* __restrict__ x, int x_dtype,
+                                                             const float* __restrict__ smooth,
+                                                             const float* __restrict__ inv_smooth, int T, int d_in,
+                                                             int qmax, int8_t* __restrict__ codes,
+                                                             float* __restrict__ s_x) {
+    const int t = blockIdx.x;
+    if (t >= T) return;
+    const size_t row = (size_t)t * d_in;
+    __shared__ float red[kThreads / kWave];
+    __shared__ float s_bcast[2];
+
+    float amax = 0.0f;
+    for (int j = threadIdx.x * 8; j < d_in; j += kThreads * 8) {
+        float v[8];
+        load8(x, x_dtype, row + j, v);
+        if (smooth) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float s = smooth[j + i];
+                float is = inv_smooth ? inv_smooth[j + i] : 1.0f / s;
+                v[i] = smooth_div(v[i], s, is);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
+    }
+    amax = wave_max(amax);
+    const int wid = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+    if (lane == 0) red[wid] = amax;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float m = red[0];
+        for (int i = 1; i < kThreads / kWave; ++i) m = fmaxf(m, red[i]);
+        float sx = m / (float)qmax;
+        s_bcast[0] = sx;
+        s_bcast[1] = (sx != 0.0f) ? 1.0f / sx : 0.0f;
+        s_x[t] = sx;
+    }
+    __syncthreads();
+    const float sx = s_bcast[0], inv_sx = s_bcast[1];
+    const bool fast = (sx >= 0x1p-90f && sx <= 0x1p90f);
+    const float fq = (float)qmax;
+
+    for (int j = threadIdx.x * 8; j < d_in; j += kThreads * 8) {
+        float v[8];
+        load8(x, x_dtype, row + j, v);
+        if (smooth) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float s = smooth[j + i];
+                float is = inv_smooth ? inv_smooth[j + i] : 1.0f / s;
+                v[i] = smooth_div(v[i], s, is);
+            }
+        }
+        uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float q = 0.0f;
+            if (sx != 0.0f) {
+                float r = fast ? div_markstein(v[i], sx, inv_sx) : v[i] / sx;
+                q = fminf(fmaxf(__builtin_rintf(r), -fq), fq);
+            }
+            uint32_t b = (uint32_t)(int32_t)q & 0xFFu;
+            packed[i >> 2] |= b << (8 * (i & 3));
+        }
+        *reinterpret_cast<v2u*>(codes + row + j) = v2u{packed[0], packed[1]};
+    }
+}
+
+hipError_t launch_quant_act(const void* x, int x_dtype, const float* smooth, const float* inv_smooth, int T,
+                            int d_in, int a_bits, int8_t* codes, float* s_x, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    const int qmax = (1 << (a_bits - 1)) - 1;
+    hipLaunchKernelGGL(quant_act_kernel<256>, dim3(T), dim3(256), 0, st, x, x_dtype, smooth, inv_smooth, T, d_in,
+                       qmax, codes, s_x);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------- x-projection
+// P[t][c] = sum_k bf16(x)[t][k] * Mt[col0 + c][k]  for c < ncols, as split-K
+// partials part[ks][t][c] (float32).  bf16 MFMA 16x16x32, fp32 accumulation.
+// Workgroup: 4 waves, 64 tokens x 320 columns (each wave 64 tokens x 80 columns);
+// the x tile is staged through LDS once per workgroup, Mt rows (K-contiguous)
+// are read straight into registers.
+constexpr int XP_TOK = 64;       // tokens per workgroup
+constexpr int XP_NBW = 5;        // 16-column blocks per wave
+constexpr int XP_COLS = 4 * XP_NBW * 16;
+constexpr int XP_KC = 256;       // K chunk staged in LDS
+constexpr int XP_LDS_LD = XP_KC * 2 + 16;  // bytes per LDS row (padded)
+
+__global__ __launch_bounds__(256) void xproj_kernel(const void* __restrict__ x, int x_dtype, int T, int d_in,
+                                                    const uint16_t* __restrict__ mt, int col0, int ncols,
+                                                    int ncols_pad, int ksplit, float* __restrict__ part) {
+    __shared__ __attribute__((aligned(16))) uint8_t xs[XP_TOK * XP_LDS_LD];
+    const int tile = blockIdx.x, ks = blockIdx.y, cgrp = blockIdx.z;
+    const int tok0 = tile * XP_TOK;
+    const int tid = threadIdx.x, wid = tid / kWave, lane = tid % kWave;
+    const int kb32 = d_in / 32;
+    const int kbeg = (int)((long)ks * kb32 / ksplit) * 32;
+    const int kend = (int)((long)(ks + 1) * kb32 / ksplit) * 32;
+    const int cbase = cgrp * XP_COLS + wid * XP_NBW * 16;  // first column of this wave (relative to col0)
+
+    v4f acc[4][XP_NBW];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < XP_NBW; ++n) acc[m][n] = v4f{0, 0, 0, 0};
+
+    const int lr = lane & 15, lg = lane >> 4;
+    for (int k0 = kbeg; k0 < kend; k0 += XP_KC) {
+        const int kc = min(XP_KC, kend - k0);
+        __syncthreads();
+        // stage x[tok0 .. +64][k0 .. +kc] as bf16 (zeros beyond T / kc)
+        for (int i = tid; i < XP_TOK * (XP_KC / 8); i += 256) {
+            const int r = i / (XP_KC / 8), c8 = i % (XP_KC / 8);
+            const int t = tok0 + r;
+            v4u val = v4u{0, 0, 0, 0};
+            if (t < T && c8 * 8 < kc) {
+                const size_t idx = (size_t)t * d_in + k0 + c8 * 8;
+                if (x_dtype == QE_BF16) {
+                    val = *reinterpret_cast<const v4u*>(reinterpret_cast<const uint16_t*>(x) + idx);
+                } else {
+                    const v4f* p = reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(x) + idx);
+                    v4f a = p[0], b = p[1];
+                    val[0] = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
+                    val[1] = f32_to_bf16_bits(a[2]) | (f32_to_bf16_bits(a[3]) << 16);
+                    val[2] = f32_to_bf16_bits(b[0]) | (f32_to_bf16_bits(b[1]) << 16);
+                    val[3] = f32_to_bf16_bits(b[2]) | (f32_to_bf16_bits(b[3]) << 16);
+                }
+            }
+            *reinterpret_cast<v4u*>(xs + r * XP_LDS_LD + c8 * 16) = val;
+        }
+        __syncthreads();
+        for (int s = 0; s < kc / 32; ++s) {
+            v8bf a[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                a[m] = *reinterpret_cast<const v8bf*>(xs + (m * 16 + lr) * XP_LDS_LD + (s * 32 + lg * 8) * 2);
+#pragma unroll
+            for (int n = 0; n < XP_NBW; ++n) {
+                const int c = cbase + n * 16 + lr;
+                v8bf b;
+                if (c < ncols) {
+                    b = *reinterpret_cast<const v8bf*>(mt + (size_t)(col0 + c) * d_in + k0 + s * 32 + lg * 8);
+                } else {
+                    b = v8bf{};
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b, acc[m][n], 0, 0, 0);
+            }
+        }
+    }
+    // store partials: lane holds rows 4*lg + r, column lr of each 16x16 block
+    float* out = part + (size_t)ks * T * ncols_pad;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int n = 0; n < XP_NBW; ++n) {
+            const int c = cbase + n * 16 + lr;
+            if (c >= ncols_pad) continue;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = tok0 + m * 16 + lg * 4 + r;
+                if (t < T) out[(size_t)t * ncols_pad + c] = acc[m][n][r];
+            }
+        }
+}
+
+hipError_t launch_xproj(const void* x, int x_dtype, int T, int d_in, const uint16_t* mt, int col0, int ncols,
+                        int ncols_pad, int ksplit, float* part, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    dim3 grid((T + XP_TOK - 1) / XP_TOK, ksplit, (ncols_pad + XP_COLS - 1) / XP_COLS);
+    hipLaunchKernelGGL(xproj_kernel, grid, dim3(256), 0, st, x, x_dtype, T, d_in, mt, col0, ncols, ncols_pad, ksplit,
+                       part);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------- x-projection reduction + router
+// One wave per token: reduce the split-K partials in a fixed order, take the
+// router argmin (lowest index on ties), and write the bf16 adapter inputs.
+__global__ __launch_bounds__(256) void xproj_finish_kernel(const float* __restrict__ part, int ksplit, int T,
+                                                           int ncols_pad, int se_col, int r_s, int rs_pad, int re_col,
+                                                           int n_r, int r_r, int rr_pad, int router_col,
+                                                           const int32_t* __restrict__ expert_in,
+                                                           float* __restrict__ scores, int32_t* __restrict__ expert_out,
+                                                           uint16_t* __restrict__ u, uint16_t* __restrict__ v) {
+    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+    const int lane = threadIdx.x % kWave;
+    if (t >= T) return;
+    auto col_sum = [&](int c) {
+        float s = 0.0f;
+        for (int k = 0; k < ksplit; ++k) s += part[((size_t)k * T + t) * ncols_pad + c];
+        return s;
+    };
+    int e = 0;
+    if (router_col >= 0) {
+        float sc = lane < n_r ? col_sum(router_col + lane) : __builtin_inff();
+        if (scores && lane < n_r) scores[(size_t)t * n_r + lane] = sc;
+        // argmin with lowest index on ties
+        float best = sc;
+        int bi = lane;
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            float ob = __shfl_xor(best, off, 64);
+            int oi = __shfl_xor(bi, off, 64);
+            if (ob < best || (ob == best && oi < bi)) {
+                best = ob;
+                bi = oi;
+            }
+        }
+        e = bi;
+        if (lane == 0 && expert_out) expert_out[t] = e;
+    } else if (expert_in) {
+        e = min(max(expert_in[t], 0), max(n_r - 1, 0));
+    }
+    if (u && se_col >= 0) {
+        for (int c = lane; c < rs_pad; c += kWave)
+            u[(size_t)t * rs_pad + c] = c < r_s ? (uint16_t)f32_to_bf16_bits(col_sum(se_col + c)) : (uint16_t)0;
+    }
+    if (v && re_col >= 0) {
+        for (int c = lane; c < rr_pad; c += kWave)
+            v[(size_t)t * rr_pad + c] =
+                c < r_r ? (uint16_t)f32_to_bf16_bits(col_sum(re_col + e * rr_pad + c)) : (uint16_t)0;
+    }
+}
+
+hipError_t launch_xproj_finish(const float* part, int ksplit, int T, int ncols_pad, int col0, int se_col, int r_s,
+                               int rs_pad, int re_col, int n_r, int r_r, int rr_pad, int router_col,
+                               const int32_t* expert_in, float* scores, int32_t* expert_out, uint16_t* u,
+                               uint16_t* v, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    // columns are relative to the projected block that starts at col0
+    auto rel = [&](int c) { return c < 0 ? -1 : c - col0; };
+    hipLaunchKernelGGL(xproj_finish_kernel, dim3((T + 3) / 4), dim3(256), 0, st, part, ksplit, T, ncols_pad,
+                       rel(se_col), r_s, rs_pad, rel(re_col), n_r, r_r, rr_pad, rel(router_col), expert_in, scores,
+                       expert_out, u, v);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- bucketing
+// Single workgroup: counts, exclusive offsets and the permutation of tokens
+// sorted by (expert, token index), built chunk by chunk in token order.
+__global__ __launch_bounds__(1024) void bucket_kernel(const int32_t* __restrict__ expert, int T, int n_r,
+                                                      int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                      int32_t* __restrict__ perm) {
+    __shared__ int cnt[kMaxRouted];
+    __shared__ int base[kMaxRouted];
+    __shared__ int wave_cnt[16][kMaxRouted];
+    const int tid = threadIdx.x, wid = tid / kWave, lane = tid % kWave;
+    if (tid < kMaxRouted) cnt[tid] = 0;
+    __syncthreads();
+    for (int t = tid; t < T; t += 1024) atomicAdd(&cnt[min(max(expert[t], 0), n_r - 1)], 1);
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int e = 0; e < n_r; ++e) {
+            base[e] = acc;
+            offsets[e] = acc;
+            counts[e] = cnt[e];
+            acc += cnt[e];
+        }
+        offsets[n_r] = acc;
+    }
+    __syncthreads();
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int c0 = 0; c0 < T; c0 += 1024) {
+        const int t = c0 + tid;
+        const int e = t < T ? min(max(expert[t], 0), n_r - 1) : -1;
+        // per-wave counts of each expert
+        for (int k = 0; k < n_r; ++k) {
+            uint64_t bal = __ballot(e == k);
+            if (lane == 0) wave_cnt[wid][k] = __popcll(bal);
+        }
+        __syncthreads();
+        int rank = 0;
+        if (e >= 0) {
+            for (int w = 0; w < wid; ++w) rank += wave_cnt[w][e];
+        }
+        // rank within the wave among lanes with the same expert
+        for (int k = 0; k < n_r; ++k) {
+            uint64_t bal = __ballot(e == k);
+            if (e == k) rank += __popcll(bal & lt_mask);
+        }
+        if (e >= 0) perm[base[e] + rank] = t;
+        __syncthreads();
+        if (tid < n_r) {
+            int tot = 0;
+            for (int w = 0; w < 16; ++w) tot += wave_cnt[w][tid];
+            base[tid] += tot;
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_bucket(const int32_t* expert, int T, int n_r, int32_t* counts, int32_t* offsets, int32_t* perm,
+                         hipStream_t st) {
+    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(1024), 0, st, expert, T, n_r, counts, offsets, perm);
+    return hipGetLastError();
+}
+
+}  // namespace qe

@@ -1,0 +1,520 @@
+// Host side of libqe: argument validation, buffer layouts, launch sequencing,
+// weight quantization/packing (host) and the Table 7 cost model.
+// See include/qe.h for the contract of every entry point.
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "qe_internal.h"
+
+namespace qe {
+hipError_t skinny_set_attributes();
+int skinny_ksplit(int d_in, int d_out);
+}  // namespace qe
+
+using namespace qe;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_fail(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return QE_ERR_HIP;
+}
+
+#define QE_TRY_HIP(expr)                            \
+    do {                                            \
+        hipError_t _e = (expr);                     \
+        if (_e != hipSuccess) return hip_fail(_e);  \
+    } while (0)
+
+#define QE_CHECK(cond, code) \
+    do {                     \
+        if (!(cond)) return (code); \
+    } while (0)
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int validate_linear(const qe_linear* lin) {
+    QE_CHECK(lin != nullptr, QE_ERR_INVALID_ARG);
+    QE_CHECK(lin->d_in > 0 && lin->d_out > 0, QE_ERR_INVALID_ARG);
+    QE_CHECK(lin->w_bits == 3 || lin->w_bits == 4, QE_ERR_INVALID_ARG);
+    QE_CHECK(lin->a_bits == 6 || lin->a_bits == 8 || lin->a_bits == 16, QE_ERR_INVALID_ARG);
+    QE_CHECK(!(lin->w_bits == 3 && lin->a_bits != 16), QE_ERR_UNSUPPORTED);
+    QE_CHECK(lin->r_shared >= 0 && lin->r_shared <= kMaxRank, QE_ERR_INVALID_ARG);
+    QE_CHECK(lin->n_routed >= 0 && lin->n_routed <= kMaxRouted, QE_ERR_INVALID_ARG);
+    if (lin->n_routed > 0) {
+        QE_CHECK(lin->r_routed >= 1 && lin->r_routed <= kMaxRank, QE_ERR_INVALID_ARG);
+    } else {
+        QE_CHECK(lin->r_routed == 0, QE_ERR_INVALID_ARG);
+    }
+    QE_CHECK(lin->d_out % 16 == 0, QE_ERR_UNSUPPORTED);
+    QE_CHECK(lin->d_in % 128 == 0, QE_ERR_UNSUPPORTED);
+    // 16 * |acc| must stay below 2^31 on the int8 path: 16 * 127 * 7 * d_in
+    QE_CHECK(lin->a_bits == 16 || (int64_t)lin->d_in * 16 * 127 * 7 < (int64_t)INT32_MAX, QE_ERR_UNSUPPORTED);
+    return QE_OK;
+}
+
+int validate_forward_common(const qe_linear* lin, int32_t T, int32_t x_dtype, const void* x, void* ws,
+                            size_t ws_bytes) {
+    int st = validate_linear(lin);
+    if (st) return st;
+    QE_CHECK(T >= 0, QE_ERR_INVALID_ARG);
+    QE_CHECK(x_dtype == QE_F32 || x_dtype == QE_BF16, QE_ERR_INVALID_ARG);
+    QE_CHECK(lin->prep != nullptr, QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(lin->prep), QE_ERR_ALIGNMENT);
+    if (x) QE_CHECK(aligned16(x), QE_ERR_ALIGNMENT);
+    if (T > 0) QE_CHECK(ws_bytes >= qe_workspace_bytes(lin, T), QE_ERR_WORKSPACE);
+    if (T > 0) QE_CHECK(ws != nullptr, QE_ERR_WORKSPACE);
+    if (ws) QE_CHECK(aligned16(ws), QE_ERR_ALIGNMENT);
+    return QE_OK;
+}
+
+inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+template <class P>
+inline P* at(const void* base, size_t off) {
+    return reinterpret_cast<P*>(reinterpret_cast<uintptr_t>(base) + off);
+}
+
+int xproj_ksplit(int T, int d_in, int ncols_pad) {
+    if (T <= 0 || ncols_pad <= 0) return 1;
+    const int tiles = (T + 63) / 64 * ((ncols_pad + 319) / 320);
+    int ks = (512 + tiles - 1) / tiles;
+    ks = std::min(ks, std::max(1, d_in / 512));
+    return std::max(ks, 1);
+}
+
+int ensure_attributes() {
+    QE_TRY_HIP(skinny_set_attributes());
+    return QE_OK;
+}
+
+}  // namespace
+
+namespace qe {
+
+PrepLayout prep_layout(const qe_linear* lin) {
+    PrepLayout L{};
+    const size_t d_in = lin->d_in, d_out = lin->d_out;
+    L.rs_pad = rank_pad(lin->r_shared);
+    L.rr_pad = lin->n_routed > 0 ? rank_pad(lin->r_routed) : 0;
+    L.has_smooth = lin->a_bits != 16;
+    L.col_se = L.rs_pad > 0 ? 0 : -1;
+    L.col_re = lin->n_routed > 0 ? L.rs_pad : -1;
+    L.col_router = lin->n_routed > 0 ? L.rs_pad + lin->n_routed * L.rr_pad : -1;
+    L.n_cols = L.rs_pad + lin->n_routed * L.rr_pad + lin->n_routed;
+    L.n_cols_pad = (L.n_cols + 15) / 16 * 16;
+    size_t off = 0;
+    L.w_tiled = off;
+    L.w_tiled_bytes = lin->w_bits == 4 ? d_out * d_in / 2 : d_out * d_in * 3 / 8;
+    off = align256(off + L.w_tiled_bytes);
+    L.w_scale = off;
+    off = align256(off + d_out * 4);
+    L.smooth = off;
+    off = align256(off + (L.has_smooth ? d_in * 4 : 0));
+    L.inv_smooth = off;
+    off = align256(off + (L.has_smooth ? d_in * 4 : 0));
+    L.mt = off;
+    off = align256(off + (size_t)L.n_cols_pad * d_in * 2);
+    L.bt_s = off;
+    off = align256(off + d_out * L.rs_pad * 2);
+    L.bt_r = off;
+    off = align256(off + (size_t)lin->n_routed * d_out * L.rr_pad * 2);
+    L.total = off;
+    return L;
+}
+
+WsLayout ws_layout(const qe_linear* lin, int T) {
+    WsLayout W{};
+    const PrepLayout P = prep_layout(lin);
+    const size_t t = T > 0 ? T : 0;
+    W.xproj_ksplit = xproj_ksplit(T, lin->d_in, P.n_cols_pad);
+    W.skinny_ksplit = lin->a_bits == 16 ? skinny_ksplit(lin->d_in, lin->d_out) : 0;
+    size_t off = 0;
+    W.codes = off;
+    off = align256(off + (lin->a_bits == 16 ? 0 : t * lin->d_in));
+    W.s_x = off;
+    off = align256(off + t * 4);
+    W.part = off;
+    off = align256(off + (size_t)W.xproj_ksplit * t * P.n_cols_pad * 4);
+    W.scores = off;
+    off = align256(off + t * std::max(lin->n_routed, 1) * 4);
+    W.expert = off;
+    off = align256(off + t * 4);
+    W.counts = off;
+    off = align256(off + 32 * 4);
+    W.offsets = off;
+    off = align256(off + 32 * 4);
+    W.perm = off;
+    off = align256(off + t * 4);
+    W.u = off;
+    off = align256(off + t * P.rs_pad * 2);
+    W.v = off;
+    off = align256(off + t * P.rr_pad * 2);
+    W.skinny = off;
+    off = align256(off + (size_t)W.skinny_ksplit * t * lin->d_out * 4);
+    W.total = off;
+    return W;
+}
+
+}  // namespace qe
+
+// ======================================================================= ABI
+extern "C" {
+
+const char* qe_status_string(int status) {
+    switch (status) {
+        case QE_OK: return "QE_OK";
+        case QE_ERR_INVALID_ARG: return "QE_ERR_INVALID_ARG";
+        case QE_ERR_UNSUPPORTED: return "QE_ERR_UNSUPPORTED";
+        case QE_ERR_ALIGNMENT: return "QE_ERR_ALIGNMENT";
+        case QE_ERR_WORKSPACE: return "QE_ERR_WORKSPACE";
+        case QE_ERR_HIP: return "QE_ERR_HIP";
+        default: return "QE_UNKNOWN_STATUS";
+    }
+}
+
+int qe_last_hip_error(void) { return g_last_hip_error; }
+
+const char* qe_version(void) { return "libqe 0.1 (gfx950)"; }
+
+// ------------------------------------------------------------------ weights
+int qe_pack_weights(const float* W_f, const float* s, int32_t d_out, int32_t d_in, int32_t w_bits, void* packed,
+                    float* w_scale) {
+    QE_CHECK(W_f && packed && w_scale, QE_ERR_INVALID_ARG);
+    QE_CHECK(d_out > 0 && d_in > 0, QE_ERR_INVALID_ARG);
+    QE_CHECK(w_bits == 3 || w_bits == 4, QE_ERR_INVALID_ARG);
+    QE_CHECK(w_bits == 4 ? d_in % 2 == 0 : d_in % 32 == 0, QE_ERR_UNSUPPORTED);
+    const float qmax = w_bits == 4 ? 7.0f : 3.0f;
+    const size_t row_bytes = w_bits == 4 ? (size_t)d_in / 2 : (size_t)d_in / 32 * 12;
+    auto work = [&](int r0, int r1) {
+        std::vector<float> wp(d_in);
+        std::vector<int> q(d_in);
+        for (int i = r0; i < r1; ++i) {
+            const float* row = W_f + (size_t)i * d_in;
+            float amax = 0.0f;
+            for (int j = 0; j < d_in; ++j) {
+                float v = s ? row[j] * s[j] : row[j];
+                wp[j] = v;
+                amax = std::max(amax, std::fabs(v));
+            }
+            const float sw = amax / qmax;
+            w_scale[i] = sw;
+            for (int j = 0; j < d_in; ++j) {
+                float c = 0.0f;
+                if (amax > 0.0f) c = std::min(std::max(std::nearbyint(wp[j] / sw), -qmax), qmax);
+                q[j] = (int)c;
+            }
+            uint8_t* out = reinterpret_cast<uint8_t*>(packed) + (size_t)i * row_bytes;
+            if (w_bits == 4) {
+                for (int m = 0; m < d_in / 2; ++m)
+                    out[m] = (uint8_t)((q[2 * m] & 0xF) | ((q[2 * m + 1] & 0xF) << 4));
+            } else {
+                for (int g = 0; g < d_in / 32; ++g) {
+                    uint32_t w3[3] = {0, 0, 0};
+                    for (int c = 0; c < 32; ++c) {
+                        const uint32_t code = (uint32_t)q[g * 32 + c] & 7u;
+                        const int bit = 3 * c, wi = bit >> 5, off = bit & 31;
+                        w3[wi] |= code << off;
+                        if (off > 29) w3[wi + 1] |= code >> (32 - off);
+                    }
+                    std::memcpy(out + (size_t)g * 12, w3, 12);
+                }
+            }
+        }
+    };
+    const int hw = std::max(1u, std::min(32u, std::thread::hardware_concurrency()));
+    const int nthreads = std::min<long>(hw, std::max<long>(1, (long)d_out * d_in / (1 << 20)));
+    if (nthreads <= 1) {
+        work(0, d_out);
+    } else {
+        std::vector<std::thread> th;
+        for (int k = 0; k < nthreads; ++k) {
+            const int r0 = (int)((long)d_out * k / nthreads), r1 = (int)((long)d_out * (k + 1) / nthreads);
+            th.emplace_back(work, r0, r1);
+        }
+        for (auto& t : th) t.join();
+    }
+    return QE_OK;
+}
+
+size_t qe_prepared_bytes(const qe_linear* lin) {
+    if (validate_linear(lin) != QE_OK) return 0;
+    return prep_layout(lin).total;
+}
+
+int qe_prepare(const qe_linear* lin, const void* w_packed, const float* w_scale, const float* smooth,
+               const uint16_t* A_s, const uint16_t* B_s, const uint16_t* A_r, const uint16_t* B_r, const uint16_t* R,
+               void* prep, void* stream) {
+    int st = validate_linear(lin);
+    if (st) return st;
+    QE_CHECK(w_packed && w_scale && prep, QE_ERR_INVALID_ARG);
+    QE_CHECK((lin->r_shared > 0) == (A_s != nullptr) && (lin->r_shared > 0) == (B_s != nullptr), QE_ERR_INVALID_ARG);
+    QE_CHECK((lin->n_routed > 0) == (A_r != nullptr) && (lin->n_routed > 0) == (B_r != nullptr) &&
+                 (lin->n_routed > 0) == (R != nullptr),
+             QE_ERR_INVALID_ARG);
+    QE_CHECK(!(lin->a_bits == 16 && smooth != nullptr), QE_ERR_INVALID_ARG);
+    for (const void* p : {w_packed, (const void*)w_scale, (const void*)prep})
+        QE_CHECK(aligned16(p), QE_ERR_ALIGNMENT);
+    const PrepLayout L = prep_layout(lin);
+    hipStream_t s = S(stream);
+    const int d_in = lin->d_in, d_out = lin->d_out;
+    if (lin->w_bits == 4) {
+        QE_TRY_HIP(launch_prep_w4(reinterpret_cast<const uint8_t*>(w_packed), d_out, d_in, at<uint8_t>(prep, L.w_tiled), s));
+    } else {
+        QE_TRY_HIP(launch_prep_w3(reinterpret_cast<const uint32_t*>(w_packed), d_out, d_in, at<uint32_t>(prep, L.w_tiled), s));
+    }
+    QE_TRY_HIP(hipMemcpyAsync(at<void>(prep, L.w_scale), w_scale, (size_t)d_out * 4, hipMemcpyDeviceToDevice, s));
+    if (L.has_smooth)
+        QE_TRY_HIP(launch_prep_smooth(smooth, d_in, at<float>(prep, L.smooth), at<float>(prep, L.inv_smooth), s));
+    // Mt: [A_s^T ; A_1^T .. A_N^T ; R^T ; zero rows]
+    uint16_t* mt = at<uint16_t>(prep, L.mt);
+    QE_TRY_HIP(launch_fill_zero(mt, (size_t)L.n_cols_pad * d_in * 2, s));
+    if (L.rs_pad > 0) QE_TRY_HIP(launch_prep_transpose(A_s, d_in, lin->r_shared, mt + (size_t)L.col_se * d_in, d_in, L.rs_pad, s));
+    for (int e = 0; e < lin->n_routed; ++e) {
+        QE_TRY_HIP(launch_prep_transpose(A_r + (size_t)e * d_in * lin->r_routed, d_in, lin->r_routed,
+                                         mt + (size_t)(L.col_re + e * L.rr_pad) * d_in, d_in, L.rr_pad, s));
+    }
+    if (lin->n_routed > 0)
+        QE_TRY_HIP(launch_prep_transpose(R, d_in, lin->n_routed, mt + (size_t)L.col_router * d_in, d_in, lin->n_routed, s));
+    // Bt_s [d_out][rs_pad], Bt_r [N][d_out][rr_pad]
+    if (L.rs_pad > 0) QE_TRY_HIP(launch_prep_transpose(B_s, lin->r_shared, d_out, at<uint16_t>(prep, L.bt_s), L.rs_pad, d_out, s));
+    for (int e = 0; e < lin->n_routed; ++e) {
+        QE_TRY_HIP(launch_prep_transpose(B_r + (size_t)e * lin->r_routed * d_out, lin->r_routed, d_out,
+                                         at<uint16_t>(prep, L.bt_r) + (size_t)e * d_out * L.rr_pad, L.rr_pad, d_out, s));
+    }
+    return QE_OK;
+}
+
+size_t qe_workspace_bytes(const qe_linear* lin, int32_t T) {
+    if (validate_linear(lin) != QE_OK || T < 0) return 0;
+    return ws_layout(lin, T).total;
+}
+
+// ------------------------------------------------------------------ a1
+int qe_quant_act(const void* x, int32_t x_dtype, const float* smooth, int32_t T, int32_t d_in, int32_t a_bits,
+                 int8_t* codes, float* s_x, void* stream) {
+    QE_CHECK(T >= 0 && d_in > 0, QE_ERR_INVALID_ARG);
+    QE_CHECK(a_bits == 6 || a_bits == 8, QE_ERR_INVALID_ARG);
+    QE_CHECK(x_dtype == QE_F32 || x_dtype == QE_BF16, QE_ERR_INVALID_ARG);
+    QE_CHECK(d_in % 8 == 0, QE_ERR_UNSUPPORTED);
+    if (T == 0) return QE_OK;
+    QE_CHECK(x && codes && s_x, QE_ERR_INVALID_ARG);
+    for (const void* p : {x, (const void*)codes, (const void*)s_x}) QE_CHECK(aligned16(p), QE_ERR_ALIGNMENT);
+    if (smooth) QE_CHECK(aligned16(smooth), QE_ERR_ALIGNMENT);
+    QE_TRY_HIP(launch_quant_act(x, x_dtype, smooth, nullptr, T, d_in, a_bits, codes, s_x, S(stream)));
+    return QE_OK;
+}
+
+// Projection of x onto the columns [c0, c0 + nc) of the prepared Mt, then the
+// per-token reduction / routing.  Internal helper for route / adapter inputs / forward.
+static int run_xpass(const qe_linear* lin, const void* x, int x_dtype, int T, bool want_se, bool want_re,
+                     bool do_route, const int32_t* expert_in, float* scores, int32_t* expert_out, uint16_t* u,
+                     uint16_t* v, void* ws, hipStream_t s) {
+    const PrepLayout P = prep_layout(lin);
+    const WsLayout W = ws_layout(lin, T);
+    int c0 = P.n_cols, c1 = 0;
+    auto include = [&](int beg, int n) {
+        if (beg < 0 || n <= 0) return;
+        c0 = std::min(c0, beg);
+        c1 = std::max(c1, beg + n);
+    };
+    if (want_se) include(P.col_se, P.rs_pad);
+    if (want_re) include(P.col_re, lin->n_routed * P.rr_pad);
+    if (do_route) include(P.col_router, lin->n_routed);
+    if (c1 <= c0) return QE_OK;
+    const int nc = c1 - c0, nc_pad = (nc + 15) / 16 * 16;
+    const int ks = std::min(W.xproj_ksplit, xproj_ksplit(T, lin->d_in, nc_pad));
+    float* part = at<float>(ws, W.part);
+    const uint16_t* mt = at<const uint16_t>(lin->prep, P.mt);
+    QE_TRY_HIP(launch_xproj(x, x_dtype, T, lin->d_in, mt, c0, nc, nc_pad, ks, part, s));
+    QE_TRY_HIP(launch_xproj_finish(part, ks, T, nc_pad, c0, want_se ? P.col_se : -1, lin->r_shared, P.rs_pad,
+                                   want_re ? P.col_re : -1, lin->n_routed, lin->r_routed, P.rr_pad,
+                                   do_route ? P.col_router : -1, expert_in, scores, expert_out, want_se ? u : nullptr,
+                                   want_re ? v : nullptr, s));
+    return QE_OK;
+}
+
+// ------------------------------------------------------------------ a5
+int qe_route(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* scores, int32_t* expert,
+             int32_t* counts, int32_t* offsets, int32_t* perm, void* ws, size_t ws_bytes, void* stream) {
+    int st = validate_forward_common(lin, T, x_dtype, x, ws, ws_bytes);
+    if (st) return st;
+    QE_CHECK(lin->n_routed > 0, QE_ERR_INVALID_ARG);
+    if (T == 0) return QE_OK;
+    QE_CHECK(x && expert && counts && offsets && perm, QE_ERR_INVALID_ARG);
+    hipStream_t s = S(stream);
+    st = run_xpass(lin, x, x_dtype, T, false, false, true, nullptr, scores, expert, nullptr, nullptr, ws, s);
+    if (st) return st;
+    QE_TRY_HIP(launch_bucket(expert, T, lin->n_routed, counts, offsets, perm, s));
+    return QE_OK;
+}
+
+// ------------------------------------------------------------------ a4/a6 inputs
+int qe_adapter_inputs(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, const int32_t* expert,
+                      uint16_t* u, uint16_t* v, void* ws, size_t ws_bytes, void* stream) {
+    int st = validate_forward_common(lin, T, x_dtype, x, ws, ws_bytes);
+    if (st) return st;
+    QE_CHECK((lin->r_shared > 0) == (u != nullptr), QE_ERR_INVALID_ARG);
+    QE_CHECK((lin->n_routed > 0) == (v != nullptr) && (lin->n_routed > 0) == (expert != nullptr), QE_ERR_INVALID_ARG);
+    if (T == 0) return QE_OK;
+    QE_CHECK(x != nullptr, QE_ERR_INVALID_ARG);
+    const PrepLayout P = prep_layout(lin);
+    // u and v are written with the padded row strides used internally, then compacted
+    // if the caller's rank is not a multiple of 32
+    const bool direct_u = !u || P.rs_pad == lin->r_shared;
+    const bool direct_v = !v || P.rr_pad == lin->r_routed;
+    QE_CHECK(direct_u && direct_v, QE_ERR_UNSUPPORTED);
+    return run_xpass(lin, x, x_dtype, T, u != nullptr, v != nullptr, false, expert, nullptr, nullptr, u, v, ws, S(stream));
+}
+
+// ------------------------------------------------------------------ a3 / a7
+static int run_gemm(const qe_linear* lin, const int8_t* codes, const float* s_x, const void* x, int x_dtype, int T,
+                    const uint16_t* u, const uint16_t* v, const int32_t* expert, float* y, int32_t* acc_debug,
+                    void* ws, hipStream_t s) {
+    const PrepLayout P = prep_layout(lin);
+    const uint16_t* bt_s = P.rs_pad > 0 ? at<const uint16_t>(lin->prep, P.bt_s) : nullptr;
+    const uint16_t* bt_r = P.rr_pad > 0 ? at<const uint16_t>(lin->prep, P.bt_r) : nullptr;
+    const float* w_scale = at<const float>(lin->prep, P.w_scale);
+    if (!bt_s) u = nullptr;
+    if (!bt_r) v = nullptr;
+    if (lin->a_bits == 16) {
+        const WsLayout W = ws_layout(lin, T);
+        float* part = at<float>(ws, W.skinny);
+        int st = ensure_attributes();
+        if (st) return st;
+        QE_TRY_HIP(launch_skinny(x, x_dtype, T, lin->d_in, lin->d_out, lin->w_bits, at<const void>(lin->prep, P.w_tiled),
+                                 W.skinny_ksplit, part, s));
+        QE_TRY_HIP(launch_skinny_finish(part, W.skinny_ksplit, T, lin->d_out, w_scale, u, bt_s, P.rs_pad, v, expert,
+                                        bt_r, P.rr_pad, y, s));
+    } else {
+        QE_TRY_HIP(launch_gemm_w4(codes, s_x, at<const uint8_t>(lin->prep, P.w_tiled), w_scale, T, lin->d_in,
+                                  lin->d_out, u, bt_s, P.rs_pad, v, expert, bt_r, P.rr_pad, lin->n_routed, y, acc_debug,
+                                  s));
+    }
+    return QE_OK;
+}
+
+int qe_wq_gemm(const qe_linear* lin, const int8_t* codes, const float* s_x, const void* x, int32_t x_dtype, int32_t T,
+               const uint16_t* u, const uint16_t* v, const int32_t* expert, float* y, int32_t* acc_debug, void* ws,
+               size_t ws_bytes, void* stream) {
+    int st = validate_forward_common(lin, T, x_dtype, x, ws, ws_bytes);
+    if (st) return st;
+    if (T == 0) return QE_OK;
+    QE_CHECK(y != nullptr, QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(y), QE_ERR_ALIGNMENT);
+    if (lin->a_bits == 16) {
+        QE_CHECK(x != nullptr && acc_debug == nullptr, QE_ERR_INVALID_ARG);
+    } else {
+        QE_CHECK(codes && s_x, QE_ERR_INVALID_ARG);
+        QE_CHECK(aligned16(codes), QE_ERR_ALIGNMENT);
+    }
+    QE_CHECK((v == nullptr) == (expert == nullptr), QE_ERR_INVALID_ARG);
+    const PrepLayout P = prep_layout(lin);
+    QE_CHECK(!u || P.rs_pad == lin->r_shared, QE_ERR_UNSUPPORTED);
+    QE_CHECK(!v || P.rr_pad == lin->r_routed, QE_ERR_UNSUPPORTED);
+    return run_gemm(lin, codes, s_x, x, x_dtype, T, u, v, expert, y, acc_debug, ws, S(stream));
+}
+
+// ------------------------------------------------------------------ a6 unfused
+int qe_routed_lora(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, const int32_t* expert,
+                   const int32_t* offsets, const int32_t* perm, float* y, void* ws, size_t ws_bytes, void* stream) {
+    int st = validate_forward_common(lin, T, x_dtype, x, ws, ws_bytes);
+    if (st) return st;
+    QE_CHECK(lin->n_routed > 0, QE_ERR_INVALID_ARG);
+    QE_CHECK(T <= 65535, QE_ERR_UNSUPPORTED);
+    if (T == 0) return QE_OK;
+    QE_CHECK(x && expert && offsets && perm && y, QE_ERR_INVALID_ARG);
+    const PrepLayout P = prep_layout(lin);
+    const WsLayout W = ws_layout(lin, T);
+    hipStream_t s = S(stream);
+    uint16_t* v = at<uint16_t>(ws, W.v);
+    st = run_xpass(lin, x, x_dtype, T, false, true, false, expert, nullptr, nullptr, nullptr, v, ws, s);
+    if (st) return st;
+    QE_TRY_HIP(launch_routed_lora(v, P.rr_pad, offsets, perm, lin->n_routed, at<const uint16_t>(lin->prep, P.bt_r), T,
+                                  lin->d_out, y, s));
+    return QE_OK;
+}
+
+// ------------------------------------------------------------------ composite
+int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* y, int32_t* expert_out,
+                      void* ws, size_t ws_bytes, void* stream) {
+    int st = validate_forward_common(lin, T, x_dtype, x, ws, ws_bytes);
+    if (st) return st;
+    if (T == 0) return QE_OK;
+    QE_CHECK(x && y, QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(y), QE_ERR_ALIGNMENT);
+    const PrepLayout P = prep_layout(lin);
+    const WsLayout W = ws_layout(lin, T);
+    hipStream_t s = S(stream);
+    int32_t* expert = expert_out ? expert_out : at<int32_t>(ws, W.expert);
+    uint16_t* u = P.rs_pad > 0 ? at<uint16_t>(ws, W.u) : nullptr;
+    uint16_t* v = lin->n_routed > 0 ? at<uint16_t>(ws, W.v) : nullptr;
+    const bool route = lin->n_routed > 0;
+    st = run_xpass(lin, x, x_dtype, T, u != nullptr, route, route, nullptr, nullptr, route ? expert : nullptr, u, v,
+                   ws, s);
+    if (st) return st;
+    int8_t* codes = nullptr;
+    float* s_x = nullptr;
+    if (lin->a_bits != 16) {
+        codes = at<int8_t>(ws, W.codes);
+        s_x = at<float>(ws, W.s_x);
+        QE_TRY_HIP(launch_quant_act(x, x_dtype, at<const float>(lin->prep, P.smooth),
+                                    at<const float>(lin->prep, P.inv_smooth), T, lin->d_in, lin->a_bits, codes, s_x, s));
+    }
+    return run_gemm(lin, codes, s_x, x, x_dtype, T, u, v, route ? expert : nullptr, y, nullptr, ws, s);
+}
+
+// ------------------------------------------------------------------ a8
+int qe_colmean_abs(const void* W, int32_t dtype, int32_t d_out, int32_t d_in, float* w, void* stream) {
+    QE_CHECK(W && w, QE_ERR_INVALID_ARG);
+    QE_CHECK(d_out > 0 && d_in > 0, QE_ERR_INVALID_ARG);
+    QE_CHECK(dtype == QE_F32 || dtype == QE_BF16, QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(W) && aligned16(w), QE_ERR_ALIGNMENT);
+    QE_TRY_HIP(launch_colmean(W, dtype, d_out, d_in, w, S(stream)));
+    return QE_OK;
+}
+
+int qe_channel_topk(const void* x, int32_t x_dtype, const float* w, int32_t T, int32_t d_in, int32_t k, int32_t* topk,
+                    uint32_t* hist, void* stream) {
+    QE_CHECK(T >= 0 && d_in > 0, QE_ERR_INVALID_ARG);
+    QE_CHECK(x_dtype == QE_F32 || x_dtype == QE_BF16, QE_ERR_INVALID_ARG);
+    QE_CHECK(k >= 1 && k <= d_in, QE_ERR_INVALID_ARG);
+    QE_CHECK(k <= 1024 && d_in <= 32768, QE_ERR_UNSUPPORTED);
+    if (T == 0) return QE_OK;
+    QE_CHECK(x && w && hist, QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(x) && aligned16(w) && aligned16(hist), QE_ERR_ALIGNMENT);
+    if (topk) QE_CHECK(aligned16(topk), QE_ERR_ALIGNMENT);
+    QE_TRY_HIP(launch_topk(x, x_dtype, w, T, d_in, k, topk, hist, S(stream)));
+    return QE_OK;
+}
+
+// ------------------------------------------------------------------ cost
+int qe_linear_cost(const qe_linear* lin, int32_t T, int32_t n_distinct, int32_t xb, double* int_macs,
+                   double* adapter_macs, double* alg_bytes) {
+    QE_CHECK(lin && T >= 0 && n_distinct >= 0 && (xb == 2 || xb == 4), QE_ERR_INVALID_ARG);
+    QE_CHECK(lin->d_in > 0 && lin->d_out > 0, QE_ERR_INVALID_ARG);
+    const double t = T, di = lin->d_in, dout = lin->d_out;
+    const double rs = lin->r_shared, nr = lin->n_routed, rr = lin->n_routed > 0 ? lin->r_routed : 0;
+    if (int_macs) *int_macs = t * di * dout;
+    if (adapter_macs) *adapter_macs = t * (di + dout) * (rs + rr) + t * di * nr;
+    if (alg_bytes) {
+        double b = t * di * xb;                              // x read once
+        b += di * dout * lin->w_bits / 8.0 + dout * 4.0;     // packed weights + scales
+        if (lin->a_bits != 16) b += di * 4.0;                // smoothing vector
+        b += t * dout * 4.0;                                 // y written once (float32)
+        b += (di + dout) * rs * 2.0;                         // shared expert
+        b += std::min<double>(n_distinct, nr) * (di + dout) * rr * 2.0;  // selected routed experts
+        b += di * nr * 2.0;                                  // router
+        *alg_bytes = b;
+    }
+    return QE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// Internal declarations shared by the libqe translation units (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/qe.h"
+
+namespace qe {
+
+// ------------------------------------------------------------------ vector types
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kMaxRouted = 16;
+constexpr int kMaxRank = 64;
+constexpr int kRankPad = 32;  // adapter ranks are padded to a multiple of one bf16 MFMA K step
+
+__host__ __device__ inline int rank_pad(int r) { return r <= 0 ? 0 : (r + kRankPad - 1) / kRankPad * kRankPad; }
+__host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// ---------------------------------------------------------- prepared-buffer map
+// All offsets are in bytes from the start of the prepared buffer.
+struct PrepLayout {
+    size_t w_tiled, w_tiled_bytes;  // main weights in the kernel layout
+    size_t w_scale;                 // float [d_out]
+    size_t smooth, inv_smooth;      // float [d_in] each (0 bytes when a_bits == 16)
+    size_t mt;                      // bf16 [n_cols_pad][d_in]: A_s^T, A_1^T..A_N^T, R^T, zero rows
+    size_t bt_s;                    // bf16 [d_out][rs_pad]  (B_s transposed, zero padded)
+    size_t bt_r;                    // bf16 [N_r][d_out][rr_pad]
+    size_t total;
+    int rs_pad, rr_pad;
+    int col_se, col_re, col_router;  // first row of each block inside mt
+    int n_cols, n_cols_pad;
+    bool has_smooth;
+};
+
+// ---------------------------------------------------------------- workspace map
+struct WsLayout {
+    size_t codes;       // int8 [T][d_in]
+    size_t s_x;         // float [T]
+    size_t part;        // float [ksplit][T][n_cols_pad]  (x-projection partials)
+    size_t scores;      // float [T][N_r]
+    size_t expert;      // int32 [T]
+    size_t counts;      // int32 [32]
+    size_t offsets;     // int32 [32]
+    size_t perm;        // int32 [T]
+    size_t u;           // bf16 [T][rs_pad]
+    size_t v;           // bf16 [T][rr_pad]
+    size_t skinny;      // float [ksplit][T][d_out]   (decode split-K partials)
+    size_t total;
+    int xproj_ksplit;
+    int skinny_ksplit;
+};
+
+PrepLayout prep_layout(const qe_linear* lin);
+WsLayout ws_layout(const qe_linear* lin, int T);
+
+// ----------------------------------------------------------- launch wrappers
+// Each returns hipSuccess or the launch error.  All arguments are validated by the
+// caller (qe_api.hip) before these are called.
+hipError_t launch_quant_act(const void* x, int x_dtype, const float* smooth, const float* inv_smooth,
+                            int T, int d_in, int a_bits, int8_t* codes, float* s_x, hipStream_t st);
+
+hipError_t launch_xproj(const void* x, int x_dtype, int T, int d_in, const uint16_t* mt, int col0, int ncols,
+                        int ncols_pad, int ksplit, float* part, hipStream_t st);
+
+// Reduces x-projection partials; routes (if router_col >= 0) or takes `expert_in`;
+// writes scores/expert and the bf16 adapter inputs u (shared) and v (selected routed).
+hipError_t launch_xproj_finish(const float* part, int ksplit, int T, int ncols_pad, int col0, int se_col,
+                               int r_s, int rs_pad, int re_col, int n_r, int r_r, int rr_pad, int router_col,
+                               const int32_t* expert_in, float* scores, int32_t* expert_out, uint16_t* u,
+                               uint16_t* v, hipStream_t st);
+
+hipError_t launch_bucket(const int32_t* expert, int T, int n_r, int32_t* counts, int32_t* offsets,
+                         int32_t* perm, hipStream_t st);
+
+hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* w_tiled, const float* w_scale,
+                          int T, int d_in, int d_out, const uint16_t* u, const uint16_t* bt_s, int rs_pad,
+                          const uint16_t* v, const int32_t* expert, const uint16_t* bt_r, int rr_pad, int n_r,
+                          float* y, int32_t* acc_debug, hipStream_t st);
+
+hipError_t launch_skinny(const void* x, int x_dtype, int T, int d_in, int d_out, int w_bits, const void* w_tiled,
+                         int ksplit, float* part, hipStream_t st);
+
+hipError_t launch_skinny_finish(const float* part, int ksplit, int T, int d_out, const float* w_scale,
+                                const uint16_t* u, const uint16_t* bt_s, int rs_pad, const uint16_t* v,
+                                const int32_t* expert, const uint16_t* bt_r, int rr_pad, float* y, hipStream_t st);
+
+hipError_t launch_routed_lora(const uint16_t* v, int rr_pad, const int32_t* offsets, const int32_t* perm, int n_r,
+                              const uint16_t* bt_r, int T, int d_out, float* y, hipStream_t st);
+
+hipError_t launch_colmean(const void* W, int dtype, int d_out, int d_in, float* w, hipStream_t st);
+
+hipError_t launch_topk(const void* x, int x_dtype, const float* w, int T, int d_in, int k, int32_t* topk,
+                       uint32_t* hist, hipStream_t st);
+
+// prepare kernels
+hipError_t launch_prep_w4(const uint8_t* packed, int d_out, int d_in, uint8_t* tiled, hipStream_t st);
+hipError_t launch_prep_w3(const uint32_t* packed, int d_out, int d_in, uint32_t* tiled, hipStream_t st);
+hipError_t launch_prep_transpose(const uint16_t* src, int rows, int cols, uint16_t* dst, int dst_ld, int dst_rows,
+                                 hipStream_t st);  // dst[c][r] = src[r][c], zero fill up to dst_rows x dst_ld
+hipError_t launch_prep_smooth(const float* s, int d_in, float* s_out, float* inv_out, hipStream_t st);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+}  // namespace qe

@@ -1,0 +1,337 @@
+"""GPU parity: every libqe entry point against the CPU oracle on the same seeded inputs.
+
+Bit-exact: activation codes and scales, int32 accumulators, routes (except router
+near-ties, which are counted and accepted), bucketing, top-k sets/order and the
+histogram.  Float outputs: max|y_gpu - y_ref| / max|y_ref| <= 2e-3 per linear.
+Full-size configurations run the GPU in the benchmark's launch configuration and
+compare sampled tokens (every output column of those tokens), which is exact
+because every step is per-token.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import qe_oracle as O
+from qe_testlib import check_routing, check_y, f32, near_ties, oracle_for, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def Q():
+    import quantized_linear_moe_amd as q
+    return q
+
+
+def _layer(Q, cfg, spec, params=None, **override):
+    params = params if params is not None else synth.gen_linear(cfg, spec)
+    w_bits, a_bits = override.get("w_bits", cfg.w_bits), override.get("a_bits", cfg.a_bits)
+    return Q.QELinear.from_params(params, w_bits, a_bits, device=DEV), params
+
+
+def _spec(cfg, name):
+    return next(l for l in cfg.linears if l.name == name)
+
+
+def _codes_ref(x, s, a_bits):
+    return O.quant_act(f32(x), s, a_bits)
+
+
+# ------------------------------------------------------------------ a1 quant
+@pytest.mark.parametrize("cfg_name,stream,lin_name", [("tiny", "x", "lin"), ("qwen2vl_2b", "x_attn", "q"),
+                                                      ("qwen2vl_72b", "x_down", "down")])
+def test_quant_act_bit_exact(Q, cfg_name, stream, lin_name):
+    cfg = synth.get_config(cfg_name)
+    x = synth.gen_activations(cfg, stream)
+    s = synth.gen_linear(cfg, _spec(cfg, lin_name), with_weight=False)["s"]
+    q_ref, sx_ref = _codes_ref(x, s, cfg.a_bits)
+    xd = x.to(DEV)
+    codes = torch.empty(x.shape, dtype=torch.int8, device=DEV)
+    s_x = torch.empty(x.shape[0], dtype=torch.float32, device=DEV)
+    Q.libqe.qe_quant_act(xd, torch.from_numpy(s).to(DEV), cfg.a_bits, codes, s_x)
+    torch.cuda.synchronize()
+    assert np.array_equal(s_x.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32))
+    assert np.array_equal(codes.cpu().numpy(), q_ref)
+
+
+def test_quant_act_golden_ties(Q):
+    import json
+    import os
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "rtn_act_cases.json")))["cases"]
+    for c in cases:
+        x = np.array(c["x"], np.float32)
+        pad = (-x.shape[1]) % 8
+        x = np.pad(x, ((0, 0), (0, pad)))
+        s = None if c["s"] is None else np.pad(np.array(c["s"], np.float32), (0, pad), constant_values=1.0)
+        codes = torch.empty(x.shape, dtype=torch.int8, device=DEV)
+        s_x = torch.empty(x.shape[0], dtype=torch.float32, device=DEV)
+        Q.libqe.qe_quant_act(torch.from_numpy(x).to(DEV), None if s is None else torch.from_numpy(s).to(DEV),
+                             c["a_bits"], codes, s_x)
+        torch.cuda.synchronize()
+        got = codes.cpu().numpy()[:, :x.shape[1] - pad]
+        assert got.tolist() == c["codes"], c["name"]
+        assert s_x.cpu().numpy().tolist() == c["s_x"], c["name"]
+
+
+# ------------------------------------------------------------------ a5 route
+@pytest.mark.parametrize("cfg_name,lin_name", [("tiny", "lin"), ("qwen2vl_2b", "q"), ("qwen2vl_72b", "down")])
+def test_route_parity(Q, cfg_name, lin_name):
+    cfg = synth.get_config(cfg_name)
+    spec = _spec(cfg, lin_name)
+    params = synth.gen_linear(cfg, spec, with_weight=False)
+    params["W_f"] = np.zeros((spec.d_out, spec.d_in), np.float32)  # weights do not enter routing
+    layer, _ = _layer(Q, cfg, spec, params)
+    x = synth.gen_activations(cfg, spec.stream)
+    T, n_r = x.shape[0], cfg.n_routed
+    ref = O.route(O.bf16_round(f32(x)) if x.dtype != torch.bfloat16 else f32(x), f32(params["R"]))
+    i32 = dict(dtype=torch.int32, device=DEV)
+    scores = torch.empty(T, n_r, dtype=torch.float32, device=DEV)
+    expert, perm = torch.empty(T, **i32), torch.empty(T, **i32)
+    counts, offsets = torch.empty(n_r, **i32), torch.empty(n_r + 1, **i32)
+    Q.libqe.qe_route(layer.lin, x.to(DEV), scores, expert, counts, offsets, perm, layer.workspace(T))
+    torch.cuda.synchronize()
+    sc = scores.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(sc - ref["scores"])) <= 1e-5 * np.max(np.abs(ref["scores"]))
+    e = expert.cpu().numpy()
+    diff = check_routing(ref, e)
+    print(f"near-ties: {int(near_ties(ref).sum())}, differing routes: {int(diff.sum())}")
+    # bucketing is exact for the GPU's routes
+    cnt = np.bincount(e, minlength=n_r)
+    assert np.array_equal(counts.cpu().numpy(), cnt)
+    assert np.array_equal(offsets.cpu().numpy(), np.concatenate([[0], np.cumsum(cnt)]))
+    assert np.array_equal(perm.cpu().numpy(), np.argsort(e, kind="stable"))
+
+
+# ------------------------------------------------------------ a3 accumulators
+@pytest.mark.parametrize("cfg_name,lin_name,T", [("tiny", "lin", None), ("tiny", "lin", 77), ("qwen2vl_2b", "gate", None),
+                                                 ("qwen2vl_2b", "k", 300)])
+def test_wq_gemm_acc_bit_exact(Q, cfg_name, lin_name, T):
+    cfg = synth.get_config(cfg_name)
+    spec = _spec(cfg, lin_name)
+    layer, params = _layer(Q, cfg, spec)
+    x = synth.gen_activations(cfg, spec.stream, T=T)
+    T = x.shape[0]
+    xd = x.to(DEV)
+    codes = torch.empty(x.shape, dtype=torch.int8, device=DEV)
+    s_x = torch.empty(T, dtype=torch.float32, device=DEV)
+    Q.libqe.qe_quant_act(xd, torch.from_numpy(params["s"]).to(DEV), cfg.a_bits, codes, s_x)
+    y = torch.empty(T, spec.d_out, dtype=torch.float32, device=DEV)
+    acc = torch.empty(T, spec.d_out, dtype=torch.int32, device=DEV)
+    Q.libqe.qe_wq_gemm(layer.lin, codes, s_x, None, T, None, None, None, y, acc, layer.workspace(T))
+    torch.cuda.synchronize()
+    qx, sx = _codes_ref(x, params["s"], cfg.a_bits)
+    qw, s_w = O.quant_weights(params["W_f"], params["s"], cfg.w_bits)
+    acc_ref, y_ref = O.main_term_int(qx, sx, qw, s_w)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), acc_ref)
+    assert rel_err(y.cpu().numpy(), y_ref) <= 2e-3
+
+
+# ------------------------------------------------------------ composite forward
+FWD_CASES = [("tiny", "lin", None)]
+FWD_CASES += [("qwen2vl_2b", l.name, None) for l in synth.get_config("qwen2vl_2b").linears]
+FWD_CASES += [("internvl2_8b", n, 192) for n in ("q", "k", "gate", "down")]
+FWD_CASES += [("qwen2vl_72b", l.name, 96) for l in synth.get_config("qwen2vl_72b").linears]
+
+
+@pytest.mark.parametrize("cfg_name,lin_name,n_sample", FWD_CASES)
+def test_linear_forward_parity(Q, cfg_name, lin_name, n_sample):
+    cfg = synth.get_config(cfg_name)
+    spec = _spec(cfg, lin_name)
+    layer, params = _layer(Q, cfg, spec)
+    x = synth.gen_activations(cfg, spec.stream)
+    T = x.shape[0]
+    y = torch.empty(T, spec.d_out, dtype=torch.float32, device=DEV)
+    expert = torch.empty(T, dtype=torch.int32, device=DEV)
+    layer.forward(x.to(DEV), y, expert)
+    torch.cuda.synchronize()
+    if n_sample is None:
+        tokens = np.arange(T)
+    else:  # sampled tokens, always including the first and the last (ragged) ones
+        rng = np.random.default_rng(123)
+        tokens = np.unique(np.concatenate([[0, T - 1], rng.choice(T, n_sample, replace=False)]))
+    x_sub = x[torch.as_tensor(tokens)]
+    ref = oracle_for(params, x, cfg.w_bits, cfg.a_bits, tokens=tokens)
+    err = check_y(y.cpu().numpy()[tokens], ref, params, x_sub, cfg.w_bits, cfg.a_bits,
+                  gpu_expert=expert.cpu().numpy()[tokens])
+    print(f"{cfg_name}/{lin_name}: max rel err {err:.3e}, near-ties {int(near_ties(ref).sum())}")
+
+
+# ------------------------------------------------------------ a7 decode (A16)
+@pytest.mark.parametrize("lin_name", ["up", "down"])
+def test_decode_w3a16_parity(Q, lin_name):
+    cfg = synth.get_config("qwen2vl_72b_decode")
+    spec = _spec(cfg, lin_name)
+    layer, params = _layer(Q, cfg, spec)
+    x = synth.gen_activations(cfg, spec.stream)
+    y = torch.empty(x.shape[0], spec.d_out, dtype=torch.float32, device=DEV)
+    expert = torch.empty(x.shape[0], dtype=torch.int32, device=DEV)
+    layer.forward(x.to(DEV), y, expert)
+    torch.cuda.synchronize()
+    ref = oracle_for(params, x, cfg.w_bits, cfg.a_bits)
+    err = check_y(y.cpu().numpy(), ref, params, x, cfg.w_bits, cfg.a_bits, gpu_expert=expert.cpu().numpy())
+    print(f"decode {lin_name}: max rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("w_bits,T,x_dtype", [(4, 5, torch.bfloat16), (3, 16, torch.float32), (3, 37, torch.bfloat16)])
+def test_decode_small_shapes(Q, w_bits, T, x_dtype):
+    cfg = synth.get_config("tiny")
+    spec = synth.LinearSpec("lin", 384, 272, "x")
+    params = synth.gen_linear(cfg, spec)
+    layer, _ = _layer(Q, cfg, spec, params, w_bits=w_bits, a_bits=16)
+    x = (torch.randn(T, spec.d_in, generator=torch.Generator().manual_seed(w_bits * 100 + T)) * 3).to(x_dtype)
+    y = torch.empty(T, spec.d_out, dtype=torch.float32, device=DEV)
+    expert = torch.empty(T, dtype=torch.int32, device=DEV)
+    layer.forward(x.to(DEV), y, expert)
+    torch.cuda.synchronize()
+    ref = oracle_for(params, x, w_bits, 16)
+    check_y(y.cpu().numpy(), ref, params, x, w_bits, 16, gpu_expert=expert.cpu().numpy())
+
+
+# ------------------------------------------------------------ edge cases
+def _custom(Q, d_in, d_out, T, w_bits=4, a_bits=8, r_s=8, n_r=4, r_r=8, seed=0, x_dtype=torch.bfloat16, x=None,
+            R=None):
+    rng = np.random.default_rng(seed)
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    params = dict(W_f=(rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32),
+                  s=rng.uniform(0.5, 2, d_in).astype(np.float32) if a_bits != 16 else None,
+                  A_s=bf(rng.standard_normal((d_in, r_s)) * 0.02) if r_s else None,
+                  B_s=bf(rng.standard_normal((r_s, d_out)) * 0.02) if r_s else None,
+                  A_r=bf(rng.standard_normal((n_r, d_in, r_r)) * 0.02) if n_r else None,
+                  B_r=bf(rng.standard_normal((n_r, r_r, d_out)) * 0.02) if n_r else None,
+                  R=(R if R is not None else bf(rng.standard_normal((d_in, n_r)) * 0.02)) if n_r else None)
+    if x is None:
+        x = torch.from_numpy(rng.standard_normal((T, d_in)).astype(np.float32) * 2).to(x_dtype)
+    layer = Q.QELinear.from_params(params, w_bits, a_bits, device=DEV)
+    y = torch.empty(T, d_out, dtype=torch.float32, device=DEV)
+    expert = torch.empty(T, dtype=torch.int32, device=DEV)
+    layer.forward(x.to(DEV), y, expert if n_r else None)
+    torch.cuda.synchronize()
+    ref = oracle_for(params, x, w_bits, a_bits)
+    err = check_y(y.cpu().numpy(), ref, params, x, w_bits, a_bits, gpu_expert=expert.cpu().numpy() if n_r else None)
+    return layer, params, x, y, expert, ref, err
+
+
+@pytest.mark.parametrize("T", [1, 2, 129, 300])
+def test_edge_token_counts(Q, T):
+    _custom(Q, 256, 272, T, seed=T)
+
+
+@pytest.mark.parametrize("a_bits,x_dtype", [(6, torch.float32), (8, torch.bfloat16), (6, torch.bfloat16)])
+def test_edge_bits_and_dtypes(Q, a_bits, x_dtype):
+    _custom(Q, 512, 400, 70, a_bits=a_bits, x_dtype=x_dtype, seed=a_bits)
+
+
+def test_edge_rtn_and_shared_only(Q):
+    _custom(Q, 256, 256, 50, r_s=0, n_r=0, r_r=0, seed=11)          # pure RTN baseline
+    _custom(Q, 256, 256, 50, r_s=32, n_r=0, r_r=0, seed=12)         # shared expert only (LQER-style)
+    _custom(Q, 256, 256, 50, r_s=0, n_r=3, r_r=16, seed=13)         # routed experts only
+    _custom(Q, 256, 256, 50, r_s=64, n_r=16, r_r=48, seed=14)       # max experts, padded rank
+
+
+def test_edge_all_tokens_one_expert_and_empty_experts(Q):
+    rng = np.random.default_rng(5)
+    d_in = 256
+    x = torch.from_numpy(np.abs(rng.standard_normal((90, d_in))).astype(np.float32) + 0.1).to(torch.bfloat16)
+    R = (rng.standard_normal((d_in, 4)) * 0.02).astype(np.float32)
+    R[:, 2] = -1.0
+    _, _, _, _, expert, ref, _ = _custom(Q, d_in, 512, 90, x=x, R=torch.from_numpy(R).to(torch.bfloat16), seed=5)
+    assert np.all(expert.cpu().numpy() == 2)
+
+
+def test_determinism_bitwise(Q):
+    cfg = synth.get_config("qwen2vl_2b")
+    spec = _spec(cfg, "down")
+    layer, _ = _layer(Q, cfg, spec)
+    x = synth.gen_activations(cfg, spec.stream).to(DEV)
+    y1, y2 = layer.forward(x), layer.forward(x)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+
+
+# ------------------------------------------------------------ a4/a6 pieces
+def test_adapter_inputs_and_unfused_routed(Q):
+    cfg = synth.get_config("qwen2vl_2b")
+    spec = _spec(cfg, "o")
+    layer, params = _layer(Q, cfg, spec)
+    x = synth.gen_activations(cfg, spec.stream, T=500)
+    T, d_out = x.shape[0], spec.d_out
+    xd = x.to(DEV)
+    ws = layer.workspace(T)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    expert, perm = torch.empty(T, **i32), torch.empty(T, **i32)
+    counts, offsets = torch.empty(cfg.n_routed, **i32), torch.empty(cfg.n_routed + 1, **i32)
+    Q.libqe.qe_route(layer.lin, xd, None, expert, counts, offsets, perm, ws)
+    u = torch.empty(T, cfg.r_shared, dtype=torch.bfloat16, device=DEV)
+    v = torch.empty(T, cfg.r_routed, dtype=torch.bfloat16, device=DEV)
+    Q.libqe.qe_adapter_inputs(layer.lin, xd, expert, u, v, ws)
+    torch.cuda.synchronize()
+    e = expert.cpu().numpy()
+    xb = f32(x)
+    u_ref = xb.astype(np.float64) @ f32(params["A_s"]).astype(np.float64)
+    v_ref = np.stack([xb[t].astype(np.float64) @ f32(params["A_r"])[e[t]] for t in range(T)])
+    assert rel_err(f32(u), u_ref) <= 8e-3 and rel_err(f32(v), v_ref) <= 8e-3
+    # main product + shared expert, then the routed experts added by the grouped kernel
+    codes = torch.empty(x.shape, dtype=torch.int8, device=DEV)
+    s_x = torch.empty(T, dtype=torch.float32, device=DEV)
+    Q.libqe.qe_quant_act(xd, torch.from_numpy(params["s"]).to(DEV), cfg.a_bits, codes, s_x)
+    y = torch.empty(T, d_out, dtype=torch.float32, device=DEV)
+    Q.libqe.qe_wq_gemm(layer.lin, codes, s_x, None, T, u, None, None, y, None, ws)
+    Q.libqe.qe_routed_lora(layer.lin, xd, expert, offsets, perm, y, ws)
+    torch.cuda.synchronize()
+    ref = oracle_for(params, x, cfg.w_bits, cfg.a_bits)
+    check_y(y.cpu().numpy(), ref, params, x, cfg.w_bits, cfg.a_bits, gpu_expert=e)
+
+
+# ------------------------------------------------------------ a8 top-k
+@pytest.mark.parametrize("cfg_name,lin_name", [("tiny", "lin"), ("internvl2_8b", "q"), ("internvl2_8b", "down")])
+def test_channel_topk_bit_exact(Q, cfg_name, lin_name):
+    cfg = synth.get_config(cfg_name)
+    spec = _spec(cfg, lin_name)
+    W = synth.gen_linear(cfg, spec)["W_f"]
+    w = O.colmean_abs(W)
+    x = synth.gen_activations(cfg, spec.stream)
+    T, d = x.shape
+    topk = torch.empty(T, cfg.k, dtype=torch.int32, device=DEV)
+    hist = torch.zeros(d, dtype=torch.int32, device=DEV)
+    xd, wd = x.to(DEV), torch.from_numpy(w).to(DEV)
+    Q.libqe.qe_channel_topk(xd, wd, cfg.k, topk, hist)
+    Q.libqe.qe_channel_topk(xd, wd, cfg.k, None, hist)  # the histogram accumulates
+    torch.cuda.synchronize()
+    t_ref, h_ref = O.channel_topk(f32(x), w, cfg.k)
+    assert np.array_equal(topk.cpu().numpy(), t_ref)
+    assert np.array_equal(hist.cpu().numpy().astype(np.int64), 2 * h_ref)
+
+
+@pytest.mark.parametrize("k", [1, 5, 64, 256])
+def test_channel_topk_ties_and_k(Q, k):
+    rng = np.random.default_rng(k)
+    x = np.round(rng.standard_normal((33, 256)) * 2).astype(np.float32)  # many exact ties
+    x[4] = 0.0
+    w = np.ones(256, np.float32)
+    w[::7] = 0.5
+    topk = torch.empty(33, k, dtype=torch.int32, device=DEV)
+    hist = torch.zeros(256, dtype=torch.int32, device=DEV)
+    Q.libqe.qe_channel_topk(torch.from_numpy(x).to(DEV), torch.from_numpy(w).to(DEV), k, topk, hist)
+    torch.cuda.synchronize()
+    t_ref, h_ref = O.channel_topk(x, w, k)
+    assert np.array_equal(topk.cpu().numpy(), t_ref)
+    assert np.array_equal(hist.cpu().numpy().astype(np.int64), h_ref)
+
+
+def test_colmean_abs(Q):
+    cfg = synth.get_config("qwen2vl_2b")
+    W = synth.gen_linear(cfg, _spec(cfg, "gate"))["W_f"]
+    Wb = torch.from_numpy(W).to(torch.bfloat16)
+    w = torch.empty(W.shape[1], dtype=torch.float32, device=DEV)
+    Q.libqe.qe_colmean_abs(Wb.to(DEV), w)
+    torch.cuda.synchronize()
+    ref = O.colmean_abs(f32(Wb))
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), ref.view(np.uint32))  # bf16 sums are exact in float64
+    Q.libqe.qe_colmean_abs(torch.from_numpy(W).to(DEV), w)
+    torch.cuda.synchronize()
+    ref32 = O.colmean_abs(W)
+    ulp = np.abs(w.cpu().numpy().view(np.int32).astype(np.int64) - ref32.view(np.int32).astype(np.int64))
+    assert ulp.max() <= 1
