@@ -1,0 +1,338 @@
+#!/usr/bin/env python3
+"""Benchmark of the Quant Experts (QE) linear hot path on one MI355X.
+
+Workload (one step): the seven decoder-layer linears of a Qwen2VL-72B-shaped layer
+(q 8192->8192, k/v 8192->1024, o 8192->8192, gate/up 8192->29568, down 29568->8192),
+W4A6, T = 4096 prefill tokens (3200 image-like + 896 text-like, synthetic), shared
+expert rank 32, 8 routed experts of rank 32, router d_in x 8.  Every linear runs the
+whole hot path: the fused prologue (x-projection for router + adapters, argmin
+routing, smoothing + per-token A6 quantization) and the int8-MFMA main GEMM with the
+dequantization and shared/routed low-rank terms fused into its epilogue.
+Inputs are resident in HBM before the timed region.
+
+Prints one JSON line.  `value` is tokens/s of the whole layer (T / step time).
+`roofline` is the main GEMM kernel (the dominant kernel), timed with HIP events
+around each of its launches on the stream it is launched on.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0    # MI355X dense int8 MFMA, tera-ops/s
+PEAK_BF16_TFLOPS = 2500.0  # dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # HBM3E
+METRIC = "QE-linear tokens/s + % int8-MFMA/HBM roofline, 72B shapes W4A6 (1 GPU)"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true")
+    return ap.parse_args()
+
+
+def gemm_source_hash():
+    h = hashlib.sha256()
+    for f in ("k_gemm_w4.hip", "qe_internal.h"):
+        with open(os.path.join(ROOT, "quantized_linear_moe_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(per_launch_alg_bytes):
+    """HBM bytes per GEMM launch from the committed rocprofv3 PMC summary, if it was
+    taken on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", "gemm_w4_qwen2vl72b_traffic.json")
+    try:
+        with open(p) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != gemm_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the QE linear on exactly one GPU; multi-GPU runs are not part of this "
+              f"benchmark (got --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import quantized_linear_moe_amd as qe
+    from quantized_linear_moe_amd import libqe
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = synth.get_config("qwen2vl_72b")
+    T = cfg.T
+    want_cpu = not args.no_cpu_baseline
+
+    # ------------------------------------------------------------ inputs (untimed)
+    t_setup = time.time()
+    xs_cpu = {s: synth.gen_activations(cfg, s) for s in cfg.streams()}
+    xs = {s: t.to(dev) for s, t in xs_cpu.items()}
+    layers, oracle_w = [], []
+    for spec in cfg.linears:
+        params = synth.gen_linear(cfg, spec)
+        layer = qe.QELinear.from_params(params, cfg.w_bits, cfg.a_bits, device=dev)
+        if want_cpu:
+            from oracle import qe_oracle as O  # CPU-baseline leg only
+            qw, s_w = O.quant_weights(params["W_f"], params["s"], cfg.w_bits)
+            oracle_w.append((qw, s_w, params))
+        del params["W_f"]
+        layers.append((spec, layer))
+        log(f"prepared {spec.name} {spec.d_in}->{spec.d_out}")
+    ws = torch.empty(max(libqe.qe_workspace_bytes(l.lin, T) for _, l in layers), dtype=torch.uint8, device=dev)
+    bufs = []
+    for spec, layer in layers:
+        bufs.append(dict(
+            codes=torch.empty(T, spec.d_in, dtype=torch.int8, device=dev),
+            s_x=torch.empty(T, dtype=torch.float32, device=dev),
+            u=torch.empty(T, libqe.rank_pad(cfg.r_shared), dtype=torch.bfloat16, device=dev),
+            v=torch.empty(T, libqe.rank_pad(cfg.r_routed), dtype=torch.bfloat16, device=dev),
+            e=torch.empty(T, dtype=torch.int32, device=dev),
+            y=torch.empty(T, spec.d_out, dtype=torch.float32, device=dev)))
+    torch.cuda.synchronize()
+    log(f"setup {time.time() - t_setup:.1f}s")
+
+    def step(ev=None):
+        for i, (spec, layer) in enumerate(layers):
+            b = bufs[i]
+            libqe.qe_linear_prologue(layer.lin, xs[spec.stream], b["codes"], b["s_x"], b["u"], b["v"], b["e"], ws)
+            if ev is not None:
+                ev[i][0].record()
+            libqe.qe_wq_gemm(layer.lin, b["codes"], b["s_x"], None, T, b["u"], b["v"], b["e"], b["y"], None, ws)
+            if ev is not None:
+                ev[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
+           for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(K):
+        step(evs[k])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / K
+    gemm_ms = np.array([[a.elapsed_time(b) for (a, b) in evs[k]] for k in range(K)])  # [K, 7]
+    gemm_ms_step = float(gemm_ms.sum(axis=1).mean())
+
+    # the composite entry point on the same inputs (must match the split prologue + GEMM)
+    for _ in range(2):
+        for i, (spec, layer) in enumerate(layers):
+            layer.forward(xs[spec.stream], bufs[i]["y"], bufs[i]["e"], ws)
+    torch.cuda.synchronize()
+    s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s2.record()
+    for _ in range(K):
+        for i, (spec, layer) in enumerate(layers):
+            layer.forward(xs[spec.stream], bufs[i]["y"], bufs[i]["e"], ws)
+    e2.record()
+    torch.cuda.synchronize()
+    ms_step_fwd = s2.elapsed_time(e2) / K
+
+    # ------------------------------------------------------------ accounting
+    int_ops = adapter_flops = alg_bytes = 0.0
+    per_linear = []
+    for i, (spec, layer) in enumerate(layers):
+        n_distinct = int(torch.unique(bufs[i]["e"]).numel())
+        im, am, ab = libqe.qe_linear_cost(layer.lin, T, n_distinct, 2)
+        int_ops += 2 * im
+        adapter_flops += 2 * am
+        alg_bytes += ab
+        per_linear.append(dict(name=spec.name, d_in=spec.d_in, d_out=spec.d_out,
+                               gemm_us=round(float(gemm_ms[:, i].mean()) * 1e3, 2),
+                               gemm_tops=round(2 * im / (gemm_ms[:, i].mean() * 1e-3) / 1e12, 1)))
+    achieved = int_ops / (gemm_ms_step * 1e-3) / 1e12
+    t_roof = max(int_ops / (PEAK_INT8_TOPS * 1e12) + adapter_flops / (PEAK_BF16_TFLOPS * 1e12),
+                 alg_bytes / (PEAK_HBM_GBS * 1e9))
+    traffic = load_traffic(None)
+
+    result = {
+        "metric": METRIC,
+        "value": round(T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": "qwen2vl_72b layer linears (q,k,v,o,gate,up,down), W4A6 prefill, T=4096, "
+                        "shared rank 32, 8 routed experts rank 32, router d_in x 8",
+            "T": T, "w_bits": 4, "a_bits": 6, "r_shared": 32, "n_routed": 8, "r_routed": 32,
+        },
+        "roofline": {
+            "kernel": "gemm_w4_kernel (int8 MFMA main GEMM + fused dequant/SE/RE epilogue)",
+            "bound": "mfma",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_INT8_TOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_INT8_TOPS, 4),
+            "traffic": traffic,
+            "launches_per_step": len(layers),
+            "avg_launch_us": round(gemm_ms_step / len(layers) * 1e3, 2),
+        },
+        "layer_roofline": {
+            "t_roof_ms": round(t_roof * 1e3, 4),
+            "frac": round(t_roof / (ms_step * 1e-3), 4),
+            "int_tops": round(int_ops / 1e12, 3), "adapter_tflop": round(adapter_flops / 1e12, 4),
+            "alg_gbytes": round(alg_bytes / 1e9, 3),
+        },
+        "breakdown": {"gemm_ms_per_step": round(gemm_ms_step, 4),
+                      "prologue_ms_per_step": round(ms_step - gemm_ms_step, 4),
+                      "ms_per_step_composite_entry": round(ms_step_fwd, 4),
+                      "wall_s_timed_region": round(wall, 3),
+                      "per_linear": per_linear},
+    }
+
+    if not args.no_extras:
+        result["extras"] = extras(torch, synth, qe, libqe, dev)
+
+    if want_cpu:
+        result["cpu_baseline"] = cpu_baseline(torch, cfg, xs_cpu, oracle_w, args.cpu_sample_tokens)
+
+    print(json.dumps(result), flush=True)
+
+
+def extras(torch, synth, qe, libqe, dev):
+    out = {}
+    # ---- decode: Qwen2VL-72B MLP up/down, W3A16, T=8 (HBM-bound weight streaming)
+    cfg = synth.get_config("qwen2vl_72b_decode")
+    layers = []
+    for spec in cfg.linears:
+        params = synth.gen_linear(cfg, spec)
+        layers.append((spec, qe.QELinear.from_params(params, cfg.w_bits, cfg.a_bits, device=dev)))
+        del params
+    xs = {s: synth.gen_activations(cfg, s).to(dev) for s in cfg.streams()}
+    T = cfg.T
+    wss = [l.workspace(T) for _, l in layers]
+    ys = [torch.empty(T, s.d_out, dtype=torch.float32, device=dev) for s, _ in layers]
+    es = [torch.empty(T, dtype=torch.int32, device=dev) for _ in layers]
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)  # larger than the 256 MB Infinity Cache
+
+    def run():
+        for i, (spec, layer) in enumerate(layers):
+            libqe.qe_linear_forward(layer.lin, xs[spec.stream], ys[i], es[i], wss[i])
+
+    for _ in range(3):
+        run()
+    cold, warm = [], []
+    for it in range(30):
+        flush.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    for it in range(30):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run()
+        b.record()
+        torch.cuda.synchronize()
+        warm.append(a.elapsed_time(b))
+    alg = 0.0
+    for i, (spec, layer) in enumerate(layers):
+        nd = int(torch.unique(es[i]).numel())
+        alg += libqe.qe_linear_cost(layer.lin, T, nd, 2)[2]
+    t_cold = float(np.median(cold)) * 1e-3
+    out["decode_qwen2vl72b_up_down_w3a16_T8"] = {
+        "us_cold_median": round(t_cold * 1e6, 2), "us_warm_median": round(float(np.median(warm)) * 1e3, 2),
+        "tokens_per_s": round(T / t_cold, 1), "alg_mbytes": round(alg / 1e6, 2),
+        "achieved_gbs": round(alg / t_cold / 1e9, 1), "hbm_frac": round(alg / t_cold / 1e9 / PEAK_HBM_GBS, 4),
+        "note": "Infinity Cache flushed (1 GiB write) before every cold iteration",
+    }
+    del layers, wss, flush
+    torch.cuda.empty_cache()
+
+    # ---- calibration statistic: InternVL2-8B down input, k = 32 (HBM / ALU bound)
+    cfg = synth.get_config("internvl2_8b")
+    spec = next(l for l in cfg.linears if l.name == "down")
+    W = torch.from_numpy(synth.gen_linear(cfg, spec)["W_f"]).to(dev)
+    w = torch.empty(spec.d_in, dtype=torch.float32, device=dev)
+    libqe.qe_colmean_abs(W, w)
+    x = synth.gen_activations(cfg, spec.stream).to(dev)
+    hist = torch.zeros(spec.d_in, dtype=torch.int32, device=dev)
+    topk = torch.empty(cfg.T, cfg.k, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        libqe.qe_channel_topk(x, w, cfg.k, topk, hist)
+    ts = []
+    for _ in range(20):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        libqe.qe_channel_topk(x, w, cfg.k, topk, hist)
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    t = float(np.median(ts)) * 1e-3
+    nbytes = x.numel() * 2 + spec.d_in * 4 * 2 + cfg.T * cfg.k * 4
+    out["topk_internvl2_8b_down_T4096_k32"] = {
+        "us_median": round(t * 1e6, 2), "tokens_per_s": round(cfg.T / t, 1),
+        "achieved_gbs": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)}
+    return out
+
+
+def cpu_baseline(torch, cfg, xs_cpu, oracle_w, n_tok):
+    """The CPU oracle as it stands, on a bounded sample of the same workload: n_tok of
+    the T tokens through all seven linears (its own weight quantization is done
+    beforehand and not timed, as the GPU's weight packing is not)."""
+    from oracle import qe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    rng = np.random.default_rng(7)
+    toks = np.sort(rng.choice(cfg.T, n_tok, replace=False))
+    f32 = lambda t: None if t is None else t.float().numpy()
+    t_total = 0.0
+    for (spec, (qw, s_w, params)) in zip(cfg.linears, oracle_w):
+        x = xs_cpu[spec.stream][torch.as_tensor(toks)].float().numpy()
+        t0 = time.perf_counter()
+        O.qe_linear(x, True, params["s"], qw, s_w, cfg.a_bits, A_s=f32(params["A_s"]), B_s=f32(params["B_s"]),
+                    A_r=f32(params["A_r"]), B_r=f32(params["B_r"]), R=f32(params["R"]))
+        t_total += time.perf_counter() - t0
+        log(f"oracle {spec.name}: {time.perf_counter() - t0:.2f}s")
+    return {"value": round(n_tok / t_total, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_tok} of {cfg.T} tokens through all 7 linears of the same layer "
+                      f"({t_total:.1f} s of oracle time; weight quantization untimed)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -160,8 +160,11 @@ int qe_route(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, fl
 
 /* (a4/a6, first half) Adapter inputs: u = bf16(x) . A_s and v[t] = bf16(x)[t] . A_{expert[t]},
  * accumulated in float32 and stored as bf16 (round to nearest even).
- * u: device bf16 [T][r_shared] (NULL iff r_shared == 0); v: device bf16 [T][r_routed]
- * (NULL iff n_routed == 0); expert: device int32 [T] in [0, n_routed) (NULL iff n_routed == 0).
+ * Adapter-input rows are padded to whole bf16 MFMA steps: u is device bf16 [T][ru] with
+ * ru = r_shared rounded up to a multiple of 32, v is [T][rv] with rv = r_routed rounded up
+ * to a multiple of 32; the padding columns are written as zeros.
+ * u: NULL iff r_shared == 0; v and expert (device int32 [T], values in [0, n_routed)):
+ * NULL iff n_routed == 0.
  */
 int qe_adapter_inputs(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T,
                       const int32_t* expert, uint16_t* u, uint16_t* v,
@@ -192,8 +195,19 @@ int qe_routed_lora(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t
                    const int32_t* expert, const int32_t* offsets, const int32_t* perm, float* y,
                    void* ws, size_t ws_bytes, void* stream);
 
-/* The whole QE linear: a1 + a5 + a4 + a6 + a3 (or a7 for a_bits 16), fused as
- * above.  y: device float32 [T][d_out] (overwritten); expert_out: device int32 [T]
+/* The activation-side half of the QE linear, fused: one pass of the x-projection gives the
+ * router scores (a5) and both adapter inputs (a4/a6 first halves), then the per-token
+ * quantization (a1).  Equivalent to qe_route + qe_adapter_inputs + qe_quant_act, with one
+ * read of x for all projections.  Outputs (device, caller-owned): codes int8 [T][d_in] and
+ * s_x float32 [T] (a_bits 6/8; both NULL for a_bits 16), u and v as for
+ * qe_adapter_inputs (padded rows), expert int32 [T].  Feed them to qe_wq_gemm.
+ */
+int qe_linear_prologue(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, int8_t* codes,
+                       float* s_x, uint16_t* u, uint16_t* v, int32_t* expert,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* The whole QE linear: qe_linear_prologue followed by qe_wq_gemm (a1 + a5 + a4 + a6 + a3,
+ * or a7 for a_bits 16).  y: device float32 [T][d_out] (overwritten); expert_out: device int32 [T]
  * or NULL (the routed expert of each token).  ws: qe_workspace_bytes(lin, T) bytes.
  */
 int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* y,

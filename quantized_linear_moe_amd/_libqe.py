@@ -46,7 +46,7 @@ class qe_linear(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"libqe.so not found at {LIB_PATH}; build it with `python -m quantized_linear_moe_amd.build` "
+            f"libqe.so not found at {LIB_PATH}; build it with `python quantized_linear_moe_amd/build.py` "
             "(hipcc, gfx950). There is no fallback implementation.")
     lib = ctypes.CDLL(LIB_PATH)
     P, I, Z, D = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.POINTER(ctypes.c_double)
@@ -64,6 +64,7 @@ def _load():
         "qe_adapter_inputs": (ctypes.c_int, [LP, P, I, I, P, P, P, P, Z, P]),
         "qe_wq_gemm": (ctypes.c_int, [LP, P, P, P, I, I, P, P, P, P, P, P, Z, P]),
         "qe_routed_lora": (ctypes.c_int, [LP, P, I, I, P, P, P, P, P, Z, P]),
+        "qe_linear_prologue": (ctypes.c_int, [LP, P, I, I, P, P, P, P, P, P, Z, P]),
         "qe_linear_forward": (ctypes.c_int, [LP, P, I, I, P, P, P, Z, P]),
         "qe_colmean_abs": (ctypes.c_int, [P, I, I, I, P, P]),
         "qe_channel_topk": (ctypes.c_int, [P, I, P, I, I, I, P, P, P]),
@@ -80,7 +81,7 @@ _lib = _load()
 EXPORTED = (
     "qe_status_string", "qe_last_hip_error", "qe_version", "qe_pack_weights", "qe_prepared_bytes", "qe_prepare",
     "qe_workspace_bytes", "qe_quant_act", "qe_route", "qe_adapter_inputs", "qe_wq_gemm", "qe_routed_lora",
-    "qe_linear_forward", "qe_colmean_abs", "qe_channel_topk", "qe_linear_cost",
+    "qe_linear_prologue", "qe_linear_forward", "qe_colmean_abs", "qe_channel_topk", "qe_linear_cost",
 )
 
 
@@ -185,6 +186,17 @@ def qe_routed_lora(lin, x, expert, offsets, perm, y, ws, stream=None):
     _check(_lib.qe_routed_lora(ctypes.byref(lin), _ptr(x), _dtype_code(x), x.shape[0], _ptr(expert), _ptr(offsets),
                                _ptr(perm), _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "qe_routed_lora")
+
+
+def qe_linear_prologue(lin, x, codes, s_x, u, v, expert, ws, stream=None):
+    _check(_lib.qe_linear_prologue(ctypes.byref(lin), _ptr(x), _dtype_code(x), x.shape[0], _ptr(codes), _ptr(s_x),
+                                   _ptr(u), _ptr(v), _ptr(expert), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)), "qe_linear_prologue")
+
+
+def rank_pad(r: int) -> int:
+    """Row stride (elements) of the adapter-input buffers u / v for rank r."""
+    return 0 if r <= 0 else (r + 31) // 32 * 32
 
 
 def qe_linear_forward(lin, x, y, expert_out, ws, stream=None):

@@ -1,6 +1,7 @@
 """Build libqe.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: python -m quantized_linear_moe_amd.build   (or build() from Python)
+Usage: python quantized_linear_moe_amd/build.py   (or load this file and call build()).
+The script imports nothing from the package, so it works before libqe.so exists.
 """
 
 import os

@@ -365,12 +365,6 @@ int qe_adapter_inputs(const qe_linear* lin, const void* x, int32_t x_dtype, int3
     QE_CHECK((lin->n_routed > 0) == (v != nullptr) && (lin->n_routed > 0) == (expert != nullptr), QE_ERR_INVALID_ARG);
     if (T == 0) return QE_OK;
     QE_CHECK(x != nullptr, QE_ERR_INVALID_ARG);
-    const PrepLayout P = prep_layout(lin);
-    // u and v are written with the padded row strides used internally, then compacted
-    // if the caller's rank is not a multiple of 32
-    const bool direct_u = !u || P.rs_pad == lin->r_shared;
-    const bool direct_v = !v || P.rr_pad == lin->r_routed;
-    QE_CHECK(direct_u && direct_v, QE_ERR_UNSUPPORTED);
     return run_xpass(lin, x, x_dtype, T, u != nullptr, v != nullptr, false, expert, nullptr, nullptr, u, v, ws, S(stream));
 }
 
@@ -416,9 +410,6 @@ int qe_wq_gemm(const qe_linear* lin, const int8_t* codes, const float* s_x, cons
         QE_CHECK(aligned16(codes), QE_ERR_ALIGNMENT);
     }
     QE_CHECK((v == nullptr) == (expert == nullptr), QE_ERR_INVALID_ARG);
-    const PrepLayout P = prep_layout(lin);
-    QE_CHECK(!u || P.rs_pad == lin->r_shared, QE_ERR_UNSUPPORTED);
-    QE_CHECK(!v || P.rr_pad == lin->r_routed, QE_ERR_UNSUPPORTED);
     return run_gemm(lin, codes, s_x, x, x_dtype, T, u, v, expert, y, acc_debug, ws, S(stream));
 }
 
@@ -443,6 +434,32 @@ int qe_routed_lora(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t
 }
 
 // ------------------------------------------------------------------ composite
+static int run_prologue(const qe_linear* lin, const void* x, int x_dtype, int T, int8_t* codes, float* s_x,
+                        uint16_t* u, uint16_t* v, int32_t* expert, void* ws, hipStream_t s) {
+    const PrepLayout P = prep_layout(lin);
+    const bool route = lin->n_routed > 0;
+    int st = run_xpass(lin, x, x_dtype, T, u != nullptr, route, route, nullptr, nullptr, route ? expert : nullptr, u,
+                       v, ws, s);
+    if (st) return st;
+    if (lin->a_bits != 16)
+        QE_TRY_HIP(launch_quant_act(x, x_dtype, at<const float>(lin->prep, P.smooth),
+                                    at<const float>(lin->prep, P.inv_smooth), T, lin->d_in, lin->a_bits, codes, s_x, s));
+    return QE_OK;
+}
+
+int qe_linear_prologue(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, int8_t* codes, float* s_x,
+                       uint16_t* u, uint16_t* v, int32_t* expert, void* ws, size_t ws_bytes, void* stream) {
+    int st = validate_forward_common(lin, T, x_dtype, x, ws, ws_bytes);
+    if (st) return st;
+    if (T == 0) return QE_OK;
+    QE_CHECK(x != nullptr, QE_ERR_INVALID_ARG);
+    QE_CHECK(lin->a_bits == 16 ? (codes == nullptr && s_x == nullptr) : (codes && s_x), QE_ERR_INVALID_ARG);
+    QE_CHECK((lin->r_shared > 0) == (u != nullptr), QE_ERR_INVALID_ARG);
+    QE_CHECK((lin->n_routed > 0) == (v != nullptr) && (lin->n_routed > 0) == (expert != nullptr), QE_ERR_INVALID_ARG);
+    if (codes) QE_CHECK(aligned16(codes), QE_ERR_ALIGNMENT);
+    return run_prologue(lin, x, x_dtype, T, codes, s_x, u, v, expert, ws, S(stream));
+}
+
 int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* y, int32_t* expert_out,
                       void* ws, size_t ws_bytes, void* stream) {
     int st = validate_forward_common(lin, T, x_dtype, x, ws, ws_bytes);
@@ -453,22 +470,15 @@ int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int3
     const PrepLayout P = prep_layout(lin);
     const WsLayout W = ws_layout(lin, T);
     hipStream_t s = S(stream);
-    int32_t* expert = expert_out ? expert_out : at<int32_t>(ws, W.expert);
-    uint16_t* u = P.rs_pad > 0 ? at<uint16_t>(ws, W.u) : nullptr;
-    uint16_t* v = lin->n_routed > 0 ? at<uint16_t>(ws, W.v) : nullptr;
     const bool route = lin->n_routed > 0;
-    st = run_xpass(lin, x, x_dtype, T, u != nullptr, route, route, nullptr, nullptr, route ? expert : nullptr, u, v,
-                   ws, s);
+    int32_t* expert = route ? (expert_out ? expert_out : at<int32_t>(ws, W.expert)) : nullptr;
+    uint16_t* u = P.rs_pad > 0 ? at<uint16_t>(ws, W.u) : nullptr;
+    uint16_t* v = route ? at<uint16_t>(ws, W.v) : nullptr;
+    int8_t* codes = lin->a_bits != 16 ? at<int8_t>(ws, W.codes) : nullptr;
+    float* s_x = lin->a_bits != 16 ? at<float>(ws, W.s_x) : nullptr;
+    st = run_prologue(lin, x, x_dtype, T, codes, s_x, u, v, expert, ws, s);
     if (st) return st;
-    int8_t* codes = nullptr;
-    float* s_x = nullptr;
-    if (lin->a_bits != 16) {
-        codes = at<int8_t>(ws, W.codes);
-        s_x = at<float>(ws, W.s_x);
-        QE_TRY_HIP(launch_quant_act(x, x_dtype, at<const float>(lin->prep, P.smooth),
-                                    at<const float>(lin->prep, P.inv_smooth), T, lin->d_in, lin->a_bits, codes, s_x, s));
-    }
-    return run_gemm(lin, codes, s_x, x, x_dtype, T, u, v, route ? expert : nullptr, y, nullptr, ws, s);
+    return run_gemm(lin, codes, s_x, x, x_dtype, T, u, v, expert, y, nullptr, ws, s);
 }
 
 // ------------------------------------------------------------------ a8

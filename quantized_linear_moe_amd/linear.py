@@ -40,10 +40,11 @@ class QELinear:
                     packed: Optional[np.ndarray] = None, w_scale: Optional[np.ndarray] = None) -> "QELinear":
         """params: W_f (float32 [d_out, d_in]) or (packed, w_scale); s; A_s, B_s, A_r, B_r, R (bf16)."""
         A_s, B_s, A_r, B_r, R = (params.get(k) for k in ("A_s", "B_s", "A_r", "B_r", "R"))
+        s = params.get("s") if a_bits != 16 else None  # weight-only layers carry no smoothing
         if packed is None:
             W_f = params["W_f"]
             d_out, d_in = W_f.shape
-            packed, w_scale = L.qe_pack_weights(W_f, params.get("s"), w_bits)
+            packed, w_scale = L.qe_pack_weights(W_f, s, w_bits)
         else:
             d_out, d_in = params["d_out"], params["d_in"]
         r_s = 0 if A_s is None else A_s.shape[1]
@@ -51,7 +52,6 @@ class QELinear:
         r_r = 0 if A_r is None else A_r.shape[2]
         self = cls(d_in, d_out, w_bits, a_bits, r_s, n_r, r_r, device)
         dev = self.device
-        s = params.get("s") if a_bits != 16 else None
         bufs = dict(
             w_packed=_dev(packed, dev), w_scale=_dev(w_scale, dev), smooth=_dev(s, dev, torch.float32),
             A_s=_dev(A_s, dev, torch.bfloat16) if r_s else None, B_s=_dev(B_s, dev, torch.bfloat16) if r_s else None,

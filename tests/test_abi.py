@@ -17,8 +17,11 @@ HEADER = os.path.join(ROOT, "include", "qe.h")
 def L():
     lib_path = os.path.join(ROOT, "quantized_linear_moe_amd", "libqe.so")
     if not os.path.exists(lib_path):  # a fresh checkout: build the HIP library (cross-compiles, no GPU needed)
-        from quantized_linear_moe_amd import build as b
-        b.build()
+        import importlib.util
+        spec = importlib.util.spec_from_file_location("qe_build", os.path.join(ROOT, "quantized_linear_moe_amd", "build.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
     from quantized_linear_moe_amd import _libqe
     return _libqe
 
