@@ -66,7 +66,8 @@ typedef enum { QE_F32 = 0, QE_BF16 = 1 } qe_dtype;
  *   n_routed     number of routed experts N_r, 0..16 (0 = no router, no routed expert)
  *   r_routed     routed-expert rank, 1..64 when n_routed > 0, else 0
  *   prep         device buffer written by qe_prepare() (qe_prepared_bytes() bytes)
- * Kernel-path constraints: d_out % 16 == 0 and d_in % 128 == 0 (else QE_ERR_UNSUPPORTED).
+ * Kernel-path constraints: d_out % 16 == 0 and d_in % 128 == 0, and d_in <= 32768 when
+ * a_bits is 6 or 8 (else QE_ERR_UNSUPPORTED).
  */
 typedef struct qe_linear {
     int32_t d_in;
@@ -138,7 +139,8 @@ size_t qe_workspace_bytes(const qe_linear* lin, int32_t T);
  *   x'[t][j] = x[t][j] / s[j];  s_x[t] = max_j |x'[t][j]| / qmax  (qmax 31 or 127)
  *   codes[t][j] = clamp(rint(x'[t][j] / s_x[t]), -qmax, qmax); all-zero token -> 0
  * x: device [T][d_in] (x_dtype); smooth: device [d_in] or NULL (identity);
- * codes: device int8 [T][d_in]; s_x: device float32 [T].  a_bits 6 or 8.
+ * codes: device int8 [T][d_in]; s_x: device float32 [T].  a_bits 6 or 8; d_in % 8 == 0 and
+ * d_in <= 32768 (else QE_ERR_UNSUPPORTED).
  */
 int qe_quant_act(const void* x, int32_t x_dtype, const float* smooth, int32_t T, int32_t d_in,
                  int32_t a_bits, int8_t* codes, float* s_x, void* stream);

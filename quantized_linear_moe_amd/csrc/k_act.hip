@@ -70,35 +70,68 @@ __device__ inline float wave_max(float v) {
 }
 
 // ---------------------------------------------------------------- a1: quant
-// One workgroup per token.  Pass 1: x' = x / s and the token's max |x'|.
-// Pass 2: codes = clamp(rint(x' / s_x), +-qmax) with s_x = amax / qmax.
-// All float32, IEEE division semantics, round half to even.
-template <int kThreads>
-__global__ __launch_bounds__(kThreads) void quant_act_kernel(const void* __restrict__ x, int x_dtype,
-                                                             const float* __restrict__ smooth,
-                                                             const float* __restrict__ inv_smooth, int T, int d_in,
-                                                             int qmax, int8_t* __restrict__ codes,
-                                                             float* __restrict__ s_x) {
+// One workgroup per token; each thread owns up to QA_IT groups of 8 consecutive
+// channels, whose x' = x / s stays in registers between the two passes.
+// Pass 1: x' and the token's max |x'|.  Pass 2: codes = clamp(rint(x' / s_x), +-qmax)
+// with s_x = amax / qmax.  All float32 with IEEE division semantics (Markstein's
+// correction, with the exact division as a wave-uniform fallback outside its
+// verified domain) and round half to even.
+constexpr int QA_IT = 4;
+
+template <bool kHasInv>
+__device__ inline void smooth8(const float* __restrict__ smooth, const float* __restrict__ inv_smooth, int j,
+                               float v[8]) {
+    const v4f s0 = *reinterpret_cast<const v4f*>(smooth + j), s1 = *reinterpret_cast<const v4f*>(smooth + j + 4);
+    float s[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+    float is[8];
+    if (kHasInv) {
+        const v4f i0 = *reinterpret_cast<const v4f*>(inv_smooth + j), i1 = *reinterpret_cast<const v4f*>(inv_smooth + j + 4);
+        is[0] = i0[0]; is[1] = i0[1]; is[2] = i0[2]; is[3] = i0[3];
+        is[4] = i1[0]; is[5] = i1[1]; is[6] = i1[2]; is[7] = i1[3];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) is[i] = 1.0f / s[i];
+    }
+    bool ok = true;
+    float r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        r[i] = div_markstein(v[i], s[i], is[i]);
+        ok = ok && in_markstein_range(v[i]);
+    }
+    if (__builtin_expect(__any(!ok), 0)) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (!in_markstein_range(v[i])) r[i] = v[i] / s[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = r[i];
+}
+
+template <bool kHasInv>
+__global__ __launch_bounds__(1024) void quant_act_kernel(const void* __restrict__ x, int x_dtype,
+                                                         const float* __restrict__ smooth,
+                                                         const float* __restrict__ inv_smooth, int T, int d_in,
+                                                         int qmax, int8_t* __restrict__ codes,
+                                                         float* __restrict__ s_x) {
     const int t = blockIdx.x;
     if (t >= T) return;
     const size_t row = (size_t)t * d_in;
-    __shared__ float red[kThreads / kWave];
+    const int nthr = blockDim.x;
+    __shared__ float red[1024 / kWave];
     __shared__ float s_bcast[2];
 
+    float xv[QA_IT][8];
     float amax = 0.0f;
-    for (int j = threadIdx.x * 8; j < d_in; j += kThreads * 8) {
-        float v[8];
-        load8(x, x_dtype, row + j, v);
-        if (smooth) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float s = smooth[j + i];
-                float is = inv_smooth ? inv_smooth[j + i] : 1.0f / s;
-                v[i] = smooth_div(v[i], s, is);
-            }
+    for (int it = 0; it < QA_IT; ++it) {
+        const int j = (it * nthr + threadIdx.x) * 8;
+        if (j < d_in) {
+            load8(x, x_dtype, row + j, xv[it]);
+            if (smooth) smooth8<kHasInv>(smooth, inv_smooth, j, xv[it]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, __builtin_fabsf(xv[it][i]));
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, __builtin_fabsf(v[i]));
     }
     amax = wave_max(amax);
     const int wid = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -106,8 +139,8 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const void* __restr
     __syncthreads();
     if (threadIdx.x == 0) {
         float m = red[0];
-        for (int i = 1; i < kThreads / kWave; ++i) m = fmaxf(m, red[i]);
-        float sx = m / (float)qmax;
+        for (int i = 1; i < nthr / kWave; ++i) m = fmaxf(m, red[i]);
+        const float sx = m / (float)qmax;
         s_bcast[0] = sx;
         s_bcast[1] = (sx != 0.0f) ? 1.0f / sx : 0.0f;
         s_x[t] = sx;
@@ -117,27 +150,22 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(const void* __restr
     const bool fast = (sx >= 0x1p-90f && sx <= 0x1p90f);
     const float fq = (float)qmax;
 
-    for (int j = threadIdx.x * 8; j < d_in; j += kThreads * 8) {
-        float v[8];
-        load8(x, x_dtype, row + j, v);
-        if (smooth) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float s = smooth[j + i];
-                float is = inv_smooth ? inv_smooth[j + i] : 1.0f / s;
-                v[i] = smooth_div(v[i], s, is);
-            }
+    for (int it = 0; it < QA_IT; ++it) {
+        const int j = (it * nthr + threadIdx.x) * 8;
+        if (j >= d_in) continue;
+        float r[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) r[i] = div_markstein(xv[it][i], sx, inv_sx);
+        if (!fast) {  // uniform over the workgroup
+#pragma unroll
+            for (int i = 0; i < 8; ++i) r[i] = xv[it][i] / sx;
         }
         uint32_t packed[2] = {0u, 0u};
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            float q = 0.0f;
-            if (sx != 0.0f) {
-                float r = fast ? div_markstein(v[i], sx, inv_sx) : v[i] / sx;
-                q = fminf(fmaxf(__builtin_rintf(r), -fq), fq);
-            }
-            uint32_t b = (uint32_t)(int32_t)q & 0xFFu;
-            packed[i >> 2] |= b << (8 * (i & 3));
+            const float q = sx != 0.0f ? fminf(fmaxf(__builtin_rintf(r[i]), -fq), fq) : 0.0f;
+            packed[i >> 2] |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * (i & 3));
         }
         *reinterpret_cast<v2u*>(codes + row + j) = v2u{packed[0], packed[1]};
     }
@@ -147,89 +175,129 @@ hipError_t launch_quant_act(const void* x, int x_dtype, const float* smooth, con
                             int d_in, int a_bits, int8_t* codes, float* s_x, hipStream_t st) {
     if (T <= 0) return hipSuccess;
     const int qmax = (1 << (a_bits - 1)) - 1;
-    hipLaunchKernelGGL(quant_act_kernel<256>, dim3(T), dim3(256), 0, st, x, x_dtype, smooth, inv_smooth, T, d_in,
-                       qmax, codes, s_x);
+    // enough threads that every channel group fits in QA_IT register slots
+    const int groups = (d_in + 7) / 8;
+    const int threads = ((groups + QA_IT - 1) / QA_IT + kWave - 1) / kWave * kWave;
+    if (threads > 1024) return hipErrorInvalidValue;  // d_in > 32768: rejected by the caller
+    if (inv_smooth || !smooth) {
+        hipLaunchKernelGGL(quant_act_kernel<true>, dim3(T), dim3(threads), 0, st, x, x_dtype, smooth, inv_smooth, T,
+                           d_in, qmax, codes, s_x);
+    } else {
+        hipLaunchKernelGGL(quant_act_kernel<false>, dim3(T), dim3(threads), 0, st, x, x_dtype, smooth, inv_smooth, T,
+                           d_in, qmax, codes, s_x);
+    }
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------- x-projection
 // P[t][c] = sum_k bf16(x)[t][k] * Mt[col0 + c][k]  for c < ncols, as split-K
 // partials part[ks][t][c] (float32).  bf16 MFMA 16x16x32, fp32 accumulation.
-// Workgroup: 4 waves, 64 tokens x 320 columns (each wave 64 tokens x 80 columns);
-// the x tile is staged through LDS once per workgroup, Mt rows (K-contiguous)
-// are read straight into registers.
-constexpr int XP_TOK = 64;       // tokens per workgroup
+// Workgroup: 4 waves, 128 tokens x 320 columns (each wave all 128 tokens x 80
+// columns).  The x tile (shared by the waves) is double-buffered through LDS in
+// 128-wide K chunks; each wave streams its Mt rows (K-contiguous, 16 bytes per
+// lane) straight into registers, one K step ahead of the MFMAs.
+constexpr int XP_TOK = 128;      // tokens per workgroup
+constexpr int XP_MB = XP_TOK / 16;
 constexpr int XP_NBW = 5;        // 16-column blocks per wave
 constexpr int XP_COLS = 4 * XP_NBW * 16;
-constexpr int XP_KC = 256;       // K chunk staged in LDS
-constexpr int XP_LDS_LD = XP_KC * 2 + 16;  // bytes per LDS row (padded)
+constexpr int XP_KC = 64;        // K chunk staged in LDS
+constexpr int XP_LDS_LD = XP_KC * 2 + 16;  // bytes per LDS row (padded against bank conflicts)
 
-__global__ __launch_bounds__(256) void xproj_kernel(const void* __restrict__ x, int x_dtype, int T, int d_in,
-                                                    const uint16_t* __restrict__ mt, int col0, int ncols,
-                                                    int ncols_pad, int ksplit, float* __restrict__ part) {
-    __shared__ __attribute__((aligned(16))) uint8_t xs[XP_TOK * XP_LDS_LD];
+__device__ inline v4u load_x8_bf16(const void* x, int x_dtype, size_t idx) {
+    if (x_dtype == QE_BF16) return *reinterpret_cast<const v4u*>(reinterpret_cast<const uint16_t*>(x) + idx);
+    const v4f* p = reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(x) + idx);
+    const v4f a = p[0], b = p[1];
+    v4u val;
+    val[0] = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
+    val[1] = f32_to_bf16_bits(a[2]) | (f32_to_bf16_bits(a[3]) << 16);
+    val[2] = f32_to_bf16_bits(b[0]) | (f32_to_bf16_bits(b[1]) << 16);
+    val[3] = f32_to_bf16_bits(b[2]) | (f32_to_bf16_bits(b[3]) << 16);
+    return val;
+}
+
+__global__ __launch_bounds__(256, 2) void xproj_kernel(const void* __restrict__ x, int x_dtype, int T, int d_in,
+                                                       const uint16_t* __restrict__ mt, int col0, int ncols,
+                                                       int ncols_pad, int ksplit, float* __restrict__ part) {
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][XP_TOK * XP_LDS_LD];
     const int tile = blockIdx.x, ks = blockIdx.y, cgrp = blockIdx.z;
     const int tok0 = tile * XP_TOK;
     const int tid = threadIdx.x, wid = tid / kWave, lane = tid % kWave;
+    const int lr = lane & 15, lg = lane >> 4;
     const int kb32 = d_in / 32;
     const int kbeg = (int)((long)ks * kb32 / ksplit) * 32;
     const int kend = (int)((long)(ks + 1) * kb32 / ksplit) * 32;
     const int cbase = cgrp * XP_COLS + wid * XP_NBW * 16;  // first column of this wave (relative to col0)
 
-    v4f acc[4][XP_NBW];
+    // staging map: 4 x 16-byte loads per thread per chunk (128 rows x 8 chunks of 8 bf16)
+    constexpr int XP_SL = XP_TOK * XP_KC / 8 / 256;
+    auto stage = [&](int k0, v4u (&reg)[XP_SL]) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+        for (int p = 0; p < XP_SL; ++p) {
+            const int i = p * 256 + tid, r = i / (XP_KC / 8), c8 = i % (XP_KC / 8);
+            const int t = tok0 + r, k = k0 + c8 * 8;
+            reg[p] = (t < T && k < kend) ? load_x8_bf16(x, x_dtype, (size_t)t * d_in + k) : v4u{0, 0, 0, 0};
+        }
+    };
+    auto commit = [&](int buf, const v4u (&reg)[XP_SL]) {
+#pragma unroll
+        for (int p = 0; p < XP_SL; ++p) {
+            const int i = p * 256 + tid, r = i / (XP_KC / 8), c8 = i % (XP_KC / 8);
+            *reinterpret_cast<v4u*>(&xs[buf][r * XP_LDS_LD + c8 * 16]) = reg[p];
+        }
+    };
+    const uint16_t* brow[XP_NBW];
+    bool bok[XP_NBW];
+#pragma unroll
+    for (int n = 0; n < XP_NBW; ++n) {
+        const int c = cbase + n * 16 + lr;
+        bok[n] = c < ncols;
+        brow[n] = mt + (size_t)(col0 + (bok[n] ? c : 0)) * d_in + lg * 8;
+    }
+    auto load_b = [&](int k, v8bf (&b)[XP_NBW]) {
+#pragma unroll
+        for (int n = 0; n < XP_NBW; ++n)
+            b[n] = (bok[n] && k < kend) ? *reinterpret_cast<const v8bf*>(brow[n] + k) : v8bf{};
+    };
+
+    v4f acc[XP_MB][XP_NBW];
+#pragma unroll
+    for (int m = 0; m < XP_MB; ++m)
 #pragma unroll
         for (int n = 0; n < XP_NBW; ++n) acc[m][n] = v4f{0, 0, 0, 0};
 
-    const int lr = lane & 15, lg = lane >> 4;
+    v4u xr[XP_SL];
+    v8bf bcur[XP_NBW], bnext[XP_NBW];
+    stage(kbeg, xr);
+    commit(0, xr);
+    load_b(kbeg, bcur);
+    __syncthreads();
+    int buf = 0;
     for (int k0 = kbeg; k0 < kend; k0 += XP_KC) {
-        const int kc = min(XP_KC, kend - k0);
-        __syncthreads();
-        // stage x[tok0 .. +64][k0 .. +kc] as bf16 (zeros beyond T / kc)
-        for (int i = tid; i < XP_TOK * (XP_KC / 8); i += 256) {
-            const int r = i / (XP_KC / 8), c8 = i % (XP_KC / 8);
-            const int t = tok0 + r;
-            v4u val = v4u{0, 0, 0, 0};
-            if (t < T && c8 * 8 < kc) {
-                const size_t idx = (size_t)t * d_in + k0 + c8 * 8;
-                if (x_dtype == QE_BF16) {
-                    val = *reinterpret_cast<const v4u*>(reinterpret_cast<const uint16_t*>(x) + idx);
-                } else {
-                    const v4f* p = reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(x) + idx);
-                    v4f a = p[0], b = p[1];
-                    val[0] = f32_to_bf16_bits(a[0]) | (f32_to_bf16_bits(a[1]) << 16);
-                    val[1] = f32_to_bf16_bits(a[2]) | (f32_to_bf16_bits(a[3]) << 16);
-                    val[2] = f32_to_bf16_bits(b[0]) | (f32_to_bf16_bits(b[1]) << 16);
-                    val[3] = f32_to_bf16_bits(b[2]) | (f32_to_bf16_bits(b[3]) << 16);
-                }
+        const bool more = k0 + XP_KC < kend;
+        if (more) stage(k0 + XP_KC, xr);
+#pragma unroll
+        for (int s = 0; s < XP_KC / 32; ++s) {
+            const int k = k0 + s * 32;
+            if (k >= kend) break;
+            load_b(k + 32, bnext);
+#pragma unroll
+            for (int m = 0; m < XP_MB; ++m) {
+                const v8bf a = *reinterpret_cast<const v8bf*>(&xs[buf][(m * 16 + lr) * XP_LDS_LD + (s * 32 + lg * 8) * 2]);
+#pragma unroll
+                for (int n = 0; n < XP_NBW; ++n)
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bcur[n], acc[m][n], 0, 0, 0);
             }
-            *reinterpret_cast<v4u*>(xs + r * XP_LDS_LD + c8 * 16) = val;
+#pragma unroll
+            for (int n = 0; n < XP_NBW; ++n) bcur[n] = bnext[n];
         }
+        if (more) commit(buf ^ 1, xr);
         __syncthreads();
-        for (int s = 0; s < kc / 32; ++s) {
-            v8bf a[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-                a[m] = *reinterpret_cast<const v8bf*>(xs + (m * 16 + lr) * XP_LDS_LD + (s * 32 + lg * 8) * 2);
-#pragma unroll
-            for (int n = 0; n < XP_NBW; ++n) {
-                const int c = cbase + n * 16 + lr;
-                v8bf b;
-                if (c < ncols) {
-                    b = *reinterpret_cast<const v8bf*>(mt + (size_t)(col0 + c) * d_in + k0 + s * 32 + lg * 8);
-                } else {
-                    b = v8bf{};
-                }
-#pragma unroll
-                for (int m = 0; m < 4; ++m) acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[m], b, acc[m][n], 0, 0, 0);
-            }
-        }
+        buf ^= 1;
     }
     // store partials: lane holds rows 4*lg + r, column lr of each 16x16 block
     float* out = part + (size_t)ks * T * ncols_pad;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < XP_MB; ++m)
 #pragma unroll
         for (int n = 0; n < XP_NBW; ++n) {
             const int c = cbase + n * 16 + lr;

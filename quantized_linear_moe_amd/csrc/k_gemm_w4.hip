@@ -116,14 +116,18 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
             v4i bop[G_NBW];
 #pragma unroll
             for (int j = 0; j < G_NBW; ++j) bop[j] = unpack_w4x16(b_cur[j][2 * s], b_cur[j][2 * s + 1]);
+            v4i a[G_MB];  // all A fragments of this K step in flight at once
 #pragma unroll
-            for (int m = 0; m < G_MB; ++m) {
-                const int row = m * 16 + lr;
-                const v4i a = *reinterpret_cast<const v4i*>(&As[cur][lds_a_offset(row, s * 4 + lg)]);
+            for (int m = 0; m < G_MB; ++m)
+                a[m] = *reinterpret_cast<const v4i*>(&As[cur][lds_a_offset(m * 16 + lr, s * 4 + lg)]);
+#pragma unroll
+            for (int m = 0; m < G_MB; ++m)
 #pragma unroll
                 for (int j = 0; j < G_NBW; ++j)
-                    acc[m][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bop[j], acc[m][j], 0, 0, 0);
-            }
+                    acc[m][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[m], bop[j], acc[m][j], 0, 0, 0);
+            // keep the eight LDS reads ahead of the 32 MFMAs that consume them
+            __builtin_amdgcn_sched_group_barrier(0x100, G_MB, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, G_MB * G_NBW, 0);
         }
         if (more) {
 #pragma unroll

@@ -57,6 +57,7 @@ int validate_linear(const qe_linear* lin) {
     QE_CHECK(lin->d_in % 128 == 0, QE_ERR_UNSUPPORTED);
     // 16 * |acc| must stay below 2^31 on the int8 path: 16 * 127 * 7 * d_in
     QE_CHECK(lin->a_bits == 16 || (int64_t)lin->d_in * 16 * 127 * 7 < (int64_t)INT32_MAX, QE_ERR_UNSUPPORTED);
+    QE_CHECK(lin->a_bits == 16 || lin->d_in <= 32768, QE_ERR_UNSUPPORTED);  // one token row per workgroup
     return QE_OK;
 }
 
@@ -82,9 +83,10 @@ inline P* at(const void* base, size_t off) {
     return reinterpret_cast<P*>(reinterpret_cast<uintptr_t>(base) + off);
 }
 
+// K splits of the x-projection: about two workgroups per CU, each with at least 512 K
 int xproj_ksplit(int T, int d_in, int ncols_pad) {
     if (T <= 0 || ncols_pad <= 0) return 1;
-    const int tiles = (T + 63) / 64 * ((ncols_pad + 319) / 320);
+    const int tiles = (T + 127) / 128 * ((ncols_pad + 319) / 320);
     int ks = (512 + tiles - 1) / tiles;
     ks = std::min(ks, std::max(1, d_in / 512));
     return std::max(ks, 1);
@@ -303,7 +305,7 @@ int qe_quant_act(const void* x, int32_t x_dtype, const float* smooth, int32_t T,
     QE_CHECK(T >= 0 && d_in > 0, QE_ERR_INVALID_ARG);
     QE_CHECK(a_bits == 6 || a_bits == 8, QE_ERR_INVALID_ARG);
     QE_CHECK(x_dtype == QE_F32 || x_dtype == QE_BF16, QE_ERR_INVALID_ARG);
-    QE_CHECK(d_in % 8 == 0, QE_ERR_UNSUPPORTED);
+    QE_CHECK(d_in % 8 == 0 && d_in <= 32768, QE_ERR_UNSUPPORTED);
     if (T == 0) return QE_OK;
     QE_CHECK(x && codes && s_x, QE_ERR_INVALID_ARG);
     for (const void* p : {x, (const void*)codes, (const void*)s_x}) QE_CHECK(aligned16(p), QE_ERR_ALIGNMENT);
