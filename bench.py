@@ -113,6 +113,7 @@ def main():
             u=torch.empty(T, libqe.rank_pad(cfg.r_shared), dtype=torch.bfloat16, device=dev),
             v=torch.empty(T, libqe.rank_pad(cfg.r_routed), dtype=torch.bfloat16, device=dev),
             e=torch.empty(T, dtype=torch.int32, device=dev),
+            perm=torch.empty(T, dtype=torch.int32, device=dev),
             y=torch.empty(T, spec.d_out, dtype=torch.float32, device=dev)))
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f}s")
@@ -120,10 +121,12 @@ def main():
     def step(ev=None):
         for i, (spec, layer) in enumerate(layers):
             b = bufs[i]
-            libqe.qe_linear_prologue(layer.lin, xs[spec.stream], b["codes"], b["s_x"], b["u"], b["v"], b["e"], ws)
+            libqe.qe_linear_prologue(layer.lin, xs[spec.stream], b["codes"], b["s_x"], b["u"], b["v"], b["e"], ws,
+                                     perm=b["perm"])
             if ev is not None:
                 ev[i][0].record()
-            libqe.qe_wq_gemm(layer.lin, b["codes"], b["s_x"], None, T, b["u"], b["v"], b["e"], b["y"], None, ws)
+            libqe.qe_wq_gemm(layer.lin, b["codes"], b["s_x"], None, T, b["u"], b["v"], b["e"], b["y"], None, ws,
+                             perm=b["perm"])
             if ev is not None:
                 ev[i][1].record()
 

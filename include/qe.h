@@ -179,13 +179,16 @@ int qe_adapter_inputs(const qe_linear* lin, const void* x, int32_t x_dtype, int3
  *               y[t][i] = acc * s_x[t] * w_scale[i] + u[t].B_s[:,i] + v[t].B_{expert[t]}[:,i]
  *   a_bits 16:  y[t][i] = w_scale[i] * sum_j bf16(x)[t][j] * q_w[i][j] + (same adapter terms)
  * codes/s_x: from qe_quant_act (a_bits 6/8; NULL for 16); x: device [T][d_in] (a_bits 16 only,
- * else ignored); u, v, expert as produced by qe_adapter_inputs / qe_route (each NULL => that
- * term is skipped); y: device float32 [T][d_out], overwritten;
- * acc_debug: device int32 [T][d_out] or NULL (a_bits 6/8 only).
+ * else ignored); u, v, expert as produced by qe_adapter_inputs / qe_route (u NULL => no shared
+ * term; v and expert both NULL => no routed term); perm: device int32 [T] or NULL, a
+ * permutation of the tokens (e.g. qe_route's, grouped by expert) in which the kernel visits
+ * them -- it changes only the schedule, not the result; ignored for a_bits 16.
+ * y: device float32 [T][d_out], overwritten; acc_debug: device int32 [T][d_out] or NULL
+ * (a_bits 6/8 only).
  */
 int qe_wq_gemm(const qe_linear* lin, const int8_t* codes, const float* s_x, const void* x,
                int32_t x_dtype, int32_t T, const uint16_t* u, const uint16_t* v,
-               const int32_t* expert, float* y, int32_t* acc_debug,
+               const int32_t* expert, const int32_t* perm, float* y, int32_t* acc_debug,
                void* ws, size_t ws_bytes, void* stream);
 
 /* (a6, unfused form) Routed experts as a grouped low-rank product over the
@@ -202,10 +205,11 @@ int qe_routed_lora(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t
  * quantization (a1).  Equivalent to qe_route + qe_adapter_inputs + qe_quant_act, with one
  * read of x for all projections.  Outputs (device, caller-owned): codes int8 [T][d_in] and
  * s_x float32 [T] (a_bits 6/8; both NULL for a_bits 16), u and v as for
- * qe_adapter_inputs (padded rows), expert int32 [T].  Feed them to qe_wq_gemm.
+ * qe_adapter_inputs (padded rows), expert int32 [T], and perm int32 [T] or NULL (tokens
+ * sorted by (expert, token), as qe_route's).  Feed them to qe_wq_gemm.
  */
 int qe_linear_prologue(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, int8_t* codes,
-                       float* s_x, uint16_t* u, uint16_t* v, int32_t* expert,
+                       float* s_x, uint16_t* u, uint16_t* v, int32_t* expert, int32_t* perm,
                        void* ws, size_t ws_bytes, void* stream);
 
 /* The whole QE linear: qe_linear_prologue followed by qe_wq_gemm (a1 + a5 + a4 + a6 + a3,

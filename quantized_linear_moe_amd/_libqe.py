@@ -62,9 +62,9 @@ def _load():
         "qe_quant_act": (ctypes.c_int, [P, I, P, I, I, I, P, P, P]),
         "qe_route": (ctypes.c_int, [LP, P, I, I, P, P, P, P, P, P, Z, P]),
         "qe_adapter_inputs": (ctypes.c_int, [LP, P, I, I, P, P, P, P, Z, P]),
-        "qe_wq_gemm": (ctypes.c_int, [LP, P, P, P, I, I, P, P, P, P, P, P, Z, P]),
+        "qe_wq_gemm": (ctypes.c_int, [LP, P, P, P, I, I, P, P, P, P, P, P, P, Z, P]),
         "qe_routed_lora": (ctypes.c_int, [LP, P, I, I, P, P, P, P, P, Z, P]),
-        "qe_linear_prologue": (ctypes.c_int, [LP, P, I, I, P, P, P, P, P, P, Z, P]),
+        "qe_linear_prologue": (ctypes.c_int, [LP, P, I, I, P, P, P, P, P, P, P, Z, P]),
         "qe_linear_forward": (ctypes.c_int, [LP, P, I, I, P, P, P, Z, P]),
         "qe_colmean_abs": (ctypes.c_int, [P, I, I, I, P, P]),
         "qe_channel_topk": (ctypes.c_int, [P, I, P, I, I, I, P, P, P]),
@@ -175,11 +175,11 @@ def qe_adapter_inputs(lin, x, expert, u, v, ws, stream=None):
            "qe_adapter_inputs")
 
 
-def qe_wq_gemm(lin, codes, s_x, x, T, u, v, expert, y, acc_debug, ws, stream=None):
+def qe_wq_gemm(lin, codes, s_x, x, T, u, v, expert, y, acc_debug, ws, stream=None, perm=None):
     xd = _dtype_code(x) if x is not None else QE_BF16
     _check(_lib.qe_wq_gemm(ctypes.byref(lin), _ptr(codes), _ptr(s_x), _ptr(x), xd, T, _ptr(u), _ptr(v), _ptr(expert),
-                           _ptr(y), _ptr(acc_debug), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
-           "qe_wq_gemm")
+                           _ptr(perm), _ptr(y), _ptr(acc_debug), _ptr(ws), ws.numel() * ws.element_size(),
+                           _stream(stream)), "qe_wq_gemm")
 
 
 def qe_routed_lora(lin, x, expert, offsets, perm, y, ws, stream=None):
@@ -188,9 +188,9 @@ def qe_routed_lora(lin, x, expert, offsets, perm, y, ws, stream=None):
            "qe_routed_lora")
 
 
-def qe_linear_prologue(lin, x, codes, s_x, u, v, expert, ws, stream=None):
+def qe_linear_prologue(lin, x, codes, s_x, u, v, expert, ws, stream=None, perm=None):
     _check(_lib.qe_linear_prologue(ctypes.byref(lin), _ptr(x), _dtype_code(x), x.shape[0], _ptr(codes), _ptr(s_x),
-                                   _ptr(u), _ptr(v), _ptr(expert), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _ptr(u), _ptr(v), _ptr(expert), _ptr(perm), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)), "qe_linear_prologue")
 
 

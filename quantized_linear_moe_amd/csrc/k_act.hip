@@ -320,51 +320,68 @@ hipError_t launch_xproj(const void* x, int x_dtype, int T, int d_in, const uint1
 }
 
 // ------------------------------------------------- x-projection reduction + router
-// One wave per token: reduce the split-K partials in a fixed order, take the
-// router argmin (lowest index on ties), and write the bf16 adapter inputs.
-__global__ __launch_bounds__(256) void xproj_finish_kernel(const float* __restrict__ part, int ksplit, int T,
-                                                           int ncols_pad, int se_col, int r_s, int rs_pad, int re_col,
-                                                           int n_r, int r_r, int rr_pad, int router_col,
-                                                           const int32_t* __restrict__ expert_in,
-                                                           float* __restrict__ scores, int32_t* __restrict__ expert_out,
-                                                           uint16_t* __restrict__ u, uint16_t* __restrict__ v) {
-    const int t = blockIdx.x * 4 + threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
+// One workgroup per token: each thread reduces columns of the split-K partials in a
+// fixed order, the router takes the argmin over its columns (lowest index on ties),
+// and the bf16 adapter inputs of the shared and of the selected routed expert are written.
+__global__ __launch_bounds__(1024) void xproj_finish_kernel(const float* __restrict__ part, int ksplit, int T,
+                                                            int ncols_pad, int se_col, int r_s, int rs_pad, int re_col,
+                                                            int n_r, int r_r, int rr_pad, int router_col,
+                                                            const int32_t* __restrict__ expert_in,
+                                                            float* __restrict__ scores, int32_t* __restrict__ expert_out,
+                                                            uint16_t* __restrict__ u, uint16_t* __restrict__ v) {
+    extern __shared__ float sums[];  // [4][ncols_pad]: quarter sums, then the total in row 0
+    __shared__ int s_e;
+    const int t = blockIdx.x;
     if (t >= T) return;
-    auto col_sum = [&](int c) {
+    const int q = threadIdx.x >> 8, c0 = threadIdx.x & 255;
+    const int k0 = ksplit * q / 4, k1 = ksplit * (q + 1) / 4;
+    const size_t stride = (size_t)T * ncols_pad;
+    for (int c = c0; c < ncols_pad; c += 256) {
+        const float* p = part + (size_t)t * ncols_pad + c;
         float s = 0.0f;
-        for (int k = 0; k < ksplit; ++k) s += part[((size_t)k * T + t) * ncols_pad + c];
-        return s;
-    };
-    int e = 0;
-    if (router_col >= 0) {
-        float sc = lane < n_r ? col_sum(router_col + lane) : __builtin_inff();
-        if (scores && lane < n_r) scores[(size_t)t * n_r + lane] = sc;
-        // argmin with lowest index on ties
-        float best = sc;
-        int bi = lane;
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            float ob = __shfl_xor(best, off, 64);
-            int oi = __shfl_xor(bi, off, 64);
-            if (ob < best || (ob == best && oi < bi)) {
-                best = ob;
-                bi = oi;
-            }
+        int k = k0;
+        for (; k + 4 <= k1; k += 4) {  // independent loads, summed in order
+            const float a0 = p[(size_t)k * stride], a1 = p[(size_t)(k + 1) * stride];
+            const float a2 = p[(size_t)(k + 2) * stride], a3 = p[(size_t)(k + 3) * stride];
+            s += a0;
+            s += a1;
+            s += a2;
+            s += a3;
         }
-        e = bi;
-        if (lane == 0 && expert_out) expert_out[t] = e;
-    } else if (expert_in) {
-        e = min(max(expert_in[t], 0), max(n_r - 1, 0));
+        for (; k < k1; ++k) s += p[(size_t)k * stride];
+        sums[q * ncols_pad + c] = s;
     }
+    __syncthreads();
+    if (q == 0) {
+        for (int c = c0; c < ncols_pad; c += 256)
+            sums[c] = ((sums[c] + sums[ncols_pad + c]) + sums[2 * ncols_pad + c]) + sums[3 * ncols_pad + c];
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int e = 0;
+        if (router_col >= 0) {
+            float best = sums[router_col];
+            for (int j = 1; j < n_r; ++j)
+                if (sums[router_col + j] < best) {  // strict: the lowest index wins ties
+                    best = sums[router_col + j];
+                    e = j;
+                }
+            if (expert_out) expert_out[t] = e;
+        } else if (expert_in) {
+            e = min(max(expert_in[t], 0), max(n_r - 1, 0));
+        }
+        s_e = e;
+    }
+    if (scores && router_col >= 0 && threadIdx.x < n_r) scores[(size_t)t * n_r + threadIdx.x] = sums[router_col + threadIdx.x];
+    __syncthreads();
+    const int e = s_e;
     if (u && se_col >= 0) {
-        for (int c = lane; c < rs_pad; c += kWave)
-            u[(size_t)t * rs_pad + c] = c < r_s ? (uint16_t)f32_to_bf16_bits(col_sum(se_col + c)) : (uint16_t)0;
+        for (int c = threadIdx.x; c < rs_pad; c += 1024)
+            u[(size_t)t * rs_pad + c] = c < r_s ? (uint16_t)f32_to_bf16_bits(sums[se_col + c]) : (uint16_t)0;
     }
     if (v && re_col >= 0) {
-        for (int c = lane; c < rr_pad; c += kWave)
-            v[(size_t)t * rr_pad + c] =
-                c < r_r ? (uint16_t)f32_to_bf16_bits(col_sum(re_col + e * rr_pad + c)) : (uint16_t)0;
+        for (int c = threadIdx.x; c < rr_pad; c += 1024)
+            v[(size_t)t * rr_pad + c] = c < r_r ? (uint16_t)f32_to_bf16_bits(sums[re_col + e * rr_pad + c]) : (uint16_t)0;
     }
 }
 
@@ -375,9 +392,9 @@ hipError_t launch_xproj_finish(const float* part, int ksplit, int T, int ncols_p
     if (T <= 0) return hipSuccess;
     // columns are relative to the projected block that starts at col0
     auto rel = [&](int c) { return c < 0 ? -1 : c - col0; };
-    hipLaunchKernelGGL(xproj_finish_kernel, dim3((T + 3) / 4), dim3(256), 0, st, part, ksplit, T, ncols_pad,
-                       rel(se_col), r_s, rs_pad, rel(re_col), n_r, r_r, rr_pad, rel(router_col), expert_in, scores,
-                       expert_out, u, v);
+    hipLaunchKernelGGL(xproj_finish_kernel, dim3(T), dim3(1024), 4 * (size_t)ncols_pad * sizeof(float), st, part, ksplit, T,
+                       ncols_pad, rel(se_col), r_s, rs_pad, rel(re_col), n_r, r_r, rr_pad, rel(router_col), expert_in,
+                       scores, expert_out, u, v);
     return hipGetLastError();
 }
 

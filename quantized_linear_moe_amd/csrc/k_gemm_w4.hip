@@ -20,7 +20,11 @@
 //   * Activation codes (shared by the 4 waves) are staged in LDS, double
 //     buffered, with an XOR swizzle of the 16-byte chunks against bank conflicts.
 //   * Workgroup tile 128 tokens x 256 channels; wave tile 128 x 64
-//     (8 x 4 MFMA blocks, 128 accumulator registers).
+//     (8 x 4 MFMA blocks, 128 accumulator registers); 64-token tiles when the
+//     grid would otherwise leave CUs idle (narrow projections).
+//   * Tokens may be visited in an expert-sorted order (`perm`): code rows are
+//     gathered and output rows scattered, so a tile meets one or two routed
+//     experts instead of all of them.
 //   * Epilogue: int32 -> float, scale by s_x and s_w, then bf16 MFMA
 //     16x16x32 steps accumulate u.B_s and, for every routed expert present in
 //     the tile, (v masked to that expert's tokens).B_e on top of it.
@@ -29,11 +33,9 @@
 
 namespace qe {
 
-constexpr int G_BM = 128;
 constexpr int G_BN = 256;
 constexpr int G_BK = 128;
-constexpr int G_MB = G_BM / 16;  // M blocks per wave
-constexpr int G_NBW = 4;         // N blocks per wave
+constexpr int G_NBW = 4;  // N blocks per wave
 
 __device__ inline v4i unpack_w4x16(uint32_t p0, uint32_t p1) {
     // tiled byte b of p holds code b (low nibble) and code b+4 (high nibble)
@@ -47,30 +49,39 @@ __device__ inline v4i unpack_w4x16(uint32_t p0, uint32_t p1) {
 
 __device__ inline int lds_a_offset(int row, int chunk) { return row * G_BK + ((chunk ^ (row & 7)) << 4); }
 
+// MB: 16-row M blocks per workgroup (tile MB*16 tokens x 256 channels).  Tile rows are
+// positions in `perm` order when perm != NULL (tokens grouped by routed expert, so a
+// tile meets few experts in the epilogue), else token order.
+template <int MB>
 __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     const int8_t* __restrict__ codes, const float* __restrict__ s_x, const v4u* __restrict__ w_tiled,
     const float* __restrict__ w_scale, int T, int d_in, int d_out, const uint16_t* __restrict__ u,
     const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v, const int32_t* __restrict__ expert,
-    const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, float* __restrict__ y, int32_t* __restrict__ acc_debug,
-    int n_tm) {
-    __shared__ __attribute__((aligned(16))) uint8_t As[2][G_BM * G_BK];
+    const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, const int32_t* __restrict__ perm, float* __restrict__ y,
+    int32_t* __restrict__ acc_debug, int n_tm) {
+    constexpr int BM = MB * 16;
+    constexpr int AL = BM * 8 / 256;  // 16-byte A loads per thread per K block
+    __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * G_BK];
 
     const int tm = blockIdx.x % n_tm, tn = blockIdx.x / n_tm;
-    const int m0 = tm * G_BM;
+    const int m0 = tm * BM;
     const int NB = d_out >> 4, KB = d_in / G_BK;
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
     const int nb0 = tn * (G_BN / 16) + wid * G_NBW;
     const int lr = lane & 15, lg = lane >> 4;
+    auto token = [&](int pos) {
+        pos = min(pos, T - 1);
+        return perm ? perm[pos] : pos;
+    };
 
-    // activation-code tile loads: 4 x 16 B per thread, 8 threads per 128-byte row
+    // activation-code tile loads: AL x 16 B per thread, 8 threads per 128-byte row
     const int a_c = tid & 7;
-    const int8_t* a_ptr[4];
-    int a_lds[4];
+    const int8_t* a_ptr[AL];
+    int a_lds[AL];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
+    for (int p = 0; p < AL; ++p) {
         const int r = (tid >> 3) + 32 * p;
-        const int gr = min(m0 + r, T - 1);
-        a_ptr[p] = codes + (size_t)gr * d_in + a_c * 16;
+        a_ptr[p] = codes + (size_t)token(m0 + r) * d_in + a_c * 16;
         a_lds[p] = lds_a_offset(r, a_c);
     }
     // weight fragment pointers (one per N block of this wave)
@@ -82,19 +93,19 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
         b_ptr[j] = w_tiled + ((size_t)(nb_ok[j] ? nb0 + j : 0) * KB) * 64 + lane;
     }
 
-    v4i acc[G_MB][G_NBW];
+    v4i acc[MB][G_NBW];
 #pragma unroll
-    for (int m = 0; m < G_MB; ++m)
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
         for (int j = 0; j < G_NBW; ++j) acc[m][j] = v4i{0, 0, 0, 0};
 
-    v4u a_reg[4], b_reg[G_NBW];
+    v4u a_reg[AL], b_reg[G_NBW];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) a_reg[p] = *reinterpret_cast<const v4u*>(a_ptr[p]);
+    for (int p = 0; p < AL; ++p) a_reg[p] = *reinterpret_cast<const v4u*>(a_ptr[p]);
 #pragma unroll
     for (int j = 0; j < G_NBW; ++j) b_reg[j] = nb_ok[j] ? b_ptr[j][0] : v4u{0, 0, 0, 0};
 #pragma unroll
-    for (int p = 0; p < 4; ++p) *reinterpret_cast<v4u*>(&As[0][a_lds[p]]) = a_reg[p];
+    for (int p = 0; p < AL; ++p) *reinterpret_cast<v4u*>(&As[0][a_lds[p]]) = a_reg[p];
     __syncthreads();
 
     for (int kb = 0; kb < KB; ++kb) {
@@ -105,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
         const bool more = (kb + 1) < KB;
         if (more) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p)
+            for (int p = 0; p < AL; ++p)
                 a_reg[p] = *reinterpret_cast<const v4u*>(a_ptr[p] + (size_t)(kb + 1) * G_BK);
 #pragma unroll
             for (int j = 0; j < G_NBW; ++j)
@@ -116,74 +127,81 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
             v4i bop[G_NBW];
 #pragma unroll
             for (int j = 0; j < G_NBW; ++j) bop[j] = unpack_w4x16(b_cur[j][2 * s], b_cur[j][2 * s + 1]);
-            v4i a[G_MB];  // all A fragments of this K step in flight at once
+            v4i a[MB];  // all A fragments of this K step in flight at once
 #pragma unroll
-            for (int m = 0; m < G_MB; ++m)
+            for (int m = 0; m < MB; ++m)
                 a[m] = *reinterpret_cast<const v4i*>(&As[cur][lds_a_offset(m * 16 + lr, s * 4 + lg)]);
 #pragma unroll
-            for (int m = 0; m < G_MB; ++m)
+            for (int m = 0; m < MB; ++m)
 #pragma unroll
                 for (int j = 0; j < G_NBW; ++j)
                     acc[m][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[m], bop[j], acc[m][j], 0, 0, 0);
-            // keep the eight LDS reads ahead of the 32 MFMAs that consume them
-            __builtin_amdgcn_sched_group_barrier(0x100, G_MB, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, G_MB * G_NBW, 0);
+            // keep the LDS reads ahead of the MFMAs that consume them
+            __builtin_amdgcn_sched_group_barrier(0x100, MB, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, MB * G_NBW, 0);
         }
         if (more) {
 #pragma unroll
-            for (int p = 0; p < 4; ++p) *reinterpret_cast<v4u*>(&As[cur ^ 1][a_lds[p]]) = a_reg[p];
+            for (int p = 0; p < AL; ++p) *reinterpret_cast<v4u*>(&As[cur ^ 1][a_lds[p]]) = a_reg[p];
         }
         __syncthreads();
     }
 
     // ------------------------------------------------------------ epilogue
-    // lane holds column (nb*16 + lr) and rows (m*16 + lg*4 + r) of each block
-    float sx[G_MB][4];
+    // lane holds column (nb*16 + lr) and rows (m*16 + lg*4 + r) of each block; the
+    // A operands of the adapter MFMAs are rows (m*16 + lr).  Processed one M block at
+    // a time to keep register pressure at the main loop's level.
+    const bool have_se = u != nullptr && rs_pad > 0;
+    v8bf bs[G_NBW];
+    if (have_se) {  // issued before the dequantization math
 #pragma unroll
-    for (int m = 0; m < G_MB; ++m)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sx[m][r] = s_x[min(m0 + m * 16 + lg * 4 + r, T - 1)];
+        for (int j = 0; j < G_NBW; ++j)
+            bs[j] = nb_ok[j] ? *reinterpret_cast<const v8bf*>(bt_s + (size_t)((nb0 + j) * 16 + lr) * rs_pad + lg * 8)
+                             : v8bf{};
+    }
     float sw[G_NBW];
 #pragma unroll
     for (int j = 0; j < G_NBW; ++j) sw[j] = nb_ok[j] ? w_scale[(nb0 + j) * 16 + lr] : 0.0f;
 
-    if (acc_debug) {
+    v4f yv[MB][G_NBW];
 #pragma unroll
-        for (int m = 0; m < G_MB; ++m)
+    for (int m = 0; m < MB; ++m) {
+        float sx[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sx[r] = s_x[token(m0 + m * 16 + lg * 4 + r)];
+        if (acc_debug) {
 #pragma unroll
             for (int j = 0; j < G_NBW; ++j) {
                 if (!nb_ok[j]) continue;
-                const int col = (nb0 + j) * 16 + lr;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = m0 + m * 16 + lg * 4 + r;
-                    if (row < T) acc_debug[(size_t)row * d_out + col] = acc[m][j][r] >> 4;
-                }
+                for (int r = 0; r < 4; ++r)
+                    if (m0 + m * 16 + lg * 4 + r < T)
+                        acc_debug[(size_t)token(m0 + m * 16 + lg * 4 + r) * d_out + (nb0 + j) * 16 + lr] = acc[m][j][r] >> 4;
             }
-    }
-
-    v4f yv[G_MB][G_NBW];
-#pragma unroll
-    for (int m = 0; m < G_MB; ++m)
+        }
 #pragma unroll
         for (int j = 0; j < G_NBW; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) yv[m][j][r] = (float)(acc[m][j][r] >> 4) * sx[m][r] * sw[j];
-
-    // shared expert: y += u . B_s
-    if (u) {
-        for (int k0 = 0; k0 < rs_pad; k0 += 32) {
-            v8bf bs[G_NBW];
+            for (int r = 0; r < 4; ++r) yv[m][j][r] = (float)(acc[m][j][r] >> 4) * sx[r] * sw[j];
+        // shared expert: y += u . B_s (one bf16 MFMA K step per 32 of rank)
+        if (have_se) {
+            const int arow = token(m0 + m * 16 + lr);
+            for (int k0 = 0; k0 < rs_pad; k0 += 32) {
+                if (k0 > 0) {
 #pragma unroll
-            for (int j = 0; j < G_NBW; ++j)
-                bs[j] = nb_ok[j] ? *reinterpret_cast<const v8bf*>(bt_s + (size_t)((nb0 + j) * 16 + lr) * rs_pad + k0 + lg * 8)
-                                 : v8bf{};
+                    for (int j = 0; j < G_NBW; ++j)
+                        bs[j] = nb_ok[j] ? *reinterpret_cast<const v8bf*>(bt_s + (size_t)((nb0 + j) * 16 + lr) * rs_pad + k0 + lg * 8)
+                                         : v8bf{};
+                }
+                const v8bf ua = *reinterpret_cast<const v8bf*>(u + (size_t)arow * rs_pad + k0 + lg * 8);
 #pragma unroll
-            for (int m = 0; m < G_MB; ++m) {
-                const int row = min(m0 + m * 16 + lr, T - 1);
-                const v8bf a = *reinterpret_cast<const v8bf*>(u + (size_t)row * rs_pad + k0 + lg * 8);
+                for (int j = 0; j < G_NBW; ++j) yv[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, bs[j], yv[m][j], 0, 0, 0);
+            }
+            if (rs_pad > 32 && m + 1 < MB) {  // restore the first K step for the next block
 #pragma unroll
-                for (int j = 0; j < G_NBW; ++j) yv[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bs[j], yv[m][j], 0, 0, 0);
+                for (int j = 0; j < G_NBW; ++j)
+                    bs[j] = nb_ok[j] ? *reinterpret_cast<const v8bf*>(bt_s + (size_t)((nb0 + j) * 16 + lr) * rs_pad + lg * 8)
+                                     : v8bf{};
             }
         }
     }
@@ -191,16 +209,18 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     // routed experts: for every expert present among the tile's tokens,
     // y += (v masked to that expert's rows) . B_e
     if (v && expert) {
-        int ex[G_MB];
+        int ex[MB];
 #pragma unroll
-        for (int m = 0; m < G_MB; ++m) {
-            const int row = m0 + m * 16 + lr;
-            ex[m] = row < T ? expert[row] : -1;
+        for (int m = 0; m < MB; ++m) ex[m] = (m0 + m * 16 + lr < T) ? expert[token(m0 + m * 16 + lr)] : -1;
+        uint32_t present = 0;
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+            for (int e = 0; e < n_r; ++e)
+                if (__ballot(ex[m] == e)) present |= 1u << e;
         }
-        const int e0 = (m0 + lane < T) ? expert[m0 + lane] : -1;
-        const int e1 = (m0 + 64 + lane < T) ? expert[m0 + 64 + lane] : -1;
-        for (int e = 0; e < n_r; ++e) {
-            if (__ballot(e0 == e || e1 == e) == 0) continue;
+        while (present) {
+            const int e = __builtin_ctz(present);
+            present &= present - 1;
             for (int k0 = 0; k0 < rr_pad; k0 += 32) {
                 v8bf br[G_NBW];
 #pragma unroll
@@ -209,42 +229,49 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
                                            bt_r + ((size_t)e * d_out + (nb0 + j) * 16 + lr) * rr_pad + k0 + lg * 8)
                                      : v8bf{};
 #pragma unroll
-                for (int m = 0; m < G_MB; ++m) {
-                    const int row = min(m0 + m * 16 + lr, T - 1);
-                    v8bf a = *reinterpret_cast<const v8bf*>(v + (size_t)row * rr_pad + k0 + lg * 8);
-                    if (ex[m] != e) a = v8bf{};
+                for (int m = 0; m < MB; ++m) {
+                    if (__ballot(ex[m] == e) == 0) continue;  // no row of this block uses expert e
+                    const v8bf va = ex[m] == e ? *reinterpret_cast<const v8bf*>(v + (size_t)token(m0 + m * 16 + lr) * rr_pad + k0 + lg * 8)
+                                               : v8bf{};
 #pragma unroll
                     for (int j = 0; j < G_NBW; ++j)
-                        yv[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, br[j], yv[m][j], 0, 0, 0);
+                        yv[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, br[j], yv[m][j], 0, 0, 0);
                 }
             }
         }
     }
 
 #pragma unroll
-    for (int m = 0; m < G_MB; ++m)
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
-        for (int j = 0; j < G_NBW; ++j) {
-            if (!nb_ok[j]) continue;
-            const int col = (nb0 + j) * 16 + lr;
+        for (int r = 0; r < 4; ++r) {
+            const int pos = m0 + m * 16 + lg * 4 + r;
+            if (pos >= T) continue;
+            const size_t rowoff = (size_t)token(pos) * d_out;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m0 + m * 16 + lg * 4 + r;
-                if (row < T) y[(size_t)row * d_out + col] = yv[m][j][r];
-            }
+            for (int j = 0; j < G_NBW; ++j)
+                if (nb_ok[j]) y[rowoff + (nb0 + j) * 16 + lr] = yv[m][j][r];
         }
 }
 
 hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* w_tiled, const float* w_scale, int T,
                           int d_in, int d_out, const uint16_t* u, const uint16_t* bt_s, int rs_pad, const uint16_t* v,
-                          const int32_t* expert, const uint16_t* bt_r, int rr_pad, int n_r, float* y,
-                          int32_t* acc_debug, hipStream_t st) {
+                          const int32_t* expert, const uint16_t* bt_r, int rr_pad, int n_r, const int32_t* perm,
+                          float* y, int32_t* acc_debug, hipStream_t st) {
     if (T <= 0) return hipSuccess;
-    const int n_tm = (T + G_BM - 1) / G_BM;
     const int n_tn = (d_out + G_BN - 1) / G_BN;
-    hipLaunchKernelGGL(gemm_w4_kernel, dim3(n_tm * n_tn), dim3(256), 0, st, codes, s_x,
-                       reinterpret_cast<const v4u*>(w_tiled), w_scale, T, d_in, d_out, u, bt_s, rs_pad, v, expert,
-                       bt_r, rr_pad, n_r, y, acc_debug, n_tm);
+    // 128-token tiles unless that leaves the chip less than two workgroups per CU
+    const bool small = (long)((T + 127) / 128) * n_tn < 512;
+    const v4u* w = reinterpret_cast<const v4u*>(w_tiled);
+    if (small) {
+        const int n_tm = (T + 63) / 64;
+        hipLaunchKernelGGL(gemm_w4_kernel<4>, dim3(n_tm * n_tn), dim3(256), 0, st, codes, s_x, w, w_scale, T, d_in, d_out,
+                           u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, perm, y, acc_debug, n_tm);
+    } else {
+        const int n_tm = (T + 127) / 128;
+        hipLaunchKernelGGL(gemm_w4_kernel<8>, dim3(n_tm * n_tn), dim3(256), 0, st, codes, s_x, w, w_scale, T, d_in, d_out,
+                           u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, perm, y, acc_debug, n_tm);
+    }
     return hipGetLastError();
 }
 

@@ -7,8 +7,9 @@
 //     each 8-code half is stored so byte b = code b | code b+4 << 4.
 //   * W3 main weights: canonical 96-bit groups -> tiles of 16 channels x 128 K,
 //     12 bytes per lane: lane l owns channel 16*nb + l%16 and codes
-//     k = 128*kb + 32*s + 8*(l/16) + m (s = 0..3, m = 0..7), code 8s+m at bits
-//     3*(8s+m) of its 96-bit little-endian value.
+//     k = 128*kb + 32*s + 8*(l/16) + p (s = 0..3, p = 0..7) in sign/magnitude form:
+//     |c| of code 8s+p at bits 4p + 2(s&1) of dword s>>1, its sign at bit 4p + 3 - s
+//     of dword 2 (the weight-streaming kernel turns 8 codes into one fp4 word).
 //   * Adapter/router matrices are transposed so every MFMA operand fragment is
 //     16 contiguous bytes, and padded with zeros to whole MFMA steps.
 
@@ -77,13 +78,14 @@ __global__ void prep_w3_kernel(const uint32_t* __restrict__ packed, int d_out, i
     const int n = nb * 16 + (lane & 15), g = lane >> 4;
     const uint32_t* row = packed + (size_t)n * (d_in / 32) * 3;
     uint32_t w[3] = {0, 0, 0};
-    for (int i = 0; i < 32; ++i) {
-        const int s = i >> 3, m = i & 7;
-        const uint32_t c = canon_w3_code(row, kb * 128 + s * 32 + g * 8 + m);
-        const int bit = 3 * i;
-        const int wi = bit >> 5, off = bit & 31;
-        w[wi] |= c << off;
-        if (off > 29) w[wi + 1] |= c >> (32 - off);
+    for (int s = 0; s < 4; ++s) {
+        for (int p = 0; p < 8; ++p) {
+            const uint32_t c = canon_w3_code(row, kb * 128 + s * 32 + g * 8 + p);  // 3-bit two's complement
+            const int v = (c & 4u) ? (int)c - 8 : (int)c;
+            const uint32_t mag = (uint32_t)(v < 0 ? -v : v), sign = v < 0 ? 1u : 0u;
+            w[s >> 1] |= mag << (4 * p + 2 * (s & 1));
+            w[2] |= sign << (4 * p + 3 - s);
+        }
     }
     uint32_t* o = tiled + idx * 3;
     o[0] = w[0];

@@ -13,7 +13,6 @@
 
 namespace qe {
 hipError_t skinny_set_attributes();
-int skinny_ksplit(int d_in, int d_out);
 }  // namespace qe
 
 using namespace qe;
@@ -97,6 +96,8 @@ int ensure_attributes() {
     return QE_OK;
 }
 
+constexpr int kSkinnyMaxT = 16;  // token counts served by the weight-streaming kernels
+
 }  // namespace
 
 namespace qe {
@@ -144,7 +145,8 @@ WsLayout ws_layout(const qe_linear* lin, int T) {
     W.s_x = off;
     off = align256(off + t * 4);
     W.part = off;
-    off = align256(off + (size_t)W.xproj_ksplit * t * P.n_cols_pad * 4);
+    const int xks = std::max(W.xproj_ksplit, T <= kSkinnyMaxT ? skinny_ksplit_proj(lin->d_in) : 1);
+    off = align256(off + (size_t)xks * t * P.n_cols_pad * 4);
     W.scores = off;
     off = align256(off + t * std::max(lin->n_routed, 1) * 4);
     W.expert = off;
@@ -332,10 +334,18 @@ static int run_xpass(const qe_linear* lin, const void* x, int x_dtype, int T, bo
     if (do_route) include(P.col_router, lin->n_routed);
     if (c1 <= c0) return QE_OK;
     const int nc = c1 - c0, nc_pad = (nc + 15) / 16 * 16;
-    const int ks = std::min(W.xproj_ksplit, xproj_ksplit(T, lin->d_in, nc_pad));
     float* part = at<float>(ws, W.part);
     const uint16_t* mt = at<const uint16_t>(lin->prep, P.mt);
-    QE_TRY_HIP(launch_xproj(x, x_dtype, T, lin->d_in, mt, c0, nc, nc_pad, ks, part, s));
+    int ks;
+    if (T <= kSkinnyMaxT) {  // few tokens: stream the projection matrix like decode weights
+        int st = ensure_attributes();
+        if (st) return st;
+        ks = skinny_ksplit_proj(lin->d_in);
+        QE_TRY_HIP(launch_skinny(x, x_dtype, T, lin->d_in, nc_pad, 16, mt + (size_t)c0 * lin->d_in, ks, part, nc_pad, s));
+    } else {
+        ks = std::min(W.xproj_ksplit, xproj_ksplit(T, lin->d_in, nc_pad));
+        QE_TRY_HIP(launch_xproj(x, x_dtype, T, lin->d_in, mt, c0, nc, nc_pad, ks, part, s));
+    }
     QE_TRY_HIP(launch_xproj_finish(part, ks, T, nc_pad, c0, want_se ? P.col_se : -1, lin->r_shared, P.rs_pad,
                                    want_re ? P.col_re : -1, lin->n_routed, lin->r_routed, P.rr_pad,
                                    do_route ? P.col_router : -1, expert_in, scores, expert_out, want_se ? u : nullptr,
@@ -372,8 +382,8 @@ int qe_adapter_inputs(const qe_linear* lin, const void* x, int32_t x_dtype, int3
 
 // ------------------------------------------------------------------ a3 / a7
 static int run_gemm(const qe_linear* lin, const int8_t* codes, const float* s_x, const void* x, int x_dtype, int T,
-                    const uint16_t* u, const uint16_t* v, const int32_t* expert, float* y, int32_t* acc_debug,
-                    void* ws, hipStream_t s) {
+                    const uint16_t* u, const uint16_t* v, const int32_t* expert, const int32_t* perm, float* y,
+                    int32_t* acc_debug, void* ws, hipStream_t s) {
     const PrepLayout P = prep_layout(lin);
     const uint16_t* bt_s = P.rs_pad > 0 ? at<const uint16_t>(lin->prep, P.bt_s) : nullptr;
     const uint16_t* bt_r = P.rr_pad > 0 ? at<const uint16_t>(lin->prep, P.bt_r) : nullptr;
@@ -386,20 +396,20 @@ static int run_gemm(const qe_linear* lin, const int8_t* codes, const float* s_x,
         int st = ensure_attributes();
         if (st) return st;
         QE_TRY_HIP(launch_skinny(x, x_dtype, T, lin->d_in, lin->d_out, lin->w_bits, at<const void>(lin->prep, P.w_tiled),
-                                 W.skinny_ksplit, part, s));
+                                 W.skinny_ksplit, part, lin->d_out, s));
         QE_TRY_HIP(launch_skinny_finish(part, W.skinny_ksplit, T, lin->d_out, w_scale, u, bt_s, P.rs_pad, v, expert,
                                         bt_r, P.rr_pad, y, s));
     } else {
         QE_TRY_HIP(launch_gemm_w4(codes, s_x, at<const uint8_t>(lin->prep, P.w_tiled), w_scale, T, lin->d_in,
-                                  lin->d_out, u, bt_s, P.rs_pad, v, expert, bt_r, P.rr_pad, lin->n_routed, y, acc_debug,
-                                  s));
+                                  lin->d_out, u, bt_s, P.rs_pad, v, expert, bt_r, P.rr_pad, lin->n_routed, perm, y,
+                                  acc_debug, s));
     }
     return QE_OK;
 }
 
 int qe_wq_gemm(const qe_linear* lin, const int8_t* codes, const float* s_x, const void* x, int32_t x_dtype, int32_t T,
-               const uint16_t* u, const uint16_t* v, const int32_t* expert, float* y, int32_t* acc_debug, void* ws,
-               size_t ws_bytes, void* stream) {
+               const uint16_t* u, const uint16_t* v, const int32_t* expert, const int32_t* perm, float* y,
+               int32_t* acc_debug, void* ws, size_t ws_bytes, void* stream) {
     int st = validate_forward_common(lin, T, x_dtype, x, ws, ws_bytes);
     if (st) return st;
     if (T == 0) return QE_OK;
@@ -412,7 +422,8 @@ int qe_wq_gemm(const qe_linear* lin, const int8_t* codes, const float* s_x, cons
         QE_CHECK(aligned16(codes), QE_ERR_ALIGNMENT);
     }
     QE_CHECK((v == nullptr) == (expert == nullptr), QE_ERR_INVALID_ARG);
-    return run_gemm(lin, codes, s_x, x, x_dtype, T, u, v, expert, y, acc_debug, ws, S(stream));
+    return run_gemm(lin, codes, s_x, x, x_dtype, T, u, v, expert, lin->a_bits == 16 ? nullptr : perm, y, acc_debug, ws,
+                    S(stream));
 }
 
 // ------------------------------------------------------------------ a6 unfused
@@ -437,12 +448,15 @@ int qe_routed_lora(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t
 
 // ------------------------------------------------------------------ composite
 static int run_prologue(const qe_linear* lin, const void* x, int x_dtype, int T, int8_t* codes, float* s_x,
-                        uint16_t* u, uint16_t* v, int32_t* expert, void* ws, hipStream_t s) {
+                        uint16_t* u, uint16_t* v, int32_t* expert, int32_t* perm, void* ws, hipStream_t s) {
     const PrepLayout P = prep_layout(lin);
+    const WsLayout W = ws_layout(lin, T);
     const bool route = lin->n_routed > 0;
     int st = run_xpass(lin, x, x_dtype, T, u != nullptr, route, route, nullptr, nullptr, route ? expert : nullptr, u,
                        v, ws, s);
     if (st) return st;
+    if (route && perm)  // tokens grouped by routed expert, for the GEMM's tile order
+        QE_TRY_HIP(launch_bucket(expert, T, lin->n_routed, at<int32_t>(ws, W.counts), at<int32_t>(ws, W.offsets), perm, s));
     if (lin->a_bits != 16)
         QE_TRY_HIP(launch_quant_act(x, x_dtype, at<const float>(lin->prep, P.smooth),
                                     at<const float>(lin->prep, P.inv_smooth), T, lin->d_in, lin->a_bits, codes, s_x, s));
@@ -450,7 +464,8 @@ static int run_prologue(const qe_linear* lin, const void* x, int x_dtype, int T,
 }
 
 int qe_linear_prologue(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, int8_t* codes, float* s_x,
-                       uint16_t* u, uint16_t* v, int32_t* expert, void* ws, size_t ws_bytes, void* stream) {
+                       uint16_t* u, uint16_t* v, int32_t* expert, int32_t* perm, void* ws, size_t ws_bytes,
+                       void* stream) {
     int st = validate_forward_common(lin, T, x_dtype, x, ws, ws_bytes);
     if (st) return st;
     if (T == 0) return QE_OK;
@@ -458,8 +473,9 @@ int qe_linear_prologue(const qe_linear* lin, const void* x, int32_t x_dtype, int
     QE_CHECK(lin->a_bits == 16 ? (codes == nullptr && s_x == nullptr) : (codes && s_x), QE_ERR_INVALID_ARG);
     QE_CHECK((lin->r_shared > 0) == (u != nullptr), QE_ERR_INVALID_ARG);
     QE_CHECK((lin->n_routed > 0) == (v != nullptr) && (lin->n_routed > 0) == (expert != nullptr), QE_ERR_INVALID_ARG);
+    QE_CHECK(!perm || lin->n_routed > 0, QE_ERR_INVALID_ARG);
     if (codes) QE_CHECK(aligned16(codes), QE_ERR_ALIGNMENT);
-    return run_prologue(lin, x, x_dtype, T, codes, s_x, u, v, expert, ws, S(stream));
+    return run_prologue(lin, x, x_dtype, T, codes, s_x, u, v, expert, perm, ws, S(stream));
 }
 
 int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* y, int32_t* expert_out,
@@ -478,9 +494,10 @@ int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int3
     uint16_t* v = route ? at<uint16_t>(ws, W.v) : nullptr;
     int8_t* codes = lin->a_bits != 16 ? at<int8_t>(ws, W.codes) : nullptr;
     float* s_x = lin->a_bits != 16 ? at<float>(ws, W.s_x) : nullptr;
-    st = run_prologue(lin, x, x_dtype, T, codes, s_x, u, v, expert, ws, s);
+    int32_t* perm = (route && lin->a_bits != 16) ? at<int32_t>(ws, W.perm) : nullptr;
+    st = run_prologue(lin, x, x_dtype, T, codes, s_x, u, v, expert, perm, ws, s);
     if (st) return st;
-    return run_gemm(lin, codes, s_x, x, x_dtype, T, u, v, expert, y, nullptr, ws, s);
+    return run_gemm(lin, codes, s_x, x, x_dtype, T, u, v, expert, perm, y, nullptr, ws, s);
 }
 
 // ------------------------------------------------------------------ a8

@@ -83,10 +83,14 @@ hipError_t launch_bucket(const int32_t* expert, int T, int n_r, int32_t* counts,
 hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* w_tiled, const float* w_scale,
                           int T, int d_in, int d_out, const uint16_t* u, const uint16_t* bt_s, int rs_pad,
                           const uint16_t* v, const int32_t* expert, const uint16_t* bt_r, int rr_pad, int n_r,
-                          float* y, int32_t* acc_debug, hipStream_t st);
+                          const int32_t* perm, float* y, int32_t* acc_debug, hipStream_t st);
 
-hipError_t launch_skinny(const void* x, int x_dtype, int T, int d_in, int d_out, int w_bits, const void* w_tiled,
-                         int ksplit, float* part, hipStream_t st);
+// weight streaming for few tokens: w_bits 3 / 4 read packed tiles, w_bits 16 reads bf16 rows
+// (the x-projection matrix); part[ks][t][c] with row stride out_ld
+hipError_t launch_skinny(const void* x, int x_dtype, int T, int d_in, int n_cols, int w_bits, const void* w_tiled,
+                         int ksplit, float* part, int out_ld, hipStream_t st);
+int skinny_ksplit(int d_in, int d_out);
+int skinny_ksplit_proj(int d_in);
 
 hipError_t launch_skinny_finish(const float* part, int ksplit, int T, int d_out, const float* w_scale,
                                 const uint16_t* u, const uint16_t* bt_s, int rs_pad, const uint16_t* v,

@@ -106,9 +106,10 @@ def test_route_parity(Q, cfg_name, lin_name):
 
 
 # ------------------------------------------------------------ a3 accumulators
-@pytest.mark.parametrize("cfg_name,lin_name,T", [("tiny", "lin", None), ("tiny", "lin", 77), ("qwen2vl_2b", "gate", None),
-                                                 ("qwen2vl_2b", "k", 300)])
-def test_wq_gemm_acc_bit_exact(Q, cfg_name, lin_name, T):
+@pytest.mark.parametrize("cfg_name,lin_name,T,permute", [("tiny", "lin", None, False), ("tiny", "lin", 77, True),
+                                                         ("qwen2vl_2b", "gate", None, False),
+                                                         ("qwen2vl_2b", "k", 300, True), ("qwen2vl_2b", "q", 1000, True)])
+def test_wq_gemm_acc_bit_exact(Q, cfg_name, lin_name, T, permute):
     cfg = synth.get_config(cfg_name)
     spec = _spec(cfg, lin_name)
     layer, params = _layer(Q, cfg, spec)
@@ -120,7 +121,9 @@ def test_wq_gemm_acc_bit_exact(Q, cfg_name, lin_name, T):
     Q.libqe.qe_quant_act(xd, torch.from_numpy(params["s"]).to(DEV), cfg.a_bits, codes, s_x)
     y = torch.empty(T, spec.d_out, dtype=torch.float32, device=DEV)
     acc = torch.empty(T, spec.d_out, dtype=torch.int32, device=DEV)
-    Q.libqe.qe_wq_gemm(layer.lin, codes, s_x, None, T, None, None, None, y, acc, layer.workspace(T))
+    # the visiting order of the tokens must not change any result
+    perm = torch.from_numpy(np.random.default_rng(T).permutation(T).astype(np.int32)).to(DEV) if permute else None
+    Q.libqe.qe_wq_gemm(layer.lin, codes, s_x, None, T, None, None, None, y, acc, layer.workspace(T), perm=perm)
     torch.cuda.synchronize()
     qx, sx = _codes_ref(x, params["s"], cfg.a_bits)
     qw, s_w = O.quant_weights(params["W_f"], params["s"], cfg.w_bits)
