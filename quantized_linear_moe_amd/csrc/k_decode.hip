@@ -30,7 +30,8 @@ constexpr int SK_LD = SK_MAX_KBLK * 128 * 2 + 16;  // LDS row stride (bytes) of 
 //             dword 1 of codes 16..31, two bits each, code 8s+p at bits 4p + 2(s&1) of
 //             dword s>>1; dword 2 holds the signs, code 8s+p at bit 4p + 3 - s.  This
 //             makes 8 codes of one MFMA step an fp4 (e2m1) word in three ALU ops.
-//   WB == 4 : 4 dwords of the int8-GEMM tile layout (see the 4-bit prepare kernel).
+//   WB == 4 : 4 dwords: the lane's 8 bytes of the two 64-K steps of the int8-GEMM tile
+//             layout (see the 4-bit prepare kernel).
 //   WB == 16: bf16 rows (K-contiguous); the fragment is loaded per step (no tile layout).
 template <int WB>
 struct Frag {
@@ -102,8 +103,10 @@ __device__ inline void load_frag(const uint32_t* __restrict__ w, int nb, int NB,
         f[1] = p[1];
         f[2] = p[2];
     } else if constexpr (WB == 4) {
-        const v4u q = *reinterpret_cast<const v4u*>(w + (((size_t)nb * KB + kb) * 64 + lane) * 4);
-        f[0] = q[0]; f[1] = q[1]; f[2] = q[2]; f[3] = q[3];
+        // two 64-K steps of the 4-bit tile layout: 8 bytes per lane each
+        const v2u q0 = *reinterpret_cast<const v2u*>(w + (((size_t)nb * 2 * KB + 2 * kb) * 64 + lane) * 2);
+        const v2u q1 = *reinterpret_cast<const v2u*>(w + (((size_t)nb * 2 * KB + 2 * kb + 1) * 64 + lane) * 2);
+        f[0] = q0[0]; f[1] = q0[1]; f[2] = q1[0]; f[3] = q1[1];
     } else {
         // bf16 rows of d_in elements: channel nb*16 + (lane & 15), K = kb*128 + s*32 + (lane >> 4)*8
         const uint16_t* row = reinterpret_cast<const uint16_t*>(w) + (size_t)(nb * 16 + (lane & 15)) * d_in +

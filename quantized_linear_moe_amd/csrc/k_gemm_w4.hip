@@ -14,11 +14,12 @@
 //     one AND or one shift+AND per 4 codes, no sign extension), so the int32
 //     accumulator holds 16*acc exactly (|16*acc| < 2^31 for d_in <= 150000 at A8)
 //     and an arithmetic shift recovers acc.
-//   * Weights are pre-tiled at load time so that every lane fetches its own
-//     16-byte fragment with one coalesced dwordx4 load (1 KB per wave per
-//     16 channels x 128 K); they go global -> VGPR without LDS.
-//   * Activation codes (shared by the 4 waves) are staged in LDS, double
-//     buffered, with an XOR swizzle of the 16-byte chunks against bank conflicts.
+//   * Weights are pre-tiled at load time: 512 contiguous bytes per 16 channels x
+//     one 64-wide K step, each lane's 8 bytes being exactly its MFMA fragment.
+//   * Both operands go global -> LDS by DMA (global_load_lds_dwordx4) into a
+//     4-stage ring, three K steps ahead of the MFMAs, with no staging registers;
+//     the activation-code rows use an XOR swizzle of their 16-byte chunks
+//     against bank conflicts.
 //   * Workgroup tile 128 tokens x 256 channels; wave tile 128 x 64
 //     (8 x 4 MFMA blocks, 128 accumulator registers); 64-token tiles when the
 //     grid would otherwise leave CUs idle (narrow projections).
@@ -34,8 +35,9 @@
 namespace qe {
 
 constexpr int G_BN = 256;
-constexpr int G_BK = 128;
-constexpr int G_NBW = 4;  // N blocks per wave
+constexpr int G_BK = 64;   // K per pipeline stage (one int8 MFMA K step)
+constexpr int G_NS = 4;    // stages in the LDS ring: loads run three stages ahead
+constexpr int G_NBW = 4;   // N blocks per wave
 
 __device__ inline v4i unpack_w4x16(uint32_t p0, uint32_t p1) {
     // tiled byte b of p holds code b (low nibble) and code b+4 (high nibble)
@@ -47,21 +49,43 @@ __device__ inline v4i unpack_w4x16(uint32_t p0, uint32_t p1) {
     return r;
 }
 
-__device__ inline int lds_a_offset(int row, int chunk) { return row * G_BK + ((chunk ^ (row & 7)) << 4); }
+// A tile rows are 64 bytes (four 16-byte chunks); chunk c of row r is stored at
+// c ^ ((r >> 1) & 3), which spreads the 16-byte reads of 8 consecutive rows over all banks.
+__device__ inline int a_swz(int row) { return (row >> 1) & 3; }
+
+// 16-byte global -> LDS copy by DMA (global_load_lds_dwordx4): lane i writes LDS bytes
+// [lds_base + 16 i, +16) of this wave's 1 KB block.  Issued as inline asm so that the
+// compiler inserts no waits of its own; the kernel waits with explicit vmcnt counts.
+__device__ inline void dma16(const void* src, uint32_t lds_base) {
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
+}
+#define QE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+// vmcnt <= n and every LDS read of this wave completed (lgkmcnt 0)
+#define QE_WAIT_VMCNT_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
+#define QE_WG_BARRIER()                   \
+    do {                                  \
+        asm volatile("" ::: "memory");    \
+        __builtin_amdgcn_s_barrier();     \
+        asm volatile("" ::: "memory");    \
+    } while (0)
 
 // MB: 16-row M blocks per workgroup (tile MB*16 tokens x 256 channels).  Tile rows are
 // positions in `perm` order when perm != NULL (tokens grouped by routed expert, so a
 // tile meets few experts in the epilogue), else token order.
 template <int MB>
 __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
-    const int8_t* __restrict__ codes, const float* __restrict__ s_x, const v4u* __restrict__ w_tiled,
+    const int8_t* __restrict__ codes, const float* __restrict__ s_x, const uint8_t* __restrict__ w_tiled,
     const float* __restrict__ w_scale, int T, int d_in, int d_out, const uint16_t* __restrict__ u,
     const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v, const int32_t* __restrict__ expert,
     const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, const int32_t* __restrict__ perm, float* __restrict__ y,
     int32_t* __restrict__ acc_debug, int n_tm) {
     constexpr int BM = MB * 16;
-    constexpr int AL = BM * 8 / 256;  // 16-byte A loads per thread per K block
-    __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * G_BK];
+    constexpr int A_STAGE = BM * G_BK;            // bytes of codes per stage
+    constexpr int B_STAGE = 4 * G_NBW * 512;      // 4 waves x 4 N blocks x 512 B of packed weights
+    constexpr int STAGE = A_STAGE + B_STAGE;
+    constexpr int A_DMA = A_STAGE / 1024 / 4;     // A copies per wave per stage
+    constexpr int OPS = A_DMA + 2;                // DMA instructions per thread per stage
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[G_NS * STAGE];
 
     const int tm = blockIdx.x % n_tm, tn = blockIdx.x / n_tm;
     const int m0 = tm * BM;
@@ -73,25 +97,35 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
         pos = min(pos, T - 1);
         return perm ? perm[pos] : pos;
     };
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
 
-    // activation-code tile loads: AL x 16 B per thread, 8 threads per 128-byte row
-    const int a_c = tid & 7;
-    const int8_t* a_ptr[AL];
-    int a_lds[AL];
+    // DMA sources.  A: copy q = wid + 4p covers tile rows 16q..16q+15; lane i fetches the
+    // logical chunk stored at its LDS slot (row 16q + i/4, slot i%4).
+    const int8_t* a_src[A_DMA];
 #pragma unroll
-    for (int p = 0; p < AL; ++p) {
-        const int r = (tid >> 3) + 32 * p;
-        a_ptr[p] = codes + (size_t)token(m0 + r) * d_in + a_c * 16;
-        a_lds[p] = lds_a_offset(r, a_c);
+    for (int p = 0; p < A_DMA; ++p) {
+        const int q = wid + 4 * p, r = 16 * q + (lane >> 2), c = (lane & 3) ^ a_swz(r);
+        a_src[p] = codes + (size_t)token(m0 + r) * d_in + c * 16;
     }
-    // weight fragment pointers (one per N block of this wave)
-    const v4u* b_ptr[G_NBW];
+    // B: copy p of this wave moves the 512-byte K-step tiles of N blocks 2p and 2p+1
+    // (lanes 0-31 and 32-63); blocks past d_out fetch block 0 and are never stored.
+    const uint8_t* b_src[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        const int nb = nb0 + 2 * p + (lane >> 5);
+        b_src[p] = w_tiled + (size_t)(nb < NB ? nb : 0) * KB * 512 + (lane & 31) * 16;
+    }
+    auto issue = [&](int stage, int kb) {  // copy K step kb into ring slot `stage`
+        const uint32_t base = lds0 + stage * STAGE;
+#pragma unroll
+        for (int p = 0; p < A_DMA; ++p) dma16(a_src[p] + (size_t)kb * G_BK, base + (wid + 4 * p) * 1024);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) dma16(b_src[p] + (size_t)kb * 512, base + A_STAGE + wid * 2048 + p * 1024);
+    };
+
     bool nb_ok[G_NBW];
 #pragma unroll
-    for (int j = 0; j < G_NBW; ++j) {
-        nb_ok[j] = (nb0 + j) < NB;
-        b_ptr[j] = w_tiled + ((size_t)(nb_ok[j] ? nb0 + j : 0) * KB) * 64 + lane;
-    }
+    for (int j = 0; j < G_NBW; ++j) nb_ok[j] = (nb0 + j) < NB;
 
     v4i acc[MB][G_NBW];
 #pragma unroll
@@ -99,53 +133,45 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
 #pragma unroll
         for (int j = 0; j < G_NBW; ++j) acc[m][j] = v4i{0, 0, 0, 0};
 
-    v4u a_reg[AL], b_reg[G_NBW];
+    // prologue: three stages in flight, then wait for the first
 #pragma unroll
-    for (int p = 0; p < AL; ++p) a_reg[p] = *reinterpret_cast<const v4u*>(a_ptr[p]);
-#pragma unroll
-    for (int j = 0; j < G_NBW; ++j) b_reg[j] = nb_ok[j] ? b_ptr[j][0] : v4u{0, 0, 0, 0};
-#pragma unroll
-    for (int p = 0; p < AL; ++p) *reinterpret_cast<v4u*>(&As[0][a_lds[p]]) = a_reg[p];
-    __syncthreads();
+    for (int st = 0; st < G_NS - 1; ++st) issue(st, min(st, KB - 1));
+    QE_WAIT_VMCNT_LDS(2 * OPS);
+    QE_WG_BARRIER();
 
     for (int kb = 0; kb < KB; ++kb) {
-        const int cur = kb & 1;
-        v4u b_cur[G_NBW];
+        // refill the slot consumed in the previous step (past the end: a harmless repeat)
+        issue((kb + G_NS - 1) % G_NS, min(kb + G_NS - 1, KB - 1));
+        const uint8_t* st = smem + (kb % G_NS) * STAGE;
+        v2u bp[G_NBW];
 #pragma unroll
-        for (int j = 0; j < G_NBW; ++j) b_cur[j] = b_reg[j];
-        const bool more = (kb + 1) < KB;
-        if (more) {
+        for (int j = 0; j < G_NBW; ++j)
+            bp[j] = *reinterpret_cast<const v2u*>(st + A_STAGE + wid * 2048 + j * 512 + lane * 8);
+        v4i a[MB];
 #pragma unroll
-            for (int p = 0; p < AL; ++p)
-                a_reg[p] = *reinterpret_cast<const v4u*>(a_ptr[p] + (size_t)(kb + 1) * G_BK);
+        for (int m = 0; m < MB; ++m) {
+            const int row = m * 16 + lr;
+            a[m] = *reinterpret_cast<const v4i*>(st + row * G_BK + ((lg ^ a_swz(row)) << 4));
+        }
+        v4i bop[G_NBW];
+#pragma unroll
+        for (int j = 0; j < G_NBW; ++j) bop[j] = unpack_w4x16(bp[j][0], bp[j][1]);
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
 #pragma unroll
             for (int j = 0; j < G_NBW; ++j)
-                b_reg[j] = nb_ok[j] ? b_ptr[j][(size_t)(kb + 1) * 64] : v4u{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            v4i bop[G_NBW];
-#pragma unroll
-            for (int j = 0; j < G_NBW; ++j) bop[j] = unpack_w4x16(b_cur[j][2 * s], b_cur[j][2 * s + 1]);
-            v4i a[MB];  // all A fragments of this K step in flight at once
-#pragma unroll
-            for (int m = 0; m < MB; ++m)
-                a[m] = *reinterpret_cast<const v4i*>(&As[cur][lds_a_offset(m * 16 + lr, s * 4 + lg)]);
-#pragma unroll
-            for (int m = 0; m < MB; ++m)
-#pragma unroll
-                for (int j = 0; j < G_NBW; ++j)
-                    acc[m][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[m], bop[j], acc[m][j], 0, 0, 0);
-            // keep the LDS reads ahead of the MFMAs that consume them
-            __builtin_amdgcn_sched_group_barrier(0x100, MB, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, MB * G_NBW, 0);
-        }
-        if (more) {
-#pragma unroll
-            for (int p = 0; p < AL; ++p) *reinterpret_cast<v4u*>(&As[cur ^ 1][a_lds[p]]) = a_reg[p];
-        }
-        __syncthreads();
+                acc[m][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[m], bop[j], acc[m][j], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, MB + G_NBW, 0);  // LDS reads first
+        __builtin_amdgcn_sched_group_barrier(0x002, 3 * G_NBW, 0);    // weight unpack
+        __builtin_amdgcn_sched_group_barrier(0x008, MB * G_NBW, 0);   // then the MFMAs
+        // nothing of this step may move below the barrier: the slot read here is the
+        // DMA target of the next step, so every LDS read must have completed (lgkmcnt 0);
+        // and step kb+1 must have landed (kb+2, kb+3 may still be in flight)
+        __builtin_amdgcn_sched_barrier(0);
+        QE_WAIT_VMCNT_LDS(2 * OPS);
+        QE_WG_BARRIER();
     }
+    QE_WAIT_VMCNT(0);
 
     // ------------------------------------------------------------ epilogue
     // lane holds column (nb*16 + lr) and rows (m*16 + lg*4 + r) of each block; the
@@ -262,7 +288,7 @@ hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* 
     const int n_tn = (d_out + G_BN - 1) / G_BN;
     // 128-token tiles unless that leaves the chip less than two workgroups per CU
     const bool small = (long)((T + 127) / 128) * n_tn < 512;
-    const v4u* w = reinterpret_cast<const v4u*>(w_tiled);
+    const uint8_t* w = w_tiled;
     if (small) {
         const int n_tm = (T + 63) / 64;
         hipLaunchKernelGGL(gemm_w4_kernel<4>, dim3(n_tm * n_tn), dim3(256), 0, st, codes, s_x, w, w_scale, T, d_in, d_out,

@@ -1,10 +1,10 @@
 // Load-time re-layout of a QE linear's parameters into the kernels' formats.
 //
 //   * W4 main weights: canonical bytes [d_out][d_in/2] (code 2m low nibble, 2m+1
-//     high nibble) -> tiles of 16 channels x 128 K, 1 KB each, ordered
-//     (channel block, K block, lane): lane l owns channel 16*nb + l%16 and, for the
-//     two int8-MFMA K steps s, codes k = 128*kb + 64*s + 16*(l/16) + [0, 16);
-//     each 8-code half is stored so byte b = code b | code b+4 << 4.
+//     high nibble) -> tiles of 16 channels x 64 K, 512 bytes each, ordered
+//     (channel block, K step, lane): lane l owns channel 16*nb + l%16 and codes
+//     k = 64*ks + 16*(l/16) + [0, 16) in 8 bytes; each 8-code half is stored so
+//     byte b = code b | code b+4 << 4.
 //   * W3 main weights: canonical 96-bit groups -> tiles of 16 channels x 128 K,
 //     12 bytes per lane: lane l owns channel 16*nb + l%16 and codes
 //     k = 128*kb + 32*s + 8*(l/16) + p (s = 0..3, p = 0..7) in sign/magnitude form:
@@ -24,19 +24,18 @@ __device__ inline int canon_w4_code(const uint8_t* row, int k) {
 }
 
 __global__ void prep_w4_kernel(const uint8_t* __restrict__ packed, int d_out, int d_in, uint32_t* __restrict__ tiled) {
-    const int KB = d_in / 128, NB = d_out / 16;
-    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // (nb, kb, lane)
-    if (idx >= (size_t)NB * KB * 64) return;
+    const int KS = d_in / 64, NB = d_out / 16;
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;  // (nb, ks, lane)
+    if (idx >= (size_t)NB * KS * 64) return;
     const int lane = (int)(idx % 64);
     const size_t nk = idx / 64;
-    const int kb = (int)(nk % KB), nb = (int)(nk / KB);
+    const int ks = (int)(nk % KS), nb = (int)(nk / KS);
     const int n = nb * 16 + (lane & 15), g = lane >> 4;
     const uint8_t* row = packed + (size_t)n * (d_in / 2);
-    uint32_t out[4];
+    uint32_t out[2];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {  // h = 2*s + half
-        const int s = h >> 1, half = h & 1;
-        const int kbase = kb * 128 + s * 64 + g * 16 + half * 8;
+    for (int h = 0; h < 2; ++h) {
+        const int kbase = ks * 64 + g * 16 + h * 8;
         uint32_t d = 0;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -46,13 +45,12 @@ __global__ void prep_w4_kernel(const uint8_t* __restrict__ packed, int d_out, in
         }
         out[h] = d;
     }
-    uint32_t* o = tiled + idx * 4;
-#pragma unroll
-    for (int h = 0; h < 4; ++h) o[h] = out[h];
+    tiled[idx * 2] = out[0];
+    tiled[idx * 2 + 1] = out[1];
 }
 
 hipError_t launch_prep_w4(const uint8_t* packed, int d_out, int d_in, uint8_t* tiled, hipStream_t st) {
-    const size_t n = (size_t)(d_out / 16) * (d_in / 128) * 64;
+    const size_t n = (size_t)(d_out / 16) * (d_in / 64) * 64;
     if (n == 0) return hipSuccess;
     hipLaunchKernelGGL(prep_w4_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, packed, d_out, d_in,
                        reinterpret_cast<uint32_t*>(tiled));
