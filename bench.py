@@ -118,6 +118,10 @@ def main():
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f}s")
 
+    # One step: every linear's prologue (route, bucket, quantize, adapter inputs) then its
+    # GEMM, in layer order on one stream.  (Running the next prologue on a second stream
+    # under the GEMM was measured slower: the GEMM occupies every CU and the prologue
+    # kernels only get the gaps.)
     def step(ev=None):
         for i, (spec, layer) in enumerate(layers):
             b = bufs[i]

@@ -10,6 +10,9 @@
 // the routed expert with the smallest predicted error); thelatestinai.com
 // listing, Table 7 (dense adapters, one d x N_r router map per token).
 
+#include <algorithm>
+
+#include "qe_dma.h"
 #include "qe_internal.h"
 
 namespace qe {
@@ -395,6 +398,486 @@ hipError_t launch_xproj_finish(const float* part, int ksplit, int T, int ncols_p
     hipLaunchKernelGGL(xproj_finish_kernel, dim3(T), dim3(1024), 4 * (size_t)ncols_pad * sizeof(float), st, part, ksplit, T,
                        ncols_pad, rel(se_col), r_s, rs_pad, rel(re_col), n_r, r_r, rr_pad, rel(router_col), expert_in,
                        scores, expert_out, u, v);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------- two-pass prologue (prefill)
+// Pass 1 (route_pass): one read of x gives, per token and K split, the shared-expert and
+// router projections (the first `ncols` rows of Mt: A_s^T, then R^T padded to 16 rows)
+// and the partial max |x / s|.  route_finish turns them into the routed expert, u and
+// s_x.  Pass 2 (expert_quant) walks the tokens in expert-sorted tiles and, in a second
+// read of x, writes the activation codes and the selected routed expert's input v.
+
+// raw storage of 8 consecutive activations, loaded ahead of use
+template <int XDT>
+struct Raw8;
+template <>
+struct Raw8<QE_BF16> {
+    v4u b;
+    __device__ void load(const void* x, size_t idx) { b = *reinterpret_cast<const v4u*>(reinterpret_cast<const uint16_t*>(x) + idx); }
+    __device__ void zero() { b = v4u{0, 0, 0, 0}; }
+    __device__ void get(float out[8]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = __uint_as_float(b[i] << 16);
+            out[2 * i + 1] = __uint_as_float(b[i] & 0xFFFF0000u);
+        }
+    }
+};
+template <>
+struct Raw8<QE_F32> {
+    v4f a, b;
+    __device__ void load(const void* x, size_t idx) {
+        const v4f* p = reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(x) + idx);
+        a = p[0];
+        b = p[1];
+    }
+    __device__ void zero() { a = b = v4f{0, 0, 0, 0}; }
+    __device__ void get(float out[8]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[i] = a[i];
+            out[4 + i] = b[i];
+        }
+    }
+};
+
+__device__ inline v4u pack_bf16x8(const float v[8]) {
+    v4u r;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = f32_to_bf16_bits(v[2 * q]) | (f32_to_bf16_bits(v[2 * q + 1]) << 16);
+    return r;
+}
+
+constexpr int RP_TOK = 64;             // tokens per workgroup
+constexpr int RP_KC = 64;              // K chunk staged in LDS
+constexpr int RP_LD = RP_KC * 2 + 16;  // LDS row stride (bytes)
+constexpr int RP_MAXN = 5;             // up to 80 projected columns
+constexpr int RP_MCH = (RP_MAXN * 16 * 8 + 255) / 256;  // Mt chunks per thread
+
+template <int XDT>
+__global__ __launch_bounds__(256) void route_pass_kernel(const void* __restrict__ x, int T, int d_in,
+                                                         const uint16_t* __restrict__ mt, int ncols,
+                                                         const float* __restrict__ smooth,
+                                                         const float* __restrict__ inv_smooth, int ksplit,
+                                                         float* __restrict__ part, float* __restrict__ amax_part) {
+    __shared__ __attribute__((aligned(16))) uint8_t xs[RP_TOK * RP_LD];
+    __shared__ __attribute__((aligned(16))) uint8_t ms[RP_MAXN * 16 * RP_LD];
+    const int tok0 = blockIdx.x * RP_TOK, ks = blockIdx.y;
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int nch = d_in / RP_KC;
+    const int kbeg = (int)((long)ks * nch / ksplit) * RP_KC, kend = (int)((long)(ks + 1) * nch / ksplit) * RP_KC;
+    const int nbk = ncols / 16;
+    const int c8 = tid & 7;
+    int trow[2];
+    bool tval[2];
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        trow[p] = tok0 + (tid >> 3) + 32 * p;
+        tval[p] = trow[p] < T;
+    }
+
+    v4f acc[RP_MAXN];
+#pragma unroll
+    for (int n = 0; n < RP_MAXN; ++n) acc[n] = v4f{0, 0, 0, 0};
+    float amax[2] = {0.0f, 0.0f};
+
+    // registers holding the next chunk: two x groups of 8, up to RP_MCH Mt groups of 8
+    Raw8<XDT> xr[2];
+    v4u mr[RP_MCH];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            if (tval[p]) xr[p].load(x, (size_t)trow[p] * d_in + k0 + c8 * 8);
+            else xr[p].zero();
+        }
+#pragma unroll
+        for (int j = 0; j < RP_MCH; ++j) {
+            const int i = tid + 256 * j, r = i >> 3;
+            if (r < ncols) mr[j] = *reinterpret_cast<const v4u*>(mt + (size_t)r * d_in + k0 + (i & 7) * 8);
+        }
+    };
+    if (kbeg < kend) fetch(kbeg);
+    for (int k0 = kbeg; k0 < kend; k0 += RP_KC) {
+        __syncthreads();  // previous chunk's MFMAs are done with the LDS tiles
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            float v[8];
+            xr[p].get(v);
+            *reinterpret_cast<v4u*>(xs + ((tid >> 3) + 32 * p) * RP_LD + c8 * 16) = pack_bf16x8(v);
+            if (tval[p]) {
+                smooth8<true>(smooth, inv_smooth, k0 + c8 * 8, v);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) amax[p] = fmaxf(amax[p], __builtin_fabsf(v[i]));
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RP_MCH; ++j) {
+            const int i = tid + 256 * j, r = i >> 3;
+            if (r < ncols) *reinterpret_cast<v4u*>(ms + r * RP_LD + (i & 7) * 16) = mr[j];
+        }
+        __syncthreads();
+        if (k0 + RP_KC < kend) fetch(k0 + RP_KC);  // in flight during the MFMAs
+#pragma unroll
+        for (int s = 0; s < RP_KC / 32; ++s) {
+            const v8bf a = *reinterpret_cast<const v8bf*>(xs + (wid * 16 + lr) * RP_LD + (s * 32 + lg * 8) * 2);
+#pragma unroll
+            for (int n = 0; n < RP_MAXN; ++n) {
+                if (n >= nbk) break;
+                const v8bf b = *reinterpret_cast<const v8bf*>(ms + (n * 16 + lr) * RP_LD + (s * 32 + lg * 8) * 2);
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[n], 0, 0, 0);
+            }
+        }
+    }
+    float* out = part + (size_t)ks * T * ncols;
+#pragma unroll
+    for (int n = 0; n < RP_MAXN; ++n) {
+        if (n >= nbk) break;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int t = tok0 + wid * 16 + lg * 4 + r;
+            if (t < T) out[(size_t)t * ncols + n * 16 + lr] = acc[n][r];
+        }
+    }
+    // the 8 threads of a token row are 8 consecutive lanes
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+        float m = amax[p];
+        m = fmaxf(m, __shfl_xor(m, 1, 64));
+        m = fmaxf(m, __shfl_xor(m, 2, 64));
+        m = fmaxf(m, __shfl_xor(m, 4, 64));
+        if (c8 == 0 && tval[p]) amax_part[(size_t)ks * T + trow[p]] = m;
+    }
+}
+
+int route_pass_ksplit(int T, int d_in) {
+    const int tiles = (T + RP_TOK - 1) / RP_TOK;
+    const int ks = std::min((1024 + tiles - 1) / tiles, std::max(1, d_in / 256));
+    return std::max(ks, 1);
+}
+
+hipError_t launch_route_pass(const void* x, int x_dtype, int T, int d_in, const uint16_t* mt, int ncols,
+                             const float* smooth, const float* inv_smooth, int ksplit, float* part, float* amax_part,
+                             hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (ncols > RP_MAXN * 16 || ncols % 16 || d_in % RP_KC || !smooth || !inv_smooth) return hipErrorInvalidValue;
+    const dim3 grid((T + RP_TOK - 1) / RP_TOK, ksplit);
+    if (x_dtype == QE_BF16)
+        hipLaunchKernelGGL(route_pass_kernel<QE_BF16>, grid, dim3(256), 0, st, x, T, d_in, mt, ncols, smooth,
+                           inv_smooth, ksplit, part, amax_part);
+    else
+        hipLaunchKernelGGL(route_pass_kernel<QE_F32>, grid, dim3(256), 0, st, x, T, d_in, mt, ncols, smooth,
+                           inv_smooth, ksplit, part, amax_part);
+    return hipGetLastError();
+}
+
+// One wave per token: fixed-order split-K sums, router argmin (lowest index on ties),
+// u = bf16(shared projection), s_x = max |x/s| / qmax (a max is exact in any order).
+__global__ __launch_bounds__(256) void route_finish_kernel(const float* __restrict__ part,
+                                                           const float* __restrict__ amax_part, int ksplit, int T,
+                                                           int ncols, int r_s, int rs_pad, int router_col, int n_r,
+                                                           int qmax, int32_t* __restrict__ expert,
+                                                           uint16_t* __restrict__ u, float* __restrict__ s_x) {
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (t >= T) return;
+    // columns lane and lane + 64 (ncols <= 80)
+    float sum[2] = {0.0f, 0.0f};
+    const size_t stride = (size_t)T * ncols;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int c = lane + 64 * j;
+        if (c < ncols) {
+            const float* p = part + (size_t)t * ncols + c;
+            for (int k = 0; k < ksplit; ++k) sum[j] += p[(size_t)k * stride];
+        }
+    }
+    if (router_col >= 0) {
+        float best = __builtin_inff();
+        int bi = 1 << 30;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {  // lane's own candidates, lower column first
+            const int c = lane + 64 * j;
+            if (c >= router_col && c < router_col + n_r && (sum[j] < best || bi == 1 << 30)) {
+                best = sum[j];
+                bi = c - router_col;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ob = __shfl_xor(best, off, 64);
+            const int oi = __shfl_xor(bi, off, 64);
+            if (ob < best || (ob == best && oi < bi)) {
+                best = ob;
+                bi = oi;
+            }
+        }
+        if (lane == 0) expert[t] = bi;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int c = lane + 64 * j;
+        if (u && c < rs_pad) u[(size_t)t * rs_pad + c] = c < r_s ? (uint16_t)f32_to_bf16_bits(sum[j]) : (uint16_t)0;
+    }
+    float m = 0.0f;
+    for (int k = lane; k < ksplit; k += 64) m = fmaxf(m, amax_part[(size_t)k * T + t]);
+    m = wave_max(m);
+    if (lane == 0) s_x[t] = m / (float)qmax;
+}
+
+hipError_t launch_route_finish(const float* part, const float* amax_part, int ksplit, int T, int ncols, int r_s,
+                               int rs_pad, int router_col, int n_r, int a_bits, int32_t* expert, uint16_t* u,
+                               float* s_x, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(route_finish_kernel, dim3((T + 3) / 4), dim3(256), 0, st, part, amax_part, ksplit, T, ncols,
+                       r_s, rs_pad, router_col, n_r, (1 << (a_bits - 1)) - 1, expert, u, s_x);
+    return hipGetLastError();
+}
+
+// Pass 2.  A workgroup takes 128 token rows in `perm` order (tokens grouped by expert),
+// one 16-row block per wave, and a K range walked in 32-wide steps by all 8 waves
+// together.  Per step a lane owns 8 consecutive channels of one row: it writes their
+// codes (x / s, then / s_x, round half to even, clamp -- the float32 operations of the
+// activation quantization kernel) and feeds bf16(x) to the MFMAs of v = x . A_e.  The
+// experts present in the tile are taken up to 8/NBR at a time; each MFMA sees only the
+// rows of its expert (A masked), so one accumulator collects every row's own expert
+// exactly.  x, the expert fragments (shared by the 8 row blocks) and the smoothing
+// factors of each step reach LDS by DMA through a 4-stage ring, three steps ahead,
+// with explicit waits and no staging registers.  With K split over workgroups the
+// partial v go to `vpart` and vpart_finish adds them in K order.
+constexpr int EQ_W = 8;              // waves per workgroup
+constexpr int EQ_ROWS = 16 * EQ_W;   // token rows per workgroup
+constexpr int EQ_NS = 4;             // ring stages
+
+template <int XDT, int NBR>
+__global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
+    const void* __restrict__ x, int T, int d_in, const float* __restrict__ smooth,
+    const float* __restrict__ inv_smooth, const float* __restrict__ s_x, int qmax, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ expert, int n_r, const uint16_t* __restrict__ mt_re, int r_r, int ksq,
+    float* __restrict__ vpart, int8_t* __restrict__ codes, uint16_t* __restrict__ v) {
+    constexpr int XOPS = XDT == QE_BF16 ? 1 : 2;  // 1 KB copies of x per wave and step
+    constexpr int RR = NBR * 16;                  // padded routed rank
+    constexpr int ESLOTS = NBR ? EQ_W / NBR : 1;  // experts per pass
+    constexpr int X_STAGE = EQ_W * XOPS * 1024;
+    constexpr int B_STAGE = NBR ? EQ_W * 1024 : 0;
+    constexpr int S_STAGE = EQ_W * 256;
+    constexpr int STAGE = X_STAGE + B_STAGE + S_STAGE;
+    constexpr int OPS = XOPS + (NBR ? 1 : 0) + 1;  // DMA instructions per wave and step
+    constexpr int ESZ = XDT == QE_BF16 ? 2 : 4;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[EQ_NS * STAGE];
+    __shared__ uint32_t s_pres[EQ_W];
+
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int tile = blockIdx.x, kq = blockIdx.y;
+    const int pos0 = tile * EQ_ROWS;
+    const int pos = pos0 + wid * 16 + lr;
+    const bool valid = pos < T;
+    const int t = valid ? (perm ? perm[pos] : pos) : 0;  // rows past T read row 0 and are never stored
+    const int e_row = (NBR && valid && expert) ? min(max(expert[t], 0), n_r - 1) : -1;
+    const float sx = valid ? s_x[t] : 0.0f;
+    const float inv_sx = sx != 0.0f ? 1.0f / sx : 0.0f;
+    const bool fast = sx >= 0x1p-90f && sx <= 0x1p90f;
+    const float fq = (float)qmax;
+    uint32_t pres = 0;
+    if (NBR)
+        for (int e = 0; e < n_r; ++e)
+            if (__ballot(e_row == e)) pres |= 1u << e;
+    if (lane == 0) s_pres[wid] = pres;
+    __syncthreads();
+    uint32_t present = 0;
+#pragma unroll
+    for (int w = 0; w < EQ_W; ++w) present |= s_pres[w];
+
+    const int nsteps = d_in / 32;
+    const int g0 = (int)((long)kq * nsteps / ksq), g1 = (int)((long)(kq + 1) * nsteps / ksq);
+    const int nst = g1 - g0;  // >= 1: ksq <= nsteps
+    const uint32_t lds0 = lds_addr(smem);
+    const char* xsrc = reinterpret_cast<const char*>(x) + ((size_t)t * d_in + lg * 8) * ESZ;
+    const float* ssrc = lane < 32 ? smooth + lane : inv_smooth + (lane - 32);
+    int8_t* crow = codes + (size_t)t * d_in + lg * 8;
+
+    v4f acc[NBR ? NBR : 1];
+#pragma unroll
+    for (int n = 0; n < (NBR ? NBR : 1); ++n) acc[n] = v4f{0, 0, 0, 0};
+
+    uint32_t pm = present;
+    bool first = true;
+    do {  // passes over the present experts; the codes are written on the first
+        int ex[ESLOTS];
+#pragma unroll
+        for (int j = 0; j < ESLOTS; ++j) {
+            ex[j] = -1;
+            if (NBR && pm) {
+                ex[j] = __builtin_ctz(pm);
+                pm &= pm - 1;
+            }
+        }
+        // this wave's expert-fragment copy: slot wid / NBR, column block wid % NBR
+        int my_e = max(ex[0], 0);  // empty slots repeat a present expert (never used)
+#pragma unroll
+        for (int j = 1; j < ESLOTS; ++j)
+            if (j == wid / (NBR ? NBR : 1) && ex[j] >= 0) my_e = ex[j];
+        const uint16_t* bsrc =
+            NBR ? mt_re + ((size_t)my_e * RR + (wid % (NBR ? NBR : 1)) * 16 + lr) * d_in + lg * 8 : nullptr;
+        auto issue = [&](int stage, int step) {
+            const uint32_t base = lds0 + stage * STAGE;
+            const size_t k = (size_t)step * 32;
+#pragma unroll
+            for (int o = 0; o < XOPS; ++o) dma16(xsrc + k * ESZ + o * 16, base + (wid * XOPS + o) * 1024);
+            if (NBR) dma16(bsrc + k, base + X_STAGE + wid * 1024);
+            dma4(ssrc + k, base + X_STAGE + B_STAGE + wid * 256);
+        };
+#pragma unroll
+        for (int st = 0; st < EQ_NS - 1; ++st) issue(st, g0 + min(st, nst - 1));
+        QE_WAIT_VMCNT_LDS((EQ_NS - 2) * OPS);
+        QE_WG_BARRIER();
+
+        for (int i = 0; i < nst; ++i) {
+            // refill the slot consumed in the previous step (past the end: a harmless repeat)
+            issue((i + EQ_NS - 1) % EQ_NS, g0 + min(i + EQ_NS - 1, nst - 1));
+            const uint8_t* st = smem + (i % EQ_NS) * STAGE;
+            float xc[8];
+            if (XDT == QE_BF16) {
+                Raw8<QE_BF16> r;
+                r.b = *reinterpret_cast<const v4u*>(st + wid * 1024 + lane * 16);
+                r.get(xc);
+            } else {
+                Raw8<QE_F32> r;
+                r.a = *reinterpret_cast<const v4f*>(st + wid * 2048 + lane * 16);
+                r.b = *reinterpret_cast<const v4f*>(st + wid * 2048 + 1024 + lane * 16);
+                r.get(xc);
+            }
+            const uint8_t* sp = st + X_STAGE + B_STAGE + wid * 256 + lg * 32;
+            const v4f s0 = *reinterpret_cast<const v4f*>(sp), s1 = *reinterpret_cast<const v4f*>(sp + 16);
+            const v4f i0 = *reinterpret_cast<const v4f*>(sp + 128), i1 = *reinterpret_cast<const v4f*>(sp + 144);
+            const v4u abits = pack_bf16x8(xc);
+            if (first) {
+                // codes: x' = x / s, q = clamp(rint(x' / s_x))
+                float xs8[8];
+                bool ok = true;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const float sq = q < 4 ? s0[q] : s1[q - 4], iq = q < 4 ? i0[q] : i1[q - 4];
+                    xs8[q] = div_markstein(xc[q], sq, iq);
+                    ok = ok && in_markstein_range(xc[q]);
+                }
+                if (__builtin_expect(__any(!ok), 0)) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const float sq = q < 4 ? s0[q] : s1[q - 4];
+                        if (!in_markstein_range(xc[q])) xs8[q] = xc[q] / sq;
+                    }
+                }
+                uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    float qv = 0.0f;
+                    if (sx != 0.0f) {
+                        const float r = fast ? div_markstein(xs8[q], sx, inv_sx) : xs8[q] / sx;
+                        qv = fminf(fmaxf(__builtin_rintf(r), -fq), fq);
+                    }
+                    packed[q >> 2] |= ((uint32_t)(int32_t)qv & 0xFFu) << (8 * (q & 3));
+                }
+                if (valid) *reinterpret_cast<v2u*>(crow + (size_t)(g0 + i) * 32) = v2u{packed[0], packed[1]};
+            }
+            if (NBR) {
+                const v4u zero4 = v4u{0, 0, 0, 0};
+#pragma unroll
+                for (int j = 0; j < ESLOTS; ++j) {
+                    if (ex[j] < 0) break;  // uniform
+                    const v4u am = e_row == ex[j] ? abits : zero4;
+#pragma unroll
+                    for (int n = 0; n < (NBR ? NBR : 1); ++n) {
+                        const v8bf bq = *reinterpret_cast<const v8bf*>(st + X_STAGE + (j * NBR + n) * 1024 + lane * 16);
+                        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const v8bf*>(&am), bq,
+                                                                         acc[n], 0, 0, 0);
+                    }
+                }
+            }
+            // the slot read here is the DMA target of the next step: every LDS read must
+            // have completed (lgkmcnt 0); and step i+1 must have landed
+            __builtin_amdgcn_sched_barrier(0);
+            QE_WAIT_VMCNT_LDS((EQ_NS - 2) * OPS);
+            QE_WG_BARRIER();
+        }
+        QE_WAIT_VMCNT(0);  // the repeated tail copies, before the ring is refilled or freed
+        QE_WG_BARRIER();
+        first = false;
+    } while (pm);
+    if (NBR == 0 || !v) return;
+
+    // lane holds column n*16 + lr and rows 4*lg + r of the wave's block
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = lg * 4 + r;
+        const int tt = __shfl(valid ? t : -1, row, 64);
+        const int p = pos0 + wid * 16 + row;
+#pragma unroll
+        for (int n = 0; n < (NBR ? NBR : 1); ++n) {
+            const int c = n * 16 + lr;
+            if (ksq == 1) {
+                if (tt >= 0) v[(size_t)tt * RR + c] = c < r_r ? (uint16_t)f32_to_bf16_bits(acc[n][r]) : (uint16_t)0;
+            } else if (p < T) {
+                vpart[((size_t)kq * T + p) * RR + c] = acc[n][r];
+            }
+        }
+    }
+}
+
+// v[perm[pos]][c] = bf16(sum over q, in order, of vpart[q][pos][c])
+__global__ __launch_bounds__(256) void vpart_finish_kernel(const float* __restrict__ vpart, int ksq, int T, int rr_pad,
+                                                           int r_r, const int32_t* __restrict__ perm,
+                                                           uint16_t* __restrict__ v) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)T * rr_pad) return;
+    const int pos = (int)(idx / rr_pad), c = (int)(idx % rr_pad);
+    float a = 0.0f;
+    for (int q = 0; q < ksq; ++q) a += vpart[(size_t)q * T * rr_pad + idx];
+    const int tt = perm ? perm[pos] : pos;
+    v[(size_t)tt * rr_pad + c] = c < r_r ? (uint16_t)f32_to_bf16_bits(a) : (uint16_t)0;
+}
+
+int expert_quant_ksplit(int T, int d_in) {
+    const int tiles = (T + EQ_ROWS - 1) / EQ_ROWS;
+    const int ks = std::min((512 + tiles - 1) / tiles, std::max(1, d_in / 32 / 8));
+    return std::max(ks, 1);
+}
+
+template <int XDT>
+static hipError_t launch_eq(dim3 grid, hipStream_t st, int nbr, const void* x, int T, int d_in, const float* smooth,
+                            const float* inv_smooth, const float* s_x, int qmax, const int32_t* perm,
+                            const int32_t* expert, int n_r, const uint16_t* mt_re, int r_r, int ksq, float* vpart,
+                            int8_t* codes, uint16_t* v) {
+#define QE_EQ_LAUNCH(NB)                                                                                            \
+    hipLaunchKernelGGL((expert_quant_kernel<XDT, NB>), grid, dim3(64 * EQ_W), 0, st, x, T, d_in, smooth,           \
+                       inv_smooth, s_x, qmax, perm, expert, n_r, mt_re, r_r, ksq, vpart, codes, v)
+    if (nbr == 0) QE_EQ_LAUNCH(0);
+    else if (nbr == 2) QE_EQ_LAUNCH(2);
+    else QE_EQ_LAUNCH(4);
+#undef QE_EQ_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_expert_quant(const void* x, int x_dtype, int T, int d_in, const float* smooth,
+                               const float* inv_smooth, const float* s_x, int a_bits, const int32_t* perm,
+                               const int32_t* expert, int n_r, const uint16_t* mt_re, int rr_pad, int r_r, int ksq,
+                               float* vpart, int8_t* codes, uint16_t* v, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    const int nbr = (expert && v) ? rr_pad / 16 : 0;
+    if ((nbr != 0 && nbr != 2 && nbr != 4) || d_in % 32 || ksq < 1 || ksq > d_in / 32 || n_r > kMaxRouted || !smooth ||
+        !inv_smooth)
+        return hipErrorInvalidValue;
+    if (ksq > 1 && nbr && !vpart) return hipErrorInvalidValue;
+    const dim3 grid((T + EQ_ROWS - 1) / EQ_ROWS, ksq);
+    const int qmax = (1 << (a_bits - 1)) - 1;
+    hipError_t err = x_dtype == QE_BF16
+                         ? launch_eq<QE_BF16>(grid, st, nbr, x, T, d_in, smooth, inv_smooth, s_x, qmax, perm, expert,
+                                              n_r, mt_re, r_r, ksq, vpart, codes, v)
+                         : launch_eq<QE_F32>(grid, st, nbr, x, T, d_in, smooth, inv_smooth, s_x, qmax, perm, expert,
+                                             n_r, mt_re, r_r, ksq, vpart, codes, v);
+    if (err != hipSuccess || ksq == 1 || !nbr) return err;
+    const size_t n = (size_t)T * rr_pad;
+    hipLaunchKernelGGL(vpart_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, vpart, ksq, T, rr_pad,
+                       r_r, perm, v);
     return hipGetLastError();
 }
 

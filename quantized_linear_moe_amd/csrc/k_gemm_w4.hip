@@ -30,6 +30,7 @@
 //     16x16x32 steps accumulate u.B_s and, for every routed expert present in
 //     the tile, (v masked to that expert's tokens).B_e on top of it.
 
+#include "qe_dma.h"
 #include "qe_internal.h"
 
 namespace qe {
@@ -52,22 +53,6 @@ __device__ inline v4i unpack_w4x16(uint32_t p0, uint32_t p1) {
 // A tile rows are 64 bytes (four 16-byte chunks); chunk c of row r is stored at
 // c ^ ((r >> 1) & 3), which spreads the 16-byte reads of 8 consecutive rows over all banks.
 __device__ inline int a_swz(int row) { return (row >> 1) & 3; }
-
-// 16-byte global -> LDS copy by DMA (global_load_lds_dwordx4): lane i writes LDS bytes
-// [lds_base + 16 i, +16) of this wave's 1 KB block.  Issued as inline asm so that the
-// compiler inserts no waits of its own; the kernel waits with explicit vmcnt counts.
-__device__ inline void dma16(const void* src, uint32_t lds_base) {
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds_base) : "memory");
-}
-#define QE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-// vmcnt <= n and every LDS read of this wave completed (lgkmcnt 0)
-#define QE_WAIT_VMCNT_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
-#define QE_WG_BARRIER()                   \
-    do {                                  \
-        asm volatile("" ::: "memory");    \
-        __builtin_amdgcn_s_barrier();     \
-        asm volatile("" ::: "memory");    \
-    } while (0)
 
 // MB: 16-row M blocks per workgroup (tile MB*16 tokens x 256 channels).  Tile rows are
 // positions in `perm` order when perm != NULL (tokens grouped by routed expert, so a
@@ -97,7 +82,7 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
         pos = min(pos, T - 1);
         return perm ? perm[pos] : pos;
     };
-    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)smem;
+    const uint32_t lds0 = lds_addr(smem);
 
     // DMA sources.  A: copy q = wid + 4p covers tile rows 16q..16q+15; lane i fetches the
     // logical chunk stored at its LDS slot (row 16q + i/4, slot i%4).

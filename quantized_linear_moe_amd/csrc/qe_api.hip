@@ -96,9 +96,14 @@ int ensure_attributes() {
     return QE_OK;
 }
 
+}  // namespace
+
+namespace qe {
 constexpr int kSkinnyMaxT = 16;  // token counts served by the weight-streaming kernels
 
-}  // namespace
+// Prefill prologue in two reads of x (route pass, then expert-sorted quantization)
+bool use_two_pass(const qe_linear* lin, int T) { return lin->a_bits != 16 && T > kSkinnyMaxT; }
+}  // namespace qe
 
 namespace qe {
 
@@ -108,10 +113,14 @@ PrepLayout prep_layout(const qe_linear* lin) {
     L.rs_pad = rank_pad(lin->r_shared);
     L.rr_pad = lin->n_routed > 0 ? rank_pad(lin->r_routed) : 0;
     L.has_smooth = lin->a_bits != 16;
+    // Mt rows: [A_s^T (rs_pad) ; R^T (padded to 16) ; A_1^T .. A_N^T (rr_pad each)], so
+    // the shared expert and the router form one leading block of at most 80 rows
+    const int router_pad = lin->n_routed > 0 ? (lin->n_routed + 15) / 16 * 16 : 0;
     L.col_se = L.rs_pad > 0 ? 0 : -1;
-    L.col_re = lin->n_routed > 0 ? L.rs_pad : -1;
-    L.col_router = lin->n_routed > 0 ? L.rs_pad + lin->n_routed * L.rr_pad : -1;
-    L.n_cols = L.rs_pad + lin->n_routed * L.rr_pad + lin->n_routed;
+    L.col_router = lin->n_routed > 0 ? L.rs_pad : -1;
+    L.col_re = lin->n_routed > 0 ? L.rs_pad + router_pad : -1;
+    L.n_lead = L.rs_pad + router_pad;
+    L.n_cols = L.n_lead + lin->n_routed * L.rr_pad;
     L.n_cols_pad = (L.n_cols + 15) / 16 * 16;
     size_t off = 0;
     L.w_tiled = off;
@@ -146,7 +155,15 @@ WsLayout ws_layout(const qe_linear* lin, int T) {
     off = align256(off + t * 4);
     W.part = off;
     const int xks = std::max(W.xproj_ksplit, T <= kSkinnyMaxT ? skinny_ksplit_proj(lin->d_in) : 1);
-    off = align256(off + (size_t)xks * t * P.n_cols_pad * 4);
+    const bool two_pass = use_two_pass(lin, T);
+    W.rp_ksplit = two_pass ? route_pass_ksplit(T, lin->d_in) : 0;
+    W.eq_ksplit = two_pass ? expert_quant_ksplit(T, lin->d_in) : 0;
+    off = align256(off + std::max((size_t)xks * t * P.n_cols_pad, (size_t)W.rp_ksplit * t * P.n_lead) * 4);
+    W.amax = off;
+    off = align256(off + (size_t)W.rp_ksplit * t * 4);
+    W.vpart = off;
+    off = align256(off + (W.eq_ksplit > 1 ? (size_t)W.eq_ksplit * t * P.rr_pad * 4 : 0));
+
     W.scores = off;
     off = align256(off + t * std::max(lin->n_routed, 1) * 4);
     W.expert = off;
@@ -277,7 +294,7 @@ int qe_prepare(const qe_linear* lin, const void* w_packed, const float* w_scale,
     QE_TRY_HIP(hipMemcpyAsync(at<void>(prep, L.w_scale), w_scale, (size_t)d_out * 4, hipMemcpyDeviceToDevice, s));
     if (L.has_smooth)
         QE_TRY_HIP(launch_prep_smooth(smooth, d_in, at<float>(prep, L.smooth), at<float>(prep, L.inv_smooth), s));
-    // Mt: [A_s^T ; A_1^T .. A_N^T ; R^T ; zero rows]
+    // Mt: [A_s^T ; R^T ; A_1^T .. A_N^T], zero rows in the padding
     uint16_t* mt = at<uint16_t>(prep, L.mt);
     QE_TRY_HIP(launch_fill_zero(mt, (size_t)L.n_cols_pad * d_in * 2, s));
     if (L.rs_pad > 0) QE_TRY_HIP(launch_prep_transpose(A_s, d_in, lin->r_shared, mt + (size_t)L.col_se * d_in, d_in, L.rs_pad, s));
@@ -452,6 +469,24 @@ static int run_prologue(const qe_linear* lin, const void* x, int x_dtype, int T,
     const PrepLayout P = prep_layout(lin);
     const WsLayout W = ws_layout(lin, T);
     const bool route = lin->n_routed > 0;
+    if (use_two_pass(lin, T)) {
+        const float* smooth = at<const float>(lin->prep, P.smooth);
+        const float* inv_smooth = at<const float>(lin->prep, P.inv_smooth);
+        const uint16_t* mt = at<const uint16_t>(lin->prep, P.mt);
+        QE_TRY_HIP(launch_route_pass(x, x_dtype, T, lin->d_in, mt, P.n_lead, smooth, inv_smooth, W.rp_ksplit,
+                                     at<float>(ws, W.part), at<float>(ws, W.amax), s));
+        QE_TRY_HIP(launch_route_finish(at<const float>(ws, W.part), at<const float>(ws, W.amax), W.rp_ksplit, T,
+                                       P.n_lead, lin->r_shared, P.rs_pad, P.col_router, lin->n_routed, lin->a_bits,
+                                       route ? expert : nullptr, u, s_x, s));
+        if (route && perm)
+            QE_TRY_HIP(launch_bucket(expert, T, lin->n_routed, at<int32_t>(ws, W.counts), at<int32_t>(ws, W.offsets),
+                                     perm, s));
+        QE_TRY_HIP(launch_expert_quant(x, x_dtype, T, lin->d_in, smooth, inv_smooth, s_x, lin->a_bits,
+                                       route ? perm : nullptr, route ? expert : nullptr, lin->n_routed,
+                                       route ? mt + (size_t)P.col_re * lin->d_in : nullptr, P.rr_pad, lin->r_routed,
+                                       W.eq_ksplit, at<float>(ws, W.vpart), codes, route ? v : nullptr, s));
+        return QE_OK;
+    }
     int st = run_xpass(lin, x, x_dtype, T, u != nullptr, route, route, nullptr, nullptr, route ? expert : nullptr, u,
                        v, ws, s);
     if (st) return st;

@@ -30,12 +30,13 @@ struct PrepLayout {
     size_t w_tiled, w_tiled_bytes;  // main weights in the kernel layout
     size_t w_scale;                 // float [d_out]
     size_t smooth, inv_smooth;      // float [d_in] each (0 bytes when a_bits == 16)
-    size_t mt;                      // bf16 [n_cols_pad][d_in]: A_s^T, A_1^T..A_N^T, R^T, zero rows
+    size_t mt;                      // bf16 [n_cols_pad][d_in]: A_s^T, R^T (16-row padded), A_1^T..A_N^T
     size_t bt_s;                    // bf16 [d_out][rs_pad]  (B_s transposed, zero padded)
     size_t bt_r;                    // bf16 [N_r][d_out][rr_pad]
     size_t total;
     int rs_pad, rr_pad;
     int col_se, col_re, col_router;  // first row of each block inside mt
+    int n_lead;                      // rows of the leading block (shared expert + router)
     int n_cols, n_cols_pad;
     bool has_smooth;
 };
@@ -53,12 +54,16 @@ struct WsLayout {
     size_t u;           // bf16 [T][rs_pad]
     size_t v;           // bf16 [T][rr_pad]
     size_t skinny;      // float [ksplit][T][d_out]   (decode split-K partials)
+    size_t amax;        // float [rp_ksplit][T]       (route pass: partial max |x/s|)
+    size_t vpart;       // float [eq_ksplit][T][rr_pad] (expert-quant split-K partials)
     size_t total;
     int xproj_ksplit;
     int skinny_ksplit;
+    int rp_ksplit, eq_ksplit;  // 0 unless the two-pass prefill prologue is used
 };
 
 PrepLayout prep_layout(const qe_linear* lin);
+bool use_two_pass(const qe_linear* lin, int T);
 WsLayout ws_layout(const qe_linear* lin, int T);
 
 // ----------------------------------------------------------- launch wrappers
@@ -76,6 +81,20 @@ hipError_t launch_xproj_finish(const float* part, int ksplit, int T, int ncols_p
                                int r_s, int rs_pad, int re_col, int n_r, int r_r, int rr_pad, int router_col,
                                const int32_t* expert_in, float* scores, int32_t* expert_out, uint16_t* u,
                                uint16_t* v, hipStream_t st);
+
+// two-pass prefill prologue
+hipError_t launch_route_pass(const void* x, int x_dtype, int T, int d_in, const uint16_t* mt, int ncols,
+                             const float* smooth, const float* inv_smooth, int ksplit, float* part, float* amax_part,
+                             hipStream_t st);
+int route_pass_ksplit(int T, int d_in);
+hipError_t launch_route_finish(const float* part, const float* amax_part, int ksplit, int T, int ncols, int r_s,
+                               int rs_pad, int router_col, int n_r, int a_bits, int32_t* expert, uint16_t* u,
+                               float* s_x, hipStream_t st);
+hipError_t launch_expert_quant(const void* x, int x_dtype, int T, int d_in, const float* smooth,
+                               const float* inv_smooth, const float* s_x, int a_bits, const int32_t* perm,
+                               const int32_t* expert, int n_r, const uint16_t* mt_re, int rr_pad, int r_r, int ksq,
+                               float* vpart, int8_t* codes, uint16_t* v, hipStream_t st);
+int expert_quant_ksplit(int T, int d_in);
 
 hipError_t launch_bucket(const int32_t* expert, int T, int n_r, int32_t* counts, int32_t* offsets,
                          int32_t* perm, hipStream_t st);

@@ -288,6 +288,76 @@ def test_adapter_inputs_and_unfused_routed(Q):
     check_y(y.cpu().numpy(), ref, params, x, cfg.w_bits, cfg.a_bits, gpu_expert=e)
 
 
+# ------------------------------------------------- a1/a4/a5/a6 fused prologue
+def _check_prologue(Q, layer, params, x, a_bits, n_r, r_s, r_r):
+    """qe_linear_prologue on x: codes and s_x bit-exact, routes exact except near-ties,
+    perm the stable bucketing of the routes, u / v within bf16 rounding of the fp64 sums."""
+    T, d_in = x.shape
+    xd = x.to(DEV)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    codes = torch.empty(T, d_in, dtype=torch.int8, device=DEV)
+    s_x = torch.empty(T, dtype=torch.float32, device=DEV)
+    u = torch.empty(T, Q.libqe.rank_pad(r_s), dtype=torch.bfloat16, device=DEV) if r_s else None
+    v = torch.empty(T, Q.libqe.rank_pad(r_r), dtype=torch.bfloat16, device=DEV) if n_r else None
+    expert = torch.empty(T, **i32) if n_r else None
+    perm = torch.empty(T, **i32) if n_r else None
+    ws = layer.workspace(T)
+    Q.libqe.qe_linear_prologue(layer.lin, xd, codes, s_x, u, v, expert, ws, perm=perm)
+    torch.cuda.synchronize()
+    q_ref, sx_ref = O.quant_act(f32(x), params["s"], a_bits)
+    assert np.array_equal(s_x.cpu().numpy().view(np.uint32), sx_ref.view(np.uint32))
+    assert np.array_equal(codes.cpu().numpy(), q_ref)
+    xb = f32(x).astype(np.float64) if x.dtype == torch.bfloat16 else O.bf16_round(f32(x)).astype(np.float64)
+
+    def close(got, want):
+        err = np.abs(got.astype(np.float64) - want)
+        assert np.all(err <= 2.0 ** -8 * np.abs(want) + 1e-3 * max(float(np.max(np.abs(want))), 1e-30))
+
+    if r_s:
+        close(f32(u)[:, :r_s], xb @ f32(params["A_s"]).astype(np.float64))
+        assert not np.any(f32(u)[:, r_s:])
+    if n_r:
+        e = expert.cpu().numpy()
+        check_routing(O.route(xb, f32(params["R"])), e)
+        assert np.array_equal(perm.cpu().numpy(), np.argsort(e, kind="stable"))
+        A_r = f32(params["A_r"]).astype(np.float64)
+        v_ref = np.zeros((T, r_r))
+        for j in range(n_r):
+            idx = np.nonzero(e == j)[0]
+            v_ref[idx] = xb[idx] @ A_r[j]
+        close(f32(v)[:, :r_r], v_ref)
+        assert not np.any(f32(v)[:, r_r:])
+
+
+@pytest.mark.parametrize("cfg_name,lin_name", [("tiny", "lin"), ("qwen2vl_2b", "q"), ("qwen2vl_2b", "down"),
+                                               ("internvl2_8b", "gate"), ("qwen2vl_72b", "down")])
+def test_prologue_parity(Q, cfg_name, lin_name):
+    cfg = synth.get_config(cfg_name)
+    spec = _spec(cfg, lin_name)
+    layer, params = _layer(Q, cfg, spec)
+    x = synth.gen_activations(cfg, spec.stream)
+    _check_prologue(Q, layer, params, x, cfg.a_bits, cfg.n_routed, cfg.r_shared, cfg.r_routed)
+
+
+@pytest.mark.parametrize("T,r_s,n_r,r_r,x_dtype", [(17, 8, 4, 8, torch.bfloat16), (300, 8, 4, 8, torch.float32),
+                                                   (129, 0, 0, 0, torch.bfloat16), (70, 32, 0, 0, torch.float32),
+                                                   (50, 0, 3, 16, torch.bfloat16), (200, 64, 16, 48, torch.bfloat16)])
+def test_prologue_shapes(Q, T, r_s, n_r, r_r, x_dtype):
+    rng = np.random.default_rng(T)
+    d_in, d_out = 384, 272
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    params = dict(W_f=(rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32),
+                  s=rng.uniform(0.5, 2, d_in).astype(np.float32),
+                  A_s=bf(rng.standard_normal((d_in, r_s)) * 0.02) if r_s else None,
+                  B_s=bf(rng.standard_normal((r_s, d_out)) * 0.02) if r_s else None,
+                  A_r=bf(rng.standard_normal((n_r, d_in, r_r)) * 0.02) if n_r else None,
+                  B_r=bf(rng.standard_normal((n_r, r_r, d_out)) * 0.02) if n_r else None,
+                  R=bf(rng.standard_normal((d_in, n_r)) * 0.02) if n_r else None)
+    x = torch.from_numpy(rng.standard_normal((T, d_in)).astype(np.float32) * 2).to(x_dtype)
+    layer = Q.QELinear.from_params(params, 4, 6, device=DEV)
+    _check_prologue(Q, layer, params, x, 6, n_r, r_s, r_r)
+
+
 # ------------------------------------------------------------ a8 top-k
 @pytest.mark.parametrize("cfg_name,lin_name", [("tiny", "lin"), ("internvl2_8b", "q"), ("internvl2_8b", "down")])
 def test_channel_topk_bit_exact(Q, cfg_name, lin_name):
