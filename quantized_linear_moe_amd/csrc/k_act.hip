@@ -402,133 +402,165 @@ hipError_t launch_xproj_finish(const float* part, int ksplit, int T, int ncols_p
 }
 
 // ------------------------------------------------------- two-pass prologue (prefill)
-// Pass 1 (route_pass): one read of x gives, per token and K split, the shared-expert and
-// router projections (the first `ncols` rows of Mt: A_s^T, then R^T padded to 16 rows)
-// and the partial max |x / s|.  route_finish turns them into the routed expert, u and
-// s_x.  Pass 2 (expert_quant) walks the tokens in expert-sorted tiles and, in a second
-// read of x, writes the activation codes and the selected routed expert's input v.
+// For bf16 activations.  Pass 1 (route_pass): one read of x gives, per token and K
+// split, the shared-expert and router projections (the first `ncols` rows of Mt: A_s^T,
+// then R^T padded to 16 rows) and the partial max |x / s|.  route_finish turns them into
+// the routed expert, u and s_x.  Pass 2 (expert_quant) walks the tokens in expert-sorted
+// tiles and, in a second read of x, writes the activation codes and the selected routed
+// expert's input v.  Both passes move their operands global -> LDS by DMA through a
+// ring of stages with explicit waits, so no load is waited for in the step that uses
+// it, and keep per-element arithmetic to the exact float32 operations plus a packed
+// range check.
 
-// raw storage of 8 consecutive activations, loaded ahead of use
-template <int XDT>
-struct Raw8;
-template <>
-struct Raw8<QE_BF16> {
-    v4u b;
-    __device__ void load(const void* x, size_t idx) { b = *reinterpret_cast<const v4u*>(reinterpret_cast<const uint16_t*>(x) + idx); }
-    __device__ void zero() { b = v4u{0, 0, 0, 0}; }
-    __device__ void get(float out[8]) const {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            out[2 * i] = __uint_as_float(b[i] << 16);
-            out[2 * i + 1] = __uint_as_float(b[i] & 0xFFFF0000u);
-        }
-    }
-};
-template <>
-struct Raw8<QE_F32> {
-    v4f a, b;
-    __device__ void load(const void* x, size_t idx) {
-        const v4f* p = reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(x) + idx);
-        a = p[0];
-        b = p[1];
-    }
-    __device__ void zero() { a = b = v4f{0, 0, 0, 0}; }
-    __device__ void get(float out[8]) const {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            out[i] = a[i];
-            out[4 + i] = b[i];
-        }
-    }
-};
+typedef uint16_t v2u16 __attribute__((ext_vector_type(2)));
 
-__device__ inline v4u pack_bf16x8(const float v[8]) {
-    v4u r;
+__device__ inline void bf16x8_unpack(const v4u w, float o[8]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) r[q] = f32_to_bf16_bits(v[2 * q]) | (f32_to_bf16_bits(v[2 * q + 1]) << 16);
-    return r;
+    for (int q = 0; q < 4; ++q) {
+        o[2 * q] = __uint_as_float(w[q] << 16);
+        o[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+    }
 }
 
-constexpr int RP_TOK = 64;             // tokens per workgroup
-constexpr int RP_KC = 64;              // K chunk staged in LDS
-constexpr int RP_LD = RP_KC * 2 + 16;  // LDS row stride (bytes)
-constexpr int RP_MAXN = 5;             // up to 80 projected columns
-constexpr int RP_MCH = (RP_MAXN * 16 * 8 + 255) / 256;  // Mt chunks per thread
+// True when each of the 8 bf16 values is zero or has |x| in [2^-100, 2^100): the domain
+// where div_markstein(x, s, 1/s) is the correctly rounded x / s.  Two packed 16-bit
+// operations per value: the magnitudes' maximum bounds the exponent from above, the
+// minimum of (magnitude - 1) from below while letting zero through (it wraps to 0xFFFF).
+__device__ inline bool bf16x8_markstein_ok(const v4u w) {
+    v2u16 mx = v2u16{0, 0}, mn = v2u16{0xFFFF, 0xFFFF};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const v2u16 m = __builtin_bit_cast(v2u16, (uint32_t)(w[q] & 0x7FFF7FFFu));
+        mx = __builtin_elementwise_max(mx, m);
+        mn = __builtin_elementwise_min(mn, m - v2u16{1, 1});
+    }
+    constexpr uint16_t kHi = (226 << 7) | 0x7F;  // largest magnitude with exponent 2^99
+    constexpr uint16_t kLo = (27 << 7) - 1;      // (smallest magnitude 2^-100) - 1
+    return mx[0] <= kHi && mx[1] <= kHi && mn[0] >= kLo && mn[1] >= kLo;
+}
 
-template <int XDT>
-__global__ __launch_bounds__(256) void route_pass_kernel(const void* __restrict__ x, int T, int d_in,
+// x' = x / s for 8 values (x exact in bf16), correctly rounded
+__device__ inline void smooth_div8(const v4u w, const v4f s0, const v4f s1, const v4f i0, const v4f i1, float o[8]) {
+    float xv[8];
+    bf16x8_unpack(w, xv);
+    const bool ok = bf16x8_markstein_ok(w);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) o[q] = div_markstein(xv[q], q < 4 ? s0[q] : s1[q - 4], q < 4 ? i0[q] : i1[q - 4]);
+    if (__builtin_expect(__any(!ok), 0)) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (!in_markstein_range(xv[q])) o[q] = xv[q] / (q < 4 ? s0[q] : s1[q - 4]);
+    }
+}
+
+// Codes of 8 smoothed values: clamp(rint(x' / s_x), +-qmax) as int8.  The clamp is a
+// med3; adding 1.5 * 2^23 rounds the clamped value to an integer (round half to even,
+// the float adder's own rounding) and leaves it in the low mantissa bits, whose low
+// byte is the two's complement code.
+__device__ inline v2u codes8(const float xs[8], float sx, float inv_sx, bool fast, float fq) {
+    float r[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) r[q] = div_markstein(xs[q], sx, inv_sx);
+    if (__builtin_expect(__any(!fast), 0)) {  // a wave-uniform branch keeps the division off the common path
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+            if (!fast) r[q] = xs[q] / sx;
+    }
+    uint32_t cb[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) cb[q] = __float_as_uint(__builtin_amdgcn_fmed3f(r[q], -fq, fq) + 12582912.0f);
+    v2u out;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t lo = __builtin_amdgcn_perm(cb[4 * h + 1], cb[4 * h], 0x0c0c0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(cb[4 * h + 3], cb[4 * h + 2], 0x0c0c0400u);
+        out[h] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    }
+    return out;
+}
+
+// ---- pass 1
+// Workgroup: 64 consecutive tokens (wave w: tokens 16w..16w+15) x a K range, walked in
+// groups of 128 channels.  The MFMA sums over K, so the channels of a group may be dealt
+// to lanes and steps in any order that A and B share: lane (row l%16, g = l/16) takes
+// channels 32g..32g+31 of its row, 8 per step.  x therefore goes straight from memory to
+// the A registers (64 contiguous bytes per lane), and the same registers give the
+// lane's max |x / s|.  The projection rows of the group and its smoothing factors are
+// loaded by all threads in one burst and staged in double-buffered LDS (16-byte chunks
+// XOR-swizzled by (row & 15)), one barrier per group.
+constexpr int RP_TOK = 64;
+constexpr int RP_KG = 128;             // channels per group
+constexpr int RP_MAXN = 5;             // up to 80 projected columns
+
+template <int MP>  // projection-row pieces (16 B) per thread and group: 3 (<= 48 rows) or 5 (<= 80)
+__global__ __launch_bounds__(256) void route_pass_kernel(const uint16_t* __restrict__ x, int T, int d_in,
                                                          const uint16_t* __restrict__ mt, int ncols,
                                                          const float* __restrict__ smooth,
                                                          const float* __restrict__ inv_smooth, int ksplit,
                                                          float* __restrict__ part, float* __restrict__ amax_part) {
-    __shared__ __attribute__((aligned(16))) uint8_t xs[RP_TOK * RP_LD];
-    __shared__ __attribute__((aligned(16))) uint8_t ms[RP_MAXN * 16 * RP_LD];
+    constexpr int M_LDS = MP * 256 * 16;
+    constexpr int BUF = M_LDS + 1024;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
     const int tok0 = blockIdx.x * RP_TOK, ks = blockIdx.y;
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-    const int nch = d_in / RP_KC;
-    const int kbeg = (int)((long)ks * nch / ksplit) * RP_KC, kend = (int)((long)(ks + 1) * nch / ksplit) * RP_KC;
+    const int ngr = d_in / RP_KG;
+    const int g_beg = (int)((long)ks * ngr / ksplit), g_end = (int)((long)(ks + 1) * ngr / ksplit);
     const int nbk = ncols / 16;
-    const int c8 = tid & 7;
-    int trow[2];
-    bool tval[2];
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        trow[p] = tok0 + (tid >> 3) + 32 * p;
-        tval[p] = trow[p] < T;
-    }
+    const int row = tok0 + wid * 16 + lr;
+    const bool rvalid = row < T;
+    const uint16_t* xrow = x + (size_t)min(row, T - 1) * d_in + lg * 32;  // rows past T repeat a valid row
 
     v4f acc[RP_MAXN];
 #pragma unroll
     for (int n = 0; n < RP_MAXN; ++n) acc[n] = v4f{0, 0, 0, 0};
-    float amax[2] = {0.0f, 0.0f};
+    float amax = 0.0f;
 
-    // registers holding the next chunk: two x groups of 8, up to RP_MCH Mt groups of 8
-    Raw8<XDT> xr[2];
-    v4u mr[RP_MCH];
-    auto fetch = [&](int k0) {
+    for (int g = g_beg; g < g_end; ++g) {
+        uint8_t* buf = smem + (g & 1) * BUF;
+        const size_t k0 = (size_t)g * RP_KG;
+        // one burst of loads
+        v4u xv[4], mv[MP];
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            if (tval[p]) xr[p].load(x, (size_t)trow[p] * d_in + k0 + c8 * 8);
-            else xr[p].zero();
+        for (int s = 0; s < 4; ++s) xv[s] = *reinterpret_cast<const v4u*>(xrow + k0 + s * 8);
+#pragma unroll
+        for (int p = 0; p < MP; ++p) {
+            const int idx = tid + 256 * p, r = idx >> 4, c = idx & 15;
+            mv[p] = r < ncols ? *reinterpret_cast<const v4u*>(mt + (size_t)r * d_in + k0 + c * 8) : v4u{0, 0, 0, 0};
         }
+        v4f sv = v4f{0, 0, 0, 0};
+        if (tid < 64) sv = *reinterpret_cast<const v4f*>((tid < 32 ? smooth : inv_smooth) + k0 + (tid & 31) * 4);
 #pragma unroll
-        for (int j = 0; j < RP_MCH; ++j) {
-            const int i = tid + 256 * j, r = i >> 3;
-            if (r < ncols) mr[j] = *reinterpret_cast<const v4u*>(mt + (size_t)r * d_in + k0 + (i & 7) * 8);
+        for (int p = 0; p < MP; ++p) {
+            const int idx = tid + 256 * p, r = idx >> 4, c = idx & 15;
+            if (r < ncols) *reinterpret_cast<v4u*>(buf + r * 256 + ((c ^ (r & 15)) << 4)) = mv[p];
         }
-    };
-    if (kbeg < kend) fetch(kbeg);
-    for (int k0 = kbeg; k0 < kend; k0 += RP_KC) {
-        __syncthreads();  // previous chunk's MFMAs are done with the LDS tiles
+        if (tid < 64) *reinterpret_cast<v4f*>(buf + M_LDS + tid * 16) = sv;
+        __syncthreads();  // (the other buffer was last read before this barrier)
+        if (rvalid) {
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            float v[8];
-            xr[p].get(v);
-            *reinterpret_cast<v4u*>(xs + ((tid >> 3) + 32 * p) * RP_LD + c8 * 16) = pack_bf16x8(v);
-            if (tval[p]) {
-                smooth8<true>(smooth, inv_smooth, k0 + c8 * 8, v);
+            for (int s = 0; s < 4; ++s) {
+                const uint8_t* sp = buf + M_LDS + (lg * 32 + s * 8) * 4;
+                const v4f s0 = *reinterpret_cast<const v4f*>(sp), s1 = *reinterpret_cast<const v4f*>(sp + 16);
+                const v4f i0 = *reinterpret_cast<const v4f*>(sp + 512), i1 = *reinterpret_cast<const v4f*>(sp + 528);
+                float xs[8];
+                smooth_div8(xv[s], s0, s1, i0, i1, xs);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) amax[p] = fmaxf(amax[p], __builtin_fabsf(v[i]));
+                for (int q = 0; q < 8; ++q) amax = fmaxf(amax, __builtin_fabsf(xs[q]));
             }
         }
 #pragma unroll
-        for (int j = 0; j < RP_MCH; ++j) {
-            const int i = tid + 256 * j, r = i >> 3;
-            if (r < ncols) *reinterpret_cast<v4u*>(ms + r * RP_LD + (i & 7) * 16) = mr[j];
-        }
-        __syncthreads();
-        if (k0 + RP_KC < kend) fetch(k0 + RP_KC);  // in flight during the MFMAs
-#pragma unroll
-        for (int s = 0; s < RP_KC / 32; ++s) {
-            const v8bf a = *reinterpret_cast<const v8bf*>(xs + (wid * 16 + lr) * RP_LD + (s * 32 + lg * 8) * 2);
+        for (int s = 0; s < 4; ++s) {
 #pragma unroll
             for (int n = 0; n < RP_MAXN; ++n) {
                 if (n >= nbk) break;
-                const v8bf b = *reinterpret_cast<const v8bf*>(ms + (n * 16 + lr) * RP_LD + (s * 32 + lg * 8) * 2);
-                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[n], 0, 0, 0);
+                const int rm = n * 16 + lr;
+                const v8bf bv = *reinterpret_cast<const v8bf*>(buf + rm * 256 + (((lg * 4 + s) ^ (rm & 15)) << 4));
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const v8bf*>(&xv[s]), bv, acc[n], 0,
+                                                                 0, 0);
             }
         }
     }
+
     float* out = part + (size_t)ks * T * ncols;
 #pragma unroll
     for (int n = 0; n < RP_MAXN; ++n) {
@@ -539,35 +571,32 @@ __global__ __launch_bounds__(256) void route_pass_kernel(const void* __restrict_
             if (t < T) out[(size_t)t * ncols + n * 16 + lr] = acc[n][r];
         }
     }
-    // the 8 threads of a token row are 8 consecutive lanes
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-        float m = amax[p];
-        m = fmaxf(m, __shfl_xor(m, 1, 64));
-        m = fmaxf(m, __shfl_xor(m, 2, 64));
-        m = fmaxf(m, __shfl_xor(m, 4, 64));
-        if (c8 == 0 && tval[p]) amax_part[(size_t)ks * T + trow[p]] = m;
-    }
+    // a row's 128 channels are spread over lanes lr, lr+16, lr+32, lr+48
+    float m = amax;
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    if (lg == 0 && rvalid) amax_part[(size_t)ks * T + row] = m;
 }
 
 int route_pass_ksplit(int T, int d_in) {
     const int tiles = (T + RP_TOK - 1) / RP_TOK;
-    const int ks = std::min((1024 + tiles - 1) / tiles, std::max(1, d_in / 256));
+    const int ks = std::min((768 + tiles - 1) / tiles, std::max(1, d_in / (2 * RP_KG)));
     return std::max(ks, 1);
 }
 
-hipError_t launch_route_pass(const void* x, int x_dtype, int T, int d_in, const uint16_t* mt, int ncols,
-                             const float* smooth, const float* inv_smooth, int ksplit, float* part, float* amax_part,
-                             hipStream_t st) {
+hipError_t launch_route_pass(const uint16_t* x, int T, int d_in, const uint16_t* mt, int ncols, const float* smooth,
+                             const float* inv_smooth, int ksplit, float* part, float* amax_part, hipStream_t st) {
     if (T <= 0) return hipSuccess;
-    if (ncols > RP_MAXN * 16 || ncols % 16 || d_in % RP_KC || !smooth || !inv_smooth) return hipErrorInvalidValue;
+    if (ncols > RP_MAXN * 16 || ncols % 16 || d_in % RP_KG || ksplit < 1 || ksplit > d_in / RP_KG || !smooth ||
+        !inv_smooth)
+        return hipErrorInvalidValue;
     const dim3 grid((T + RP_TOK - 1) / RP_TOK, ksplit);
-    if (x_dtype == QE_BF16)
-        hipLaunchKernelGGL(route_pass_kernel<QE_BF16>, grid, dim3(256), 0, st, x, T, d_in, mt, ncols, smooth,
-                           inv_smooth, ksplit, part, amax_part);
+    if (ncols <= 48)
+        hipLaunchKernelGGL(route_pass_kernel<3>, grid, dim3(256), 0, st, x, T, d_in, mt, ncols, smooth, inv_smooth,
+                           ksplit, part, amax_part);
     else
-        hipLaunchKernelGGL(route_pass_kernel<QE_F32>, grid, dim3(256), 0, st, x, T, d_in, mt, ncols, smooth,
-                           inv_smooth, ksplit, part, amax_part);
+        hipLaunchKernelGGL(route_pass_kernel<5>, grid, dim3(256), 0, st, x, T, d_in, mt, ncols, smooth, inv_smooth,
+                           ksplit, part, amax_part);
     return hipGetLastError();
 }
 
@@ -580,15 +609,21 @@ __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restri
                                                            uint16_t* __restrict__ u, float* __restrict__ s_x) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (t >= T) return;
-    // columns lane and lane + 64 (ncols <= 80)
+    // columns lane and lane + 64 (ncols <= 80); partials loaded 8 at a time, added in order
     float sum[2] = {0.0f, 0.0f};
     const size_t stride = (size_t)T * ncols;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int c = lane + 64 * j;
-        if (c < ncols) {
-            const float* p = part + (size_t)t * ncols + c;
-            for (int k = 0; k < ksplit; ++k) sum[j] += p[(size_t)k * stride];
+        if (c >= ncols) continue;
+        const float* p = part + (size_t)t * ncols + c;
+        for (int k0 = 0; k0 < ksplit; k0 += 8) {
+            float vals[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) vals[q] = k0 + q < ksplit ? p[(size_t)(k0 + q) * stride] : 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (k0 + q < ksplit) sum[j] += vals[q];
         }
     }
     if (router_col >= 0) {
@@ -633,49 +668,114 @@ hipError_t launch_route_finish(const float* part, const float* amax_part, int ks
     return hipGetLastError();
 }
 
-// Pass 2.  A workgroup takes 128 token rows in `perm` order (tokens grouped by expert),
-// one 16-row block per wave, and a K range walked in 32-wide steps by all 8 waves
-// together.  Per step a lane owns 8 consecutive channels of one row: it writes their
-// codes (x / s, then / s_x, round half to even, clamp -- the float32 operations of the
-// activation quantization kernel) and feeds bf16(x) to the MFMAs of v = x . A_e.  The
-// experts present in the tile are taken up to 8/NBR at a time; each MFMA sees only the
-// rows of its expert (A masked), so one accumulator collects every row's own expert
-// exactly.  x, the expert fragments (shared by the 8 row blocks) and the smoothing
-// factors of each step reach LDS by DMA through a 4-stage ring, three steps ahead,
-// with explicit waits and no staging registers.  With K split over workgroups the
-// partial v go to `vpart` and vpart_finish adds them in K order.
-constexpr int EQ_W = 8;              // waves per workgroup
-constexpr int EQ_ROWS = 16 * EQ_W;   // token rows per workgroup
-constexpr int EQ_NS = 4;             // ring stages
+// ---- pass 2
+// A workgroup takes 128 token rows of the expert-sorted order, one 16-row block per
+// wave, and a K range walked in groups of 128 channels (four 32-wide
+// MFMA steps).  As in pass 1, lane (row l%16, g = l/16) takes channels 32g..32g+31 of
+// its row: x goes straight to registers (64 contiguous bytes) and the lane writes the
+// 32 codes of those channels as 32 contiguous bytes, so each code row segment of 128
+// bytes is written whole.  The experts present in the tile are taken ESLOTS at a time;
+// each MFMA sees only the rows of its expert (A masked), so one accumulator collects
+// every row's own expert exactly.  The group's expert fragments (16 KB, each wave
+// loading 2 KB) and smoothing factors are staged in double-buffered LDS for all 8 row
+// blocks, one barrier per group.  With K split over workgroups the partial v go to
+// `vpart` and vpart_finish adds them in K order.
+//   Bucketing is done here too: every workgroup counts the routes (wave ballots over
+// contiguous token ranges, so a stable rank is the prefix over waves plus the rank in
+// the wave) and picks the tokens of its own positions; the first workgroup of a tile
+// writes them to `perm`.  Equal experts keep token order.
+constexpr int EQ_W = 8;             // waves per workgroup
+constexpr int EQ_ROWS = 16 * EQ_W;  // token rows per workgroup
+constexpr int EQ_KG = 128;          // channels per group
+constexpr int EQ_TPL = 8;           // routes read per lane and batch while bucketing
 
-template <int XDT, int NBR>
+template <int NBR>
 __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
-    const void* __restrict__ x, int T, int d_in, const float* __restrict__ smooth,
-    const float* __restrict__ inv_smooth, const float* __restrict__ s_x, int qmax, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ expert, int n_r, const uint16_t* __restrict__ mt_re, int r_r, int ksq,
+    const uint16_t* __restrict__ x, int T, int d_in, const float* __restrict__ smooth,
+    const float* __restrict__ inv_smooth, const float* __restrict__ s_x, int qmax, const int32_t* __restrict__ expert,
+    int n_r, const uint16_t* __restrict__ mt_re, int r_r, int ksq, int32_t* __restrict__ perm_out,
     float* __restrict__ vpart, int8_t* __restrict__ codes, uint16_t* __restrict__ v) {
-    constexpr int XOPS = XDT == QE_BF16 ? 1 : 2;  // 1 KB copies of x per wave and step
-    constexpr int RR = NBR * 16;                  // padded routed rank
-    constexpr int ESLOTS = NBR ? EQ_W / NBR : 1;  // experts per pass
-    constexpr int X_STAGE = EQ_W * XOPS * 1024;
-    constexpr int B_STAGE = NBR ? EQ_W * 1024 : 0;
-    constexpr int S_STAGE = EQ_W * 256;
-    constexpr int STAGE = X_STAGE + B_STAGE + S_STAGE;
-    constexpr int OPS = XOPS + (NBR ? 1 : 0) + 1;  // DMA instructions per wave and step
-    constexpr int ESZ = XDT == QE_BF16 ? 2 : 4;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[EQ_NS * STAGE];
+    constexpr int RR = NBR * 16;               // padded routed rank
+    constexpr int NB1 = NBR ? NBR : 1;
+    constexpr int ESLOTS = NBR == 4 ? 1 : 2;   // experts per pass: 16 KB of fragments per group
+    constexpr int B_LDS = NBR ? 16384 : 0;
+    constexpr int BUF = B_LDS + 1024;          // + smoothing factors and reciprocals (128 each)
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
     __shared__ uint32_t s_pres[EQ_W];
 
+    __shared__ int s_cnt[EQ_W][kMaxRouted];
+    __shared__ int s_tok[EQ_ROWS];
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int tile = blockIdx.x, kq = blockIdx.y;
     const int pos0 = tile * EQ_ROWS;
-    const int pos = pos0 + wid * 16 + lr;
-    const bool valid = pos < T;
-    const int t = valid ? (perm ? perm[pos] : pos) : 0;  // rows past T read row 0 and are never stored
-    const int e_row = (NBR && valid && expert) ? min(max(expert[t], 0), n_r - 1) : -1;
+    const bool routed = expert != nullptr && n_r > 0;
+
+    // ---- the tokens of positions pos0 .. pos0 + EQ_ROWS - 1
+    if (tid < EQ_ROWS) s_tok[tid] = pos0 + tid < T ? pos0 + tid : -1;
+    if (routed) {
+        const int tw0 = (int)((long)wid * T / EQ_W), tw1 = (int)((long)(wid + 1) * T / EQ_W);  // wave's tokens
+        const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+        int cnt[kMaxRouted];
+#pragma unroll
+        for (int e = 0; e < kMaxRouted; ++e) cnt[e] = 0;
+        for (int b0 = tw0; b0 < tw1; b0 += 64 * EQ_TPL) {
+            int ev[EQ_TPL];
+#pragma unroll
+            for (int j = 0; j < EQ_TPL; ++j)  // unconditional loads (clamped index), masked after
+                ev[j] = expert[min(b0 + 64 * j + lane, T - 1)];
+#pragma unroll
+            for (int j = 0; j < EQ_TPL; ++j) ev[j] = b0 + 64 * j + lane < tw1 ? min(max(ev[j], 0), n_r - 1) : -1;
+#pragma unroll
+            for (int j = 0; j < EQ_TPL; ++j)
+#pragma unroll
+                for (int e = 0; e < kMaxRouted; ++e)
+                    if (e < n_r) cnt[e] += __popcll(__ballot(ev[j] == e));
+        }
+        if (lane == 0)
+#pragma unroll
+            for (int e = 0; e < kMaxRouted; ++e) s_cnt[wid][e] = cnt[e];
+        __syncthreads();
+        // expert boundaries, and this wave's base rank in each expert
+        int off = 0;
+        for (int e = 0; e < n_r; ++e) {
+            int tot = 0, base = 0;
+#pragma unroll
+            for (int w = 0; w < EQ_W; ++w) {
+                const int c = s_cnt[w][e];
+                base += w < wid ? c : 0;
+                tot += c;
+            }
+            const int lo = max(pos0, off) - off, hi = min(pos0 + EQ_ROWS, off + tot) - off;  // ranks of expert e here
+            if (lo < hi && base < hi && base + s_cnt[wid][e] > lo) {
+                int rank = base;
+                for (int b0 = tw0; b0 < tw1 && rank < hi; b0 += 64 * EQ_TPL) {
+                    int ev[EQ_TPL];
+#pragma unroll
+                    for (int j = 0; j < EQ_TPL; ++j) ev[j] = expert[min(b0 + 64 * j + lane, T - 1)];
+#pragma unroll
+                    for (int j = 0; j < EQ_TPL; ++j) {
+                        const int tk = b0 + 64 * j + lane;
+                        const bool f = tk < tw1 && min(max(ev[j], 0), n_r - 1) == e;
+                        const uint64_t bal = __ballot(f);
+                        const int r = rank + __popcll(bal & lt);
+                        if (f && r >= lo && r < hi) s_tok[off + r - pos0] = tk;
+                        rank += __popcll(bal);
+                    }
+                }
+            }
+            off += tot;
+        }
+    }
+    __syncthreads();
+    if (perm_out && kq == 0 && tid < EQ_ROWS && pos0 + tid < T) perm_out[pos0 + tid] = s_tok[tid];
+
+    const int t_row = s_tok[wid * 16 + lr];
+    const bool valid = t_row >= 0;
+    const int t = valid ? t_row : 0;  // rows past T read row 0 and are never stored
+    const int e_row = (NBR && valid && routed) ? min(max(expert[t], 0), n_r - 1) : -1;
     const float sx = valid ? s_x[t] : 0.0f;
     const float inv_sx = sx != 0.0f ? 1.0f / sx : 0.0f;
-    const bool fast = sx >= 0x1p-90f && sx <= 0x1p90f;
+    const bool fast = (sx >= 0x1p-90f && sx <= 0x1p90f) || sx == 0.0f;
     const float fq = (float)qmax;
     uint32_t pres = 0;
     if (NBR)
@@ -687,20 +787,18 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
 #pragma unroll
     for (int w = 0; w < EQ_W; ++w) present |= s_pres[w];
 
-    const int nsteps = d_in / 32;
-    const int g0 = (int)((long)kq * nsteps / ksq), g1 = (int)((long)(kq + 1) * nsteps / ksq);
-    const int nst = g1 - g0;  // >= 1: ksq <= nsteps
-    const uint32_t lds0 = lds_addr(smem);
-    const char* xsrc = reinterpret_cast<const char*>(x) + ((size_t)t * d_in + lg * 8) * ESZ;
-    const float* ssrc = lane < 32 ? smooth + lane : inv_smooth + (lane - 32);
-    int8_t* crow = codes + (size_t)t * d_in + lg * 8;
+    const int ngr = d_in / EQ_KG;
+    const int g_beg = (int)((long)kq * ngr / ksq), g_end = (int)((long)(kq + 1) * ngr / ksq);
+    const uint16_t* xrow = x + (size_t)t * d_in + lg * 32;
+    int8_t* crow = codes + (size_t)t * d_in + lg * 32;
 
-    v4f acc[NBR ? NBR : 1];
+    v4f acc[NB1];
 #pragma unroll
-    for (int n = 0; n < (NBR ? NBR : 1); ++n) acc[n] = v4f{0, 0, 0, 0};
+    for (int n = 0; n < NB1; ++n) acc[n] = v4f{0, 0, 0, 0};
 
     uint32_t pm = present;
     bool first = true;
+    int gi = 0;  // groups processed (LDS buffer parity)
     do {  // passes over the present experts; the codes are written on the first
         int ex[ESLOTS];
 #pragma unroll
@@ -711,96 +809,74 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
                 pm &= pm - 1;
             }
         }
-        // this wave's expert-fragment copy: slot wid / NBR, column block wid % NBR
-        int my_e = max(ex[0], 0);  // empty slots repeat a present expert (never used)
+        // fragment copies b = 2*wid + q: MFMA step b%4, column block (b/4)%NB1, slot b/(4*NB1)
+        const uint16_t* bsrc[2];
 #pragma unroll
-        for (int j = 1; j < ESLOTS; ++j)
-            if (j == wid / (NBR ? NBR : 1) && ex[j] >= 0) my_e = ex[j];
-        const uint16_t* bsrc =
-            NBR ? mt_re + ((size_t)my_e * RR + (wid % (NBR ? NBR : 1)) * 16 + lr) * d_in + lg * 8 : nullptr;
-        auto issue = [&](int stage, int step) {
-            const uint32_t base = lds0 + stage * STAGE;
-            const size_t k = (size_t)step * 32;
+        for (int q = 0; q < 2; ++q) {
+            const int b = 2 * wid + q, bs = b & 3, bn = (b >> 2) % NB1, bj = b / (4 * NB1);
+            int e = max(ex[0], 0);  // empty slots repeat a present expert (never used)
 #pragma unroll
-            for (int o = 0; o < XOPS; ++o) dma16(xsrc + k * ESZ + o * 16, base + (wid * XOPS + o) * 1024);
-            if (NBR) dma16(bsrc + k, base + X_STAGE + wid * 1024);
-            dma4(ssrc + k, base + X_STAGE + B_STAGE + wid * 256);
-        };
+            for (int j = 1; j < ESLOTS; ++j)
+                if (j == bj && ex[j] >= 0) e = ex[j];
+            bsrc[q] = NBR ? mt_re + ((size_t)e * RR + bn * 16 + lr) * d_in + lg * 32 + bs * 8 : nullptr;
+        }
+        for (int g = g_beg; g < g_end; ++g, ++gi) {
+            uint8_t* buf = smem + (gi & 1) * BUF;
+            const size_t k0 = (size_t)g * EQ_KG;
+            // one burst of loads
+            v4u xv[4];
 #pragma unroll
-        for (int st = 0; st < EQ_NS - 1; ++st) issue(st, g0 + min(st, nst - 1));
-        QE_WAIT_VMCNT_LDS((EQ_NS - 2) * OPS);
-        QE_WG_BARRIER();
-
-        for (int i = 0; i < nst; ++i) {
-            // refill the slot consumed in the previous step (past the end: a harmless repeat)
-            issue((i + EQ_NS - 1) % EQ_NS, g0 + min(i + EQ_NS - 1, nst - 1));
-            const uint8_t* st = smem + (i % EQ_NS) * STAGE;
-            float xc[8];
-            if (XDT == QE_BF16) {
-                Raw8<QE_BF16> r;
-                r.b = *reinterpret_cast<const v4u*>(st + wid * 1024 + lane * 16);
-                r.get(xc);
-            } else {
-                Raw8<QE_F32> r;
-                r.a = *reinterpret_cast<const v4f*>(st + wid * 2048 + lane * 16);
-                r.b = *reinterpret_cast<const v4f*>(st + wid * 2048 + 1024 + lane * 16);
-                r.get(xc);
+            for (int s = 0; s < 4; ++s) xv[s] = *reinterpret_cast<const v4u*>(xrow + k0 + s * 8);
+            v4u bv[2];
+            if (NBR) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) bv[q] = *reinterpret_cast<const v4u*>(bsrc[q] + k0);
             }
-            const uint8_t* sp = st + X_STAGE + B_STAGE + wid * 256 + lg * 32;
-            const v4f s0 = *reinterpret_cast<const v4f*>(sp), s1 = *reinterpret_cast<const v4f*>(sp + 16);
-            const v4f i0 = *reinterpret_cast<const v4f*>(sp + 128), i1 = *reinterpret_cast<const v4f*>(sp + 144);
-            const v4u abits = pack_bf16x8(xc);
+            v4f sv = v4f{0, 0, 0, 0};
+            if (first && tid < 64)
+                sv = *reinterpret_cast<const v4f*>((tid < 32 ? smooth : inv_smooth) + k0 + (tid & 31) * 4);
+            if (NBR) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) *reinterpret_cast<v4u*>(buf + (2 * wid + q) * 1024 + lane * 16) = bv[q];
+            }
+            if (first && tid < 64) *reinterpret_cast<v4f*>(buf + B_LDS + tid * 16) = sv;
+            __syncthreads();  // (the other buffer was last read before this barrier)
             if (first) {
-                // codes: x' = x / s, q = clamp(rint(x' / s_x))
-                float xs8[8];
-                bool ok = true;
+                v2u cw[4];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const float sq = q < 4 ? s0[q] : s1[q - 4], iq = q < 4 ? i0[q] : i1[q - 4];
-                    xs8[q] = div_markstein(xc[q], sq, iq);
-                    ok = ok && in_markstein_range(xc[q]);
+                for (int s = 0; s < 4; ++s) {
+                    const uint8_t* sp = buf + B_LDS + (lg * 32 + s * 8) * 4;
+                    const v4f s0 = *reinterpret_cast<const v4f*>(sp), s1 = *reinterpret_cast<const v4f*>(sp + 16);
+                    const v4f i0 = *reinterpret_cast<const v4f*>(sp + 512),
+                              i1 = *reinterpret_cast<const v4f*>(sp + 528);
+                    float xs[8];
+                    smooth_div8(xv[s], s0, s1, i0, i1, xs);
+                    cw[s] = codes8(xs, sx, inv_sx, fast, fq);
                 }
-                if (__builtin_expect(__any(!ok), 0)) {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const float sq = q < 4 ? s0[q] : s1[q - 4];
-                        if (!in_markstein_range(xc[q])) xs8[q] = xc[q] / sq;
-                    }
+                if (valid) {
+                    *reinterpret_cast<v4u*>(crow + k0) = v4u{cw[0][0], cw[0][1], cw[1][0], cw[1][1]};
+                    *reinterpret_cast<v4u*>(crow + k0 + 16) = v4u{cw[2][0], cw[2][1], cw[3][0], cw[3][1]};
                 }
-                uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    float qv = 0.0f;
-                    if (sx != 0.0f) {
-                        const float r = fast ? div_markstein(xs8[q], sx, inv_sx) : xs8[q] / sx;
-                        qv = fminf(fmaxf(__builtin_rintf(r), -fq), fq);
-                    }
-                    packed[q >> 2] |= ((uint32_t)(int32_t)qv & 0xFFu) << (8 * (q & 3));
-                }
-                if (valid) *reinterpret_cast<v2u*>(crow + (size_t)(g0 + i) * 32) = v2u{packed[0], packed[1]};
             }
             if (NBR) {
                 const v4u zero4 = v4u{0, 0, 0, 0};
 #pragma unroll
-                for (int j = 0; j < ESLOTS; ++j) {
-                    if (ex[j] < 0) break;  // uniform
-                    const v4u am = e_row == ex[j] ? abits : zero4;
+                for (int s = 0; s < 4; ++s) {
 #pragma unroll
-                    for (int n = 0; n < (NBR ? NBR : 1); ++n) {
-                        const v8bf bq = *reinterpret_cast<const v8bf*>(st + X_STAGE + (j * NBR + n) * 1024 + lane * 16);
-                        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const v8bf*>(&am), bq,
-                                                                         acc[n], 0, 0, 0);
+                    for (int j = 0; j < ESLOTS; ++j) {
+                        if (ex[j] < 0) break;  // uniform
+                        const v4u am = e_row == ex[j] ? xv[s] : zero4;
+#pragma unroll
+                        for (int n = 0; n < NB1; ++n) {
+                            const v8bf bq =
+                                *reinterpret_cast<const v8bf*>(buf + ((j * NB1 + n) * 4 + s) * 1024 + lane * 16);
+                            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const v8bf*>(&am), bq,
+                                                                             acc[n], 0, 0, 0);
+                        }
                     }
                 }
             }
-            // the slot read here is the DMA target of the next step: every LDS read must
-            // have completed (lgkmcnt 0); and step i+1 must have landed
-            __builtin_amdgcn_sched_barrier(0);
-            QE_WAIT_VMCNT_LDS((EQ_NS - 2) * OPS);
-            QE_WG_BARRIER();
         }
-        QE_WAIT_VMCNT(0);  // the repeated tail copies, before the ring is refilled or freed
-        QE_WG_BARRIER();
         first = false;
     } while (pm);
     if (NBR == 0 || !v) return;
@@ -809,10 +885,10 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int row = lg * 4 + r;
-        const int tt = __shfl(valid ? t : -1, row, 64);
+        const int tt = s_tok[wid * 16 + row];
         const int p = pos0 + wid * 16 + row;
 #pragma unroll
-        for (int n = 0; n < (NBR ? NBR : 1); ++n) {
+        for (int n = 0; n < NB1; ++n) {
             const int c = n * 16 + lr;
             if (ksq == 1) {
                 if (tt >= 0) v[(size_t)tt * RR + c] = c < r_r ? (uint16_t)f32_to_bf16_bits(acc[n][r]) : (uint16_t)0;
@@ -838,42 +914,30 @@ __global__ __launch_bounds__(256) void vpart_finish_kernel(const float* __restri
 
 int expert_quant_ksplit(int T, int d_in) {
     const int tiles = (T + EQ_ROWS - 1) / EQ_ROWS;
-    const int ks = std::min((512 + tiles - 1) / tiles, std::max(1, d_in / 32 / 8));
+    const int ks = std::min((512 + tiles - 1) / tiles, std::max(1, d_in / (2 * EQ_KG)));
     return std::max(ks, 1);
 }
 
-template <int XDT>
-static hipError_t launch_eq(dim3 grid, hipStream_t st, int nbr, const void* x, int T, int d_in, const float* smooth,
-                            const float* inv_smooth, const float* s_x, int qmax, const int32_t* perm,
-                            const int32_t* expert, int n_r, const uint16_t* mt_re, int r_r, int ksq, float* vpart,
-                            int8_t* codes, uint16_t* v) {
-#define QE_EQ_LAUNCH(NB)                                                                                            \
-    hipLaunchKernelGGL((expert_quant_kernel<XDT, NB>), grid, dim3(64 * EQ_W), 0, st, x, T, d_in, smooth,           \
-                       inv_smooth, s_x, qmax, perm, expert, n_r, mt_re, r_r, ksq, vpart, codes, v)
+hipError_t launch_expert_quant(const uint16_t* x, int T, int d_in, const float* smooth, const float* inv_smooth,
+                               const float* s_x, int a_bits, const int32_t* expert, int n_r, const uint16_t* mt_re,
+                               int rr_pad, int r_r, int ksq, int32_t* perm, float* vpart, int8_t* codes, uint16_t* v,
+                               hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    const int nbr = (expert && v) ? rr_pad / 16 : 0;
+    if ((nbr != 0 && nbr != 2 && nbr != 4) || d_in % EQ_KG || ksq < 1 || ksq > d_in / EQ_KG || n_r > kMaxRouted ||
+        !smooth || !inv_smooth)
+        return hipErrorInvalidValue;
+    if (ksq > 1 && nbr && (!vpart || !perm)) return hipErrorInvalidValue;
+    const dim3 grid((T + EQ_ROWS - 1) / EQ_ROWS, ksq);
+    const int qmax = (1 << (a_bits - 1)) - 1;
+#define QE_EQ_LAUNCH(NB)                                                                                             \
+    hipLaunchKernelGGL((expert_quant_kernel<NB>), grid, dim3(64 * EQ_W), 0, st, x, T, d_in, smooth, inv_smooth, s_x, \
+                       qmax, expert, n_r, mt_re, r_r, ksq, perm, vpart, codes, v)
     if (nbr == 0) QE_EQ_LAUNCH(0);
     else if (nbr == 2) QE_EQ_LAUNCH(2);
     else QE_EQ_LAUNCH(4);
 #undef QE_EQ_LAUNCH
-    return hipGetLastError();
-}
-
-hipError_t launch_expert_quant(const void* x, int x_dtype, int T, int d_in, const float* smooth,
-                               const float* inv_smooth, const float* s_x, int a_bits, const int32_t* perm,
-                               const int32_t* expert, int n_r, const uint16_t* mt_re, int rr_pad, int r_r, int ksq,
-                               float* vpart, int8_t* codes, uint16_t* v, hipStream_t st) {
-    if (T <= 0) return hipSuccess;
-    const int nbr = (expert && v) ? rr_pad / 16 : 0;
-    if ((nbr != 0 && nbr != 2 && nbr != 4) || d_in % 32 || ksq < 1 || ksq > d_in / 32 || n_r > kMaxRouted || !smooth ||
-        !inv_smooth)
-        return hipErrorInvalidValue;
-    if (ksq > 1 && nbr && !vpart) return hipErrorInvalidValue;
-    const dim3 grid((T + EQ_ROWS - 1) / EQ_ROWS, ksq);
-    const int qmax = (1 << (a_bits - 1)) - 1;
-    hipError_t err = x_dtype == QE_BF16
-                         ? launch_eq<QE_BF16>(grid, st, nbr, x, T, d_in, smooth, inv_smooth, s_x, qmax, perm, expert,
-                                              n_r, mt_re, r_r, ksq, vpart, codes, v)
-                         : launch_eq<QE_F32>(grid, st, nbr, x, T, d_in, smooth, inv_smooth, s_x, qmax, perm, expert,
-                                             n_r, mt_re, r_r, ksq, vpart, codes, v);
+    hipError_t err = hipGetLastError();
     if (err != hipSuccess || ksq == 1 || !nbr) return err;
     const size_t n = (size_t)T * rr_pad;
     hipLaunchKernelGGL(vpart_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, vpart, ksq, T, rr_pad,

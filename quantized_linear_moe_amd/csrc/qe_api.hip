@@ -101,8 +101,9 @@ int ensure_attributes() {
 namespace qe {
 constexpr int kSkinnyMaxT = 16;  // token counts served by the weight-streaming kernels
 
-// Prefill prologue in two reads of x (route pass, then expert-sorted quantization)
-bool use_two_pass(const qe_linear* lin, int T) { return lin->a_bits != 16 && T > kSkinnyMaxT; }
+// Prefill prologue in two reads of x (route pass, then expert-sorted quantization), for
+// bf16 activations; the workspace is sized for it whatever the activation type
+bool two_pass_sized(const qe_linear* lin, int T) { return lin->a_bits != 16 && T > kSkinnyMaxT; }
 }  // namespace qe
 
 namespace qe {
@@ -155,7 +156,7 @@ WsLayout ws_layout(const qe_linear* lin, int T) {
     off = align256(off + t * 4);
     W.part = off;
     const int xks = std::max(W.xproj_ksplit, T <= kSkinnyMaxT ? skinny_ksplit_proj(lin->d_in) : 1);
-    const bool two_pass = use_two_pass(lin, T);
+    const bool two_pass = two_pass_sized(lin, T);
     W.rp_ksplit = two_pass ? route_pass_ksplit(T, lin->d_in) : 0;
     W.eq_ksplit = two_pass ? expert_quant_ksplit(T, lin->d_in) : 0;
     off = align256(off + std::max((size_t)xks * t * P.n_cols_pad, (size_t)W.rp_ksplit * t * P.n_lead) * 4);
@@ -469,22 +470,21 @@ static int run_prologue(const qe_linear* lin, const void* x, int x_dtype, int T,
     const PrepLayout P = prep_layout(lin);
     const WsLayout W = ws_layout(lin, T);
     const bool route = lin->n_routed > 0;
-    if (use_two_pass(lin, T)) {
+    if (two_pass_sized(lin, T) && x_dtype == QE_BF16) {
         const float* smooth = at<const float>(lin->prep, P.smooth);
         const float* inv_smooth = at<const float>(lin->prep, P.inv_smooth);
         const uint16_t* mt = at<const uint16_t>(lin->prep, P.mt);
-        QE_TRY_HIP(launch_route_pass(x, x_dtype, T, lin->d_in, mt, P.n_lead, smooth, inv_smooth, W.rp_ksplit,
+        const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+        QE_TRY_HIP(launch_route_pass(xb, T, lin->d_in, mt, P.n_lead, smooth, inv_smooth, W.rp_ksplit,
                                      at<float>(ws, W.part), at<float>(ws, W.amax), s));
         QE_TRY_HIP(launch_route_finish(at<const float>(ws, W.part), at<const float>(ws, W.amax), W.rp_ksplit, T,
                                        P.n_lead, lin->r_shared, P.rs_pad, P.col_router, lin->n_routed, lin->a_bits,
                                        route ? expert : nullptr, u, s_x, s));
-        if (route && perm)
-            QE_TRY_HIP(launch_bucket(expert, T, lin->n_routed, at<int32_t>(ws, W.counts), at<int32_t>(ws, W.offsets),
-                                     perm, s));
-        QE_TRY_HIP(launch_expert_quant(x, x_dtype, T, lin->d_in, smooth, inv_smooth, s_x, lin->a_bits,
-                                       route ? perm : nullptr, route ? expert : nullptr, lin->n_routed,
+        QE_TRY_HIP(launch_expert_quant(xb, T, lin->d_in, smooth, inv_smooth, s_x, lin->a_bits,
+                                       route ? expert : nullptr, lin->n_routed,
                                        route ? mt + (size_t)P.col_re * lin->d_in : nullptr, P.rr_pad, lin->r_routed,
-                                       W.eq_ksplit, at<float>(ws, W.vpart), codes, route ? v : nullptr, s));
+                                       W.eq_ksplit, route ? (perm ? perm : at<int32_t>(ws, W.perm)) : nullptr,
+                                       at<float>(ws, W.vpart), codes, route ? v : nullptr, s));
         return QE_OK;
     }
     int st = run_xpass(lin, x, x_dtype, T, u != nullptr, route, route, nullptr, nullptr, route ? expert : nullptr, u,

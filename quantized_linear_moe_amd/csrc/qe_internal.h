@@ -55,15 +55,15 @@ struct WsLayout {
     size_t v;           // bf16 [T][rr_pad]
     size_t skinny;      // float [ksplit][T][d_out]   (decode split-K partials)
     size_t amax;        // float [rp_ksplit][T]       (route pass: partial max |x/s|)
-    size_t vpart;       // float [eq_ksplit][T][rr_pad] (expert-quant split-K partials)
     size_t total;
     int xproj_ksplit;
     int skinny_ksplit;
+    size_t vpart;       // float [eq_ksplit][T][rr_pad] (expert-quant split-K partials)
     int rp_ksplit, eq_ksplit;  // 0 unless the two-pass prefill prologue is used
 };
 
 PrepLayout prep_layout(const qe_linear* lin);
-bool use_two_pass(const qe_linear* lin, int T);
+bool two_pass_sized(const qe_linear* lin, int T);
 WsLayout ws_layout(const qe_linear* lin, int T);
 
 // ----------------------------------------------------------- launch wrappers
@@ -83,17 +83,18 @@ hipError_t launch_xproj_finish(const float* part, int ksplit, int T, int ncols_p
                                uint16_t* v, hipStream_t st);
 
 // two-pass prefill prologue
-hipError_t launch_route_pass(const void* x, int x_dtype, int T, int d_in, const uint16_t* mt, int ncols,
-                             const float* smooth, const float* inv_smooth, int ksplit, float* part, float* amax_part,
-                             hipStream_t st);
+hipError_t launch_route_pass(const uint16_t* x, int T, int d_in, const uint16_t* mt, int ncols, const float* smooth,
+                             const float* inv_smooth, int ksplit, float* part, float* amax_part, hipStream_t st);
 int route_pass_ksplit(int T, int d_in);
 hipError_t launch_route_finish(const float* part, const float* amax_part, int ksplit, int T, int ncols, int r_s,
                                int rs_pad, int router_col, int n_r, int a_bits, int32_t* expert, uint16_t* u,
                                float* s_x, hipStream_t st);
-hipError_t launch_expert_quant(const void* x, int x_dtype, int T, int d_in, const float* smooth,
-                               const float* inv_smooth, const float* s_x, int a_bits, const int32_t* perm,
-                               const int32_t* expert, int n_r, const uint16_t* mt_re, int rr_pad, int r_r, int ksq,
-                               float* vpart, int8_t* codes, uint16_t* v, hipStream_t st);
+// Expert-sorted codes + selected-expert v; buckets the routes itself and writes perm
+// (needed when ksq > 1: the split-K finish scatters v through it)
+hipError_t launch_expert_quant(const uint16_t* x, int T, int d_in, const float* smooth, const float* inv_smooth,
+                               const float* s_x, int a_bits, const int32_t* expert, int n_r, const uint16_t* mt_re,
+                               int rr_pad, int r_r, int ksq, int32_t* perm, float* vpart, int8_t* codes, uint16_t* v,
+                               hipStream_t st);
 int expert_quant_ksplit(int T, int d_in);
 
 hipError_t launch_bucket(const int32_t* expert, int T, int n_r, int32_t* counts, int32_t* offsets,
