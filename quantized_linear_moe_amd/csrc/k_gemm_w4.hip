@@ -57,7 +57,9 @@ __device__ inline int a_swz(int row) { return (row >> 1) & 3; }
 // MB: 16-row M blocks per workgroup (tile MB*16 tokens x 256 channels).  Tile rows are
 // positions in `perm` order when perm != NULL (tokens grouped by routed expert, so a
 // tile meets few experts in the epilogue), else token order.
-template <int MB>
+// kFast: adapter ranks <= 32 and no accumulator dump; the epilogue then reads every
+// operand from LDS (see below).
+template <int MB, bool kFast>
 __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     const int8_t* __restrict__ codes, const float* __restrict__ s_x, const uint8_t* __restrict__ w_tiled,
     const float* __restrict__ w_scale, int T, int d_in, int d_out, const uint16_t* __restrict__ u,
@@ -112,6 +114,28 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
 #pragma unroll
     for (int j = 0; j < G_NBW; ++j) nb_ok[j] = (nb0 + j) < NB;
 
+    // The tile's rows, read once: token, activation scale and routed expert (clamped
+    // into range) go to LDS for the epilogue; every wave derives the set of experts present.
+    __shared__ int s_tok[BM];
+    __shared__ __attribute__((aligned(16))) float s_sx[BM];
+    __shared__ int s_ex[BM];
+    const bool routed = v != nullptr && expert != nullptr && bt_r != nullptr && rr_pad > 0 && n_r > 0;
+    uint32_t present = 0;
+#pragma unroll
+    for (int r0 = 0; r0 < BM; r0 += 64) {
+        const int r = r0 + lane, pos = m0 + r;
+        const int tk = token(pos);
+        const int ex = (routed && pos < T) ? min(max(expert[tk], 0), n_r - 1) : -1;
+        if (routed)
+            for (int e = 0; e < n_r; ++e)
+                if (__ballot(ex == e)) present |= 1u << e;
+        if (wid == 0) {
+            s_tok[r] = tk;
+            s_sx[r] = s_x[tk];
+            s_ex[r] = ex;
+        }
+    }
+
     v4i acc[MB][G_NBW];
 #pragma unroll
     for (int m = 0; m < MB; ++m)
@@ -159,10 +183,142 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     QE_WAIT_VMCNT(0);
 
     // ------------------------------------------------------------ epilogue
+    // lane holds column (nb*16 + lr) and rows (m*16 + lg*4 + r) of each block; the A
+    // operands of the adapter MFMAs are rows (m*16 + lr).
+    //
+    // Common case (kFast): the ring is free now, so the u and v rows of the tile, this
+    // wave's B_s fragments and the B_e fragments of up to NSLOT experts present arrive by
+    // DMA in one burst; each 16-row block is then dequantized, corrected and stored with
+    // every operand read from LDS.  A tile with more experts than the ring holds adds the
+    // rest in further rounds, reading back the y rows it stored.
+    const bool have_se = u != nullptr && bt_s != nullptr && rs_pad > 0;
+    if constexpr (kFast) {
+        constexpr int U_OFF = 0, V_OFF = MB * 1024, BS_OFF = 2 * MB * 1024, BR_OFF = BS_OFF + 16384;
+        constexpr int NSLOT = (G_NS * STAGE - BR_OFF) / 16384;  // experts per round
+        static_assert(NSLOT >= 1, "LDS ring too small for the epilogue operands");
+        QE_WAIT_VMCNT_LDS(0);
+        QE_WG_BARRIER();  // every wave is done with the ring
+        int nbj[G_NBW];   // fragment sources; blocks past d_out repeat a valid block (never stored)
+#pragma unroll
+        for (int j = 0; j < G_NBW; ++j) nbj[j] = nb_ok[j] ? nb0 + j : 0;
+        if (have_se) {
+#pragma unroll
+            for (int p = 0; p < MB / 4; ++p) {
+                const int m = wid + 4 * p;
+                dma16(u + (size_t)s_tok[m * 16 + lr] * rs_pad + lg * 8, lds0 + U_OFF + m * 1024);
+            }
+#pragma unroll
+            for (int j = 0; j < G_NBW; ++j)
+                dma16(bt_s + (size_t)(nbj[j] * 16 + lr) * rs_pad + lg * 8, lds0 + BS_OFF + (wid * G_NBW + j) * 1024);
+        }
+        if (present) {
+#pragma unroll
+            for (int p = 0; p < MB / 4; ++p) {
+                const int m = wid + 4 * p;
+                dma16(v + (size_t)s_tok[m * 16 + lr] * rr_pad + lg * 8, lds0 + V_OFF + m * 1024);
+            }
+        }
+        int es[NSLOT];
+        uint32_t pend = present;
+        auto stage_experts = [&]() {
+#pragma unroll
+            for (int sl = 0; sl < NSLOT; ++sl) {
+                es[sl] = -1;
+                if (pend) {
+                    es[sl] = __builtin_ctz(pend);
+                    pend &= pend - 1;
+#pragma unroll
+                    for (int j = 0; j < G_NBW; ++j)
+                        dma16(bt_r + ((size_t)es[sl] * d_out + nbj[j] * 16 + lr) * rr_pad + lg * 8,
+                              lds0 + BR_OFF + sl * 16384 + (wid * G_NBW + j) * 1024);
+                }
+            }
+        };
+        stage_experts();
+        float sw[G_NBW];
+#pragma unroll
+        for (int j = 0; j < G_NBW; ++j) sw[j] = nb_ok[j] ? w_scale[(nb0 + j) * 16 + lr] : 0.0f;
+        QE_WAIT_VMCNT_LDS(0);
+        QE_WG_BARRIER();
+        auto routed = [&](int m, v4f (&yv)[G_NBW]) {  // y += (v masked to expert e's rows) . B_e
+            const int exm = s_ex[m * 16 + lr];
+#pragma unroll
+            for (int sl = 0; sl < NSLOT; ++sl) {
+                if (es[sl] < 0) break;  // uniform
+                const bool mine = exm == es[sl];
+                if (__ballot(mine) == 0) continue;  // no row of this block uses the expert
+                const v8bf va = mine ? *reinterpret_cast<const v8bf*>(smem + V_OFF + m * 1024 + lane * 16) : v8bf{};
+                const uint8_t* lbr = smem + BR_OFF + sl * 16384 + wid * G_NBW * 1024 + lane * 16;
+#pragma unroll
+                for (int j = 0; j < G_NBW; ++j)
+                    yv[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, *reinterpret_cast<const v8bf*>(lbr + j * 1024),
+                                                                    yv[j], 0, 0, 0);
+            }
+        };
+        const uint8_t* lbs = smem + BS_OFF + wid * G_NBW * 1024 + lane * 16;
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+            const v4f sx = *reinterpret_cast<const v4f*>(&s_sx[m * 16 + lg * 4]);
+            v4f yv[G_NBW];
+#pragma unroll
+            for (int j = 0; j < G_NBW; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) yv[j][r] = (float)(acc[m][j][r] >> 4) * sx[r] * sw[j];
+            if (have_se) {  // y += u . B_s
+                const v8bf ua = *reinterpret_cast<const v8bf*>(smem + U_OFF + m * 1024 + lane * 16);
+#pragma unroll
+                for (int j = 0; j < G_NBW; ++j)
+                    yv[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, *reinterpret_cast<const v8bf*>(lbs + j * 1024),
+                                                                    yv[j], 0, 0, 0);
+            }
+            routed(m, yv);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m * 16 + lg * 4 + r;
+                if (m0 + row >= T) continue;
+                float* yrow = y + (size_t)s_tok[row] * d_out;
+#pragma unroll
+                for (int j = 0; j < G_NBW; ++j)
+                    if (nb_ok[j]) yrow[(nb0 + j) * 16 + lr] = yv[j][r];
+            }
+            __builtin_amdgcn_sched_barrier(0);  // one block at a time: keeps register pressure flat
+        }
+        while (pend) {  // more experts than one round holds (uniform; rare)
+            QE_WAIT_VMCNT_LDS(0);
+            QE_WG_BARRIER();
+            stage_experts();
+            QE_WAIT_VMCNT_LDS(0);
+            QE_WG_BARRIER();
+            for (int m = 0; m < MB; ++m) {
+                v4f yv[G_NBW];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {  // this lane's own stores of the first round
+                    const int row = m * 16 + lg * 4 + r;
+                    const float* yrow = y + (size_t)s_tok[row] * d_out;
+#pragma unroll
+                    for (int j = 0; j < G_NBW; ++j)
+                        yv[j][r] = (nb_ok[j] && m0 + row < T) ? yrow[(nb0 + j) * 16 + lr] : 0.0f;
+                }
+                routed(m, yv);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = m * 16 + lg * 4 + r;
+                    if (m0 + row >= T) continue;
+                    float* yrow = y + (size_t)s_tok[row] * d_out;
+#pragma unroll
+                    for (int j = 0; j < G_NBW; ++j)
+                        if (nb_ok[j]) yrow[(nb0 + j) * 16 + lr] = yv[j][r];
+                }
+            }
+        }
+        return;
+    }
+
+    // General case (larger ranks, or the accumulator dump): operands straight from memory.
+    if constexpr (!kFast) {
     // lane holds column (nb*16 + lr) and rows (m*16 + lg*4 + r) of each block; the
     // A operands of the adapter MFMAs are rows (m*16 + lr).  Processed one M block at
     // a time to keep register pressure at the main loop's level.
-    const bool have_se = u != nullptr && rs_pad > 0;
     v8bf bs[G_NBW];
     if (have_se) {  // issued before the dequantization math
 #pragma unroll
@@ -263,6 +419,7 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
             for (int j = 0; j < G_NBW; ++j)
                 if (nb_ok[j]) y[rowoff + (nb0 + j) * 16 + lr] = yv[m][j][r];
         }
+    }
 }
 
 hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* w_tiled, const float* w_scale, int T,
@@ -274,15 +431,20 @@ hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* 
     // 128-token tiles unless that leaves the chip less than two workgroups per CU
     const bool small = (long)((T + 127) / 128) * n_tn < 512;
     const uint8_t* w = w_tiled;
+    const bool fast = !acc_debug && rs_pad <= 32 && rr_pad <= 32;
+#define QE_GEMM_LAUNCH(MBV, FAST, NTM)                                                                          \
+    hipLaunchKernelGGL((gemm_w4_kernel<MBV, FAST>), dim3((NTM) * n_tn), dim3(256), 0, st, codes, s_x, w, w_scale, T, \
+                       d_in, d_out, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, perm, y, acc_debug, NTM)
     if (small) {
         const int n_tm = (T + 63) / 64;
-        hipLaunchKernelGGL(gemm_w4_kernel<4>, dim3(n_tm * n_tn), dim3(256), 0, st, codes, s_x, w, w_scale, T, d_in, d_out,
-                           u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, perm, y, acc_debug, n_tm);
+        if (fast) QE_GEMM_LAUNCH(4, true, n_tm);
+        else QE_GEMM_LAUNCH(4, false, n_tm);
     } else {
         const int n_tm = (T + 127) / 128;
-        hipLaunchKernelGGL(gemm_w4_kernel<8>, dim3(n_tm * n_tn), dim3(256), 0, st, codes, s_x, w, w_scale, T, d_in, d_out,
-                           u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, perm, y, acc_debug, n_tm);
+        if (fast) QE_GEMM_LAUNCH(8, true, n_tm);
+        else QE_GEMM_LAUNCH(8, false, n_tm);
     }
+#undef QE_GEMM_LAUNCH
     return hipGetLastError();
 }
 
