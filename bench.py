@@ -5,14 +5,19 @@ Workload (one step): the seven decoder-layer linears of a Qwen2VL-72B-shaped lay
 (q 8192->8192, k/v 8192->1024, o 8192->8192, gate/up 8192->29568, down 29568->8192),
 W4A6, T = 4096 prefill tokens (3200 image-like + 896 text-like, synthetic), shared
 expert rank 32, 8 routed experts of rank 32, router d_in x 8.  Every linear runs the
-whole hot path: the fused prologue (x-projection for router + adapters, argmin
-routing, smoothing + per-token A6 quantization) and the int8-MFMA main GEMM with the
-dequantization and shared/routed low-rank terms fused into its epilogue.
-Inputs are resident in HBM before the timed region.
+whole hot path: the prologue (route pass: router and shared-expert projections and
+the per-token max |x/s|; route finish: argmin routing, u, s_x; expert-sorted pass:
+A6 codes, stable bucketing and the selected routed expert's input v) and the
+int8-MFMA main GEMM with the dequantization and the shared/routed low-rank terms
+fused into its epilogue.  Inputs are resident in HBM before the timed region.
 
 Prints one JSON line.  `value` is tokens/s of the whole layer (T / step time).
-`roofline` is the main GEMM kernel (the dominant kernel), timed with HIP events
-around each of its launches on the stream it is launched on.
+`roofline` is the dominant kernel, the 128-token-tile instantiation of the main GEMM
+(q, o, gate, up and down use it; the narrow k and v projections use 64-token tiles),
+timed with HIP events around each of its launches on the stream it is launched on.
+
+`--copy-calibration` only times a 1 GiB device copy (the reference kernel for the
+HBM byte counters) and exits.
 """
 
 import argparse
@@ -42,15 +47,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     return ap.parse_args()
 
 
 def gemm_source_hash():
     h = hashlib.sha256()
-    for f in ("k_gemm_w4.hip", "qe_internal.h"):
+    for f in ("k_gemm_w4.hip", "qe_dma.h", "qe_internal.h"):
         with open(os.path.join(ROOT, "quantized_linear_moe_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -67,11 +73,39 @@ def load_traffic(per_launch_alg_bytes):
         return None
     if d.get("kernel_source_hash") != gemm_source_hash():
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d.get("hbm_bytes_per_launch", {}).get("total")
+
+
+def uses_128_token_tiles(T, d_out):
+    """The GEMM launcher's tile choice: 128-token tiles unless that gives fewer than
+    512 workgroups."""
+    return ((T + 127) // 128) * ((d_out + 255) // 256) >= 512
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 28  # 1 GiB of float32, four times the Infinity Cache
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(5):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / 5
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "ms": round(ms, 4),
+                      "gbs_read_plus_write": round(8 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures the QE linear on exactly one GPU; multi-GPU runs are not part of this "
@@ -180,7 +214,10 @@ def main():
         per_linear.append(dict(name=spec.name, d_in=spec.d_in, d_out=spec.d_out,
                                gemm_us=round(float(gemm_ms[:, i].mean()) * 1e3, 2),
                                gemm_tops=round(2 * im / (gemm_ms[:, i].mean() * 1e-3) / 1e12, 1)))
-    achieved = int_ops / (gemm_ms_step * 1e-3) / 1e12
+    big = [i for i, (spec, _) in enumerate(layers) if uses_128_token_tiles(T, spec.d_out)]
+    big_ops = sum(2 * libqe.qe_linear_cost(layers[i][1].lin, T, 1, 2)[0] for i in big)
+    big_ms = float(gemm_ms[:, big].sum(axis=1).mean())  # per step
+    achieved = big_ops / (big_ms * 1e-3) / 1e12
     t_roof = max(int_ops / (PEAK_INT8_TOPS * 1e12) + adapter_flops / (PEAK_BF16_TFLOPS * 1e12),
                  alg_bytes / (PEAK_HBM_GBS * 1e9))
     traffic = load_traffic(None)
@@ -204,15 +241,16 @@ def main():
             "T": T, "w_bits": 4, "a_bits": 6, "r_shared": 32, "n_routed": 8, "r_routed": 32,
         },
         "roofline": {
-            "kernel": "gemm_w4_kernel (int8 MFMA main GEMM + fused dequant/SE/RE epilogue)",
+            "kernel": "gemm_w4_kernel<8, true> (int8 MFMA main GEMM, 128-token tiles, fused dequant/SE/RE epilogue)",
             "bound": "mfma",
             "achieved": round(achieved, 1),
             "peak": PEAK_INT8_TOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_INT8_TOPS, 4),
             "traffic": traffic,
-            "launches_per_step": len(layers),
-            "avg_launch_us": round(gemm_ms_step / len(layers) * 1e3, 2),
+            "launches_per_step": len(big),
+            "avg_launch_us": round(big_ms / len(big) * 1e3, 2),
+            "ops_per_launch": round(big_ops / len(big)),
         },
         "layer_roofline": {
             "t_roof_ms": round(t_roof * 1e3, 4),
