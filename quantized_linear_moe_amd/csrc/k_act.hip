@@ -492,12 +492,13 @@ constexpr int RP_TOK = 64;
 constexpr int RP_KG = 128;             // channels per group
 constexpr int RP_MAXN = 5;             // up to 80 projected columns
 
-template <int MP>  // projection-row pieces (16 B) per thread and group: 3 (<= 48 rows) or 5 (<= 80)
+template <int NBK>  // 16-row blocks of projection rows (ncols = 16*NBK <= 80); also the 16-B pieces per thread
 __global__ __launch_bounds__(256) void route_pass_kernel(const uint16_t* __restrict__ x, int T, int d_in,
                                                          const uint16_t* __restrict__ mt, int ncols,
                                                          const float* __restrict__ smooth,
                                                          const float* __restrict__ inv_smooth, int ksplit,
                                                          float* __restrict__ part, float* __restrict__ amax_part) {
+    constexpr int MP = NBK;  // ncols*16 chunks of 16 B over 256 threads
     constexpr int M_LDS = MP * 256 * 16;
     constexpr int BUF = M_LDS + 1024;
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
@@ -505,66 +506,86 @@ __global__ __launch_bounds__(256) void route_pass_kernel(const uint16_t* __restr
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int ngr = d_in / RP_KG;
     const int g_beg = (int)((long)ks * ngr / ksplit), g_end = (int)((long)(ks + 1) * ngr / ksplit);
-    const int nbk = ncols / 16;
     const int row = tok0 + wid * 16 + lr;
     const bool rvalid = row < T;
     const uint16_t* xrow = x + (size_t)min(row, T - 1) * d_in + lg * 32;  // rows past T repeat a valid row
 
-    v4f acc[RP_MAXN];
+    v4f acc[NBK > 0 ? NBK : 1];
 #pragma unroll
-    for (int n = 0; n < RP_MAXN; ++n) acc[n] = v4f{0, 0, 0, 0};
+    for (int n = 0; n < (NBK > 0 ? NBK : 1); ++n) acc[n] = v4f{0, 0, 0, 0};
     float amax = 0.0f;
 
-    for (int g = g_beg; g < g_end; ++g) {
-        uint8_t* buf = smem + (g & 1) * BUF;
+    // group g+1's loads are issued before group g is processed (two register sets; loads
+    // past the range repeat the last group and are not used)
+    struct Regs {
+        v4u x[4], m[MP > 0 ? MP : 1];
+        v4f s;
+    };
+    const uint16_t* msrc = ncols > 0 ? mt : x;  // without projection rows: any valid data, never used
+    auto load = [&](Regs& R, int g) {
         const size_t k0 = (size_t)g * RP_KG;
-        // one burst of loads
-        v4u xv[4], mv[MP];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) xv[s] = *reinterpret_cast<const v4u*>(xrow + k0 + s * 8);
+        for (int q = 0; q < 4; ++q) R.x[q] = *reinterpret_cast<const v4u*>(xrow + k0 + q * 8);
 #pragma unroll
         for (int p = 0; p < MP; ++p) {
             const int idx = tid + 256 * p, r = idx >> 4, c = idx & 15;
-            mv[p] = r < ncols ? *reinterpret_cast<const v4u*>(mt + (size_t)r * d_in + k0 + c * 8) : v4u{0, 0, 0, 0};
+            R.m[p] = *reinterpret_cast<const v4u*>(msrc + (size_t)min(r, max(ncols - 1, 0)) * d_in + k0 + c * 8);
         }
-        v4f sv = v4f{0, 0, 0, 0};
-        if (tid < 64) sv = *reinterpret_cast<const v4f*>((tid < 32 ? smooth : inv_smooth) + k0 + (tid & 31) * 4);
+        R.s = *reinterpret_cast<const v4f*>(((tid & 32) ? inv_smooth : smooth) + k0 + (tid & 31) * 4);
+    };
+    auto process = [&](const Regs& R, int g) {
+        uint8_t* buf = smem + (g & 1) * BUF;
 #pragma unroll
         for (int p = 0; p < MP; ++p) {
             const int idx = tid + 256 * p, r = idx >> 4, c = idx & 15;
-            if (r < ncols) *reinterpret_cast<v4u*>(buf + r * 256 + ((c ^ (r & 15)) << 4)) = mv[p];
+            if (r < ncols) *reinterpret_cast<v4u*>(buf + r * 256 + ((c ^ (r & 15)) << 4)) = R.m[p];
         }
-        if (tid < 64) *reinterpret_cast<v4f*>(buf + M_LDS + tid * 16) = sv;
-        __syncthreads();  // (the other buffer was last read before this barrier)
+        if (tid < 64) *reinterpret_cast<v4f*>(buf + M_LDS + tid * 16) = R.s;
+        // the stores above are complete in every wave (the other buffer was last read
+        // before this barrier); the next group's loads stay in flight
+        QE_WAIT_LDS();
+        QE_WG_BARRIER();
         if (rvalid) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint8_t* sp = buf + M_LDS + (lg * 32 + s * 8) * 4;
+            for (int q = 0; q < 4; ++q) {
+                const uint8_t* sp = buf + M_LDS + (lg * 32 + q * 8) * 4;
                 const v4f s0 = *reinterpret_cast<const v4f*>(sp), s1 = *reinterpret_cast<const v4f*>(sp + 16);
                 const v4f i0 = *reinterpret_cast<const v4f*>(sp + 512), i1 = *reinterpret_cast<const v4f*>(sp + 528);
                 float xs[8];
-                smooth_div8(xv[s], s0, s1, i0, i1, xs);
+                smooth_div8(R.x[q], s0, s1, i0, i1, xs);
 #pragma unroll
-                for (int q = 0; q < 8; ++q) amax = fmaxf(amax, __builtin_fabsf(xs[q]));
+                for (int e = 0; e < 8; ++e) amax = fmaxf(amax, __builtin_fabsf(xs[e]));
             }
         }
+        v8bf bv[4][NBK > 0 ? NBK : 1];  // all B fragments of the group first, then the MFMAs
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int n = 0; n < RP_MAXN; ++n) {
-                if (n >= nbk) break;
+            for (int n = 0; n < NBK; ++n) {
                 const int rm = n * 16 + lr;
-                const v8bf bv = *reinterpret_cast<const v8bf*>(buf + rm * 256 + (((lg * 4 + s) ^ (rm & 15)) << 4));
-                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const v8bf*>(&xv[s]), bv, acc[n], 0,
-                                                                 0, 0);
+                bv[q][n] = *reinterpret_cast<const v8bf*>(buf + rm * 256 + (((lg * 4 + q) ^ (rm & 15)) << 4));
             }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int n = 0; n < NBK; ++n)
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const v8bf*>(&R.x[q]), bv[q][n],
+                                                                 acc[n], 0, 0, 0);
+    };
+    if (g_beg < g_end) {
+        Regs A, B;
+        load(A, g_beg);
+        for (int g = g_beg; g < g_end; g += 2) {
+            load(B, min(g + 1, g_end - 1));
+            process(A, g);
+            load(A, min(g + 2, g_end - 1));
+            if (g + 1 < g_end) process(B, g + 1);
         }
     }
 
     float* out = part + (size_t)ks * T * ncols;
 #pragma unroll
-    for (int n = 0; n < RP_MAXN; ++n) {
-        if (n >= nbk) break;
+    for (int n = 0; n < NBK; ++n) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int t = tok0 + wid * 16 + lg * 4 + r;
@@ -591,12 +612,18 @@ hipError_t launch_route_pass(const uint16_t* x, int T, int d_in, const uint16_t*
         !inv_smooth)
         return hipErrorInvalidValue;
     const dim3 grid((T + RP_TOK - 1) / RP_TOK, ksplit);
-    if (ncols <= 48)
-        hipLaunchKernelGGL(route_pass_kernel<3>, grid, dim3(256), 0, st, x, T, d_in, mt, ncols, smooth, inv_smooth,
-                           ksplit, part, amax_part);
-    else
-        hipLaunchKernelGGL(route_pass_kernel<5>, grid, dim3(256), 0, st, x, T, d_in, mt, ncols, smooth, inv_smooth,
-                           ksplit, part, amax_part);
+#define QE_RP_LAUNCH(NB)                                                                                            \
+    hipLaunchKernelGGL(route_pass_kernel<NB>, grid, dim3(256), 0, st, x, T, d_in, mt, ncols, smooth, inv_smooth, \
+                       ksplit, part, amax_part)
+    switch (ncols / 16) {
+        case 0: QE_RP_LAUNCH(0); break;
+        case 1: QE_RP_LAUNCH(1); break;
+        case 2: QE_RP_LAUNCH(2); break;
+        case 3: QE_RP_LAUNCH(3); break;
+        case 4: QE_RP_LAUNCH(4); break;
+        default: QE_RP_LAUNCH(5); break;
+    }
+#undef QE_RP_LAUNCH
     return hipGetLastError();
 }
 
@@ -840,7 +867,10 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
                 for (int q = 0; q < 2; ++q) *reinterpret_cast<v4u*>(buf + (2 * wid + q) * 1024 + lane * 16) = bv[q];
             }
             if (first && tid < 64) *reinterpret_cast<v4f*>(buf + B_LDS + tid * 16) = sv;
-            __syncthreads();  // (the other buffer was last read before this barrier)
+            // the stores above are complete in every wave (the other buffer was last read
+            // before this barrier); earlier code stores need not have landed
+            QE_WAIT_LDS();
+            QE_WG_BARRIER();
             if (first) {
                 v2u cw[4];
 #pragma unroll
@@ -861,18 +891,21 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
             if (NBR) {
                 const v4u zero4 = v4u{0, 0, 0, 0};
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
+                for (int j = 0; j < ESLOTS; ++j) {
+                    if (ex[j] < 0) break;  // uniform
+                    v8bf bq[4][NB1];  // the slot's fragments of the group first, then its MFMAs
 #pragma unroll
-                    for (int j = 0; j < ESLOTS; ++j) {
-                        if (ex[j] < 0) break;  // uniform
+                    for (int s = 0; s < 4; ++s)
+#pragma unroll
+                        for (int n = 0; n < NB1; ++n)
+                            bq[s][n] = *reinterpret_cast<const v8bf*>(buf + ((j * NB1 + n) * 4 + s) * 1024 + lane * 16);
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) {
                         const v4u am = e_row == ex[j] ? xv[s] : zero4;
 #pragma unroll
-                        for (int n = 0; n < NB1; ++n) {
-                            const v8bf bq =
-                                *reinterpret_cast<const v8bf*>(buf + ((j * NB1 + n) * 4 + s) * 1024 + lane * 16);
-                            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const v8bf*>(&am), bq,
-                                                                             acc[n], 0, 0, 0);
-                        }
+                        for (int n = 0; n < NB1; ++n)
+                            acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const v8bf*>(&am),
+                                                                             bq[s][n], acc[n], 0, 0, 0);
                     }
                 }
             }

@@ -253,7 +253,7 @@ int skinny_ksplit(int d_in, int d_out) {
 }
 
 // K splits of the small-T x-projection: few partials per output, so its reduction stays short
-int skinny_ksplit_proj(int d_in) { return std::max(1, std::min(d_in / 128, 32)); }
+int skinny_ksplit_proj(int d_in) { return std::max(1, std::min(d_in / 128, 128)); }
 
 // w_bits 3 / 4: packed tiles; w_bits 16: bf16 rows (the x-projection matrix), n_cols columns
 hipError_t launch_skinny(const void* x, int x_dtype, int T, int d_in, int n_cols, int w_bits, const void* w_tiled,

@@ -86,13 +86,49 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     };
     const uint32_t lds0 = lds_addr(smem);
 
+    // The tile's rows, read once: token, activation scale and routed expert (clamped into
+    // range) go to LDS for the DMA sources and the epilogue; every wave derives the set of
+    // experts present.  Two bursts of loads: the tokens, then what they index.
+    __shared__ int s_tok[BM];
+    __shared__ __attribute__((aligned(16))) float s_sx[BM];
+    __shared__ int s_ex[BM];
+    const bool routed = v != nullptr && expert != nullptr && bt_r != nullptr && rr_pad > 0 && n_r > 0;
+    uint32_t present = 0;
+    {
+        constexpr int RPL = (BM + 63) / 64;  // rows per lane
+        int tk[RPL], ex[RPL];
+        float sx[RPL];
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) tk[i] = perm ? perm[min(m0 + 64 * i + lane, T - 1)] : min(m0 + 64 * i + lane, T - 1);
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            sx[i] = s_x[tk[i]];
+            ex[i] = routed ? expert[tk[i]] : 0;
+        }
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const int r = 64 * i + lane;
+            const int e = (routed && m0 + r < T) ? min(max(ex[i], 0), n_r - 1) : -1;
+            if (routed)
+                for (int q = 0; q < n_r; ++q)
+                    if (__ballot(e == q)) present |= 1u << q;
+            if (wid == 0) {
+                s_tok[r] = tk[i];
+                s_sx[r] = sx[i];
+                s_ex[r] = e;
+            }
+        }
+    }
+    __syncthreads();
+
+
     // DMA sources.  A: copy q = wid + 4p covers tile rows 16q..16q+15; lane i fetches the
     // logical chunk stored at its LDS slot (row 16q + i/4, slot i%4).
     const int8_t* a_src[A_DMA];
 #pragma unroll
     for (int p = 0; p < A_DMA; ++p) {
         const int q = wid + 4 * p, r = 16 * q + (lane >> 2), c = (lane & 3) ^ a_swz(r);
-        a_src[p] = codes + (size_t)token(m0 + r) * d_in + c * 16;
+        a_src[p] = codes + (size_t)s_tok[r] * d_in + c * 16;
     }
     // B: copy p of this wave moves the 512-byte K-step tiles of N blocks 2p and 2p+1
     // (lanes 0-31 and 32-63); blocks past d_out fetch block 0 and are never stored.
@@ -113,28 +149,6 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     bool nb_ok[G_NBW];
 #pragma unroll
     for (int j = 0; j < G_NBW; ++j) nb_ok[j] = (nb0 + j) < NB;
-
-    // The tile's rows, read once: token, activation scale and routed expert (clamped
-    // into range) go to LDS for the epilogue; every wave derives the set of experts present.
-    __shared__ int s_tok[BM];
-    __shared__ __attribute__((aligned(16))) float s_sx[BM];
-    __shared__ int s_ex[BM];
-    const bool routed = v != nullptr && expert != nullptr && bt_r != nullptr && rr_pad > 0 && n_r > 0;
-    uint32_t present = 0;
-#pragma unroll
-    for (int r0 = 0; r0 < BM; r0 += 64) {
-        const int r = r0 + lane, pos = m0 + r;
-        const int tk = token(pos);
-        const int ex = (routed && pos < T) ? min(max(expert[tk], 0), n_r - 1) : -1;
-        if (routed)
-            for (int e = 0; e < n_r; ++e)
-                if (__ballot(ex == e)) present |= 1u << e;
-        if (wid == 0) {
-            s_tok[r] = tk;
-            s_sx[r] = s_x[tk];
-            s_ex[r] = ex;
-        }
-    }
 
     v4i acc[MB][G_NBW];
 #pragma unroll

@@ -31,6 +31,10 @@ __device__ inline uint32_t lds_addr(T* p) {
 #define QE_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 // vmcnt <= n and every LDS access of this wave completed (lgkmcnt 0)
 #define QE_WAIT_VMCNT_LDS(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4))
+// every LDS access of this wave completed (lgkmcnt 0); vector-memory loads stay in flight
+#define QE_WAIT_LDS() __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4))
+// Workgroup barrier without the memory fence of __syncthreads (which also waits for every
+// outstanding global load): callers wait for what the barrier must order themselves.
 #define QE_WG_BARRIER()                   \
     do {                                  \
         asm volatile("" ::: "memory");    \
