@@ -46,7 +46,7 @@ hipError_t launch_colmean(const void* W, int dtype, int d_out, int d_in, float* 
 }
 
 // ----------------------------------------------------------------------- top-k
-constexpr int TK_THREADS = 256;
+constexpr int TK_THREADS = 256;  // one thread per radix bin in the digit search
 constexpr int TK_MAX_K = 1024;
 constexpr int TK_MAX_D = 32768;
 
@@ -106,15 +106,18 @@ __global__ __launch_bounds__(TK_THREADS) void topk_kernel(const void* __restrict
             if ((key & mask) == prefix) atomicAdd(&bins[(key >> shift) & 255u], 1u);
         }
         __syncthreads();
-        if (tid == 0) {
-            uint32_t rem = s_remaining, above = 0;
-            int b = 255;
-            for (; b > 0; --b) {
-                if (above + bins[b] >= rem) break;
-                above += bins[b];
+        // digit of the k-th largest: bins in descending order, one per thread; the thread
+        // whose inclusive prefix first reaches the remaining count owns it (exactly one does,
+        // as the bins hold every key still matching the prefix)
+        {
+            const uint32_t rem = s_remaining;
+            const uint32_t cnt = bins[255 - tid];
+            uint32_t total;
+            const uint32_t excl = block_excl_scan(cnt, wave_tot, &total);
+            if (excl < rem && excl + cnt >= rem) {
+                s_remaining = rem - excl;
+                s_prefix = prefix | ((uint32_t)(255 - tid) << shift);
             }
-            s_remaining = rem - above;
-            s_prefix = prefix | ((uint32_t)b << shift);
         }
         __syncthreads();
         prefix = s_prefix;
