@@ -20,12 +20,6 @@ namespace qe {
 // ---------------------------------------------------------------- helpers
 __device__ inline float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// float32 -> bf16 bits, round to nearest even (inputs finite)
-__device__ inline uint32_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
 // a / b correctly rounded, given inv_b = RN(1/b).  One multiply and two fused
 // multiply-adds (Markstein's correction).  Exact for |a| in [2^-100, 2^100] and b
 // in [2^-90, 2^90] with quotients of magnitude >= 2^-3; callers fall back to the

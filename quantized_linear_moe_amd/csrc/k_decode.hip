@@ -119,29 +119,44 @@ __device__ inline void load_frag(const uint32_t* __restrict__ w, int nb, int NB,
     }
 }
 
-// part[ks][t][c] = sum over this workgroup's K range of bf16(x)[t][k] * W[c][k], for the
-// token tile t0..t0+15 and channels c of its 8 channel blocks (out_ld = row stride of part).
-template <int WB>
-__global__ __launch_bounds__(256) void skinny_kernel(const void* __restrict__ x, int x_dtype, int T, int t0, int d_in,
-                                                     int n_cols, const uint32_t* __restrict__ w_tiled, int ksplit,
-                                                     float* __restrict__ part, int out_ld) {
+// One workgroup's tile of a split-K product:
+//   part[ks][t][c] = sum over the K blocks [kb0, kb1) of split ks of bf16(x)[t][k] * W[c][k]
+// for tokens t0 .. t0+15 and the NBW 16-channel blocks starting at nb0 (blocks at or past NB
+// add nothing and are not written); out_ld = row stride of part, ld = LDS row stride of the
+// x tile (>= 256 * (kb1 - kb0) + 16).
+template <int WB, int NBW>
+__device__ __attribute__((always_inline)) inline void skinny_tile(const void* __restrict__ x, int x_dtype, int T, int t0,
+                                                                  int d_in, int NB, int nb0,
+                                                                  const uint32_t* __restrict__ w_tiled, int ks,
+                                                                  int ksplit, int ld, float* __restrict__ part,
+                                                                  int out_ld) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint8_t* xs = smem;                          // [ntok][SK_LD] x tile
-    float* red = reinterpret_cast<float*>(smem);  // [4][SK_NB][64][4], reuses the LDS after the main loop
-    const int NB = n_cols >> 4, KB = d_in >> 7;
-    const int grp = blockIdx.x, ks = blockIdx.y;
+    uint8_t* xs = smem;                          // [ntok][ld] x tile
+    float* red = reinterpret_cast<float*>(smem);  // [4][NBW][64][4], reuses the LDS after the main loop
+    const int KB = d_in >> 7;
     const int kb0 = (int)((long)ks * KB / ksplit), kb1 = (int)((long)(ks + 1) * KB / ksplit);
     const int nkb = kb1 - kb0;
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int ntok = min(16, T - t0);
     constexpr int FW = Frag<WB>::kWords;
+    // the next K block is prefetched into registers except for wide bf16 tiles, whose
+    // fragments are 4x larger (two waves per SIMD)
+    constexpr bool kPrefetch = WB != 16 || NBW <= 2;
 
-    // weight fragments of this wave's first K block are requested before the x tile is staged
-    uint32_t f[SK_NB][FW], fn[SK_NB][FW];
+    // weight fragments of this wave's first K block are requested before the x tile is staged.
+    // With prefetching, loads are unconditional: channel blocks past NB and K blocks past the
+    // wave's range read a valid block instead (discarded), because a branch around a load makes
+    // the compiler wait for every load in flight.
+    uint32_t f[NBW][FW], fn[NBW][FW];
     int kb = kb0 + wid;
-    if (kb < kb1) {
+    auto nbc = [&](int j) { return min(nb0 + j, NB - 1); };
+    auto kbc = [&](int k) { return min(k, kb1 - 1); };
+    if constexpr (kPrefetch) {
 #pragma unroll
-        for (int j = 0; j < SK_NB; ++j) load_frag<WB>(w_tiled, grp * SK_NB + j, NB, kb, KB, lane, d_in, f[j]);
+        for (int j = 0; j < NBW; ++j) load_frag<WB>(w_tiled, nbc(j), NB, kbc(kb), KB, lane, d_in, f[j]);
+    } else if (kb < kb1) {
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) load_frag<WB>(w_tiled, nb0 + j, NB, kb, KB, lane, d_in, f[j]);
     }
 
     // stage x[t0 .. t0+ntok)[kb0*128 .. kb1*128) as bf16, eight independent 16-byte loads
@@ -176,58 +191,66 @@ __global__ __launch_bounds__(256) void skinny_kernel(const void* __restrict__ x,
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int i = base + q * 256 + tid;
-            if (i < total) *reinterpret_cast<v4u*>(xs + (i / kc8) * SK_LD + (i % kc8) * 16) = val[q];
+            if (i < total) *reinterpret_cast<v4u*>(xs + (i / kc8) * ld + (i % kc8) * 16) = val[q];
         }
     }
     __syncthreads();
 
-    v4f acc[SK_NB];
+    v4f acc[NBW];
 #pragma unroll
-    for (int j = 0; j < SK_NB; ++j) acc[j] = v4f{0, 0, 0, 0};
+    for (int j = 0; j < NBW; ++j) acc[j] = v4f{0, 0, 0, 0};
 
-    for (; kb < kb1; kb += 4) {
-        // next K block of this wave, one block ahead (the bf16 rows are 4x larger and are
-        // not double-buffered, to keep two waves per SIMD)
-        const bool more = WB != 16 && kb + 4 < kb1;
-        if (more) {
-#pragma unroll
-            for (int j = 0; j < SK_NB; ++j) load_frag<WB>(w_tiled, grp * SK_NB + j, NB, kb + 4, KB, lane, d_in, fn[j]);
-        }
-        const uint8_t* xrow = xs + lr * SK_LD + (kb - kb0) * 256;
+    // MFMAs of one K block held in w[] (x from the LDS tile; a block past the range gets zero x)
+    auto mma = [&](const uint32_t (&w)[NBW][FW], int k) {
+        const bool use = lr < ntok && k < kb1;
+        const uint8_t* xrow = xs + lr * ld + (kbc(k) - kb0) * 256;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const v8bf a = lr < ntok ? *reinterpret_cast<const v8bf*>(xrow + x_step_offset<WB>(s, lg) * 2) : v8bf{};
+            const v8bf a = use ? *reinterpret_cast<const v8bf*>(xrow + x_step_offset<WB>(s, lg) * 2) : v8bf{};
 #pragma unroll
-            for (int j = 0; j < SK_NB; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, weight_frag<WB>(f[j], s), acc[j], 0, 0, 0);
+            for (int j = 0; j < NBW; ++j)
+                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, weight_frag<WB>(w[j], s), acc[j], 0, 0, 0);
         }
-        if (more) {
+    };
+    if constexpr (kPrefetch) {
+        // two register buffers in turn, one K block (4 apart: the waves interleave) ahead; the
+        // trip count is fixed and the body has no branch, so each wait is for the older buffer
+        // only and the other stays in flight
+        const int npair = (max(kb1 - kb, 0) + 7) / 8;
+        for (int p = 0; p < npair; ++p, kb += 8) {
 #pragma unroll
-            for (int j = 0; j < SK_NB; ++j)
+            for (int j = 0; j < NBW; ++j) load_frag<WB>(w_tiled, nbc(j), NB, kbc(kb + 4), KB, lane, d_in, fn[j]);
+            mma(f, kb);
 #pragma unroll
-                for (int q = 0; q < FW; ++q) f[j][q] = fn[j][q];
-        } else if (WB == 16 && kb + 4 < kb1) {
+            for (int j = 0; j < NBW; ++j) load_frag<WB>(w_tiled, nbc(j), NB, kbc(kb + 8), KB, lane, d_in, f[j]);
+            mma(fn, kb + 4);
+        }
+    } else {
+        for (; kb < kb1; kb += 4) {
+            mma(f, kb);
+            if (kb + 4 < kb1) {
 #pragma unroll
-            for (int j = 0; j < SK_NB; ++j) load_frag<WB>(w_tiled, grp * SK_NB + j, NB, kb + 4, KB, lane, d_in, f[j]);
+                for (int j = 0; j < NBW; ++j) load_frag<WB>(w_tiled, nb0 + j, NB, kb + 4, KB, lane, d_in, f[j]);
+            }
         }
     }
     // reduce the 4 waves' accumulators (fixed order) through LDS
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < SK_NB; ++j)
-        *reinterpret_cast<v4f*>(red + ((wid * SK_NB + j) * 64 + lane) * 4) = acc[j];
+    for (int j = 0; j < NBW; ++j)
+        *reinterpret_cast<v4f*>(red + ((wid * NBW + j) * 64 + lane) * 4) = acc[j];
     __syncthreads();
     if (wid == 0) {
         float* out = part + (size_t)ks * T * out_ld;
 #pragma unroll
-        for (int j = 0; j < SK_NB; ++j) {
-            v4f sum = *reinterpret_cast<const v4f*>(red + ((0 * SK_NB + j) * 64 + lane) * 4);
+        for (int j = 0; j < NBW; ++j) {
+            v4f sum = *reinterpret_cast<const v4f*>(red + ((0 * NBW + j) * 64 + lane) * 4);
 #pragma unroll
             for (int w = 1; w < 4; ++w) {
-                const v4f o = *reinterpret_cast<const v4f*>(red + ((w * SK_NB + j) * 64 + lane) * 4);
+                const v4f o = *reinterpret_cast<const v4f*>(red + ((w * NBW + j) * 64 + lane) * 4);
                 sum += o;
             }
-            const int nb = grp * SK_NB + j;
+            const int nb = nb0 + j;
             if (nb >= NB) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -235,6 +258,37 @@ __global__ __launch_bounds__(256) void skinny_kernel(const void* __restrict__ x,
                 if (tt < ntok) out[(size_t)(t0 + tt) * out_ld + nb * 16 + lr] = sum[r];
             }
         }
+    }
+}
+
+template <int WB>
+__global__ __launch_bounds__(256) void skinny_kernel(const void* __restrict__ x, int x_dtype, int T, int t0, int d_in,
+                                                     int n_cols, const uint32_t* __restrict__ w_tiled, int ksplit,
+                                                     float* __restrict__ part, int out_ld) {
+    skinny_tile<WB, SK_NB>(x, x_dtype, T, t0, d_in, n_cols >> 4, blockIdx.x * SK_NB, w_tiled, blockIdx.y, ksplit,
+                           SK_LD, part, out_ld);
+}
+
+// Decode GEMV, one launch for both streams of a weight-only linear with T <= 16: the first
+// n_pwg workgroups project x onto Mt (the shared-expert, router and routed-expert input
+// matrices, bf16 rows) two channel blocks at a time, the rest stream the packed weights
+// eight channel blocks at a time; each writes split-K partials for the finish kernel.  The
+// register budget is three waves per SIMD: the plan's three workgroups per compute unit.
+template <int WB>
+__global__ __launch_bounds__(256, 3) void decode_gemv_kernel(const void* __restrict__ x, int x_dtype, int T, int d_in,
+                                                          int d_out, const uint32_t* __restrict__ w_tiled, int ks_m,
+                                                          int ld_m, float* __restrict__ part_m,
+                                                          const uint32_t* __restrict__ mt, int ncp, int ks_p, int ld_p,
+                                                          float* __restrict__ part_p, int n_pwg) {
+    const int bid = blockIdx.x;
+    if (bid < n_pwg) {
+        const int NBp = ncp >> 4, pgroups = (NBp + 1) >> 1;
+        skinny_tile<16, 2>(x, x_dtype, T, 0, d_in, NBp, (bid % pgroups) * 2, mt, bid / pgroups, ks_p, ld_p,
+                           part_p, ncp);
+    } else {
+        const int b = bid - n_pwg, NB = d_out >> 4, groups = (NB + SK_NB - 1) / SK_NB;
+        skinny_tile<WB, SK_NB>(x, x_dtype, T, 0, d_in, NB, (b % groups) * SK_NB, w_tiled, b / groups, ks_m, ld_m,
+                               part_m, d_out);
     }
 }
 
@@ -276,6 +330,192 @@ hipError_t launch_skinny(const void* x, int x_dtype, int T, int d_in, int n_cols
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+// ------------------------------------------------------------------ fused decode
+// Split-K plan of decode_gemv_kernel: workgroups stream about the same number of bytes and
+// all of them are resident in one round (three per compute unit: the kernel's register
+// footprint), so none starts late and the tail is one memory latency.  The x tile of a
+// workgroup fits a third of the LDS.
+constexpr int DG_WG_PER_CU = 3;
+constexpr int DG_SLOTS = DG_WG_PER_CU * 256;
+constexpr int DG_TILE_BUDGET = 52 * 1024;
+constexpr int DG_MAX_KBLK = 32;
+
+DecodePlan decode_plan(int d_in, int d_out, int w_bits, int ncp, int T) {
+    DecodePlan P{};
+    const int KB = d_in / 128, ntok = std::min(16, std::max(T, 1));
+    const int groups = (d_out / 16 + SK_NB - 1) / SK_NB;
+    const int pgroups = (ncp / 16 + 1) / 2;
+    const double mblk = 128.0 * 128.0 * w_bits / 8.0;  // bytes of one main K block (8 channel blocks)
+    const double pblk = 32.0 * 128.0 * 2.0;            // bytes of one projection K block (2 channel blocks, bf16)
+    const double total = (double)groups * KB * mblk + (double)pgroups * KB * pblk;
+    const double per_wg = total / DG_SLOTS;
+    const int cap = std::max(1, std::min(DG_MAX_KBLK, (DG_TILE_BUDGET / ntok - 16) / 256));
+    const int ks_min = (KB + cap - 1) / cap;  // splits needed for the x tile to fit
+    auto clampks = [&](int ks) { return std::max(ks_min, std::min(KB, std::max(1, ks))); };
+    P.ks_m = clampks((int)std::lround(KB * mblk / per_wg));
+    P.n_mwg = groups * P.ks_m;
+    if (pgroups > 0) {
+        // the projection takes the slots the main weights leave, at about the same bytes per workgroup
+        const int fit = (DG_SLOTS - P.n_mwg) / pgroups;
+        P.ks_p = clampks(std::min((int)std::lround(KB * pblk / per_wg), fit));
+    }
+    P.n_pwg = pgroups * P.ks_p;
+    P.ld_m = (KB + P.ks_m - 1) / P.ks_m * 256 + 16;
+    P.ld_p = pgroups > 0 ? (KB + P.ks_p - 1) / P.ks_p * 256 + 16 : 0;
+    P.lds = std::max({(size_t)ntok * P.ld_m, (size_t)ntok * P.ld_p, SK_RED_BYTES});
+    return P;
+}
+
+hipError_t launch_decode_gemv(const void* x, int x_dtype, int T, int d_in, int d_out, int w_bits, const void* w_tiled,
+                              const DecodePlan& P, float* part_m, const uint16_t* mt, int ncp, float* part_p,
+                              hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (T > 16 || P.lds > 64 * 1024) return hipErrorInvalidValue;
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(w_tiled);
+    const uint32_t* m = reinterpret_cast<const uint32_t*>(mt);
+    const int nwg = P.n_pwg + P.n_mwg;
+    if (w_bits == 3) {
+        hipLaunchKernelGGL(decode_gemv_kernel<3>, dim3(nwg), dim3(256), P.lds, st, x, x_dtype, T, d_in, d_out, w, P.ks_m,
+                           P.ld_m, part_m, m, ncp, P.ks_p, P.ld_p, part_p, P.n_pwg);
+    } else {
+        hipLaunchKernelGGL(decode_gemv_kernel<4>, dim3(nwg), dim3(256), P.lds, st, x, x_dtype, T, d_in, d_out, w, P.ks_m,
+                           P.ld_m, part_m, m, ncp, P.ks_p, P.ld_p, part_p, P.n_pwg);
+    }
+    return hipGetLastError();
+}
+
+// Finish of the fused decode.  Every workgroup first turns the projection partials into the
+// routed expert of each token (argmin of the router scores, lowest index on ties) and the bf16
+// adapter inputs u (shared expert) and v (the token's routed expert), then writes, for its 64
+// channels and all tokens (wave w handles tokens w and w + 8),
+//   y[t][i] = s_w[i] * sum_ks part_m[ks][t][i] + u[t].Bt_s[i] + v[t].Bt_r[e_t][i]
+// Partials are summed in split order; their loads are issued in independent batches of 16 (a
+// dependent chain of loads would cost one memory latency per split), and the phases are
+// ordered so that about three memory latencies are exposed.
+constexpr int DF_CH = 64;
+constexpr int DF_THREADS = 512;
+
+// sum_k p[k * stride] for k = 0 .. n-1, in order
+__device__ inline float sum_splits(const float* __restrict__ p, size_t stride, int n) {
+    constexpr int B = 16;
+    float sum = 0.0f;
+    for (int k = 0; k < n; k += B) {
+        float a[B];
+#pragma unroll
+        for (int q = 0; q < B; ++q) a[q] = k + q < n ? p[(size_t)(k + q) * stride] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < B; ++q)
+            if (k + q < n) sum += a[q];
+    }
+    return sum;
+}
+
+__global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
+    const float* __restrict__ part_m, int ks_m, int T, int d_out, const float* __restrict__ w_scale,
+    const float* __restrict__ part_p, int ks_p, int ncp, int col_se, int r_s, int rs_pad, int col_re, int n_r,
+    int r_r, int rr_pad, int col_router, const uint16_t* __restrict__ bt_s, const uint16_t* __restrict__ bt_r,
+    int32_t* __restrict__ expert_out, float* __restrict__ y) {
+    __shared__ float s_sc[16][kMaxRouted];
+    __shared__ int s_e[16];
+    __shared__ float s_u[16][kMaxRank];
+    __shared__ float s_v[16][kMaxRank];
+    const int tid = threadIdx.x;
+    const int c = tid & (DF_CH - 1), t = tid >> 6;  // wave t: tokens t and t + 8
+    const int i = min(blockIdx.x * DF_CH + c, d_out - 1);
+    const size_t pstride = (size_t)T * ncp;
+
+    // 1. router scores and u (independent of each other)
+    const int nsc = T * n_r, nu = T * rs_pad;
+    for (int it = tid; it < nsc + nu; it += DF_THREADS) {
+        if (it < nsc) {
+            const int tt = it / n_r, e = it % n_r;
+            s_sc[tt][e] = sum_splits(part_p + (size_t)tt * ncp + col_router + e, pstride, ks_p);
+        } else {
+            const int tt = (it - nsc) / rs_pad, m = (it - nsc) % rs_pad;
+            const float a = m < r_s ? sum_splits(part_p + (size_t)tt * ncp + col_se + m, pstride, ks_p) : 0.0f;
+            s_u[tt][m] = __uint_as_float(f32_to_bf16_bits(a) << 16);
+        }
+    }
+    __syncthreads();
+    // 2. the routed expert of each token
+    if (n_r > 0 && tid < T) {
+        int e = 0;
+        float best = s_sc[tid][0];
+        for (int j = 1; j < n_r; ++j)
+            if (s_sc[tid][j] < best) {  // strict: the lowest index wins ties
+                best = s_sc[tid][j];
+                e = j;
+            }
+        s_e[tid] = e;
+        if (expert_out && blockIdx.x == 0) expert_out[tid] = e;
+    }
+    __syncthreads();
+    // 3. v of the selected experts, the shared-expert row and the main-weight sum
+    for (int it = tid; it < T * rr_pad; it += DF_THREADS) {
+        const int tt = it / rr_pad, m = it % rr_pad;
+        const float a =
+            m < r_r ? sum_splits(part_p + (size_t)tt * ncp + col_re + s_e[tt] * rr_pad + m, pstride, ks_p) : 0.0f;
+        s_v[tt][m] = __uint_as_float(f32_to_bf16_bits(a) << 16);
+    }
+    v4u bs[kMaxRank / 8];
+#pragma unroll
+    for (int q = 0; q < kMaxRank / 8; ++q)
+        bs[q] = 8 * q < rs_pad ? *reinterpret_cast<const v4u*>(bt_s + (size_t)i * rs_pad + 8 * q) : v4u{0, 0, 0, 0};
+    float out[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int tt = t + 8 * h;
+        out[h] = tt < T ? sum_splits(part_m + (size_t)tt * d_out + i, (size_t)T * d_out, ks_m) * w_scale[i] : 0.0f;
+    }
+    __syncthreads();
+    // 4. the routed expert's row, then the two dot products
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int tt = t + 8 * h;
+        if (tt >= T) break;  // wave-uniform; no barrier follows
+        const int e = n_r > 0 ? s_e[tt] : -1;
+        v4u br[kMaxRank / 8];
+        const uint16_t* row = bt_r + ((size_t)max(e, 0) * d_out + i) * rr_pad;
+#pragma unroll
+        for (int q = 0; q < kMaxRank / 8; ++q)
+            br[q] = (e >= 0 && 8 * q < rr_pad) ? *reinterpret_cast<const v4u*>(row + 8 * q) : v4u{0, 0, 0, 0};
+        float du = 0.0f, dv = 0.0f;
+#pragma unroll
+        for (int q = 0; q < kMaxRank / 8; ++q) {
+            if (8 * q >= rs_pad) break;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                du = __builtin_fmaf(s_u[tt][8 * q + 2 * k], __uint_as_float(bs[q][k] << 16), du);
+                du = __builtin_fmaf(s_u[tt][8 * q + 2 * k + 1], __uint_as_float(bs[q][k] & 0xFFFF0000u), du);
+            }
+        }
+        if (e >= 0) {
+#pragma unroll
+            for (int q = 0; q < kMaxRank / 8; ++q) {
+                if (8 * q >= rr_pad) break;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    dv = __builtin_fmaf(s_v[tt][8 * q + 2 * k], __uint_as_float(br[q][k] << 16), dv);
+                    dv = __builtin_fmaf(s_v[tt][8 * q + 2 * k + 1], __uint_as_float(br[q][k] & 0xFFFF0000u), dv);
+                }
+            }
+        }
+        if (blockIdx.x * DF_CH + c < d_out) y[(size_t)tt * d_out + i] = (out[h] + du) + dv;
+    }
+}
+
+hipError_t launch_decode_finish(const float* part_m, int ks_m, int T, int d_out, const float* w_scale,
+                                const float* part_p, int ks_p, int ncp, int col_se, int r_s, int rs_pad, int col_re,
+                                int n_r, int r_r, int rr_pad, int col_router, const uint16_t* bt_s,
+                                const uint16_t* bt_r, int32_t* expert_out, float* y, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (T > 16 || n_r > kMaxRouted || rs_pad > kMaxRank || rr_pad > kMaxRank) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(decode_finish_kernel, dim3((d_out + DF_CH - 1) / DF_CH), dim3(DF_THREADS), 0, st, part_m, ks_m, T,
+                       d_out, w_scale, part_p, ks_p, ncp, col_se, r_s, rs_pad, col_re, n_r, r_r, rr_pad, col_router,
+                       bt_s, bt_r, expert_out, y);
+    return hipGetLastError();
 }
 
 hipError_t skinny_set_attributes() {

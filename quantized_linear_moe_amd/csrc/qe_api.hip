@@ -149,13 +149,15 @@ WsLayout ws_layout(const qe_linear* lin, int T) {
     const size_t t = T > 0 ? T : 0;
     W.xproj_ksplit = xproj_ksplit(T, lin->d_in, P.n_cols_pad);
     W.skinny_ksplit = lin->a_bits == 16 ? skinny_ksplit(lin->d_in, lin->d_out) : 0;
+    const bool fused_decode = lin->a_bits == 16 && T <= kSkinnyMaxT;
+    const DecodePlan D = fused_decode ? decode_plan(lin->d_in, lin->d_out, lin->w_bits, P.n_cols_pad, T) : DecodePlan{};
     size_t off = 0;
     W.codes = off;
     off = align256(off + (lin->a_bits == 16 ? 0 : t * lin->d_in));
     W.s_x = off;
     off = align256(off + t * 4);
     W.part = off;
-    const int xks = std::max(W.xproj_ksplit, T <= kSkinnyMaxT ? skinny_ksplit_proj(lin->d_in) : 1);
+    const int xks = std::max({W.xproj_ksplit, T <= kSkinnyMaxT ? skinny_ksplit_proj(lin->d_in) : 1, D.ks_p});
     const bool two_pass = two_pass_sized(lin, T);
     W.rp_ksplit = two_pass ? route_pass_ksplit(T, lin->d_in) : 0;
     W.eq_ksplit = two_pass ? expert_quant_ksplit(T, lin->d_in) : 0;
@@ -180,7 +182,7 @@ WsLayout ws_layout(const qe_linear* lin, int T) {
     W.v = off;
     off = align256(off + t * P.rr_pad * 2);
     W.skinny = off;
-    off = align256(off + (size_t)W.skinny_ksplit * t * lin->d_out * 4);
+    off = align256(off + (size_t)std::max(W.skinny_ksplit, D.ks_m) * t * lin->d_out * 4);
     W.total = off;
     return W;
 }
@@ -527,6 +529,24 @@ int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int3
     int32_t* expert = route ? (expert_out ? expert_out : at<int32_t>(ws, W.expert)) : nullptr;
     uint16_t* u = P.rs_pad > 0 ? at<uint16_t>(ws, W.u) : nullptr;
     uint16_t* v = route ? at<uint16_t>(ws, W.v) : nullptr;
+    if (lin->a_bits == 16 && T <= kSkinnyMaxT) {
+        // decode: one launch streams the projection matrix and the packed weights, one finishes
+        int e = ensure_attributes();
+        if (e) return e;
+        const DecodePlan D = decode_plan(lin->d_in, lin->d_out, lin->w_bits, P.n_cols_pad, T);
+        float* part_m = at<float>(ws, W.skinny);
+        float* part_p = at<float>(ws, W.part);
+        QE_TRY_HIP(launch_decode_gemv(x, x_dtype, T, lin->d_in, lin->d_out, lin->w_bits,
+                                      at<const void>(lin->prep, P.w_tiled), D, part_m,
+                                      at<const uint16_t>(lin->prep, P.mt), P.n_cols_pad, part_p, s));
+        QE_TRY_HIP(launch_decode_finish(part_m, D.ks_m, T, lin->d_out, at<const float>(lin->prep, P.w_scale), part_p,
+                                        D.ks_p, P.n_cols_pad, P.col_se, lin->r_shared, P.rs_pad, P.col_re,
+                                        lin->n_routed, lin->r_routed, P.rr_pad, P.col_router,
+                                        P.rs_pad > 0 ? at<const uint16_t>(lin->prep, P.bt_s) : nullptr,
+                                        P.rr_pad > 0 ? at<const uint16_t>(lin->prep, P.bt_r) : nullptr,
+                                        route ? expert : nullptr, y, s));
+        return QE_OK;
+    }
     int8_t* codes = lin->a_bits != 16 ? at<int8_t>(ws, W.codes) : nullptr;
     float* s_x = lin->a_bits != 16 ? at<float>(ws, W.s_x) : nullptr;
     int32_t* perm = (route && lin->a_bits != 16) ? at<int32_t>(ws, W.perm) : nullptr;

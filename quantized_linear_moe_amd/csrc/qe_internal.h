@@ -22,6 +22,12 @@ constexpr int kMaxRank = 64;
 constexpr int kRankPad = 32;  // adapter ranks are padded to a multiple of one bf16 MFMA K step
 
 __host__ __device__ inline int rank_pad(int r) { return r <= 0 ? 0 : (r + kRankPad - 1) / kRankPad * kRankPad; }
+
+// float32 -> bf16 bits, round to nearest even (inputs finite)
+__device__ inline uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
 __host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // ---------------------------------------------------------- prepared-buffer map
@@ -111,6 +117,23 @@ hipError_t launch_skinny(const void* x, int x_dtype, int T, int d_in, int n_cols
                          int ksplit, float* part, int out_ld, hipStream_t st);
 int skinny_ksplit(int d_in, int d_out);
 int skinny_ksplit_proj(int d_in);
+
+// fused weight-only decode (T <= 16): one GEMV launch for the projection and the packed
+// weights, one finish launch
+struct DecodePlan {
+    int ks_m, ks_p;      // K splits of the main weights and of the projection
+    int n_mwg, n_pwg;    // workgroups of each stream
+    int ld_m, ld_p;      // LDS row strides of their x tiles
+    size_t lds;          // dynamic LDS bytes
+};
+DecodePlan decode_plan(int d_in, int d_out, int w_bits, int ncp, int T);
+hipError_t launch_decode_gemv(const void* x, int x_dtype, int T, int d_in, int d_out, int w_bits, const void* w_tiled,
+                              const DecodePlan& P, float* part_m, const uint16_t* mt, int ncp, float* part_p,
+                              hipStream_t st);
+hipError_t launch_decode_finish(const float* part_m, int ks_m, int T, int d_out, const float* w_scale,
+                                const float* part_p, int ks_p, int ncp, int col_se, int r_s, int rs_pad, int col_re,
+                                int n_r, int r_r, int rr_pad, int col_router, const uint16_t* bt_s,
+                                const uint16_t* bt_r, int32_t* expert_out, float* y, hipStream_t st);
 
 hipError_t launch_skinny_finish(const float* part, int ksplit, int T, int d_out, const float* w_scale,
                                 const uint16_t* u, const uint16_t* bt_s, int rs_pad, const uint16_t* v,

@@ -193,6 +193,25 @@ def test_decode_small_shapes(Q, w_bits, T, x_dtype):
     check_y(y.cpu().numpy(), ref, params, x, w_bits, 16, gpu_expert=expert.cpu().numpy())
 
 
+# weight-streaming GEMV: K ranges longer than the in-flight ring, workgroups whose waves get no
+# K block, a partial last channel group, 16 tokens (smaller x tile budget) and the largest d_in
+@pytest.mark.parametrize("w_bits,d_in,d_out,T", [(3, 4096, 1040, 8), (4, 3200, 400, 1), (3, 32768, 48, 2),
+                                                 (4, 1152, 4096, 16), (3, 8192, 272, 13)])
+def test_decode_stream_shapes(Q, w_bits, d_in, d_out, T):
+    cfg = synth.get_config("tiny")
+    spec = synth.LinearSpec("lin", d_in, d_out, "x")
+    params = synth.gen_linear(cfg, spec)
+    layer, _ = _layer(Q, cfg, spec, params, w_bits=w_bits, a_bits=16)
+    x = (torch.randn(T, d_in, generator=torch.Generator().manual_seed(d_in + T)) * 2).to(torch.bfloat16)
+    y = torch.empty(T, d_out, dtype=torch.float32, device=DEV)
+    expert = torch.empty(T, dtype=torch.int32, device=DEV)
+    layer.forward(x.to(DEV), y, expert)
+    torch.cuda.synchronize()
+    ref = oracle_for(params, x, w_bits, 16)
+    err = check_y(y.cpu().numpy(), ref, params, x, w_bits, 16, gpu_expert=expert.cpu().numpy())
+    print(f"stream W{w_bits} {d_in}x{d_out} T={T}: max rel err {err:.3e}")
+
+
 # ------------------------------------------------------------ edge cases
 def _custom(Q, d_in, d_out, T, w_bits=4, a_bits=8, r_s=8, n_r=4, r_r=8, seed=0, x_dtype=torch.bfloat16, x=None,
             R=None):
