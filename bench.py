@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--write-traffic", nargs=4, metavar="DIR",
+                    help="rocprofv3 CSV directories: bench FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE, "
+                         "copy WRITE_SIZE; writes the GEMM traffic summary under profiles/ and exits")
     return ap.parse_args()
 
 
@@ -74,6 +77,67 @@ def load_traffic(per_launch_alg_bytes):
     if d.get("kernel_source_hash") != gemm_source_hash():
         return None
     return d.get("hbm_bytes_per_launch", {}).get("total")
+
+
+TRAFFIC_KERNEL = "gemm_w4_kernel<8, true>"
+
+
+def write_traffic(d_bench_fetch, d_bench_write, d_copy_fetch, d_copy_write):
+    """Write profiles/gemm_w4_qwen2vl72b_traffic.json from four rocprofv3 --pmc runs (CSV output
+    directories): FETCH_SIZE and WRITE_SIZE of this benchmark (--steps 2 --warmup 1
+    --no-cpu-baseline --no-extras), then of --copy-calibration.  The counters of the dominant
+    GEMM are averaged over its dispatches and scaled by what they read for the 1 GiB copy."""
+    import csv
+    import glob
+
+    def rows(d):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not f:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        with open(f[0]) as fh:
+            return list(csv.DictReader(fh))
+
+    def mean_kib(d, counter, match):
+        vals = [float(r["Counter_Value"]) for r in rows(d)
+                if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
+        if not vals:
+            raise SystemExit(f"no {counter} rows for the kernel under {d}")
+        return sum(vals) / len(vals), len(vals)
+
+    is_gemm = lambda k: TRAFFIC_KERNEL in k
+    is_copy = lambda k: "copyBuffer" in k
+    g_fetch, n_fetch = mean_kib(d_bench_fetch, "FETCH_SIZE", is_gemm)
+    g_write, n_write = mean_kib(d_bench_write, "WRITE_SIZE", is_gemm)
+    c_fetch, _ = mean_kib(d_copy_fetch, "FETCH_SIZE", is_copy)
+    c_write, _ = mean_kib(d_copy_write, "WRITE_SIZE", is_copy)
+    copy_bytes = 1 << 30
+    f_fetch, f_write = copy_bytes / (c_fetch * 1024), copy_bytes / (c_write * 1024)
+    fetch, write = g_fetch * 1024 * f_fetch, g_write * 1024 * f_write
+    cmd = "rocprofv3 --pmc {c} --output-format csv -d {d} -o p -- python3 bench.py {a}"
+    bench_args = "--steps 2 --warmup 1 --no-cpu-baseline --no-extras"
+    out = {
+        "kernel": TRAFFIC_KERNEL,
+        "workload": "Qwen2VL-72B layer linears q, o, gate, up, down; W4A6; T=4096; averaged over their launches",
+        "kernel_source_hash": gemm_source_hash(),
+        "commands": [cmd.format(c="FETCH_SIZE", d=d_bench_fetch, a=bench_args),
+                     cmd.format(c="WRITE_SIZE", d=d_bench_write, a=bench_args),
+                     cmd.format(c="FETCH_SIZE", d=d_copy_fetch, a="--copy-calibration"),
+                     cmd.format(c="WRITE_SIZE", d=d_copy_write, a="--copy-calibration")],
+        "gemm_dispatches_averaged": {"FETCH_SIZE": n_fetch, "WRITE_SIZE": n_write},
+        "gemm_FETCH_SIZE_KiB": round(g_fetch, 1),
+        "gemm_WRITE_SIZE_KiB": round(g_write, 1),
+        "copy_calibration": {"bytes_read": copy_bytes, "bytes_written": copy_bytes,
+                             "FETCH_SIZE_KiB": round(c_fetch, 1), "WRITE_SIZE_KiB": round(c_write, 1),
+                             "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)},
+        "hbm_bytes_per_launch": {"fetch": round(fetch), "write": round(write), "total": round(fetch + write)},
+        "note": "FETCH_SIZE counts L2 misses going to the fabric, so hits in the 256 MB Infinity Cache are "
+                "included; each of the 8 XCDs streams the weights through its own L2.",
+    }
+    path = os.path.join(ROOT, "profiles", "gemm_w4_qwen2vl72b_traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(path, out["hbm_bytes_per_launch"])
 
 
 def uses_128_token_tiles(T, d_out):
@@ -103,6 +167,9 @@ def copy_calibration():
 
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     if args.copy_calibration:
         copy_calibration()
         return
@@ -265,8 +332,13 @@ def main():
                       "per_linear": per_linear},
     }
 
+    peaks = measured_peaks(torch, libqe, dev)
+    result["measured_peaks"] = peaks
+    result["roofline"]["peak_measured"] = peaks["int8_mfma_tops"]
+    result["roofline"]["frac_measured"] = round(achieved / peaks["int8_mfma_tops"], 4)
+
     if not args.no_extras:
-        result["extras"] = extras(torch, synth, qe, libqe, dev)
+        result["extras"] = extras(torch, synth, qe, libqe, dev, peaks["copy_gbs"])
 
     if want_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, cfg, xs_cpu, oracle_w, args.cpu_sample_tokens)
@@ -274,7 +346,46 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def extras(torch, synth, qe, libqe, dev):
+def measured_peaks(torch, libqe, dev):
+    """Rates this device sustains, from the library's probe kernels timed with events on the
+    stream they run on: an int8 MFMA loop (the main GEMM's instruction, 2048 workgroups, about
+    25 ms) on small constant operands, the highest rate the power-limited matrix cores sustain,
+    and on operands in the main GEMM's value ranges; and a 1 GiB streaming copy.  Median of
+    five runs each."""
+    def median_ms(fn, reps=5):
+        fn()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    blocks, iters = 2048, 30000
+    sink = torch.empty(blocks * 256 * 4, dtype=torch.int32, device=dev)
+    rates = []
+    for operands in (0, 1):
+        ops = libqe.qe_probe_mfma_i8(sink, blocks, iters, operands)
+        t = median_ms(lambda: libqe.qe_probe_mfma_i8(sink, blocks, iters, operands))
+        rates.append(ops / (t * 1e-3) / 1e12)
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    t_copy = median_ms(lambda: libqe.qe_probe_copy(src, dst, nbytes))
+    del sink, src, dst
+    torch.cuda.empty_cache()
+    return {"int8_mfma_tops": round(rates[0], 1),
+            "int8_mfma_tops_gemm_operands": round(rates[1], 1),
+            "copy_gbs": round(2 * nbytes / (t_copy * 1e-3) / 1e9, 1),
+            "method": "qe_probe_mfma_i8 (2048 workgroups x 4 waves x 240000 MFMA 16x16x64 i8; small "
+                      "constant operands, then operands in the A6 x W4 code ranges) and qe_probe_copy "
+                      "(1 GiB read + 1 GiB write), median of 5"}
+
+
+def extras(torch, synth, qe, libqe, dev, copy_gbs=None):
     out = {}
     # ---- decode: Qwen2VL-72B MLP up/down, W3A16, T=8 (HBM-bound weight streaming)
     cfg = synth.get_config("qwen2vl_72b_decode")
@@ -325,6 +436,7 @@ def extras(torch, synth, qe, libqe, dev):
         "us_warm_median": round(float(np.median(warm)) * 1e3, 2),
         "tokens_per_s": round(T / t_cold, 1), "alg_mbytes": round(alg / 1e6, 2),
         "achieved_gbs": round(alg / t_cold / 1e9, 1), "hbm_frac": round(alg / t_cold / 1e9 / PEAK_HBM_GBS, 4),
+        "hbm_frac_of_measured_copy": round(alg / t_cold / 1e9 / copy_gbs, 4) if copy_gbs else None,
         "note": "Infinity Cache flushed by reading 1 GiB before every cold iteration",
     }
     del layers, wss, flush

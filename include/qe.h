@@ -253,6 +253,27 @@ int qe_channel_topk(const void* x, int32_t x_dtype, const float* w, int32_t T, i
 int qe_linear_cost(const qe_linear* lin, int32_t T, int32_t n_distinct_experts, int32_t x_bytes_per_elt,
                    double* int_macs, double* adapter_macs, double* alg_bytes);
 
+/* ---------------------------------------------------------- measurement aids --
+ * Not part of the QE computation: kernels whose duration, measured by the caller with
+ * events on `stream`, gives the rates this device sustains, reported beside the
+ * published peaks when the hot path's kernels are placed on their roofline.
+ *
+ * qe_probe_mfma_i8: `blocks` workgroups of 256 threads (blocks >= 1); each of their waves
+ *   issues 8 * iters int8 16x16x64 MFMAs (the main GEMM's instruction) into 8 independent
+ *   accumulators, on register operands fixed through the loop.  The matrix cores are
+ *   power-limited, so the rate depends on the values: operands = 0 uses small constant
+ *   bytes (the highest rate the part sustains), operands = 1 random values in the main
+ *   GEMM's ranges (A6 codes in [-31, 31] times 4-bit codes scaled by 16).  *ops receives
+ *   the integer operations enqueued (2 * 16 * 16 * 64 per MFMA).  out: device int32
+ *   [blocks * 256 * 4], a result sink the caller owns.  iters >= 1.
+ * qe_probe_copy: copies `bytes` (a multiple of 16) from src to dst; both device pointers,
+ *   16-byte aligned, caller-owned, not overlapping.  The traffic is 2 * bytes.
+ * Both only enqueue work (no synchronization); invalid arguments return
+ * QE_ERR_INVALID_ARG / QE_ERR_ALIGNMENT and launch nothing.
+ */
+int qe_probe_mfma_i8(int32_t* out, int32_t blocks, int32_t iters, int32_t operands, double* ops, void* stream);
+int qe_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

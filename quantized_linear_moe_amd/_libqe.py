@@ -69,6 +69,8 @@ def _load():
         "qe_colmean_abs": (ctypes.c_int, [P, I, I, I, P, P]),
         "qe_channel_topk": (ctypes.c_int, [P, I, P, I, I, I, P, P, P]),
         "qe_linear_cost": (ctypes.c_int, [LP, I, I, I, D, D, D]),
+        "qe_probe_mfma_i8": (ctypes.c_int, [P, I, I, I, D, P]),
+        "qe_probe_copy": (ctypes.c_int, [P, P, Z, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -82,6 +84,7 @@ EXPORTED = (
     "qe_status_string", "qe_last_hip_error", "qe_version", "qe_pack_weights", "qe_prepared_bytes", "qe_prepare",
     "qe_workspace_bytes", "qe_quant_act", "qe_route", "qe_adapter_inputs", "qe_wq_gemm", "qe_routed_lora",
     "qe_linear_prologue", "qe_linear_forward", "qe_colmean_abs", "qe_channel_topk", "qe_linear_cost",
+    "qe_probe_mfma_i8", "qe_probe_copy",
 )
 
 
@@ -213,6 +216,19 @@ def qe_channel_topk(x, w, k, topk, hist, stream=None):
     T, d_in = x.shape
     _check(_lib.qe_channel_topk(_ptr(x), _dtype_code(x), _ptr(w), T, d_in, k, _ptr(topk), _ptr(hist),
                                 _stream(stream)), "qe_channel_topk")
+
+
+def qe_probe_mfma_i8(out, blocks, iters, operands=0, stream=None):
+    """Enqueue the int8 MFMA throughput probe; returns the integer operations enqueued."""
+    ops = ctypes.c_double()
+    _check(_lib.qe_probe_mfma_i8(_ptr(out), blocks, iters, operands, ctypes.byref(ops), _stream(stream)),
+           "qe_probe_mfma_i8")
+    return ops.value
+
+
+def qe_probe_copy(src, dst, nbytes, stream=None):
+    """Enqueue the streaming copy probe of nbytes from src to dst (traffic: 2 * nbytes)."""
+    _check(_lib.qe_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "qe_probe_copy")
 
 
 def qe_linear_cost(lin, T, n_distinct, x_bytes):

@@ -1,0 +1,90 @@
+// Measurement aids, not part of the QE computation: kernels whose duration, taken by the
+// caller with events on the launch stream, gives the rates this device sustains, to set
+// beside the published peaks in the roofline of the hot path's kernels.
+//
+//   probe_mfma_i8_kernel : int8 matrix-core throughput (v_mfma_i32_16x16x64_i8, the main
+//                          GEMM's instruction), a loop on register operands
+//   probe_copy_kernel    : streaming HBM copy (16-byte loads and stores)
+
+#include "qe_internal.h"
+
+namespace qe {
+
+typedef int32_t v4i __attribute__((ext_vector_type(4)));
+
+constexpr int PM_ACC = 8;  // independent accumulators per wave: cover the MFMA latency
+
+// Each wave issues PM_ACC * iters MFMAs on register operands fixed through the loop.  The
+// matrix cores of this part are power-limited, so the rate depends on the operand values:
+//   operands 0: small constant bytes (1 .. 11): the highest rate the part sustains
+//   operands 1: random per lane in the main GEMM's value ranges: A6 codes in [-31, 31] times
+//               4-bit weight codes scaled by 16 (the GEMM's int4-in-int8 encoding)
+__global__ __launch_bounds__(256) void probe_mfma_i8_kernel(int32_t* __restrict__ out, int iters, int operands) {
+    const uint32_t lane_id = blockIdx.x * 256u + threadIdx.x;
+    uint32_t h = (lane_id + 1u) * 0x9E3779B9u;
+    auto rnd = [&h]() {
+        h = h * 1664525u + 1013904223u;
+        return h >> 8;
+    };
+    v4i a, b;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (operands == 0) {
+            a[q] = q + 1;
+            b[q] = 2 * q + 5;
+        } else {
+            uint32_t wa = 0, wb = 0;
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                const int ca = (int)(rnd() % 63u) - 31, cb = ((int)(rnd() % 15u) - 7) * 16;
+                wa |= (uint32_t)(ca & 0xFF) << (8 * y);
+                wb |= (uint32_t)(cb & 0xFF) << (8 * y);
+            }
+            a[q] = (int32_t)wa;
+            b[q] = (int32_t)wb;
+        }
+    }
+    v4i acc[PM_ACC];
+#pragma unroll
+    for (int j = 0; j < PM_ACC; ++j) acc[j] = v4i{0, 0, 0, 0};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int j = 0; j < PM_ACC; ++j) acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[j], 0, 0, 0);
+    }
+    v4i sum = acc[0];
+#pragma unroll
+    for (int j = 1; j < PM_ACC; ++j) sum += acc[j];
+    *reinterpret_cast<v4i*>(out + (size_t)lane_id * 4) = sum;
+}
+
+__global__ __launch_bounds__(256) void probe_copy_kernel(const v4u* __restrict__ src, v4u* __restrict__ dst,
+                                                         size_t n16) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {  // four independent 16-byte loads in flight
+        const v4u v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+        dst[i] = v0;
+        dst[i + stride] = v1;
+        dst[i + 2 * stride] = v2;
+        dst[i + 3 * stride] = v3;
+    }
+    for (; i < n16; i += stride) dst[i] = src[i];
+}
+
+hipError_t launch_probe_mfma_i8(int32_t* out, int blocks, int iters, int operands, hipStream_t st) {
+    hipLaunchKernelGGL(probe_mfma_i8_kernel, dim3(blocks), dim3(256), 0, st, out, iters, operands);
+    return hipGetLastError();
+}
+
+double probe_mfma_i8_ops(int blocks, int iters) {
+    return 2.0 * 16 * 16 * 64 * (double)PM_ACC * iters * 4.0 * blocks;  // 4 waves per workgroup
+}
+
+hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t st) {
+    const size_t n16 = bytes / 16;
+    hipLaunchKernelGGL(probe_copy_kernel, dim3(256 * 16), dim3(256), 0, st, reinterpret_cast<const v4u*>(src),
+                       reinterpret_cast<v4u*>(dst), n16);
+    return hipGetLastError();
+}
+
+}  // namespace qe

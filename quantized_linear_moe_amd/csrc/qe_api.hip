@@ -579,6 +579,25 @@ int qe_channel_topk(const void* x, int32_t x_dtype, const float* w, int32_t T, i
     return QE_OK;
 }
 
+// ------------------------------------------------------------------ measurement aids
+int qe_probe_mfma_i8(int32_t* out, int32_t blocks, int32_t iters, int32_t operands, double* ops, void* stream) {
+    QE_CHECK(out && blocks >= 1 && iters >= 1 && (operands == 0 || operands == 1), QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(out), QE_ERR_ALIGNMENT);
+    QE_TRY_HIP(launch_probe_mfma_i8(out, blocks, iters, operands, S(stream)));
+    if (ops) *ops = probe_mfma_i8_ops(blocks, iters);
+    return QE_OK;
+}
+
+int qe_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+    QE_CHECK(src && dst && bytes % 16 == 0, QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(src) && aligned16(dst), QE_ERR_ALIGNMENT);
+    const char *a = static_cast<const char*>(src), *b = static_cast<const char*>(dst);
+    QE_CHECK(a + bytes <= b || b + bytes <= a, QE_ERR_INVALID_ARG);
+    if (bytes == 0) return QE_OK;
+    QE_TRY_HIP(launch_probe_copy(src, dst, bytes, S(stream)));
+    return QE_OK;
+}
+
 // ------------------------------------------------------------------ cost
 int qe_linear_cost(const qe_linear* lin, int32_t T, int32_t n_distinct, int32_t xb, double* int_macs,
                    double* adapter_macs, double* alg_bytes) {
