@@ -413,6 +413,42 @@ def test_channel_topk_ties_and_k(Q, k):
     assert np.array_equal(hist.cpu().numpy().astype(np.int64), h_ref)
 
 
+# the threshold path and the exact path: mass ties that overflow the candidate list, k above
+# the threshold path's limit, d_in not a multiple of 8 (scalar loads), the largest d_in, k = d_in,
+# zero weights and -0 activations
+@pytest.mark.parametrize("T,d_in,k,pattern,dtype", [
+    (9, 14336, 32, "normal", torch.bfloat16),
+    (5, 32768, 40, "normal", torch.float32),
+    (7, 1001, 17, "normal", torch.float32),
+    (6, 3000, 300, "normal", torch.bfloat16),
+    (4, 5000, 32, "constant", torch.bfloat16),
+    (5, 2048, 100, "few_levels", torch.float32),
+    (3, 100, 100, "normal", torch.float32),
+    (6, 4096, 1024, "few_levels", torch.bfloat16),
+])
+def test_channel_topk_paths(Q, T, d_in, k, pattern, dtype):
+    rng = np.random.default_rng(d_in + k)
+    if pattern == "normal":
+        x = rng.standard_normal((T, d_in)).astype(np.float32)
+    elif pattern == "constant":
+        x = np.full((T, d_in), 1.5, np.float32)
+    else:
+        x = rng.integers(-3, 4, (T, d_in)).astype(np.float32)
+    x[0, ::5] = -0.0
+    x = torch.from_numpy(x).to(dtype)
+    w = rng.uniform(0.5, 2.0, d_in).astype(np.float32)
+    w[::11] = 0.0
+    if pattern != "normal":
+        w[:] = 1.0
+    topk = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    hist = torch.zeros(d_in, dtype=torch.int32, device=DEV)
+    Q.libqe.qe_channel_topk(x.to(DEV), torch.from_numpy(w).to(DEV), k, topk, hist)
+    torch.cuda.synchronize()
+    t_ref, h_ref = O.channel_topk(f32(x), w, k)
+    assert np.array_equal(topk.cpu().numpy(), t_ref)
+    assert np.array_equal(hist.cpu().numpy().astype(np.int64), h_ref)
+
+
 def test_colmean_abs(Q):
     cfg = synth.get_config("qwen2vl_2b")
     W = synth.gen_linear(cfg, _spec(cfg, "gate"))["W_f"]
