@@ -385,8 +385,55 @@ def measured_peaks(torch, libqe, dev):
                       "(1 GiB read + 1 GiB write), median of 5"}
 
 
+def layer_throughput(torch, synth, qe, libqe, dev, name, steps=10):
+    """The composite entry point over every linear of a configuration, one stream, inputs resident:
+    tokens/s, the int8 rate of the whole step and its fraction of the spec roofline."""
+    cfg = synth.get_config(name)
+    T = cfg.T
+    xs = {s: synth.gen_activations(cfg, s).to(dev) for s in cfg.streams()}
+    layers = []
+    for spec in cfg.linears:
+        params = synth.gen_linear(cfg, spec)
+        layers.append((spec, qe.QELinear.from_params(params, cfg.w_bits, cfg.a_bits, device=dev)))
+        del params
+    ws = torch.empty(max(libqe.qe_workspace_bytes(l.lin, T) for _, l in layers), dtype=torch.uint8, device=dev)
+    ys = [torch.empty(T, spec.d_out, dtype=torch.float32, device=dev) for spec, _ in layers]
+    es = [torch.empty(T, dtype=torch.int32, device=dev) for _ in layers]
+
+    def run():
+        for i, (spec, layer) in enumerate(layers):
+            libqe.qe_linear_forward(layer.lin, xs[spec.stream], ys[i], es[i], ws)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) / steps * 1e-3
+    int_ops = adapter_flops = alg = 0.0
+    for i, (spec, layer) in enumerate(layers):
+        im, am, ab = libqe.qe_linear_cost(layer.lin, T, int(torch.unique(es[i]).numel()), 2)
+        int_ops, adapter_flops, alg = int_ops + 2 * im, adapter_flops + 2 * am, alg + ab
+    t_roof = max(int_ops / (PEAK_INT8_TOPS * 1e12) + adapter_flops / (PEAK_BF16_TFLOPS * 1e12),
+                 alg / (PEAK_HBM_GBS * 1e9))
+    del layers, ws, xs, ys, es
+    torch.cuda.empty_cache()
+    return {"linears": [f"{s.name} {s.d_in}->{s.d_out}" for s in cfg.linears], "T": T,
+            "w_bits": cfg.w_bits, "a_bits": cfg.a_bits, "us_per_step": round(t * 1e6, 2),
+            "tokens_per_s": round(T / t, 1), "int8_tops": round(int_ops / t / 1e12, 1),
+            "layer_roofline_frac": round(t_roof / t, 4)}
+
+
 def extras(torch, synth, qe, libqe, dev, copy_gbs=None):
     out = {}
+    # ---- the other configurations: a small single linear (latency), a 2B layer, an 8B layer
+    out["linear_tiny_w4a8_T64"] = layer_throughput(torch, synth, qe, libqe, dev, "tiny", steps=50)
+    out["layer_qwen2vl2b_w4a6_T2048"] = layer_throughput(torch, synth, qe, libqe, dev, "qwen2vl_2b")
+    out["layer_internvl2_8b_w4a8_T4096"] = layer_throughput(torch, synth, qe, libqe, dev, "internvl2_8b")
     # ---- decode: Qwen2VL-72B MLP up/down, W3A16, T=8 (HBM-bound weight streaming)
     cfg = synth.get_config("qwen2vl_72b_decode")
     layers = []

@@ -37,7 +37,7 @@ namespace qe {
 
 constexpr int G_BN = 256;
 constexpr int G_BK = 64;   // K per pipeline stage (one int8 MFMA K step)
-constexpr int G_NS = 4;    // stages in the LDS ring: loads run three stages ahead
+constexpr int G_NS = 4;    // stages in the LDS ring of 128-token tiles: loads run three stages ahead
 constexpr int G_NBW = 4;   // N blocks per wave
 
 __device__ inline v4i unpack_w4x16(uint32_t p0, uint32_t p1) {
@@ -72,7 +72,10 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     constexpr int STAGE = A_STAGE + B_STAGE;
     constexpr int A_DMA = A_STAGE / 1024 / 4;     // A copies per wave per stage
     constexpr int OPS = A_DMA + 2;                // DMA instructions per thread per stage
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[G_NS * STAGE];
+    // ring depth: 64-token tiles run few workgroups per CU with short K steps, so their loads
+    // run further ahead to cover the memory latency
+    constexpr int NS = MB == 4 ? 8 : G_NS;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
     const int tm = blockIdx.x % n_tm, tn = blockIdx.x / n_tm;
     const int m0 = tm * BM;
@@ -158,14 +161,14 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
 
     // prologue: three stages in flight, then wait for the first
 #pragma unroll
-    for (int st = 0; st < G_NS - 1; ++st) issue(st, min(st, KB - 1));
-    QE_WAIT_VMCNT_LDS(2 * OPS);
+    for (int st = 0; st < NS - 1; ++st) issue(st, min(st, KB - 1));
+    QE_WAIT_VMCNT_LDS((NS - 2) * OPS);
     QE_WG_BARRIER();
 
     for (int kb = 0; kb < KB; ++kb) {
         // refill the slot consumed in the previous step (past the end: a harmless repeat)
-        issue((kb + G_NS - 1) % G_NS, min(kb + G_NS - 1, KB - 1));
-        const uint8_t* st = smem + (kb % G_NS) * STAGE;
+        issue((kb + NS - 1) % NS, min(kb + NS - 1, KB - 1));
+        const uint8_t* st = smem + (kb % NS) * STAGE;
         v2u bp[G_NBW];
 #pragma unroll
         for (int j = 0; j < G_NBW; ++j)
@@ -189,9 +192,9 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
         __builtin_amdgcn_sched_group_barrier(0x008, MB * G_NBW, 0);   // then the MFMAs
         // nothing of this step may move below the barrier: the slot read here is the
         // DMA target of the next step, so every LDS read must have completed (lgkmcnt 0);
-        // and step kb+1 must have landed (kb+2, kb+3 may still be in flight)
+        // and step kb+1 must have landed (the NS-2 later steps may still be in flight)
         __builtin_amdgcn_sched_barrier(0);
-        QE_WAIT_VMCNT_LDS(2 * OPS);
+        QE_WAIT_VMCNT_LDS((NS - 2) * OPS);
         QE_WG_BARRIER();
     }
     QE_WAIT_VMCNT(0);
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     const bool have_se = u != nullptr && bt_s != nullptr && rs_pad > 0;
     if constexpr (kFast) {
         constexpr int U_OFF = 0, V_OFF = MB * 1024, BS_OFF = 2 * MB * 1024, BR_OFF = BS_OFF + 16384;
-        constexpr int NSLOT = (G_NS * STAGE - BR_OFF) / 16384;  // experts per round
+        constexpr int NSLOT = (NS * STAGE - BR_OFF) / 16384;  // experts per round
         static_assert(NSLOT >= 1, "LDS ring too small for the epilogue operands");
         QE_WAIT_VMCNT_LDS(0);
         QE_WG_BARRIER();  // every wave is done with the ring
