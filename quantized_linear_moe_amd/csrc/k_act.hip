@@ -14,6 +14,7 @@
 
 #include "qe_dma.h"
 #include "qe_internal.h"
+#include "qe_splits.h"
 
 namespace qe {
 
@@ -630,22 +631,29 @@ __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restri
                                                            uint16_t* __restrict__ u, float* __restrict__ s_x) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (t >= T) return;
-    // columns lane and lane + 64 (ncols <= 80); partials loaded 8 at a time, added in order
+    // columns lane and lane + 64 (ncols <= 80), and the activation maxima: the partials of up to
+    // 16 splits of both columns and the maxima are requested together, then added in split order
     float sum[2] = {0.0f, 0.0f};
     const size_t stride = (size_t)T * ncols;
+    constexpr int KB16 = 16;
+    float vals[2][KB16];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-        const int c = lane + 64 * j;
-        if (c >= ncols) continue;
+        const int c = min(lane + 64 * j, max(ncols - 1, 0));  // a column past ncols reads a valid one, unused
         const float* p = part + (size_t)t * ncols + c;
-        for (int k0 = 0; k0 < ksplit; k0 += 8) {
-            float vals[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) vals[q] = k0 + q < ksplit ? p[(size_t)(k0 + q) * stride] : 0.0f;
+        for (int q = 0; q < KB16; ++q) vals[j][q] = (q < ksplit && ncols > 0) ? p[(size_t)q * stride] : 0.0f;
+    }
+    float m = 0.0f;
+    for (int k = lane; k < ksplit; k += 64) m = fmaxf(m, amax_part[(size_t)k * T + t]);
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                if (k0 + q < ksplit) sum[j] += vals[q];
-        }
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int q = 0; q < KB16; ++q)
+            if (q < ksplit) sum[j] += vals[j][q];
+        const float* p = part + (size_t)t * ncols + min(lane + 64 * j, max(ncols - 1, 0));
+        if (ncols > 0)
+            for (int k = KB16; k < ksplit; ++k) sum[j] += p[(size_t)k * stride];  // more than 16 splits: rare
     }
     if (router_col >= 0) {
         float best = __builtin_inff();
@@ -674,8 +682,6 @@ __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restri
         const int c = lane + 64 * j;
         if (u && c < rs_pad) u[(size_t)t * rs_pad + c] = c < r_s ? (uint16_t)f32_to_bf16_bits(sum[j]) : (uint16_t)0;
     }
-    float m = 0.0f;
-    for (int k = lane; k < ksplit; k += 64) m = fmaxf(m, amax_part[(size_t)k * T + t]);
     m = wave_max(m);
     if (lane == 0) s_x[t] = m / (float)qmax;
 }
@@ -933,9 +939,8 @@ __global__ __launch_bounds__(256) void vpart_finish_kernel(const float* __restri
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= (size_t)T * rr_pad) return;
     const int pos = (int)(idx / rr_pad), c = (int)(idx % rr_pad);
-    float a = 0.0f;
-    for (int q = 0; q < ksq; ++q) a += vpart[(size_t)q * T * rr_pad + idx];
     const int tt = perm ? perm[pos] : pos;
+    const float a = sum_splits(vpart + idx, (size_t)T * rr_pad, ksq);
     v[(size_t)tt * rr_pad + c] = c < r_r ? (uint16_t)f32_to_bf16_bits(a) : (uint16_t)0;
 }
 

@@ -18,6 +18,7 @@
 #include <algorithm>
 
 #include "qe_internal.h"
+#include "qe_splits.h"
 
 namespace qe {
 
@@ -396,21 +397,6 @@ hipError_t launch_decode_gemv(const void* x, int x_dtype, int T, int d_in, int d
 // ordered so that about three memory latencies are exposed.
 constexpr int DF_CH = 64;
 constexpr int DF_THREADS = 512;
-
-// sum_k p[k * stride] for k = 0 .. n-1, in order
-__device__ inline float sum_splits(const float* __restrict__ p, size_t stride, int n) {
-    constexpr int B = 16;
-    float sum = 0.0f;
-    for (int k = 0; k < n; k += B) {
-        float a[B];
-#pragma unroll
-        for (int q = 0; q < B; ++q) a[q] = k + q < n ? p[(size_t)(k + q) * stride] : 0.0f;
-#pragma unroll
-        for (int q = 0; q < B; ++q)
-            if (k + q < n) sum += a[q];
-    }
-    return sum;
-}
 
 __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
     const float* __restrict__ part_m, int ks_m, int T, int d_out, const float* __restrict__ w_scale,

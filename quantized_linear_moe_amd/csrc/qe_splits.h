@@ -1,0 +1,26 @@
+// Split-K reduction helper shared by the finish kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+
+namespace qe {
+
+// sum_k p[k * stride] for k = 0 .. n-1, added in order; the loads are issued in independent
+// batches of 16 (a chain of dependent loads would cost one memory latency per term)
+__device__ inline float sum_splits(const float* __restrict__ p, size_t stride, int n) {
+    constexpr int B = 16;
+    float sum = 0.0f;
+    for (int k = 0; k < n; k += B) {
+        float a[B];
+#pragma unroll
+        for (int q = 0; q < B; ++q) a[q] = k + q < n ? p[(size_t)(k + q) * stride] : 0.0f;
+#pragma unroll
+        for (int q = 0; q < B; ++q)
+            if (k + q < n) sum += a[q];
+    }
+    return sum;
+}
+
+}  // namespace qe
