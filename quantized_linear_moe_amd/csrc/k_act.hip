@@ -847,13 +847,14 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
                 if (j == bj && ex[j] >= 0) e = ex[j];
             bsrc[q] = NBR ? mt_re + ((size_t)e * RR + bn * 16 + lr) * d_in + lg * 32 + bs * 8 : nullptr;
         }
+        // x of the pass's first group; each group then requests the next one's x (clamped to the
+        // last group, so the load is unconditional) before its arithmetic
+        v4u xv[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) xv[s] = *reinterpret_cast<const v4u*>(xrow + (size_t)g_beg * EQ_KG + s * 8);
         for (int g = g_beg; g < g_end; ++g, ++gi) {
             uint8_t* buf = smem + (gi & 1) * BUF;
             const size_t k0 = (size_t)g * EQ_KG;
-            // one burst of loads
-            v4u xv[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) xv[s] = *reinterpret_cast<const v4u*>(xrow + k0 + s * 8);
             v4u bv[2];
             if (NBR) {
 #pragma unroll
@@ -871,6 +872,10 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
             // before this barrier); earlier code stores need not have landed
             QE_WAIT_LDS();
             QE_WG_BARRIER();
+            v4u xn[4];
+            const size_t kn = (size_t)min(g + 1, g_end - 1) * EQ_KG;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) xn[s] = *reinterpret_cast<const v4u*>(xrow + kn + s * 8);
             if (first) {
                 v2u cw[4];
 #pragma unroll
@@ -909,6 +914,8 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
                     }
                 }
             }
+#pragma unroll
+            for (int s = 0; s < 4; ++s) xv[s] = xn[s];
         }
         first = false;
     } while (pm);
