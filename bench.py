@@ -513,6 +513,46 @@ def extras(torch, synth, qe, libqe, dev, copy_gbs=None):
     out["topk_internvl2_8b_down_T4096_k32"] = {
         "us_median": round(t * 1e6, 2), "tokens_per_s": round(cfg.T / t, 1),
         "achieved_gbs": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)}
+
+    # ---- the rest of the statistic on the same top-k lists: frequency partition (host),
+    # co-occurrence counts of the N_r * k token-dependent channels (GPU), NPMI spectral
+    # clustering (host); the 65536-token line repeats the 4096 tokens sixteen times
+    n_r = cfg.n_routed
+    hist.zero_()
+    libqe.qe_channel_topk(x, w, cfg.k, topk, hist)
+    h = hist.cpu().numpy().view(np.uint32)
+    t0 = time.perf_counter()
+    _, dep, slot = libqe.qe_partition_channels(h, cfg.k, n_r)
+    t_part = time.perf_counter() - t0
+    slot_d = torch.from_numpy(slot).to(dev)
+    n_dep = len(dep)
+    cooc = torch.zeros(n_dep, n_dep, dtype=torch.int32, device=dev)
+    cws = torch.empty(libqe.qe_cooccur_workspace_bytes(16 * cfg.T, n_dep), dtype=torch.uint8, device=dev)
+    for T_c, tk in ((cfg.T, topk), (16 * cfg.T, topk.repeat(16, 1).contiguous())):
+        for _ in range(3):
+            libqe.qe_cooccur(tk, slot_d, n_dep, cooc, cws)
+        ts = []
+        for _ in range(20):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            libqe.qe_cooccur(tk, slot_d, n_dep, cooc, cws)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        t = float(np.median(ts)) * 1e-3
+        nbytes = T_c * cfg.k * 4 + spec.d_in * 4 + 2 * n_dep * n_dep * 4
+        out[f"cooccur_internvl2_8b_down_T{T_c}_k{cfg.k}_C{n_dep}"] = {
+            "us_median": round(t * 1e6, 2), "tokens_per_s": round(T_c / t, 1),
+            "achieved_gbs": round(nbytes / t / 1e9, 1), "hbm_frac": round(nbytes / t / 1e9 / PEAK_HBM_GBS, 4)}
+    cooc.zero_()
+    libqe.qe_cooccur(topk, slot_d, n_dep, cooc, cws)
+    c = cooc.cpu().numpy().view(np.uint32)
+    t0 = time.perf_counter()
+    labels = libqe.qe_cluster_channels(c, cfg.T, n_r, 0.2)
+    t_clu = time.perf_counter() - t0
+    out["partition_cluster_host_internvl2_8b_down"] = {
+        "partition_ms": round(t_part * 1e3, 3), "cluster_ms": round(t_clu * 1e3, 2), "channels": n_dep,
+        "cluster_sizes": np.bincount(labels, minlength=n_r).tolist(), "note": "host C++, one thread"}
     return out
 
 

@@ -240,6 +240,63 @@ int qe_colmean_abs(const void* W, int32_t dtype, int32_t d_out, int32_t d_in, fl
 int qe_channel_topk(const void* x, int32_t x_dtype, const float* w, int32_t T, int32_t d_in,
                     int32_t k, int32_t* topk, uint32_t* hist, void* stream);
 
+/* ------------------------------------------ channel partition and clustering --
+ * The rest of the calibration statistic (DeepRead summary, "Method": channels ordered
+ * by selection frequency, the first k token-independent and the next N_r * k
+ * token-dependent; the token-dependent channels grouped into N_r clusters by spectral
+ * clustering of their NPMI co-occurrence similarity; PaperDaily post, "核心设计":
+ * O[t][i], the co-occurrence counts, p(i), p(i,j), NPMI and its threshold; listing,
+ * Figure 6).
+ *
+ * qe_partition_channels (host, synchronous): orders the channels by hist descending,
+ *   ties by ascending channel index, and writes indep[0..k) = the first k and
+ *   dep[0..n_r*k) = the next n_r*k.  slot (optional) receives, for every channel, its
+ *   position in dep or -1.  hist: host uint32 [d_in] (qe_channel_topk's histogram copied
+ *   to the host); indep, dep, slot: host int32 buffers of k, n_r*k and d_in entries.
+ *   Requires k >= 1, n_r >= 1, k * (1 + n_r) <= d_in.
+ */
+int qe_partition_channels(const uint32_t* hist, int32_t d_in, int32_t k, int32_t n_r, int32_t* indep,
+                          int32_t* dep, int32_t* slot);
+
+/* qe_cooccur (device): cooc[i][j] += #{t : topk[t] holds both dep[i] and dep[j]}, i.e.
+ *   cooc += O^T O with O[t][i] = 1 when token t selected the i-th token-dependent channel.
+ *   The diagonal counts each channel's selections.  cooc is ACCUMULATED over calls (the
+ *   caller zeroes it), so a calibration set can be fed in batches of tokens.
+ *   topk: device int32 [T][k] as written by qe_channel_topk (each row a set of distinct
+ *   channels); slot: device int32 [d_in] as written by qe_partition_channels (entries
+ *   outside [0, n_dep) mark channels that are not token-dependent; topk entries outside
+ *   [0, d_in) are skipped); cooc: device uint32 [n_dep][n_dep]; ws: device scratch of
+ *   ws_bytes >= qe_cooccur_workspace_bytes(T, n_dep) (the per-token channel bit masks;
+ *   contents on entry do not matter, else QE_ERR_WORKSPACE).  All 16-byte aligned.
+ *   1 <= k <= min(d_in, 1024); 1 <= n_dep <= 8192.  T == 0 is a no-op.
+ * qe_cooccur_workspace_bytes: scratch bytes for T tokens (0 for invalid sizes); enough for
+ *   any call with at most T tokens.
+ */
+size_t qe_cooccur_workspace_bytes(int32_t T, int32_t n_dep);
+int qe_cooccur(const int32_t* topk, int32_t T, int32_t k, const int32_t* slot, int32_t d_in, int32_t n_dep,
+               uint32_t* cooc, void* ws, size_t ws_bytes, void* stream);
+
+/* qe_cluster_channels (host, synchronous): from the co-occurrence counts of n_dep
+ *   token-dependent channels over T tokens,
+ *     NPMI(i,j) = ln(p_ij / (p_i p_j)) / -ln p_ij,  p_ij = cooc[i][j] / T, p_i = cooc[i][i] / T,
+ *     with -1 where p_ij = 0 and +1 where p_ij = 1;
+ *     S[i][j] = NPMI(i,j) if NPMI(i,j) >= threshold, else 0;
+ *     L = I - D^-1/2 S D^-1/2 (d_i = sum_j S[i][j]; rows with d_i = 0 contribute nothing);
+ *     U = eigenvectors of the n_clusters smallest eigenvalues of L, rows scaled to unit
+ *     length (Ng, Jordan and Weiss); labels = K-Means of the rows of U (Lloyd's iteration
+ *     from farthest-point seeds starting at row 0; ties to the lower index), numbered in
+ *     order of each cluster's lowest member.
+ *   cooc: host uint32 [n_dep][n_dep] (qe_cooccur's result copied to the host; symmetric,
+ *   cooc[i][j] <= min(cooc[i][i], cooc[j][j]), cooc[i][i] <= T, else QE_ERR_INVALID_ARG);
+ *   labels: host int32 [n_dep]; similarity (host double [n_dep][n_dep]), eigvals (host
+ *   double [n_clusters], ascending) and embedding (host double [n_dep][n_clusters]) are
+ *   optional outputs (NULL to skip).  1 <= n_clusters <= n_dep <= 2048; T >= 1;
+ *   0 <= threshold <= 1.  Returns QE_ERR_UNSUPPORTED if the eigenvalue iteration does not
+ *   converge.
+ */
+int qe_cluster_channels(const uint32_t* cooc, int32_t n_dep, int64_t T, int32_t n_clusters, double threshold,
+                        int32_t* labels, double* similarity, double* eigvals, double* embedding);
+
 /* ----------------------------------------------------------------- accounting --
  * Algorithmic work of one QE linear over T tokens (listing, Table 7, generalised
  * to d_in != d_out):

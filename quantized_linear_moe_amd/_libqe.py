@@ -68,6 +68,10 @@ def _load():
         "qe_linear_forward": (ctypes.c_int, [LP, P, I, I, P, P, P, Z, P]),
         "qe_colmean_abs": (ctypes.c_int, [P, I, I, I, P, P]),
         "qe_channel_topk": (ctypes.c_int, [P, I, P, I, I, I, P, P, P]),
+        "qe_partition_channels": (ctypes.c_int, [P, I, I, I, P, P, P]),
+        "qe_cooccur_workspace_bytes": (Z, [I, I]),
+        "qe_cooccur": (ctypes.c_int, [P, I, I, P, I, I, P, P, Z, P]),
+        "qe_cluster_channels": (ctypes.c_int, [P, I, ctypes.c_int64, I, ctypes.c_double, P, P, P, P]),
         "qe_linear_cost": (ctypes.c_int, [LP, I, I, I, D, D, D]),
         "qe_probe_mfma_i8": (ctypes.c_int, [P, I, I, I, D, P]),
         "qe_probe_copy": (ctypes.c_int, [P, P, Z, P]),
@@ -84,7 +88,8 @@ EXPORTED = (
     "qe_status_string", "qe_last_hip_error", "qe_version", "qe_pack_weights", "qe_prepared_bytes", "qe_prepare",
     "qe_workspace_bytes", "qe_quant_act", "qe_route", "qe_adapter_inputs", "qe_wq_gemm", "qe_routed_lora",
     "qe_linear_prologue", "qe_linear_forward", "qe_colmean_abs", "qe_channel_topk", "qe_linear_cost",
-    "qe_probe_mfma_i8", "qe_probe_copy",
+    "qe_probe_mfma_i8", "qe_probe_copy", "qe_partition_channels", "qe_cooccur_workspace_bytes",
+    "qe_cooccur", "qe_cluster_channels",
 )
 
 
@@ -216,6 +221,44 @@ def qe_channel_topk(x, w, k, topk, hist, stream=None):
     T, d_in = x.shape
     _check(_lib.qe_channel_topk(_ptr(x), _dtype_code(x), _ptr(w), T, d_in, k, _ptr(topk), _ptr(hist),
                                 _stream(stream)), "qe_channel_topk")
+
+
+def qe_partition_channels(hist: np.ndarray, k: int, n_r: int):
+    """Host frequency partition; returns (indep int32 [k], dep int32 [n_r*k], slot int32 [d_in])."""
+    hist = np.ascontiguousarray(hist, dtype=np.uint32)
+    d_in = hist.shape[0]
+    indep = np.empty(max(k, 0), np.int32)
+    dep = np.empty(max(k * n_r, 0), np.int32)
+    slot = np.empty(d_in, np.int32)
+    _check(_lib.qe_partition_channels(_ptr(hist), d_in, k, n_r, _ptr(indep), _ptr(dep), _ptr(slot)),
+           "qe_partition_channels")
+    return indep, dep, slot
+
+
+def qe_cooccur_workspace_bytes(T, n_dep) -> int:
+    return _lib.qe_cooccur_workspace_bytes(T, n_dep)
+
+
+def qe_cooccur(topk, slot, n_dep, cooc, ws, stream=None):
+    """Enqueue cooc += O^T O for the token-dependent channels (device tensors; ws: a byte
+    tensor of at least qe_cooccur_workspace_bytes(T, n_dep) bytes)."""
+    T, k = topk.shape
+    _check(_lib.qe_cooccur(_ptr(topk), T, k, _ptr(slot), slot.shape[0], n_dep, _ptr(cooc), _ptr(ws),
+                           ws.numel() * ws.element_size(), _stream(stream)), "qe_cooccur")
+
+
+def qe_cluster_channels(cooc: np.ndarray, T: int, n_clusters: int, threshold: float = 0.2, outputs: bool = False):
+    """Host NPMI similarity, spectral embedding and K-Means; returns labels int32 [n_dep], and with
+    outputs=True also (similarity, eigvals, embedding)."""
+    cooc = np.ascontiguousarray(cooc, dtype=np.uint32)
+    n = cooc.shape[0]
+    labels = np.empty(n, np.int32)
+    sim = np.empty((n, n), np.float64) if outputs else None
+    ev = np.empty(max(n_clusters, 0), np.float64) if outputs else None
+    emb = np.empty((n, max(n_clusters, 0)), np.float64) if outputs else None
+    _check(_lib.qe_cluster_channels(_ptr(cooc), n, T, n_clusters, threshold, _ptr(labels), _ptr(sim), _ptr(ev),
+                                    _ptr(emb)), "qe_cluster_channels")
+    return (labels, sim, ev, emb) if outputs else labels
 
 
 def qe_probe_mfma_i8(out, blocks, iters, operands=0, stream=None):

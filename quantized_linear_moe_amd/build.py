@@ -14,7 +14,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libqe.so")
-SOURCES = ["qe_api.hip", "k_act.hip", "k_gemm_w4.hip", "k_decode.hip", "k_stat.hip", "k_prep.hip", "k_probe.hip"]
+SOURCES = ["qe_api.hip", "k_act.hip", "k_gemm_w4.hip", "k_decode.hip", "k_stat.hip", "k_prep.hip", "k_probe.hip",
+           "k_cooc.hip", "calib_host.hip"]
 ARCH = "gfx950"
 
 

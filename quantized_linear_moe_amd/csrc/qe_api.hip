@@ -9,6 +9,7 @@
 #include <thread>
 #include <vector>
 
+#include "qe_calib.h"
 #include "qe_internal.h"
 
 namespace qe {
@@ -576,6 +577,62 @@ int qe_channel_topk(const void* x, int32_t x_dtype, const float* w, int32_t T, i
     QE_CHECK(aligned16(x) && aligned16(w) && aligned16(hist), QE_ERR_ALIGNMENT);
     if (topk) QE_CHECK(aligned16(topk), QE_ERR_ALIGNMENT);
     QE_TRY_HIP(launch_topk(x, x_dtype, w, T, d_in, k, topk, hist, S(stream)));
+    return QE_OK;
+}
+
+// ------------------------------------------------------ channel partition and clustering
+int qe_partition_channels(const uint32_t* hist, int32_t d_in, int32_t k, int32_t n_r, int32_t* indep,
+                          int32_t* dep, int32_t* slot) {
+    QE_CHECK(hist && indep && dep, QE_ERR_INVALID_ARG);
+    QE_CHECK(d_in >= 1 && k >= 1 && n_r >= 1, QE_ERR_INVALID_ARG);
+    QE_CHECK((int64_t)k * (1 + (int64_t)n_r) <= d_in, QE_ERR_INVALID_ARG);
+    std::vector<int32_t> order(d_in);
+    frequency_order(hist, d_in, order.data());
+    const int n_dep = k * n_r;
+    std::copy(order.begin(), order.begin() + k, indep);
+    std::copy(order.begin() + k, order.begin() + k + n_dep, dep);
+    if (slot) {
+        std::fill(slot, slot + d_in, -1);
+        for (int m = 0; m < n_dep; ++m) slot[dep[m]] = m;
+    }
+    return QE_OK;
+}
+
+size_t qe_cooccur_workspace_bytes(int32_t T, int32_t n_dep) {
+    if (T < 0 || n_dep < 1 || n_dep > 8192) return 0;
+    return cooccur_workspace_bytes(T, n_dep);
+}
+
+int qe_cooccur(const int32_t* topk, int32_t T, int32_t k, const int32_t* slot, int32_t d_in, int32_t n_dep,
+               uint32_t* cooc, void* ws, size_t ws_bytes, void* stream) {
+    QE_CHECK(T >= 0 && d_in >= 1 && n_dep >= 1 && k >= 1 && k <= d_in, QE_ERR_INVALID_ARG);
+    QE_CHECK(k <= 1024 && n_dep <= 8192, QE_ERR_UNSUPPORTED);
+    if (T == 0) return QE_OK;
+    QE_CHECK(topk && slot && cooc, QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(topk) && aligned16(slot) && aligned16(cooc), QE_ERR_ALIGNMENT);
+    QE_CHECK(ws != nullptr && ws_bytes >= cooccur_workspace_bytes(T, n_dep), QE_ERR_WORKSPACE);
+    QE_CHECK(aligned16(ws), QE_ERR_ALIGNMENT);
+    QE_TRY_HIP(launch_cooccur(topk, T, k, slot, d_in, n_dep, cooc, ws, S(stream)));
+    return QE_OK;
+}
+
+int qe_cluster_channels(const uint32_t* cooc, int32_t n_dep, int64_t T, int32_t n_clusters, double threshold,
+                        int32_t* labels, double* similarity, double* eigvals, double* embedding) {
+    QE_CHECK(cooc && labels, QE_ERR_INVALID_ARG);
+    QE_CHECK(n_dep >= 1 && T >= 1 && n_clusters >= 1 && n_clusters <= n_dep, QE_ERR_INVALID_ARG);
+    QE_CHECK(threshold >= 0.0 && threshold <= 1.0, QE_ERR_INVALID_ARG);  // also rejects NaN
+    QE_CHECK(n_dep <= 2048, QE_ERR_UNSUPPORTED);
+    const size_t n = (size_t)n_dep;
+    for (size_t i = 0; i < n; ++i) {
+        const uint32_t cii = cooc[i * n + i];
+        QE_CHECK((int64_t)cii <= T, QE_ERR_INVALID_ARG);
+        for (size_t j = 0; j < n; ++j) {
+            const uint32_t cij = cooc[i * n + j];
+            QE_CHECK(cij == cooc[j * n + i] && cij <= cii && cij <= cooc[j * n + j], QE_ERR_INVALID_ARG);
+        }
+    }
+    if (spectral_cluster(cooc, n_dep, T, n_clusters, threshold, labels, similarity, eigvals, embedding) != 0)
+        return QE_ERR_UNSUPPORTED;
     return QE_OK;
 }
 
