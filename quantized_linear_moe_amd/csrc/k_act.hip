@@ -594,9 +594,11 @@ __global__ __launch_bounds__(256) void route_pass_kernel(const uint16_t* __restr
     if (lg == 0 && rvalid) amax_part[(size_t)ks * T + row] = m;
 }
 
+// Enough workgroups to stream x at full rate, at least two channel groups each, and at most
+// 16 splits: the finish kernel loads up to 16 partials of a column at once.
 int route_pass_ksplit(int T, int d_in) {
     const int tiles = (T + RP_TOK - 1) / RP_TOK;
-    const int ks = std::min((768 + tiles - 1) / tiles, std::max(1, d_in / (2 * RP_KG)));
+    const int ks = std::min({(768 + tiles - 1) / tiles, std::max(1, d_in / (2 * RP_KG)), 16});
     return std::max(ks, 1);
 }
 

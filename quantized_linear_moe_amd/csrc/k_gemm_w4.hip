@@ -29,6 +29,11 @@
 //   * Epilogue: int32 -> float, scale by s_x and s_w, then bf16 MFMA
 //     16x16x32 steps accumulate u.B_s and, for every routed expert present in
 //     the tile, (v masked to that expert's tokens).B_e on top of it.
+//   * Few tokens (a grid far below the CU count): the K steps are split over
+//     gridDim.y workgroups that store their exact int32 partial sums; a finish
+//     kernel adds them in split order (still exact) and applies the epilogue.
+
+#include <algorithm>
 
 #include "qe_dma.h"
 #include "qe_internal.h"
@@ -65,7 +70,7 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     const float* __restrict__ w_scale, int T, int d_in, int d_out, const uint16_t* __restrict__ u,
     const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v, const int32_t* __restrict__ expert,
     const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, const int32_t* __restrict__ perm, float* __restrict__ y,
-    int32_t* __restrict__ acc_debug, int n_tm) {
+    int32_t* __restrict__ acc_debug, int n_tm, int32_t* __restrict__ part) {
     constexpr int BM = MB * 16;
     constexpr int A_STAGE = BM * G_BK;            // bytes of codes per stage
     constexpr int B_STAGE = 4 * G_NBW * 512;      // 4 waves x 4 N blocks x 512 B of packed weights
@@ -80,6 +85,8 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     const int tm = blockIdx.x % n_tm, tn = blockIdx.x / n_tm;
     const int m0 = tm * BM;
     const int NB = d_out >> 4, KB = d_in / G_BK;
+    // K steps of this workgroup: all of them, or split gridDim.y of `part`'s partial sums
+    const int kb_beg = (int)((long)blockIdx.y * KB / gridDim.y), nk = (int)((long)(blockIdx.y + 1) * KB / gridDim.y) - kb_beg;
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
     const int nb0 = tn * (G_BN / 16) + wid * G_NBW;
     const int lr = lane & 15, lg = lane >> 4;
@@ -141,8 +148,9 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
         const int nb = nb0 + 2 * p + (lane >> 5);
         b_src[p] = w_tiled + (size_t)(nb < NB ? nb : 0) * KB * 512 + (lane & 31) * 16;
     }
-    auto issue = [&](int stage, int kb) {  // copy K step kb into ring slot `stage`
+    auto issue = [&](int stage, int i) {  // copy the workgroup's K step i into ring slot `stage`
         const uint32_t base = lds0 + stage * STAGE;
+        const int kb = kb_beg + i;
 #pragma unroll
         for (int p = 0; p < A_DMA; ++p) dma16(a_src[p] + (size_t)kb * G_BK, base + (wid + 4 * p) * 1024);
 #pragma unroll
@@ -161,13 +169,13 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
 
     // prologue: three stages in flight, then wait for the first
 #pragma unroll
-    for (int st = 0; st < NS - 1; ++st) issue(st, min(st, KB - 1));
+    for (int st = 0; st < NS - 1; ++st) issue(st, min(st, nk - 1));
     QE_WAIT_VMCNT_LDS((NS - 2) * OPS);
     QE_WG_BARRIER();
 
-    for (int kb = 0; kb < KB; ++kb) {
+    for (int kb = 0; kb < nk; ++kb) {
         // refill the slot consumed in the previous step (past the end: a harmless repeat)
-        issue((kb + NS - 1) % NS, min(kb + NS - 1, KB - 1));
+        issue((kb + NS - 1) % NS, min(kb + NS - 1, nk - 1));
         const uint8_t* st = smem + (kb % NS) * STAGE;
         v2u bp[G_NBW];
 #pragma unroll
@@ -198,6 +206,22 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
         QE_WG_BARRIER();
     }
     QE_WAIT_VMCNT(0);
+
+    if (part) {  // split K: this workgroup's exact partial sums, in token order
+        int32_t* pt = part + (size_t)blockIdx.y * T * d_out;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m * 16 + lg * 4 + r;
+                if (m0 + row >= T) continue;
+                int32_t* prow = pt + (size_t)s_tok[row] * d_out;
+#pragma unroll
+                for (int j = 0; j < G_NBW; ++j)
+                    if (nb_ok[j]) prow[(nb0 + j) * 16 + lr] = acc[m][j][r] >> 4;
+            }
+        return;
+    }
 
     // ------------------------------------------------------------ epilogue
     // lane holds column (nb*16 + lr) and rows (m*16 + lg*4 + r) of each block; the A
@@ -439,19 +463,34 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     }
 }
 
+// K splits of the main product (fast epilogue only): 1 unless the 64-token-tile grid
+// leaves CUs idle.  The 64-token tiles hold one workgroup per CU (their LDS ring), so the
+// split grid is kept to one round of 256 workgroups; each split keeps at least 8 K steps,
+// and the int32 partials (written and read once) stay within twice the packed weights.
+int gemm_ksplit(int T, int d_in, int d_out) {
+    const long tiles = (long)((T + 63) / 64) * ((d_out + G_BN - 1) / G_BN);
+    if (T <= 0 || tiles >= 128) return 1;
+    const long ks = std::min({256 / tiles, (long)(d_in / G_BK / 8), (long)d_in / (4L * T)});
+    return (int)std::max(ks, 1L);
+}
+
 hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* w_tiled, const float* w_scale, int T,
                           int d_in, int d_out, const uint16_t* u, const uint16_t* bt_s, int rs_pad, const uint16_t* v,
                           const int32_t* expert, const uint16_t* bt_r, int rr_pad, int n_r, const int32_t* perm,
-                          float* y, int32_t* acc_debug, hipStream_t st) {
+                          float* y, int32_t* acc_debug, int ksplit, int32_t* part, hipStream_t st) {
     if (T <= 0) return hipSuccess;
     const int n_tn = (d_out + G_BN - 1) / G_BN;
     // 128-token tiles unless that leaves the chip less than two workgroups per CU
     const bool small = (long)((T + 127) / 128) * n_tn < 512;
     const uint8_t* w = w_tiled;
+    const bool split = ksplit > 1 && part != nullptr && acc_debug == nullptr && rs_pad <= 32 && rr_pad <= 32;
+    if (split && !small) return hipErrorInvalidValue;
     const bool fast = !acc_debug && rs_pad <= 32 && rr_pad <= 32;
-#define QE_GEMM_LAUNCH(MBV, FAST, NTM)                                                                          \
-    hipLaunchKernelGGL((gemm_w4_kernel<MBV, FAST>), dim3((NTM) * n_tn), dim3(256), 0, st, codes, s_x, w, w_scale, T, \
-                       d_in, d_out, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, perm, y, acc_debug, NTM)
+    const int ks = split ? ksplit : 1;
+    int32_t* pp = split ? part : nullptr;
+#define QE_GEMM_LAUNCH(MBV, FAST, NTM)                                                                     \
+    hipLaunchKernelGGL((gemm_w4_kernel<MBV, FAST>), dim3((NTM) * n_tn, ks), dim3(256), 0, st, codes, s_x, w, \
+                       w_scale, T, d_in, d_out, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, perm, y, acc_debug, NTM, pp)
     if (small) {
         const int n_tm = (T + 63) / 64;
         if (fast) QE_GEMM_LAUNCH(4, true, n_tm);
@@ -462,7 +501,11 @@ hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* 
         else QE_GEMM_LAUNCH(8, false, n_tm);
     }
 #undef QE_GEMM_LAUNCH
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !split) return e;
+    const bool routed = v != nullptr && expert != nullptr && bt_r != nullptr && rr_pad > 0 && n_r > 0;
+    return launch_gemm_split_finish(part, ks, T, d_out, s_x, w_scale, rs_pad > 0 ? u : nullptr, bt_s, rs_pad,
+                                    routed ? v : nullptr, routed ? expert : nullptr, n_r, bt_r, rr_pad, y, st);
 }
 
 }  // namespace qe

@@ -182,8 +182,10 @@ WsLayout ws_layout(const qe_linear* lin, int T) {
     off = align256(off + t * P.rs_pad * 2);
     W.v = off;
     off = align256(off + t * P.rr_pad * 2);
+    W.gemm_ksplit = lin->a_bits != 16 ? gemm_ksplit(T, lin->d_in, lin->d_out) : 1;
     W.skinny = off;
-    off = align256(off + (size_t)std::max(W.skinny_ksplit, D.ks_m) * t * lin->d_out * 4);
+    off = align256(off + (size_t)std::max({W.skinny_ksplit, D.ks_m, W.gemm_ksplit > 1 ? W.gemm_ksplit : 0}) * t *
+                             lin->d_out * 4);
     W.total = off;
     return W;
 }
@@ -421,9 +423,11 @@ static int run_gemm(const qe_linear* lin, const int8_t* codes, const float* s_x,
         QE_TRY_HIP(launch_skinny_finish(part, W.skinny_ksplit, T, lin->d_out, w_scale, u, bt_s, P.rs_pad, v, expert,
                                         bt_r, P.rr_pad, y, s));
     } else {
+        const WsLayout W = ws_layout(lin, T);
+        const int ks = acc_debug ? 1 : W.gemm_ksplit;
         QE_TRY_HIP(launch_gemm_w4(codes, s_x, at<const uint8_t>(lin->prep, P.w_tiled), w_scale, T, lin->d_in,
                                   lin->d_out, u, bt_s, P.rs_pad, v, expert, bt_r, P.rr_pad, lin->n_routed, perm, y,
-                                  acc_debug, s));
+                                  acc_debug, ks, ks > 1 ? at<int32_t>(ws, W.skinny) : nullptr, s));
     }
     return QE_OK;
 }

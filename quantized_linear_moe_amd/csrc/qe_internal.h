@@ -66,6 +66,7 @@ struct WsLayout {
     int skinny_ksplit;
     size_t vpart;       // float [eq_ksplit][T][rr_pad] (expert-quant split-K partials)
     int rp_ksplit, eq_ksplit;  // 0 unless the two-pass prefill prologue is used
+    int gemm_ksplit;           // K splits of the A6/A8 main product (partials in `skinny`)
 };
 
 PrepLayout prep_layout(const qe_linear* lin);
@@ -106,10 +107,18 @@ int expert_quant_ksplit(int T, int d_in);
 hipError_t launch_bucket(const int32_t* expert, int T, int n_r, int32_t* counts, int32_t* offsets,
                          int32_t* perm, hipStream_t st);
 
+// ksplit > 1 (with part: int32 [ksplit][T][d_out]) splits the K steps over workgroups and
+// adds the partial sums in a finish kernel; only for grids of 64-token tiles (gemm_ksplit)
 hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* w_tiled, const float* w_scale,
                           int T, int d_in, int d_out, const uint16_t* u, const uint16_t* bt_s, int rs_pad,
                           const uint16_t* v, const int32_t* expert, const uint16_t* bt_r, int rr_pad, int n_r,
-                          const int32_t* perm, float* y, int32_t* acc_debug, hipStream_t st);
+                          const int32_t* perm, float* y, int32_t* acc_debug, int ksplit, int32_t* part,
+                          hipStream_t st);
+int gemm_ksplit(int T, int d_in, int d_out);
+hipError_t launch_gemm_split_finish(const int32_t* part, int ksplit, int T, int d_out, const float* s_x,
+                                    const float* w_scale, const uint16_t* u, const uint16_t* bt_s, int rs_pad,
+                                    const uint16_t* v, const int32_t* expert, int n_r, const uint16_t* bt_r,
+                                    int rr_pad, float* y, hipStream_t st);
 
 // weight streaming for few tokens: w_bits 3 / 4 read packed tiles, w_bits 16 reads bf16 rows
 // (the x-projection matrix); part[ks][t][c] with row stride out_ld

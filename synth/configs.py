@@ -160,7 +160,27 @@ _C5 = QEConfig(
     description="Qwen2VL-72B-shaped MLP up/down in decode, T=8, W3A16 weight-only",
 )
 
-CONFIGS: Dict[str, QEConfig] = {c.name: c for c in (_C1, _C2, _C3, _C4, _C5)}
+# The linear shapes of the listing's Table 8 (NPU speedups of QE over fp16 for Qwen2VL-7B
+# linears in prefill at sequence length 128): IC x OC = 3584 x 3584, 3584 x 18944 and
+# 18944 x 3584; the table covers W4A6, W4A8 and W3A16 (this default is W4A6).
+_C6 = QEConfig(
+    name="qwen2vl_7b_s128",
+    seed=5,
+    T=128,
+    w_bits=4,
+    a_bits=6,
+    r_shared=32,
+    n_routed=8,
+    r_routed=32,
+    k=32,
+    linears=(LinearSpec("q", 3584, 3584, "x_attn"), LinearSpec("up", 3584, 18944, "x_mlp"),
+             LinearSpec("down", 18944, 3584, "x_down")),
+    acts=_streams(ActRecipe(modalities=((96, 4, 20.0, 64, 2, 10.0), (32, 4, 20.0, 64, 2, 10.0))),
+                  names=("x_attn", "x_mlp", "x_down")),
+    description="Qwen2VL-7B linear shapes of Table 8, prefill s=128 (96 image-like + 32 text-like tokens)",
+)
+
+CONFIGS: Dict[str, QEConfig] = {c.name: c for c in (_C1, _C2, _C3, _C4, _C5, _C6)}
 
 
 def get_config(name: str) -> QEConfig:

@@ -1,0 +1,97 @@
+"""GPU parity of the quantized linear at few tokens, where the main product splits its K
+steps over workgroups (exact int32 partial sums added by a finish kernel): the listing's
+Table 8 shapes (Qwen2VL-7B linears, prefill s = 128, W4A6 and W4A8) and decode with
+quantized activations (Qwen2VL-72B MLP, T = 8)."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import qe_oracle as O
+from qe_testlib import check_y, oracle_for, rel_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module")
+def Q():
+    import quantized_linear_moe_amd as q
+    return q
+
+
+def _spec(cfg, name):
+    return next(l for l in cfg.linears if l.name == name)
+
+
+def _cfg(name, **kw):
+    return dataclasses.replace(synth.get_config(name), **kw)
+
+
+# main product alone: the split-K result equals the one-pass result bit for bit (the
+# accumulator dump forces one pass), and both equal the oracle's exact accumulators
+@pytest.mark.parametrize("cfg_name,lin_name,T", [("qwen2vl_7b_s128", "q", None), ("qwen2vl_7b_s128", "down", None),
+                                                 ("qwen2vl_7b_s128", "up", 77), ("qwen2vl_72b_decode", "up", None),
+                                                 ("qwen2vl_72b_decode", "down", 3)])
+def test_split_k_main_product_bit_exact(Q, cfg_name, lin_name, T):
+    cfg = _cfg(cfg_name, w_bits=4, a_bits=6)
+    spec = _spec(cfg, lin_name)
+    params = synth.gen_linear(cfg, spec)
+    layer = Q.QELinear.from_params(params, 4, 6, device=DEV)
+    x = synth.gen_activations(cfg, spec.stream, T=T)
+    T = x.shape[0]
+    codes = torch.empty(x.shape, dtype=torch.int8, device=DEV)
+    s_x = torch.empty(T, dtype=torch.float32, device=DEV)
+    Q.libqe.qe_quant_act(x.to(DEV), torch.from_numpy(params["s"]).to(DEV), 6, codes, s_x)
+    ws = layer.workspace(T)
+    y_split = torch.empty(T, spec.d_out, dtype=torch.float32, device=DEV)
+    y_one = torch.empty_like(y_split)
+    acc = torch.empty(T, spec.d_out, dtype=torch.int32, device=DEV)
+    Q.libqe.qe_wq_gemm(layer.lin, codes, s_x, None, T, None, None, None, y_split, None, ws)
+    Q.libqe.qe_wq_gemm(layer.lin, codes, s_x, None, T, None, None, None, y_one, acc, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(y_split.cpu().numpy().view(np.uint32), y_one.cpu().numpy().view(np.uint32))
+    qx, sx = O.quant_act(x.float().numpy(), params["s"], 6)
+    qw, s_w = O.quant_weights(params["W_f"], params["s"], 4)
+    acc_ref, y_ref = O.main_term_int(qx, sx, qw, s_w)
+    assert np.array_equal(acc.cpu().numpy().astype(np.int64), acc_ref)
+    assert rel_err(y_split.cpu().numpy(), y_ref) <= 2e-3
+
+
+# the whole QE linear (prologue, split-K main product, shared and routed terms)
+@pytest.mark.parametrize("lin_name", ["q", "up", "down"])
+@pytest.mark.parametrize("a_bits", [6, 8])
+def test_table8_shapes_forward(Q, lin_name, a_bits):
+    cfg = _cfg("qwen2vl_7b_s128", a_bits=a_bits)
+    spec = _spec(cfg, lin_name)
+    params = synth.gen_linear(cfg, spec)
+    layer = Q.QELinear.from_params(params, 4, a_bits, device=DEV)
+    x = synth.gen_activations(cfg, spec.stream)
+    T = x.shape[0]
+    y = torch.empty(T, spec.d_out, dtype=torch.float32, device=DEV)
+    expert = torch.empty(T, dtype=torch.int32, device=DEV)
+    layer.forward(x.to(DEV), y, expert)
+    torch.cuda.synchronize()
+    ref = oracle_for(params, x, 4, a_bits)
+    err = check_y(y.cpu().numpy(), ref, params, x, 4, a_bits, gpu_expert=expert.cpu().numpy())
+    print(f"7B {lin_name} W4A{a_bits} T={T}: max rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("lin_name", ["up", "down"])
+@pytest.mark.parametrize("a_bits,T", [(6, 8), (8, 8), (6, 1), (8, 16)])
+def test_decode_quantized_activations(Q, lin_name, a_bits, T):
+    cfg = _cfg("qwen2vl_72b_decode", w_bits=4, a_bits=a_bits)
+    spec = _spec(cfg, lin_name)
+    params = synth.gen_linear(cfg, spec)
+    layer = Q.QELinear.from_params(params, 4, a_bits, device=DEV)
+    x = synth.gen_activations(cfg, spec.stream, T=T)
+    y = torch.empty(T, spec.d_out, dtype=torch.float32, device=DEV)
+    expert = torch.empty(T, dtype=torch.int32, device=DEV)
+    layer.forward(x.to(DEV), y, expert)
+    torch.cuda.synchronize()
+    ref = oracle_for(params, x, 4, a_bits)
+    err = check_y(y.cpu().numpy(), ref, params, x, 4, a_bits, gpu_expert=expert.cpu().numpy())
+    print(f"decode {lin_name} W4A{a_bits} T={T}: max rel err {err:.3e}")
