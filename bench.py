@@ -428,14 +428,69 @@ def layer_throughput(torch, synth, qe, libqe, dev, name, steps=10):
             "layer_roofline_frac": round(t_roof / t, 4)}
 
 
-def extras(torch, synth, qe, libqe, dev, copy_gbs=None):
-    out = {}
-    # ---- the other configurations: a small single linear (latency), a 2B layer, an 8B layer
-    out["linear_tiny_w4a8_T64"] = layer_throughput(torch, synth, qe, libqe, dev, "tiny", steps=50)
-    out["layer_qwen2vl2b_w4a6_T2048"] = layer_throughput(torch, synth, qe, libqe, dev, "qwen2vl_2b")
-    out["layer_internvl2_8b_w4a8_T4096"] = layer_throughput(torch, synth, qe, libqe, dev, "internvl2_8b")
-    # ---- decode: Qwen2VL-72B MLP up/down, W3A16, T=8 (HBM-bound weight streaming)
-    cfg = synth.get_config("qwen2vl_72b_decode")
+TABLE8_NPU = {(3584, 3584): {"W4A6": 3.56, "W4A8": 3.50, "W3A16": 4.10},
+              (3584, 18944): {"W4A6": 3.60, "W4A8": 3.59, "W3A16": 4.50},
+              (18944, 3584): {"W4A6": 3.84, "W4A8": 3.77, "W3A16": 4.50}}
+
+
+def table8(torch, synth, qe, libqe, dev, reps=20):
+    """The listing's Table 8 workload on this GPU: each Qwen2VL-7B linear shape at s = 128 as a
+    QE linear (W4A6, W4A8, W3A16: the composite entry point, inputs resident) against the same
+    linear in bf16 through torch (hipBLASLt), warm.  The pages' column is an analytical NPU
+    model's speedup over fp16, given for context."""
+    import dataclasses
+
+    def med_us(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts)) * 1e3
+
+    base = synth.get_config("qwen2vl_7b_s128")
+    rows = []
+    for spec in base.linears:
+        x = synth.gen_activations(base, spec.stream).to(dev)
+        W = None
+        for wb, ab in ((4, 6), (4, 8), (3, 16)):
+            cfg = dataclasses.replace(base, w_bits=wb, a_bits=ab)
+            params = synth.gen_linear(cfg, spec)
+            if W is None:
+                W = torch.from_numpy(params["W_f"]).to(torch.bfloat16).to(dev)
+                xb = x.to(torch.bfloat16)
+                t_bf16 = med_us(lambda: torch.nn.functional.linear(xb, W))
+            layer = qe.QELinear.from_params(params, wb, ab, device=dev)
+            del params
+            ws = layer.workspace(base.T)
+            y = torch.empty(base.T, spec.d_out, dtype=torch.float32, device=dev)
+            t_qe = med_us(lambda: libqe.qe_linear_forward(layer.lin, x, y, None, ws))
+            key = f"W{wb}A{ab}"
+            bf16_roof_us = max(2.0 * spec.d_in * spec.d_out / (PEAK_HBM_GBS * 1e3),
+                               2.0 * base.T * spec.d_in * spec.d_out / (PEAK_BF16_TFLOPS * 1e6))
+            rows.append({"shape": f"{spec.d_in}x{spec.d_out}", "bits": key, "qe_us": round(t_qe, 2),
+                         "bf16_torch_us": round(t_bf16, 2), "speedup_vs_bf16": round(t_bf16 / t_qe, 3),
+                         "bf16_roofline_us": round(bf16_roof_us, 2),
+                         "speedup_vs_bf16_roofline": round(bf16_roof_us / t_qe, 3),
+                         "npu_speedup_pages": TABLE8_NPU[(spec.d_in, spec.d_out)][key]})
+            del layer, ws, y
+        del W, x
+        torch.cuda.empty_cache()
+    return {"T": base.T, "rows": rows,
+            "note": "bf16_roofline_us = max(bf16 weight bytes / 8 TB/s, flops / 2.5 PFLOP/s)"}
+
+
+def decode_line(torch, synth, qe, libqe, dev, w_bits, a_bits, copy_gbs=None):
+    """Qwen2VL-72B MLP up + down at T = 8 through the composite entry point, cold (the Infinity
+    Cache flushed before every iteration) and warm."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.get_config("qwen2vl_72b_decode"), w_bits=w_bits, a_bits=a_bits)
     layers = []
     for spec in cfg.linears:
         params = synth.gen_linear(cfg, spec)
@@ -477,7 +532,7 @@ def extras(torch, synth, qe, libqe, dev, copy_gbs=None):
         nd = int(torch.unique(es[i]).numel())
         alg += libqe.qe_linear_cost(layer.lin, T, nd, 2)[2]
     t_cold = float(np.median(cold)) * 1e-3
-    out["decode_qwen2vl72b_up_down_w3a16_T8"] = {
+    res = {
         "us_cold_median": round(t_cold * 1e6, 2), "us_cold_p10": round(float(np.percentile(cold, 10)) * 1e3, 2),
         "us_cold_p90": round(float(np.percentile(cold, 90)) * 1e3, 2),
         "us_warm_median": round(float(np.median(warm)) * 1e3, 2),
@@ -488,6 +543,20 @@ def extras(torch, synth, qe, libqe, dev, copy_gbs=None):
     }
     del layers, wss, flush
     torch.cuda.empty_cache()
+    return res
+
+
+def extras(torch, synth, qe, libqe, dev, copy_gbs=None):
+    out = {}
+    out["table8_qwen2vl7b_s128"] = table8(torch, synth, qe, libqe, dev)
+    # ---- the other configurations: a small single linear (latency), a 2B layer, an 8B layer
+    out["linear_tiny_w4a8_T64"] = layer_throughput(torch, synth, qe, libqe, dev, "tiny", steps=50)
+    out["layer_qwen2vl2b_w4a6_T2048"] = layer_throughput(torch, synth, qe, libqe, dev, "qwen2vl_2b")
+    out["layer_internvl2_8b_w4a8_T4096"] = layer_throughput(torch, synth, qe, libqe, dev, "internvl2_8b")
+    # ---- decode: Qwen2VL-72B MLP up/down, T=8 (HBM-bound weight streaming): W3A16 (the
+    # configuration's own), and W4A6 (quantized activations: few-token split-K main product)
+    out["decode_qwen2vl72b_up_down_w3a16_T8"] = decode_line(torch, synth, qe, libqe, dev, 3, 16, copy_gbs)
+    out["decode_qwen2vl72b_up_down_w4a6_T8"] = decode_line(torch, synth, qe, libqe, dev, 4, 6, copy_gbs)
 
     # ---- calibration statistic: InternVL2-8B down input, k = 32 (HBM / ALU bound)
     cfg = synth.get_config("internvl2_8b")
