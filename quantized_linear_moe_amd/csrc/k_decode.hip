@@ -14,8 +14,13 @@
 // accumulators through LDS, so one float32 partial per (K split, token,
 // channel) leaves the workgroup.  Tokens (<= 16 per pass) form the MFMA M side;
 // the token tile of x for the workgroup's K range is staged in LDS once.
+//
+// With quantized activations (W4A6 / W4A8 decode) the same tile streams the 4-bit weights
+// against the int8 activation codes on the int8 matrix cores (int32 partials, exact), and
+// the finish applies s_x[t] * s_w[i] as the main GEMM's epilogue does.
 
 #include <algorithm>
+#include <type_traits>
 
 #include "qe_internal.h"
 #include "qe_splits.h"
@@ -34,9 +39,10 @@ constexpr int SK_LD = SK_MAX_KBLK * 128 * 2 + 16;  // LDS row stride (bytes) of 
 //   WB == 4 : 4 dwords: the lane's 8 bytes of the two 64-K steps of the int8-GEMM tile
 //             layout (see the 4-bit prepare kernel).
 //   WB == 16: bf16 rows (K-contiguous); the fragment is loaded per step (no tile layout).
+//   WB == 8 : the 4-bit layout of WB == 4, multiplied with int8 activation codes.
 template <int WB>
 struct Frag {
-    static constexpr int kWords = WB == 3 ? 3 : WB == 4 ? 4 : 16;
+    static constexpr int kWords = WB == 3 ? 3 : (WB == 4 || WB == 8) ? 4 : 16;
 };
 
 __device__ inline uint32_t pack_bf16_pair_from_int(int lo, int hi) {
@@ -103,7 +109,7 @@ __device__ inline void load_frag(const uint32_t* __restrict__ w, int nb, int NB,
         f[0] = p[0];
         f[1] = p[1];
         f[2] = p[2];
-    } else if constexpr (WB == 4) {
+    } else if constexpr (WB == 4 || WB == 8) {
         // two 64-K steps of the 4-bit tile layout: 8 bytes per lane each
         const v2u q0 = *reinterpret_cast<const v2u*>(w + (((size_t)nb * 2 * KB + 2 * kb) * 64 + lane) * 2);
         const v2u q1 = *reinterpret_cast<const v2u*>(w + (((size_t)nb * 2 * KB + 2 * kb + 1) * 64 + lane) * 2);
@@ -124,7 +130,8 @@ __device__ inline void load_frag(const uint32_t* __restrict__ w, int nb, int NB,
 //   part[ks][t][c] = sum over the K blocks [kb0, kb1) of split ks of bf16(x)[t][k] * W[c][k]
 // for tokens t0 .. t0+15 and the NBW 16-channel blocks starting at nb0 (blocks at or past NB
 // add nothing and are not written); out_ld = row stride of part, ld = LDS row stride of the
-// x tile (>= 256 * (kb1 - kb0) + 16).
+// x tile (>= 256 * (kb1 - kb0) + 16).  WB == 8: x is int8 codes [T][d_in] and part holds the
+// exact int32 sums (the float buffer reinterpreted).
 template <int WB, int NBW>
 __device__ __attribute__((always_inline)) inline void skinny_tile(const void* __restrict__ x, int x_dtype, int T, int t0,
                                                                   int d_in, int NB, int nb0,
@@ -132,8 +139,10 @@ __device__ __attribute__((always_inline)) inline void skinny_tile(const void* __
                                                                   int ksplit, int ld, float* __restrict__ part,
                                                                   int out_ld) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    constexpr bool kI8 = WB == 8;
+    typedef __attribute__((ext_vector_type(4))) std::conditional_t<kI8, int, float> acc4;
     uint8_t* xs = smem;                          // [ntok][ld] x tile
-    float* red = reinterpret_cast<float*>(smem);  // [4][NBW][64][4], reuses the LDS after the main loop
+    acc4* red = reinterpret_cast<acc4*>(smem);   // [4][NBW][64], reuses the LDS after the main loop
     const int KB = d_in >> 7;
     const int kb0 = (int)((long)ks * KB / ksplit), kb1 = (int)((long)(ks + 1) * KB / ksplit);
     const int nkb = kb1 - kb0;
@@ -160,9 +169,9 @@ __device__ __attribute__((always_inline)) inline void skinny_tile(const void* __
         for (int j = 0; j < NBW; ++j) load_frag<WB>(w_tiled, nb0 + j, NB, kb, KB, lane, d_in, f[j]);
     }
 
-    // stage x[t0 .. t0+ntok)[kb0*128 .. kb1*128) as bf16, eight independent 16-byte loads
-    // per thread in flight per batch
-    const int kc8 = nkb * 16;  // 16-byte chunks per row
+    // stage x[t0 .. t0+ntok)[kb0*128 .. kb1*128) as bf16 (or int8 codes), eight independent
+    // 16-byte loads per thread in flight per batch
+    const int kc8 = nkb * (kI8 ? 8 : 16);  // 16-byte chunks per row
     const int total = ntok * kc8;
     for (int base = 0; base < total; base += 256 * 8) {
         v4u val[8];
@@ -172,8 +181,10 @@ __device__ __attribute__((always_inline)) inline void skinny_tile(const void* __
             val[q] = v4u{0, 0, 0, 0};
             if (i < total) {
                 const int r = i / kc8, c8 = i % kc8;
-                const size_t idx = (size_t)(t0 + r) * d_in + (size_t)kb0 * 128 + c8 * 8;
-                if (x_dtype == QE_BF16) {
+                const size_t idx = (size_t)(t0 + r) * d_in + (size_t)kb0 * 128 + c8 * (kI8 ? 16 : 8);
+                if constexpr (kI8) {
+                    val[q] = *reinterpret_cast<const v4u*>(reinterpret_cast<const int8_t*>(x) + idx);
+                } else if (x_dtype == QE_BF16) {
                     val[q] = *reinterpret_cast<const v4u*>(reinterpret_cast<const uint16_t*>(x) + idx);
                 } else {
                     const v4f* p = reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(x) + idx);
@@ -197,20 +208,34 @@ __device__ __attribute__((always_inline)) inline void skinny_tile(const void* __
     }
     __syncthreads();
 
-    v4f acc[NBW];
+    acc4 acc[NBW];
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) acc[j] = v4f{0, 0, 0, 0};
+    for (int j = 0; j < NBW; ++j) acc[j] = acc4{0, 0, 0, 0};
 
     // MFMAs of one K block held in w[] (x from the LDS tile; a block past the range gets zero x)
     auto mma = [&](const uint32_t (&w)[NBW][FW], int k) {
         const bool use = lr < ntok && k < kb1;
-        const uint8_t* xrow = xs + lr * ld + (kbc(k) - kb0) * 256;
+        if constexpr (kI8) {
+            // two 64-wide int8 steps: the lane's 16 codes at K offset 16*lg of each step, and the
+            // weight fragment's 8 bytes of that step expanded to 16*code
+            const uint8_t* xrow = xs + lr * ld + (kbc(k) - kb0) * 128;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const v8bf a = use ? *reinterpret_cast<const v8bf*>(xrow + x_step_offset<WB>(s, lg) * 2) : v8bf{};
+            for (int s = 0; s < 2; ++s) {
+                const v4i a = use ? *reinterpret_cast<const v4i*>(xrow + s * 64 + lg * 16) : v4i{0, 0, 0, 0};
 #pragma unroll
-            for (int j = 0; j < NBW; ++j)
-                acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, weight_frag<WB>(w[j], s), acc[j], 0, 0, 0);
+                for (int j = 0; j < NBW; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, unpack_w4x16(w[j][2 * s], w[j][2 * s + 1]),
+                                                                   acc[j], 0, 0, 0);
+            }
+        } else {
+            const uint8_t* xrow = xs + lr * ld + (kbc(k) - kb0) * 256;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const v8bf a = use ? *reinterpret_cast<const v8bf*>(xrow + x_step_offset<WB>(s, lg) * 2) : v8bf{};
+#pragma unroll
+                for (int j = 0; j < NBW; ++j)
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, weight_frag<WB>(w[j], s), acc[j], 0, 0, 0);
+            }
         }
     };
     if constexpr (kPrefetch) {
@@ -238,25 +263,25 @@ __device__ __attribute__((always_inline)) inline void skinny_tile(const void* __
     // reduce the 4 waves' accumulators (fixed order) through LDS
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < NBW; ++j)
-        *reinterpret_cast<v4f*>(red + ((wid * NBW + j) * 64 + lane) * 4) = acc[j];
+    for (int j = 0; j < NBW; ++j) red[(wid * NBW + j) * 64 + lane] = acc[j];
     __syncthreads();
     if (wid == 0) {
         float* out = part + (size_t)ks * T * out_ld;
 #pragma unroll
         for (int j = 0; j < NBW; ++j) {
-            v4f sum = *reinterpret_cast<const v4f*>(red + ((0 * NBW + j) * 64 + lane) * 4);
+            acc4 sum = red[j * 64 + lane];
 #pragma unroll
-            for (int w = 1; w < 4; ++w) {
-                const v4f o = *reinterpret_cast<const v4f*>(red + ((w * NBW + j) * 64 + lane) * 4);
-                sum += o;
-            }
+            for (int w = 1; w < 4; ++w) sum += red[(w * NBW + j) * 64 + lane];
             const int nb = nb0 + j;
             if (nb >= NB) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int tt = lg * 4 + r;
-                if (tt < ntok) out[(size_t)(t0 + tt) * out_ld + nb * 16 + lr] = sum[r];
+                if (tt >= ntok) continue;
+                if constexpr (kI8)  // 16 * sum exactly: the expanded weights carry a factor 16
+                    reinterpret_cast<int32_t*>(out)[(size_t)(t0 + tt) * out_ld + nb * 16 + lr] = sum[r] >> 4;
+                else
+                    out[(size_t)(t0 + tt) * out_ld + nb * 16 + lr] = sum[r];
             }
         }
     }
@@ -276,7 +301,8 @@ __global__ __launch_bounds__(256) void skinny_kernel(const void* __restrict__ x,
 // eight channel blocks at a time; each writes split-K partials for the finish kernel.  The
 // register budget is three waves per SIMD: the plan's three workgroups per compute unit.
 template <int WB>
-__global__ __launch_bounds__(256, 3) void decode_gemv_kernel(const void* __restrict__ x, int x_dtype, int T, int d_in,
+__global__ __launch_bounds__(256, 3) void decode_gemv_kernel(const void* __restrict__ x, int x_dtype,
+                                                          const int8_t* __restrict__ codes, int T, int d_in,
                                                           int d_out, const uint32_t* __restrict__ w_tiled, int ks_m,
                                                           int ld_m, float* __restrict__ part_m,
                                                           const uint32_t* __restrict__ mt, int ncp, int ks_p, int ld_p,
@@ -288,8 +314,8 @@ __global__ __launch_bounds__(256, 3) void decode_gemv_kernel(const void* __restr
                            part_p, ncp);
     } else {
         const int b = bid - n_pwg, NB = d_out >> 4, groups = (NB + SK_NB - 1) / SK_NB;
-        skinny_tile<WB, SK_NB>(x, x_dtype, T, 0, d_in, NB, (b % groups) * SK_NB, w_tiled, b / groups, ks_m, ld_m,
-                               part_m, d_out);
+        skinny_tile<WB, SK_NB>(WB == 8 ? static_cast<const void*>(codes) : x, x_dtype, T, 0, d_in, NB,
+                               (b % groups) * SK_NB, w_tiled, b / groups, ks_m, ld_m, part_m, d_out);
     }
 }
 
@@ -369,21 +395,22 @@ DecodePlan decode_plan(int d_in, int d_out, int w_bits, int ncp, int T) {
     return P;
 }
 
-hipError_t launch_decode_gemv(const void* x, int x_dtype, int T, int d_in, int d_out, int w_bits, const void* w_tiled,
-                              const DecodePlan& P, float* part_m, const uint16_t* mt, int ncp, float* part_p,
-                              hipStream_t st) {
+// codes != NULL: quantized activations (W4 only), int32 main partials
+hipError_t launch_decode_gemv(const void* x, int x_dtype, const int8_t* codes, int T, int d_in, int d_out, int w_bits,
+                              const void* w_tiled, const DecodePlan& P, float* part_m, const uint16_t* mt, int ncp,
+                              float* part_p, hipStream_t st) {
     if (T <= 0) return hipSuccess;
-    if (T > 16 || P.lds > 64 * 1024) return hipErrorInvalidValue;
+    if (T > 16 || P.lds > 64 * 1024 || (codes && w_bits != 4)) return hipErrorInvalidValue;
     const uint32_t* w = reinterpret_cast<const uint32_t*>(w_tiled);
     const uint32_t* m = reinterpret_cast<const uint32_t*>(mt);
     const int nwg = P.n_pwg + P.n_mwg;
-    if (w_bits == 3) {
-        hipLaunchKernelGGL(decode_gemv_kernel<3>, dim3(nwg), dim3(256), P.lds, st, x, x_dtype, T, d_in, d_out, w, P.ks_m,
-                           P.ld_m, part_m, m, ncp, P.ks_p, P.ld_p, part_p, P.n_pwg);
-    } else {
-        hipLaunchKernelGGL(decode_gemv_kernel<4>, dim3(nwg), dim3(256), P.lds, st, x, x_dtype, T, d_in, d_out, w, P.ks_m,
-                           P.ld_m, part_m, m, ncp, P.ks_p, P.ld_p, part_p, P.n_pwg);
-    }
+#define QE_DG_LAUNCH(WBV)                                                                                        \
+    hipLaunchKernelGGL(decode_gemv_kernel<WBV>, dim3(nwg), dim3(256), P.lds, st, x, x_dtype, codes, T, d_in, d_out, \
+                       w, P.ks_m, P.ld_m, part_m, m, ncp, P.ks_p, P.ld_p, part_p, P.n_pwg)
+    if (codes) QE_DG_LAUNCH(8);
+    else if (w_bits == 3) QE_DG_LAUNCH(3);
+    else QE_DG_LAUNCH(4);
+#undef QE_DG_LAUNCH
     return hipGetLastError();
 }
 
@@ -392,6 +419,8 @@ hipError_t launch_decode_gemv(const void* x, int x_dtype, int T, int d_in, int d
 // adapter inputs u (shared expert) and v (the token's routed expert), then writes, for its 64
 // channels and all tokens (wave w handles tokens w and w + 8),
 //   y[t][i] = s_w[i] * sum_ks part_m[ks][t][i] + u[t].Bt_s[i] + v[t].Bt_r[e_t][i]
+// or, with quantized activations (s_x != NULL, int32 main partials),
+//   y[t][i] = (float)(sum_ks part_m[ks][t][i]) * s_x[t] * s_w[i] + (the same adapter terms).
 // Partials are summed in split order; their loads are issued in independent batches of 16 (a
 // dependent chain of loads would cost one memory latency per split), and the phases are
 // ordered so that about three memory latencies are exposed.
@@ -399,7 +428,8 @@ constexpr int DF_CH = 64;
 constexpr int DF_THREADS = 512;
 
 __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
-    const float* __restrict__ part_m, int ks_m, int T, int d_out, const float* __restrict__ w_scale,
+    const float* __restrict__ part_m, const float* __restrict__ s_x, int ks_m, int T, int d_out,
+    const float* __restrict__ w_scale,
     const float* __restrict__ part_p, int ks_p, int ncp, int col_se, int r_s, int rs_pad, int col_re, int n_r,
     int r_r, int rr_pad, int col_router, const uint16_t* __restrict__ bt_s, const uint16_t* __restrict__ bt_r,
     int32_t* __restrict__ expert_out, float* __restrict__ y) {
@@ -453,7 +483,15 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int tt = t + 8 * h;
-        out[h] = tt < T ? sum_splits(part_m + (size_t)tt * d_out + i, (size_t)T * d_out, ks_m) * w_scale[i] : 0.0f;
+        if (tt >= T) {
+            out[h] = 0.0f;
+        } else if (s_x) {
+            const int32_t acc =
+                sum_splits_i32(reinterpret_cast<const int32_t*>(part_m) + (size_t)tt * d_out + i, (size_t)T * d_out, ks_m);
+            out[h] = (float)acc * s_x[tt] * w_scale[i];
+        } else {
+            out[h] = sum_splits(part_m + (size_t)tt * d_out + i, (size_t)T * d_out, ks_m) * w_scale[i];
+        }
     }
     __syncthreads();
     // 4. the routed expert's row, then the two dot products
@@ -492,14 +530,15 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
     }
 }
 
-hipError_t launch_decode_finish(const float* part_m, int ks_m, int T, int d_out, const float* w_scale,
-                                const float* part_p, int ks_p, int ncp, int col_se, int r_s, int rs_pad, int col_re,
-                                int n_r, int r_r, int rr_pad, int col_router, const uint16_t* bt_s,
-                                const uint16_t* bt_r, int32_t* expert_out, float* y, hipStream_t st) {
+hipError_t launch_decode_finish(const float* part_m, const float* s_x, int ks_m, int T, int d_out,
+                                const float* w_scale, const float* part_p, int ks_p, int ncp, int col_se, int r_s,
+                                int rs_pad, int col_re, int n_r, int r_r, int rr_pad, int col_router,
+                                const uint16_t* bt_s, const uint16_t* bt_r, int32_t* expert_out, float* y,
+                                hipStream_t st) {
     if (T <= 0) return hipSuccess;
     if (T > 16 || n_r > kMaxRouted || rs_pad > kMaxRank || rr_pad > kMaxRank) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(decode_finish_kernel, dim3((d_out + DF_CH - 1) / DF_CH), dim3(DF_THREADS), 0, st, part_m, ks_m, T,
-                       d_out, w_scale, part_p, ks_p, ncp, col_se, r_s, rs_pad, col_re, n_r, r_r, rr_pad, col_router,
+    hipLaunchKernelGGL(decode_finish_kernel, dim3((d_out + DF_CH - 1) / DF_CH), dim3(DF_THREADS), 0, st, part_m, s_x,
+                       ks_m, T, d_out, w_scale, part_p, ks_p, ncp, col_se, r_s, rs_pad, col_re, n_r, r_r, rr_pad, col_router,
                        bt_s, bt_r, expert_out, y);
     return hipGetLastError();
 }

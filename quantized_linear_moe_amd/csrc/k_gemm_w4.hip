@@ -45,16 +45,6 @@ constexpr int G_BK = 64;   // K per pipeline stage (one int8 MFMA K step)
 constexpr int G_NS = 4;    // stages in the LDS ring of 128-token tiles: loads run three stages ahead
 constexpr int G_NBW = 4;   // N blocks per wave
 
-__device__ inline v4i unpack_w4x16(uint32_t p0, uint32_t p1) {
-    // tiled byte b of p holds code b (low nibble) and code b+4 (high nibble)
-    v4i r;
-    r[0] = (int)((p0 << 4) & 0xF0F0F0F0u);
-    r[1] = (int)(p0 & 0xF0F0F0F0u);
-    r[2] = (int)((p1 << 4) & 0xF0F0F0F0u);
-    r[3] = (int)(p1 & 0xF0F0F0F0u);
-    return r;
-}
-
 // A tile rows are 64 bytes (four 16-byte chunks); chunk c of row r is stored at
 // c ^ ((r >> 1) & 3), which spreads the 16-byte reads of 8 consecutive rows over all banks.
 __device__ inline int a_swz(int row) { return (row >> 1) & 3; }

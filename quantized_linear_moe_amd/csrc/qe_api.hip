@@ -150,7 +150,7 @@ WsLayout ws_layout(const qe_linear* lin, int T) {
     const size_t t = T > 0 ? T : 0;
     W.xproj_ksplit = xproj_ksplit(T, lin->d_in, P.n_cols_pad);
     W.skinny_ksplit = lin->a_bits == 16 ? skinny_ksplit(lin->d_in, lin->d_out) : 0;
-    const bool fused_decode = lin->a_bits == 16 && T <= kSkinnyMaxT;
+    const bool fused_decode = T <= kSkinnyMaxT && (lin->a_bits == 16 || lin->w_bits == 4);
     const DecodePlan D = fused_decode ? decode_plan(lin->d_in, lin->d_out, lin->w_bits, P.n_cols_pad, T) : DecodePlan{};
     size_t off = 0;
     W.codes = off;
@@ -534,17 +534,28 @@ int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int3
     int32_t* expert = route ? (expert_out ? expert_out : at<int32_t>(ws, W.expert)) : nullptr;
     uint16_t* u = P.rs_pad > 0 ? at<uint16_t>(ws, W.u) : nullptr;
     uint16_t* v = route ? at<uint16_t>(ws, W.v) : nullptr;
-    if (lin->a_bits == 16 && T <= kSkinnyMaxT) {
-        // decode: one launch streams the projection matrix and the packed weights, one finishes
+    if (T <= kSkinnyMaxT && (lin->a_bits == 16 || lin->w_bits == 4)) {
+        // decode: one launch streams the projection matrix and the packed weights, one finishes;
+        // with quantized activations the codes are made first and the weights meet them on the
+        // int8 matrix cores
         int e = ensure_attributes();
         if (e) return e;
         const DecodePlan D = decode_plan(lin->d_in, lin->d_out, lin->w_bits, P.n_cols_pad, T);
         float* part_m = at<float>(ws, W.skinny);
         float* part_p = at<float>(ws, W.part);
-        QE_TRY_HIP(launch_decode_gemv(x, x_dtype, T, lin->d_in, lin->d_out, lin->w_bits,
+        int8_t* dcodes = nullptr;
+        float* ds_x = nullptr;
+        if (lin->a_bits != 16) {
+            dcodes = at<int8_t>(ws, W.codes);
+            ds_x = at<float>(ws, W.s_x);
+            QE_TRY_HIP(launch_quant_act(x, x_dtype, at<const float>(lin->prep, P.smooth),
+                                        at<const float>(lin->prep, P.inv_smooth), T, lin->d_in, lin->a_bits, dcodes,
+                                        ds_x, s));
+        }
+        QE_TRY_HIP(launch_decode_gemv(x, x_dtype, dcodes, T, lin->d_in, lin->d_out, lin->w_bits,
                                       at<const void>(lin->prep, P.w_tiled), D, part_m,
                                       at<const uint16_t>(lin->prep, P.mt), P.n_cols_pad, part_p, s));
-        QE_TRY_HIP(launch_decode_finish(part_m, D.ks_m, T, lin->d_out, at<const float>(lin->prep, P.w_scale), part_p,
+        QE_TRY_HIP(launch_decode_finish(part_m, ds_x, D.ks_m, T, lin->d_out, at<const float>(lin->prep, P.w_scale), part_p,
                                         D.ks_p, P.n_cols_pad, P.col_se, lin->r_shared, P.rs_pad, P.col_re,
                                         lin->n_routed, lin->r_routed, P.rr_pad, P.col_router,
                                         P.rs_pad > 0 ? at<const uint16_t>(lin->prep, P.bt_s) : nullptr,

@@ -30,6 +30,19 @@ __device__ inline uint32_t f32_to_bf16_bits(float f) {
 }
 __host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// 16 four-bit weight codes of one int8-MFMA fragment (8 bytes of the tiled layout, byte b holding
+// code b in the low nibble and code b+4 in the high one) as int8 values 16*code: each nibble moves
+// into the high half of its byte, so no sign extension is needed and an int32 accumulator holds
+// 16 * sum exactly (recovered by an arithmetic shift)
+__device__ inline v4i unpack_w4x16(uint32_t p0, uint32_t p1) {
+    v4i r;
+    r[0] = (int)((p0 << 4) & 0xF0F0F0F0u);
+    r[1] = (int)(p0 & 0xF0F0F0F0u);
+    r[2] = (int)((p1 << 4) & 0xF0F0F0F0u);
+    r[3] = (int)(p1 & 0xF0F0F0F0u);
+    return r;
+}
+
 // ---------------------------------------------------------- prepared-buffer map
 // All offsets are in bytes from the start of the prepared buffer.
 struct PrepLayout {
@@ -139,13 +152,14 @@ struct DecodePlan {
     size_t lds;          // dynamic LDS bytes
 };
 DecodePlan decode_plan(int d_in, int d_out, int w_bits, int ncp, int T);
-hipError_t launch_decode_gemv(const void* x, int x_dtype, int T, int d_in, int d_out, int w_bits, const void* w_tiled,
-                              const DecodePlan& P, float* part_m, const uint16_t* mt, int ncp, float* part_p,
-                              hipStream_t st);
-hipError_t launch_decode_finish(const float* part_m, int ks_m, int T, int d_out, const float* w_scale,
-                                const float* part_p, int ks_p, int ncp, int col_se, int r_s, int rs_pad, int col_re,
-                                int n_r, int r_r, int rr_pad, int col_router, const uint16_t* bt_s,
-                                const uint16_t* bt_r, int32_t* expert_out, float* y, hipStream_t st);
+hipError_t launch_decode_gemv(const void* x, int x_dtype, const int8_t* codes, int T, int d_in, int d_out, int w_bits,
+                              const void* w_tiled, const DecodePlan& P, float* part_m, const uint16_t* mt, int ncp,
+                              float* part_p, hipStream_t st);
+hipError_t launch_decode_finish(const float* part_m, const float* s_x, int ks_m, int T, int d_out,
+                                const float* w_scale, const float* part_p, int ks_p, int ncp, int col_se, int r_s,
+                                int rs_pad, int col_re, int n_r, int r_r, int rr_pad, int col_router,
+                                const uint16_t* bt_s, const uint16_t* bt_r, int32_t* expert_out, float* y,
+                                hipStream_t st);
 
 hipError_t launch_skinny_finish(const float* part, int ksplit, int T, int d_out, const float* w_scale,
                                 const uint16_t* u, const uint16_t* bt_s, int rs_pad, const uint16_t* v,

@@ -23,4 +23,18 @@ __device__ inline float sum_splits(const float* __restrict__ p, size_t stride, i
     return sum;
 }
 
+// The same for exact int32 partial sums (integer adds: any order gives the same result)
+__device__ inline int32_t sum_splits_i32(const int32_t* __restrict__ p, size_t stride, int n) {
+    constexpr int B = 16;
+    int32_t sum = 0;
+    for (int k = 0; k < n; k += B) {
+        int32_t a[B];
+#pragma unroll
+        for (int q = 0; q < B; ++q) a[q] = k + q < n ? p[(size_t)(k + q) * stride] : 0;
+#pragma unroll
+        for (int q = 0; q < B; ++q) sum += a[q];
+    }
+    return sum;
+}
+
 }  // namespace qe

@@ -95,3 +95,31 @@ def test_decode_quantized_activations(Q, lin_name, a_bits, T):
     ref = oracle_for(params, x, 4, a_bits)
     err = check_y(y.cpu().numpy(), ref, params, x, 4, a_bits, gpu_expert=expert.cpu().numpy())
     print(f"decode {lin_name} W4A{a_bits} T={T}: max rel err {err:.3e}")
+
+
+# decode with quantized activations runs the int8 weight-streaming path; without adapters its
+# output is the dequantized exact accumulator, bit for bit the main GEMM's
+@pytest.mark.parametrize("d_in,d_out,T,a_bits", [(8192, 29568, 8, 6), (29568, 8192, 3, 8), (1152, 4096, 16, 6),
+                                                 (4096, 1040, 1, 8), (3200, 400, 5, 6)])
+def test_decode_int8_main_term_bit_exact(Q, d_in, d_out, T, a_bits):
+    rng = np.random.default_rng(d_in + T)
+    params = dict(W_f=(rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32),
+                  s=rng.uniform(0.5, 2, d_in).astype(np.float32))
+    layer = Q.QELinear.from_params(params, 4, a_bits, device=DEV)
+    x = torch.from_numpy((rng.standard_normal((T, d_in)) * 2).astype(np.float32)).to(torch.bfloat16)
+    x[0, :7] = 40.0  # an outlier row segment
+    xd = x.to(DEV)
+    ws = layer.workspace(T)
+    y_dec = torch.empty(T, d_out, dtype=torch.float32, device=DEV)
+    layer.forward(xd, y_dec, None, ws)
+    codes = torch.empty(T, d_in, dtype=torch.int8, device=DEV)
+    s_x = torch.empty(T, dtype=torch.float32, device=DEV)
+    Q.libqe.qe_quant_act(xd, torch.from_numpy(params["s"]).to(DEV), a_bits, codes, s_x)
+    y_gemm = torch.empty_like(y_dec)
+    Q.libqe.qe_wq_gemm(layer.lin, codes, s_x, None, T, None, None, None, y_gemm, None, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(y_dec.cpu().numpy().view(np.uint32), y_gemm.cpu().numpy().view(np.uint32))
+    qx, sx = O.quant_act(x.float().numpy(), params["s"], a_bits)
+    qw, s_w = O.quant_weights(params["W_f"], params["s"], 4)
+    _, y_ref = O.main_term_int(qx, sx, qw, s_w)
+    assert rel_err(y_dec.cpu().numpy(), y_ref) <= 2e-3
