@@ -717,8 +717,12 @@ constexpr int EQ_W = 8;             // waves per workgroup
 constexpr int EQ_ROWS = 16 * EQ_W;  // token rows per workgroup
 constexpr int EQ_KG = 128;          // channels per group
 constexpr int EQ_TPL = 8;           // routes read per lane and batch while bucketing
+constexpr int EQ_FEW_T = 256;       // token counts that take the few-token form
 
-template <int NBR>
+// ESL > 0: the few-token form (a tile then holds most experts): ESL experts per pass, and each
+// group's fragments are requested one group ahead (more registers, fewer passes and no
+// exposed fragment load per group); ESL == 0: 1 or 2 experts per pass, as for many tokens.
+template <int NBR, int ESL>
 __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
     const uint16_t* __restrict__ x, int T, int d_in, const float* __restrict__ smooth,
     const float* __restrict__ inv_smooth, const float* __restrict__ s_x, int qmax, const int32_t* __restrict__ expert,
@@ -726,8 +730,11 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
     float* __restrict__ vpart, int8_t* __restrict__ codes, uint16_t* __restrict__ v) {
     constexpr int RR = NBR * 16;               // padded routed rank
     constexpr int NB1 = NBR ? NBR : 1;
-    constexpr int ESLOTS = NBR == 4 ? 1 : 2;   // experts per pass: 16 KB of fragments per group
-    constexpr int B_LDS = NBR ? 16384 : 0;
+    constexpr int ESLOTS = ESL > 0 ? ESL : NBR == 4 ? 1 : 2;  // experts per pass
+    constexpr bool kFew = ESL > 0;
+    constexpr int COPIES = NBR ? ESLOTS * NB1 * 4 / EQ_W : 0;  // 1-KB fragment copies per wave and group
+    static_assert(NBR == 0 || COPIES * EQ_W == ESLOTS * NB1 * 4, "fragment copies must split evenly over the waves");
+    constexpr int B_LDS = NBR ? ESLOTS * NB1 * 4 * 1024 : 0;
     constexpr int BUF = B_LDS + 1024;          // + smoothing factors and reciprocals (128 each)
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
     __shared__ uint32_t s_pres[EQ_W];
@@ -747,6 +754,9 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
         int cnt[kMaxRouted];
 #pragma unroll
         for (int e = 0; e < kMaxRouted; ++e) cnt[e] = 0;
+        // the wave's first batch of routes (clamped into range, -1 past the wave's tokens) stays
+        // in registers for the ranking below: with up to 512 tokens per wave it is all of them
+        int ev0[EQ_TPL];
         for (int b0 = tw0; b0 < tw1; b0 += 64 * EQ_TPL) {
             int ev[EQ_TPL];
 #pragma unroll
@@ -754,6 +764,10 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
                 ev[j] = expert[min(b0 + 64 * j + lane, T - 1)];
 #pragma unroll
             for (int j = 0; j < EQ_TPL; ++j) ev[j] = b0 + 64 * j + lane < tw1 ? min(max(ev[j], 0), n_r - 1) : -1;
+            if (b0 == tw0) {
+#pragma unroll
+                for (int j = 0; j < EQ_TPL; ++j) ev0[j] = ev[j];
+            }
 #pragma unroll
             for (int j = 0; j < EQ_TPL; ++j)
 #pragma unroll
@@ -779,12 +793,20 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
                 int rank = base;
                 for (int b0 = tw0; b0 < tw1 && rank < hi; b0 += 64 * EQ_TPL) {
                     int ev[EQ_TPL];
+                    if (b0 == tw0) {
 #pragma unroll
-                    for (int j = 0; j < EQ_TPL; ++j) ev[j] = expert[min(b0 + 64 * j + lane, T - 1)];
+                        for (int j = 0; j < EQ_TPL; ++j) ev[j] = ev0[j];
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < EQ_TPL; ++j) {
+                            const int tk = b0 + 64 * j + lane;
+                            ev[j] = tk < tw1 ? min(max(expert[min(tk, T - 1)], 0), n_r - 1) : -1;
+                        }
+                    }
 #pragma unroll
                     for (int j = 0; j < EQ_TPL; ++j) {
                         const int tk = b0 + 64 * j + lane;
-                        const bool f = tk < tw1 && min(max(ev[j], 0), n_r - 1) == e;
+                        const bool f = ev[j] == e;
                         const uint64_t bal = __ballot(f);
                         const int r = rank + __popcll(bal & lt);
                         if (f && r >= lo && r < hi) s_tok[off + r - pos0] = tk;
@@ -838,11 +860,11 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
                 pm &= pm - 1;
             }
         }
-        // fragment copies b = 2*wid + q: MFMA step b%4, column block (b/4)%NB1, slot b/(4*NB1)
-        const uint16_t* bsrc[2];
+        // fragment copies b = COPIES*wid + q: MFMA step b%4, column block (b/4)%NB1, slot b/(4*NB1)
+        const uint16_t* bsrc[COPIES > 0 ? COPIES : 1];
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int b = 2 * wid + q, bs = b & 3, bn = (b >> 2) % NB1, bj = b / (4 * NB1);
+        for (int q = 0; q < COPIES; ++q) {
+            const int b = COPIES * wid + q, bs = b & 3, bn = (b >> 2) % NB1, bj = b / (4 * NB1);
             int e = max(ex[0], 0);  // empty slots repeat a present expert (never used)
 #pragma unroll
             for (int j = 1; j < ESLOTS; ++j)
@@ -854,20 +876,25 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
         v4u xv[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) xv[s] = *reinterpret_cast<const v4u*>(xrow + (size_t)g_beg * EQ_KG + s * 8);
+        v4u bv[COPIES > 0 ? COPIES : 1];
+        if (NBR && kFew) {  // the first group's fragments; later groups' are requested a group ahead
+#pragma unroll
+            for (int q = 0; q < COPIES; ++q) bv[q] = *reinterpret_cast<const v4u*>(bsrc[q] + (size_t)g_beg * EQ_KG);
+        }
         for (int g = g_beg; g < g_end; ++g, ++gi) {
             uint8_t* buf = smem + (gi & 1) * BUF;
             const size_t k0 = (size_t)g * EQ_KG;
-            v4u bv[2];
-            if (NBR) {
+            if (NBR && !kFew) {
 #pragma unroll
-                for (int q = 0; q < 2; ++q) bv[q] = *reinterpret_cast<const v4u*>(bsrc[q] + k0);
+                for (int q = 0; q < COPIES; ++q) bv[q] = *reinterpret_cast<const v4u*>(bsrc[q] + k0);
             }
             v4f sv = v4f{0, 0, 0, 0};
             if (first && tid < 64)
                 sv = *reinterpret_cast<const v4f*>((tid < 32 ? smooth : inv_smooth) + k0 + (tid & 31) * 4);
             if (NBR) {
 #pragma unroll
-                for (int q = 0; q < 2; ++q) *reinterpret_cast<v4u*>(buf + (2 * wid + q) * 1024 + lane * 16) = bv[q];
+                for (int q = 0; q < COPIES; ++q)
+                    *reinterpret_cast<v4u*>(buf + (COPIES * wid + q) * 1024 + lane * 16) = bv[q];
             }
             if (first && tid < 64) *reinterpret_cast<v4f*>(buf + B_LDS + tid * 16) = sv;
             // the stores above are complete in every wave (the other buffer was last read
@@ -878,6 +905,10 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
             const size_t kn = (size_t)min(g + 1, g_end - 1) * EQ_KG;
 #pragma unroll
             for (int s = 0; s < 4; ++s) xn[s] = *reinterpret_cast<const v4u*>(xrow + kn + s * 8);
+            if (NBR && kFew) {
+#pragma unroll
+                for (int q = 0; q < COPIES; ++q) bv[q] = *reinterpret_cast<const v4u*>(bsrc[q] + kn);
+            }
             if (first) {
                 v2u cw[4];
 #pragma unroll
@@ -971,12 +1002,19 @@ hipError_t launch_expert_quant(const uint16_t* x, int T, int d_in, const float* 
     if (ksq > 1 && nbr && (!vpart || !perm)) return hipErrorInvalidValue;
     const dim3 grid((T + EQ_ROWS - 1) / EQ_ROWS, ksq);
     const int qmax = (1 << (a_bits - 1)) - 1;
-#define QE_EQ_LAUNCH(NB)                                                                                             \
-    hipLaunchKernelGGL((expert_quant_kernel<NB>), grid, dim3(64 * EQ_W), 0, st, x, T, d_in, smooth, inv_smooth, s_x, \
-                       qmax, expert, n_r, mt_re, r_r, ksq, perm, vpart, codes, v)
-    if (nbr == 0) QE_EQ_LAUNCH(0);
-    else if (nbr == 2) QE_EQ_LAUNCH(2);
-    else QE_EQ_LAUNCH(4);
+#define QE_EQ_LAUNCH(NB, ESLV)                                                                                      \
+    hipLaunchKernelGGL((expert_quant_kernel<NB, ESLV>), grid, dim3(64 * EQ_W), 0, st, x, T, d_in, smooth, inv_smooth, \
+                       s_x, qmax, expert, n_r, mt_re, r_r, ksq, perm, vpart, codes, v)
+    // few tokens: a 128-row tile holds most experts, so take them 8 (rank 32) or 4 (rank 64) at a time
+    const bool few = T <= EQ_FEW_T;
+    if (nbr == 0) QE_EQ_LAUNCH(0, 0);
+    else if (nbr == 2) {
+        if (few) QE_EQ_LAUNCH(2, 8);
+        else QE_EQ_LAUNCH(2, 0);
+    } else {
+        if (few) QE_EQ_LAUNCH(4, 4);
+        else QE_EQ_LAUNCH(4, 0);
+    }
 #undef QE_EQ_LAUNCH
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || ksq == 1 || !nbr) return err;
