@@ -721,13 +721,15 @@ constexpr int EQ_FEW_T = 256;       // token counts that take the few-token form
 
 // ESL > 0: the few-token form (a tile then holds most experts): ESL experts per pass, and each
 // group's fragments are requested one group ahead (more registers, fewer passes and no
-// exposed fragment load per group); ESL == 0: 1 or 2 experts per pass, as for many tokens.
+// exposed fragment load per group); ESL == 0: 1 or 2 experts per pass.  sort_rows == false
+// keeps the tokens in their order (no bucketing, no permutation written): for few tokens
+// whose main product is split over K, whose epilogue does not gain from grouped experts.
 template <int NBR, int ESL>
 __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
     const uint16_t* __restrict__ x, int T, int d_in, const float* __restrict__ smooth,
     const float* __restrict__ inv_smooth, const float* __restrict__ s_x, int qmax, const int32_t* __restrict__ expert,
     int n_r, const uint16_t* __restrict__ mt_re, int r_r, int ksq, int32_t* __restrict__ perm_out,
-    float* __restrict__ vpart, int8_t* __restrict__ codes, uint16_t* __restrict__ v) {
+    float* __restrict__ vpart, int8_t* __restrict__ codes, uint16_t* __restrict__ v, bool sort_rows) {
     constexpr int RR = NBR * 16;               // padded routed rank
     constexpr int NB1 = NBR ? NBR : 1;
     constexpr int ESLOTS = ESL > 0 ? ESL : NBR == 4 ? 1 : 2;  // experts per pass
@@ -748,7 +750,7 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
 
     // ---- the tokens of positions pos0 .. pos0 + EQ_ROWS - 1
     if (tid < EQ_ROWS) s_tok[tid] = pos0 + tid < T ? pos0 + tid : -1;
-    if (routed) {
+    if (routed && sort_rows) {
         const int tw0 = (int)((long)wid * T / EQ_W), tw1 = (int)((long)(wid + 1) * T / EQ_W);  // wave's tokens
         const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
         int cnt[kMaxRouted];
@@ -984,29 +986,37 @@ __global__ __launch_bounds__(256) void vpart_finish_kernel(const float* __restri
     v[(size_t)tt * rr_pad + c] = c < r_r ? (uint16_t)f32_to_bf16_bits(a) : (uint16_t)0;
 }
 
+// K splits: about 512 workgroups with at least two channel groups each; few tokens (one or two
+// row tiles) take one group per workgroup where at most 64 splits allow it, since each group
+// costs a memory latency that so few workgroups cannot hide
+bool expert_quant_few(int T) { return T <= EQ_FEW_T; }
+
 int expert_quant_ksplit(int T, int d_in) {
     const int tiles = (T + EQ_ROWS - 1) / EQ_ROWS;
-    const int ks = std::min((512 + tiles - 1) / tiles, std::max(1, d_in / (2 * EQ_KG)));
+    const int ks = T <= EQ_FEW_T ? std::min(d_in / EQ_KG, 64)
+                                 : std::min((512 + tiles - 1) / tiles, std::max(1, d_in / (2 * EQ_KG)));
     return std::max(ks, 1);
 }
 
 hipError_t launch_expert_quant(const uint16_t* x, int T, int d_in, const float* smooth, const float* inv_smooth,
                                const float* s_x, int a_bits, const int32_t* expert, int n_r, const uint16_t* mt_re,
                                int rr_pad, int r_r, int ksq, int32_t* perm, float* vpart, int8_t* codes, uint16_t* v,
-                               hipStream_t st) {
+                               bool keep_order, hipStream_t st) {
     if (T <= 0) return hipSuccess;
     const int nbr = (expert && v) ? rr_pad / 16 : 0;
     if ((nbr != 0 && nbr != 2 && nbr != 4) || d_in % EQ_KG || ksq < 1 || ksq > d_in / EQ_KG || n_r > kMaxRouted ||
         !smooth || !inv_smooth)
         return hipErrorInvalidValue;
-    if (ksq > 1 && nbr && (!vpart || !perm)) return hipErrorInvalidValue;
+    const bool few = expert_quant_few(T);
+    keep_order = keep_order && few;
+    if (ksq > 1 && nbr && (!vpart || (!perm && !keep_order))) return hipErrorInvalidValue;
     const dim3 grid((T + EQ_ROWS - 1) / EQ_ROWS, ksq);
     const int qmax = (1 << (a_bits - 1)) - 1;
 #define QE_EQ_LAUNCH(NB, ESLV)                                                                                      \
     hipLaunchKernelGGL((expert_quant_kernel<NB, ESLV>), grid, dim3(64 * EQ_W), 0, st, x, T, d_in, smooth, inv_smooth, \
-                       s_x, qmax, expert, n_r, mt_re, r_r, ksq, perm, vpart, codes, v)
-    // few tokens: a 128-row tile holds most experts, so take them 8 (rank 32) or 4 (rank 64) at a time
-    const bool few = T <= EQ_FEW_T;
+                       s_x, qmax, expert, n_r, mt_re, r_r, ksq, keep_order ? nullptr : perm, vpart, codes, v, \
+                       !keep_order)
+    // few tokens: the experts are taken 8 (rank 32) or 4 (rank 64) at a time
     if (nbr == 0) QE_EQ_LAUNCH(0, 0);
     else if (nbr == 2) {
         if (few) QE_EQ_LAUNCH(2, 8);
@@ -1020,7 +1030,7 @@ hipError_t launch_expert_quant(const uint16_t* x, int T, int d_in, const float* 
     if (err != hipSuccess || ksq == 1 || !nbr) return err;
     const size_t n = (size_t)T * rr_pad;
     hipLaunchKernelGGL(vpart_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, vpart, ksq, T, rr_pad,
-                       r_r, perm, v);
+                       r_r, keep_order ? nullptr : perm, v);
     return hipGetLastError();
 }
 

@@ -14,6 +14,8 @@
 
 namespace qe {
 hipError_t skinny_set_attributes();
+// token counts for which the expert-sorted quantization pass may keep token order
+bool expert_quant_few(int T);
 }  // namespace qe
 
 using namespace qe;
@@ -472,8 +474,11 @@ int qe_routed_lora(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t
 }
 
 // ------------------------------------------------------------------ composite
+// keep_order: few tokens may stay in token order in the two-pass prologue (perm is then not
+// written; the caller passes perm == NULL)
 static int run_prologue(const qe_linear* lin, const void* x, int x_dtype, int T, int8_t* codes, float* s_x,
-                        uint16_t* u, uint16_t* v, int32_t* expert, int32_t* perm, void* ws, hipStream_t s) {
+                        uint16_t* u, uint16_t* v, int32_t* expert, int32_t* perm, void* ws, hipStream_t s,
+                        bool keep_order = false) {
     const PrepLayout P = prep_layout(lin);
     const WsLayout W = ws_layout(lin, T);
     const bool route = lin->n_routed > 0;
@@ -491,7 +496,7 @@ static int run_prologue(const qe_linear* lin, const void* x, int x_dtype, int T,
                                        route ? expert : nullptr, lin->n_routed,
                                        route ? mt + (size_t)P.col_re * lin->d_in : nullptr, P.rr_pad, lin->r_routed,
                                        W.eq_ksplit, route ? (perm ? perm : at<int32_t>(ws, W.perm)) : nullptr,
-                                       at<float>(ws, W.vpart), codes, route ? v : nullptr, s));
+                                       at<float>(ws, W.vpart), codes, route ? v : nullptr, keep_order, s));
         return QE_OK;
     }
     int st = run_xpass(lin, x, x_dtype, T, u != nullptr, route, route, nullptr, nullptr, route ? expert : nullptr, u,
@@ -565,8 +570,12 @@ int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int3
     }
     int8_t* codes = lin->a_bits != 16 ? at<int8_t>(ws, W.codes) : nullptr;
     float* s_x = lin->a_bits != 16 ? at<float>(ws, W.s_x) : nullptr;
-    int32_t* perm = (route && lin->a_bits != 16) ? at<int32_t>(ws, W.perm) : nullptr;
-    st = run_prologue(lin, x, x_dtype, T, codes, s_x, u, v, expert, perm, ws, s);
+    // the GEMM visits the tokens grouped by expert, except for few tokens whose main product
+    // is split over K (its finish handles every token's expert alike): then the two-pass
+    // prologue keeps token order and skips the bucketing
+    const bool keep_order = two_pass_sized(lin, T) && x_dtype == QE_BF16 && expert_quant_few(T) && W.gemm_ksplit > 1;
+    int32_t* perm = (route && lin->a_bits != 16 && !keep_order) ? at<int32_t>(ws, W.perm) : nullptr;
+    st = run_prologue(lin, x, x_dtype, T, codes, s_x, u, v, expert, perm, ws, s, keep_order);
     if (st) return st;
     return run_gemm(lin, codes, s_x, x, x_dtype, T, u, v, expert, perm, y, nullptr, ws, s);
 }

@@ -114,7 +114,7 @@ hipError_t launch_route_finish(const float* part, const float* amax_part, int ks
 hipError_t launch_expert_quant(const uint16_t* x, int T, int d_in, const float* smooth, const float* inv_smooth,
                                const float* s_x, int a_bits, const int32_t* expert, int n_r, const uint16_t* mt_re,
                                int rr_pad, int r_r, int ksq, int32_t* perm, float* vpart, int8_t* codes, uint16_t* v,
-                               hipStream_t st);
+                               bool keep_order, hipStream_t st);
 int expert_quant_ksplit(int T, int d_in);
 
 hipError_t launch_bucket(const int32_t* expert, int T, int n_r, int32_t* counts, int32_t* offsets,
