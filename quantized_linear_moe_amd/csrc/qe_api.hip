@@ -16,6 +16,10 @@ namespace qe {
 hipError_t skinny_set_attributes();
 // token counts for which the expert-sorted quantization pass may keep token order
 bool expert_quant_few(int T);
+// weight-only (A16) main product for more than 16 tokens: float partials [ksplit][T][d_out]
+int gemm_a16_ksplit(int T, int d_in, int d_out, int w_bits);
+hipError_t launch_gemm_a16(const void* x, int x_dtype, int T, int d_in, int d_out, int w_bits, const void* w_tiled,
+                           int ksplit, float* part, hipStream_t st);
 }  // namespace qe
 
 using namespace qe;
@@ -151,7 +155,9 @@ WsLayout ws_layout(const qe_linear* lin, int T) {
     const PrepLayout P = prep_layout(lin);
     const size_t t = T > 0 ? T : 0;
     W.xproj_ksplit = xproj_ksplit(T, lin->d_in, P.n_cols_pad);
-    W.skinny_ksplit = lin->a_bits == 16 ? skinny_ksplit(lin->d_in, lin->d_out) : 0;
+    W.skinny_ksplit = lin->a_bits != 16 ? 0
+                      : T <= kSkinnyMaxT ? skinny_ksplit(lin->d_in, lin->d_out)
+                                         : gemm_a16_ksplit(T, lin->d_in, lin->d_out, lin->w_bits);
     const bool fused_decode = T <= kSkinnyMaxT && (lin->a_bits == 16 || lin->w_bits == 4);
     const DecodePlan D = fused_decode ? decode_plan(lin->d_in, lin->d_out, lin->w_bits, P.n_cols_pad, T) : DecodePlan{};
     size_t off = 0;
@@ -420,8 +426,12 @@ static int run_gemm(const qe_linear* lin, const int8_t* codes, const float* s_x,
         float* part = at<float>(ws, W.skinny);
         int st = ensure_attributes();
         if (st) return st;
-        QE_TRY_HIP(launch_skinny(x, x_dtype, T, lin->d_in, lin->d_out, lin->w_bits, at<const void>(lin->prep, P.w_tiled),
-                                 W.skinny_ksplit, part, lin->d_out, s));
+        if (T <= kSkinnyMaxT)  // weight streaming, the tokens as one MFMA block
+            QE_TRY_HIP(launch_skinny(x, x_dtype, T, lin->d_in, lin->d_out, lin->w_bits,
+                                     at<const void>(lin->prep, P.w_tiled), W.skinny_ksplit, part, lin->d_out, s));
+        else  // every weight fragment used for 64 or 128 tokens
+            QE_TRY_HIP(launch_gemm_a16(x, x_dtype, T, lin->d_in, lin->d_out, lin->w_bits,
+                                       at<const void>(lin->prep, P.w_tiled), W.skinny_ksplit, part, s));
         QE_TRY_HIP(launch_skinny_finish(part, W.skinny_ksplit, T, lin->d_out, w_scale, u, bt_s, P.rs_pad, v, expert,
                                         bt_r, P.rr_pad, y, s));
     } else {
