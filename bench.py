@@ -546,8 +546,56 @@ def decode_line(torch, synth, qe, libqe, dev, w_bits, a_bits, copy_gbs=None):
     return res
 
 
+def sweeps(torch, synth, qe, libqe, dev, reps=10):
+    """Variants the pages study: the number of routed experts N_r (Table 6: 2, 4, 8, 16) on the
+    Qwen2VL-72B q projection (8192 -> 8192, W4A6, T = 4096, the composite entry point), and the
+    top-k size k of the calibration statistic on the InternVL2-8B down input (T = 4096)."""
+    import dataclasses
+
+    def med_us(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts)) * 1e3
+
+    out = {"n_routed_qwen2vl72b_q_w4a6_T4096": [], "topk_k_internvl2_8b_down_T4096": []}
+    base = synth.get_config("qwen2vl_72b")
+    spec = next(l for l in base.linears if l.name == "q")
+    x = synth.gen_activations(base, spec.stream).to(dev)
+    for n_r in (2, 4, 8, 16):
+        cfg = dataclasses.replace(base, n_routed=n_r)
+        layer = qe.QELinear.from_params(synth.gen_linear(cfg, spec), cfg.w_bits, cfg.a_bits, device=dev)
+        ws = layer.workspace(base.T)
+        y = torch.empty(base.T, spec.d_out, dtype=torch.float32, device=dev)
+        t = med_us(lambda: libqe.qe_linear_forward(layer.lin, x, y, None, ws))
+        out["n_routed_qwen2vl72b_q_w4a6_T4096"].append({"n_routed": n_r, "us": round(t, 2),
+                                                        "tokens_per_s": round(base.T / t * 1e6, 1)})
+        del layer, ws, y
+    del x
+    cfg = synth.get_config("internvl2_8b")
+    spec = next(l for l in cfg.linears if l.name == "down")
+    x = synth.gen_activations(cfg, spec.stream).to(dev)
+    w = torch.rand(spec.d_in, dtype=torch.float32, device=dev) + 0.5
+    hist = torch.zeros(spec.d_in, dtype=torch.int32, device=dev)
+    for k in (4, 8, 16, 32, 64):
+        topk = torch.empty(cfg.T, k, dtype=torch.int32, device=dev)
+        t = med_us(lambda: libqe.qe_channel_topk(x, w, k, topk, hist))
+        out["topk_k_internvl2_8b_down_T4096"].append({"k": k, "us": round(t, 2)})
+    torch.cuda.empty_cache()
+    return out
+
+
 def extras(torch, synth, qe, libqe, dev, copy_gbs=None):
     out = {}
+    out["sweeps"] = sweeps(torch, synth, qe, libqe, dev)
     out["table8_qwen2vl7b_s128"] = table8(torch, synth, qe, libqe, dev)
     # ---- the other configurations: a small single linear (latency), a 2B layer, an 8B layer
     out["linear_tiny_w4a8_T64"] = layer_throughput(torch, synth, qe, libqe, dev, "tiny", steps=50)
