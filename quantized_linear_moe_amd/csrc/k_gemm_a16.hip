@@ -5,7 +5,8 @@
 //
 //   part[ks][t][i] = sum over the K blocks of split ks of bf16(x)[t][j] * q_w[i][j]
 //
-// then the decode path's finish kernel applies y = s_w * sum + the low-rank terms.  W3A16 is
+// then y = s_w * sum + the low-rank terms: in the epilogue of the many-token kernel (when K is
+// not split), else in the decode path's finish kernel.  W3A16 is
 // one of the pages' settings (thelatestinai.com listing, Tables 1-3 and Table 8).  Codes are
 // small integers, exact in bf16, so the product is exact up to float32 accumulation.
 //
@@ -16,9 +17,19 @@
 // fetches its weight fragments straight into registers one K block ahead (two register sets
 // in turn, so no copy forces a wait).  The K blocks may be split over gridDim.y when the tile
 // grid leaves CUs idle.
+//
+// Many tokens (>= 512): 128 tokens x 256 channels per workgroup (wave tile 128 x 64: each x
+// fragment read from LDS feeds four MFMAs, which keeps the LDS traffic at half its bandwidth
+// when the matrix cores run at full rate), and both the x tile and the
+// weight fragments go global -> LDS by DMA into a three-stage ring (two K blocks in flight,
+// explicit vmcnt waits, no staging registers); x rows are stored with their 16-byte chunks
+// XOR-swizzled by row against bank conflicts.  Its epilogue scales by s_w and adds u.B_s and,
+// for every routed expert present among the tile's tokens, (v masked to that expert's rows).B_e
+// with bf16 MFMAs, so y is written once and the adapter rows are read once per tile.
 
 #include <algorithm>
 
+#include "qe_dma.h"
 #include "qe_internal.h"
 #include "qe_wfrag.h"
 
@@ -141,7 +152,199 @@ __global__ __launch_bounds__(256, 2) void gemm_a16_kernel(const void* __restrict
     }
 }
 
+constexpr int GR_NS = 3;  // ring stages
+
+// Many-token form (see the file comment): tile 128 x 256, wave w owns channel blocks 4w .. 4w+3.
+template <int WB>
+__global__ __launch_bounds__(256, 1) void gemm_a16_ring_kernel(
+    const void* __restrict__ x, int T, int d_in, int d_out, const uint32_t* __restrict__ w_tiled, int n_tm,
+    float* __restrict__ part, const float* __restrict__ w_scale, const uint16_t* __restrict__ u,
+    const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v, const int32_t* __restrict__ expert,
+    const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, float* __restrict__ y) {
+    constexpr int MB = 8, BM = 128, NBW = 4;
+    constexpr int FW = Frag<WB>::kWords;
+    constexpr int X_BYTES = BM * 256;                     // x tile of one K block
+    constexpr int W_WAVE = NBW * FW * 256;                // one wave's fragments (FW dwords x 64 lanes per block)
+    constexpr int STAGE = X_BYTES + 4 * W_WAVE;
+    constexpr int X_DMA = BM * 16 / 256;                  // 16-byte x copies per thread and stage
+    constexpr int OPS = X_DMA + NBW * FW;                 // DMA instructions per thread and stage
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[GR_NS * STAGE];
+
+    const int tm = blockIdx.x % n_tm, tn = blockIdx.x / n_tm;
+    const int m0 = tm * BM;
+    const int NB = d_out >> 4, KB = d_in >> 7;
+    const int kb0 = (int)((long)blockIdx.y * KB / gridDim.y), kb1 = (int)((long)(blockIdx.y + 1) * KB / gridDim.y);
+    const int nk = kb1 - kb0;
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int nb0 = tn * 16 + NBW * wid;
+    const uint32_t lds0 = lds_addr(smem);
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+
+    // x copy p of this thread: chunk i = 256 p + tid is LDS slot (row i / 16, slot i % 16) and
+    // holds the row's logical chunk slot ^ (row & 15)
+    const uint16_t* xsrc[X_DMA];
+#pragma unroll
+    for (int p = 0; p < X_DMA; ++p) {
+        const int i = p * 256 + tid, row = i >> 4, slot = i & 15;
+        xsrc[p] = xb + (size_t)min(m0 + row, T - 1) * d_in + ((slot ^ (row & 15)) << 3);
+    }
+    // weight dword q of block j: LDS words [(wid*NBW + j)*FW + q][lane]
+    auto wsrc = [&](int j, int q, int kb) -> const uint32_t* {
+        const int nb = min(nb0 + j, NB - 1);  // blocks past d_out repeat a valid block (never stored)
+        if constexpr (WB == 3) {
+            return w_tiled + (((size_t)nb * KB + kb) * 64 + lane) * 3 + q;
+        } else {  // two 64-K steps of two dwords
+            return w_tiled + (((size_t)nb * 2 * KB + 2 * kb + (q >> 1)) * 64 + lane) * 2 + (q & 1);
+        }
+    };
+    auto issue = [&](int stage, int i) {  // K block kb0 + i into ring slot `stage`
+        const int kb = kb0 + i;
+        const uint32_t base = lds0 + stage * STAGE;
+#pragma unroll
+        for (int p = 0; p < X_DMA; ++p) dma16(xsrc[p] + (size_t)kb * 128, base + (p * 256 + wid * 64) * 16);
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int q = 0; q < FW; ++q)
+                dma4(wsrc(j, q, kb), base + X_BYTES + wid * W_WAVE + (j * FW + q) * 256);
+    };
+
+    v4f acc[MB][NBW];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) acc[m][j] = v4f{0, 0, 0, 0};
+
+#pragma unroll
+    for (int st = 0; st < GR_NS - 1; ++st) issue(st, min(st, nk - 1));
+    QE_WAIT_VMCNT_LDS((GR_NS - 2) * OPS);
+    QE_WG_BARRIER();
+
+    for (int i = 0; i < nk; ++i) {
+        // refill the slot consumed in the previous step (past the end: a harmless repeat)
+        issue((i + GR_NS - 1) % GR_NS, min(i + GR_NS - 1, nk - 1));
+        const uint8_t* st = smem + (i % GR_NS) * STAGE;
+        const uint32_t* wl = reinterpret_cast<const uint32_t*>(st + X_BYTES + wid * W_WAVE);
+        uint32_t f[NBW][FW];
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int q = 0; q < FW; ++q) f[j][q] = wl[(j * FW + q) * 64 + lane];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            v8bf b[NBW];
+#pragma unroll
+            for (int j = 0; j < NBW; ++j) b[j] = weight_frag<WB>(f[j], s);
+            const int c = x_step_offset<WB>(s, lg) >> 3;  // 16-byte chunk of the row
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                const int row = m * 16 + lr;
+                const v8bf a = *reinterpret_cast<const v8bf*>(st + row * 256 + ((c ^ (row & 15)) << 4));
+#pragma unroll
+                for (int j = 0; j < NBW; ++j)
+                    acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[m][j], 0, 0, 0);
+            }
+        }
+        // the slot read here is refilled in the next step: every LDS read must have completed, and
+        // the next block must have landed (the later one may still be in flight)
+        __builtin_amdgcn_sched_barrier(0);
+        QE_WAIT_VMCNT_LDS((GR_NS - 2) * OPS);
+        QE_WG_BARRIER();
+    }
+    QE_WAIT_VMCNT(0);
+
+    // lane holds rows 16m + 4lg + r, column 16 nb + lr of each block; the A operands of the
+    // adapter MFMAs are rows 16m + lr
+    if (y != nullptr) {  // K not split: the whole epilogue here
+        bool nb_ok[NBW];
+        int nbc[NBW];  // fragment sources; blocks past d_out repeat block 0 (never stored)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            nb_ok[j] = nb0 + j < NB;
+            nbc[j] = nb_ok[j] ? nb0 + j : 0;
+            const float sw = w_scale[nbc[j] * 16 + lr];
+#pragma unroll
+            for (int m = 0; m < MB; ++m) acc[m][j] *= sw;
+        }
+        auto arow = [&](int m) { return min(m0 + m * 16 + lr, T - 1); };
+        if (u != nullptr && bt_s != nullptr && rs_pad > 0) {
+            for (int k0 = 0; k0 < rs_pad; k0 += 32) {
+                v8bf bs[NBW];
+#pragma unroll
+                for (int j = 0; j < NBW; ++j)
+                    bs[j] = *reinterpret_cast<const v8bf*>(bt_s + (size_t)(nbc[j] * 16 + lr) * rs_pad + k0 + lg * 8);
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    const v8bf ua = *reinterpret_cast<const v8bf*>(u + (size_t)arow(m) * rs_pad + k0 + lg * 8);
+#pragma unroll
+                    for (int j = 0; j < NBW; ++j)
+                        acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, bs[j], acc[m][j], 0, 0, 0);
+                }
+            }
+        }
+        if (v != nullptr && expert != nullptr && bt_r != nullptr && rr_pad > 0 && n_r > 0) {
+            int ex[MB];
+            uint32_t present = 0;
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                ex[m] = m0 + m * 16 + lr < T ? min(max(expert[arow(m)], 0), n_r - 1) : -1;
+                for (int q = 0; q < n_r; ++q)
+                    if (__ballot(ex[m] == q)) present |= 1u << q;
+            }
+            while (present) {  // wave-uniform
+                const int e = __builtin_ctz(present);
+                present &= present - 1;
+                for (int k0 = 0; k0 < rr_pad; k0 += 32) {
+                    v8bf br[NBW];
+#pragma unroll
+                    for (int j = 0; j < NBW; ++j)
+                        br[j] = *reinterpret_cast<const v8bf*>(bt_r + ((size_t)e * d_out + nbc[j] * 16 + lr) * rr_pad +
+                                                               k0 + lg * 8);
+#pragma unroll
+                    for (int m = 0; m < MB; ++m) {
+                        if (__ballot(ex[m] == e) == 0) continue;  // no row of this block uses expert e
+                        const v8bf va = ex[m] == e
+                                            ? *reinterpret_cast<const v8bf*>(v + (size_t)arow(m) * rr_pad + k0 + lg * 8)
+                                            : v8bf{};
+#pragma unroll
+                        for (int j = 0; j < NBW; ++j)
+                            acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, br[j], acc[m][j], 0, 0, 0);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            if (!nb_ok[j]) continue;
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = m0 + m * 16 + lg * 4 + r;
+                    if (t < T) y[(size_t)t * d_out + (nb0 + j) * 16 + lr] = acc[m][j][r];
+                }
+        }
+        return;
+    }
+
+    float* out = part + (size_t)blockIdx.y * T * d_out;
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        const int nb = nb0 + j;
+        if (nb >= NB) continue;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = m0 + m * 16 + lg * 4 + r;
+                if (t < T) out[(size_t)t * d_out + nb * 16 + lr] = acc[m][j][r];
+            }
+    }
+}
+
 inline int a16_mb(int T) { return T >= 512 ? 8 : 4; }
+// channel blocks per workgroup: the ring kernel (many tokens, bf16 x) takes 16
+inline int a16_nbg(int T, int x_dtype) { return T >= 512 && x_dtype == QE_BF16 ? 16 : GA_NB; }
 
 }  // namespace
 
@@ -157,18 +360,30 @@ int gemm_a16_ksplit(int T, int d_in, int d_out, int w_bits) {
     return (int)std::max(ks, 1L);
 }
 
+// The whole A16 main product with its epilogue: y = s_w * (x . q_w^T) + u.B_s + v.B_{e_t}.
+// part: float [ksplit][T][d_out] scratch (unused when the many-token kernel finishes in place).
 hipError_t launch_gemm_a16(const void* x, int x_dtype, int T, int d_in, int d_out, int w_bits, const void* w_tiled,
-                           int ksplit, float* part, hipStream_t st) {
+                           int ksplit, float* part, const float* w_scale, const uint16_t* u, const uint16_t* bt_s,
+                           int rs_pad, const uint16_t* v, const int32_t* expert, const uint16_t* bt_r, int rr_pad,
+                           int n_r, float* y, hipStream_t st) {
     if (T <= 0) return hipSuccess;
     if ((w_bits != 3 && w_bits != 4) || d_in % 128 || d_out % 16 || ksplit < 1 || ksplit > d_in / 128)
         return hipErrorInvalidValue;
-    const int mb = a16_mb(T), BM = 16 * mb;
-    const int n_tm = (T + BM - 1) / BM, n_tn = (d_out / 16 + GA_NB - 1) / GA_NB;
+    const int mb = a16_mb(T), BM = 16 * mb, nbg = a16_nbg(T, x_dtype);
+    const int n_tm = (T + BM - 1) / BM, n_tn = (d_out / 16 + nbg - 1) / nbg;
     const uint32_t* w = reinterpret_cast<const uint32_t*>(w_tiled);
+    const bool ring = mb == 8 && x_dtype == QE_BF16;
+    const bool fused = ring && ksplit == 1;
 #define QE_A16_LAUNCH(WBV, MBV)                                                                                   \
     hipLaunchKernelGGL((gemm_a16_kernel<WBV, MBV>), dim3(n_tm * n_tn, ksplit), dim3(256), 0, st, x, x_dtype, T, \
                        d_in, d_out, w, n_tm, part)
-    if (w_bits == 3) {
+#define QE_RING_LAUNCH(WBV)                                                                                         \
+    hipLaunchKernelGGL(gemm_a16_ring_kernel<WBV>, dim3(n_tm * n_tn, ksplit), dim3(256), 0, st, x, T, d_in, d_out, w, \
+                       n_tm, part, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, fused ? y : nullptr)
+    if (ring) {  // many tokens: the DMA ring (bf16 rows copied as they are)
+        if (w_bits == 3) QE_RING_LAUNCH(3);
+        else QE_RING_LAUNCH(4);
+    } else if (w_bits == 3) {
         if (mb == 8) QE_A16_LAUNCH(3, 8);
         else QE_A16_LAUNCH(3, 4);
     } else {
@@ -176,7 +391,10 @@ hipError_t launch_gemm_a16(const void* x, int x_dtype, int T, int d_in, int d_ou
         else QE_A16_LAUNCH(4, 4);
     }
 #undef QE_A16_LAUNCH
-    return hipGetLastError();
+#undef QE_RING_LAUNCH
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || fused) return e;
+    return launch_skinny_finish(part, ksplit, T, d_out, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, y, st);
 }
 
 }  // namespace qe

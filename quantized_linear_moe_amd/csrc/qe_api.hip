@@ -16,10 +16,13 @@ namespace qe {
 hipError_t skinny_set_attributes();
 // token counts for which the expert-sorted quantization pass may keep token order
 bool expert_quant_few(int T);
-// weight-only (A16) main product for more than 16 tokens: float partials [ksplit][T][d_out]
+// weight-only (A16) main product for more than 16 tokens with its epilogue (part: float
+// [ksplit][T][d_out] scratch)
 int gemm_a16_ksplit(int T, int d_in, int d_out, int w_bits);
 hipError_t launch_gemm_a16(const void* x, int x_dtype, int T, int d_in, int d_out, int w_bits, const void* w_tiled,
-                           int ksplit, float* part, hipStream_t st);
+                           int ksplit, float* part, const float* w_scale, const uint16_t* u, const uint16_t* bt_s,
+                           int rs_pad, const uint16_t* v, const int32_t* expert, const uint16_t* bt_r, int rr_pad,
+                           int n_r, float* y, hipStream_t st);
 }  // namespace qe
 
 using namespace qe;
@@ -426,12 +429,15 @@ static int run_gemm(const qe_linear* lin, const int8_t* codes, const float* s_x,
         float* part = at<float>(ws, W.skinny);
         int st = ensure_attributes();
         if (st) return st;
-        if (T <= kSkinnyMaxT)  // weight streaming, the tokens as one MFMA block
-            QE_TRY_HIP(launch_skinny(x, x_dtype, T, lin->d_in, lin->d_out, lin->w_bits,
-                                     at<const void>(lin->prep, P.w_tiled), W.skinny_ksplit, part, lin->d_out, s));
-        else  // every weight fragment used for 64 or 128 tokens
+        if (T > kSkinnyMaxT) {  // every weight fragment used for 64 or 128 tokens
             QE_TRY_HIP(launch_gemm_a16(x, x_dtype, T, lin->d_in, lin->d_out, lin->w_bits,
-                                       at<const void>(lin->prep, P.w_tiled), W.skinny_ksplit, part, s));
+                                       at<const void>(lin->prep, P.w_tiled), W.skinny_ksplit, part, w_scale, u, bt_s,
+                                       P.rs_pad, v, expert, bt_r, P.rr_pad, lin->n_routed, y, s));
+            return QE_OK;
+        }
+        // weight streaming, the tokens as one MFMA block
+        QE_TRY_HIP(launch_skinny(x, x_dtype, T, lin->d_in, lin->d_out, lin->w_bits, at<const void>(lin->prep, P.w_tiled),
+                                 W.skinny_ksplit, part, lin->d_out, s));
         QE_TRY_HIP(launch_skinny_finish(part, W.skinny_ksplit, T, lin->d_out, w_scale, u, bt_s, P.rs_pad, v, expert,
                                         bt_r, P.rr_pad, y, s));
     } else {
