@@ -5,8 +5,8 @@
 //
 //   part[ks][t][i] = sum over the K blocks of split ks of bf16(x)[t][j] * q_w[i][j]
 //
-// then y = s_w * sum + the low-rank terms: in the epilogue of the many-token kernel (when K is
-// not split), else in the decode path's finish kernel.  W3A16 is
+// then y = s_w * sum + the low-rank terms: in the kernels' epilogue when K is not split, else
+// in the decode path's finish kernel.  W3A16 is
 // one of the pages' settings (thelatestinai.com listing, Tables 1-3 and Table 8).  Codes are
 // small integers, exact in bf16, so the product is exact up to float32 accumulation.
 //
@@ -52,10 +52,93 @@ __device__ inline v4u load_x8(const void* __restrict__ x, int x_dtype, size_t id
                cvt(b[2]) | (cvt(b[3]) << 16)};
 }
 
+// Epilogue of a tile whose K range is complete: y = s_w * acc + u.B_s + v.B_{e_t} (bf16 MFMAs
+// for the low-rank terms, one round per routed expert present among the tile's tokens).  Lane
+// holds rows m0 + 16m + 4lg + r, column 16 (nb0 + j) + lr of each block; the A operands of the
+// adapter MFMAs are rows m0 + 16m + lr.
+template <int MB, int NBW>
+__device__ __attribute__((always_inline)) inline void a16_epilogue(
+    v4f (&acc)[MB][NBW], int m0, int nb0, int T, int d_out, int lane, const float* __restrict__ w_scale,
+    const uint16_t* __restrict__ u, const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ expert, const uint16_t* __restrict__ bt_r, int rr_pad, int n_r,
+    float* __restrict__ y) {
+    const int NB = d_out >> 4, lr = lane & 15, lg = lane >> 4;
+    bool nb_ok[NBW];
+    int nbc[NBW];  // fragment sources; blocks past d_out repeat block 0 (never stored)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        nb_ok[j] = nb0 + j < NB;
+        nbc[j] = nb_ok[j] ? nb0 + j : 0;
+        const float sw = w_scale[nbc[j] * 16 + lr];
+#pragma unroll
+        for (int m = 0; m < MB; ++m) acc[m][j] *= sw;
+    }
+    auto arow = [&](int m) { return min(m0 + m * 16 + lr, T - 1); };
+    if (u != nullptr && bt_s != nullptr && rs_pad > 0) {
+        for (int k0 = 0; k0 < rs_pad; k0 += 32) {
+            v8bf bs[NBW];
+#pragma unroll
+            for (int j = 0; j < NBW; ++j)
+                bs[j] = *reinterpret_cast<const v8bf*>(bt_s + (size_t)(nbc[j] * 16 + lr) * rs_pad + k0 + lg * 8);
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                const v8bf ua = *reinterpret_cast<const v8bf*>(u + (size_t)arow(m) * rs_pad + k0 + lg * 8);
+#pragma unroll
+                for (int j = 0; j < NBW; ++j)
+                    acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, bs[j], acc[m][j], 0, 0, 0);
+            }
+        }
+    }
+    if (v != nullptr && expert != nullptr && bt_r != nullptr && rr_pad > 0 && n_r > 0) {
+        int ex[MB];
+        uint32_t present = 0;
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+            ex[m] = m0 + m * 16 + lr < T ? min(max(expert[arow(m)], 0), n_r - 1) : -1;
+            for (int q = 0; q < n_r; ++q)
+                if (__ballot(ex[m] == q)) present |= 1u << q;
+        }
+        while (present) {  // wave-uniform
+            const int e = __builtin_ctz(present);
+            present &= present - 1;
+            for (int k0 = 0; k0 < rr_pad; k0 += 32) {
+                v8bf br[NBW];
+#pragma unroll
+                for (int j = 0; j < NBW; ++j)
+                    br[j] = *reinterpret_cast<const v8bf*>(bt_r + ((size_t)e * d_out + nbc[j] * 16 + lr) * rr_pad +
+                                                           k0 + lg * 8);
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    if (__ballot(ex[m] == e) == 0) continue;  // no row of this block uses expert e
+                    const v8bf va = ex[m] == e
+                                        ? *reinterpret_cast<const v8bf*>(v + (size_t)arow(m) * rr_pad + k0 + lg * 8)
+                                        : v8bf{};
+#pragma unroll
+                    for (int j = 0; j < NBW; ++j)
+                        acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, br[j], acc[m][j], 0, 0, 0);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        if (!nb_ok[j]) continue;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = m0 + m * 16 + lg * 4 + r;
+                if (t < T) y[(size_t)t * d_out + (nb0 + j) * 16 + lr] = acc[m][j][r];
+            }
+    }
+}
+
 template <int WB, int MB>
-__global__ __launch_bounds__(256, 2) void gemm_a16_kernel(const void* __restrict__ x, int x_dtype, int T, int d_in,
-                                                          int d_out, const uint32_t* __restrict__ w_tiled, int n_tm,
-                                                          float* __restrict__ part) {
+__global__ __launch_bounds__(256, 2) void gemm_a16_kernel(
+    const void* __restrict__ x, int x_dtype, int T, int d_in, int d_out, const uint32_t* __restrict__ w_tiled, int n_tm,
+    float* __restrict__ part, const float* __restrict__ w_scale, const uint16_t* __restrict__ u,
+    const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v, const int32_t* __restrict__ expert,
+    const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, float* __restrict__ y) {
     constexpr int BM = 16 * MB;
     constexpr int FW = Frag<WB>::kWords;
     constexpr int XCH = BM * 16 / 256;  // 16-byte chunks of the x tile per thread and K block
@@ -136,6 +219,10 @@ __global__ __launch_bounds__(256, 2) void gemm_a16_kernel(const void* __restrict
         __syncthreads();
     }
 
+    if (y != nullptr) {  // K not split: the whole epilogue here
+        a16_epilogue<MB, 2>(acc, m0, nb0, T, d_out, lane, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y);
+        return;
+    }
     // lane holds rows 16m + 4lg + r, column lr of each block
     float* out = part + (size_t)blockIdx.y * T * d_out;
 #pragma unroll
@@ -256,74 +343,7 @@ __global__ __launch_bounds__(256, 1) void gemm_a16_ring_kernel(
     // lane holds rows 16m + 4lg + r, column 16 nb + lr of each block; the A operands of the
     // adapter MFMAs are rows 16m + lr
     if (y != nullptr) {  // K not split: the whole epilogue here
-        bool nb_ok[NBW];
-        int nbc[NBW];  // fragment sources; blocks past d_out repeat block 0 (never stored)
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-            nb_ok[j] = nb0 + j < NB;
-            nbc[j] = nb_ok[j] ? nb0 + j : 0;
-            const float sw = w_scale[nbc[j] * 16 + lr];
-#pragma unroll
-            for (int m = 0; m < MB; ++m) acc[m][j] *= sw;
-        }
-        auto arow = [&](int m) { return min(m0 + m * 16 + lr, T - 1); };
-        if (u != nullptr && bt_s != nullptr && rs_pad > 0) {
-            for (int k0 = 0; k0 < rs_pad; k0 += 32) {
-                v8bf bs[NBW];
-#pragma unroll
-                for (int j = 0; j < NBW; ++j)
-                    bs[j] = *reinterpret_cast<const v8bf*>(bt_s + (size_t)(nbc[j] * 16 + lr) * rs_pad + k0 + lg * 8);
-#pragma unroll
-                for (int m = 0; m < MB; ++m) {
-                    const v8bf ua = *reinterpret_cast<const v8bf*>(u + (size_t)arow(m) * rs_pad + k0 + lg * 8);
-#pragma unroll
-                    for (int j = 0; j < NBW; ++j)
-                        acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, bs[j], acc[m][j], 0, 0, 0);
-                }
-            }
-        }
-        if (v != nullptr && expert != nullptr && bt_r != nullptr && rr_pad > 0 && n_r > 0) {
-            int ex[MB];
-            uint32_t present = 0;
-#pragma unroll
-            for (int m = 0; m < MB; ++m) {
-                ex[m] = m0 + m * 16 + lr < T ? min(max(expert[arow(m)], 0), n_r - 1) : -1;
-                for (int q = 0; q < n_r; ++q)
-                    if (__ballot(ex[m] == q)) present |= 1u << q;
-            }
-            while (present) {  // wave-uniform
-                const int e = __builtin_ctz(present);
-                present &= present - 1;
-                for (int k0 = 0; k0 < rr_pad; k0 += 32) {
-                    v8bf br[NBW];
-#pragma unroll
-                    for (int j = 0; j < NBW; ++j)
-                        br[j] = *reinterpret_cast<const v8bf*>(bt_r + ((size_t)e * d_out + nbc[j] * 16 + lr) * rr_pad +
-                                                               k0 + lg * 8);
-#pragma unroll
-                    for (int m = 0; m < MB; ++m) {
-                        if (__ballot(ex[m] == e) == 0) continue;  // no row of this block uses expert e
-                        const v8bf va = ex[m] == e
-                                            ? *reinterpret_cast<const v8bf*>(v + (size_t)arow(m) * rr_pad + k0 + lg * 8)
-                                            : v8bf{};
-#pragma unroll
-                        for (int j = 0; j < NBW; ++j)
-                            acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, br[j], acc[m][j], 0, 0, 0);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < NBW; ++j) {
-            if (!nb_ok[j]) continue;
-#pragma unroll
-            for (int m = 0; m < MB; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int t = m0 + m * 16 + lg * 4 + r;
-                    if (t < T) y[(size_t)t * d_out + (nb0 + j) * 16 + lr] = acc[m][j][r];
-                }
-        }
+        a16_epilogue<MB, NBW>(acc, m0, nb0, T, d_out, lane, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y);
         return;
     }
 
@@ -373,10 +393,11 @@ hipError_t launch_gemm_a16(const void* x, int x_dtype, int T, int d_in, int d_ou
     const int n_tm = (T + BM - 1) / BM, n_tn = (d_out / 16 + nbg - 1) / nbg;
     const uint32_t* w = reinterpret_cast<const uint32_t*>(w_tiled);
     const bool ring = mb == 8 && x_dtype == QE_BF16;
-    const bool fused = ring && ksplit == 1;
-#define QE_A16_LAUNCH(WBV, MBV)                                                                                   \
-    hipLaunchKernelGGL((gemm_a16_kernel<WBV, MBV>), dim3(n_tm * n_tn, ksplit), dim3(256), 0, st, x, x_dtype, T, \
-                       d_in, d_out, w, n_tm, part)
+    const bool fused = ksplit == 1;
+#define QE_A16_LAUNCH(WBV, MBV)                                                                                      \
+    hipLaunchKernelGGL((gemm_a16_kernel<WBV, MBV>), dim3(n_tm * n_tn, ksplit), dim3(256), 0, st, x, x_dtype, T,    \
+                       d_in, d_out, w, n_tm, part, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r,        \
+                       fused ? y : nullptr)
 #define QE_RING_LAUNCH(WBV)                                                                                         \
     hipLaunchKernelGGL(gemm_a16_ring_kernel<WBV>, dim3(n_tm * n_tn, ksplit), dim3(256), 0, st, x, T, d_in, d_out, w, \
                        n_tm, part, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, fused ? y : nullptr)

@@ -93,11 +93,13 @@ inline P* at(const void* base, size_t off) {
 }
 
 // K splits of the x-projection: about two workgroups per CU, each with at least 512 K
+// K splits of the x-projection: about 512 workgroups with at least 512 channels each; a grid of
+// a few tiles instead takes one 128-channel chunk per workgroup (at most 64 splits), since each
+// of a workgroup's K steps waits for its projection rows and so few workgroups cannot hide it
 int xproj_ksplit(int T, int d_in, int ncols_pad) {
     if (T <= 0 || ncols_pad <= 0) return 1;
     const int tiles = (T + 127) / 128 * ((ncols_pad + 319) / 320);
-    int ks = (512 + tiles - 1) / tiles;
-    ks = std::min(ks, std::max(1, d_in / 512));
+    int ks = tiles <= 4 ? std::min(d_in / 128, 64) : std::min((512 + tiles - 1) / tiles, std::max(1, d_in / 512));
     return std::max(ks, 1);
 }
 
