@@ -593,8 +593,43 @@ def sweeps(torch, synth, qe, libqe, dev, reps=10):
     return out
 
 
+def prefill_w3a16(torch, synth, qe, libqe, dev, reps=5):
+    """Weight-only prefill: the Qwen2VL-72B MLP up and down projections at W3A16 over the 4096
+    prefill tokens (the pages' weight-only setting), composite entry point, inputs resident."""
+    import dataclasses
+    base = synth.get_config("qwen2vl_72b")
+    cfg = dataclasses.replace(synth.get_config("qwen2vl_72b_decode"), T=base.T)
+    rows, total = [], 0.0
+    for spec in cfg.linears:
+        x = synth.gen_activations(base, spec.stream).to(dev)
+        layer = qe.QELinear.from_params(synth.gen_linear(cfg, spec), 3, 16, device=dev)
+        ws = layer.workspace(base.T)
+        y = torch.empty(base.T, spec.d_out, dtype=torch.float32, device=dev)
+        for _ in range(2):
+            libqe.qe_linear_forward(layer.lin, x, y, None, ws)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            libqe.qe_linear_forward(layer.lin, x, y, None, ws)
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        t = float(np.median(ts)) * 1e-3
+        flops = 2.0 * base.T * spec.d_in * spec.d_out
+        rows.append({"linear": f"{spec.name} {spec.d_in}->{spec.d_out}", "us": round(t * 1e6, 1),
+                     "bf16_tflops": round(flops / t / 1e12, 1),
+                     "frac_of_bf16_peak": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)})
+        total += t
+        del layer, ws, y, x
+        torch.cuda.empty_cache()
+    return {"T": base.T, "rows": rows, "tokens_per_s_up_down": round(base.T / total, 1)}
+
+
 def extras(torch, synth, qe, libqe, dev, copy_gbs=None):
     out = {}
+    out["prefill_qwen2vl72b_up_down_w3a16_T4096"] = prefill_w3a16(torch, synth, qe, libqe, dev)
     out["sweeps"] = sweeps(torch, synth, qe, libqe, dev)
     out["table8_qwen2vl7b_s128"] = table8(torch, synth, qe, libqe, dev)
     # ---- the other configurations: a small single linear (latency), a 2B layer, an 8B layer
