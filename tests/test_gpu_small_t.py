@@ -127,28 +127,37 @@ def test_decode_int8_main_term_bit_exact(Q, d_in, d_out, T, a_bits):
 
 # weight-only (A16) linears with more than 16 tokens: the bf16-MFMA GEMM that uses every weight
 # fragment for 64 or 128 tokens (ragged token tails, K splits, float32 activations)
-@pytest.mark.parametrize("w_bits,d_in,d_out,T,dtype", [
-    (3, 3584, 3584, 128, torch.bfloat16), (3, 18944, 3584, 128, torch.bfloat16), (3, 3584, 18944, 128, torch.bfloat16),
-    (4, 1152, 4096, 600, torch.bfloat16), (3, 4096, 1040, 17, torch.float32), (3, 8192, 272, 300, torch.bfloat16),
-    (4, 256, 272, 1000, torch.float32)])
-def test_a16_gemm_forward(Q, w_bits, d_in, d_out, T, dtype):
+A16_CASES = [(3, 3584, 3584, 128, torch.bfloat16), (3, 18944, 3584, 128, torch.bfloat16),
+             (3, 3584, 18944, 128, torch.bfloat16), (4, 1152, 4096, 600, torch.bfloat16),
+             (3, 4096, 1040, 17, torch.float32), (3, 8192, 272, 300, torch.bfloat16), (4, 256, 272, 1000, torch.float32)]
+A16_CASES = [c + (32, 8, 32) for c in A16_CASES] + [
+    (3, 4096, 1040, 700, torch.bfloat16, 64, 16, 64), (4, 2048, 528, 513, torch.bfloat16, 0, 3, 16),
+    (3, 1024, 256, 2048, torch.bfloat16, 8, 0, 0)]
+
+
+@pytest.mark.parametrize("w_bits,d_in,d_out,T,dtype,r_s,n_r,r_r", A16_CASES)
+def test_a16_gemm_forward(Q, w_bits, d_in, d_out, T, dtype, r_s, n_r, r_r):
+    # last cases: a ragged 256-channel tile with rank-64 adapters and 16 experts, routed experts
+    # only, and a shared expert only
     rng = np.random.default_rng(d_in * 7 + T)
     bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
-    r_s, n_r, r_r = 32, 8, 32
     params = dict(W_f=(rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32), s=None,
-                  A_s=bf(rng.standard_normal((d_in, r_s)) * 0.02), B_s=bf(rng.standard_normal((r_s, d_out)) * 0.02),
-                  A_r=bf(rng.standard_normal((n_r, d_in, r_r)) * 0.02),
-                  B_r=bf(rng.standard_normal((n_r, r_r, d_out)) * 0.02), R=bf(rng.standard_normal((d_in, n_r)) * 0.02))
+                  A_s=bf(rng.standard_normal((d_in, r_s)) * 0.02) if r_s else None,
+                  B_s=bf(rng.standard_normal((r_s, d_out)) * 0.02) if r_s else None,
+                  A_r=bf(rng.standard_normal((n_r, d_in, r_r)) * 0.02) if n_r else None,
+                  B_r=bf(rng.standard_normal((n_r, r_r, d_out)) * 0.02) if n_r else None,
+                  R=bf(rng.standard_normal((d_in, n_r)) * 0.02) if n_r else None)
     layer = Q.QELinear.from_params(params, w_bits, 16, device=DEV)
     x = torch.from_numpy((rng.standard_normal((T, d_in)) * 2).astype(np.float32)).to(dtype)
     y = torch.empty(T, d_out, dtype=torch.float32, device=DEV)
-    expert = torch.empty(T, dtype=torch.int32, device=DEV)
+    expert = torch.empty(T, dtype=torch.int32, device=DEV) if n_r else None
     layer.forward(x.to(DEV), y, expert)
     torch.cuda.synchronize()
     tokens = np.arange(T) if T <= 300 else np.unique(np.concatenate([[0, T - 1], rng.choice(T, 128, replace=False)]))
     x_sub = x[torch.as_tensor(tokens)]
     ref = oracle_for(params, x, w_bits, 16, tokens=tokens)
-    err = check_y(y.cpu().numpy()[tokens], ref, params, x_sub, w_bits, 16, gpu_expert=expert.cpu().numpy()[tokens])
+    err = check_y(y.cpu().numpy()[tokens], ref, params, x_sub, w_bits, 16,
+                  gpu_expert=expert.cpu().numpy()[tokens] if n_r else None)
     print(f"A16 W{w_bits} {d_in}x{d_out} T={T}: max rel err {err:.3e}")
 
 
