@@ -338,7 +338,7 @@ def main():
     result["roofline"]["frac_measured"] = round(achieved / peaks["int8_mfma_tops"], 4)
 
     if not args.no_extras:
-        result["extras"] = extras(torch, synth, qe, libqe, dev, peaks["copy_gbs"])
+        result["extras"] = extras(torch, synth, qe, libqe, dev, peaks)
 
     if want_cpu:
         result["cpu_baseline"] = cpu_baseline(torch, cfg, xs_cpu, oracle_w, args.cpu_sample_tokens)
@@ -350,8 +350,8 @@ def measured_peaks(torch, libqe, dev):
     """Rates this device sustains, from the library's probe kernels timed with events on the
     stream they run on: an int8 MFMA loop (the main GEMM's instruction, 2048 workgroups, about
     25 ms) on small constant operands, the highest rate the power-limited matrix cores sustain,
-    and on operands in the main GEMM's value ranges; and a 1 GiB streaming copy.  Median of
-    five runs each."""
+    and on operands in the main GEMM's value ranges; the same for the bf16 MFMA (the weight-only
+    GEMM's instruction); and a 1 GiB streaming copy.  Median of five runs each."""
     def median_ms(fn, reps=5):
         fn()
         ts = []
@@ -371,6 +371,12 @@ def measured_peaks(torch, libqe, dev):
         ops = libqe.qe_probe_mfma_i8(sink, blocks, iters, operands)
         t = median_ms(lambda: libqe.qe_probe_mfma_i8(sink, blocks, iters, operands))
         rates.append(ops / (t * 1e-3) / 1e12)
+    sink_f = torch.empty(blocks * 256 * 4, dtype=torch.float32, device=dev)
+    for operands in (0, 1):
+        flops = libqe.qe_probe_mfma_bf16(sink_f, blocks, iters, operands)
+        t = median_ms(lambda: libqe.qe_probe_mfma_bf16(sink_f, blocks, iters, operands))
+        rates.append(flops / (t * 1e-3) / 1e12)
+    del sink_f
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -379,9 +385,12 @@ def measured_peaks(torch, libqe, dev):
     torch.cuda.empty_cache()
     return {"int8_mfma_tops": round(rates[0], 1),
             "int8_mfma_tops_gemm_operands": round(rates[1], 1),
+            "bf16_mfma_tflops": round(rates[2], 1),
+            "bf16_mfma_tflops_gemm_operands": round(rates[3], 1),
             "copy_gbs": round(2 * nbytes / (t_copy * 1e-3) / 1e9, 1),
             "method": "qe_probe_mfma_i8 (2048 workgroups x 4 waves x 240000 MFMA 16x16x64 i8; small "
-                      "constant operands, then operands in the A6 x W4 code ranges) and qe_probe_copy "
+                      "constant operands, then operands in the A6 x W4 code ranges), qe_probe_mfma_bf16 (the same "
+                      "on MFMA 16x16x32 bf16; operands in the A16 x W3 ranges) and qe_probe_copy "
                       "(1 GiB read + 1 GiB write), median of 5"}
 
 
@@ -593,9 +602,11 @@ def sweeps(torch, synth, qe, libqe, dev, reps=10):
     return out
 
 
-def prefill_w3a16(torch, synth, qe, libqe, dev, reps=5):
+def prefill_w3a16(torch, synth, qe, libqe, dev, bf16_measured, reps=5):
     """Weight-only prefill: the Qwen2VL-72B MLP up and down projections at W3A16 over the 4096
-    prefill tokens (the pages' weight-only setting), composite entry point, inputs resident."""
+    prefill tokens (the pages' weight-only setting), composite entry point, inputs resident;
+    rates against the bf16 spec peak and the rate the bf16 MFMA probe sustains on operands in
+    this GEMM's ranges."""
     import dataclasses
     base = synth.get_config("qwen2vl_72b")
     cfg = dataclasses.replace(synth.get_config("qwen2vl_72b_decode"), T=base.T)
@@ -620,16 +631,19 @@ def prefill_w3a16(torch, synth, qe, libqe, dev, reps=5):
         flops = 2.0 * base.T * spec.d_in * spec.d_out
         rows.append({"linear": f"{spec.name} {spec.d_in}->{spec.d_out}", "us": round(t * 1e6, 1),
                      "bf16_tflops": round(flops / t / 1e12, 1),
-                     "frac_of_bf16_peak": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)})
+                     "frac_of_bf16_peak": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "frac_of_bf16_measured": round(flops / t / 1e12 / bf16_measured, 4)})
         total += t
         del layer, ws, y, x
         torch.cuda.empty_cache()
     return {"T": base.T, "rows": rows, "tokens_per_s_up_down": round(base.T / total, 1)}
 
 
-def extras(torch, synth, qe, libqe, dev, copy_gbs=None):
+def extras(torch, synth, qe, libqe, dev, peaks):
     out = {}
-    out["prefill_qwen2vl72b_up_down_w3a16_T4096"] = prefill_w3a16(torch, synth, qe, libqe, dev)
+    copy_gbs = peaks["copy_gbs"]
+    out["prefill_qwen2vl72b_up_down_w3a16_T4096"] = prefill_w3a16(torch, synth, qe, libqe, dev,
+                                                                   peaks["bf16_mfma_tflops_gemm_operands"])
     out["sweeps"] = sweeps(torch, synth, qe, libqe, dev)
     out["table8_qwen2vl7b_s128"] = table8(torch, synth, qe, libqe, dev)
     # ---- the other configurations: a small single linear (latency), a 2B layer, an 8B layer

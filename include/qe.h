@@ -323,12 +323,18 @@ int qe_linear_cost(const qe_linear* lin, int32_t T, int32_t n_distinct_experts, 
  *   GEMM's ranges (A6 codes in [-31, 31] times 4-bit codes scaled by 16).  *ops receives
  *   the integer operations enqueued (2 * 16 * 16 * 64 per MFMA).  out: device int32
  *   [blocks * 256 * 4], a result sink the caller owns.  iters >= 1.
+ * qe_probe_mfma_bf16: the same loop on bf16 16x16x32 MFMAs (the weight-only GEMM's
+ *   instruction) with float32 accumulators: operands = 0 small constants, operands = 1
+ *   random values in that GEMM's ranges (activations of unit scale, 3-bit codes times a
+ *   scale near 2^-7).  *flops receives 2 * 16 * 16 * 32 per MFMA.  out: device float32
+ *   [blocks * 256 * 4], a result sink the caller owns.
  * qe_probe_copy: copies `bytes` (a multiple of 16) from src to dst; both device pointers,
  *   16-byte aligned, caller-owned, not overlapping.  The traffic is 2 * bytes.
  * Both only enqueue work (no synchronization); invalid arguments return
  * QE_ERR_INVALID_ARG / QE_ERR_ALIGNMENT and launch nothing.
  */
 int qe_probe_mfma_i8(int32_t* out, int32_t blocks, int32_t iters, int32_t operands, double* ops, void* stream);
+int qe_probe_mfma_bf16(float* out, int32_t blocks, int32_t iters, int32_t operands, double* flops, void* stream);
 int qe_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 
 #ifdef __cplusplus

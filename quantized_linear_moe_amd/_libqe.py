@@ -74,6 +74,7 @@ def _load():
         "qe_cluster_channels": (ctypes.c_int, [P, I, ctypes.c_int64, I, ctypes.c_double, P, P, P, P]),
         "qe_linear_cost": (ctypes.c_int, [LP, I, I, I, D, D, D]),
         "qe_probe_mfma_i8": (ctypes.c_int, [P, I, I, I, D, P]),
+        "qe_probe_mfma_bf16": (ctypes.c_int, [P, I, I, I, D, P]),
         "qe_probe_copy": (ctypes.c_int, [P, P, Z, P]),
     }
     for name, (res, args) in sig.items():
@@ -88,7 +89,7 @@ EXPORTED = (
     "qe_status_string", "qe_last_hip_error", "qe_version", "qe_pack_weights", "qe_prepared_bytes", "qe_prepare",
     "qe_workspace_bytes", "qe_quant_act", "qe_route", "qe_adapter_inputs", "qe_wq_gemm", "qe_routed_lora",
     "qe_linear_prologue", "qe_linear_forward", "qe_colmean_abs", "qe_channel_topk", "qe_linear_cost",
-    "qe_probe_mfma_i8", "qe_probe_copy", "qe_partition_channels", "qe_cooccur_workspace_bytes",
+    "qe_probe_mfma_i8", "qe_probe_mfma_bf16", "qe_probe_copy", "qe_partition_channels", "qe_cooccur_workspace_bytes",
     "qe_cooccur", "qe_cluster_channels",
 )
 
@@ -267,6 +268,14 @@ def qe_probe_mfma_i8(out, blocks, iters, operands=0, stream=None):
     _check(_lib.qe_probe_mfma_i8(_ptr(out), blocks, iters, operands, ctypes.byref(ops), _stream(stream)),
            "qe_probe_mfma_i8")
     return ops.value
+
+
+def qe_probe_mfma_bf16(out, blocks, iters, operands=0, stream=None):
+    """Enqueue the bf16 MFMA throughput probe; returns the floating-point operations enqueued."""
+    flops = ctypes.c_double()
+    _check(_lib.qe_probe_mfma_bf16(_ptr(out), blocks, iters, operands, ctypes.byref(flops), _stream(stream)),
+           "qe_probe_mfma_bf16")
+    return flops.value
 
 
 def qe_probe_copy(src, dst, nbytes, stream=None):

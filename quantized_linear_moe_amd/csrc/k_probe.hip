@@ -4,6 +4,8 @@
 //
 //   probe_mfma_i8_kernel : int8 matrix-core throughput (v_mfma_i32_16x16x64_i8, the main
 //                          GEMM's instruction), a loop on register operands
+//   probe_mfma_bf16_kernel: bf16 matrix-core throughput (v_mfma_f32_16x16x32_bf16, the
+//                          weight-only GEMM's instruction), the same loop
 //   probe_copy_kernel    : streaming HBM copy (16-byte loads and stores)
 
 #include "qe_internal.h"
@@ -11,6 +13,8 @@
 namespace qe {
 
 typedef int32_t v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int PM_ACC = 8;  // independent accumulators per wave: cover the MFMA latency
 
@@ -57,6 +61,42 @@ __global__ __launch_bounds__(256) void probe_mfma_i8_kernel(int32_t* __restrict_
     *reinterpret_cast<v4i*>(out + (size_t)lane_id * 4) = sum;
 }
 
+// The bf16 counterpart: operands 0 holds small constants (1, 2, 3, 4 as bf16), operands 1
+// random values in the weight-only GEMM's ranges: activations of about unit scale with a
+// random sign and exponent, and weights that are 3-bit codes times a scale near 2^-7.
+__global__ __launch_bounds__(256) void probe_mfma_bf16_kernel(float* __restrict__ out, int iters, int operands) {
+    const uint32_t lane_id = blockIdx.x * 256u + threadIdx.x;
+    uint32_t h = (lane_id + 1u) * 0x9E3779B9u;
+    auto rnd = [&h]() {
+        h = h * 1664525u + 1013904223u;
+        return h >> 8;
+    };
+    v8bf a, b;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        if (operands == 0) {
+            a[q] = (__bf16)(float)(q % 4 + 1);
+            b[q] = (__bf16)(float)(q % 2 + 1);
+        } else {
+            const uint32_t r = rnd();
+            const float xa = (1.0f + (r & 127) / 128.0f) * (float)(1 << ((r >> 7) & 3)) * 0.25f;
+            a[q] = (__bf16)((r >> 9) & 1 ? -xa : xa);
+            b[q] = (__bf16)(((int)((r >> 10) & 7) - 4) * 0.0078125f);
+        }
+    }
+    v4f acc[PM_ACC];
+#pragma unroll
+    for (int j = 0; j < PM_ACC; ++j) acc[j] = v4f{0, 0, 0, 0};
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int j = 0; j < PM_ACC; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+    }
+    v4f sum = acc[0];
+#pragma unroll
+    for (int j = 1; j < PM_ACC; ++j) sum += acc[j];
+    *reinterpret_cast<v4f*>(out + (size_t)lane_id * 4) = sum;
+}
+
 __global__ __launch_bounds__(256) void probe_copy_kernel(const v4u* __restrict__ src, v4u* __restrict__ dst,
                                                          size_t n16) {
     const size_t stride = (size_t)gridDim.x * 256;
@@ -78,6 +118,15 @@ hipError_t launch_probe_mfma_i8(int32_t* out, int blocks, int iters, int operand
 
 double probe_mfma_i8_ops(int blocks, int iters) {
     return 2.0 * 16 * 16 * 64 * (double)PM_ACC * iters * 4.0 * blocks;  // 4 waves per workgroup
+}
+
+hipError_t launch_probe_mfma_bf16(float* out, int blocks, int iters, int operands, hipStream_t st) {
+    hipLaunchKernelGGL(probe_mfma_bf16_kernel, dim3(blocks), dim3(256), 0, st, out, iters, operands);
+    return hipGetLastError();
+}
+
+double probe_mfma_bf16_flops(int blocks, int iters) {
+    return 2.0 * 16 * 16 * 32 * (double)PM_ACC * iters * 4.0 * blocks;
 }
 
 hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t st) {

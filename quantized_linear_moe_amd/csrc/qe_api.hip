@@ -687,6 +687,14 @@ int qe_probe_mfma_i8(int32_t* out, int32_t blocks, int32_t iters, int32_t operan
     return QE_OK;
 }
 
+int qe_probe_mfma_bf16(float* out, int32_t blocks, int32_t iters, int32_t operands, double* flops, void* stream) {
+    QE_CHECK(out && blocks >= 1 && iters >= 1 && (operands == 0 || operands == 1), QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(out), QE_ERR_ALIGNMENT);
+    QE_TRY_HIP(launch_probe_mfma_bf16(out, blocks, iters, operands, S(stream)));
+    if (flops) *flops = probe_mfma_bf16_flops(blocks, iters);
+    return QE_OK;
+}
+
 int qe_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
     QE_CHECK(src && dst && bytes % 16 == 0, QE_ERR_INVALID_ARG);
     QE_CHECK(aligned16(src) && aligned16(dst), QE_ERR_ALIGNMENT);

@@ -141,6 +141,8 @@ int skinny_ksplit(int d_in, int d_out);
 int skinny_ksplit_proj(int d_in);
 hipError_t launch_probe_mfma_i8(int32_t* out, int blocks, int iters, int operands, hipStream_t st);
 double probe_mfma_i8_ops(int blocks, int iters);
+hipError_t launch_probe_mfma_bf16(float* out, int blocks, int iters, int operands, hipStream_t st);
+double probe_mfma_bf16_flops(int blocks, int iters);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
 
 // fused weight-only decode (T <= 16): one GEMV launch for the projection and the packed

@@ -44,3 +44,16 @@ def test_probe_argument_errors(L):
     other = torch.zeros(64, dtype=torch.int32, device=DEV)
     with pytest.raises(L.QEError):
         L.qe_probe_copy(buf, other, 20)  # not a multiple of 16
+
+
+def test_probe_mfma_bf16_reports_its_operations(L):
+    blocks, iters = 8, 3
+    sink = torch.zeros(blocks * 256 * 4, dtype=torch.float32, device=DEV)
+    flops = L.qe_probe_mfma_bf16(sink, blocks, iters, 0)
+    torch.cuda.synchronize()
+    assert flops == 2 * 16 * 16 * 32 * 8 * iters * 4 * blocks
+    # constant operands: every lane's four outputs are sums of 8 accumulators, each
+    # iters times a row of A (1, 2, 3, 4 repeated) against a column of B (1, 2 repeated)
+    assert torch.all(sink == sink[0]) and float(sink[0]) == 8 * iters * 8 * (1 * 1 + 2 * 2 + 3 * 1 + 4 * 2)
+    with pytest.raises(L.QEError):
+        L.qe_probe_mfma_bf16(sink, 1, 1, 2)
