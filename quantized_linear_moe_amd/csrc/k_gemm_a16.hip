@@ -21,9 +21,11 @@
 // Many tokens (>= 512): 128 tokens x 256 channels per workgroup (wave tile 128 x 64: each x
 // fragment read from LDS feeds four MFMAs, which keeps the LDS traffic at half its bandwidth
 // when the matrix cores run at full rate), and both the x tile and the
-// weight fragments go global -> LDS by DMA into a three-stage ring (two K blocks in flight,
-// explicit vmcnt waits, no staging registers); x rows are stored with their 16-byte chunks
-// XOR-swizzled by row against bank conflicts.  Its epilogue scales by s_w and adds u.B_s and,
+// weight fragments go global -> LDS by DMA into a three-stage ring of 64-K half blocks (two
+// halves in flight, explicit vmcnt waits, no staging registers); x rows are stored with their
+// 16-byte chunks XOR-swizzled by row against bank conflicts.  A stage is 24 KB, so two
+// workgroups share a CU and each SIMD holds two waves that cover each other's LDS and
+// barrier latency.  Its epilogue scales by s_w and adds u.B_s and,
 // for every routed expert present among the tile's tokens, (v masked to that expert's rows).B_e
 // with bf16 MFMAs, so y is written once and the adapter rows are read once per tile.
 
@@ -52,9 +54,11 @@ __device__ inline v4u load_x8(const void* __restrict__ x, int x_dtype, size_t id
                cvt(b[2]) | (cvt(b[3]) << 16)};
 }
 
-// Epilogue of a tile whose K range is complete: y = s_w * acc + u.B_s + v.B_{e_t} (bf16 MFMAs
-// for the low-rank terms, one round per routed expert present among the tile's tokens).  Lane
-// holds rows m0 + 16m + 4lg + r, column 16 (nb0 + j) + lr of each block; the A operands of the
+// Epilogue of a tile whose K range is complete: y = s_w * acc + u.B_s + v.B_{e_t}.  Per 16-row
+// block m the low-rank terms go into a small accumulator of their own (bf16 MFMAs; one round
+// per routed expert present among the block's rows, v masked to that expert's rows), and the
+// block's outputs are written once.  acc is only read here, so no loop carries it.  Lane holds
+// rows m0 + 16m + 4lg + r, column 16 (nb0 + j) + lr of each block; the A operands of the
 // adapter MFMAs are rows m0 + 16m + lr.
 template <int MB, int NBW>
 __device__ __attribute__((always_inline)) inline void a16_epilogue(
@@ -63,73 +67,63 @@ __device__ __attribute__((always_inline)) inline void a16_epilogue(
     const int32_t* __restrict__ expert, const uint16_t* __restrict__ bt_r, int rr_pad, int n_r,
     float* __restrict__ y) {
     const int NB = d_out >> 4, lr = lane & 15, lg = lane >> 4;
+    const bool shared = u != nullptr && bt_s != nullptr && rs_pad > 0;
+    const bool routed = v != nullptr && expert != nullptr && bt_r != nullptr && rr_pad > 0 && n_r > 0;
     bool nb_ok[NBW];
     int nbc[NBW];  // fragment sources; blocks past d_out repeat block 0 (never stored)
+    float sw[NBW];
 #pragma unroll
     for (int j = 0; j < NBW; ++j) {
         nb_ok[j] = nb0 + j < NB;
         nbc[j] = nb_ok[j] ? nb0 + j : 0;
-        const float sw = w_scale[nbc[j] * 16 + lr];
-#pragma unroll
-        for (int m = 0; m < MB; ++m) acc[m][j] *= sw;
+        sw[j] = w_scale[nbc[j] * 16 + lr];
     }
-    auto arow = [&](int m) { return min(m0 + m * 16 + lr, T - 1); };
-    if (u != nullptr && bt_s != nullptr && rs_pad > 0) {
-        for (int k0 = 0; k0 < rs_pad; k0 += 32) {
-            v8bf bs[NBW];
 #pragma unroll
-            for (int j = 0; j < NBW; ++j)
-                bs[j] = *reinterpret_cast<const v8bf*>(bt_s + (size_t)(nbc[j] * 16 + lr) * rs_pad + k0 + lg * 8);
+    for (int m = 0; m < MB; ++m) {
+        const int ar = min(m0 + m * 16 + lr, T - 1);
+        v4f ad[NBW];
 #pragma unroll
-            for (int m = 0; m < MB; ++m) {
-                const v8bf ua = *reinterpret_cast<const v8bf*>(u + (size_t)arow(m) * rs_pad + k0 + lg * 8);
+        for (int j = 0; j < NBW; ++j) ad[j] = v4f{0, 0, 0, 0};
+        if (shared) {
+            for (int k0 = 0; k0 < rs_pad; k0 += 32) {
+                const v8bf ua = *reinterpret_cast<const v8bf*>(u + (size_t)ar * rs_pad + k0 + lg * 8);
 #pragma unroll
-                for (int j = 0; j < NBW; ++j)
-                    acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, bs[j], acc[m][j], 0, 0, 0);
-            }
-        }
-    }
-    if (v != nullptr && expert != nullptr && bt_r != nullptr && rr_pad > 0 && n_r > 0) {
-        int ex[MB];
-        uint32_t present = 0;
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-            ex[m] = m0 + m * 16 + lr < T ? min(max(expert[arow(m)], 0), n_r - 1) : -1;
-            for (int q = 0; q < n_r; ++q)
-                if (__ballot(ex[m] == q)) present |= 1u << q;
-        }
-        while (present) {  // wave-uniform
-            const int e = __builtin_ctz(present);
-            present &= present - 1;
-            for (int k0 = 0; k0 < rr_pad; k0 += 32) {
-                v8bf br[NBW];
-#pragma unroll
-                for (int j = 0; j < NBW; ++j)
-                    br[j] = *reinterpret_cast<const v8bf*>(bt_r + ((size_t)e * d_out + nbc[j] * 16 + lr) * rr_pad +
-                                                           k0 + lg * 8);
-#pragma unroll
-                for (int m = 0; m < MB; ++m) {
-                    if (__ballot(ex[m] == e) == 0) continue;  // no row of this block uses expert e
-                    const v8bf va = ex[m] == e
-                                        ? *reinterpret_cast<const v8bf*>(v + (size_t)arow(m) * rr_pad + k0 + lg * 8)
-                                        : v8bf{};
-#pragma unroll
-                    for (int j = 0; j < NBW; ++j)
-                        acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, br[j], acc[m][j], 0, 0, 0);
+                for (int j = 0; j < NBW; ++j) {
+                    const v8bf bs =
+                        *reinterpret_cast<const v8bf*>(bt_s + (size_t)(nbc[j] * 16 + lr) * rs_pad + k0 + lg * 8);
+                    ad[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, bs, ad[j], 0, 0, 0);
                 }
             }
         }
-    }
+        if (routed) {
+            const int ex = m0 + m * 16 + lr < T ? min(max(expert[ar], 0), n_r - 1) : -1;
+            uint32_t present = 0;
+            for (int q = 0; q < n_r; ++q)
+                if (__ballot(ex == q)) present |= 1u << q;
+            while (present) {  // wave-uniform
+                const int e = __builtin_ctz(present);
+                present &= present - 1;
+                for (int k0 = 0; k0 < rr_pad; k0 += 32) {
+                    const v8bf va =
+                        ex == e ? *reinterpret_cast<const v8bf*>(v + (size_t)ar * rr_pad + k0 + lg * 8) : v8bf{};
 #pragma unroll
-    for (int j = 0; j < NBW; ++j) {
-        if (!nb_ok[j]) continue;
+                    for (int j = 0; j < NBW; ++j) {
+                        const v8bf br = *reinterpret_cast<const v8bf*>(
+                            bt_r + ((size_t)e * d_out + nbc[j] * 16 + lr) * rr_pad + k0 + lg * 8);
+                        ad[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, br, ad[j], 0, 0, 0);
+                    }
+                }
+            }
+        }
 #pragma unroll
-        for (int m = 0; m < MB; ++m)
+        for (int j = 0; j < NBW; ++j) {
+            if (!nb_ok[j]) continue;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = m0 + m * 16 + lg * 4 + r;
-                if (t < T) y[(size_t)t * d_out + (nb0 + j) * 16 + lr] = acc[m][j][r];
+                if (t < T) y[(size_t)t * d_out + (nb0 + j) * 16 + lr] = acc[m][j][r] * sw[j] + ad[j][r];
             }
+        }
     }
 }
 
@@ -239,61 +233,63 @@ __global__ __launch_bounds__(256, 2) void gemm_a16_kernel(
     }
 }
 
-constexpr int GR_NS = 3;  // ring stages
+constexpr int GR_NS = 3;  // ring stages of 64 K: loads run two stages ahead
 
-// Many-token form (see the file comment): tile 128 x 256, wave w owns channel blocks 4w .. 4w+3.
+// row-dependent XOR of the 16-byte chunk index in a 128-byte x row: every 8 and every 16
+// consecutive rows read at one logical chunk fall on distinct bank groups
+__device__ inline int ring_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
 template <int WB>
-__global__ __launch_bounds__(256, 1) void gemm_a16_ring_kernel(
+__global__ __launch_bounds__(256, 2) void gemm_a16_ring_kernel(
     const void* __restrict__ x, int T, int d_in, int d_out, const uint32_t* __restrict__ w_tiled, int n_tm,
     float* __restrict__ part, const float* __restrict__ w_scale, const uint16_t* __restrict__ u,
     const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v, const int32_t* __restrict__ expert,
     const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, float* __restrict__ y) {
     constexpr int MB = 8, BM = 128, NBW = 4;
-    constexpr int FW = Frag<WB>::kWords;
-    constexpr int X_BYTES = BM * 256;                     // x tile of one K block
-    constexpr int W_WAVE = NBW * FW * 256;                // one wave's fragments (FW dwords x 64 lanes per block)
-    constexpr int STAGE = X_BYTES + 4 * W_WAVE;
-    constexpr int X_DMA = BM * 16 / 256;                  // 16-byte x copies per thread and stage
-    constexpr int OPS = X_DMA + NBW * FW;                 // DMA instructions per thread and stage
+    constexpr int X_BYTES = BM * 128;                     // x tile of one 64-K half block
+    constexpr int W_WAVE = NBW * 2 * 256;                 // one wave's two fragment dwords per block
+    constexpr int STAGE = X_BYTES + 4 * W_WAVE;           // 24 KB: two workgroups fit one CU
+    constexpr int X_DMA = X_BYTES / 16 / 256;             // 16-byte x copies per thread and stage
+    constexpr int OPS = X_DMA + 2 * NBW;                  // DMA instructions per thread and stage
     __shared__ __attribute__((aligned(1024))) uint8_t smem[GR_NS * STAGE];
 
     const int tm = blockIdx.x % n_tm, tn = blockIdx.x / n_tm;
     const int m0 = tm * BM;
     const int NB = d_out >> 4, KB = d_in >> 7;
     const int kb0 = (int)((long)blockIdx.y * KB / gridDim.y), kb1 = (int)((long)(blockIdx.y + 1) * KB / gridDim.y);
-    const int nk = kb1 - kb0;
+    const int nh = 2 * (kb1 - kb0);  // 64-K halves
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int nb0 = tn * 16 + NBW * wid;
     const uint32_t lds0 = lds_addr(smem);
-    const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(x) + (size_t)kb0 * 128;
 
-    // x copy p of this thread: chunk i = 256 p + tid is LDS slot (row i / 16, slot i % 16) and
-    // holds the row's logical chunk slot ^ (row & 15)
+    // x copy p of this thread: chunk i = 256 p + tid is LDS slot (row i / 8, slot i % 8) and
+    // holds the row's logical chunk slot ^ ring_swz(row)
     const uint16_t* xsrc[X_DMA];
 #pragma unroll
     for (int p = 0; p < X_DMA; ++p) {
-        const int i = p * 256 + tid, row = i >> 4, slot = i & 15;
-        xsrc[p] = xb + (size_t)min(m0 + row, T - 1) * d_in + ((slot ^ (row & 15)) << 3);
+        const int i = p * 256 + tid, row = i >> 3, slot = i & 7;
+        xsrc[p] = xb + (size_t)min(m0 + row, T - 1) * d_in + ((slot ^ ring_swz(row)) << 3);
     }
-    // weight dword q of block j: LDS words [(wid*NBW + j)*FW + q][lane]
-    auto wsrc = [&](int j, int q, int kb) -> const uint32_t* {
+    // the two fragment dwords a half block uses: W3 the magnitudes of its two steps and the
+    // signs, W4 its two steps' codes
+    auto wsrc = [&](int j, int hh, int qq, int kb) -> const uint32_t* {
         const int nb = min(nb0 + j, NB - 1);  // blocks past d_out repeat a valid block (never stored)
         if constexpr (WB == 3) {
-            return w_tiled + (((size_t)nb * KB + kb) * 64 + lane) * 3 + q;
-        } else {  // two 64-K steps of two dwords
-            return w_tiled + (((size_t)nb * 2 * KB + 2 * kb + (q >> 1)) * 64 + lane) * 2 + (q & 1);
+            return w_tiled + (((size_t)nb * KB + kb) * 64 + lane) * 3 + (qq ? 2 : hh);
+        } else {
+            return w_tiled + (((size_t)nb * 2 * KB + 2 * kb + hh) * 64 + lane) * 2 + qq;
         }
     };
-    auto issue = [&](int stage, int i) {  // K block kb0 + i into ring slot `stage`
-        const int kb = kb0 + i;
+    auto issue = [&](int stage, int h) {  // half block h of this workgroup's K range into `stage`
         const uint32_t base = lds0 + stage * STAGE;
 #pragma unroll
-        for (int p = 0; p < X_DMA; ++p) dma16(xsrc[p] + (size_t)kb * 128, base + (p * 256 + wid * 64) * 16);
+        for (int p = 0; p < X_DMA; ++p) dma16(xsrc[p] + (size_t)h * 64, base + (p * 256 + wid * 64) * 16);
 #pragma unroll
         for (int j = 0; j < NBW; ++j)
 #pragma unroll
-            for (int q = 0; q < FW; ++q)
-                dma4(wsrc(j, q, kb), base + X_BYTES + wid * W_WAVE + (j * FW + q) * 256);
+            for (int qq = 0; qq < 2; ++qq)
+                dma4(wsrc(j, h & 1, qq, kb0 + (h >> 1)), base + X_BYTES + wid * W_WAVE + (j * 2 + qq) * 256);
     };
 
     v4f acc[MB][NBW];
@@ -303,40 +299,55 @@ __global__ __launch_bounds__(256, 1) void gemm_a16_ring_kernel(
         for (int j = 0; j < NBW; ++j) acc[m][j] = v4f{0, 0, 0, 0};
 
 #pragma unroll
-    for (int st = 0; st < GR_NS - 1; ++st) issue(st, min(st, nk - 1));
+    for (int st = 0; st < GR_NS - 1; ++st) issue(st, min(st, nh - 1));
     QE_WAIT_VMCNT_LDS((GR_NS - 2) * OPS);
     QE_WG_BARRIER();
 
-    for (int i = 0; i < nk; ++i) {
-        // refill the slot consumed in the previous step (past the end: a harmless repeat)
-        issue((i + GR_NS - 1) % GR_NS, min(i + GR_NS - 1, nk - 1));
+    auto half = [&](int i, auto hh_c) {  // half i (of parity hh) of the K range
+        constexpr int hh = decltype(hh_c)::value;
+        // refill the slot consumed in the previous half (past the end: a harmless repeat)
+        issue((i + GR_NS - 1) % GR_NS, min(i + GR_NS - 1, nh - 1));
         const uint8_t* st = smem + (i % GR_NS) * STAGE;
         const uint32_t* wl = reinterpret_cast<const uint32_t*>(st + X_BYTES + wid * W_WAVE);
-        uint32_t f[NBW][FW];
+        uint32_t f[NBW][Frag<WB>::kWords];
 #pragma unroll
-        for (int j = 0; j < NBW; ++j)
+        for (int j = 0; j < NBW; ++j) {
+            const uint32_t g0 = wl[(j * 2) * 64 + lane], g1 = wl[(j * 2 + 1) * 64 + lane];
 #pragma unroll
-            for (int q = 0; q < FW; ++q) f[j][q] = wl[(j * FW + q) * 64 + lane];
+            for (int q = 0; q < Frag<WB>::kWords; ++q) f[j][q] = 0;
+            if constexpr (WB == 3) {
+                f[j][hh] = g0;
+                f[j][2] = g1;
+            } else {
+                f[j][2 * hh] = g0;
+                f[j][2 * hh + 1] = g1;
+            }
+        }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s2 = 0; s2 < 2; ++s2) {
+            const int s = 2 * hh + s2;
             v8bf b[NBW];
 #pragma unroll
             for (int j = 0; j < NBW; ++j) b[j] = weight_frag<WB>(f[j], s);
-            const int c = x_step_offset<WB>(s, lg) >> 3;  // 16-byte chunk of the row
+            const int c = (x_step_offset<WB>(s, lg) - 64 * hh) >> 3;  // 16-byte chunk of the row
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
                 const int row = m * 16 + lr;
-                const v8bf a = *reinterpret_cast<const v8bf*>(st + row * 256 + ((c ^ (row & 15)) << 4));
+                const v8bf a = *reinterpret_cast<const v8bf*>(st + row * 128 + ((c ^ ring_swz(row)) << 4));
 #pragma unroll
                 for (int j = 0; j < NBW; ++j)
                     acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], acc[m][j], 0, 0, 0);
             }
         }
-        // the slot read here is refilled in the next step: every LDS read must have completed, and
-        // the next block must have landed (the later one may still be in flight)
+        // the slot read here is refilled in the next half: every LDS read must have completed,
+        // and the next half must have landed (the later one may still be in flight)
         __builtin_amdgcn_sched_barrier(0);
         QE_WAIT_VMCNT_LDS((GR_NS - 2) * OPS);
         QE_WG_BARRIER();
+    };
+    for (int i = 0; i < nh; i += 2) {
+        half(i, std::integral_constant<int, 0>{});
+        half(i + 1, std::integral_constant<int, 1>{});
     }
     QE_WAIT_VMCNT(0);
 
