@@ -235,9 +235,15 @@ __global__ __launch_bounds__(256, 2) void gemm_a16_kernel(
 
 constexpr int GR_NS = 3;  // ring stages of 64 K: loads run two stages ahead
 
-// row-dependent XOR of the 16-byte chunk index in a 128-byte x row: every 8 and every 16
-// consecutive rows read at one logical chunk fall on distinct bank groups
-__device__ inline int ring_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// x rows in the ring are 128 bytes (eight 16-byte chunks).  At MFMA step s2 of a half block,
+// lane (lr, lg) reads logical chunk 4 s2 + lg (3-bit weights) or 2 lg + s2 (4-bit weights); the
+// 4-bit layout stores logical chunk 2 a + b at chunk 4 b + a, so both read physical chunk
+// 4 s2 + lg, and that chunk is XORed with row & 7.  Measured with the LDS bank-conflict
+// counter on this part: no conflicts for either format (XOR with (row & 7) ^ ((row >> 3) & 1)
+// doubles the LDS cycles, and so does the 4-bit order without the rotation).
+__device__ inline int ring_swz(int row) { return row & 7; }
+template <int WB>
+__device__ inline int ring_logical_chunk(int pc) { return WB == 4 ? 2 * (pc & 3) + (pc >> 2) : pc; }
 
 template <int WB>
 __global__ __launch_bounds__(256, 2) void gemm_a16_ring_kernel(
@@ -258,38 +264,46 @@ __global__ __launch_bounds__(256, 2) void gemm_a16_ring_kernel(
     const int NB = d_out >> 4, KB = d_in >> 7;
     const int kb0 = (int)((long)blockIdx.y * KB / gridDim.y), kb1 = (int)((long)(blockIdx.y + 1) * KB / gridDim.y);
     const int nh = 2 * (kb1 - kb0);  // 64-K halves
-    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: LDS bases stay scalar
     const int nb0 = tn * 16 + NBW * wid;
     const uint32_t lds0 = lds_addr(smem);
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(x) + (size_t)kb0 * 128;
 
     // x copy p of this thread: chunk i = 256 p + tid is LDS slot (row i / 8, slot i % 8) and
-    // holds the row's logical chunk slot ^ ring_swz(row)
+    // holds physical chunk slot ^ ring_swz(row) of the row
     const uint16_t* xsrc[X_DMA];
 #pragma unroll
     for (int p = 0; p < X_DMA; ++p) {
         const int i = p * 256 + tid, row = i >> 3, slot = i & 7;
-        xsrc[p] = xb + (size_t)min(m0 + row, T - 1) * d_in + ((slot ^ ring_swz(row)) << 3);
+        xsrc[p] = xb + (size_t)min(m0 + row, T - 1) * d_in + (ring_logical_chunk<WB>(slot ^ ring_swz(row)) << 3);
     }
-    // the two fragment dwords a half block uses: W3 the magnitudes of its two steps and the
-    // signs, W4 its two steps' codes
-    auto wsrc = [&](int j, int hh, int qq, int kb) -> const uint32_t* {
-        const int nb = min(nb0 + j, NB - 1);  // blocks past d_out repeat a valid block (never stored)
-        if constexpr (WB == 3) {
-            return w_tiled + (((size_t)nb * KB + kb) * 64 + lane) * 3 + (qq ? 2 : hh);
-        } else {
-            return w_tiled + (((size_t)nb * 2 * KB + 2 * kb + hh) * 64 + lane) * 2 + qq;
-        }
-    };
+    // this lane's fragment dwords of K block kb0 for each of the wave's channel blocks (blocks
+    // past d_out repeat a valid block, never stored); a half block uses two of them: W3 the
+    // magnitudes of its two steps and the signs, W4 its two steps' codes
+    const uint32_t* wsrc[NBW];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        const size_t nb = min(nb0 + j, NB - 1);
+        wsrc[j] = WB == 3 ? w_tiled + ((nb * KB + kb0) * 64 + lane) * 3 : w_tiled + ((nb * 2 * KB + 2 * kb0) * 64 + lane) * 2;
+    }
     auto issue = [&](int stage, int h) {  // half block h of this workgroup's K range into `stage`
         const uint32_t base = lds0 + stage * STAGE;
 #pragma unroll
-        for (int p = 0; p < X_DMA; ++p) dma16(xsrc[p] + (size_t)h * 64, base + (p * 256 + wid * 64) * 16);
+        for (int p = 0; p < X_DMA; ++p) dma16(xsrc[p] + h * 64, base + (p * 256 + wid * 64) * 16);
+        const uint32_t wbase = base + X_BYTES + wid * W_WAVE;
 #pragma unroll
-        for (int j = 0; j < NBW; ++j)
-#pragma unroll
-            for (int qq = 0; qq < 2; ++qq)
-                dma4(wsrc(j, h & 1, qq, kb0 + (h >> 1)), base + X_BYTES + wid * W_WAVE + (j * 2 + qq) * 256);
+        for (int j = 0; j < NBW; ++j) {
+            if constexpr (WB == 3) {
+                const uint32_t* q = wsrc[j] + (h >> 1) * 192;
+                dma4(q + (h & 1), wbase + (j * 2) * 256);
+                dma4(q + 2, wbase + (j * 2 + 1) * 256);
+            } else {
+                const uint32_t* q = wsrc[j] + h * 128;
+                dma4(q, wbase + (j * 2) * 256);
+                dma4(q + 1, wbase + (j * 2 + 1) * 256);
+            }
+        }
     };
 
     v4f acc[MB][NBW];
@@ -329,7 +343,7 @@ __global__ __launch_bounds__(256, 2) void gemm_a16_ring_kernel(
             v8bf b[NBW];
 #pragma unroll
             for (int j = 0; j < NBW; ++j) b[j] = weight_frag<WB>(f[j], s);
-            const int c = (x_step_offset<WB>(s, lg) - 64 * hh) >> 3;  // 16-byte chunk of the row
+            const int c = 4 * s2 + lg;  // physical chunk of the step's 8 activations
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
                 const int row = m * 16 + lr;
