@@ -1,0 +1,127 @@
+"""CPU oracle for the construction of the QE experts (post-training, before inference).
+
+Test infrastructure only: tests, the smoke check and the benchmark's CPU baseline import it;
+the library never does.  fp64 throughout, numpy's QR / SVD as library primitives.
+
+Sources (pages as titles, with the section each step follows):
+  * MCISLAB DeepRead summary of "Quant Experts", section "Method", Shared Expert (SE): the
+    layer's quantization error is E = W_f - W_q; the SE is a low-rank reconstruction of it,
+    with channel-wise scaling of the activations.  Routed Experts (REs): the error left after
+    the SE goes to the REs, one low-rank adapter per cluster of token-dependent channels.
+    Section "Experiments": total rank r = 64 split evenly between SE and REs, k = 32, N_r = 8.
+  * PaperDaily post "西交大提出Quant Experts：token级量化补偿", section "核心设计": the SE
+    reconstructs the error by a whitening SVD, which balances the scales of the directions
+    before the decomposition so the low-rank factors capture the dominant error.
+  * Halko, Martinsson and Tropp, "Finding structure with randomness" (SIAM Review 2011),
+    Algorithm 4.4 (randomized subspace iteration) and Algorithm 5.1 (direct SVD of the
+    small matrix): the randomized truncated SVD, with the Gaussian test matrix an input.
+
+Readings where the pages leave a step open (each also listed in the design notes):
+  * W_q is the effective quantized weight in the input domain of x: the codes of
+    W_f * diag(s) times the row scale, divided by s (the adapters act on x, not x / s).
+  * Whitening is diagonal: input channel j is weighted by the RMS of its calibration
+    activations, c_j = sqrt(mean_t x[t, j]^2), so the SVD of M = diag(c) E^T minimizes the
+    expected output error sum_t |x_t (E^T - A B)|^2 under a diagonal activation covariance;
+    A = diag(1/c) U_r S_r^(1/2) (rows with c_j = 0 are zero), B = S_r^(1/2) V_r^T.
+  * The SE approximates the whole E; the RE of cluster g approximates the residual
+    E_1 = E - (A_s B_s)^T on the input channels of that cluster only (weights c_j on the
+    cluster, 0 elsewhere), so its A rows outside the cluster are zero.
+  * The router fit is not covered here.
+parity pinned: every function below has CPU pins in tests/test_oracle_experts.py.
+"""
+
+from typing import Dict, Optional, Sequence, Tuple
+
+import numpy as np
+
+from . import qe_oracle as O
+
+
+def quant_error(W_f: np.ndarray, s: Optional[np.ndarray], w_bits: int) -> np.ndarray:
+    """E = W_f - W_q with W_q = diag(s_w) q diag(1/s) ([DeepRead] "Method", SE).
+
+    The codes and row scales are the weight quantizer's (float32 decisions); E in fp64.
+    """
+    q, s_w = O.quant_weights(W_f, s, w_bits)
+    Wq = s_w.astype(np.float64)[:, None] * q.astype(np.float64)
+    if s is not None:
+        Wq = Wq / np.asarray(s, dtype=np.float64)[None, :]
+    return np.asarray(W_f, dtype=np.float64) - Wq
+
+
+def channel_rms(x: np.ndarray) -> np.ndarray:
+    """Whitening weights c_j = sqrt(mean_t x[t, j]^2) over the calibration tokens."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.sqrt(np.mean(x * x, axis=0))
+
+
+def _factors(U: np.ndarray, S: np.ndarray, Vt: np.ndarray, w: np.ndarray, r: int):
+    """A = diag(1/w) U_r S_r^(1/2) (zero rows where w = 0), B = S_r^(1/2) V_r^T."""
+    root = np.sqrt(S[:r])
+    inv = np.zeros_like(w, dtype=np.float64)
+    nz = w > 0
+    inv[nz] = 1.0 / w[nz]
+    A = inv[:, None] * U[:, :r] * root[None, :]
+    B = root[:, None] * Vt[:r, :]
+    return A, B, S[:r].copy()
+
+
+def whitened_lowrank(E: np.ndarray, w: np.ndarray, r: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """The definition: truncated SVD of M = diag(w) E^T, rank r (Eckart-Young optimal).
+
+    Returns A [d_in, r], B [r, d_out] with diag(w) A B = M_r, and the r singular values.
+    """
+    M = np.asarray(w, dtype=np.float64)[:, None] * np.asarray(E, dtype=np.float64).T
+    U, S, Vt = np.linalg.svd(M, full_matrices=False)
+    return _factors(U, S, Vt, np.asarray(w, dtype=np.float64), r)
+
+
+def randomized_lowrank(E: np.ndarray, w: np.ndarray, omega: np.ndarray, r: int,
+                       power_iters: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Randomized truncated SVD of M = diag(w) E^T with test matrix omega [d_out, k], k >= r.
+
+    Halko-Martinsson-Tropp Algorithm 4.4: Y = M omega, Q = qr(Y); power_iters times
+    (Q~ = qr(M^T Q), Q = qr(M Q~)); then Algorithm 5.1: B = Q^T M, B = U~ S V^T, U = Q U~.
+    """
+    M = np.asarray(w, dtype=np.float64)[:, None] * np.asarray(E, dtype=np.float64).T
+    Q, _ = np.linalg.qr(M @ np.asarray(omega, dtype=np.float64))
+    for _ in range(power_iters):
+        Qt, _ = np.linalg.qr(M.T @ Q)
+        Q, _ = np.linalg.qr(M @ Qt)
+    Bsmall = Q.T @ M
+    Ut, S, Vt = np.linalg.svd(Bsmall, full_matrices=False)
+    return _factors(Q @ Ut, S, Vt, np.asarray(w, dtype=np.float64), r)
+
+
+def build_experts(W_f: np.ndarray, s: Optional[np.ndarray], w_bits: int, c: np.ndarray,
+                  dep_channels: Sequence[int], labels: Sequence[int], n_r: int, r_s: int, r_r: int,
+                  omegas: np.ndarray, power_iters: int) -> Dict[str, np.ndarray]:
+    """SE and REs of one linear ([DeepRead] "Method": SE first, the residual to the REs).
+
+    c: whitening weights [d_in]; dep_channels / labels: the token-dependent channels and
+    their cluster in [0, n_r); omegas [1 + n_r, d_out, k]: the test matrix of the SE fit,
+    then of each RE fit.  Returns A_s [d_in, r_s], B_s [r_s, d_out], A_r [n_r, d_in, r_r],
+    B_r [n_r, r_r, d_out], sigma_s, sigma_r, and the residual error E_1 [d_out, d_in].
+    """
+    E = quant_error(W_f, s, w_bits)
+    c = np.asarray(c, dtype=np.float64)
+    d_out, d_in = E.shape
+    out: Dict[str, np.ndarray] = {}
+    if r_s > 0:
+        A_s, B_s, sig_s = randomized_lowrank(E, c, omegas[0], r_s, power_iters)
+        E1 = E - (A_s @ B_s).T
+    else:
+        A_s, B_s, sig_s = np.zeros((d_in, 0)), np.zeros((0, d_out)), np.zeros(0)
+        E1 = E
+    A_r = np.zeros((n_r, d_in, r_r))
+    B_r = np.zeros((n_r, r_r, d_out))
+    sig_r = np.zeros((n_r, r_r))
+    dep = np.asarray(dep_channels, dtype=np.int64)
+    lab = np.asarray(labels, dtype=np.int64)
+    for g in range(n_r):
+        wg = np.zeros(d_in)
+        ch = dep[lab == g]
+        wg[ch] = c[ch]
+        A_r[g], B_r[g], sig_r[g] = randomized_lowrank(E1, wg, omegas[1 + g], r_r, power_iters)
+    out.update(A_s=A_s, B_s=B_s, sigma_s=sig_s, A_r=A_r, B_r=B_r, sigma_r=sig_r, E1=E1)
+    return out
