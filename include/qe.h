@@ -310,6 +310,64 @@ int qe_cluster_channels(const uint32_t* cooc, int32_t n_dep, int64_t T, int32_t 
 int qe_linear_cost(const qe_linear* lin, int32_t T, int32_t n_distinct_experts, int32_t x_bytes_per_elt,
                    double* int_macs, double* adapter_macs, double* alg_bytes);
 
+/* ------------------------------------------------------- expert construction --
+ * Building the shared and routed experts of one linear after calibration (MCISLAB DeepRead
+ * summary of "Quant Experts", section "Method": the quantization error E = W_f - W_q is
+ * reconstructed by the low-rank shared expert, the error left after it by one low-rank
+ * routed expert per cluster of token-dependent channels; PaperDaily post "西交大提出Quant
+ * Experts：token级量化补偿", section "核心设计": by a whitening SVD).  The whitening is
+ * diagonal, with the RMS of each input channel's calibration activations; the truncated SVD
+ * is the randomized subspace iteration of Halko, Martinsson and Tropp ("Finding structure with
+ * randomness", Algorithms 4.4 and 5.1) with the Gaussian test matrix supplied by the caller.
+ * The router fit is not provided.
+ *
+ * qe_quant_error: E = W_f - diag(s_w) q diag(1/s) (float32, device [d_out][d_in]) with the
+ *   codes and row scales qe_pack_weights takes (same float32 arithmetic).  W_f device float32
+ *   [d_out][d_in]; s device float32 [d_in] or NULL; w_bits 3 or 4.  Enqueued on `stream`.
+ * qe_channel_rms: c[j] = sqrt(mean_t x[t][j]^2) over T calibration tokens (x device
+ *   [T][d_in], QE_F32 or QE_BF16; c device float32 [d_in]; sums in double).  ws: device,
+ *   qe_channel_rms_workspace_bytes(T, d_in) bytes.  Enqueued.
+ * qe_sub_lowrank: E[i][j] -= sum_l A[j][l] B[l][i] in place (A device float32 [d_in][r], B
+ *   device float32 [r][d_out], 1 <= r <= 64).  Enqueued.
+ * qe_lowrank_fit: rank-`rank` factors of M = diag(w) E^T (w device float32 [d_in], entries >= 0,
+ *   or NULL for ones; E device float32 [d_out][d_in]); omega device float32 [d_out][k], the
+ *   test matrix (Gaussian entries); 1 <= rank <= k <= min(128, d_in, d_out); 0 <= power_iters
+ *   <= 16.  Outputs on the HOST: A float32 [d_in][rank] = diag(1/w) U_r S_r^(1/2) (rows with
+ *   w = 0 are zero), B float32 [rank][d_out] = S_r^(1/2) V_r^T, sigma double [rank] (descending).
+ *   ws: device, qe_lowrank_workspace_bytes(d_out, d_in, k) bytes.  Synchronizes `stream` (the
+ *   thin QR factorizations run on the host in double between the GPU passes over E).
+ * qe_build_experts: the whole construction for one linear: E = qe_quant_error(W_f, s); the SE
+ *   (rank r_shared, 0 = none) = qe_lowrank_fit(E, c, omegas[0]); E_1 = E - (A_s B_s)^T; for each
+ *   routed expert g < n_routed (<= 16): qe_lowrank_fit(E_1, c on the channels dep_channels[t]
+ *   with labels[t] == g and 0 elsewhere, omegas[1 + g]) with rank r_routed (1..64; ignored when
+ *   n_routed == 0).  c: device float32 [d_in] (qe_channel_rms); dep_channels, labels: HOST int32
+ *   [n_dep] (channel ids in [0, d_in), cluster ids in [0, n_routed), e.g. from
+ *   qe_partition_channels and qe_cluster_channels); omegas: device float32 [1 + n_routed][d_out][k]
+ *   (entry 0 unused when r_shared == 0).  Outputs on the HOST, float32: A_s [d_in][r_shared],
+ *   B_s [r_shared][d_out], A_r [n_routed][d_in][r_routed], B_r [n_routed][r_routed][d_out];
+ *   sigma_s [r_shared], sigma_r [n_routed][r_routed] double.  ws: device,
+ *   qe_build_experts_workspace_bytes(d_out, d_in, k, max(r_shared, r_routed)) bytes (it holds E).
+ *   Synchronizes `stream`.
+ * Errors: QE_ERR_INVALID_ARG / QE_ERR_ALIGNMENT / QE_ERR_WORKSPACE before any work;
+ * QE_ERR_UNSUPPORTED if the small eigenvalue iteration fails to converge; QE_ERR_HIP.
+ */
+int qe_quant_error(const float* W_f, const float* s, int32_t d_out, int32_t d_in, int32_t w_bits, float* E,
+                   void* stream);
+size_t qe_channel_rms_workspace_bytes(int32_t T, int32_t d_in);
+int qe_channel_rms(const void* x, int32_t x_dtype, int32_t T, int32_t d_in, float* c, void* ws, size_t ws_bytes,
+                   void* stream);
+int qe_sub_lowrank(float* E, int32_t d_out, int32_t d_in, const float* A, const float* B, int32_t r, void* stream);
+size_t qe_lowrank_workspace_bytes(int32_t d_out, int32_t d_in, int32_t k);
+int qe_lowrank_fit(const float* E, int32_t d_out, int32_t d_in, const float* w, const float* omega, int32_t k,
+                   int32_t rank, int32_t power_iters, float* A, float* B, double* sigma, void* ws, size_t ws_bytes,
+                   void* stream);
+size_t qe_build_experts_workspace_bytes(int32_t d_out, int32_t d_in, int32_t k, int32_t r_max);
+int qe_build_experts(const float* W_f, const float* s, int32_t d_out, int32_t d_in, int32_t w_bits, const float* c,
+                     const int32_t* dep_channels, const int32_t* labels, int32_t n_dep, int32_t n_routed,
+                     int32_t r_shared, int32_t r_routed, const float* omegas, int32_t k, int32_t power_iters,
+                     float* A_s, float* B_s, float* A_r, float* B_r, double* sigma_s, double* sigma_r, void* ws,
+                     size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------- measurement aids --
  * Not part of the QE computation: kernels whose duration, measured by the caller with
  * events on `stream`, gives the rates this device sustains, reported beside the

@@ -73,6 +73,14 @@ def _load():
         "qe_cooccur": (ctypes.c_int, [P, I, I, P, I, I, P, P, Z, P]),
         "qe_cluster_channels": (ctypes.c_int, [P, I, ctypes.c_int64, I, ctypes.c_double, P, P, P, P]),
         "qe_linear_cost": (ctypes.c_int, [LP, I, I, I, D, D, D]),
+        "qe_quant_error": (ctypes.c_int, [P, P, I, I, I, P, P]),
+        "qe_channel_rms_workspace_bytes": (Z, [I, I]),
+        "qe_channel_rms": (ctypes.c_int, [P, I, I, I, P, P, Z, P]),
+        "qe_sub_lowrank": (ctypes.c_int, [P, I, I, P, P, I, P]),
+        "qe_lowrank_workspace_bytes": (Z, [I, I, I]),
+        "qe_lowrank_fit": (ctypes.c_int, [P, I, I, P, P, I, I, I, P, P, P, P, Z, P]),
+        "qe_build_experts_workspace_bytes": (Z, [I, I, I, I]),
+        "qe_build_experts": (ctypes.c_int, [P, P, I, I, I, P, P, P, I, I, I, I, P, I, I, P, P, P, P, P, P, P, Z, P]),
         "qe_probe_mfma_i8": (ctypes.c_int, [P, I, I, I, D, P]),
         "qe_probe_mfma_bf16": (ctypes.c_int, [P, I, I, I, D, P]),
         "qe_probe_copy": (ctypes.c_int, [P, P, Z, P]),
@@ -90,7 +98,9 @@ EXPORTED = (
     "qe_workspace_bytes", "qe_quant_act", "qe_route", "qe_adapter_inputs", "qe_wq_gemm", "qe_routed_lora",
     "qe_linear_prologue", "qe_linear_forward", "qe_colmean_abs", "qe_channel_topk", "qe_linear_cost",
     "qe_probe_mfma_i8", "qe_probe_mfma_bf16", "qe_probe_copy", "qe_partition_channels", "qe_cooccur_workspace_bytes",
-    "qe_cooccur", "qe_cluster_channels",
+    "qe_cooccur", "qe_cluster_channels", "qe_quant_error", "qe_channel_rms_workspace_bytes", "qe_channel_rms",
+    "qe_sub_lowrank", "qe_lowrank_workspace_bytes", "qe_lowrank_fit", "qe_build_experts_workspace_bytes",
+    "qe_build_experts",
 )
 
 
@@ -260,6 +270,71 @@ def qe_cluster_channels(cooc: np.ndarray, T: int, n_clusters: int, threshold: fl
     _check(_lib.qe_cluster_channels(_ptr(cooc), n, T, n_clusters, threshold, _ptr(labels), _ptr(sim), _ptr(ev),
                                     _ptr(emb)), "qe_cluster_channels")
     return (labels, sim, ev, emb) if outputs else labels
+
+
+def qe_quant_error(W_f, s, w_bits, E, stream=None):
+    """Enqueue E = W_f - W_q (device float32 tensors; s may be None)."""
+    d_out, d_in = W_f.shape
+    _check(_lib.qe_quant_error(_ptr(W_f), _ptr(s), d_out, d_in, w_bits, _ptr(E), _stream(stream)), "qe_quant_error")
+
+
+def qe_channel_rms(x, c, ws, stream=None):
+    """Enqueue c = per-channel RMS of x over its tokens (ws: a device byte tensor of at least
+    qe_channel_rms_workspace_bytes(T, d_in) bytes)."""
+    T, d_in = x.shape
+    _check(_lib.qe_channel_rms(_ptr(x), _dtype_code(x), T, d_in, _ptr(c), _ptr(ws), ws.numel() * ws.element_size(),
+                               _stream(stream)), "qe_channel_rms")
+
+
+def qe_channel_rms_workspace_bytes(T: int, d_in: int) -> int:
+    return _lib.qe_channel_rms_workspace_bytes(T, d_in)
+
+
+def qe_sub_lowrank(E, A, B, stream=None):
+    """Enqueue E -= (A B)^T in place (device float32: E [d_out, d_in], A [d_in, r], B [r, d_out])."""
+    d_out, d_in = E.shape
+    _check(_lib.qe_sub_lowrank(_ptr(E), d_out, d_in, _ptr(A), _ptr(B), A.shape[1], _stream(stream)), "qe_sub_lowrank")
+
+
+def qe_lowrank_workspace_bytes(d_out: int, d_in: int, k: int) -> int:
+    return _lib.qe_lowrank_workspace_bytes(d_out, d_in, k)
+
+
+def qe_lowrank_fit(E, w, omega, rank, power_iters, ws, stream=None):
+    """Randomized truncated SVD of diag(w) E^T (device inputs; omega [d_out, k]); returns host
+    numpy (A [d_in, rank] float32, B [rank, d_out] float32, sigma [rank] float64)."""
+    d_out, d_in = E.shape
+    k = omega.shape[1]
+    A = np.empty((d_in, rank), np.float32)
+    B = np.empty((rank, d_out), np.float32)
+    sig = np.empty(rank, np.float64)
+    _check(_lib.qe_lowrank_fit(_ptr(E), d_out, d_in, _ptr(w), _ptr(omega), k, rank, power_iters, _ptr(A), _ptr(B),
+                               _ptr(sig), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "qe_lowrank_fit")
+    return A, B, sig
+
+
+def qe_build_experts_workspace_bytes(d_out: int, d_in: int, k: int, r_max: int) -> int:
+    return _lib.qe_build_experts_workspace_bytes(d_out, d_in, k, r_max)
+
+
+def qe_build_experts(W_f, s, w_bits, c, dep_channels, labels, n_routed, r_shared, r_routed, omegas, power_iters, ws,
+                     stream=None):
+    """SE and REs of one linear (device W_f, s, c, omegas [1 + n_routed, d_out, k]; host dep_channels
+    and labels); returns a dict of host numpy arrays A_s, B_s, A_r, B_r (float32), sigma_s, sigma_r."""
+    d_out, d_in = W_f.shape
+    k = omegas.shape[2]
+    dep = np.ascontiguousarray(dep_channels, dtype=np.int32)
+    lab = np.ascontiguousarray(labels, dtype=np.int32)
+    rr = r_routed if n_routed else 0
+    out = dict(A_s=np.empty((d_in, r_shared), np.float32), B_s=np.empty((r_shared, d_out), np.float32),
+               A_r=np.empty((n_routed, d_in, rr), np.float32), B_r=np.empty((n_routed, rr, d_out), np.float32),
+               sigma_s=np.empty(r_shared, np.float64), sigma_r=np.empty((n_routed, rr), np.float64))
+    _check(_lib.qe_build_experts(_ptr(W_f), _ptr(s), d_out, d_in, w_bits, _ptr(c), _ptr(dep), _ptr(lab), dep.shape[0],
+                                 n_routed, r_shared, r_routed, _ptr(omegas), k, power_iters, _ptr(out["A_s"]),
+                                 _ptr(out["B_s"]), _ptr(out["A_r"]), _ptr(out["B_r"]), _ptr(out["sigma_s"]),
+                                 _ptr(out["sigma_r"]), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "qe_build_experts")
+    return out
 
 
 def qe_probe_mfma_i8(out, blocks, iters, operands=0, stream=None):

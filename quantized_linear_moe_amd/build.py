@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libqe.so")
 SOURCES = ["qe_api.hip", "k_act.hip", "k_gemm_w4.hip", "k_decode.hip", "k_stat.hip", "k_prep.hip", "k_probe.hip",
-           "k_cooc.hip", "calib_host.hip", "k_gemm_a16.hip"]
+           "k_cooc.hip", "calib_host.hip", "k_gemm_a16.hip", "k_lowrank.hip"]
 ARCH = "gfx950"
 
 

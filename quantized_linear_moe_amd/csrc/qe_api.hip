@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "qe_calib.h"
+#include "qe_lowrank.h"
 #include "qe_internal.h"
 
 namespace qe {
@@ -676,6 +677,89 @@ int qe_cluster_channels(const uint32_t* cooc, int32_t n_dep, int64_t T, int32_t 
     if (spectral_cluster(cooc, n_dep, T, n_clusters, threshold, labels, similarity, eigvals, embedding) != 0)
         return QE_ERR_UNSUPPORTED;
     return QE_OK;
+}
+
+// ------------------------------------------------------------------ expert construction
+namespace {
+int lowrank_status(hipError_t e) {
+    if (e == hipSuccess) return QE_OK;
+    if (e == hipErrorNotSupported) return QE_ERR_UNSUPPORTED;  // eigenvalue iteration did not converge
+    return hip_fail(e);
+}
+}  // namespace
+
+int qe_quant_error(const float* W_f, const float* s, int32_t d_out, int32_t d_in, int32_t w_bits, float* E,
+                   void* stream) {
+    QE_CHECK(W_f && E && d_out > 0 && d_in > 0 && (w_bits == 3 || w_bits == 4), QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(W_f) && aligned16(E) && (!s || aligned16(s)), QE_ERR_ALIGNMENT);
+    QE_TRY_HIP(launch_quant_error(W_f, s, d_out, d_in, w_bits, E, S(stream)));
+    return QE_OK;
+}
+
+size_t qe_channel_rms_workspace_bytes(int32_t T, int32_t d_in) {
+    return T > 0 && d_in > 0 ? channel_rms_workspace_bytes(T, d_in) : 0;
+}
+
+int qe_channel_rms(const void* x, int32_t x_dtype, int32_t T, int32_t d_in, float* c, void* ws, size_t ws_bytes,
+                   void* stream) {
+    QE_CHECK(x && c && ws && T > 0 && d_in > 0 && (x_dtype == QE_F32 || x_dtype == QE_BF16), QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(x) && aligned16(c) && aligned16(ws), QE_ERR_ALIGNMENT);
+    QE_CHECK(ws_bytes >= channel_rms_workspace_bytes(T, d_in), QE_ERR_WORKSPACE);
+    QE_TRY_HIP(launch_channel_rms(x, x_dtype, T, d_in, c, ws, S(stream)));
+    return QE_OK;
+}
+
+int qe_sub_lowrank(float* E, int32_t d_out, int32_t d_in, const float* A, const float* B, int32_t r, void* stream) {
+    QE_CHECK(E && A && B && d_out > 0 && d_in > 0 && r >= 1 && r <= 64, QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(E) && aligned16(A) && aligned16(B), QE_ERR_ALIGNMENT);
+    QE_TRY_HIP(launch_sub_lowrank(E, d_out, d_in, A, B, r, S(stream)));
+    return QE_OK;
+}
+
+size_t qe_lowrank_workspace_bytes(int32_t d_out, int32_t d_in, int32_t k) {
+    return d_out > 0 && d_in > 0 && k > 0 ? lowrank_workspace_bytes(d_out, d_in, k) : 0;
+}
+
+int qe_lowrank_fit(const float* E, int32_t d_out, int32_t d_in, const float* w, const float* omega, int32_t k,
+                   int32_t rank, int32_t power_iters, float* A, float* B, double* sigma, void* ws, size_t ws_bytes,
+                   void* stream) {
+    QE_CHECK(E && omega && A && B && sigma && ws, QE_ERR_INVALID_ARG);
+    QE_CHECK(d_out > 0 && d_in > 0 && k >= 1 && k <= 128 && k <= d_in && k <= d_out, QE_ERR_INVALID_ARG);
+    QE_CHECK(rank >= 1 && rank <= k && power_iters >= 0 && power_iters <= 16, QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(E) && aligned16(omega) && aligned16(ws) && (!w || aligned16(w)), QE_ERR_ALIGNMENT);
+    QE_CHECK(ws_bytes >= lowrank_workspace_bytes(d_out, d_in, k), QE_ERR_WORKSPACE);
+    return lowrank_status(lowrank_fit(E, d_out, d_in, w, omega, k, rank, power_iters, A, B, sigma, ws, S(stream)));
+}
+
+size_t qe_build_experts_workspace_bytes(int32_t d_out, int32_t d_in, int32_t k, int32_t r_max) {
+    return d_out > 0 && d_in > 0 && k > 0 && r_max >= 0 ? build_experts_workspace_bytes(d_out, d_in, k, r_max) : 0;
+}
+
+int qe_build_experts(const float* W_f, const float* s, int32_t d_out, int32_t d_in, int32_t w_bits, const float* c,
+                     const int32_t* dep_channels, const int32_t* labels, int32_t n_dep, int32_t n_routed,
+                     int32_t r_shared, int32_t r_routed, const float* omegas, int32_t k, int32_t power_iters,
+                     float* A_s, float* B_s, float* A_r, float* B_r, double* sigma_s, double* sigma_r, void* ws,
+                     size_t ws_bytes, void* stream) {
+    QE_CHECK(W_f && c && omegas && ws && (w_bits == 3 || w_bits == 4), QE_ERR_INVALID_ARG);
+    QE_CHECK(d_out > 0 && d_in > 0 && k >= 1 && k <= 128 && k <= d_in && k <= d_out, QE_ERR_INVALID_ARG);
+    QE_CHECK(r_shared >= 0 && r_shared <= 64 && r_shared <= k && power_iters >= 0 && power_iters <= 16,
+             QE_ERR_INVALID_ARG);
+    QE_CHECK(n_routed >= 0 && n_routed <= 16, QE_ERR_INVALID_ARG);
+    if (r_shared > 0) QE_CHECK(A_s && B_s && sigma_s, QE_ERR_INVALID_ARG);
+    if (n_routed > 0) {
+        QE_CHECK(r_routed >= 1 && r_routed <= 64 && r_routed <= k, QE_ERR_INVALID_ARG);
+        QE_CHECK(A_r && B_r && sigma_r && n_dep >= 0 && (n_dep == 0 || (dep_channels && labels)), QE_ERR_INVALID_ARG);
+        for (int t = 0; t < n_dep; ++t)
+            QE_CHECK(dep_channels[t] >= 0 && dep_channels[t] < d_in && labels[t] >= 0 && labels[t] < n_routed,
+                     QE_ERR_INVALID_ARG);
+    }
+    QE_CHECK(aligned16(W_f) && aligned16(c) && aligned16(omegas) && aligned16(ws) && (!s || aligned16(s)),
+             QE_ERR_ALIGNMENT);
+    const int r_max = std::max(r_shared, n_routed > 0 ? r_routed : 0);
+    QE_CHECK(ws_bytes >= build_experts_workspace_bytes(d_out, d_in, k, r_max), QE_ERR_WORKSPACE);
+    return lowrank_status(build_experts(W_f, s, d_out, d_in, w_bits, c, dep_channels, labels, n_dep, n_routed,
+                                        r_shared, n_routed > 0 ? r_routed : 0, omegas, k, power_iters, A_s, B_s, A_r,
+                                        B_r, sigma_s, sigma_r, ws, S(stream)));
 }
 
 // ------------------------------------------------------------------ measurement aids
