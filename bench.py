@@ -658,7 +658,8 @@ def extras(torch, synth, qe, libqe, dev, peaks):
     # ---- calibration statistic: InternVL2-8B down input, k = 32 (HBM / ALU bound)
     cfg = synth.get_config("internvl2_8b")
     spec = next(l for l in cfg.linears if l.name == "down")
-    W = torch.from_numpy(synth.gen_linear(cfg, spec)["W_f"]).to(dev)
+    lp = synth.gen_linear(cfg, spec)
+    W = torch.from_numpy(lp["W_f"]).to(dev)
     w = torch.empty(spec.d_in, dtype=torch.float32, device=dev)
     libqe.qe_colmean_abs(W, w)
     x = synth.gen_activations(cfg, spec.stream).to(dev)
@@ -719,6 +720,40 @@ def extras(torch, synth, qe, libqe, dev, peaks):
     out["partition_cluster_host_internvl2_8b_down"] = {
         "partition_ms": round(t_part * 1e3, 3), "cluster_ms": round(t_clu * 1e3, 2), "channels": n_dep,
         "cluster_sizes": np.bincount(labels, minlength=n_r).tolist(), "note": "host C++, one thread"}
+
+    # ---- expert construction on the same linear and clusters: whitening weights from the
+    # calibration tokens, then the SE (rank 32) and the 8 REs (rank 32 each) from the weight
+    # quantization error by randomized truncated SVD (k = 40 columns, 2 power iterations)
+    W_f = W
+    s_d = torch.from_numpy(lp["s"]).to(dev)
+    r_s = r_r = 32
+    k_sv, q_it = 40, 2
+    cr = torch.empty(spec.d_in, device=dev)
+    rws = torch.empty(libqe.qe_channel_rms_workspace_bytes(cfg.T, spec.d_in), dtype=torch.uint8, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(1)
+    omegas = torch.randn(1 + n_r, spec.d_out, k_sv, device=dev, generator=gen)
+    bws = torch.empty(libqe.qe_build_experts_workspace_bytes(spec.d_out, spec.d_in, k_sv, 32), dtype=torch.uint8,
+                      device=dev)
+    ts, tr = [], []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        libqe.qe_channel_rms(x, cr, rws)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ex = libqe.qe_build_experts(W_f, s_d, cfg.w_bits, cr, dep, labels, n_r, r_s, r_r, omegas, q_it, bws)
+        ts.append(time.perf_counter() - t1)
+        tr.append(t1 - t0)
+    fits = 1 + n_r
+    out["expert_build_internvl2_8b_down"] = {
+        "d_in": spec.d_in, "d_out": spec.d_out, "w_bits": cfg.w_bits, "r_shared": r_s, "n_routed": n_r,
+        "r_routed": r_r, "k_columns": k_sv, "power_iters": q_it,
+        "channel_rms_ms": round(float(np.median(tr)) * 1e3, 3), "build_ms": round(float(np.median(ts)) * 1e3, 1),
+        "ms_per_fit": round(float(np.median(ts)) * 1e3 / fits, 1),
+        "passes_over_E_per_fit": 2 * q_it + 2,
+        "sigma_shared_top": [round(float(v), 5) for v in ex["sigma_s"][:4]],
+        "note": "wall clock of the synchronous entry point: GPU thin products over E (float32) and host "
+                "Householder QR / eigenproblem in double between them"}
     return out
 
 

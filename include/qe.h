@@ -334,8 +334,10 @@ int qe_linear_cost(const qe_linear* lin, int32_t T, int32_t n_distinct_experts, 
  *   test matrix (Gaussian entries); 1 <= rank <= k <= min(128, d_in, d_out); 0 <= power_iters
  *   <= 16.  Outputs on the HOST: A float32 [d_in][rank] = diag(1/w) U_r S_r^(1/2) (rows with
  *   w = 0 are zero), B float32 [rank][d_out] = S_r^(1/2) V_r^T, sigma double [rank] (descending).
- *   ws: device, qe_lowrank_workspace_bytes(d_out, d_in, k) bytes.  Synchronizes `stream` (the
- *   thin QR factorizations run on the host in double between the GPU passes over E).
+ *   ws: device, qe_lowrank_workspace_bytes(d_out, d_in, k) bytes.  Synchronizes `stream`: the
+ *   passes over E, the k x k Gram matrices (double sums) and the products with k x k matrices
+ *   run on the GPU; the k x k eigenproblems that orthonormalize (twice, by the Gram matrix;
+ *   directions below 1e-11 of its largest eigenvalue dropped as null) run on the host.
  * qe_build_experts: the whole construction for one linear: E = qe_quant_error(W_f, s); the SE
  *   (rank r_shared, 0 = none) = qe_lowrank_fit(E, c, omegas[0]); E_1 = E - (A_s B_s)^T; for each
  *   routed expert g < n_routed (<= 16): qe_lowrank_fit(E_1, c on the channels dep_channels[t]

@@ -14,15 +14,18 @@
 //   Z = M^T Q (= B^T with B = Q^T M);  B B^T = Z^T Z = U~ S^2 U~^T;  U = Q U~, V = Z U~ S^-1;
 //   A = diag(1/w) U_r S_r^(1/2) (rows with w = 0 are zero), B = S_r^(1/2) V_r^T.
 //
-// The passes over E (d_out x d_in float32, up to ~1 GB for the largest linears) run on the
-// GPU: the thin products M X and M^T X with X of k <= 128 columns (float32 FMAs, LDS tiles,
-// contraction split over workgroups with atomic adds).  The host does the work on the thin
-// matrices in double: Householder QR (Golub and Van Loan, "Matrix Computations", section
-// 5.2.1) and the k x k symmetric eigenproblem.
+// Everything that touches a d-long dimension runs on the GPU: the thin products M X and M^T X
+// with X of k <= 128 columns over E (d_out x d_in float32, up to ~1 GB for the largest
+// linears; float32 FMAs, LDS tiles, contraction split over workgroups with atomic adds), the
+// k x k Gram matrices X^T X (float64 sums) and the products X S with k x k matrices S.  The
+// host only solves k x k symmetric eigenproblems in double.  Orthonormalization is by the Gram
+// matrix, twice (the two-pass scheme of CholeskyQR2, Fukaya et al. 2014, with the eigenvalue
+// decomposition in place of the Cholesky factor): X = Y V diag(lambda)^(-1/2), directions whose
+// eigenvalue is below 1e-11 of the largest dropped as null (they give zero columns), then the
+// same on X, which restores orthogonality to working precision.
 
 #include <algorithm>
 #include <cmath>
-#include <thread>
 #include <vector>
 
 #include "qe_calib.h"
@@ -241,70 +244,62 @@ hipError_t thin(bool trans, const float* E, int d_out, int d_in, const float* S,
     return hipGetLastError();
 }
 
-// ------------------------------------------------------------------ host: thin QR
-// Orthonormal basis of the columns of Y (row-major [m][n], m >= n, float32 from the device)
-// by Householder reflections in double, written row-major to Q (double) and Qf (float32).
-// Work is column-major; the updates of the trailing columns are split over threads.
-void householder_q(const float* Y, int m, int n, double* Q, float* Qf) {
-    std::vector<double> a((size_t)m * n), q((size_t)m * n, 0.0), beta(n, 0.0);
-    for (int i = 0; i < m; ++i)
-        for (int j = 0; j < n; ++j) a[(size_t)j * m + i] = Y[(size_t)i * n + j];
-    const int n_thr = std::max(1, std::min<int>((int)std::thread::hardware_concurrency(), 8));
-    auto parallel_cols = [&](int c0, int c1, auto&& fn) {  // fn(c) for c in [c0, c1)
-        const long work = (long)(c1 - c0) * (m - 0);
-        if (work < (1L << 18) || n_thr == 1) {
-            for (int c = c0; c < c1; ++c) fn(c);
-            return;
+// ------------------------------------------------------------------ Gram matrices
+// G[a][l] += sum_r Y[r][a] Y[r][l] over the rows of blockIdx.x (Y float32 [m][k], G double
+// [k][k], zeroed by the caller); float64 products and sums.
+template <int KP>
+__global__ __launch_bounds__(256) void gram_kernel(const float* __restrict__ Y, int m, int k, int rpb,
+                                                   double* __restrict__ G) {
+    __shared__ float Ys[32][KP];
+    constexpr int NP = KP * KP / 256;
+    const int tid = threadIdx.x;
+    const int r_beg = blockIdx.x * rpb, r_end = min(m, r_beg + rpb);
+    double acc[NP];
+#pragma unroll
+    for (int u = 0; u < NP; ++u) acc[u] = 0.0;
+    for (int r0 = r_beg; r0 < r_end; r0 += 32) {
+        for (int e = tid; e < 32 * KP; e += 256) {
+            const int br = e / KP, l = e % KP, r = r0 + br;
+            Ys[br][l] = (r < r_end && l < k) ? Y[(size_t)r * k + l] : 0.0f;
         }
-        std::vector<std::thread> th;
-        const int per = (c1 - c0 + n_thr - 1) / n_thr;
-        for (int t = 0; t < n_thr; ++t) {
-            const int b = c0 + t * per, e = std::min(c1, b + per);
-            if (b >= e) break;
-            th.emplace_back([&, b, e] {
-                for (int c = b; c < e; ++c) fn(c);
-            });
+        __syncthreads();
+        for (int br = 0; br < 32; ++br) {
+#pragma unroll
+            for (int u = 0; u < NP; ++u) {
+                const int p = tid + 256 * u;
+                acc[u] += (double)Ys[br][p / KP] * (double)Ys[br][p % KP];
+            }
         }
-        for (auto& t : th) t.join();
-    };
-    for (int j = 0; j < n; ++j) {
-        double* v = &a[(size_t)j * m];
-        double nrm = 0.0;
-        for (int i = j; i < m; ++i) nrm += v[i] * v[i];
-        nrm = std::sqrt(nrm);
-        if (nrm == 0.0) continue;  // a zero column: no reflection
-        const double alpha = v[j] >= 0.0 ? -nrm : nrm;
-        v[j] -= alpha;
-        double vv = 0.0;
-        for (int i = j; i < m; ++i) vv += v[i] * v[i];
-        beta[j] = 2.0 / vv;
-        parallel_cols(j + 1, n, [&](int c) {
-            double* col = &a[(size_t)c * m];
-            double dot = 0.0;
-            for (int i = j; i < m; ++i) dot += v[i] * col[i];
-            const double f = beta[j] * dot;
-            for (int i = j; i < m; ++i) col[i] -= f * v[i];
-        });
+        __syncthreads();
     }
-    // Q = H_0 ... H_{n-1} [I; 0], applied from the last reflection; columns below c < j stay zero
-    for (int c = 0; c < n; ++c) q[(size_t)c * m + c] = 1.0;
-    for (int j = n - 1; j >= 0; --j) {
-        if (beta[j] == 0.0) continue;
-        const double* v = &a[(size_t)j * m];
-        parallel_cols(j, n, [&](int c) {
-            double* col = &q[(size_t)c * m];
-            double dot = 0.0;
-            for (int i = j; i < m; ++i) dot += v[i] * col[i];
-            const double f = beta[j] * dot;
-            for (int i = j; i < m; ++i) col[i] -= f * v[i];
-        });
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+        const int p = tid + 256 * u, a = p / KP, l = p % KP;
+        if (a < k && l < k) atomicAdd(&G[(size_t)a * k + l], acc[u]);
     }
-    for (int i = 0; i < m; ++i)
-        for (int j = 0; j < n; ++j) {
-            const double x = q[(size_t)j * m + i];
-            if (Q) Q[(size_t)i * n + j] = x;
-            Qf[(size_t)i * n + j] = (float)x;
-        }
+}
+
+hipError_t gram(const float* Y, int m, int k, double* G, hipStream_t st) {
+    hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<float*>(G), (size_t)2 * k * k);
+    const int blocks = std::max(1, std::min(256, (m + 31) / 32));
+    const int rpb = ((m + blocks - 1) / blocks + 31) / 32 * 32;
+    const int nb = (m + rpb - 1) / rpb;
+    if (k <= 32) hipLaunchKernelGGL(gram_kernel<32>, dim3(nb), dim3(256), 0, st, Y, m, k, rpb, G);
+    else if (k <= 64) hipLaunchKernelGGL(gram_kernel<64>, dim3(nb), dim3(256), 0, st, Y, m, k, rpb, G);
+    else hipLaunchKernelGGL(gram_kernel<128>, dim3(nb), dim3(256), 0, st, Y, m, k, rpb, G);
+    return hipGetLastError();
+}
+
+// Host: eigen-decomposition of the symmetric k x k matrix G (double, from the device) into
+// ascending eigenvalues lam and eigenvector columns V (row-major [k][k]).  Returns false when
+// the iteration does not converge.
+bool host_eigen(const std::vector<double>& Gh, int k, std::vector<double>& lam, std::vector<double>& V) {
+    std::vector<double> A(Gh);
+    for (int a = 0; a < k; ++a)  // symmetrize the float64 sums (their order differs per entry)
+        for (int b = a + 1; b < k; ++b) A[(size_t)a * k + b] = A[(size_t)b * k + a] = 0.5 * (A[(size_t)a * k + b] + A[(size_t)b * k + a]);
+    lam.resize(k);
+    V.resize((size_t)k * k);
+    return symmetric_eigen(A.data(), k, lam.data(), V.data()) == 0;
 }
 
 }  // namespace
@@ -334,86 +329,107 @@ hipError_t launch_sub_lowrank(float* E, int d_out, int d_in, const float* A, con
     return hipGetLastError();
 }
 
-// device workspace: Y / Q [d_in][k], Z / Q~ [d_out][k] (float32)
+// device workspace (float32 unless noted): Y, Q [d_in][k]; Z, Q~ [d_out][k]; T [max(d_in,
+// d_out)][k]; G [k][k] double; S [k][k]
 size_t lowrank_workspace_bytes(int d_out, int d_in, int k) {
-    return ((size_t)2 * d_in * k + (size_t)2 * d_out * k) * sizeof(float);
+    return align256((size_t)2 * d_in * k * 4) + align256((size_t)2 * d_out * k * 4) +
+           align256((size_t)std::max(d_in, d_out) * k * 4) + align256((size_t)k * k * 8) + align256((size_t)k * k * 4);
 }
 
 hipError_t lowrank_fit(const float* E, int d_out, int d_in, const float* w, const float* omega, int k, int rank,
                        int power_iters, float* A, float* B, double* sigma, void* ws, hipStream_t st) {
-    float* Yd = static_cast<float*>(ws);
+    char* p = static_cast<char*>(ws);
+    float* Yd = reinterpret_cast<float*>(p);
     float* Qd = Yd + (size_t)d_in * k;
-    float* Zd = Qd + (size_t)d_in * k;
+    p += align256((size_t)2 * d_in * k * 4);
+    float* Zd = reinterpret_cast<float*>(p);
     float* Qtd = Zd + (size_t)d_out * k;
-    std::vector<float> hf((size_t)std::max(d_in, d_out) * k), qf((size_t)std::max(d_in, d_out) * k);
-    std::vector<double> Qh((size_t)d_in * k), Zh((size_t)d_out * k);
+    p += align256((size_t)2 * d_out * k * 4);
+    float* Td = reinterpret_cast<float*>(p);
+    p += align256((size_t)std::max(d_in, d_out) * k * 4);
+    double* Gd = reinterpret_cast<double*>(p);
+    p += align256((size_t)k * k * 8);
+    float* Sd = reinterpret_cast<float*>(p);
+    std::vector<double> Gh((size_t)k * k), lam, V;
+    std::vector<float> Sh((size_t)k * k);
     hipError_t e;
-#define QE_TRY(expr)                          \
-    do {                                      \
+#define QE_TRY(expr)                              \
+    do {                                          \
         if ((e = (expr)) != hipSuccess) return e; \
     } while (0)
-    // orthonormal basis of a device [m][k] matrix, back on the device in `dst`
-    auto orth = [&](const float* src, int m, float* dst, double* keep) -> hipError_t {
+    // Gram matrix of a device [m][kk] matrix -> host eigen-decomposition
+    auto gram_eigen = [&](const float* X, int m) -> hipError_t {
         hipError_t r;
-        if ((r = hipMemcpyAsync(hf.data(), src, (size_t)m * k * sizeof(float), hipMemcpyDeviceToHost, st)) != hipSuccess)
-            return r;
+        if ((r = gram(X, m, k, Gd, st)) != hipSuccess) return r;
+        if ((r = hipMemcpyAsync(Gh.data(), Gd, (size_t)k * k * 8, hipMemcpyDeviceToHost, st)) != hipSuccess) return r;
         if ((r = hipStreamSynchronize(st)) != hipSuccess) return r;
-        householder_q(hf.data(), m, k, keep, qf.data());
-        if ((r = hipMemcpyAsync(dst, qf.data(), (size_t)m * k * sizeof(float), hipMemcpyHostToDevice, st)) != hipSuccess)
-            return r;
-        return hipStreamSynchronize(st);  // qf is reused by the next call
+        return host_eigen(Gh, k, lam, V) ? hipSuccess : hipErrorNotSupported;
+    };
+    // dst = src S with the k x k matrix S on the device (dst may not alias src)
+    auto apply = [&](const float* src, int m, int cols, float* dst) -> hipError_t {
+        hipError_t r;
+        if ((r = hipMemcpyAsync(Sd, Sh.data(), (size_t)k * cols * 4, hipMemcpyHostToDevice, st)) != hipSuccess) return r;
+        if ((r = thin(false, src, m, k, Sd, cols, nullptr, dst, st)) != hipSuccess) return r;
+        return hipStreamSynchronize(st);  // Sh is refilled by the next step
+    };
+    // orthonormal basis of the columns of src [m][k], written to dst (may alias src)
+    auto orth = [&](const float* src, int m, float* dst) -> hipError_t {
+        hipError_t r;
+        const float* in = src;
+        for (int pass = 0; pass < 2; ++pass) {
+            if ((r = gram_eigen(in, m)) != hipSuccess) return r;
+            const double top = std::max(lam[k - 1], 0.0);
+            for (int a = 0; a < k; ++a)
+                for (int i = 0; i < k; ++i)
+                    Sh[(size_t)a * k + i] = lam[i] > 1e-11 * top ? (float)(V[(size_t)a * k + i] / std::sqrt(lam[i])) : 0.0f;
+            float* out = pass == 0 ? Td : dst;
+            if ((r = apply(in, m, k, out)) != hipSuccess) return r;
+            in = out;
+        }
+        return hipSuccess;
     };
     QE_TRY(thin(true, E, d_out, d_in, omega, k, w, Yd, st));  // Y = M omega
-    QE_TRY(orth(Yd, d_in, Qd, Qh.data()));
+    QE_TRY(orth(Yd, d_in, Qd));
     for (int it = 0; it < power_iters; ++it) {
         QE_TRY(thin(false, E, d_out, d_in, Qd, k, w, Zd, st));  // M^T Q
-        QE_TRY(orth(Zd, d_out, Qtd, nullptr));
+        QE_TRY(orth(Zd, d_out, Qtd));
         QE_TRY(thin(true, E, d_out, d_in, Qtd, k, w, Yd, st));  // M Q~
-        QE_TRY(orth(Yd, d_in, Qd, Qh.data()));
+        QE_TRY(orth(Yd, d_in, Qd));
     }
     QE_TRY(thin(false, E, d_out, d_in, Qd, k, w, Zd, st));  // Z = M^T Q = B^T
-    QE_TRY(hipMemcpyAsync(hf.data(), Zd, (size_t)d_out * k * sizeof(float), hipMemcpyDeviceToHost, st));
-    QE_TRY(hipStreamSynchronize(st));
-#undef QE_TRY
-    for (size_t i = 0; i < (size_t)d_out * k; ++i) Zh[i] = hf[i];
-
-    // B B^T = Z^T Z = U~ S^2 U~^T (eigenvalues ascending from the solver)
-    std::vector<double> G((size_t)k * k, 0.0), lam(k), Ut((size_t)k * k);
-    for (int i = 0; i < d_out; ++i) {
-        const double* z = &Zh[(size_t)i * k];
-        for (int a = 0; a < k; ++a)
-            for (int b = 0; b <= a; ++b) G[(size_t)a * k + b] += z[a] * z[b];
+    // B B^T = Z^T Z = U~ S^2 U~^T (ascending); U = Q U~, V = Z U~ S^-1
+    QE_TRY(gram_eigen(Zd, d_out));
+    std::vector<double> root(rank), inv(rank);
+    for (int l = 0; l < rank; ++l) {
+        const double sg = std::sqrt(std::max(lam[k - 1 - l], 0.0));
+        sigma[l] = sg;
+        root[l] = std::sqrt(sg);
+        inv[l] = sg > 0.0 ? root[l] / sg : 0.0;
     }
+    // U_r S_r^(1/2) = Q (U~ S^(1/2)) -> Yd [d_in][rank]; V_r S_r^(1/2) = Z (U~ S^(-1/2)) -> Qtd [d_out][rank]
     for (int a = 0; a < k; ++a)
-        for (int b = a + 1; b < k; ++b) G[(size_t)a * k + b] = G[(size_t)b * k + a];
-    if (symmetric_eigen(G.data(), k, lam.data(), Ut.data()) != 0) return hipErrorNotSupported;  // no convergence
-    std::vector<float> wv;
+        for (int l = 0; l < rank; ++l) Sh[(size_t)a * rank + l] = (float)(V[(size_t)a * k + (k - 1 - l)] * root[l]);
+    QE_TRY(apply(Qd, d_in, rank, Yd));
+    for (int a = 0; a < k; ++a)
+        for (int l = 0; l < rank; ++l) Sh[(size_t)a * rank + l] = (float)(V[(size_t)a * k + (k - 1 - l)] * inv[l]);
+    QE_TRY(apply(Zd, d_out, rank, Qtd));
+    std::vector<float> us((size_t)d_in * rank), vs((size_t)d_out * rank), wv;
+    QE_TRY(hipMemcpyAsync(us.data(), Yd, us.size() * 4, hipMemcpyDeviceToHost, st));
+    QE_TRY(hipMemcpyAsync(vs.data(), Qtd, vs.size() * 4, hipMemcpyDeviceToHost, st));
     if (w) {
         wv.resize(d_in);
-        if ((e = hipMemcpyAsync(wv.data(), w, (size_t)d_in * sizeof(float), hipMemcpyDeviceToHost, st)) != hipSuccess)
-            return e;
-        if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
+        QE_TRY(hipMemcpyAsync(wv.data(), w, (size_t)d_in * 4, hipMemcpyDeviceToHost, st));
     }
-    std::vector<double> u(d_in), v(d_out);
-    for (int l = 0; l < rank; ++l) {
-        const int c = k - 1 - l;  // l-th largest
-        const double s2 = std::max(lam[c], 0.0), sg = std::sqrt(s2), root = std::sqrt(sg);
-        sigma[l] = sg;
-        for (int j = 0; j < d_in; ++j) {
-            double acc = 0.0;
-            for (int a = 0; a < k; ++a) acc += Qh[(size_t)j * k + a] * Ut[(size_t)a * k + c];
-            const double wj = w ? (double)wv[j] : 1.0;
-            A[(size_t)j * rank + l] = wj > 0.0 ? (float)(acc / wj * root) : 0.0f;
-        }
-        for (int i = 0; i < d_out; ++i) {
-            double acc = 0.0;
-            for (int a = 0; a < k; ++a) acc += Zh[(size_t)i * k + a] * Ut[(size_t)a * k + c];
-            B[(size_t)l * d_out + i] = sg > 0.0 ? (float)(acc / sg * root) : 0.0f;
-        }
+    QE_TRY(hipStreamSynchronize(st));
+#undef QE_TRY
+    for (int j = 0; j < d_in; ++j) {
+        const float wj = w ? wv[j] : 1.0f;
+        for (int l = 0; l < rank; ++l) A[(size_t)j * rank + l] = wj > 0.0f ? us[(size_t)j * rank + l] / wj : 0.0f;
     }
+    for (int l = 0; l < rank; ++l)
+        for (int i = 0; i < d_out; ++i) B[(size_t)l * d_out + i] = vs[(size_t)i * rank + l];
     return hipSuccess;
 }
-
 
 size_t build_experts_workspace_bytes(int d_out, int d_in, int k, int r_max) {
     return align256((size_t)d_out * d_in * sizeof(float)) + align256(lowrank_workspace_bytes(d_out, d_in, k)) +
