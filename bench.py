@@ -752,8 +752,8 @@ def extras(torch, synth, qe, libqe, dev, peaks):
         "ms_per_fit": round(float(np.median(ts)) * 1e3 / fits, 1),
         "passes_over_E_per_fit": 2 * q_it + 2,
         "sigma_shared_top": [round(float(v), 5) for v in ex["sigma_s"][:4]],
-        "note": "wall clock of the synchronous entry point: GPU thin products over E (float32) and host "
-                "Householder QR / eigenproblem in double between them"}
+        "note": "wall clock of the synchronous entry point: GPU passes over E (float32), Gram matrices (float64) "
+                "and k x k products on the GPU, k x k eigenproblems on the host between them"}
     return out
 
 
