@@ -19,10 +19,11 @@
 // linears; float32 FMAs, LDS tiles, contraction split over workgroups with atomic adds), the
 // k x k Gram matrices X^T X (float64 sums) and the products X S with k x k matrices S.  The
 // host only solves k x k symmetric eigenproblems in double.  Orthonormalization is by the Gram
-// matrix, twice (the two-pass scheme of CholeskyQR2, Fukaya et al. 2014, with the eigenvalue
-// decomposition in place of the Cholesky factor): X = Y V diag(lambda)^(-1/2), directions whose
-// eigenvalue is below 1e-11 of the largest dropped as null (they give zero columns), then the
-// same on X, which restores orthogonality to working precision.
+// matrix (the scheme of CholeskyQR2, Fukaya et al. 2014, with the eigenvalue decomposition in
+// place of the Cholesky factor): X = Y V diag(lambda)^(-1/2), directions whose eigenvalue is
+// below 1e-11 of the largest dropped as null (they give zero columns), then, when the kept
+// eigenvalues span more than 1e4, the same on X, which restores orthogonality to working
+// precision.
 
 #include <algorithm>
 #include <cmath>
@@ -174,6 +175,203 @@ __global__ __launch_bounds__(256) void thin_kernel(const float* __restrict__ E, 
     }
 }
 
+// ------------------------------------------------------- passes over E (matrix cores)
+// The two products that read the whole of E, on v_mfma_f32_16x16x4_f32 (float32 in, float32
+// sums): lane (i = lane % 16, g = lane / 16) supplies A[i][g] and B[g][i], and holds
+// D[4g + r][i].  Each workgroup (4 waves) reads a contiguous slice of E once; the k-column
+// operand is staged in LDS (rows padded against bank conflicts) and shared by the waves.  The
+// contraction is split over gridDim.y into long ranges, so few partial sums meet in the
+// atomic adds.  NL: 16-column blocks of the k columns (k <= 16 NL).
+typedef float v4f_t __attribute__((ext_vector_type(4)));
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+constexpr int PX_ROWS = 64;  // E rows per stage of the M X pass
+constexpr int PT_COLS = 64;  // E columns per stage of the M^T X pass
+
+// Y[a][l] += w[a] sum_b E[b][a] X[b][l]: a over d_in (a wave owns 32 consecutive a, two
+// 16-blocks, as float2 per lane: a = a0 + 2 i + j for block j), b over the E rows of the split.
+// The next stage's E values and X rows are loaded into registers while the current stage's
+// MFMAs run; X goes through two LDS buffers (one barrier per stage).
+template <int NL, bool VEC>
+__global__ __launch_bounds__(256) void pass_mx_kernel(const float* __restrict__ E, int d_out, int d_in,
+                                                      const float* __restrict__ X, int k, const float* __restrict__ w,
+                                                      int bpb, float* __restrict__ Y) {
+    constexpr int LD = NL * 16 + 4;
+    constexpr int NS = PX_ROWS / 4;                        // MFMA K steps per stage
+    constexpr int XR = (PX_ROWS * NL * 16 + 255) / 256;    // X values per thread and stage
+    __shared__ float Xs[2][PX_ROWS][LD];
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    const int a0 = (blockIdx.x * 4 + wid) * 32;
+    const int b_beg = blockIdx.y * bpb, b_end = min(d_out, b_beg + bpb);
+    const int a = a0 + 2 * li;
+    v4f_t acc[2][NL];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int lb = 0; lb < NL; ++lb) acc[j][lb] = v4f_t{0, 0, 0, 0};
+    // Every load is unconditional at a clamped address and nothing uses its value before the
+    // next stage, so the loads of a stage are all in flight together.  Clamped E rows (b past the
+    // range) meet X rows that are zeroed in LDS, and clamped E columns (a past d_in) feed output
+    // rows that are never stored, so E needs no masking; X is masked when it is written to LDS.
+    const int a_lo = min(a, d_in - 1), a_hi = min(a + 1, d_in - 1);
+    const int a_v = min(a, d_in - 2);  // VEC (d_in even): an aligned pair inside the row
+    auto load = [&](int b0, v2f_t (&ev)[NS], float (&xr)[XR]) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const float* row = E + (size_t)min(b0 + 4 * s + lg, b_end - 1) * d_in;
+            if constexpr (VEC) {
+                ev[s] = *reinterpret_cast<const v2f_t*>(row + a_v);
+            } else {
+                ev[s][0] = row[a_lo];
+                ev[s][1] = row[a_hi];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < XR; ++u) {
+            const int e = tid + 256 * u, br = e / (NL * 16), l = e % (NL * 16);
+            xr[u] = X[(size_t)min(b0 + br, b_end - 1) * k + min(l, k - 1)];
+        }
+    };
+    v2f_t ev[NS], en[NS];
+    float xr[XR], xn[XR];
+    load(b_beg, en, xn);
+    int buf = 0;
+    for (int b0 = b_beg; b0 < b_end; b0 += PX_ROWS) {
+#pragma unroll
+        for (int s = 0; s < NS; ++s) ev[s] = en[s];
+#pragma unroll
+        for (int u = 0; u < XR; ++u) xr[u] = xn[u];
+#pragma unroll
+        for (int u = 0; u < XR; ++u) {
+            const int e = tid + 256 * u, br = e / (NL * 16), l = e % (NL * 16);
+            if (e < PX_ROWS * NL * 16) Xs[buf][br][l] = (b0 + br < b_end && l < k) ? xr[u] : 0.0f;
+        }
+        __syncthreads();  // also orders this buffer's previous reads (two stages ago) before the writes above
+        if (b0 + PX_ROWS < b_end) load(b0 + PX_ROWS, en, xn);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+#pragma unroll
+            for (int lb = 0; lb < NL; ++lb) {
+                const float bv = Xs[buf][4 * s + lg][16 * lb + li];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[j][lb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ev[s][j], bv, acc[j][lb], 0, 0, 0);
+            }
+        }
+        buf ^= 1;
+    }
+    // block j, row 4 lg + r <-> a = a0 + 2 (4 lg + r) + j; column 16 lb + li
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ao = a0 + 2 * (4 * lg + r) + j;
+            if (ao >= d_in) continue;
+            const float wa = w ? w[ao] : 1.0f;
+#pragma unroll
+            for (int lb = 0; lb < NL; ++lb) {
+                const int l = 16 * lb + li;
+                if (l < k) atomicAdd(&Y[(size_t)ao * k + l], acc[j][lb][r] * wa);
+            }
+        }
+}
+
+// Z[a][l] += sum_b E[a][b] w[b] Q[b][l]: a over d_out (a wave owns 32 rows, two 16-blocks),
+// b over the E columns of the split, 16 per MFMA group: lane (i, g) loads E[row][b0 + 4 g ..
+// + 3] as float4 and MFMA q of the group takes component q (K slot g <-> b = b0 + 4 g + q).
+// Pipelined like pass_mx_kernel.
+template <int NL, bool VEC>
+__global__ __launch_bounds__(256) void pass_mtx_kernel(const float* __restrict__ E, int d_out, int d_in,
+                                                       const float* __restrict__ Q, int k, const float* __restrict__ w,
+                                                       int bpb, float* __restrict__ Z) {
+    constexpr int LD = NL * 16 + 4;
+    constexpr int NC = PT_COLS / 16;                        // MFMA groups per stage
+    constexpr int QR = (PT_COLS * NL * 16 + 255) / 256;     // Q values per thread and stage
+    __shared__ float Qs[2][PT_COLS][LD];
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, li = lane & 15, lg = lane >> 4;
+    const int a0 = (blockIdx.x * 4 + wid) * 32;
+    const int b_beg = blockIdx.y * bpb, b_end = min(d_in, b_beg + bpb);
+    v4f_t acc[2][NL];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int lb = 0; lb < NL; ++lb) acc[j][lb] = v4f_t{0, 0, 0, 0};
+    const float* rows[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) rows[j] = E + (size_t)min(a0 + 16 * j + li, d_out - 1) * d_in;
+    // unconditional loads at clamped addresses whose values are used only at the next stage
+    // (see pass_mx_kernel): clamped columns meet Q rows zeroed in LDS, clamped rows feed output
+    // rows never stored; Q is masked and scaled by w when it is written to LDS.  The vector form
+    // needs d_in % 4 == 0, so a clamped column stays aligned.
+    auto load = [&](int b0, v4f_t (&ev)[NC][2], float (&qr)[QR], float (&wr)[QR]) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int b = b0 + 16 * c + 4 * lg;
+                if constexpr (VEC) {
+                    ev[c][j] = *reinterpret_cast<const v4f_t*>(rows[j] + min(b, d_in - 4));
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) ev[c][j][q] = rows[j][min(b + q, d_in - 1)];
+                }
+            }
+#pragma unroll
+        for (int u = 0; u < QR; ++u) {
+            const int e = tid + 256 * u, br = e / (NL * 16), l = e % (NL * 16);
+            const int bc = min(b0 + br, b_end - 1);
+            qr[u] = Q[(size_t)bc * k + min(l, k - 1)];
+            wr[u] = w != nullptr ? w[bc] : 1.0f;
+        }
+    };
+    v4f_t ev[NC][2], en[NC][2];
+    float qr[QR], qn[QR], wr[QR], wn[QR];
+    load(b_beg, en, qn, wn);
+    int buf = 0;
+    for (int b0 = b_beg; b0 < b_end; b0 += PT_COLS) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) ev[c][j] = en[c][j];
+#pragma unroll
+        for (int u = 0; u < QR; ++u) {
+            qr[u] = qn[u];
+            wr[u] = wn[u];
+        }
+#pragma unroll
+        for (int u = 0; u < QR; ++u) {
+            const int e = tid + 256 * u, br = e / (NL * 16), l = e % (NL * 16);
+            if (e < PT_COLS * NL * 16) Qs[buf][br][l] = (b0 + br < b_end && l < k) ? qr[u] * wr[u] : 0.0f;
+        }
+        __syncthreads();  // also orders this buffer's previous reads (two stages ago) before the writes above
+        if (b0 + PT_COLS < b_end) load(b0 + PT_COLS, en, qn, wn);
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int lb = 0; lb < NL; ++lb) {
+                    const float bv = Qs[buf][16 * c + 4 * lg + q][16 * lb + li];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[j][lb] = __builtin_amdgcn_mfma_f32_16x16x4f32(ev[c][j][q], bv, acc[j][lb], 0, 0, 0);
+                }
+        buf ^= 1;
+    }
+    // block j, row 4 lg + r <-> a = a0 + 16 j + 4 lg + r; column 16 lb + li
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int ao = a0 + 16 * j + 4 * lg + r;
+            if (ao >= d_out) continue;
+#pragma unroll
+            for (int lb = 0; lb < NL; ++lb) {
+                const int l = 16 * lb + li;
+                if (l < k) atomicAdd(&Z[(size_t)ao * k + l], acc[j][lb][r]);
+            }
+        }
+}
+
 __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ p, size_t n) {
     for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.0f;
 }
@@ -241,6 +439,47 @@ hipError_t thin(bool trans, const float* E, int d_out, int d_in, const float* S,
     else if (k <= 64) QE_THIN(64);
     else QE_THIN(128);
 #undef QE_THIN
+    return hipGetLastError();
+}
+
+// One pass over E on the matrix cores: trans ? (C = diag(w) E^T S, [d_in][k]) : (C = E diag(w) S,
+// [d_out][k]); C zeroed first.  About 512 workgroups, each with a long contraction range.
+hipError_t pass_over_e(bool trans, const float* E, int d_out, int d_in, const float* S, int k, const float* w, float* C,
+                       hipStream_t st) {
+    const int n_a = trans ? d_in : d_out, n_b = trans ? d_out : d_in;
+    const size_t nc = (size_t)n_a * k;
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)std::min<size_t>((nc + 255) / 256, 4096)), dim3(256), 0, st, C, nc);
+    const int step = trans ? PX_ROWS : PT_COLS;
+    const int tiles = (n_a + 127) / 128;
+    const int steps = (n_b + step - 1) / step;
+    const int splits = std::max(1, std::min((512 + tiles - 1) / tiles, steps / 4));
+    const int bpb = (steps + splits - 1) / splits * step;
+    const dim3 grid(tiles, (n_b + bpb - 1) / bpb);
+    const int nl = (k + 15) / 16;
+#define QE_PASS(NLV)                                                                                          \
+    do {                                                                                                      \
+        if (trans) {                                                                                          \
+            if (d_in % 2 == 0)                                                                                \
+                hipLaunchKernelGGL((pass_mx_kernel<NLV, true>), grid, dim3(256), 0, st, E, d_out, d_in, S, k, w, bpb, C); \
+            else                                                                                              \
+                hipLaunchKernelGGL((pass_mx_kernel<NLV, false>), grid, dim3(256), 0, st, E, d_out, d_in, S, k, w, bpb, C); \
+        } else if (d_in % 4 == 0) {                                                                           \
+            hipLaunchKernelGGL((pass_mtx_kernel<NLV, true>), grid, dim3(256), 0, st, E, d_out, d_in, S, k, w, bpb, C); \
+        } else {                                                                                              \
+            hipLaunchKernelGGL((pass_mtx_kernel<NLV, false>), grid, dim3(256), 0, st, E, d_out, d_in, S, k, w, bpb, C); \
+        }                                                                                                     \
+    } while (0)
+    switch (nl) {
+        case 1: QE_PASS(1); break;
+        case 2: QE_PASS(2); break;
+        case 3: QE_PASS(3); break;
+        case 4: QE_PASS(4); break;
+        case 5: QE_PASS(5); break;
+        case 6: QE_PASS(6); break;
+        case 7: QE_PASS(7); break;
+        default: QE_PASS(8); break;
+    }
+#undef QE_PASS
     return hipGetLastError();
 }
 
@@ -372,31 +611,39 @@ hipError_t lowrank_fit(const float* E, int d_out, int d_in, const float* w, cons
         if ((r = thin(false, src, m, k, Sd, cols, nullptr, dst, st)) != hipSuccess) return r;
         return hipStreamSynchronize(st);  // Sh is refilled by the next step
     };
-    // orthonormal basis of the columns of src [m][k], written to dst (may alias src)
+    // orthonormal basis of the columns of src [m][k], written to dst (may alias src).  The
+    // second pass is needed only when the kept eigenvalues span more than 1e4 (a condition
+    // number above 100, where float32 rounding of the first product leaves columns measurably
+    // non-orthogonal); otherwise the first product goes straight to dst.
     auto orth = [&](const float* src, int m, float* dst) -> hipError_t {
         hipError_t r;
         const float* in = src;
         for (int pass = 0; pass < 2; ++pass) {
             if ((r = gram_eigen(in, m)) != hipSuccess) return r;
             const double top = std::max(lam[k - 1], 0.0);
+            double low = top;
+            for (int i = 0; i < k; ++i)
+                if (lam[i] > 1e-11 * top) low = std::min(low, lam[i]);
             for (int a = 0; a < k; ++a)
                 for (int i = 0; i < k; ++i)
                     Sh[(size_t)a * k + i] = lam[i] > 1e-11 * top ? (float)(V[(size_t)a * k + i] / std::sqrt(lam[i])) : 0.0f;
-            float* out = pass == 0 ? Td : dst;
+            const bool last = pass == 1 || low >= 1e-4 * top;
+            float* out = last ? dst : Td;
             if ((r = apply(in, m, k, out)) != hipSuccess) return r;
+            if (last) break;
             in = out;
         }
         return hipSuccess;
     };
-    QE_TRY(thin(true, E, d_out, d_in, omega, k, w, Yd, st));  // Y = M omega
+    QE_TRY(pass_over_e(true, E, d_out, d_in, omega, k, w, Yd, st));  // Y = M omega
     QE_TRY(orth(Yd, d_in, Qd));
     for (int it = 0; it < power_iters; ++it) {
-        QE_TRY(thin(false, E, d_out, d_in, Qd, k, w, Zd, st));  // M^T Q
+        QE_TRY(pass_over_e(false, E, d_out, d_in, Qd, k, w, Zd, st));  // M^T Q
         QE_TRY(orth(Zd, d_out, Qtd));
-        QE_TRY(thin(true, E, d_out, d_in, Qtd, k, w, Yd, st));  // M Q~
+        QE_TRY(pass_over_e(true, E, d_out, d_in, Qtd, k, w, Yd, st));  // M Q~
         QE_TRY(orth(Yd, d_in, Qd));
     }
-    QE_TRY(thin(false, E, d_out, d_in, Qd, k, w, Zd, st));  // Z = M^T Q = B^T
+    QE_TRY(pass_over_e(false, E, d_out, d_in, Qd, k, w, Zd, st));  // Z = M^T Q = B^T
     // B B^T = Z^T Z = U~ S^2 U~^T (ascending); U = Q U~, V = Z U~ S^-1
     QE_TRY(gram_eigen(Zd, d_out));
     std::vector<double> root(rank), inv(rank);
