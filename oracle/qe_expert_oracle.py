@@ -26,7 +26,13 @@ Readings where the pages leave a step open (each also listed in the design notes
   * The SE approximates the whole E; the RE of cluster g approximates the residual
     E_1 = E - (A_s B_s)^T on the input channels of that cluster only (weights c_j on the
     cluster, 0 elsewhere), so its A rows outside the cluster are zero.
-  * The router fit is not covered here.
+  * The router predicts, for each routed expert, the error that would remain on a token if that
+    expert were used, and the token takes the expert with the smallest prediction (DeepRead,
+    "Method", REs; WisPaper post "[CVPR 2025] Quant Experts: Adapting PTQ to the Heterogeneity
+    of Vision-Language Tokens", section "Critical Insight": a prediction of the absolute mean
+    error).  Its target for token t and expert g is the mean absolute residual over the
+    output channels, mean_i |x_t (E_1^T - A_g B_g)|_i, and R is the ridge least-squares fit
+    (X^T X + lam I) R = X^T target with lam = ridge * trace(X^T X) / d_in.
 parity pinned: every function below has CPU pins in tests/test_oracle_experts.py.
 """
 
@@ -125,3 +131,22 @@ def build_experts(W_f: np.ndarray, s: Optional[np.ndarray], w_bits: int, c: np.n
         A_r[g], B_r[g], sig_r[g] = randomized_lowrank(E1, wg, omegas[1 + g], r_r, power_iters)
     out.update(A_s=A_s, B_s=B_s, sigma_s=sig_s, A_r=A_r, B_r=B_r, sigma_r=sig_r, E1=E1)
     return out
+
+
+def router_targets(E1: np.ndarray, X: np.ndarray, A_r: np.ndarray, B_r: np.ndarray) -> np.ndarray:
+    """target[t, g] = mean_i |x_t (E_1^T - A_g B_g)|_i: the error expert g leaves on token t."""
+    X = np.asarray(X, dtype=np.float64)
+    base = X @ np.asarray(E1, dtype=np.float64).T
+    out = np.empty((X.shape[0], A_r.shape[0]))
+    for g in range(A_r.shape[0]):
+        res = base - (X @ np.asarray(A_r[g], dtype=np.float64)) @ np.asarray(B_r[g], dtype=np.float64)
+        out[:, g] = np.mean(np.abs(res), axis=1)
+    return out
+
+
+def router_fit(X: np.ndarray, target: np.ndarray, ridge: float) -> np.ndarray:
+    """Ridge least squares: R = (X^T X + lam I)^-1 X^T target, lam = ridge * trace(X^T X) / d_in."""
+    X = np.asarray(X, dtype=np.float64)
+    G = X.T @ X
+    lam = ridge * np.trace(G) / X.shape[1]
+    return np.linalg.solve(G + lam * np.eye(X.shape[1]), X.T @ np.asarray(target, dtype=np.float64))

@@ -177,3 +177,45 @@ def test_build_experts_structure():
         assert after < before
         if len(ch) <= r_r:  # a cluster no wider than the rank is reconstructed exactly
             assert after < 1e-10 * before
+
+
+def test_router_targets_hand_example():
+    # one token x = [1, 2], E_1 = [[1, 0], [0, 1]] (so x E_1^T = [1, 2]); expert 0 reproduces E_1^T
+    # exactly (A B = I): residual 0; expert 1 is zero: residual [1, 2], mean 1.5; expert 2 has
+    # A B = [[0, 0], [0, 2]]: residual [1, 2 - 4] = [1, -2], mean 1.5 as well
+    Xm = np.array([[1.0, 2.0]])
+    E1 = np.eye(2)
+    A = np.array([np.eye(2), np.zeros((2, 2)), np.diag([0.0, 2.0])])
+    B = np.array([np.eye(2), np.zeros((2, 2)), np.eye(2)])
+    assert np.allclose(X.router_targets(E1, Xm, A, B), [[0.0, 1.5, 1.5]])
+
+
+def test_router_fit_recovers_a_consistent_system():
+    # target = X R* exactly: with a vanishing ridge the fit returns R*; its gradient vanishes
+    rng = np.random.default_rng(30)
+    Xm = rng.standard_normal((200, 12))
+    Rs = rng.standard_normal((12, 4))
+    R = X.router_fit(Xm, Xm @ Rs, 1e-12)
+    assert np.allclose(R, Rs, atol=1e-8)
+    t = rng.standard_normal((200, 4))
+    for ridge in (0.0, 0.1):
+        R = X.router_fit(Xm, t, ridge)
+        lam = ridge * np.sum(Xm * Xm) / 12
+        grad = Xm.T @ (Xm @ R - t) + lam * R  # optimality of the ridge objective
+        assert np.max(np.abs(grad)) < 1e-9 * np.max(np.abs(Xm.T @ t))
+    # a large ridge shrinks the fit toward zero
+    assert np.max(np.abs(X.router_fit(Xm, t, 1e6))) < 1e-5
+
+
+def test_router_targets_rank_experts_by_their_residual():
+    # an expert that removes part of E_1 leaves less error on every token than one that does not
+    rng = np.random.default_rng(31)
+    d_out, d_in = 10, 16
+    E1 = rng.standard_normal((d_out, d_in))
+    U, S, Vt = np.linalg.svd(E1.T, full_matrices=False)
+    A = np.array([U[:, :4] * S[:4], np.zeros((d_in, 4))])
+    B = np.array([Vt[:4], np.zeros((4, d_out))])
+    Xm = rng.standard_normal((50, d_in))
+    tg = X.router_targets(E1, Xm, A, B)
+    assert np.all(tg[:, 0] < tg[:, 1])
+    assert np.allclose(tg[:, 1], np.mean(np.abs(Xm @ E1.T), axis=1))
