@@ -744,6 +744,29 @@ def extras(torch, synth, qe, libqe, dev, peaks):
         ex = libqe.qe_build_experts(W_f, s_d, cfg.w_bits, cr, dep, labels, n_r, r_s, r_r, omegas, q_it, bws)
         ts.append(time.perf_counter() - t1)
         tr.append(t1 - t0)
+    # router: targets on the calibration tokens from the residual after the SE, then the ridge fit
+    E1 = torch.empty(spec.d_out, spec.d_in, device=dev)
+    libqe.qe_quant_error(W_f, s_d, cfg.w_bits, E1)
+    libqe.qe_sub_lowrank(E1, torch.from_numpy(ex["A_s"]).to(dev), torch.from_numpy(ex["B_s"]).to(dev))
+    A_r = torch.from_numpy(ex["A_r"]).to(dev)
+    B_r = torch.from_numpy(ex["B_r"]).to(dev)
+    tgt = torch.empty(cfg.T, n_r, device=dev)
+    tws = torch.empty(libqe.qe_router_targets_workspace_bytes(spec.d_out, spec.d_in, n_r, r_r), dtype=torch.uint8,
+                      device=dev)
+    fws = torch.empty(libqe.qe_router_fit_workspace_bytes(cfg.T, spec.d_in, n_r), dtype=torch.uint8, device=dev)
+    t_tg, t_fit = [], []
+    for _ in range(2):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        libqe.qe_router_targets(E1, x, A_r, B_r, tgt, tws)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        R_fit, iters = libqe.qe_router_fit(x, tgt, 1e-2, 500, 1e-5, fws)
+        t_fit.append(time.perf_counter() - t1)
+        t_tg.append(t1 - t0)
+    pred = (x.float() @ torch.from_numpy(R_fit).to(dev)).argmin(1)
+    agree = float((pred == tgt.argmin(1)).float().mean())
+    del E1, A_r, B_r, fws, tws
     fits = 1 + n_r
     out["expert_build_internvl2_8b_down"] = {
         "d_in": spec.d_in, "d_out": spec.d_out, "w_bits": cfg.w_bits, "r_shared": r_s, "n_routed": n_r,
@@ -751,6 +774,9 @@ def extras(torch, synth, qe, libqe, dev, peaks):
         "channel_rms_ms": round(float(np.median(tr)) * 1e3, 3), "build_ms": round(float(np.median(ts)) * 1e3, 1),
         "ms_per_fit": round(float(np.median(ts)) * 1e3 / fits, 1),
         "passes_over_E_per_fit": 2 * q_it + 2,
+        "router_targets_ms": round(float(np.median(t_tg)) * 1e3, 1),
+        "router_fit_ms": round(float(np.median(t_fit)) * 1e3, 1), "router_fit_cg_iters": iters,
+        "router_ridge": 1e-2, "router_argmin_agreement_on_calibration": round(agree, 4),
         "sigma_shared_top": [round(float(v), 5) for v in ex["sigma_s"][:4]],
         "note": "wall clock of the synchronous entry point: GPU passes over E (float32), Gram matrices (float64) "
                 "and k x k products on the GPU, k x k eigenproblems on the host between them"}

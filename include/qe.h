@@ -319,7 +319,7 @@ int qe_linear_cost(const qe_linear* lin, int32_t T, int32_t n_distinct_experts, 
  * diagonal, with the RMS of each input channel's calibration activations; the truncated SVD
  * is the randomized subspace iteration of Halko, Martinsson and Tropp ("Finding structure with
  * randomness", Algorithms 4.4 and 5.1) with the Gaussian test matrix supplied by the caller.
- * The router fit is not provided.
+ * The router fit is by ridge least squares on per-token targets (below).
  *
  * qe_quant_error: E = W_f - diag(s_w) q diag(1/s) (float32, device [d_out][d_in]) with the
  *   codes and row scales qe_pack_weights takes (same float32 arithmetic).  W_f device float32
@@ -369,6 +369,32 @@ int qe_build_experts(const float* W_f, const float* s, int32_t d_out, int32_t d_
                      int32_t r_shared, int32_t r_routed, const float* omegas, int32_t k, int32_t power_iters,
                      float* A_s, float* B_s, float* A_r, float* B_r, double* sigma_s, double* sigma_r, void* ws,
                      size_t ws_bytes, void* stream);
+
+/* Router fit (MCISLAB DeepRead summary, "Method", Routed Experts: the router estimates the error
+ * each routed expert would leave on a token and the token takes the smallest; WisPaper post
+ * "[CVPR 2025] Quant Experts: Adapting PTQ to the Heterogeneity of Vision-Language Tokens",
+ * section "Critical Analysis & Insight": an absolute mean error prediction).
+ * qe_router_targets: target[t][g] = mean_i |x_t (E_1^T - A_g B_g)|_i over the d_out outputs for
+ *   T calibration tokens x (device [T][d_in], QE_F32 or QE_BF16); E_1 device float32 [d_out][d_in]
+ *   (the error left after the shared expert); A_r device float32 [n_routed][d_in][r_routed], B_r
+ *   [n_routed][r_routed][d_out] (n_routed <= 16, r_routed <= 64); target device float32
+ *   [T][n_routed].  ws: device, qe_router_targets_workspace_bytes(...) bytes.  Enqueued.
+ * qe_router_fit: R = argmin |X R - target|^2 + lam |R|^2 with lam = ridge * |X|_F^2 / d_in, by
+ *   conjugate gradients on (X^T X + lam I) R = X^T target (one system per column), until every
+ *   column's residual is below tol times its right-hand side or after max_iters iterations.
+ *   x device [T][d_in] (QE_F32 / QE_BF16), target device float32 [T][n_routed]; R HOST float32
+ *   [d_in][n_routed] (the router, to be given to qe_prepare in bf16); *iters_done (optional)
+ *   receives the iterations taken.  ws: device, qe_router_fit_workspace_bytes(T, d_in, n_routed)
+ *   bytes (it holds a float32 copy of x).  Synchronizes `stream`.
+ */
+size_t qe_router_targets_workspace_bytes(int32_t d_out, int32_t d_in, int32_t n_routed, int32_t r_routed);
+int qe_router_targets(const float* E1, int32_t d_out, int32_t d_in, const void* x, int32_t x_dtype, int32_t T,
+                      const float* A_r, const float* B_r, int32_t n_routed, int32_t r_routed, float* target, void* ws,
+                      size_t ws_bytes, void* stream);
+size_t qe_router_fit_workspace_bytes(int32_t T, int32_t d_in, int32_t n_routed);
+int qe_router_fit(const void* x, int32_t x_dtype, int32_t T, int32_t d_in, const float* target, int32_t n_routed,
+                  double ridge, int32_t max_iters, double tol, float* R, int32_t* iters_done, void* ws, size_t ws_bytes,
+                  void* stream);
 
 /* ---------------------------------------------------------- measurement aids --
  * Not part of the QE computation: kernels whose duration, measured by the caller with

@@ -29,7 +29,7 @@ Readings where the pages leave a step open (each also listed in the design notes
   * The router predicts, for each routed expert, the error that would remain on a token if that
     expert were used, and the token takes the expert with the smallest prediction (DeepRead,
     "Method", REs; WisPaper post "[CVPR 2025] Quant Experts: Adapting PTQ to the Heterogeneity
-    of Vision-Language Tokens", section "Critical Insight": a prediction of the absolute mean
+    of Vision-Language Tokens", section "Critical Analysis & Insight": a prediction of the absolute mean
     error).  Its target for token t and expert g is the mean absolute residual over the
     output channels, mean_i |x_t (E_1^T - A_g B_g)|_i, and R is the ridge least-squares fit
     (X^T X + lam I) R = X^T target with lam = ridge * trace(X^T X) / d_in.

@@ -81,6 +81,10 @@ def _load():
         "qe_lowrank_fit": (ctypes.c_int, [P, I, I, P, P, I, I, I, P, P, P, P, Z, P]),
         "qe_build_experts_workspace_bytes": (Z, [I, I, I, I]),
         "qe_build_experts": (ctypes.c_int, [P, P, I, I, I, P, P, P, I, I, I, I, P, I, I, P, P, P, P, P, P, P, Z, P]),
+        "qe_router_targets_workspace_bytes": (Z, [I, I, I, I]),
+        "qe_router_targets": (ctypes.c_int, [P, I, I, P, I, I, P, P, I, I, P, P, Z, P]),
+        "qe_router_fit_workspace_bytes": (Z, [I, I, I]),
+        "qe_router_fit": (ctypes.c_int, [P, I, I, I, P, I, ctypes.c_double, I, ctypes.c_double, P, P, P, Z, P]),
         "qe_probe_mfma_i8": (ctypes.c_int, [P, I, I, I, D, P]),
         "qe_probe_mfma_bf16": (ctypes.c_int, [P, I, I, I, D, P]),
         "qe_probe_copy": (ctypes.c_int, [P, P, Z, P]),
@@ -100,7 +104,8 @@ EXPORTED = (
     "qe_probe_mfma_i8", "qe_probe_mfma_bf16", "qe_probe_copy", "qe_partition_channels", "qe_cooccur_workspace_bytes",
     "qe_cooccur", "qe_cluster_channels", "qe_quant_error", "qe_channel_rms_workspace_bytes", "qe_channel_rms",
     "qe_sub_lowrank", "qe_lowrank_workspace_bytes", "qe_lowrank_fit", "qe_build_experts_workspace_bytes",
-    "qe_build_experts",
+    "qe_build_experts", "qe_router_targets_workspace_bytes", "qe_router_targets", "qe_router_fit_workspace_bytes",
+    "qe_router_fit",
 )
 
 
@@ -335,6 +340,35 @@ def qe_build_experts(W_f, s, w_bits, c, dep_channels, labels, n_routed, r_shared
                                  _ptr(out["sigma_r"]), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "qe_build_experts")
     return out
+
+
+def qe_router_targets_workspace_bytes(d_out: int, d_in: int, n_routed: int, r_routed: int) -> int:
+    return _lib.qe_router_targets_workspace_bytes(d_out, d_in, n_routed, r_routed)
+
+
+def qe_router_targets(E1, x, A_r, B_r, target, ws, stream=None):
+    """Enqueue target[t, g] = mean_i |x_t (E1^T - A_g B_g)|_i (device tensors; A_r, B_r float32)."""
+    d_out, d_in = E1.shape
+    n_r, _, r_r = A_r.shape
+    _check(_lib.qe_router_targets(_ptr(E1), d_out, d_in, _ptr(x), _dtype_code(x), x.shape[0], _ptr(A_r), _ptr(B_r),
+                                  n_r, r_r, _ptr(target), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "qe_router_targets")
+
+
+def qe_router_fit_workspace_bytes(T: int, d_in: int, n_routed: int) -> int:
+    return _lib.qe_router_fit_workspace_bytes(T, d_in, n_routed)
+
+
+def qe_router_fit(x, target, ridge, max_iters, tol, ws, stream=None):
+    """Ridge least-squares router fit by conjugate gradients; returns (R host float32 [d_in, n_r], iterations)."""
+    T, d_in = x.shape
+    n_r = target.shape[1]
+    R = np.empty((d_in, n_r), np.float32)
+    it = ctypes.c_int32()
+    _check(_lib.qe_router_fit(_ptr(x), _dtype_code(x), T, d_in, _ptr(target), n_r, ridge, max_iters, tol, _ptr(R),
+                              ctypes.byref(it), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "qe_router_fit")
+    return R, it.value
 
 
 def qe_probe_mfma_i8(out, blocks, iters, operands=0, stream=None):

@@ -483,6 +483,115 @@ hipError_t pass_over_e(bool trans, const float* E, int d_out, int d_in, const fl
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ router fit
+constexpr int RT_TOK = 128;  // calibration tokens per chunk of the target computation
+
+// XT[j][t] = x[t0 + t][j] as float32, t < kc (32 x 32 tiles through LDS)
+__global__ __launch_bounds__(256) void transpose_chunk_kernel(const void* __restrict__ x, int x_dtype, int t0, int kc,
+                                                              int d_in, float* __restrict__ XT) {
+    __shared__ float tile[32][33];
+    const int j0 = blockIdx.x * 32, tt0 = blockIdx.y * 32, tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+    for (int r = ty; r < 32; r += 8) {
+        const int t = tt0 + r, j = j0 + tx;
+        float v = 0.0f;
+        if (t < kc && j < d_in) {
+            const size_t idx = (size_t)(t0 + t) * d_in + j;
+            v = x_dtype == QE_BF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(x)[idx] << 16)
+                                   : reinterpret_cast<const float*>(x)[idx];
+        }
+        tile[r][tx] = v;
+    }
+    __syncthreads();
+    for (int r = ty; r < 32; r += 8) {
+        const int j = j0 + r, t = tt0 + tx;
+        if (j < d_in && t < kc) XT[(size_t)j * kc + t] = tile[tx][r];
+    }
+}
+
+__global__ __launch_bounds__(256) void to_f32_kernel(const void* __restrict__ x, int x_dtype, size_t n,
+                                                     float* __restrict__ out) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        out[i] = x_dtype == QE_BF16 ? __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(x)[i] << 16)
+                                    : reinterpret_cast<const float*>(x)[i];
+}
+
+// target[t0 + t][g] = mean_i |Z[i][t] - sum_l B_g[l][i] U_g[t][l]|   (one workgroup per (t, g))
+__global__ __launch_bounds__(256) void router_target_kernel(const float* __restrict__ Z, int kc, int d_out,
+                                                            const float* __restrict__ B_r, int r_r,
+                                                            const float* __restrict__ U, int t0, int n_r,
+                                                            float* __restrict__ target) {
+    __shared__ float u[64];
+    __shared__ double red[256];
+    const int t = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+    if (tid < r_r) u[tid] = U[((size_t)g * kc + t) * r_r + tid];
+    __syncthreads();
+    const float* Bg = B_r + (size_t)g * r_r * d_out;
+    double acc = 0.0;
+    for (int i = tid; i < d_out; i += 256) {
+        float v = Z[(size_t)i * kc + t];
+        for (int l = 0; l < r_r; ++l) v -= Bg[(size_t)l * d_out + i] * u[l];
+        acc += fabs((double)v);
+    }
+    red[tid] = acc;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if (tid < h) red[tid] += red[tid + h];
+        __syncthreads();
+    }
+    if (tid == 0) target[(size_t)(t0 + t) * n_r + g] = (float)(red[0] / d_out);
+}
+
+// out[g] = sum_j a[j][g] b[j][g] (float64), one workgroup per column g of [d][n] matrices
+__global__ __launch_bounds__(256) void coldot_kernel(const float* __restrict__ a, const float* __restrict__ b, int d,
+                                                     int n, double* __restrict__ out) {
+    __shared__ double red[256];
+    const int g = blockIdx.x, tid = threadIdx.x;
+    double acc = 0.0;
+    for (int j = tid; j < d; j += 256) acc += (double)a[(size_t)j * n + g] * (double)b[(size_t)j * n + g];
+    red[tid] = acc;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if (tid < h) red[tid] += red[tid + h];
+        __syncthreads();
+    }
+    if (tid == 0) out[g] = red[0];
+}
+
+// sum of squares of n floats (float64), accumulated into *out (zeroed by the caller)
+__global__ __launch_bounds__(256) void sumsq_kernel(const float* __restrict__ a, size_t n, double* __restrict__ out) {
+    __shared__ double red[256];
+    double acc = 0.0;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        acc += (double)a[i] * (double)a[i];
+    red[threadIdx.x] = acc;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if (threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) atomicAdd(out, red[0]);
+}
+
+// conjugate-gradient updates on [d][n] matrices with per-column scalars (float64 on the device):
+//   mode 0: q += lam p;  mode 1: R += alpha p, r -= alpha q;  mode 2: p = r + beta p
+__global__ __launch_bounds__(256) void cg_update_kernel(int mode, int d, int n, double lam,
+                                                        const double* __restrict__ coef, float* __restrict__ R,
+                                                        float* __restrict__ r, float* __restrict__ p,
+                                                        float* __restrict__ q) {
+    const size_t total = (size_t)d * n;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+        const int g = (int)(i % n);
+        if (mode == 0) {
+            q[i] = (float)((double)q[i] + lam * p[i]);
+        } else if (mode == 1) {
+            R[i] = (float)((double)R[i] + coef[g] * p[i]);
+            r[i] = (float)((double)r[i] - coef[g] * q[i]);
+        } else {
+            p[i] = (float)((double)r[i] + coef[g] * p[i]);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ Gram matrices
 // G[a][l] += sum_r Y[r][a] Y[r][l] over the rows of blockIdx.x (Y float32 [m][k], G double
 // [k][k], zeroed by the caller); float64 products and sums.
@@ -731,6 +840,122 @@ hipError_t build_experts(const float* W_f, const float* s, int d_out, int d_in, 
     QE_TRY(hipStreamSynchronize(st));
 #undef QE_TRY
     return hipSuccess;
+}
+
+
+// ---------------------------------------------------------------- router targets and fit
+size_t router_targets_workspace_bytes(int d_out, int d_in, int n_r, int r_r) {
+    return align256((size_t)d_in * RT_TOK * 4) + align256((size_t)d_out * RT_TOK * 4) +
+           align256((size_t)n_r * RT_TOK * r_r * 4);
+}
+
+// target[t][g] = mean_i |x_t (E_1^T - A_g B_g)|_i for T calibration tokens, 128 at a time: one
+// pass over E_1 per chunk gives x E_1^T, then the tiny products x A_g and the reduction.
+hipError_t router_targets(const float* E1, int d_out, int d_in, const void* x, int x_dtype, int T, const float* A_r,
+                          const float* B_r, int n_r, int r_r, float* target, void* ws, hipStream_t st) {
+    char* p = static_cast<char*>(ws);
+    float* XT = reinterpret_cast<float*>(p);
+    p += align256((size_t)d_in * RT_TOK * 4);
+    float* Zc = reinterpret_cast<float*>(p);
+    p += align256((size_t)d_out * RT_TOK * 4);
+    float* U = reinterpret_cast<float*>(p);
+    hipError_t e;
+    for (int t0 = 0; t0 < T; t0 += RT_TOK) {
+        const int kc = std::min(RT_TOK, T - t0);
+        hipLaunchKernelGGL(transpose_chunk_kernel, dim3((d_in + 31) / 32, (kc + 31) / 32), dim3(256), 0, st, x,
+                           x_dtype, t0, kc, d_in, XT);
+        if ((e = pass_over_e(false, E1, d_out, d_in, XT, kc, nullptr, Zc, st)) != hipSuccess) return e;  // Z = E_1 X^T
+        for (int g = 0; g < n_r; ++g)  // U_g = X A_g  ([kc][r_r]; XT as a [d_in][kc] matrix)
+            if ((e = pass_over_e(true, XT, d_in, kc, A_r + (size_t)g * d_in * r_r, r_r, nullptr,
+                                 U + (size_t)g * kc * r_r, st)) != hipSuccess)
+                return e;
+        hipLaunchKernelGGL(router_target_kernel, dim3(kc, n_r), dim3(256), 0, st, Zc, kc, d_out, B_r, r_r, U, t0, n_r,
+                           target);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+size_t router_fit_workspace_bytes(int T, int d_in, int n_r) {
+    return align256((size_t)T * d_in * 4) + 5 * align256((size_t)d_in * n_r * 4) + align256((size_t)T * n_r * 4) +
+           align256(((size_t)n_r + 1) * 8);
+}
+
+// Ridge least squares (X^T X + lam I) R = X^T target, lam = ridge * |X|_F^2 / d_in, by conjugate
+// gradients on the normal equations, one independent system per column; the products with X
+// are the passes over a float32 copy of X.  Stops when every column's residual is below
+// tol times its right-hand side, or after max_iters.  R: host [d_in][n_r].
+hipError_t router_fit(const void* x, int x_dtype, int T, int d_in, const float* target, int n_r, double ridge,
+                      int max_iters, double tol, float* R, int* iters_done, void* ws, hipStream_t st) {
+    char* p = static_cast<char*>(ws);
+    float* Xf = reinterpret_cast<float*>(p);
+    p += align256((size_t)T * d_in * 4);
+    float* vec[5];
+    for (int v = 0; v < 5; ++v) {
+        vec[v] = reinterpret_cast<float*>(p);
+        p += align256((size_t)d_in * n_r * 4);
+    }
+    float *Rd = vec[0], *rd = vec[1], *pd = vec[2], *qd = vec[3], *bd = vec[4];
+    float* Xp = reinterpret_cast<float*>(p);
+    p += align256((size_t)T * n_r * 4);
+    double* dd = reinterpret_cast<double*>(p);  // [n_r] dots, then one sum of squares
+    const size_t nv = (size_t)d_in * n_r;
+    const unsigned gv = (unsigned)std::min<size_t>((nv + 255) / 256, 1024);
+    std::vector<double> rr(n_r), rr_new(n_r), bb(n_r), pq(n_r), coef(n_r);
+    hipError_t e;
+#define QE_TRY(expr)                              \
+    do {                                          \
+        if ((e = (expr)) != hipSuccess) return e; \
+    } while (0)
+    auto dots = [&](const float* a, const float* b, std::vector<double>& out) -> hipError_t {
+        hipLaunchKernelGGL(coldot_kernel, dim3(n_r), dim3(256), 0, st, a, b, d_in, n_r, dd);
+        hipError_t r;
+        if ((r = hipMemcpyAsync(out.data(), dd, (size_t)n_r * 8, hipMemcpyDeviceToHost, st)) != hipSuccess) return r;
+        return hipStreamSynchronize(st);
+    };
+    auto upload_coef = [&]() -> hipError_t {
+        hipError_t r;
+        if ((r = hipMemcpyAsync(dd, coef.data(), (size_t)n_r * 8, hipMemcpyHostToDevice, st)) != hipSuccess) return r;
+        return hipStreamSynchronize(st);  // coef is refilled by the next step
+    };
+    const size_t nx = (size_t)T * d_in;
+    hipLaunchKernelGGL(to_f32_kernel, dim3((unsigned)std::min<size_t>((nx + 255) / 256, 4096)), dim3(256), 0, st, x,
+                       x_dtype, nx, Xf);
+    hipLaunchKernelGGL(zero_kernel, dim3(1), dim3(256), 0, st, reinterpret_cast<float*>(dd + n_r), (size_t)2);
+    hipLaunchKernelGGL(sumsq_kernel, dim3(1024), dim3(256), 0, st, Xf, nx, dd + n_r);
+    double fro = 0.0;
+    QE_TRY(hipMemcpyAsync(&fro, dd + n_r, 8, hipMemcpyDeviceToHost, st));
+    QE_TRY(hipStreamSynchronize(st));
+    const double lam = ridge * fro / d_in;
+    QE_TRY(pass_over_e(true, Xf, T, d_in, target, n_r, nullptr, bd, st));  // b = X^T target
+    hipLaunchKernelGGL(zero_kernel, dim3(gv), dim3(256), 0, st, Rd, nv);
+    QE_TRY(hipMemcpyAsync(rd, bd, nv * 4, hipMemcpyDeviceToDevice, st));
+    QE_TRY(hipMemcpyAsync(pd, bd, nv * 4, hipMemcpyDeviceToDevice, st));
+    QE_TRY(dots(bd, bd, bb));
+    rr = bb;
+    int it = 0;
+    for (; it < max_iters; ++it) {
+        bool done = true;
+        for (int g = 0; g < n_r; ++g) done = done && rr[g] <= tol * tol * bb[g];
+        if (done) break;
+        QE_TRY(pass_over_e(false, Xf, T, d_in, pd, n_r, nullptr, Xp, st));  // X p
+        QE_TRY(pass_over_e(true, Xf, T, d_in, Xp, n_r, nullptr, qd, st));   // X^T X p
+        hipLaunchKernelGGL(cg_update_kernel, dim3(gv), dim3(256), 0, st, 0, d_in, n_r, lam, dd, Rd, rd, pd, qd);
+        QE_TRY(dots(pd, qd, pq));
+        for (int g = 0; g < n_r; ++g) coef[g] = pq[g] > 0.0 ? rr[g] / pq[g] : 0.0;  // alpha
+        QE_TRY(upload_coef());
+        hipLaunchKernelGGL(cg_update_kernel, dim3(gv), dim3(256), 0, st, 1, d_in, n_r, lam, dd, Rd, rd, pd, qd);
+        QE_TRY(dots(rd, rd, rr_new));
+        for (int g = 0; g < n_r; ++g) coef[g] = rr[g] > 0.0 ? rr_new[g] / rr[g] : 0.0;  // beta
+        QE_TRY(upload_coef());
+        hipLaunchKernelGGL(cg_update_kernel, dim3(gv), dim3(256), 0, st, 2, d_in, n_r, lam, dd, Rd, rd, pd, qd);
+        rr = rr_new;
+    }
+    if (iters_done) *iters_done = it;
+    QE_TRY(hipMemcpyAsync(R, Rd, nv * 4, hipMemcpyDeviceToHost, st));
+    QE_TRY(hipStreamSynchronize(st));
+#undef QE_TRY
+    return hipGetLastError();
 }
 
 }  // namespace qe

@@ -762,6 +762,43 @@ int qe_build_experts(const float* W_f, const float* s, int32_t d_out, int32_t d_
                                         B_r, sigma_s, sigma_r, ws, S(stream)));
 }
 
+size_t qe_router_targets_workspace_bytes(int32_t d_out, int32_t d_in, int32_t n_routed, int32_t r_routed) {
+    return d_out > 0 && d_in > 0 && n_routed > 0 && r_routed > 0
+               ? router_targets_workspace_bytes(d_out, d_in, n_routed, r_routed)
+               : 0;
+}
+
+int qe_router_targets(const float* E1, int32_t d_out, int32_t d_in, const void* x, int32_t x_dtype, int32_t T,
+                      const float* A_r, const float* B_r, int32_t n_routed, int32_t r_routed, float* target, void* ws,
+                      size_t ws_bytes, void* stream) {
+    QE_CHECK(E1 && x && A_r && B_r && target && ws && d_out > 0 && d_in > 0 && T > 0, QE_ERR_INVALID_ARG);
+    QE_CHECK(n_routed >= 1 && n_routed <= 16 && r_routed >= 1 && r_routed <= 64, QE_ERR_INVALID_ARG);
+    QE_CHECK(x_dtype == QE_F32 || x_dtype == QE_BF16, QE_ERR_INVALID_ARG);
+    for (const void* q : {(const void*)E1, x, (const void*)A_r, (const void*)B_r, (const void*)target, (const void*)ws})
+        QE_CHECK(aligned16(q), QE_ERR_ALIGNMENT);
+    QE_CHECK(ws_bytes >= router_targets_workspace_bytes(d_out, d_in, n_routed, r_routed), QE_ERR_WORKSPACE);
+    QE_TRY_HIP(router_targets(E1, d_out, d_in, x, x_dtype, T, A_r, B_r, n_routed, r_routed, target, ws, S(stream)));
+    return QE_OK;
+}
+
+size_t qe_router_fit_workspace_bytes(int32_t T, int32_t d_in, int32_t n_routed) {
+    return T > 0 && d_in > 0 && n_routed > 0 ? router_fit_workspace_bytes(T, d_in, n_routed) : 0;
+}
+
+int qe_router_fit(const void* x, int32_t x_dtype, int32_t T, int32_t d_in, const float* target, int32_t n_routed,
+                  double ridge, int32_t max_iters, double tol, float* R, int32_t* iters_done, void* ws, size_t ws_bytes,
+                  void* stream) {
+    QE_CHECK(x && target && R && ws && T > 0 && d_in > 0 && n_routed >= 1 && n_routed <= 16, QE_ERR_INVALID_ARG);
+    QE_CHECK(x_dtype == QE_F32 || x_dtype == QE_BF16, QE_ERR_INVALID_ARG);
+    QE_CHECK(ridge >= 0.0 && max_iters >= 0 && max_iters <= 100000 && tol >= 0.0, QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(x) && aligned16(target) && aligned16(ws), QE_ERR_ALIGNMENT);
+    QE_CHECK(ws_bytes >= router_fit_workspace_bytes(T, d_in, n_routed), QE_ERR_WORKSPACE);
+    int done = 0;
+    QE_TRY_HIP(router_fit(x, x_dtype, T, d_in, target, n_routed, ridge, max_iters, tol, R, &done, ws, S(stream)));
+    if (iters_done) *iters_done = done;
+    return QE_OK;
+}
+
 // ------------------------------------------------------------------ measurement aids
 int qe_probe_mfma_i8(int32_t* out, int32_t blocks, int32_t iters, int32_t operands, double* ops, void* stream) {
     QE_CHECK(out && blocks >= 1 && iters >= 1 && (operands == 0 || operands == 1), QE_ERR_INVALID_ARG);

@@ -34,4 +34,13 @@ hipError_t build_experts(const float* W_f, const float* s, int d_out, int d_in, 
                          const float* omegas, int k, int power_iters, float* A_s, float* B_s, float* A_r, float* B_r,
                          double* sigma_s, double* sigma_r, void* ws, hipStream_t st);
 
+// Router: per-token targets mean_i |x_t (E_1^T - A_g B_g)|_i and the ridge least-squares fit of
+// R to them (see router_targets / router_fit in k_lowrank.hip); arguments validated by the caller.
+size_t router_targets_workspace_bytes(int d_out, int d_in, int n_r, int r_r);
+hipError_t router_targets(const float* E1, int d_out, int d_in, const void* x, int x_dtype, int T, const float* A_r,
+                          const float* B_r, int n_r, int r_r, float* target, void* ws, hipStream_t st);
+size_t router_fit_workspace_bytes(int T, int d_in, int n_r);
+hipError_t router_fit(const void* x, int x_dtype, int T, int d_in, const float* target, int n_r, double ridge,
+                      int max_iters, double tol, float* R, int* iters_done, void* ws, hipStream_t st);
+
 }  // namespace qe

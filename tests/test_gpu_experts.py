@@ -1,7 +1,7 @@
 """GPU parity of the expert construction against the oracle: the quantization error, the
-whitening weights, the rank-r subtraction, the randomized truncated SVD and the whole SE / RE
-build, at small sizes with ragged tiles and at the Qwen2VL-72B down-projection size (checked
-there through properties that hold at any size)."""
+whitening weights, the rank-r subtraction, the randomized truncated SVD, the whole SE / RE
+build, and the router's targets and ridge least-squares fit, at small sizes with ragged tiles
+and at full layer sizes (sampled, or checked through properties that hold at any size)."""
 
 import numpy as np
 import pytest
@@ -202,3 +202,55 @@ def test_expert_argument_errors(L):
     c = torch.ones(16, device=DEV)
     with pytest.raises(L.QEError):  # a label outside [0, n_routed)
         L.qe_build_experts(E, None, 4, c, [1, 2], [0, 3], 2, 2, 2, torch.zeros(3, 8, 4, device=DEV), 1, ws)
+
+
+@pytest.mark.parametrize("T,dtype", [(300, torch.bfloat16), (129, torch.float32), (1, torch.bfloat16)])
+def test_router_targets_match_oracle(L, T, dtype):
+    rng = np.random.default_rng(T)
+    d_out, d_in, n_r, r_r = 96, 200, 3, 5
+    E1 = (rng.standard_normal((d_out, d_in)) * 0.01).astype(np.float32)
+    A = (rng.standard_normal((n_r, d_in, r_r)) * 0.1).astype(np.float32)
+    A[1, 50:] = 0.0  # an expert on part of the channels
+    B = (rng.standard_normal((n_r, r_r, d_out)) * 0.01).astype(np.float32)
+    x = torch.from_numpy((rng.standard_normal((T, d_in)) * rng.uniform(0.2, 4, d_in)).astype(np.float32)).to(dtype)
+    tg = torch.empty(T, n_r, device=DEV)
+    ws = torch.empty(L.qe_router_targets_workspace_bytes(d_out, d_in, n_r, r_r), dtype=torch.uint8, device=DEV)
+    L.qe_router_targets(_dev(E1), x.to(DEV), _dev(A), _dev(B), tg, ws)
+    torch.cuda.synchronize()
+    ref = X.router_targets(E1, x.float().numpy(), A, B)
+    assert np.allclose(tg.cpu().numpy(), ref, rtol=2e-5, atol=1e-7 * np.max(ref))
+
+
+def test_router_targets_full_size_sampled(L):
+    # InternVL2-8B down projection (14336 -> 4096), W4 error, 8 experts of rank 32, 256 tokens;
+    # the oracle recomputes 24 sampled tokens
+    rng = np.random.default_rng(40)
+    d_out, d_in, n_r, r_r, T = 4096, 14336, 8, 32, 256
+    W = torch.randn(d_out, d_in, device=DEV) * 0.02
+    E1 = torch.empty_like(W)
+    L.qe_quant_error(W, None, 4, E1)
+    del W
+    A = torch.randn(n_r, d_in, r_r, device=DEV) * 0.01
+    B = torch.randn(n_r, r_r, d_out, device=DEV) * 0.01
+    x = (torch.randn(T, d_in, device=DEV) * 2).to(torch.bfloat16)
+    tg = torch.empty(T, n_r, device=DEV)
+    ws = torch.empty(L.qe_router_targets_workspace_bytes(d_out, d_in, n_r, r_r), dtype=torch.uint8, device=DEV)
+    L.qe_router_targets(E1, x, A, B, tg, ws)
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 22, replace=False)]))
+    ref = X.router_targets(E1.cpu().numpy(), x[torch.as_tensor(toks, device=DEV)].float().cpu().numpy(),
+                           A.cpu().numpy(), B.cpu().numpy())
+    assert np.allclose(tg.cpu().numpy()[toks], ref, rtol=1e-4)
+
+
+@pytest.mark.parametrize("T,d_in,n_r,ridge,dtype", [(600, 128, 4, 1e-2, torch.float32), (100, 256, 8, 5e-2, torch.bfloat16),
+                                                   (1000, 333, 1, 1e-3, torch.float32)])
+def test_router_fit_matches_closed_form(L, T, d_in, n_r, ridge, dtype):
+    rng = np.random.default_rng(T + d_in)
+    x = torch.from_numpy((rng.standard_normal((T, d_in)) * rng.uniform(0.5, 2, d_in)).astype(np.float32)).to(dtype)
+    tgt = rng.uniform(0.0, 1.0, (T, n_r)).astype(np.float32)
+    ws = torch.empty(L.qe_router_fit_workspace_bytes(T, d_in, n_r), dtype=torch.uint8, device=DEV)
+    R, it = L.qe_router_fit(x.to(DEV), _dev(tgt), ridge, 2000, 1e-7, ws)
+    ref = X.router_fit(x.float().numpy(), tgt, ridge)
+    assert it < 2000
+    assert np.max(np.abs(R - ref)) <= 2e-3 * np.max(np.abs(ref))
