@@ -280,6 +280,48 @@ def qe_linear(x: np.ndarray, x_is_bf16: bool, s: Optional[np.ndarray], qw: np.nd
     return out
 
 
+def route_top2(xb: np.ndarray, R: np.ndarray) -> Dict[str, np.ndarray]:
+    """Two routed experts per token: the smallest and the second-smallest score.
+
+    [PaperDaily] "核心设计": at inference only the top-1 or the top-2 routed experts are
+    activated.  Ties go to the lower expert index (a stable sort of the scores), so expert
+    is route()'s choice and expert2 the best of the others.  margin2 is the gap between the
+    second and third smallest scores (for near-tie checks).
+    """
+    sc = np.asarray(xb, np.float64) @ np.asarray(R, np.float64)
+    T, n_r = sc.shape
+    order = np.argsort(sc, axis=1, kind="stable")
+    ss = np.take_along_axis(sc, order, axis=1)
+    margin2 = ss[:, 2] - ss[:, 1] if n_r >= 3 else np.full(T, np.inf)
+    return dict(scores=sc, expert=order[:, 0].astype(np.int32), expert2=order[:, 1].astype(np.int32),
+                margin2=margin2)
+
+
+def qe_linear_top2(x: np.ndarray, x_is_bf16: bool, s: Optional[np.ndarray], qw: np.ndarray, s_w: np.ndarray,
+                   a_bits: int, A_s, B_s, A_r, B_r, R, experts_override: Optional[np.ndarray] = None
+                   ) -> Dict[str, np.ndarray]:
+    """qe_linear with the two routed experts of route_top2, both corrections added.
+
+    Reading (the pages give no rule for combining two experts): each routed expert is fitted
+    to the error carried by its own cluster of token-dependent channels, so the two selected
+    corrections are complementary and are summed with weight one.  experts_override [T, 2]
+    replaces the router's pair (used only to re-evaluate near-tie tokens).
+    """
+    x32 = np.asarray(x, np.float32)
+    xb = x32 if x_is_bf16 else bf16_round(x32)
+    r2 = route_top2(xb, R)
+    pair = np.stack([r2["expert"], r2["expert2"]], axis=1) if experts_override is None else \
+        np.asarray(experts_override, np.int32)
+    out = qe_linear(x, x_is_bf16, s, qw, s_w, a_bits, A_s=A_s, B_s=B_s, A_r=A_r, B_r=B_r, R=R,
+                    expert_override=pair[:, 0])
+    y = out["y64"] + routed_term(xb, A_r, B_r, pair[:, 1])
+    out.update(r2)
+    out["experts"] = pair
+    out["y"] = y.astype(np.float32)
+    out["y64"] = y
+    return out
+
+
 # ------------------------------------------------------------- channel top-k stat
 def colmean_abs(W_f: np.ndarray) -> np.ndarray:
     """w = Mean_row(|W_f|): mean over output rows of |W_f|, one value per input channel.

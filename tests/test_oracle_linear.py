@@ -153,3 +153,28 @@ def test_adapters_read_bf16_of_unsmoothed_x():
     se = (xb @ p["A_s"]) @ p["B_s"]
     re = O.routed_term(_bf(x), p["A_r"], p["B_r"], full["expert"])
     assert np.allclose(full["y64"] - base["y64"], se + re, rtol=1e-9, atol=1e-12)
+
+
+def test_route_top2_hand_example():
+    # scores = x when R is the identity: row [3, 1, 2] -> experts 1 then 2; row [1, 1, 0] -> 2, then
+    # the tie between 0 and 1 goes to the lower index 0; row [5, 5, 5] -> 0 then 1
+    xb = np.array([[3.0, 1.0, 2.0], [1.0, 1.0, 0.0], [5.0, 5.0, 5.0]])
+    r = O.route_top2(xb, np.eye(3))
+    assert r["expert"].tolist() == [1, 2, 0] and r["expert2"].tolist() == [2, 0, 1]
+    assert np.allclose(r["margin2"], [1.0, 0.0, 0.0])
+    assert np.array_equal(r["expert"], O.route(xb, np.eye(3))["expert"])
+
+
+def test_top2_with_two_experts_uses_both_for_every_token():
+    # with N_r = 2 every token takes both routed experts, so the output is main + SE + RE_0 + RE_1
+    # whatever the router says (R is random here)
+    x, s, W, p = _tiny(40, n_r=2)
+    qw, s_w = O.quant_weights(W, s, 4)
+    out = O.qe_linear_top2(x, False, s, qw, s_w, 8, p["A_s"], p["B_s"], p["A_r"], p["B_r"], p["R"])
+    xb = _bf(x)
+    qx, s_x = O.quant_act(x, s, 8)
+    _, y_main = O.main_term_int(qx, s_x, qw, s_w)
+    want = y_main + O.lowrank(xb, p["A_s"], p["B_s"]) + O.lowrank(xb, p["A_r"][0], p["B_r"][0]) + \
+        O.lowrank(xb, p["A_r"][1], p["B_r"][1])
+    assert np.allclose(out["y64"], want, rtol=0, atol=1e-12)
+    assert np.all(out["experts"][:, 0] != out["experts"][:, 1])
