@@ -310,6 +310,21 @@ int qe_cluster_channels(const uint32_t* cooc, int32_t n_dep, int64_t T, int32_t 
 int qe_linear_cost(const qe_linear* lin, int32_t T, int32_t n_distinct_experts, int32_t x_bytes_per_elt,
                    double* int_macs, double* adapter_macs, double* alg_bytes);
 
+/* Top-2 routing (PaperDaily post "西交大提出Quant Experts：token级量化补偿", section "核心设计":
+ * at inference only the top-1 or the top-2 routed experts are activated).  The token takes the
+ * two experts with the smallest router scores (the lower index on ties) and both routed
+ * corrections are added: each routed expert is fitted to the error of its own cluster of
+ * channels, so the two corrections are complementary (the pages give no combining rule).
+ * qe_linear_forward_top2: y as qe_linear_forward plus (x A_e2) B_e2 for the second expert e2 =
+ *   the smallest score among the experts other than the forward's first expert.  Requires
+ *   n_routed >= 2, T <= 65535.  expert_out / expert2_out: optional device int32 [T].  ws:
+ *   qe_top2_workspace_bytes(lin, T) bytes (qe_workspace_bytes' layout plus the scores and the
+ *   second expert's grouping).  Enqueued; errors as qe_linear_forward.
+ */
+size_t qe_top2_workspace_bytes(const qe_linear* lin, int32_t T);
+int qe_linear_forward_top2(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* y,
+                           int32_t* expert_out, int32_t* expert2_out, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------- expert construction --
  * Building the shared and routed experts of one linear after calibration (MCISLAB DeepRead
  * summary of "Quant Experts", section "Method": the quantization error E = W_f - W_q is

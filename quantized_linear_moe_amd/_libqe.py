@@ -73,6 +73,8 @@ def _load():
         "qe_cooccur": (ctypes.c_int, [P, I, I, P, I, I, P, P, Z, P]),
         "qe_cluster_channels": (ctypes.c_int, [P, I, ctypes.c_int64, I, ctypes.c_double, P, P, P, P]),
         "qe_linear_cost": (ctypes.c_int, [LP, I, I, I, D, D, D]),
+        "qe_top2_workspace_bytes": (Z, [LP, I]),
+        "qe_linear_forward_top2": (ctypes.c_int, [LP, P, I, I, P, P, P, P, Z, P]),
         "qe_quant_error": (ctypes.c_int, [P, P, I, I, I, P, P]),
         "qe_channel_rms_workspace_bytes": (Z, [I, I]),
         "qe_channel_rms": (ctypes.c_int, [P, I, I, I, P, P, Z, P]),
@@ -102,7 +104,7 @@ EXPORTED = (
     "qe_workspace_bytes", "qe_quant_act", "qe_route", "qe_adapter_inputs", "qe_wq_gemm", "qe_routed_lora",
     "qe_linear_prologue", "qe_linear_forward", "qe_colmean_abs", "qe_channel_topk", "qe_linear_cost",
     "qe_probe_mfma_i8", "qe_probe_mfma_bf16", "qe_probe_copy", "qe_partition_channels", "qe_cooccur_workspace_bytes",
-    "qe_cooccur", "qe_cluster_channels", "qe_quant_error", "qe_channel_rms_workspace_bytes", "qe_channel_rms",
+    "qe_cooccur", "qe_cluster_channels", "qe_top2_workspace_bytes", "qe_linear_forward_top2", "qe_quant_error", "qe_channel_rms_workspace_bytes", "qe_channel_rms",
     "qe_sub_lowrank", "qe_lowrank_workspace_bytes", "qe_lowrank_fit", "qe_build_experts_workspace_bytes",
     "qe_build_experts", "qe_router_targets_workspace_bytes", "qe_router_targets", "qe_router_fit_workspace_bytes",
     "qe_router_fit",
@@ -275,6 +277,18 @@ def qe_cluster_channels(cooc: np.ndarray, T: int, n_clusters: int, threshold: fl
     _check(_lib.qe_cluster_channels(_ptr(cooc), n, T, n_clusters, threshold, _ptr(labels), _ptr(sim), _ptr(ev),
                                     _ptr(emb)), "qe_cluster_channels")
     return (labels, sim, ev, emb) if outputs else labels
+
+
+def qe_top2_workspace_bytes(lin: qe_linear, T: int) -> int:
+    return _lib.qe_top2_workspace_bytes(ctypes.byref(lin), T)
+
+
+def qe_linear_forward_top2(lin: qe_linear, x, y, expert_out=None, expert2_out=None, ws=None, stream=None):
+    """Enqueue the QE linear with the two routed experts of smallest score per token."""
+    T = x.shape[0]
+    _check(_lib.qe_linear_forward_top2(ctypes.byref(lin), _ptr(x), _dtype_code(x), T, _ptr(y), _ptr(expert_out),
+                                       _ptr(expert2_out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                       _stream(stream)), "qe_linear_forward_top2")
 
 
 def qe_quant_error(W_f, s, w_bits, E, stream=None):

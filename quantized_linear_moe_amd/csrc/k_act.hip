@@ -1089,6 +1089,34 @@ __global__ __launch_bounds__(1024) void bucket_kernel(const int32_t* __restrict_
     }
 }
 
+// Top-2 routing: expert2[t] = the best (smallest-score) expert other than expert1[t], the lower
+// index on ties; scores [T][n_r] from the router pass.
+__global__ __launch_bounds__(256) void second_expert_kernel(const float* __restrict__ scores,
+                                                            const int32_t* __restrict__ expert1, int T, int n_r,
+                                                            int32_t* __restrict__ expert2) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t >= T) return;
+    const int e1 = expert1[t];
+    int best = -1;
+    float bv = 0.0f;
+    for (int e = 0; e < n_r; ++e) {
+        if (e == e1) continue;
+        const float v = scores[(size_t)t * n_r + e];
+        if (best < 0 || v < bv) {
+            best = e;
+            bv = v;
+        }
+    }
+    expert2[t] = best;
+}
+
+hipError_t launch_second_expert(const float* scores, const int32_t* expert1, int T, int n_r, int32_t* expert2,
+                                hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    hipLaunchKernelGGL(second_expert_kernel, dim3((T + 255) / 256), dim3(256), 0, st, scores, expert1, T, n_r, expert2);
+    return hipGetLastError();
+}
+
 hipError_t launch_bucket(const int32_t* expert, int T, int n_r, int32_t* counts, int32_t* offsets, int32_t* perm,
                          hipStream_t st) {
     hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(1024), 0, st, expert, T, n_r, counts, offsets, perm);

@@ -679,6 +679,55 @@ int qe_cluster_channels(const uint32_t* cooc, int32_t n_dep, int64_t T, int32_t 
     return QE_OK;
 }
 
+// ------------------------------------------------------------------ top-2 routing
+// qe_linear_forward with the two routed experts of smallest score per token: the forward (its
+// fused first expert), then the router scores, the best other expert, its adapter input and its
+// term through the grouped routed path (added into y).
+size_t qe_top2_workspace_bytes(const qe_linear* lin, int32_t T) {
+    const size_t base = qe_workspace_bytes(lin, T);
+    if (base == 0 || lin->n_routed < 2 || T < 0) return 0;
+    const size_t t4 = align256((size_t)std::max(T, 1) * 4);
+    return align256(base) + 4 * t4 + align256((size_t)std::max(T, 1) * lin->n_routed * 4) +
+           2 * align256(((size_t)lin->n_routed + 1) * 4);
+}
+
+int qe_linear_forward_top2(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* y,
+                           int32_t* expert_out, int32_t* expert2_out, void* ws, size_t ws_bytes, void* stream) {
+    const size_t need = qe_top2_workspace_bytes(lin, T);
+    QE_CHECK(lin && lin->n_routed >= 2 && need > 0, QE_ERR_INVALID_ARG);
+    QE_CHECK(T <= 65535, QE_ERR_UNSUPPORTED);
+    QE_CHECK(ws_bytes >= need, QE_ERR_WORKSPACE);
+    const size_t base = qe_workspace_bytes(lin, T);
+    if (T == 0) return validate_forward_common(lin, T, x_dtype, x, ws, ws_bytes);
+    char* p = static_cast<char*>(ws) + align256(base);
+    const size_t t4 = align256((size_t)T * 4);
+    int32_t* e1 = reinterpret_cast<int32_t*>(p);
+    int32_t* e2 = reinterpret_cast<int32_t*>(p + t4);
+    int32_t* perm = reinterpret_cast<int32_t*>(p + 2 * t4);
+    int32_t* e_tmp = reinterpret_cast<int32_t*>(p + 3 * t4);
+    float* scores = reinterpret_cast<float*>(p + 4 * t4);
+    char* q = p + 4 * t4 + align256((size_t)T * lin->n_routed * 4);
+    int32_t* offsets = reinterpret_cast<int32_t*>(q);
+    int32_t* counts = reinterpret_cast<int32_t*>(q + align256(((size_t)lin->n_routed + 1) * 4));
+    int st = qe_linear_forward(lin, x, x_dtype, T, y, e1, ws, base, stream);
+    if (st) return st;
+    const PrepLayout P = prep_layout(lin);
+    const WsLayout W = ws_layout(lin, T);
+    hipStream_t s = S(stream);
+    st = run_xpass(lin, x, x_dtype, T, false, false, true, nullptr, scores, e_tmp, nullptr, nullptr, ws, s);
+    if (st) return st;
+    QE_TRY_HIP(launch_second_expert(scores, e1, T, lin->n_routed, e2, s));
+    uint16_t* v = at<uint16_t>(ws, W.v);
+    st = run_xpass(lin, x, x_dtype, T, false, true, false, e2, nullptr, nullptr, nullptr, v, ws, s);
+    if (st) return st;
+    QE_TRY_HIP(launch_bucket(e2, T, lin->n_routed, counts, offsets, perm, s));
+    QE_TRY_HIP(launch_routed_lora(v, P.rr_pad, offsets, perm, lin->n_routed, at<const uint16_t>(lin->prep, P.bt_r), T,
+                                  lin->d_out, y, s));
+    if (expert_out) QE_TRY_HIP(hipMemcpyAsync(expert_out, e1, (size_t)T * 4, hipMemcpyDeviceToDevice, s));
+    if (expert2_out) QE_TRY_HIP(hipMemcpyAsync(expert2_out, e2, (size_t)T * 4, hipMemcpyDeviceToDevice, s));
+    return QE_OK;
+}
+
 // ------------------------------------------------------------------ expert construction
 namespace {
 int lowrank_status(hipError_t e) {

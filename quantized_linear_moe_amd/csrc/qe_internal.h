@@ -117,6 +117,8 @@ hipError_t launch_expert_quant(const uint16_t* x, int T, int d_in, const float* 
                                bool keep_order, hipStream_t st);
 int expert_quant_ksplit(int T, int d_in);
 
+hipError_t launch_second_expert(const float* scores, const int32_t* expert1, int T, int n_r, int32_t* expert2,
+                                hipStream_t st);
 hipError_t launch_bucket(const int32_t* expert, int T, int n_r, int32_t* counts, int32_t* offsets,
                          int32_t* perm, hipStream_t st);
 
