@@ -557,8 +557,9 @@ def decode_line(torch, synth, qe, libqe, dev, w_bits, a_bits, copy_gbs=None):
 
 def sweeps(torch, synth, qe, libqe, dev, reps=10):
     """Variants the pages study: the number of routed experts N_r (Table 6: 2, 4, 8, 16) on the
-    Qwen2VL-72B q projection (8192 -> 8192, W4A6, T = 4096, the composite entry point), and the
-    top-k size k of the calibration statistic on the InternVL2-8B down input (T = 4096)."""
+    Qwen2VL-72B q projection (8192 -> 8192, W4A6, T = 4096, the composite entry point), with
+    top-2 routing at N_r = 8, and the top-k size k of the calibration statistic on the
+    InternVL2-8B down input (T = 4096)."""
     import dataclasses
 
     def med_us(fn):
@@ -585,8 +586,13 @@ def sweeps(torch, synth, qe, libqe, dev, reps=10):
         ws = layer.workspace(base.T)
         y = torch.empty(base.T, spec.d_out, dtype=torch.float32, device=dev)
         t = med_us(lambda: libqe.qe_linear_forward(layer.lin, x, y, None, ws))
-        out["n_routed_qwen2vl72b_q_w4a6_T4096"].append({"n_routed": n_r, "us": round(t, 2),
-                                                        "tokens_per_s": round(base.T / t * 1e6, 1)})
+        row = {"n_routed": n_r, "us": round(t, 2), "tokens_per_s": round(base.T / t * 1e6, 1)}
+        if n_r == 8:  # top-2 routing on the same linear: the second expert through the grouped path
+            ws2 = torch.empty(libqe.qe_top2_workspace_bytes(layer.lin, base.T), dtype=torch.uint8, device=dev)
+            t2 = med_us(lambda: libqe.qe_linear_forward_top2(layer.lin, x, y, None, None, ws2))
+            row.update(top2_us=round(t2, 2), top2_tokens_per_s=round(base.T / t2 * 1e6, 1))
+            del ws2
+        out["n_routed_qwen2vl72b_q_w4a6_T4096"].append(row)
         del layer, ws, y
     del x
     cfg = synth.get_config("internvl2_8b")

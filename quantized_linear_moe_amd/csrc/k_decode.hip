@@ -564,31 +564,81 @@ hipError_t launch_gemm_split_finish(const int32_t* part, int ksplit, int T, int 
     return hipGetLastError();
 }
 
-// Unfused routed experts, grouped by expert bucket: thread per (bucket position, channel);
-// y[perm[p]][i] += v[perm[p]] . Bt_r[e][i] with e the bucket of position p.
+// Unfused routed experts, grouped by expert bucket: y[perm[p]][i] += v[perm[p]] . Bt_r[e][i] with
+// e the bucket of position p.  A workgroup takes 64 bucket positions x 256 channels (wave: 64
+// channels); each 16-position block makes one round of bf16 MFMAs per expert present in it (the
+// buckets are contiguous, so usually one), with A masked to that expert's rows, and adds its
+// result into y in place (every (token, channel) appears once in a grouping).  Column lr of
+// channel block nb is channel 64 w + 4 lr + nb, so a lane's four blocks are four consecutive
+// channels: each row's update is one 16-byte read-modify-write per lane.
+constexpr int RL_P = 64;
+
 __global__ __launch_bounds__(256) void routed_lora_kernel(const uint16_t* __restrict__ v, int rr_pad,
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ perm, int n_r,
                                                           const uint16_t* __restrict__ bt_r, int T, int d_out,
                                                           float* __restrict__ y) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    const int p = blockIdx.y;
-    if (i >= d_out || p >= T) return;
-    int e = 0;
-    while (e + 1 < n_r && offsets[e + 1] <= p) ++e;
-    const int t = min(max(perm[p], 0), T - 1);
-    float a = 0.0f;
-    for (int m = 0; m < rr_pad; ++m)
-        a = __builtin_fmaf(__uint_as_float((uint32_t)v[(size_t)t * rr_pad + m] << 16),
-                           __uint_as_float((uint32_t)bt_r[((size_t)e * d_out + i) * rr_pad + m] << 16), a);
-    y[(size_t)t * d_out + i] += a;
+    const int p0 = blockIdx.x * RL_P, tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15,
+              lg = lane >> 4;
+    const int nw = blockIdx.y * 256 + wid * 64;
+    auto expert_of = [&](int p) {
+        int e = 0;
+        while (e + 1 < n_r && offsets[e + 1] <= p) ++e;
+        return e;
+    };
+    v4f acc[4][4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = v4f{0, 0, 0, 0};
+    int chs[4];
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) chs[nb] = min(nw + 4 * lr + nb, d_out - 1);  // past d_out: never stored
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+        const int pb = p0 + 16 * mb;
+        if (pb >= T) break;  // wave-uniform
+        const int p = min(pb + lr, T - 1);
+        const bool prow = pb + lr < T;
+        const int e_row = expert_of(p);
+        const int t = min(max(perm[p], 0), T - 1);
+        const int e_lo = expert_of(pb), e_hi = expert_of(min(pb + 15, T - 1));
+        for (int e = e_lo; e <= e_hi; ++e) {  // wave-uniform bounds
+            for (int k0 = 0; k0 < rr_pad; k0 += 32) {
+                const v8bf av = *reinterpret_cast<const v8bf*>(v + (size_t)t * rr_pad + k0 + lg * 8);
+                const v8bf a = (prow && e_row == e) ? av : v8bf{};
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    const v8bf b =
+                        *reinterpret_cast<const v8bf*>(bt_r + ((size_t)e * d_out + chs[nb]) * rr_pad + k0 + lg * 8);
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[mb][nb], 0, 0, 0);
+                }
+            }
+        }
+    }
+    // lane holds positions pb + 4 lg + r and channels nw + 4 lr + nb (d_out is a multiple of 16)
+    const int ch0 = nw + 4 * lr;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int p = p0 + 16 * mb + 4 * lg + r;
+            if (p >= T || ch0 >= d_out) continue;
+            const int t = min(max(perm[p], 0), T - 1);
+            v4f* dst = reinterpret_cast<v4f*>(y + (size_t)t * d_out + ch0);
+            v4f o = *dst;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) o[nb] += acc[mb][nb][r];
+            *dst = o;
+        }
 }
 
 hipError_t launch_routed_lora(const uint16_t* v, int rr_pad, const int32_t* offsets, const int32_t* perm, int n_r,
                               const uint16_t* bt_r, int T, int d_out, float* y, hipStream_t st) {
     if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(routed_lora_kernel, dim3((d_out + 255) / 256, T), dim3(256), 0, st, v, rr_pad, offsets, perm,
-                       n_r, bt_r, T, d_out, y);
+    if (rr_pad % 32 || n_r < 1 || d_out % 16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(routed_lora_kernel, dim3((T + RL_P - 1) / RL_P, (d_out + 255) / 256), dim3(256), 0, st, v,
+                       rr_pad, offsets, perm, n_r, bt_r, T, d_out, y);
     return hipGetLastError();
 }
 

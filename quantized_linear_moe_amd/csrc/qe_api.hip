@@ -355,6 +355,26 @@ int qe_quant_act(const void* x, int32_t x_dtype, const float* smooth, int32_t T,
 
 // Projection of x onto the columns [c0, c0 + nc) of the prepared Mt, then the
 // per-token reduction / routing.  Internal helper for route / adapter inputs / forward.
+// Split-K partial sums of x onto the projection columns [c0, c0 + nc) (padded to nc_pad); *ks
+// receives the split count the finish kernel needs.
+static int xpass_partials(const qe_linear* lin, const void* x, int x_dtype, int T, int c0, int nc, int nc_pad,
+                          float* part, void* ws, hipStream_t s, int* ks) {
+    const PrepLayout P = prep_layout(lin);
+    const WsLayout W = ws_layout(lin, T);
+    const uint16_t* mt = at<const uint16_t>(lin->prep, P.mt);
+    if (T <= kSkinnyMaxT) {  // few tokens: stream the projection matrix like decode weights
+        int st = ensure_attributes();
+        if (st) return st;
+        *ks = skinny_ksplit_proj(lin->d_in);
+        QE_TRY_HIP(launch_skinny(x, x_dtype, T, lin->d_in, nc_pad, 16, mt + (size_t)c0 * lin->d_in, *ks, part, nc_pad, s));
+    } else {
+        *ks = std::min(W.xproj_ksplit, xproj_ksplit(T, lin->d_in, nc_pad));
+        QE_TRY_HIP(launch_xproj(x, x_dtype, T, lin->d_in, mt, c0, nc, nc_pad, *ks, part, s));
+    }
+    (void)ws;
+    return QE_OK;
+}
+
 static int run_xpass(const qe_linear* lin, const void* x, int x_dtype, int T, bool want_se, bool want_re,
                      bool do_route, const int32_t* expert_in, float* scores, int32_t* expert_out, uint16_t* u,
                      uint16_t* v, void* ws, hipStream_t s) {
@@ -372,17 +392,9 @@ static int run_xpass(const qe_linear* lin, const void* x, int x_dtype, int T, bo
     if (c1 <= c0) return QE_OK;
     const int nc = c1 - c0, nc_pad = (nc + 15) / 16 * 16;
     float* part = at<float>(ws, W.part);
-    const uint16_t* mt = at<const uint16_t>(lin->prep, P.mt);
-    int ks;
-    if (T <= kSkinnyMaxT) {  // few tokens: stream the projection matrix like decode weights
-        int st = ensure_attributes();
-        if (st) return st;
-        ks = skinny_ksplit_proj(lin->d_in);
-        QE_TRY_HIP(launch_skinny(x, x_dtype, T, lin->d_in, nc_pad, 16, mt + (size_t)c0 * lin->d_in, ks, part, nc_pad, s));
-    } else {
-        ks = std::min(W.xproj_ksplit, xproj_ksplit(T, lin->d_in, nc_pad));
-        QE_TRY_HIP(launch_xproj(x, x_dtype, T, lin->d_in, mt, c0, nc, nc_pad, ks, part, s));
-    }
+    int ks = 0;
+    int st = xpass_partials(lin, x, x_dtype, T, c0, nc, nc_pad, part, ws, s, &ks);
+    if (st) return st;
     QE_TRY_HIP(launch_xproj_finish(part, ks, T, nc_pad, c0, want_se ? P.col_se : -1, lin->r_shared, P.rs_pad,
                                    want_re ? P.col_re : -1, lin->n_routed, lin->r_routed, P.rr_pad,
                                    do_route ? P.col_router : -1, expert_in, scores, expert_out, want_se ? u : nullptr,
@@ -714,12 +726,21 @@ int qe_linear_forward_top2(const qe_linear* lin, const void* x, int32_t x_dtype,
     const PrepLayout P = prep_layout(lin);
     const WsLayout W = ws_layout(lin, T);
     hipStream_t s = S(stream);
-    st = run_xpass(lin, x, x_dtype, T, false, false, true, nullptr, scores, e_tmp, nullptr, nullptr, ws, s);
+    // one pass of x onto the router and every routed expert's input columns; the finish runs twice
+    // on its partials: the scores first, then v of the second expert
+    const int c0 = std::min(P.col_re, P.col_router);
+    const int c1 = std::max(P.col_re + lin->n_routed * P.rr_pad, P.col_router + lin->n_routed);
+    const int nc = c1 - c0, nc_pad = (nc + 15) / 16 * 16;
+    float* part = at<float>(ws, W.part);
+    int ks = 0;
+    st = xpass_partials(lin, x, x_dtype, T, c0, nc, nc_pad, part, ws, s, &ks);
     if (st) return st;
+    QE_TRY_HIP(launch_xproj_finish(part, ks, T, nc_pad, c0, -1, lin->r_shared, P.rs_pad, -1, lin->n_routed,
+                                   lin->r_routed, P.rr_pad, P.col_router, nullptr, scores, e_tmp, nullptr, nullptr, s));
     QE_TRY_HIP(launch_second_expert(scores, e1, T, lin->n_routed, e2, s));
     uint16_t* v = at<uint16_t>(ws, W.v);
-    st = run_xpass(lin, x, x_dtype, T, false, true, false, e2, nullptr, nullptr, nullptr, v, ws, s);
-    if (st) return st;
+    QE_TRY_HIP(launch_xproj_finish(part, ks, T, nc_pad, c0, -1, lin->r_shared, P.rs_pad, P.col_re, lin->n_routed,
+                                   lin->r_routed, P.rr_pad, -1, e2, nullptr, nullptr, nullptr, v, s));
     QE_TRY_HIP(launch_bucket(e2, T, lin->n_routed, counts, offsets, perm, s));
     QE_TRY_HIP(launch_routed_lora(v, P.rr_pad, offsets, perm, lin->n_routed, at<const uint16_t>(lin->prep, P.bt_r), T,
                                   lin->d_out, y, s));
