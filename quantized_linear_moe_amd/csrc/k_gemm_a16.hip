@@ -387,6 +387,49 @@ __global__ __launch_bounds__(256, 2) void gemm_a16_ring_kernel(
     }
 }
 
+// Finish of a K-split A16 product: a workgroup sums the float partials of a 16-token x 64-channel
+// tile (a 16 x 16 block per wave, small enough that narrow outputs still give hundreds of
+// workgroups) straight into the MFMA accumulator layout (fixed split order) and applies the
+// epilogue of the unsplit kernels, so each adapter row is read once per 16 tokens (a thread per
+// output re-read them for every token).
+__global__ __launch_bounds__(256) void gemm_a16_finish_kernel(
+    const float* __restrict__ part, int ksplit, int T, int d_out, int n_tm, const float* __restrict__ w_scale,
+    const uint16_t* __restrict__ u, const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v,
+    const int32_t* __restrict__ expert, const uint16_t* __restrict__ bt_r, int rr_pad, int n_r,
+    float* __restrict__ y) {
+    constexpr int MB = 1, NBW = 1;
+    const int tm = blockIdx.x % n_tm, tn = blockIdx.x / n_tm;
+    const int m0 = tm * 16;
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int nb0 = tn * 4 + NBW * wid;
+    const int NB = d_out >> 4;
+    v4f acc[MB][NBW];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) acc[m][j] = v4f{0, 0, 0, 0};
+    // lane holds rows m0 + 16m + 4lg + r and column 16 (nb0 + j) + lr; rows and blocks past the
+    // ends read a valid partial (never stored)
+    size_t off[MB][NBW][4];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                off[m][j][r] = (size_t)min(m0 + 16 * m + 4 * lg + r, T - 1) * d_out + min(nb0 + j, NB - 1) * 16 + lr;
+    for (int ks = 0; ks < ksplit; ++ks) {
+        const float* pk = part + (size_t)ks * T * d_out;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int j = 0; j < NBW; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[m][j][r] += pk[off[m][j][r]];
+    }
+    a16_epilogue<MB, NBW>(acc, m0, nb0, T, d_out, lane, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y);
+}
+
 inline int a16_mb(int T) { return T >= 512 ? 8 : 4; }
 // channel blocks per workgroup: the ring kernel (many tokens, bf16 x) takes 16
 inline int a16_nbg(int T, int x_dtype) { return T >= 512 && x_dtype == QE_BF16 ? 16 : GA_NB; }
@@ -440,7 +483,10 @@ hipError_t launch_gemm_a16(const void* x, int x_dtype, int T, int d_in, int d_ou
 #undef QE_RING_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || fused) return e;
-    return launch_skinny_finish(part, ksplit, T, d_out, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, y, st);
+    const int f_tm = (T + 15) / 16;
+    hipLaunchKernelGGL(gemm_a16_finish_kernel, dim3(f_tm * ((d_out / 16 + 3) / 4)), dim3(256), 0, st, part,
+                       ksplit, T, d_out, f_tm, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y);
+    return hipGetLastError();
 }
 
 }  // namespace qe
