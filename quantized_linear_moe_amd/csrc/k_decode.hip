@@ -517,52 +517,6 @@ hipError_t launch_skinny_finish(const float* part, int ksplit, int T, int d_out,
     return hipGetLastError();
 }
 
-// Split-K main product, A6/A8: one thread per output,
-//   y[t][i] = (sum over splits of the exact int32 partials) * s_x[t] * s_w[i]
-//             + u[t] . Bt_s[i] + v[t] . Bt_r[e_t][i]
-// with the adapter rows read as 16-byte vectors (the expert clamped into range, as in the
-// fused epilogue).
-__global__ __launch_bounds__(256) void gemm_split_finish_kernel(const int32_t* __restrict__ part, int ksplit, int T,
-                                                                int d_out, const float* __restrict__ s_x,
-                                                                const float* __restrict__ w_scale,
-                                                                const uint16_t* __restrict__ u,
-                                                                const uint16_t* __restrict__ bt_s, int rs_pad,
-                                                                const uint16_t* __restrict__ v,
-                                                                const int32_t* __restrict__ expert, int n_r,
-                                                                const uint16_t* __restrict__ bt_r, int rr_pad,
-                                                                float* __restrict__ y) {
-    const int i = blockIdx.x * 256 + threadIdx.x, t = blockIdx.y;
-    if (i >= d_out) return;
-    const int32_t* p = part + (size_t)t * d_out + i;
-    const size_t stride = (size_t)T * d_out;
-    int32_t acc = 0;  // integer sums: exact in any order
-    int k = 0;
-    for (; k + 8 <= ksplit; k += 8) {
-        int32_t a[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) a[q] = p[(size_t)(k + q) * stride];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc += a[q];
-    }
-    for (; k < ksplit; ++k) acc += p[(size_t)k * stride];
-    float out = (float)acc * s_x[t] * w_scale[i];
-    if (u) out += dot_bf16_rows(u + (size_t)t * rs_pad, bt_s + (size_t)i * rs_pad, rs_pad);
-    if (v && expert && n_r > 0) {
-        const int e = min(max(expert[t], 0), n_r - 1);
-        out += dot_bf16_rows(v + (size_t)t * rr_pad, bt_r + ((size_t)e * d_out + i) * rr_pad, rr_pad);
-    }
-    y[(size_t)t * d_out + i] = out;
-}
-
-hipError_t launch_gemm_split_finish(const int32_t* part, int ksplit, int T, int d_out, const float* s_x,
-                                    const float* w_scale, const uint16_t* u, const uint16_t* bt_s, int rs_pad,
-                                    const uint16_t* v, const int32_t* expert, int n_r, const uint16_t* bt_r,
-                                    int rr_pad, float* y, hipStream_t st) {
-    if (T <= 0) return hipSuccess;
-    hipLaunchKernelGGL(gemm_split_finish_kernel, dim3((d_out + 255) / 256, T), dim3(256), 0, st, part, ksplit, T,
-                       d_out, s_x, w_scale, u, bt_s, rs_pad, v, expert, n_r, bt_r, rr_pad, y);
-    return hipGetLastError();
-}
 
 // Unfused routed experts, grouped by expert bucket: y[perm[p]][i] += v[perm[p]] . Bt_r[e][i] with
 // e the bucket of position p.  A workgroup takes 64 bucket positions x 256 channels (wave: 64

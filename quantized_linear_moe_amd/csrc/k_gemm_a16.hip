@@ -430,6 +430,35 @@ __global__ __launch_bounds__(256) void gemm_a16_finish_kernel(
     a16_epilogue<MB, NBW>(acc, m0, nb0, T, d_out, lane, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y);
 }
 
+// Finish of a K-split int8 main product (A6 / A8 with few tokens): the int32 partials of a 16 x 64
+// tile summed in split order (exact), times s_x[t], then the same epilogue (times s_w, low-rank
+// terms on MFMA, adapter rows read once per 16 tokens).  The main term is ((float)acc * s_x) * s_w,
+// as in the unsplit GEMM.
+__global__ __launch_bounds__(256) void gemm_i8_finish_kernel(
+    const int32_t* __restrict__ part, int ksplit, int T, int d_out, int n_tm, const float* __restrict__ s_x,
+    const float* __restrict__ w_scale, const uint16_t* __restrict__ u, const uint16_t* __restrict__ bt_s, int rs_pad,
+    const uint16_t* __restrict__ v, const int32_t* __restrict__ expert, const uint16_t* __restrict__ bt_r,
+    int rr_pad, int n_r, float* __restrict__ y) {
+    const int tm = blockIdx.x % n_tm, tn = blockIdx.x / n_tm;
+    const int m0 = tm * 16;
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int nb0 = tn * 4 + wid;
+    const int NB = d_out >> 4;
+    size_t off[4];
+    int32_t si[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) off[r] = (size_t)min(m0 + 4 * lg + r, T - 1) * d_out + min(nb0, NB - 1) * 16 + lr;
+    for (int ks = 0; ks < ksplit; ++ks) {
+        const int32_t* pk = part + (size_t)ks * T * d_out;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) si[r] += pk[off[r]];
+    }
+    v4f acc[1][1];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[0][0][r] = (float)si[r] * s_x[min(m0 + 4 * lg + r, T - 1)];
+    a16_epilogue<1, 1>(acc, m0, nb0, T, d_out, lane, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y);
+}
+
 inline int a16_mb(int T) { return T >= 512 ? 8 : 4; }
 // channel blocks per workgroup: the ring kernel (many tokens, bf16 x) takes 16
 inline int a16_nbg(int T, int x_dtype) { return T >= 512 && x_dtype == QE_BF16 ? 16 : GA_NB; }
@@ -486,6 +515,18 @@ hipError_t launch_gemm_a16(const void* x, int x_dtype, int T, int d_in, int d_ou
     const int f_tm = (T + 15) / 16;
     hipLaunchKernelGGL(gemm_a16_finish_kernel, dim3(f_tm * ((d_out / 16 + 3) / 4)), dim3(256), 0, st, part,
                        ksplit, T, d_out, f_tm, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_split_finish(const int32_t* part, int ksplit, int T, int d_out, const float* s_x,
+                                    const float* w_scale, const uint16_t* u, const uint16_t* bt_s, int rs_pad,
+                                    const uint16_t* v, const int32_t* expert, int n_r, const uint16_t* bt_r,
+                                    int rr_pad, float* y, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (d_out % 16) return hipErrorInvalidValue;
+    const int n_tm = (T + 15) / 16;
+    hipLaunchKernelGGL(gemm_i8_finish_kernel, dim3(n_tm * ((d_out / 16 + 3) / 4)), dim3(256), 0, st, part, ksplit, T,
+                       d_out, n_tm, s_x, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y);
     return hipGetLastError();
 }
 
