@@ -540,11 +540,20 @@ __global__ __launch_bounds__(256) void routed_lora_kernel(const uint16_t* __rest
         while (e + 1 < n_r && offsets[e + 1] <= p) ++e;
         return e;
     };
-    v4f acc[4][4];
+    // The y rows this lane updates are requested first, at clamped addresses, so their latency
+    // overlaps the adapter loads and MFMAs; lane holds positions pb + 4 lg + r and channels
+    // ch0 .. ch0 + 3 (d_out is a multiple of 16, so a clamped ch0 stays 16-byte aligned).
+    const int ch0 = nw + 4 * lr, ch0c = min(ch0, d_out - 4);
+    int tr[4][4];
+    v4f yo[4][4];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = v4f{0, 0, 0, 0};
+        for (int r = 0; r < 4; ++r) tr[mb][r] = min(max(perm[min(p0 + 16 * mb + 4 * lg + r, T - 1)], 0), T - 1);
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) yo[mb][r] = *reinterpret_cast<const v4f*>(y + (size_t)tr[mb][r] * d_out + ch0c);
     int chs[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) chs[nb] = min(nw + 4 * lr + nb, d_out - 1);  // past d_out: never stored
@@ -552,6 +561,9 @@ __global__ __launch_bounds__(256) void routed_lora_kernel(const uint16_t* __rest
     for (int mb = 0; mb < 4; ++mb) {
         const int pb = p0 + 16 * mb;
         if (pb >= T) break;  // wave-uniform
+        v4f acc[4];
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[nb] = v4f{0, 0, 0, 0};
         const int p = min(pb + lr, T - 1);
         const bool prow = pb + lr < T;
         const int e_row = expert_of(p);
@@ -565,26 +577,20 @@ __global__ __launch_bounds__(256) void routed_lora_kernel(const uint16_t* __rest
                 for (int nb = 0; nb < 4; ++nb) {
                     const v8bf b =
                         *reinterpret_cast<const v8bf*>(bt_r + ((size_t)e * d_out + chs[nb]) * rr_pad + k0 + lg * 8);
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[mb][nb], 0, 0, 0);
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[nb], 0, 0, 0);
                 }
             }
         }
-    }
-    // lane holds positions pb + 4 lg + r and channels nw + 4 lr + nb (d_out is a multiple of 16)
-    const int ch0 = nw + 4 * lr;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+        // each (token, channel) appears once in a grouping, so the in-place update is race-free
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int p = p0 + 16 * mb + 4 * lg + r;
-            if (p >= T || ch0 >= d_out) continue;
-            const int t = min(max(perm[p], 0), T - 1);
-            v4f* dst = reinterpret_cast<v4f*>(y + (size_t)t * d_out + ch0);
-            v4f o = *dst;
+            if (pb + 4 * lg + r >= T || ch0 >= d_out) continue;
+            v4f o = yo[mb][r];
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) o[nb] += acc[mb][nb][r];
-            *dst = o;
+            for (int nb = 0; nb < 4; ++nb) o[nb] += acc[nb][r];
+            *reinterpret_cast<v4f*>(y + (size_t)tr[mb][r] * d_out + ch0) = o;
         }
+    }
 }
 
 hipError_t launch_routed_lora(const uint16_t* v, int rr_pad, const int32_t* offsets, const int32_t* perm, int n_r,
