@@ -327,14 +327,31 @@ __global__ __launch_bounds__(1024) void xproj_finish_kernel(const float* __restr
                                                             const int32_t* __restrict__ expert_in,
                                                             float* __restrict__ scores, int32_t* __restrict__ expert_out,
                                                             uint16_t* __restrict__ u, uint16_t* __restrict__ v) {
-    extern __shared__ float sums[];  // [4][ncols_pad]: quarter sums, then the total in row 0
+    extern __shared__ float sums[];  // [nq][ncols_pad]: partial sums over split ranges, then the total in row 0
     __shared__ int s_e;
     const int t = blockIdx.x;
     if (t >= T) return;
+    const int nq = blockDim.x >> 8;  // 1 or 4 ranges of splits
     const int q = threadIdx.x >> 8, c0 = threadIdx.x & 255;
-    const int k0 = ksplit * q / 4, k1 = ksplit * (q + 1) / 4;
+    const int k0 = ksplit * q / nq, k1 = ksplit * (q + 1) / nq;
     const size_t stride = (size_t)T * ncols_pad;
-    for (int c = c0; c < ncols_pad; c += 256) {
+    // Columns this call reads: only the router's when nothing else is written, only the shared
+    // and the given expert's columns when the expert comes in; else every column.
+    const bool only_router = router_col >= 0 && !u && !v;
+    const int e_in = (router_col < 0 && expert_in) ? min(max(expert_in[t], 0), max(n_r - 1, 0)) : -1;
+    auto for_cols = [&](auto&& f) {
+        if (only_router) {
+            for (int c = c0; c < n_r; c += 256) f(router_col + c);
+        } else if (e_in >= 0) {
+            if (u && se_col >= 0)
+                for (int c = c0; c < rs_pad; c += 256) f(se_col + c);
+            if (v && re_col >= 0)
+                for (int c = c0; c < rr_pad; c += 256) f(re_col + e_in * rr_pad + c);
+        } else {
+            for (int c = c0; c < ncols_pad; c += 256) f(c);
+        }
+    };
+    for_cols([&](int c) {
         const float* p = part + (size_t)t * ncols_pad + c;
         float s = 0.0f;
         int k = k0;
@@ -348,12 +365,12 @@ __global__ __launch_bounds__(1024) void xproj_finish_kernel(const float* __restr
         }
         for (; k < k1; ++k) s += p[(size_t)k * stride];
         sums[q * ncols_pad + c] = s;
-    }
+    });
     __syncthreads();
-    if (q == 0) {
-        for (int c = c0; c < ncols_pad; c += 256)
+    if (q == 0 && nq == 4)
+        for_cols([&](int c) {
             sums[c] = ((sums[c] + sums[ncols_pad + c]) + sums[2 * ncols_pad + c]) + sums[3 * ncols_pad + c];
-    }
+        });
     __syncthreads();
     if (threadIdx.x == 0) {
         int e = 0;
@@ -374,11 +391,11 @@ __global__ __launch_bounds__(1024) void xproj_finish_kernel(const float* __restr
     __syncthreads();
     const int e = s_e;
     if (u && se_col >= 0) {
-        for (int c = threadIdx.x; c < rs_pad; c += 1024)
+        for (int c = threadIdx.x; c < rs_pad; c += blockDim.x)
             u[(size_t)t * rs_pad + c] = c < r_s ? (uint16_t)f32_to_bf16_bits(sums[se_col + c]) : (uint16_t)0;
     }
     if (v && re_col >= 0) {
-        for (int c = threadIdx.x; c < rr_pad; c += 1024)
+        for (int c = threadIdx.x; c < rr_pad; c += blockDim.x)
             v[(size_t)t * rr_pad + c] = c < r_r ? (uint16_t)f32_to_bf16_bits(sums[re_col + e * rr_pad + c]) : (uint16_t)0;
     }
 }
@@ -390,7 +407,11 @@ hipError_t launch_xproj_finish(const float* part, int ksplit, int T, int ncols_p
     if (T <= 0) return hipSuccess;
     // columns are relative to the projected block that starts at col0
     auto rel = [&](int c) { return c < 0 ? -1 : c - col0; };
-    hipLaunchKernelGGL(xproj_finish_kernel, dim3(T), dim3(1024), 4 * (size_t)ncols_pad * sizeof(float), st, part, ksplit, T,
+    // a call that reads only a few columns (router alone, or one known expert) takes one wave
+    // group per token: the dispatch of 16 waves per token would cost more than its loads
+    const bool few = (router_col >= 0 && !u && !v) || (router_col < 0 && expert_in);
+    const int nq = few ? 1 : 4;
+    hipLaunchKernelGGL(xproj_finish_kernel, dim3(T), dim3(256 * nq), nq * (size_t)ncols_pad * sizeof(float), st, part, ksplit, T,
                        ncols_pad, rel(se_col), r_s, rs_pad, rel(re_col), n_r, r_r, rr_pad, rel(router_col), expert_in,
                        scores, expert_out, u, v);
     return hipGetLastError();
