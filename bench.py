@@ -45,12 +45,23 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512,
+                    help="tokens of the workload the C oracle runs on every host core")
+    ap.add_argument("--cpu-sample-tokens-1t", type=int, default=16,
+                    help="tokens the C oracle runs on one host thread")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="time the int8 and bf16 MFMA ceilings of this part at the 72B layer's GEMM shapes: the "
+                         "library's main GEMM, torch's int8 and bf16 matrix products (hipBLASLt) and the MFMA "
+                         "probe loops; prints one JSON line and exits")
+    ap.add_argument("--mfma-counters", metavar="DIR",
+                    help="summarize a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_I8 "
+                         "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE GRBM_COUNT --kernel-trace "
+                         "--output-format csv run (its output directory) per kernel and exit")
     ap.add_argument("--write-traffic", nargs=4, metavar="DIR",
                     help="rocprofv3 CSV directories: bench FETCH_SIZE, bench WRITE_SIZE, copy FETCH_SIZE, "
                          "copy WRITE_SIZE; writes the GEMM traffic summary under profiles/ and exits")
@@ -80,6 +91,49 @@ def load_traffic(per_launch_alg_bytes):
 
 
 TRAFFIC_KERNEL = "gemm_w4_kernel<8, true>"
+
+
+def mfma_counters(d, n_simd=1024, n_xcd=8):
+    """Matrix-core utilization and effective clock per kernel from one rocprofv3 counter run
+    (CSV output).  Per dispatch: GRBM_GUI_ACTIVE is summed over the 8 XCDs, so
+    clock = GRBM_GUI_ACTIVE / 8 / duration; MFMA busy = sum of SQ_VALU_MFMA_BUSY_CYCLES over
+    the 1024 SIMDs / (GRBM_GUI_ACTIVE / 8 * 1024) (rocprofv3's MfmaUtil); int8 / bf16 ops =
+    SQ_INSTS_VALU_MFMA_MOPS_* * 512.  Dispatches shorter than 100 us are left out (their
+    GRBM counts include the dispatch overhead around the kernel)."""
+    import csv
+    import glob
+    import collections
+    cc = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    kt = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)
+    if not cc or not kt:
+        raise SystemExit(f"no counter_collection.csv / kernel_trace.csv under {d}")
+    dur = {}
+    with open(kt[0]) as fh:
+        for r in csv.DictReader(fh):
+            dur[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    disp = collections.defaultdict(dict)
+    with open(cc[0]) as fh:
+        for r in csv.DictReader(fh):
+            v = disp[r["Dispatch_Id"]]
+            v[r["Counter_Name"]] = v.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            v["kernel"] = r["Kernel_Name"]
+    groups = collections.defaultdict(list)
+    for did, v in disp.items():
+        if did in dur and dur[did] >= 100_000:
+            v["ns"] = dur[did]
+            groups[v["kernel"].split("(")[0][:72]].append(v)
+    print(f"{'kernel':72s} {'n':>4s} {'avg_us':>9s} {'clock_GHz':>9s} {'mfma_busy':>9s} {'int8_TOP/s':>10s} "
+          f"{'bf16_TFLOP/s':>12s}")
+    for name, vs in sorted(groups.items(), key=lambda kv: -sum(v["ns"] for v in kv[1])):
+        ns = sum(v["ns"] for v in vs)
+        gui = sum(v.get("GRBM_GUI_ACTIVE", 0.0) for v in vs)
+        busy = sum(v.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for v in vs)
+        i8 = sum(v.get("SQ_INSTS_VALU_MFMA_MOPS_I8", 0.0) for v in vs) * 512
+        bf = sum(v.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for v in vs) * 512
+        clock = gui / n_xcd / ns
+        util = busy / (gui / n_xcd * n_simd) if gui else 0.0
+        print(f"{name:72s} {len(vs):4d} {ns / len(vs) / 1e3:9.1f} {clock:9.3f} {util:9.3f} {i8 / ns / 1e3:10.1f} "
+              f"{bf / ns / 1e3:12.1f}")
 
 
 def write_traffic(d_bench_fetch, d_bench_write, d_copy_fetch, d_copy_write):
@@ -165,6 +219,80 @@ def copy_calibration():
                       "gbs_read_plus_write": round(8 * n / (ms * 1e-3) / 1e9, 1)}), flush=True)
 
 
+def ceiling(reps=20):
+    """The int8 (and bf16) matrix-core rate this part reaches at the Qwen2VL-72B layer's GEMM shapes
+    (T = 4096 tokens; q 8192x8192, gate/up 8192x29568, down 29568x8192), by three independent routes:
+    the library's main GEMM (prologue first, then qe_wq_gemm timed alone), torch's int8 product
+    torch._int_mm and torch's bf16 linear (both hipBLASLt) on the same shapes, and the MFMA probe
+    loops.  Median of `reps` event-timed launches each, on torch's current stream (the one every
+    launch here uses).  Run under rocprofv3 --pmc for the matrix-core busy cycles and the clock."""
+    import torch
+    import synth
+    import quantized_linear_moe_amd as qe
+    from quantized_linear_moe_amd import libqe
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def med_ms(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    cfg = synth.get_config("qwen2vl_72b")
+    T = cfg.T
+    rows = []
+    for name in ("q", "gate", "down"):
+        spec = next(l for l in cfg.linears if l.name == name)
+        params = synth.gen_linear(cfg, spec)
+        layer = qe.QELinear.from_params(params, cfg.w_bits, cfg.a_bits, device=dev)
+        x = synth.gen_activations(cfg, spec.stream).to(dev)
+        ws = layer.workspace(T)
+        codes = torch.empty(T, spec.d_in, dtype=torch.int8, device=dev)
+        s_x = torch.empty(T, dtype=torch.float32, device=dev)
+        u = torch.empty(T, libqe.rank_pad(cfg.r_shared), dtype=torch.bfloat16, device=dev)
+        v = torch.empty(T, libqe.rank_pad(cfg.r_routed), dtype=torch.bfloat16, device=dev)
+        e = torch.empty(T, dtype=torch.int32, device=dev)
+        perm = torch.empty(T, dtype=torch.int32, device=dev)
+        y = torch.empty(T, spec.d_out, dtype=torch.float32, device=dev)
+        libqe.qe_linear_prologue(layer.lin, x, codes, s_x, u, v, e, ws, perm=perm)
+        t_qe = med_ms(lambda: libqe.qe_wq_gemm(layer.lin, codes, s_x, None, T, u, v, e, y, None, ws, perm=perm))
+        ops = 2.0 * T * spec.d_in * spec.d_out
+        row = {"shape": f"{T}x{spec.d_in}x{spec.d_out}", "linear": name,
+               "qe_gemm_us": round(t_qe * 1e3, 1), "qe_gemm_tops": round(ops / (t_qe * 1e-3) / 1e12, 1)}
+        # torch int8 product: codes [T, d_in] times an int8 matrix of the same shape as the weights
+        wq = torch.randint(-7, 8, (spec.d_out, spec.d_in), dtype=torch.int8, device=dev)
+        for lay, b in (("nt", wq.t()), ("nn", wq.t().contiguous())):
+            try:
+                t_i = med_ms(lambda: torch._int_mm(codes, b))
+                row[f"torch_int_mm_{lay}_us"] = round(t_i * 1e3, 1)
+                row[f"torch_int_mm_{lay}_tops"] = round(ops / (t_i * 1e-3) / 1e12, 1)
+            except RuntimeError as ex:  # not every layout is supported by the library
+                row[f"torch_int_mm_{lay}_error"] = str(ex).splitlines()[0][:160]
+        del wq
+        wb = torch.from_numpy(params["W_f"]).to(torch.bfloat16).to(dev)
+        xb = x.to(torch.bfloat16)
+        t_b = med_ms(lambda: torch.nn.functional.linear(xb, wb))
+        row["torch_bf16_linear_us"] = round(t_b * 1e3, 1)
+        row["torch_bf16_linear_tflops"] = round(ops / (t_b * 1e-3) / 1e12, 1)
+        rows.append(row)
+        log(f"ceiling {name}: {row}")
+        del layer, x, ws, codes, s_x, u, v, e, perm, y, wb, xb, params
+        torch.cuda.empty_cache()
+    peaks = measured_peaks(torch, libqe, dev)
+    print(json.dumps({"ceiling_qwen2vl72b_T4096": rows, "probes": peaks,
+                      "spec": {"int8_tops": PEAK_INT8_TOPS, "bf16_tflops": PEAK_BF16_TFLOPS}}), flush=True)
+
+
 def main():
     args = parse()
     if args.write_traffic:
@@ -172,6 +300,12 @@ def main():
         return
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.ceiling:
+        ceiling()
+        return
+    if args.mfma_counters:
+        mfma_counters(args.mfma_counters)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -194,15 +328,14 @@ def main():
     t_setup = time.time()
     xs_cpu = {s: synth.gen_activations(cfg, s) for s in cfg.streams()}
     xs = {s: t.to(dev) for s, t in xs_cpu.items()}
-    layers, oracle_w = [], []
+    layers, host_params = [], []
     for spec in cfg.linears:
         params = synth.gen_linear(cfg, spec)
         layer = qe.QELinear.from_params(params, cfg.w_bits, cfg.a_bits, device=dev)
         if want_cpu:
-            from oracle import qe_oracle as O  # CPU-baseline leg only
-            qw, s_w = O.quant_weights(params["W_f"], params["s"], cfg.w_bits)
-            oracle_w.append((qw, s_w, params))
-        del params["W_f"]
+            host_params.append(params)  # the CPU-baseline leg quantizes W_f with the oracle
+        else:
+            del params["W_f"]
         layers.append((spec, layer))
         log(f"prepared {spec.name} {spec.d_in}->{spec.d_out}")
     ws = torch.empty(max(libqe.qe_workspace_bytes(l.lin, T) for _, l in layers), dtype=torch.uint8, device=dev)
@@ -216,6 +349,8 @@ def main():
             e=torch.empty(T, dtype=torch.int32, device=dev),
             perm=torch.empty(T, dtype=torch.int32, device=dev),
             y=torch.empty(T, spec.d_out, dtype=torch.float32, device=dev)))
+    # reading 1 GiB (four times the 256 MB Infinity Cache) evicts it with clean lines
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     log(f"setup {time.time() - t_setup:.1f}s")
 
@@ -239,28 +374,41 @@ def main():
         step()
     torch.cuda.synchronize()
 
+    ev_t = lambda: torch.cuda.Event(enable_timing=True)
     K = args.steps
-    evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in layers]
-           for _ in range(K)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [[(ev_t(), ev_t()) for _ in layers] for _ in range(K)]
+    marks = [ev_t() for _ in range(K + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    start.record()
+    marks[0].record()
     for k in range(K):
         step(evs[k])
-    end.record()
+        marks[k + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(end) / K
+    ms_step = marks[0].elapsed_time(marks[K]) / K
+    step_ms = np.array([marks[k].elapsed_time(marks[k + 1]) for k in range(K)])
     gemm_ms = np.array([[a.elapsed_time(b) for (a, b) in evs[k]] for k in range(K)])  # [K, 7]
     gemm_ms_step = float(gemm_ms.sum(axis=1).mean())
+
+    # cold steps: the Infinity Cache flushed before each (timed alone, not part of `value`)
+    cold = []
+    for _ in range(min(K, 20)):
+        flush.sum()
+        a, b = ev_t(), ev_t()
+        a.record()
+        step()
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
 
     # the composite entry point on the same inputs (must match the split prologue + GEMM)
     for _ in range(2):
         for i, (spec, layer) in enumerate(layers):
             layer.forward(xs[spec.stream], bufs[i]["y"], bufs[i]["e"], ws)
     torch.cuda.synchronize()
-    s2, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s2, e2 = ev_t(), ev_t()
     s2.record()
     for _ in range(K):
         for i, (spec, layer) in enumerate(layers):
@@ -272,15 +420,19 @@ def main():
     # ------------------------------------------------------------ accounting
     int_ops = adapter_flops = alg_bytes = 0.0
     per_linear = []
+    gpu_routes = []
     for i, (spec, layer) in enumerate(layers):
-        n_distinct = int(torch.unique(bufs[i]["e"]).numel())
+        e_host = bufs[i]["e"].cpu().numpy()
+        gpu_routes.append(e_host)
+        n_distinct = int(np.unique(e_host).size)
         im, am, ab = libqe.qe_linear_cost(layer.lin, T, n_distinct, 2)
         int_ops += 2 * im
         adapter_flops += 2 * am
         alg_bytes += ab
         per_linear.append(dict(name=spec.name, d_in=spec.d_in, d_out=spec.d_out,
                                gemm_us=round(float(gemm_ms[:, i].mean()) * 1e3, 2),
-                               gemm_tops=round(2 * im / (gemm_ms[:, i].mean() * 1e-3) / 1e12, 1)))
+                               gemm_tops=round(2 * im / (gemm_ms[:, i].mean() * 1e-3) / 1e12, 1),
+                               expert_histogram=np.bincount(e_host, minlength=cfg.n_routed).tolist()))
     big = [i for i, (spec, _) in enumerate(layers) if uses_128_token_tiles(T, spec.d_out)]
     big_ops = sum(2 * libqe.qe_linear_cost(layers[i][1].lin, T, 1, 2)[0] for i in big)
     big_ms = float(gemm_ms[:, big].sum(axis=1).mean())  # per step
@@ -307,7 +459,17 @@ def main():
                         "shared rank 32, 8 routed experts rank 32, router d_in x 8",
             "T": T, "w_bits": 4, "a_bits": 6, "r_shared": 32, "n_routed": 8, "r_routed": 32,
         },
+        "step_ms": {"median": round(float(np.median(step_ms)), 4), "p10": round(float(np.percentile(step_ms, 10)), 4),
+                    "p90": round(float(np.percentile(step_ms, 90)), 4),
+                    "cold_median": round(float(np.median(cold)), 4),
+                    "cold_p10": round(float(np.percentile(cold, 10)), 4),
+                    "cold_p90": round(float(np.percentile(cold, 90)), 4), "cold_steps": len(cold),
+                    "note": "per-step HIP events over the K timed steps (warm: inputs and weights as the previous "
+                            "step left the caches); cold: the Infinity Cache flushed by reading 1 GiB before each "
+                            "step"},
         "roofline": {
+            "scope": "dominant kernel only: the main GEMM's 128-token-tile launches (q, o, gate, up, down); the "
+                     "whole step is in layer_roofline",
             "kernel": "gemm_w4_kernel<8, true> (int8 MFMA main GEMM, 128-token tiles, fused dequant/SE/RE epilogue)",
             "bound": "mfma",
             "achieved": round(achieved, 1),
@@ -334,14 +496,13 @@ def main():
 
     peaks = measured_peaks(torch, libqe, dev)
     result["measured_peaks"] = peaks
-    result["roofline"]["peak_measured"] = peaks["int8_mfma_tops"]
-    result["roofline"]["frac_measured"] = round(achieved / peaks["int8_mfma_tops"], 4)
 
     if not args.no_extras:
         result["extras"] = extras(torch, synth, qe, libqe, dev, peaks)
 
     if want_cpu:
-        result["cpu_baseline"] = cpu_baseline(torch, cfg, xs_cpu, oracle_w, args.cpu_sample_tokens)
+        result["cpu_baseline"] = cpu_baseline(torch, cfg, xs_cpu, host_params, gpu_routes, args.cpu_sample_tokens,
+                                              args.cpu_sample_tokens_1t)
 
     print(json.dumps(result), flush=True)
 
@@ -789,30 +950,65 @@ def extras(torch, synth, qe, libqe, dev, peaks):
     return out
 
 
-def cpu_baseline(torch, cfg, xs_cpu, oracle_w, n_tok):
-    """The CPU oracle as it stands, on a bounded sample of the same workload: n_tok of
-    the T tokens through all seven linears (its own weight quantization is done
-    beforehand and not timed, as the GPU's weight packing is not)."""
+def cpu_baseline(torch, cfg, xs_cpu, host_params, gpu_routes, n_tok, n_tok_1t):
+    """The plain C oracle (OpenMP over tokens) as it stands, on a bounded sample of the same
+    workload: n_tok of the T tokens through all seven linears on every host thread, and n_tok_1t
+    tokens on one thread (its weight quantization is done beforehand and not timed, as the GPU's
+    weight packing is not).  The numpy oracle is timed on the same sample beside it.  The
+    oracle's router also runs on all T tokens of every linear: near-tie tokens (the two smallest
+    scores closer than 1e-4 of their magnitude) are counted, and so are tokens whose GPU route
+    differs from the oracle's (allowed only at near-ties)."""
     from oracle import qe_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    from oracle import qe_ref as C
     rng = np.random.default_rng(7)
     toks = np.sort(rng.choice(cfg.T, n_tok, replace=False))
     f32 = lambda t: None if t is None else t.float().numpy()
-    t_total = 0.0
-    for (spec, (qw, s_w, params)) in zip(cfg.linears, oracle_w):
-        x = xs_cpu[spec.stream][torch.as_tensor(toks)].float().numpy()
+    n_all = C.num_threads()
+    t_all = t_one = t_np = 0.0
+    routes = []
+    for li, (spec, params) in enumerate(zip(cfg.linears, host_params)):
+        qw, s_w = C.quant_weights(params["W_f"], params["s"], cfg.w_bits)
+        del params["W_f"]
+        ad = dict(A_s=f32(params["A_s"]), B_s=f32(params["B_s"]), A_r=f32(params["A_r"]), B_r=f32(params["B_r"]),
+                  R=f32(params["R"]))
+        x_all = xs_cpu[spec.stream].float().numpy()
+        x = x_all[toks]
+        C.set_threads(n_all)
         t0 = time.perf_counter()
-        O.qe_linear(x, True, params["s"], qw, s_w, cfg.a_bits, A_s=f32(params["A_s"]), B_s=f32(params["B_s"]),
-                    A_r=f32(params["A_r"]), B_r=f32(params["B_r"]), R=f32(params["R"]))
-        t_total += time.perf_counter() - t0
-        log(f"oracle {spec.name}: {time.perf_counter() - t0:.2f}s")
-    return {"value": round(n_tok / t_total, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_tok} of {cfg.T} tokens through all 7 linears of the same layer "
-                      f"({t_total:.1f} s of oracle time; weight quantization untimed)"}
+        C.qe_linear(x, True, params["s"], qw, s_w, cfg.a_bits, **ad)
+        t_all += time.perf_counter() - t0
+        C.set_threads(1)
+        t0 = time.perf_counter()
+        C.qe_linear(x[:n_tok_1t], True, params["s"], qw, s_w, cfg.a_bits, **ad)
+        t_one += time.perf_counter() - t0
+        C.set_threads(n_all)
+        t0 = time.perf_counter()
+        O.qe_linear(x, True, params["s"], qw, s_w, cfg.a_bits, **ad)
+        t_np += time.perf_counter() - t0
+        r = C.route(x_all, ad["R"])
+        near = r["margin"] < 1e-4 * r["margin_scale"]
+        differ = gpu_routes[li] != r["expert"]
+        routes.append({"linear": spec.name, "near_tie_tokens": int(near.sum()), "routes_differing": int(differ.sum()),
+                       "routes_differing_away_from_near_ties": int((differ & ~near).sum()),
+                       "oracle_expert_histogram": np.bincount(r["expert"], minlength=cfg.n_routed).tolist()})
+        log(f"oracle {spec.name}: all-core {t_all:.2f}s cumulative; routes {routes[-1]}")
+        del qw, x_all
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), "unknown")
+    except OSError:  # pragma: no cover
+        model = "unknown"
+    return {"value": round(n_tok / t_all, 2), "unit": "tokens/s", "cores": int(n_all), "kind": "oracle",
+            "sample": f"{n_tok} of {cfg.T} tokens through all 7 linears of the same layer on {n_all} threads "
+                      f"({t_all:.1f} s of oracle time); weight quantization untimed",
+            "implementation": "plain C oracle (oracle/qe_ref.c: loops in index order, int64 / double sums, "
+                              "gcc -O3 -march=x86-64-v3 -fopenmp over tokens)",
+            "cpu_model": model,
+            "one_thread": {"value": round(n_tok_1t / t_one, 3), "unit": "tokens/s",
+                           "sample": f"{n_tok_1t} tokens through all 7 linears ({t_one:.1f} s)"},
+            "numpy_oracle": {"value": round(n_tok / t_np, 2), "unit": "tokens/s",
+                             "sample": f"the same {n_tok} tokens ({t_np:.1f} s; BLAS float64 products)"},
+            "routing_vs_oracle_all_tokens": routes}
 
 
 if __name__ == "__main__":

@@ -162,6 +162,9 @@ int qe_route(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, fl
 
 /* (a4/a6, first half) Adapter inputs: u = bf16(x) . A_s and v[t] = bf16(x)[t] . A_{expert[t]},
  * accumulated in float32 and stored as bf16 (round to nearest even).
+ * DeepRead summary, "Method": the shared expert and each routed expert are low-rank
+ * adapters on the layer input; the listing's Table 7 counts d*r multiply-adds per token for
+ * each (dense over all input channels), which is this projection plus the second half.
  * Adapter-input rows are padded to whole bf16 MFMA steps: u is device bf16 [T][ru] with
  * ru = r_shared rounded up to a multiple of 32, v is [T][rv] with rv = r_routed rounded up
  * to a multiple of 32; the padding columns are written as zeros.
@@ -194,6 +197,8 @@ int qe_wq_gemm(const qe_linear* lin, const int8_t* codes, const float* s_x, cons
 /* (a6, unfused form) Routed experts as a grouped low-rank product over the
  * expert buckets: for each expert e and each token t in perm[offsets[e]..offsets[e+1]):
  *   y[t] += (bf16(x)[t] . A_e) . B_e      (y is ADDED to, not overwritten)
+ * DeepRead summary, "Method", Routed Experts: each token uses the one routed low-rank
+ * adapter its router picked; PaperDaily post "核心设计": the compensations are added.
  * expert/offsets/perm as produced by qe_route.
  */
 int qe_routed_lora(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T,
@@ -202,7 +207,9 @@ int qe_routed_lora(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t
 
 /* The activation-side half of the QE linear, fused: one pass of the x-projection gives the
  * router scores (a5) and both adapter inputs (a4/a6 first halves), then the per-token
- * quantization (a1).  Equivalent to qe_route + qe_adapter_inputs + qe_quant_act, with one
+ * quantization (a1).  DeepRead summary, "Method": smoothing and activation quantization
+ * (Shared Expert paragraph), the router that picks the expert with the smallest predicted
+ * error and the adapters on the layer input (Routed Experts paragraph).  Equivalent to qe_route + qe_adapter_inputs + qe_quant_act, with one
  * read of x for all projections.  Outputs (device, caller-owned): codes int8 [T][d_in] and
  * s_x float32 [T] (a_bits 6/8; both NULL for a_bits 16), u and v as for
  * qe_adapter_inputs (padded rows), expert int32 [T], and perm int32 [T] or NULL (tokens
@@ -213,7 +220,9 @@ int qe_linear_prologue(const qe_linear* lin, const void* x, int32_t x_dtype, int
                        void* ws, size_t ws_bytes, void* stream);
 
 /* The whole QE linear: qe_linear_prologue followed by qe_wq_gemm (a1 + a5 + a4 + a6 + a3,
- * or a7 for a_bits 16).  y: device float32 [T][d_out] (overwritten); expert_out: device int32 [T]
+ * or a7 for a_bits 16).  DeepRead summary, "Method": every token uses the quantized layer,
+ * the fixed shared expert and one routed expert chosen by the router; PaperDaily post
+ * "核心设计": the three results are summed; listing, Table 7: the cost s*d^2 + s*d*(2r + N_r).  y: device float32 [T][d_out] (overwritten); expert_out: device int32 [T]
  * or NULL (the routed expert of each token).  ws: qe_workspace_bytes(lin, T) bytes.
  */
 int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* y,

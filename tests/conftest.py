@@ -25,3 +25,14 @@ def pytest_collection_modifyitems(config, items):
     for it in items:
         if "gpu" in it.keywords:
             it.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    try:
+        from qe_testlib import ROUTING_REPORT
+    except Exception:  # pragma: no cover
+        return
+    if ROUTING_REPORT:
+        terminalreporter.section("routing against the oracle (near-ties may take either expert)")
+        for line in ROUTING_REPORT:
+            terminalreporter.write_line(line)

@@ -141,3 +141,19 @@ def test_pack_w3_layout_and_roundtrip():
             words = [(v >> (32 * k)) & 0xFFFFFFFF for k in range(3)]
             assert [int(w) for w in p[r, g]] == words
     assert np.array_equal(O.unpack_w3(p), c)
+
+
+def _load_weight_cases():
+    with open(os.path.join(GOLDEN, "rtn_weight_cases.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _load_weight_cases(), ids=lambda c: c["name"])
+def test_quant_weights_golden_cases(case):
+    # exact .5 ties must round to even (2.5 -> 2, 3.5 -> 4, 0.5 -> 0, 1.5 -> 2): a
+    # floor(v + 0.5) or round-half-away quantizer fails these
+    W = np.array(case["W"], np.float32)
+    s = np.array(case["s"], np.float32) if case["s"] is not None else None
+    q, s_w = O.quant_weights(W, s, case["w_bits"])
+    assert q.tolist() == case["codes"]
+    assert s_w.tolist() == case["s_w"]
