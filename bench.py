@@ -47,9 +47,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512,
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048,
                     help="tokens of the workload the C oracle runs on every host core")
-    ap.add_argument("--cpu-sample-tokens-1t", type=int, default=16,
+    ap.add_argument("--cpu-sample-tokens-1t", type=int, default=64,
                     help="tokens the C oracle runs on one host thread")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true")

@@ -394,6 +394,48 @@ int qe_build_experts(const float* W_f, const float* s, int32_t d_out, int32_t d_
                      float* A_s, float* B_s, float* A_r, float* B_r, double* sigma_s, double* sigma_r, void* ws,
                      size_t ws_bytes, void* stream);
 
+/* Expert construction by covariance whitening (the default construction).  PaperDaily post
+ * "西交大提出Quant Experts：token级量化补偿", section "核心设计": the error minus the shared and
+ * routed compensations, multiplied by the input token, is to leave the smallest residual, and
+ * the whitening SVD computes a covariance and whitens with it.  Reading: the SE of rank r is
+ * the minimizer of sum_t |(E - A_hat) x_t|^2 over the calibration tokens, i.e. A_hat =
+ * U_r U_r^T E with U_r the top-r eigenvectors of the error-output covariance
+ * C = sum_t (E x_t)(E x_t)^T (Eckart-Young on Z = E X^T; the same subspace as the SVD of E L
+ * with L L^T = X^T X); the RE of cluster g is the same fit of the residual E_1 = E - A_hat_s
+ * restricted to the cluster's input channels (DeepRead summary, "Method": the error left after
+ * the SE goes to one routed expert per cluster).  The top-r vectors come from the randomized
+ * subspace iteration (Halko, Martinsson and Tropp, Algorithms 4.4 and 5.1) on the operator Z,
+ * applied by passes over E and X; Z and C are never formed.
+ * qe_lowrank_fit_cov: factors of E diag(mask) for tokens X (device float32 [T][d_in]); mask
+ *   device float32 [d_in] of 0/1 or NULL (all channels); E device float32 [d_out][d_in];
+ *   omega device float32 [T][k] (Gaussian entries); 1 <= rank <= k <= min(128, d_out, T);
+ *   0 <= power_iters <= 16.  Outputs on the HOST: A float32 [d_in][rank] = diag(mask) E^T U_r,
+ *   B float32 [rank][d_out] = U_r^T (so x A B = x A_hat^T), sigma double [rank] = the top
+ *   singular values of Z (descending; directions below 1e-11 of the largest eigenvalue are
+ *   dropped: zero sigma and zero columns).  ws: device, qe_lowrank_cov_workspace_bytes(d_out,
+ *   d_in, T, k) bytes.  Synchronizes `stream`.
+ * qe_build_experts_cov: E = qe_quant_error(W_f, s); the SE (rank r_shared, 0 = none) =
+ *   qe_lowrank_fit_cov(E, all channels, omegas[0]); E_1 = E - (A_s B_s)^T; routed expert g <
+ *   n_routed (<= 16): qe_lowrank_fit_cov(E_1, mask of the channels dep_channels[t] with
+ *   labels[t] == g, omegas[1 + g]), rank r_routed (1..64).  x: device [T][d_in] calibration
+ *   tokens (QE_F32 or QE_BF16; the layer input the adapters read); omegas device float32
+ *   [1 + n_routed][T][k]; dep_channels, labels HOST int32 [n_dep].  Outputs on the HOST as for
+ *   qe_build_experts.  ws: device, qe_build_experts_cov_workspace_bytes(d_out, d_in, T, k,
+ *   max(r_shared, r_routed)) bytes (it holds E and a float32 copy of x).  Synchronizes `stream`.
+ * Errors: QE_ERR_INVALID_ARG / QE_ERR_ALIGNMENT / QE_ERR_WORKSPACE before any work;
+ * QE_ERR_UNSUPPORTED if the small eigenvalue iteration fails to converge; QE_ERR_HIP.
+ */
+size_t qe_lowrank_cov_workspace_bytes(int32_t d_out, int32_t d_in, int32_t T, int32_t k);
+int qe_lowrank_fit_cov(const float* E, int32_t d_out, int32_t d_in, const float* X, int32_t T, const float* mask,
+                       const float* omega, int32_t k, int32_t rank, int32_t power_iters, float* A, float* B,
+                       double* sigma, void* ws, size_t ws_bytes, void* stream);
+size_t qe_build_experts_cov_workspace_bytes(int32_t d_out, int32_t d_in, int32_t T, int32_t k, int32_t r_max);
+int qe_build_experts_cov(const float* W_f, const float* s, int32_t d_out, int32_t d_in, int32_t w_bits,
+                         const void* x, int32_t x_dtype, int32_t T, const int32_t* dep_channels,
+                         const int32_t* labels, int32_t n_dep, int32_t n_routed, int32_t r_shared, int32_t r_routed,
+                         const float* omegas, int32_t k, int32_t power_iters, float* A_s, float* B_s, float* A_r,
+                         float* B_r, double* sigma_s, double* sigma_r, void* ws, size_t ws_bytes, void* stream);
+
 /* Router fit (MCISLAB DeepRead summary, "Method", Routed Experts: the router estimates the error
  * each routed expert would leave on a token and the token takes the smallest; WisPaper post
  * "[CVPR 2025] Quant Experts: Adapting PTQ to the Heterogeneity of Vision-Language Tokens",

@@ -33,6 +33,22 @@ Readings where the pages leave a step open (each also listed in the design notes
     error).  Its target for token t and expert g is the mean absolute residual over the
     output channels, mean_i |x_t (E_1^T - A_g B_g)|_i, and R is the ridge least-squares fit
     (X^T X + lam I) R = X^T target with lam = ridge * trace(X^T X) / d_in.
+Covariance-whitened construction (the reading the library's default expert build follows):
+  * PaperDaily "核心设计" states the objective: the original error, minus the shared expert's
+    and the routed expert's compensation, multiplied by the input token, should leave the
+    smallest residual; and the whitening computes a covariance and whitens with it so that
+    the SVD captures the error's main components instead of directions that are merely
+    large.  The plain reading: the SE is the rank-r_s minimizer of
+    sum_t |(E - A_hat) x_t|^2 over the calibration tokens, and the covariance is that of the
+    error outputs E x_t: C = sum_t (E x_t)(E x_t)^T = Z Z^T with Z = E X^T.  By Eckart-Young
+    on Z, A_hat = U_r U_r^T E with U_r the top-r eigenvectors of C (A_hat X^T = U_r U_r^T Z is
+    then the best rank-r approximation of Z).  This is the same subspace as the SVD of E L
+    with L L^T = X^T X (whitening by the activation second moment); the pins check both.
+    Factors: A = E^T U_r [d_in, r], B = U_r^T [r, d_out], so x A B = x A_hat^T.
+  * The RE of cluster g minimizes the same objective for the residual E_1 = E - A_hat_s on
+    the cluster's input channels only: E_1[:, C_g] with the tokens' values on C_g.
+  * Eigen-directions below 1e-12 of the largest eigenvalue are dropped (zero columns), so
+    a cluster no wider than the rank reproduces E_1[:, C_g] exactly.
 parity pinned: every function below has CPU pins in tests/test_oracle_experts.py.
 """
 
@@ -150,3 +166,77 @@ def router_fit(X: np.ndarray, target: np.ndarray, ridge: float) -> np.ndarray:
     G = X.T @ X
     lam = ridge * np.trace(G) / X.shape[1]
     return np.linalg.solve(G + lam * np.eye(X.shape[1]), X.T @ np.asarray(target, dtype=np.float64))
+
+
+# ------------------------------------------------------------------ covariance whitening
+def error_cov_lowrank(E: np.ndarray, X: np.ndarray, r: int, tol: float = 1e-12
+                      ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Rank-r minimizer of sum_t |(E - A_hat) x_t|^2 (PaperDaily "核心设计").
+
+    E [d_out, n] (the error on n input channels), X [T, n] (calibration tokens on those
+    channels).  U_r = top-r eigenvectors of the error-output covariance C = Z Z^T, Z = E X^T;
+    A_hat = U_r U_r^T E.  Returns A = E^T U_r [n, r], B = U_r^T [r, d_out] and the singular
+    values of Z (sqrt of the top-r eigenvalues, 0 for dropped directions), descending.
+    When n < d_out the eigenproblem is reduced exactly through a thin QR of E (range(Z) lies
+    in range(E)): E = Q R, C = Q (R X^T X R^T) Q^T.
+    """
+    E = np.asarray(E, dtype=np.float64)
+    X = np.asarray(X, dtype=np.float64)
+    d_out, n = E.shape
+    if n < d_out:
+        Qe, Re = np.linalg.qr(E)
+        Zs = Re @ X.T
+        lam, W = np.linalg.eigh(Zs @ Zs.T)
+        U = Qe @ W
+    else:
+        Z = E @ X.T
+        lam, U = np.linalg.eigh(Z @ Z.T)
+    order = np.argsort(lam)[::-1][:r]
+    lam, U = lam[order], U[:, order]
+    top = max(float(lam[0]) if len(lam) else 0.0, 0.0)
+    keep = lam > tol * top if top > 0 else np.zeros(len(lam), bool)
+    U = np.where(keep[None, :], U, 0.0)
+    sig = np.where(keep, np.sqrt(np.maximum(lam, 0.0)), 0.0)
+    if U.shape[1] < r:  # fewer directions than the rank
+        U = np.concatenate([U, np.zeros((d_out, r - U.shape[1]))], axis=1)
+        sig = np.concatenate([sig, np.zeros(r - len(sig))])
+    return E.T @ U, U.T.copy(), sig
+
+
+def output_residual(E: np.ndarray, X: np.ndarray, A: np.ndarray, B: np.ndarray) -> float:
+    """sqrt(sum_t |(E - (A B)^T) x_t|^2) = |X E^T - X A B|_F."""
+    X = np.asarray(X, dtype=np.float64)
+    return float(np.linalg.norm(X @ np.asarray(E, np.float64).T - (X @ np.asarray(A, np.float64)) @ B))
+
+
+def build_experts_cov(W_f: np.ndarray, s: Optional[np.ndarray], w_bits: int, X: np.ndarray,
+                      dep_channels: Sequence[int], labels: Sequence[int], n_r: int, r_s: int, r_r: int
+                      ) -> Dict[str, np.ndarray]:
+    """SE and REs by covariance whitening ([DeepRead] "Method": the SE first, the residual to
+    the REs, one per cluster; [PaperDaily] "核心设计": the residual-times-token objective).
+
+    X [T, d_in]: calibration tokens (the layer input the adapters read, bf16 values).
+    Returns A_s, B_s, sigma_s, A_r [n_r, d_in, r_r] (zero outside the cluster's channels),
+    B_r, sigma_r and E1 = E - (A_s B_s)^T.
+    """
+    E = quant_error(W_f, s, w_bits)
+    X = np.asarray(X, dtype=np.float64)
+    d_out, d_in = E.shape
+    if r_s > 0:
+        A_s, B_s, sig_s = error_cov_lowrank(E, X, r_s)
+        E1 = E - (A_s @ B_s).T
+    else:
+        A_s, B_s, sig_s = np.zeros((d_in, 0)), np.zeros((0, d_out)), np.zeros(0)
+        E1 = E
+    A_r = np.zeros((n_r, d_in, r_r))
+    B_r = np.zeros((n_r, r_r, d_out))
+    sig_r = np.zeros((n_r, r_r))
+    dep = np.asarray(dep_channels, dtype=np.int64)
+    lab = np.asarray(labels, dtype=np.int64)
+    for g in range(n_r):
+        ch = np.sort(dep[lab == g])
+        if len(ch) == 0:
+            continue
+        Ag, B_r[g], sig_r[g] = error_cov_lowrank(E1[:, ch], X[:, ch], r_r)
+        A_r[g][ch] = Ag
+    return dict(A_s=A_s, B_s=B_s, sigma_s=sig_s, A_r=A_r, B_r=B_r, sigma_r=sig_r, E1=E1)

@@ -83,6 +83,11 @@ def _load():
         "qe_lowrank_fit": (ctypes.c_int, [P, I, I, P, P, I, I, I, P, P, P, P, Z, P]),
         "qe_build_experts_workspace_bytes": (Z, [I, I, I, I]),
         "qe_build_experts": (ctypes.c_int, [P, P, I, I, I, P, P, P, I, I, I, I, P, I, I, P, P, P, P, P, P, P, Z, P]),
+        "qe_lowrank_cov_workspace_bytes": (Z, [I, I, I, I]),
+        "qe_lowrank_fit_cov": (ctypes.c_int, [P, I, I, P, I, P, P, I, I, I, P, P, P, P, Z, P]),
+        "qe_build_experts_cov_workspace_bytes": (Z, [I, I, I, I, I]),
+        "qe_build_experts_cov": (ctypes.c_int, [P, P, I, I, I, P, I, I, P, P, I, I, I, I, P, I, I, P, P, P, P, P, P,
+                                                P, Z, P]),
         "qe_router_targets_workspace_bytes": (Z, [I, I, I, I]),
         "qe_router_targets": (ctypes.c_int, [P, I, I, P, I, I, P, P, I, I, P, P, Z, P]),
         "qe_router_fit_workspace_bytes": (Z, [I, I, I]),
@@ -106,7 +111,8 @@ EXPORTED = (
     "qe_probe_mfma_i8", "qe_probe_mfma_bf16", "qe_probe_copy", "qe_partition_channels", "qe_cooccur_workspace_bytes",
     "qe_cooccur", "qe_cluster_channels", "qe_top2_workspace_bytes", "qe_linear_forward_top2", "qe_quant_error", "qe_channel_rms_workspace_bytes", "qe_channel_rms",
     "qe_sub_lowrank", "qe_lowrank_workspace_bytes", "qe_lowrank_fit", "qe_build_experts_workspace_bytes",
-    "qe_build_experts", "qe_router_targets_workspace_bytes", "qe_router_targets", "qe_router_fit_workspace_bytes",
+    "qe_build_experts", "qe_lowrank_cov_workspace_bytes", "qe_lowrank_fit_cov",
+    "qe_build_experts_cov_workspace_bytes", "qe_build_experts_cov", "qe_router_targets_workspace_bytes", "qe_router_targets", "qe_router_fit_workspace_bytes",
     "qe_router_fit",
 )
 
@@ -353,6 +359,50 @@ def qe_build_experts(W_f, s, w_bits, c, dep_channels, labels, n_routed, r_shared
                                  _ptr(out["B_s"]), _ptr(out["A_r"]), _ptr(out["B_r"]), _ptr(out["sigma_s"]),
                                  _ptr(out["sigma_r"]), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "qe_build_experts")
+    return out
+
+
+def qe_lowrank_cov_workspace_bytes(d_out: int, d_in: int, T: int, k: int) -> int:
+    return _lib.qe_lowrank_cov_workspace_bytes(d_out, d_in, T, k)
+
+
+def qe_lowrank_fit_cov(E, X, mask, omega, rank, power_iters, ws, stream=None):
+    """Covariance-whitened fit of E diag(mask) on tokens X (device float32 [T, d_in]; omega [T, k]);
+    returns host numpy (A [d_in, rank] float32, B [rank, d_out] float32, sigma [rank] float64)."""
+    d_out, d_in = E.shape
+    T, k = omega.shape
+    A = np.empty((d_in, rank), np.float32)
+    B = np.empty((rank, d_out), np.float32)
+    sig = np.empty(rank, np.float64)
+    _check(_lib.qe_lowrank_fit_cov(_ptr(E), d_out, d_in, _ptr(X), T, _ptr(mask), _ptr(omega), k, rank, power_iters,
+                                   _ptr(A), _ptr(B), _ptr(sig), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)), "qe_lowrank_fit_cov")
+    return A, B, sig
+
+
+def qe_build_experts_cov_workspace_bytes(d_out: int, d_in: int, T: int, k: int, r_max: int) -> int:
+    return _lib.qe_build_experts_cov_workspace_bytes(d_out, d_in, T, k, r_max)
+
+
+def qe_build_experts_cov(W_f, s, w_bits, x, dep_channels, labels, n_routed, r_shared, r_routed, omegas, power_iters,
+                         ws, stream=None):
+    """SE and REs by covariance whitening over the calibration tokens x (device W_f, s, x [T, d_in],
+    omegas [1 + n_routed, T, k]; host dep_channels and labels); returns a dict of host numpy arrays
+    A_s, B_s, A_r, B_r (float32), sigma_s, sigma_r."""
+    d_out, d_in = W_f.shape
+    T = x.shape[0]
+    k = omegas.shape[2]
+    dep = np.ascontiguousarray(dep_channels, dtype=np.int32)
+    lab = np.ascontiguousarray(labels, dtype=np.int32)
+    rr = r_routed if n_routed else 0
+    out = dict(A_s=np.empty((d_in, r_shared), np.float32), B_s=np.empty((r_shared, d_out), np.float32),
+               A_r=np.empty((n_routed, d_in, rr), np.float32), B_r=np.empty((n_routed, rr, d_out), np.float32),
+               sigma_s=np.empty(r_shared, np.float64), sigma_r=np.empty((n_routed, rr), np.float64))
+    _check(_lib.qe_build_experts_cov(_ptr(W_f), _ptr(s), d_out, d_in, w_bits, _ptr(x), _dtype_code(x), T, _ptr(dep),
+                                     _ptr(lab), dep.shape[0], n_routed, r_shared, r_routed, _ptr(omegas), k,
+                                     power_iters, _ptr(out["A_s"]), _ptr(out["B_s"]), _ptr(out["A_r"]),
+                                     _ptr(out["B_r"]), _ptr(out["sigma_s"]), _ptr(out["sigma_r"]), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)), "qe_build_experts_cov")
     return out
 
 

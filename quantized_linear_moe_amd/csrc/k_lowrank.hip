@@ -650,6 +650,61 @@ bool host_eigen(const std::vector<double>& Gh, int k, std::vector<double>& lam, 
     return symmetric_eigen(A.data(), k, lam.data(), V.data()) == 0;
 }
 
+// The k x k side of a randomized fit: Gram matrices of device [m][k] matrices (double sums on
+// the GPU, eigen-decomposition on the host), products with host k x k matrices, and the
+// orthonormalization by the Gram matrix.  Device scratch: G (k x k double), S (k x k float)
+// and T ([m_max][k] float) for the first pass of a two-pass orthonormalization.
+struct SmallOps {
+    int k;
+    hipStream_t st;
+    double* Gd;
+    float* Sd;
+    float* Td;
+    std::vector<double> Gh, lam, V;
+    std::vector<float> Sh;
+    SmallOps(int k_, hipStream_t st_, double* G, float* S, float* T)
+        : k(k_), st(st_), Gd(G), Sd(S), Td(T), Gh((size_t)k_ * k_), Sh((size_t)k_ * k_) {}
+    // eigen-decomposition (ascending) of X^T X for a device [m][k] matrix X
+    hipError_t gram_eigen(const float* X, int m) {
+        hipError_t r;
+        if ((r = gram(X, m, k, Gd, st)) != hipSuccess) return r;
+        if ((r = hipMemcpyAsync(Gh.data(), Gd, (size_t)k * k * 8, hipMemcpyDeviceToHost, st)) != hipSuccess) return r;
+        if ((r = hipStreamSynchronize(st)) != hipSuccess) return r;
+        return host_eigen(Gh, k, lam, V) ? hipSuccess : hipErrorNotSupported;
+    }
+    // dst = src Sh ([m][k] times the host [k][cols] matrix Sh; dst may not alias src)
+    hipError_t apply(const float* src, int m, int cols, float* dst) {
+        hipError_t r;
+        if ((r = hipMemcpyAsync(Sd, Sh.data(), (size_t)k * cols * 4, hipMemcpyHostToDevice, st)) != hipSuccess) return r;
+        if ((r = thin(false, src, m, k, Sd, cols, nullptr, dst, st)) != hipSuccess) return r;
+        return hipStreamSynchronize(st);  // Sh is refilled by the next step
+    }
+    // orthonormal basis of the columns of src [m][k], written to dst (may alias src).  The
+    // second pass is needed only when the kept eigenvalues span more than 1e4 (a condition
+    // number above 100, where float32 rounding of the first product leaves columns measurably
+    // non-orthogonal); otherwise the first product goes straight to dst.
+    hipError_t orth(const float* src, int m, float* dst) {
+        hipError_t r;
+        const float* in = src;
+        for (int pass = 0; pass < 2; ++pass) {
+            if ((r = gram_eigen(in, m)) != hipSuccess) return r;
+            const double top = std::max(lam[k - 1], 0.0);
+            double low = top;
+            for (int i = 0; i < k; ++i)
+                if (lam[i] > 1e-11 * top) low = std::min(low, lam[i]);
+            for (int a = 0; a < k; ++a)
+                for (int i = 0; i < k; ++i)
+                    Sh[(size_t)a * k + i] = lam[i] > 1e-11 * top ? (float)(V[(size_t)a * k + i] / std::sqrt(lam[i])) : 0.0f;
+            const bool last = pass == 1 || low >= 1e-4 * top;
+            float* out = last ? dst : Td;
+            if ((r = apply(in, m, k, out)) != hipSuccess) return r;
+            if (last) break;
+            in = out;
+        }
+        return hipSuccess;
+    }
+};
+
 }  // namespace
 
 hipError_t launch_quant_error(const float* W_f, const float* s, int d_out, int d_in, int w_bits, float* E,
@@ -698,52 +753,18 @@ hipError_t lowrank_fit(const float* E, int d_out, int d_in, const float* w, cons
     double* Gd = reinterpret_cast<double*>(p);
     p += align256((size_t)k * k * 8);
     float* Sd = reinterpret_cast<float*>(p);
-    std::vector<double> Gh((size_t)k * k), lam, V;
-    std::vector<float> Sh((size_t)k * k);
+    SmallOps so(k, st, Gd, Sd, Td);
+    std::vector<double>& lam = so.lam;
+    std::vector<double>& V = so.V;
+    std::vector<float>& Sh = so.Sh;
     hipError_t e;
 #define QE_TRY(expr)                              \
     do {                                          \
         if ((e = (expr)) != hipSuccess) return e; \
     } while (0)
-    // Gram matrix of a device [m][kk] matrix -> host eigen-decomposition
-    auto gram_eigen = [&](const float* X, int m) -> hipError_t {
-        hipError_t r;
-        if ((r = gram(X, m, k, Gd, st)) != hipSuccess) return r;
-        if ((r = hipMemcpyAsync(Gh.data(), Gd, (size_t)k * k * 8, hipMemcpyDeviceToHost, st)) != hipSuccess) return r;
-        if ((r = hipStreamSynchronize(st)) != hipSuccess) return r;
-        return host_eigen(Gh, k, lam, V) ? hipSuccess : hipErrorNotSupported;
-    };
-    // dst = src S with the k x k matrix S on the device (dst may not alias src)
-    auto apply = [&](const float* src, int m, int cols, float* dst) -> hipError_t {
-        hipError_t r;
-        if ((r = hipMemcpyAsync(Sd, Sh.data(), (size_t)k * cols * 4, hipMemcpyHostToDevice, st)) != hipSuccess) return r;
-        if ((r = thin(false, src, m, k, Sd, cols, nullptr, dst, st)) != hipSuccess) return r;
-        return hipStreamSynchronize(st);  // Sh is refilled by the next step
-    };
-    // orthonormal basis of the columns of src [m][k], written to dst (may alias src).  The
-    // second pass is needed only when the kept eigenvalues span more than 1e4 (a condition
-    // number above 100, where float32 rounding of the first product leaves columns measurably
-    // non-orthogonal); otherwise the first product goes straight to dst.
-    auto orth = [&](const float* src, int m, float* dst) -> hipError_t {
-        hipError_t r;
-        const float* in = src;
-        for (int pass = 0; pass < 2; ++pass) {
-            if ((r = gram_eigen(in, m)) != hipSuccess) return r;
-            const double top = std::max(lam[k - 1], 0.0);
-            double low = top;
-            for (int i = 0; i < k; ++i)
-                if (lam[i] > 1e-11 * top) low = std::min(low, lam[i]);
-            for (int a = 0; a < k; ++a)
-                for (int i = 0; i < k; ++i)
-                    Sh[(size_t)a * k + i] = lam[i] > 1e-11 * top ? (float)(V[(size_t)a * k + i] / std::sqrt(lam[i])) : 0.0f;
-            const bool last = pass == 1 || low >= 1e-4 * top;
-            float* out = last ? dst : Td;
-            if ((r = apply(in, m, k, out)) != hipSuccess) return r;
-            if (last) break;
-            in = out;
-        }
-        return hipSuccess;
-    };
+    auto gram_eigen = [&](const float* X, int m) { return so.gram_eigen(X, m); };
+    auto apply = [&](const float* src, int m, int cols, float* dst) { return so.apply(src, m, cols, dst); };
+    auto orth = [&](const float* src, int m, float* dst) { return so.orth(src, m, dst); };
     QE_TRY(pass_over_e(true, E, d_out, d_in, omega, k, w, Yd, st));  // Y = M omega
     QE_TRY(orth(Yd, d_in, Qd));
     for (int it = 0; it < power_iters; ++it) {
@@ -842,6 +863,145 @@ hipError_t build_experts(const float* W_f, const float* s, int d_out, int d_in, 
     return hipSuccess;
 }
 
+
+// ---------------------------------------------------------------- covariance whitening
+// The SE minimizes sum_t |(E - A_hat) x_t|^2 over the calibration tokens (PaperDaily post,
+// "核心设计": the residual of the error minus the compensations, times the input token), and
+// the whitening is by the covariance of the error outputs C = Z Z^T, Z = E diag(m) X^T
+// (d_out x T; m a 0/1 channel mask, all ones for the SE, the cluster's channels for an RE).
+// Eckart-Young on Z: A_hat = U_r U_r^T E diag(m) with U_r the top-r left singular vectors of
+// Z.  They come from the randomized subspace iteration (Halko, Martinsson and Tropp,
+// Algorithms 4.4 and 5.1) on the operator Z, applied through passes over E and over a float32
+// copy of X, never forming Z or C:
+//   Y = E diag(m) X^T omega, Q = orth(Y); power_iters times: H = orth(X diag(m) E^T Q),
+//   Q = orth(E diag(m) X^T H); then P = diag(m) E^T Q, H = X P = Z^T Q, H^T H = U~ S^2 U~^T,
+//   U_r = Q U~_r, A = P U~_r = diag(m) E^T U_r, B = U_r^T.
+// Directions whose eigenvalue is below 1e-11 of the largest are dropped (zero columns).
+
+// device workspace (float32 unless noted): P [d_in][k]; Y, Q [d_out][k]; H, H2 [T][k];
+// T [max(d_in, d_out, T)][k]; G [k][k] double; S [k][k]
+size_t lowrank_cov_workspace_bytes(int d_out, int d_in, int T, int k) {
+    return align256((size_t)d_in * k * 4) + 2 * align256((size_t)d_out * k * 4) + 2 * align256((size_t)T * k * 4) +
+           align256((size_t)std::max(std::max(d_in, d_out), T) * k * 4) + align256((size_t)k * k * 8) +
+           align256((size_t)k * k * 4);
+}
+
+hipError_t lowrank_fit_cov(const float* E, int d_out, int d_in, const float* X, int T, const float* mask,
+                           const float* omega, int k, int rank, int power_iters, float* A, float* B, double* sigma,
+                           void* ws, hipStream_t st) {
+    char* p = static_cast<char*>(ws);
+    auto take = [&p](size_t bytes) {
+        float* q = reinterpret_cast<float*>(p);
+        p += align256(bytes);
+        return q;
+    };
+    float* Pd = take((size_t)d_in * k * 4);
+    float* Yd = take((size_t)d_out * k * 4);
+    float* Qd = take((size_t)d_out * k * 4);
+    float* Hd = take((size_t)T * k * 4);
+    float* H2d = take((size_t)T * k * 4);
+    float* Td = take((size_t)std::max(std::max(d_in, d_out), T) * k * 4);
+    double* Gd = reinterpret_cast<double*>(take((size_t)k * k * 8));
+    float* Sd = take((size_t)k * k * 4);
+    SmallOps so(k, st, Gd, Sd, Td);
+    hipError_t e;
+#define QE_TRY(expr)                              \
+    do {                                          \
+        if ((e = (expr)) != hipSuccess) return e; \
+    } while (0)
+    QE_TRY(pass_over_e(true, X, T, d_in, omega, k, mask, Pd, st));  // P = diag(m) X^T omega
+    QE_TRY(pass_over_e(false, E, d_out, d_in, Pd, k, nullptr, Yd, st));  // Y = E P
+    QE_TRY(so.orth(Yd, d_out, Qd));
+    for (int it = 0; it < power_iters; ++it) {
+        QE_TRY(pass_over_e(true, E, d_out, d_in, Qd, k, mask, Pd, st));   // P = diag(m) E^T Q
+        QE_TRY(pass_over_e(false, X, T, d_in, Pd, k, nullptr, Hd, st));   // H = X P = Z^T Q
+        QE_TRY(so.orth(Hd, T, H2d));
+        QE_TRY(pass_over_e(true, X, T, d_in, H2d, k, mask, Pd, st));      // P = diag(m) X^T H
+        QE_TRY(pass_over_e(false, E, d_out, d_in, Pd, k, nullptr, Yd, st));  // Y = E P = Z H
+        QE_TRY(so.orth(Yd, d_out, Qd));
+    }
+    QE_TRY(pass_over_e(true, E, d_out, d_in, Qd, k, mask, Pd, st));  // P = diag(m) E^T Q
+    QE_TRY(pass_over_e(false, X, T, d_in, Pd, k, nullptr, Hd, st));  // H = Z^T Q
+    QE_TRY(so.gram_eigen(Hd, T));  // Q^T Z Z^T Q = U~ S^2 U~^T (ascending)
+    const double top = std::max(so.lam[k - 1], 0.0);
+    for (int a = 0; a < k; ++a)
+        for (int l = 0; l < rank; ++l) {
+            const int c = k - 1 - l;
+            so.Sh[(size_t)a * rank + l] = so.lam[c] > 1e-11 * top ? (float)so.V[(size_t)a * k + c] : 0.0f;
+        }
+    for (int l = 0; l < rank; ++l) {
+        const double lv = so.lam[k - 1 - l];
+        sigma[l] = lv > 1e-11 * top ? std::sqrt(lv) : 0.0;
+    }
+    QE_TRY(so.apply(Pd, d_in, rank, Td));  // A = P U~_r  [d_in][rank]
+    QE_TRY(so.apply(Qd, d_out, rank, Yd));  // U_r = Q U~_r [d_out][rank]
+    std::vector<float> ud((size_t)d_out * rank);
+    QE_TRY(hipMemcpyAsync(A, Td, (size_t)d_in * rank * 4, hipMemcpyDeviceToHost, st));
+    QE_TRY(hipMemcpyAsync(ud.data(), Yd, ud.size() * 4, hipMemcpyDeviceToHost, st));
+    QE_TRY(hipStreamSynchronize(st));
+#undef QE_TRY
+    for (int l = 0; l < rank; ++l)
+        for (int i = 0; i < d_out; ++i) B[(size_t)l * d_out + i] = ud[(size_t)i * rank + l];
+    return hipSuccess;
+}
+
+size_t build_experts_cov_workspace_bytes(int d_out, int d_in, int T, int k, int r_max) {
+    return align256((size_t)d_out * d_in * 4) + align256((size_t)T * d_in * 4) +
+           align256(lowrank_cov_workspace_bytes(d_out, d_in, T, k)) + align256((size_t)d_in * 4) +
+           align256((size_t)d_in * r_max * 4) + align256((size_t)r_max * d_out * 4);
+}
+
+// SE on the whole error, then each RE on the residual's cluster columns, both by covariance
+// whitening over the calibration tokens x.  Host outputs; synchronizes `st`.
+hipError_t build_experts_cov(const float* W_f, const float* s, int d_out, int d_in, int w_bits, const void* x,
+                             int x_dtype, int T, const int32_t* dep, const int32_t* labels, int n_dep, int n_r,
+                             int r_s, int r_r, const float* omegas, int k, int power_iters, float* A_s, float* B_s,
+                             float* A_r, float* B_r, double* sigma_s, double* sigma_r, void* ws, hipStream_t st) {
+    const int r_max = std::max(r_s, r_r);
+    char* p = static_cast<char*>(ws);
+    float* E = reinterpret_cast<float*>(p);
+    p += align256((size_t)d_out * d_in * 4);
+    float* Xf = reinterpret_cast<float*>(p);
+    p += align256((size_t)T * d_in * 4);
+    void* lws = p;
+    p += align256(lowrank_cov_workspace_bytes(d_out, d_in, T, k));
+    float* md = reinterpret_cast<float*>(p);
+    p += align256((size_t)d_in * 4);
+    float* Ad = reinterpret_cast<float*>(p);
+    p += align256((size_t)d_in * r_max * 4);
+    float* Bd = reinterpret_cast<float*>(p);
+    hipError_t e;
+#define QE_TRY(expr)                              \
+    do {                                          \
+        if ((e = (expr)) != hipSuccess) return e; \
+    } while (0)
+    const size_t nx = (size_t)T * d_in;
+    hipLaunchKernelGGL(to_f32_kernel, dim3((unsigned)std::min<size_t>((nx + 255) / 256, 4096)), dim3(256), 0, st, x,
+                       x_dtype, nx, Xf);
+    QE_TRY(hipGetLastError());
+    QE_TRY(launch_quant_error(W_f, s, d_out, d_in, w_bits, E, st));
+    if (r_s > 0) {
+        QE_TRY(lowrank_fit_cov(E, d_out, d_in, Xf, T, nullptr, omegas, k, r_s, power_iters, A_s, B_s, sigma_s, lws,
+                               st));
+        QE_TRY(hipMemcpyAsync(Ad, A_s, (size_t)d_in * r_s * 4, hipMemcpyHostToDevice, st));
+        QE_TRY(hipMemcpyAsync(Bd, B_s, (size_t)r_s * d_out * 4, hipMemcpyHostToDevice, st));
+        QE_TRY(launch_sub_lowrank(E, d_out, d_in, Ad, Bd, r_s, st));  // E_1 = E - (A_s B_s)^T
+    }
+    std::vector<float> mh(d_in);
+    for (int g = 0; g < n_r; ++g) {
+        std::fill(mh.begin(), mh.end(), 0.0f);
+        for (int t = 0; t < n_dep; ++t)
+            if (labels[t] == g) mh[dep[t]] = 1.0f;
+        QE_TRY(hipMemcpyAsync(md, mh.data(), (size_t)d_in * 4, hipMemcpyHostToDevice, st));
+        QE_TRY(hipStreamSynchronize(st));  // mh is refilled for the next cluster
+        QE_TRY(lowrank_fit_cov(E, d_out, d_in, Xf, T, md, omegas + (size_t)(1 + g) * T * k, k, r_r, power_iters,
+                               A_r + (size_t)g * d_in * r_r, B_r + (size_t)g * r_r * d_out, sigma_r + (size_t)g * r_r,
+                               lws, st));
+    }
+    QE_TRY(hipStreamSynchronize(st));
+#undef QE_TRY
+    return hipSuccess;
+}
 
 // ---------------------------------------------------------------- router targets and fit
 size_t router_targets_workspace_bytes(int d_out, int d_in, int n_r, int r_r) {

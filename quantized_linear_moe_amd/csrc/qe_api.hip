@@ -832,6 +832,57 @@ int qe_build_experts(const float* W_f, const float* s, int32_t d_out, int32_t d_
                                         B_r, sigma_s, sigma_r, ws, S(stream)));
 }
 
+size_t qe_lowrank_cov_workspace_bytes(int32_t d_out, int32_t d_in, int32_t T, int32_t k) {
+    return d_out > 0 && d_in > 0 && T > 0 && k > 0 ? lowrank_cov_workspace_bytes(d_out, d_in, T, k) : 0;
+}
+
+int qe_lowrank_fit_cov(const float* E, int32_t d_out, int32_t d_in, const float* X, int32_t T, const float* mask,
+                       const float* omega, int32_t k, int32_t rank, int32_t power_iters, float* A, float* B,
+                       double* sigma, void* ws, size_t ws_bytes, void* stream) {
+    QE_CHECK(E && X && omega && A && B && sigma && ws, QE_ERR_INVALID_ARG);
+    QE_CHECK(d_out > 0 && d_in > 0 && T > 0 && k >= 1 && k <= 128 && k <= d_out && k <= T, QE_ERR_INVALID_ARG);
+    QE_CHECK(rank >= 1 && rank <= k && power_iters >= 0 && power_iters <= 16, QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(E) && aligned16(X) && aligned16(omega) && aligned16(ws) && (!mask || aligned16(mask)),
+             QE_ERR_ALIGNMENT);
+    QE_CHECK(ws_bytes >= lowrank_cov_workspace_bytes(d_out, d_in, T, k), QE_ERR_WORKSPACE);
+    return lowrank_status(
+        lowrank_fit_cov(E, d_out, d_in, X, T, mask, omega, k, rank, power_iters, A, B, sigma, ws, S(stream)));
+}
+
+size_t qe_build_experts_cov_workspace_bytes(int32_t d_out, int32_t d_in, int32_t T, int32_t k, int32_t r_max) {
+    return d_out > 0 && d_in > 0 && T > 0 && k > 0 && r_max >= 0
+               ? build_experts_cov_workspace_bytes(d_out, d_in, T, k, r_max)
+               : 0;
+}
+
+int qe_build_experts_cov(const float* W_f, const float* s, int32_t d_out, int32_t d_in, int32_t w_bits,
+                         const void* x, int32_t x_dtype, int32_t T, const int32_t* dep_channels,
+                         const int32_t* labels, int32_t n_dep, int32_t n_routed, int32_t r_shared, int32_t r_routed,
+                         const float* omegas, int32_t k, int32_t power_iters, float* A_s, float* B_s, float* A_r,
+                         float* B_r, double* sigma_s, double* sigma_r, void* ws, size_t ws_bytes, void* stream) {
+    QE_CHECK(W_f && x && omegas && ws && (w_bits == 3 || w_bits == 4), QE_ERR_INVALID_ARG);
+    QE_CHECK(x_dtype == QE_F32 || x_dtype == QE_BF16, QE_ERR_INVALID_ARG);
+    QE_CHECK(d_out > 0 && d_in > 0 && T > 0 && k >= 1 && k <= 128 && k <= d_out && k <= T, QE_ERR_INVALID_ARG);
+    QE_CHECK(r_shared >= 0 && r_shared <= 64 && r_shared <= k && power_iters >= 0 && power_iters <= 16,
+             QE_ERR_INVALID_ARG);
+    QE_CHECK(n_routed >= 0 && n_routed <= 16, QE_ERR_INVALID_ARG);
+    if (r_shared > 0) QE_CHECK(A_s && B_s && sigma_s, QE_ERR_INVALID_ARG);
+    if (n_routed > 0) {
+        QE_CHECK(r_routed >= 1 && r_routed <= 64 && r_routed <= k, QE_ERR_INVALID_ARG);
+        QE_CHECK(A_r && B_r && sigma_r && n_dep >= 0 && (n_dep == 0 || (dep_channels && labels)), QE_ERR_INVALID_ARG);
+        for (int t = 0; t < n_dep; ++t)
+            QE_CHECK(dep_channels[t] >= 0 && dep_channels[t] < d_in && labels[t] >= 0 && labels[t] < n_routed,
+                     QE_ERR_INVALID_ARG);
+    }
+    QE_CHECK(aligned16(W_f) && aligned16(x) && aligned16(omegas) && aligned16(ws) && (!s || aligned16(s)),
+             QE_ERR_ALIGNMENT);
+    const int r_max = std::max(r_shared, n_routed > 0 ? r_routed : 0);
+    QE_CHECK(ws_bytes >= build_experts_cov_workspace_bytes(d_out, d_in, T, k, r_max), QE_ERR_WORKSPACE);
+    return lowrank_status(build_experts_cov(W_f, s, d_out, d_in, w_bits, x, x_dtype, T, dep_channels, labels, n_dep,
+                                            n_routed, r_shared, n_routed > 0 ? r_routed : 0, omegas, k, power_iters,
+                                            A_s, B_s, A_r, B_r, sigma_s, sigma_r, ws, S(stream)));
+}
+
 size_t qe_router_targets_workspace_bytes(int32_t d_out, int32_t d_in, int32_t n_routed, int32_t r_routed) {
     return d_out > 0 && d_in > 0 && n_routed > 0 && r_routed > 0
                ? router_targets_workspace_bytes(d_out, d_in, n_routed, r_routed)

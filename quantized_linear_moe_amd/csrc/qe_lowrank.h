@@ -34,6 +34,19 @@ hipError_t build_experts(const float* W_f, const float* s, int d_out, int d_in, 
                          const float* omegas, int k, int power_iters, float* A_s, float* B_s, float* A_r, float* B_r,
                          double* sigma_s, double* sigma_r, void* ws, hipStream_t st);
 
+// Covariance-whitened fit of E diag(mask) on the calibration tokens X (device float32 [T][d_in];
+// mask device float32 0/1 [d_in] or NULL; omega device [T][k]): A [d_in][rank], B [rank][d_out],
+// sigma [rank] host outputs (see lowrank_fit_cov in k_lowrank.hip).  Synchronizes `st`.
+size_t lowrank_cov_workspace_bytes(int d_out, int d_in, int T, int k);
+hipError_t lowrank_fit_cov(const float* E, int d_out, int d_in, const float* X, int T, const float* mask,
+                           const float* omega, int k, int rank, int power_iters, float* A, float* B, double* sigma,
+                           void* ws, hipStream_t st);
+size_t build_experts_cov_workspace_bytes(int d_out, int d_in, int T, int k, int r_max);
+hipError_t build_experts_cov(const float* W_f, const float* s, int d_out, int d_in, int w_bits, const void* x,
+                             int x_dtype, int T, const int32_t* dep, const int32_t* labels, int n_dep, int n_r,
+                             int r_s, int r_r, const float* omegas, int k, int power_iters, float* A_s, float* B_s,
+                             float* A_r, float* B_r, double* sigma_s, double* sigma_r, void* ws, hipStream_t st);
+
 // Router: per-token targets mean_i |x_t (E_1^T - A_g B_g)|_i and the ridge least-squares fit of
 // R to them (see router_targets / router_fit in k_lowrank.hip); arguments validated by the caller.
 size_t router_targets_workspace_bytes(int d_out, int d_in, int n_r, int r_r);

@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 from oracle import qe_expert_oracle as X
+from oracle import qe_expert_oracle as X_
 
 
 def _orth(rng, n, m):
@@ -219,3 +220,95 @@ def test_router_targets_rank_experts_by_their_residual():
     tg = X.router_targets(E1, Xm, A, B)
     assert np.all(tg[:, 0] < tg[:, 1])
     assert np.allclose(tg[:, 1], np.mean(np.abs(Xm @ E1.T), axis=1))
+
+
+# ------------------------------------------------------------- covariance whitening
+def _correlated(rng, T, n, rank_x=None):
+    """Calibration tokens with strongly correlated channels: a few shared latent factors
+    mixed into every channel, plus small independent noise and per-channel scales."""
+    k = rank_x or max(2, n // 4)
+    F = rng.standard_normal((T, k))
+    M = rng.standard_normal((k, n))
+    return (F @ M + 0.05 * rng.standard_normal((T, n))) * rng.uniform(0.2, 3.0, n)[None, :]
+
+
+@pytest.mark.parametrize("d_out,n", [(40, 24), (24, 40)])  # both branches (n < d_out: thin QR)
+def test_error_cov_lowrank_matches_svd_of_error_outputs(d_out, n):
+    # Definition through the SVD of Z = E X^T: A_hat = U_r U_r^T E with U_r its left vectors
+    rng = np.random.default_rng(21)
+    E = rng.standard_normal((d_out, n))
+    X = _correlated(rng, 60, n)
+    r = 6
+    A, B, sig = X_.error_cov_lowrank(E, X, r)
+    U, S, _ = np.linalg.svd(E @ X.T)
+    ref = U[:, :r] @ U[:, :r].T @ E
+    assert np.allclose((A @ B).T, ref, atol=1e-9 * np.abs(ref).max())
+    assert np.allclose(sig, S[:r], rtol=1e-9)
+
+
+def test_error_cov_lowrank_equals_cholesky_whitened_svd():
+    # The same minimizer derived the other way: whiten by L with L L^T = X^T X (the activation
+    # second moment), truncate the SVD of E L, un-whiten: A_hat = [E L]_r L^-1.
+    rng = np.random.default_rng(22)
+    E = rng.standard_normal((30, 20))
+    X = _correlated(rng, 200, 20, rank_x=20)
+    r = 5
+    A, B, _ = X_.error_cov_lowrank(E, X, r)
+    L = np.linalg.cholesky(X.T @ X)
+    U, S, Vt = np.linalg.svd(E @ L)
+    ref = (U[:, :r] * S[:r]) @ Vt[:r] @ np.linalg.inv(L)
+    assert np.allclose((A @ B).T, ref, atol=1e-8 * np.abs(ref).max())
+
+
+def test_error_cov_lowrank_is_optimal_and_beats_diagonal_whitening():
+    rng = np.random.default_rng(23)
+    E = rng.standard_normal((48, 32))
+    X = _correlated(rng, 300, 32, rank_x=6)
+    r = 4
+    A, B, sig = X_.error_cov_lowrank(E, X, r)
+    res = X_.output_residual(E, X, A, B)
+    # Eckart-Young: the residual is the energy of the dropped singular values of Z
+    S = np.linalg.svd(E @ X.T, compute_uv=False)
+    assert abs(res - np.sqrt(np.sum(S[r:] ** 2))) <= 1e-9 * res
+    # no random rank-r perturbation of the factors does better
+    for _ in range(50):
+        Ap = A + 1e-3 * np.abs(A).max() * rng.standard_normal(A.shape)
+        Bp = B + 1e-3 * np.abs(B).max() * rng.standard_normal(B.shape)
+        assert X_.output_residual(E, X, Ap, Bp) >= res * (1 - 1e-12)
+    # the diagonal (per-channel RMS) whitening ignores the correlations and must lose here
+    Ad, Bd, _ = X_.whitened_lowrank(E, X_.channel_rms(X), r)
+    assert X_.output_residual(E, X, Ad, Bd) > 1.05 * res
+
+
+def test_error_cov_lowrank_full_rank_and_degenerate_cases():
+    rng = np.random.default_rng(24)
+    E = rng.standard_normal((20, 6))
+    X = rng.standard_normal((50, 6))
+    A, B, sig = X_.error_cov_lowrank(E, X, 8)  # rank above the number of channels
+    assert np.allclose((A @ B).T, E, atol=1e-10)  # full recovery: the cluster case
+    assert np.all(sig[6:] == 0) and np.all(sig[:6] > 0)
+    A0, B0, s0 = X_.error_cov_lowrank(E, np.zeros((50, 6)), 3)  # no calibration energy
+    assert not A0.any() and not B0.any() and not s0.any()
+
+
+def test_build_experts_cov_structure():
+    rng = np.random.default_rng(25)
+    d_out, d_in, T = 24, 64, 200
+    W = (rng.standard_normal((d_out, d_in)) * 0.05).astype(np.float32)
+    s = rng.uniform(0.5, 2, d_in).astype(np.float32)
+    X = _correlated(rng, T, d_in, rank_x=10)
+    dep = np.array([3, 9, 10, 20, 33, 40, 41, 50, 51, 60])
+    lab = np.array([0, 0, 1, 1, 1, 2, 2, 2, 0, 1])
+    out = X_.build_experts_cov(W, s, 4, X, dep, lab, 3, 4, 8)
+    E = X_.quant_error(W, s, 4)
+    assert np.allclose(out["E1"], E - (out["A_s"] @ out["B_s"]).T)
+    for g in range(3):
+        ch = np.sort(dep[lab == g])
+        others = np.setdiff1d(np.arange(d_in), ch)
+        assert not out["A_r"][g][others].any()
+        # clusters no wider than the rank are reproduced exactly on their channels
+        rec = (out["A_r"][g][ch] @ out["B_r"][g]).T
+        assert np.allclose(rec, out["E1"][:, ch], atol=1e-9)
+    # the SE is the covariance-whitened fit of E itself
+    A, B, _ = X_.error_cov_lowrank(E, X, 4)
+    assert np.allclose(A @ B, out["A_s"] @ out["B_s"])
