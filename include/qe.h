@@ -228,6 +228,24 @@ int qe_linear_prologue(const qe_linear* lin, const void* x, int32_t x_dtype, int
 int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* y,
                       int32_t* expert_out, void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): qe_linear_forward without a workspace argument.  It
+ * computes exactly what qe_linear_forward computes (the same kernels), with its workspace in a
+ * file-scope device array of qe_noalloc_scratch_bytes() bytes (64 MiB) that each GPU holds from
+ * the library's first use on it until the process ends; its device address is looked up once
+ * per device on the first call made with that device current.  The call itself allocates
+ * nothing.  Calls with qe_workspace_bytes(lin, T) > qe_noalloc_scratch_bytes() return
+ * QE_ERR_WORKSPACE and launch nothing (the decode and few-token calls of the 72B-wide linears
+ * fit; whole 4096-token prefills of them do not).  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (different streams, or threads without ordering) race
+ * and give undefined results; calls ordered on one stream are safe.  The array keeps the last
+ * call's contents; every value the kernels read from it is written earlier in the same call.
+ * Other arguments, errors and output as for qe_linear_forward.
+ */
+size_t qe_noalloc_scratch_bytes(void);
+int qe_linear_forward_noalloc(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* y,
+                              int32_t* expert_out, void* stream);
+
 /* ------------------------------------------------- channel-importance statistic --
  * (a8 helper) w[j] = (sum_i |W[i][j]|) / d_out: the column mean of |W_f|, one value
  * per input channel (DeepRead summary, "Method", first paragraph: Mean_row(|W_f|)).

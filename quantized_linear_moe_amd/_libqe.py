@@ -66,6 +66,8 @@ def _load():
         "qe_routed_lora": (ctypes.c_int, [LP, P, I, I, P, P, P, P, P, Z, P]),
         "qe_linear_prologue": (ctypes.c_int, [LP, P, I, I, P, P, P, P, P, P, P, Z, P]),
         "qe_linear_forward": (ctypes.c_int, [LP, P, I, I, P, P, P, Z, P]),
+        "qe_noalloc_scratch_bytes": (Z, []),
+        "qe_linear_forward_noalloc": (ctypes.c_int, [LP, P, I, I, P, P, P]),
         "qe_colmean_abs": (ctypes.c_int, [P, I, I, I, P, P]),
         "qe_channel_topk": (ctypes.c_int, [P, I, P, I, I, I, P, P, P]),
         "qe_partition_channels": (ctypes.c_int, [P, I, I, I, P, P, P]),
@@ -107,7 +109,7 @@ _lib = _load()
 EXPORTED = (
     "qe_status_string", "qe_last_hip_error", "qe_version", "qe_pack_weights", "qe_prepared_bytes", "qe_prepare",
     "qe_workspace_bytes", "qe_quant_act", "qe_route", "qe_adapter_inputs", "qe_wq_gemm", "qe_routed_lora",
-    "qe_linear_prologue", "qe_linear_forward", "qe_colmean_abs", "qe_channel_topk", "qe_linear_cost",
+    "qe_linear_prologue", "qe_linear_forward", "qe_noalloc_scratch_bytes", "qe_linear_forward_noalloc", "qe_colmean_abs", "qe_channel_topk", "qe_linear_cost",
     "qe_probe_mfma_i8", "qe_probe_mfma_bf16", "qe_probe_copy", "qe_partition_channels", "qe_cooccur_workspace_bytes",
     "qe_cooccur", "qe_cluster_channels", "qe_top2_workspace_bytes", "qe_linear_forward_top2", "qe_quant_error", "qe_channel_rms_workspace_bytes", "qe_channel_rms",
     "qe_sub_lowrank", "qe_lowrank_workspace_bytes", "qe_lowrank_fit", "qe_build_experts_workspace_bytes",
@@ -234,6 +236,16 @@ def rank_pad(r: int) -> int:
 def qe_linear_forward(lin, x, y, expert_out, ws, stream=None):
     _check(_lib.qe_linear_forward(ctypes.byref(lin), _ptr(x), _dtype_code(x), x.shape[0], _ptr(y), _ptr(expert_out),
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "qe_linear_forward")
+
+
+def qe_noalloc_scratch_bytes() -> int:
+    return _lib.qe_noalloc_scratch_bytes()
+
+
+def qe_linear_forward_noalloc(lin, x, y, expert_out, stream=None):
+    """qe_linear_forward with the library's per-GPU scratch array as its workspace."""
+    _check(_lib.qe_linear_forward_noalloc(ctypes.byref(lin), _ptr(x), _dtype_code(x), x.shape[0], _ptr(y),
+                                          _ptr(expert_out), _stream(stream)), "qe_linear_forward_noalloc")
 
 
 def qe_colmean_abs(W, w, stream=None):

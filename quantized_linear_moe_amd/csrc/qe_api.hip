@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <thread>
 #include <vector>
 
@@ -113,6 +114,11 @@ int ensure_attributes() {
 
 namespace qe {
 constexpr int kSkinnyMaxT = 16;  // token counts served by the weight-streaming kernels
+// Size of the per-GPU scratch array of qe_linear_forward_noalloc: enough for the decode and
+// few-token calls of every linear up to the 72B MLP widths (its workspace at 16 tokens and
+// 29568 input channels is about 15 MB).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+int noalloc_scratch(void** out);
 
 // Prefill prologue in two reads of x (route pass, then expert-sorted quantization), for
 // bf16 activations; the workspace is sized for it whatever the activation type
@@ -204,6 +210,37 @@ WsLayout ws_layout(const qe_linear* lin, int T) {
     return W;
 }
 
+}  // namespace qe
+
+// ------------------------------------------------------------ allocation-free forward
+// The workspace of qe_linear_forward_noalloc: one file-scope device array per GPU, held until
+// the process ends.  Host code never passes the array's name to a kernel (on the host it only
+// names a stand-in): its device address is taken per device with hipGetSymbolAddress on the
+// first call on that device, with that device current, and only that address is used.
+static __device__ __align__(256) uint8_t scratch[qe::kNoAllocScratchBytes];
+
+namespace qe {
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of the current device's scratch array (looked up once per device).
+int noalloc_scratch(void** out) {
+    int dev = 0;
+    QE_TRY_HIP(hipGetDevice(&dev));
+    QE_CHECK(dev >= 0 && dev < kMaxDevices, QE_ERR_UNSUPPORTED);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        QE_TRY_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+        QE_CHECK(ptr != nullptr, QE_ERR_HIP);
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return QE_OK;
+}
 }  // namespace qe
 
 // ======================================================================= ABI
@@ -609,6 +646,21 @@ int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int3
     st = run_prologue(lin, x, x_dtype, T, codes, s_x, u, v, expert, perm, ws, s, keep_order);
     if (st) return st;
     return run_gemm(lin, codes, s_x, x, x_dtype, T, u, v, expert, perm, y, nullptr, ws, s);
+}
+
+size_t qe_noalloc_scratch_bytes(void) { return qe::kNoAllocScratchBytes; }
+
+int qe_linear_forward_noalloc(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* y,
+                              int32_t* expert_out, void* stream) {
+    int st = validate_linear(lin);
+    if (st) return st;
+    QE_CHECK(T >= 0, QE_ERR_INVALID_ARG);
+    if (T == 0) return QE_OK;
+    QE_CHECK(ws_layout(lin, T).total <= qe::kNoAllocScratchBytes, QE_ERR_WORKSPACE);
+    void* scratch_dev = nullptr;
+    st = qe::noalloc_scratch(&scratch_dev);
+    if (st) return st;
+    return qe_linear_forward(lin, x, x_dtype, T, y, expert_out, scratch_dev, qe::kNoAllocScratchBytes, stream);
 }
 
 // ------------------------------------------------------------------ a8
