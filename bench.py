@@ -656,9 +656,9 @@ def table8(torch, synth, qe, libqe, dev, reps=20):
             "note": "bf16_roofline_us = max(bf16 weight bytes / 8 TB/s, flops / 2.5 PFLOP/s)"}
 
 
-def decode_line(torch, synth, qe, libqe, dev, w_bits, a_bits, copy_gbs=None):
+def decode_line(torch, synth, qe, libqe, dev, w_bits, a_bits, copy_gbs=None, y_bf16=False):
     """Qwen2VL-72B MLP up + down at T = 8 through the composite entry point, cold (the Infinity
-    Cache flushed before every iteration) and warm."""
+    Cache flushed before every iteration) and warm; y float32, or bf16 with y_bf16."""
     import dataclasses
     cfg = dataclasses.replace(synth.get_config("qwen2vl_72b_decode"), w_bits=w_bits, a_bits=a_bits)
     layers = []
@@ -669,7 +669,10 @@ def decode_line(torch, synth, qe, libqe, dev, w_bits, a_bits, copy_gbs=None):
     xs = {s: synth.gen_activations(cfg, s).to(dev) for s in cfg.streams()}
     T = cfg.T
     wss = [l.workspace(T) for _, l in layers]
-    ys = [torch.empty(T, s.d_out, dtype=torch.float32, device=dev) for s, _ in layers]
+    for _, l in layers:
+        l.lin.y_dtype = libqe.QE_BF16 if y_bf16 else libqe.QE_F32
+    ydt = torch.bfloat16 if y_bf16 else torch.float32
+    ys = [torch.empty(T, s.d_out, dtype=ydt, device=dev) for s, _ in layers]
     es = [torch.empty(T, dtype=torch.int32, device=dev) for _ in layers]
     # Reading 1 GiB (four times the 256 MB Infinity Cache) evicts it with clean lines; a write
     # flush would leave dirty lines whose write-back lands inside the timed region.
@@ -701,6 +704,22 @@ def decode_line(torch, synth, qe, libqe, dev, w_bits, a_bits, copy_gbs=None):
     for i, (spec, layer) in enumerate(layers):
         nd = int(torch.unique(es[i]).numel())
         alg += libqe.qe_linear_cost(layer.lin, T, nd, 2)[2]
+    # the read-only streaming rate of the same byte count, cold: the measured counterpart of a
+    # path whose traffic is almost all weight reads
+    nb = int(alg) // 16 * 16
+    buf = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(libqe.qe_probe_read_sink_bytes() // 4, dtype=torch.int32, device=dev)
+    reads = []
+    for it in range(10):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        libqe.qe_probe_read(buf, nb, sink)
+        b.record()
+        torch.cuda.synchronize()
+        reads.append(a.elapsed_time(b))
+    read_gbs = nb / (float(np.median(reads)) * 1e-3) / 1e9
+    del buf, sink
     t_cold = float(np.median(cold)) * 1e-3
     res = {
         "us_cold_median": round(t_cold * 1e6, 2), "us_cold_p10": round(float(np.percentile(cold, 10)) * 1e3, 2),
@@ -708,8 +727,12 @@ def decode_line(torch, synth, qe, libqe, dev, w_bits, a_bits, copy_gbs=None):
         "us_warm_median": round(float(np.median(warm)) * 1e3, 2),
         "tokens_per_s": round(T / t_cold, 1), "alg_mbytes": round(alg / 1e6, 2),
         "achieved_gbs": round(alg / t_cold / 1e9, 1), "hbm_frac": round(alg / t_cold / 1e9 / PEAK_HBM_GBS, 4),
+        "read_probe_gbs_same_bytes_cold": round(read_gbs, 1),
+        "frac_of_measured_read": round(alg / t_cold / 1e9 / read_gbs, 4),
         "hbm_frac_of_measured_copy": round(alg / t_cold / 1e9 / copy_gbs, 4) if copy_gbs else None,
-        "note": "Infinity Cache flushed by reading 1 GiB before every cold iteration",
+        "note": "Infinity Cache flushed by reading 1 GiB before every cold iteration; hbm_frac is against the "
+                "8 TB/s spec, frac_of_measured_read against qe_probe_read streaming the same number of bytes "
+                "cold, hbm_frac_of_measured_copy against a 1 GiB read + write copy",
     }
     del layers, wss, flush
     torch.cuda.empty_cache()
@@ -821,6 +844,10 @@ def extras(torch, synth, qe, libqe, dev, peaks):
     # configuration's own), and W4A6 (quantized activations: few-token split-K main product)
     out["decode_qwen2vl72b_up_down_w3a16_T8"] = decode_line(torch, synth, qe, libqe, dev, 3, 16, copy_gbs)
     out["decode_qwen2vl72b_up_down_w4a6_T8"] = decode_line(torch, synth, qe, libqe, dev, 4, 6, copy_gbs)
+    out["decode_qwen2vl72b_up_down_w3a16_T8_bf16y"] = decode_line(torch, synth, qe, libqe, dev, 3, 16, copy_gbs,
+                                                                  y_bf16=True)
+    out["decode_qwen2vl72b_up_down_w4a6_T8_bf16y"] = decode_line(torch, synth, qe, libqe, dev, 4, 6, copy_gbs,
+                                                                 y_bf16=True)
 
     # ---- calibration statistic: InternVL2-8B down input, k = 32 (HBM / ALU bound)
     cfg = synth.get_config("internvl2_8b")

@@ -65,6 +65,11 @@ typedef enum { QE_F32 = 0, QE_BF16 = 1 } qe_dtype;
  *   r_shared     shared-expert rank, 0..64 (0 = no shared expert)
  *   n_routed     number of routed experts N_r, 0..16 (0 = no router, no routed expert)
  *   r_routed     routed-expert rank, 1..64 when n_routed > 0, else 0
+ *   y_dtype      element type of the outputs y this linear writes: QE_F32 (0), or QE_BF16 (1),
+ *                the round-to-nearest-even of the float32 value the QE_F32 setting writes
+ *                (the bf16-output option of the decode settings, listing Tables 1-3 and 8);
+ *                every `float* y` argument of the calls below then points at bf16 elements.
+ *                qe_routed_lora and qe_linear_forward_top2 add into y and take QE_F32 only.
  *   prep         device buffer written by qe_prepare() (qe_prepared_bytes() bytes)
  * Kernel-path constraints: d_out % 16 == 0 and d_in % 128 == 0, and d_in <= 32768 when
  * a_bits is 6 or 8 (else QE_ERR_UNSUPPORTED).
@@ -77,7 +82,7 @@ typedef struct qe_linear {
     int32_t r_shared;
     int32_t n_routed;
     int32_t r_routed;
-    int32_t reserved;
+    int32_t y_dtype;
     const void* prep;
 } qe_linear;
 
@@ -330,7 +335,7 @@ int qe_cluster_channels(const uint32_t* cooc, int32_t n_dep, int64_t T, int32_t 
  *   int_macs      = T * d_in * d_out                        (the quantized product)
  *   adapter_macs  = T * (d_in + d_out) * (r_shared + r_routed) + T * d_in * n_routed
  *   alg_bytes     = minimum HBM traffic: x read once, packed weights, scales, y written
- *                   once (float32), A_s, B_s, R and the A_e, B_e of n_distinct_experts
+ *                   once (4 or 2 bytes per element as y_dtype says), A_s, B_s, R and the A_e, B_e of n_distinct_experts
  *                   distinct routed experts actually selected.
  * Host-only; x_bytes_per_elt is 2 (bf16) or 4 (float32).
  */
@@ -500,12 +505,17 @@ int qe_router_fit(const void* x, int32_t x_dtype, int32_t T, int32_t d_in, const
  *   [blocks * 256 * 4], a result sink the caller owns.
  * qe_probe_copy: copies `bytes` (a multiple of 16) from src to dst; both device pointers,
  *   16-byte aligned, caller-owned, not overlapping.  The traffic is 2 * bytes.
+ * qe_probe_read: reads `bytes` (a multiple of 16) from src once (device, 16-byte aligned) and
+ *   writes one folded word per thread to sink (device, qe_probe_read_sink_bytes() bytes): the
+ *   read-only streaming rate, for weight-streaming kernels whose traffic is almost all reads.
  * Both only enqueue work (no synchronization); invalid arguments return
  * QE_ERR_INVALID_ARG / QE_ERR_ALIGNMENT and launch nothing.
  */
 int qe_probe_mfma_i8(int32_t* out, int32_t blocks, int32_t iters, int32_t operands, double* ops, void* stream);
 int qe_probe_mfma_bf16(float* out, int32_t blocks, int32_t iters, int32_t operands, double* flops, void* stream);
 int qe_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+size_t qe_probe_read_sink_bytes(void);
+int qe_probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

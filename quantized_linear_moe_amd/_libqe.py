@@ -38,7 +38,7 @@ class qe_linear(ctypes.Structure):
         ("r_shared", ctypes.c_int32),
         ("n_routed", ctypes.c_int32),
         ("r_routed", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("y_dtype", ctypes.c_int32),
         ("prep", ctypes.c_void_p),
     ]
 
@@ -97,6 +97,8 @@ def _load():
         "qe_probe_mfma_i8": (ctypes.c_int, [P, I, I, I, D, P]),
         "qe_probe_mfma_bf16": (ctypes.c_int, [P, I, I, I, D, P]),
         "qe_probe_copy": (ctypes.c_int, [P, P, Z, P]),
+        "qe_probe_read_sink_bytes": (Z, []),
+        "qe_probe_read": (ctypes.c_int, [P, Z, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -110,7 +112,7 @@ EXPORTED = (
     "qe_status_string", "qe_last_hip_error", "qe_version", "qe_pack_weights", "qe_prepared_bytes", "qe_prepare",
     "qe_workspace_bytes", "qe_quant_act", "qe_route", "qe_adapter_inputs", "qe_wq_gemm", "qe_routed_lora",
     "qe_linear_prologue", "qe_linear_forward", "qe_noalloc_scratch_bytes", "qe_linear_forward_noalloc", "qe_colmean_abs", "qe_channel_topk", "qe_linear_cost",
-    "qe_probe_mfma_i8", "qe_probe_mfma_bf16", "qe_probe_copy", "qe_partition_channels", "qe_cooccur_workspace_bytes",
+    "qe_probe_mfma_i8", "qe_probe_mfma_bf16", "qe_probe_copy", "qe_probe_read_sink_bytes", "qe_probe_read", "qe_partition_channels", "qe_cooccur_workspace_bytes",
     "qe_cooccur", "qe_cluster_channels", "qe_top2_workspace_bytes", "qe_linear_forward_top2", "qe_quant_error", "qe_channel_rms_workspace_bytes", "qe_channel_rms",
     "qe_sub_lowrank", "qe_lowrank_workspace_bytes", "qe_lowrank_fit", "qe_build_experts_workspace_bytes",
     "qe_build_experts", "qe_lowrank_cov_workspace_bytes", "qe_lowrank_fit_cov",
@@ -466,6 +468,14 @@ def qe_probe_mfma_bf16(out, blocks, iters, operands=0, stream=None):
 def qe_probe_copy(src, dst, nbytes, stream=None):
     """Enqueue the streaming copy probe of nbytes from src to dst (traffic: 2 * nbytes)."""
     _check(_lib.qe_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)), "qe_probe_copy")
+
+
+def qe_probe_read_sink_bytes() -> int:
+    return _lib.qe_probe_read_sink_bytes()
+
+
+def qe_probe_read(src, nbytes, sink, stream=None):
+    _check(_lib.qe_probe_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)), "qe_probe_read")
 
 
 def qe_linear_cost(lin, T, n_distinct, x_bytes):

@@ -338,7 +338,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
     const float* __restrict__ w_scale,
     const float* __restrict__ part_p, int ks_p, int ncp, int col_se, int r_s, int rs_pad, int col_re, int n_r,
     int r_r, int rr_pad, int col_router, const uint16_t* __restrict__ bt_s, const uint16_t* __restrict__ bt_r,
-    int32_t* __restrict__ expert_out, float* __restrict__ y) {
+    int32_t* __restrict__ expert_out, float* __restrict__ y, bool y_bf16) {
     __shared__ float s_sc[16][kMaxRouted];
     __shared__ int s_e[16];
     __shared__ float s_u[16][kMaxRank];
@@ -432,7 +432,7 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
                 }
             }
         }
-        if (blockIdx.x * DF_CH + c < d_out) y[(size_t)tt * d_out + i] = (out[h] + du) + dv;
+        if (blockIdx.x * DF_CH + c < d_out) store_y(y, (size_t)tt * d_out + i, (out[h] + du) + dv, y_bf16);
     }
 }
 
@@ -440,12 +440,12 @@ hipError_t launch_decode_finish(const float* part_m, const float* s_x, int ks_m,
                                 const float* w_scale, const float* part_p, int ks_p, int ncp, int col_se, int r_s,
                                 int rs_pad, int col_re, int n_r, int r_r, int rr_pad, int col_router,
                                 const uint16_t* bt_s, const uint16_t* bt_r, int32_t* expert_out, float* y,
-                                hipStream_t st) {
+                                bool y_bf16, hipStream_t st) {
     if (T <= 0) return hipSuccess;
     if (T > 16 || n_r > kMaxRouted || rs_pad > kMaxRank || rr_pad > kMaxRank) return hipErrorInvalidValue;
     hipLaunchKernelGGL(decode_finish_kernel, dim3((d_out + DF_CH - 1) / DF_CH), dim3(DF_THREADS), 0, st, part_m, s_x,
                        ks_m, T, d_out, w_scale, part_p, ks_p, ncp, col_se, r_s, rs_pad, col_re, n_r, r_r, rr_pad, col_router,
-                       bt_s, bt_r, expert_out, y);
+                       bt_s, bt_r, expert_out, y, y_bf16);
     return hipGetLastError();
 }
 
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(const float* __restr
                                                             const uint16_t* __restrict__ v,
                                                             const int32_t* __restrict__ expert,
                                                             const uint16_t* __restrict__ bt_r, int rr_pad,
-                                                            float* __restrict__ y) {
+                                                            float* __restrict__ y, bool y_bf16) {
     const int i = blockIdx.x * 256 + threadIdx.x, t = blockIdx.y;
     if (i >= d_out) return;
     const float* p = part + (size_t)t * d_out + i;
@@ -505,15 +505,16 @@ __global__ __launch_bounds__(256) void skinny_finish_kernel(const float* __restr
     float out = s * w_scale[i];
     if (u) out += dot_bf16_rows(u + (size_t)t * rs_pad, bt_s + (size_t)i * rs_pad, rs_pad);
     if (v && expert) out += dot_bf16_rows(v + (size_t)t * rr_pad, bt_r + ((size_t)expert[t] * d_out + i) * rr_pad, rr_pad);
-    y[(size_t)t * d_out + i] = out;
+    store_y(y, (size_t)t * d_out + i, out, y_bf16);
 }
 
 hipError_t launch_skinny_finish(const float* part, int ksplit, int T, int d_out, const float* w_scale,
                                 const uint16_t* u, const uint16_t* bt_s, int rs_pad, const uint16_t* v,
-                                const int32_t* expert, const uint16_t* bt_r, int rr_pad, float* y, hipStream_t st) {
+                                const int32_t* expert, const uint16_t* bt_r, int rr_pad, float* y, bool y_bf16,
+                                hipStream_t st) {
     if (T <= 0) return hipSuccess;
     hipLaunchKernelGGL(skinny_finish_kernel, dim3((d_out + 255) / 256, T), dim3(256), 0, st, part, ksplit, T, d_out,
-                       w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, y);
+                       w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, y, y_bf16);
     return hipGetLastError();
 }
 

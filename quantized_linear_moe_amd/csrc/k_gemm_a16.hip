@@ -65,7 +65,7 @@ __device__ __attribute__((always_inline)) inline void a16_epilogue(
     v4f (&acc)[MB][NBW], int m0, int nb0, int T, int d_out, int lane, const float* __restrict__ w_scale,
     const uint16_t* __restrict__ u, const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ expert, const uint16_t* __restrict__ bt_r, int rr_pad, int n_r,
-    float* __restrict__ y) {
+    float* __restrict__ y, bool y_bf16) {
     const int NB = d_out >> 4, lr = lane & 15, lg = lane >> 4;
     const bool shared = u != nullptr && bt_s != nullptr && rs_pad > 0;
     const bool routed = v != nullptr && expert != nullptr && bt_r != nullptr && rr_pad > 0 && n_r > 0;
@@ -121,7 +121,7 @@ __device__ __attribute__((always_inline)) inline void a16_epilogue(
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int t = m0 + m * 16 + lg * 4 + r;
-                if (t < T) y[(size_t)t * d_out + (nb0 + j) * 16 + lr] = acc[m][j][r] * sw[j] + ad[j][r];
+                if (t < T) store_y(y, (size_t)t * d_out + (nb0 + j) * 16 + lr, acc[m][j][r] * sw[j] + ad[j][r], y_bf16);
             }
         }
     }
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256, 2) void gemm_a16_kernel(
     const void* __restrict__ x, int x_dtype, int T, int d_in, int d_out, const uint32_t* __restrict__ w_tiled, int n_tm,
     float* __restrict__ part, const float* __restrict__ w_scale, const uint16_t* __restrict__ u,
     const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v, const int32_t* __restrict__ expert,
-    const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, float* __restrict__ y) {
+    const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, float* __restrict__ y, bool y_bf16) {
     constexpr int BM = 16 * MB;
     constexpr int FW = Frag<WB>::kWords;
     constexpr int XCH = BM * 16 / 256;  // 16-byte chunks of the x tile per thread and K block
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256, 2) void gemm_a16_kernel(
     }
 
     if (y != nullptr) {  // K not split: the whole epilogue here
-        a16_epilogue<MB, 2>(acc, m0, nb0, T, d_out, lane, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y);
+        a16_epilogue<MB, 2>(acc, m0, nb0, T, d_out, lane, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y, y_bf16);
         return;
     }
     // lane holds rows 16m + 4lg + r, column lr of each block
@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void gemm_a16_ring_kernel(
     const void* __restrict__ x, int T, int d_in, int d_out, const uint32_t* __restrict__ w_tiled, int n_tm,
     float* __restrict__ part, const float* __restrict__ w_scale, const uint16_t* __restrict__ u,
     const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v, const int32_t* __restrict__ expert,
-    const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, float* __restrict__ y) {
+    const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, float* __restrict__ y, bool y_bf16) {
     constexpr int MB = 8, BM = 128, NBW = 4;
     constexpr int X_BYTES = BM * 128;                     // x tile of one 64-K half block
     constexpr int W_WAVE = NBW * 2 * 256;                 // one wave's two fragment dwords per block
@@ -368,7 +368,7 @@ __global__ __launch_bounds__(256, 2) void gemm_a16_ring_kernel(
     // lane holds rows 16m + 4lg + r, column 16 nb + lr of each block; the A operands of the
     // adapter MFMAs are rows 16m + lr
     if (y != nullptr) {  // K not split: the whole epilogue here
-        a16_epilogue<MB, NBW>(acc, m0, nb0, T, d_out, lane, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y);
+        a16_epilogue<MB, NBW>(acc, m0, nb0, T, d_out, lane, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y, y_bf16);
         return;
     }
 
@@ -396,7 +396,7 @@ __global__ __launch_bounds__(256) void gemm_a16_finish_kernel(
     const float* __restrict__ part, int ksplit, int T, int d_out, int n_tm, const float* __restrict__ w_scale,
     const uint16_t* __restrict__ u, const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v,
     const int32_t* __restrict__ expert, const uint16_t* __restrict__ bt_r, int rr_pad, int n_r,
-    float* __restrict__ y) {
+    float* __restrict__ y, bool y_bf16) {
     constexpr int MB = 1, NBW = 1;
     const int tm = blockIdx.x % n_tm, tn = blockIdx.x / n_tm;
     const int m0 = tm * 16;
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(256) void gemm_a16_finish_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[m][j][r] += pk[off[m][j][r]];
     }
-    a16_epilogue<MB, NBW>(acc, m0, nb0, T, d_out, lane, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y);
+    a16_epilogue<MB, NBW>(acc, m0, nb0, T, d_out, lane, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y, y_bf16);
 }
 
 // Finish of a K-split int8 main product (A6 / A8 with few tokens): the int32 partials of a 16 x 64
@@ -438,7 +438,7 @@ __global__ __launch_bounds__(256) void gemm_i8_finish_kernel(
     const int32_t* __restrict__ part, int ksplit, int T, int d_out, int n_tm, const float* __restrict__ s_x,
     const float* __restrict__ w_scale, const uint16_t* __restrict__ u, const uint16_t* __restrict__ bt_s, int rs_pad,
     const uint16_t* __restrict__ v, const int32_t* __restrict__ expert, const uint16_t* __restrict__ bt_r,
-    int rr_pad, int n_r, float* __restrict__ y) {
+    int rr_pad, int n_r, float* __restrict__ y, bool y_bf16) {
     const int tm = blockIdx.x % n_tm, tn = blockIdx.x / n_tm;
     const int m0 = tm * 16;
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
@@ -456,7 +456,7 @@ __global__ __launch_bounds__(256) void gemm_i8_finish_kernel(
     v4f acc[1][1];
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[0][0][r] = (float)si[r] * s_x[min(m0 + 4 * lg + r, T - 1)];
-    a16_epilogue<1, 1>(acc, m0, nb0, T, d_out, lane, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y);
+    a16_epilogue<1, 1>(acc, m0, nb0, T, d_out, lane, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y, y_bf16);
 }
 
 inline int a16_mb(int T) { return T >= 512 ? 8 : 4; }
@@ -482,7 +482,7 @@ int gemm_a16_ksplit(int T, int d_in, int d_out, int w_bits) {
 hipError_t launch_gemm_a16(const void* x, int x_dtype, int T, int d_in, int d_out, int w_bits, const void* w_tiled,
                            int ksplit, float* part, const float* w_scale, const uint16_t* u, const uint16_t* bt_s,
                            int rs_pad, const uint16_t* v, const int32_t* expert, const uint16_t* bt_r, int rr_pad,
-                           int n_r, float* y, hipStream_t st) {
+                           int n_r, float* y, bool y_bf16, hipStream_t st) {
     if (T <= 0) return hipSuccess;
     if ((w_bits != 3 && w_bits != 4) || d_in % 128 || d_out % 16 || ksplit < 1 || ksplit > d_in / 128)
         return hipErrorInvalidValue;
@@ -494,10 +494,10 @@ hipError_t launch_gemm_a16(const void* x, int x_dtype, int T, int d_in, int d_ou
 #define QE_A16_LAUNCH(WBV, MBV)                                                                                      \
     hipLaunchKernelGGL((gemm_a16_kernel<WBV, MBV>), dim3(n_tm * n_tn, ksplit), dim3(256), 0, st, x, x_dtype, T,    \
                        d_in, d_out, w, n_tm, part, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r,        \
-                       fused ? y : nullptr)
+                       fused ? y : nullptr, y_bf16)
 #define QE_RING_LAUNCH(WBV)                                                                                         \
     hipLaunchKernelGGL(gemm_a16_ring_kernel<WBV>, dim3(n_tm * n_tn, ksplit), dim3(256), 0, st, x, T, d_in, d_out, w, \
-                       n_tm, part, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, fused ? y : nullptr)
+                       n_tm, part, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, fused ? y : nullptr, y_bf16)
     if (ring) {  // many tokens: the DMA ring (bf16 rows copied as they are)
         if (w_bits == 3) QE_RING_LAUNCH(3);
         else QE_RING_LAUNCH(4);
@@ -514,19 +514,19 @@ hipError_t launch_gemm_a16(const void* x, int x_dtype, int T, int d_in, int d_ou
     if (e != hipSuccess || fused) return e;
     const int f_tm = (T + 15) / 16;
     hipLaunchKernelGGL(gemm_a16_finish_kernel, dim3(f_tm * ((d_out / 16 + 3) / 4)), dim3(256), 0, st, part,
-                       ksplit, T, d_out, f_tm, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y);
+                       ksplit, T, d_out, f_tm, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y, y_bf16);
     return hipGetLastError();
 }
 
 hipError_t launch_gemm_split_finish(const int32_t* part, int ksplit, int T, int d_out, const float* s_x,
                                     const float* w_scale, const uint16_t* u, const uint16_t* bt_s, int rs_pad,
                                     const uint16_t* v, const int32_t* expert, int n_r, const uint16_t* bt_r,
-                                    int rr_pad, float* y, hipStream_t st) {
+                                    int rr_pad, float* y, bool y_bf16, hipStream_t st) {
     if (T <= 0) return hipSuccess;
     if (d_out % 16) return hipErrorInvalidValue;
     const int n_tm = (T + 15) / 16;
     hipLaunchKernelGGL(gemm_i8_finish_kernel, dim3(n_tm * ((d_out / 16 + 3) / 4)), dim3(256), 0, st, part, ksplit, T,
-                       d_out, n_tm, s_x, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y);
+                       d_out, n_tm, s_x, w_scale, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, y, y_bf16);
     return hipGetLastError();
 }
 

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     const float* __restrict__ w_scale, int T, int d_in, int d_out, const uint16_t* __restrict__ u,
     const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v, const int32_t* __restrict__ expert,
     const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, const int32_t* __restrict__ perm, float* __restrict__ y,
-    int32_t* __restrict__ acc_debug, int n_tm, int32_t* __restrict__ part) {
+    int32_t* __restrict__ acc_debug, int n_tm, int32_t* __restrict__ part, bool y_bf16) {
     constexpr int BM = MB * 16;
     constexpr int A_STAGE = BM * G_BK;            // bytes of codes per stage
     constexpr int B_STAGE = 4 * G_NBW * 512;      // 4 waves x 4 N blocks x 512 B of packed weights
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
             const size_t rowoff = (size_t)token(pos) * d_out;
 #pragma unroll
             for (int j = 0; j < G_NBW; ++j)
-                if (nb_ok[j]) y[rowoff + (nb0 + j) * 16 + lr] = yv[m][j][r];
+                if (nb_ok[j]) store_y(y, rowoff + (nb0 + j) * 16 + lr, yv[m][j][r], y_bf16);
         }
     }
 }
@@ -467,7 +467,7 @@ int gemm_ksplit(int T, int d_in, int d_out) {
 hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* w_tiled, const float* w_scale, int T,
                           int d_in, int d_out, const uint16_t* u, const uint16_t* bt_s, int rs_pad, const uint16_t* v,
                           const int32_t* expert, const uint16_t* bt_r, int rr_pad, int n_r, const int32_t* perm,
-                          float* y, int32_t* acc_debug, int ksplit, int32_t* part, hipStream_t st) {
+                          float* y, int32_t* acc_debug, int ksplit, int32_t* part, bool y_bf16, hipStream_t st) {
     if (T <= 0) return hipSuccess;
     const int n_tn = (d_out + G_BN - 1) / G_BN;
     // 128-token tiles unless that leaves the chip less than two workgroups per CU
@@ -475,12 +475,14 @@ hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* 
     const uint8_t* w = w_tiled;
     const bool split = ksplit > 1 && part != nullptr && acc_debug == nullptr && rs_pad <= 32 && rr_pad <= 32;
     if (split && !small) return hipErrorInvalidValue;
-    const bool fast = !acc_debug && rs_pad <= 32 && rr_pad <= 32;
+    // bf16 outputs take the general epilogue, which stores every output once from registers (the
+    // fast one adds the routed terms of tiles with many experts onto the stored y)
+    const bool fast = !acc_debug && !y_bf16 && rs_pad <= 32 && rr_pad <= 32;
     const int ks = split ? ksplit : 1;
     int32_t* pp = split ? part : nullptr;
 #define QE_GEMM_LAUNCH(MBV, FAST, NTM)                                                                     \
     hipLaunchKernelGGL((gemm_w4_kernel<MBV, FAST>), dim3((NTM) * n_tn, ks), dim3(256), 0, st, codes, s_x, w, \
-                       w_scale, T, d_in, d_out, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, perm, y, acc_debug, NTM, pp)
+                       w_scale, T, d_in, d_out, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, perm, y, acc_debug, NTM, pp, y_bf16)
     if (small) {
         const int n_tm = (T + 63) / 64;
         if (fast) QE_GEMM_LAUNCH(4, true, n_tm);
@@ -495,7 +497,7 @@ hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* 
     if (e != hipSuccess || !split) return e;
     const bool routed = v != nullptr && expert != nullptr && bt_r != nullptr && rr_pad > 0 && n_r > 0;
     return launch_gemm_split_finish(part, ks, T, d_out, s_x, w_scale, rs_pad > 0 ? u : nullptr, bt_s, rs_pad,
-                                    routed ? v : nullptr, routed ? expert : nullptr, n_r, bt_r, rr_pad, y, st);
+                                    routed ? v : nullptr, routed ? expert : nullptr, n_r, bt_r, rr_pad, y, y_bf16, st);
 }
 
 }  // namespace qe

@@ -7,6 +7,7 @@
 //   probe_mfma_bf16_kernel: bf16 matrix-core throughput (v_mfma_f32_16x16x32_bf16, the
 //                          weight-only GEMM's instruction), the same loop
 //   probe_copy_kernel    : streaming HBM copy (16-byte loads and stores)
+//   probe_read_kernel    : streaming HBM read (16-byte loads folded into one word per thread)
 
 #include "qe_internal.h"
 
@@ -110,6 +111,33 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(const v4u* __restrict__
     }
     for (; i < n16; i += stride) dst[i] = src[i];
 }
+
+// Reads every 16-byte chunk once (four independent loads in flight per thread) and folds the
+// words with XOR, so no load can be dropped; one word per thread goes to `sink`.
+__global__ __launch_bounds__(256) void probe_read_kernel(const v4u* __restrict__ src, size_t n16,
+                                                         uint32_t* __restrict__ sink) {
+    const size_t stride = (size_t)gridDim.x * 256;
+    size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    uint32_t h = 0;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const v4u v0 = src[i], v1 = src[i + stride], v2 = src[i + 2 * stride], v3 = src[i + 3 * stride];
+        h ^= v0[0] ^ v0[1] ^ v0[2] ^ v0[3] ^ v1[0] ^ v1[1] ^ v1[2] ^ v1[3];
+        h ^= v2[0] ^ v2[1] ^ v2[2] ^ v2[3] ^ v3[0] ^ v3[1] ^ v3[2] ^ v3[3];
+    }
+    for (; i < n16; i += stride) {
+        const v4u v = src[i];
+        h ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+    }
+    sink[(size_t)blockIdx.x * 256 + threadIdx.x] = h;
+}
+
+hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st) {
+    hipLaunchKernelGGL(probe_read_kernel, dim3(256 * 16), dim3(256), 0, st, reinterpret_cast<const v4u*>(src),
+                       bytes / 16, sink);
+    return hipGetLastError();
+}
+
+size_t probe_read_sink_words() { return (size_t)256 * 16 * 256; }
 
 hipError_t launch_probe_mfma_i8(int32_t* out, int blocks, int iters, int operands, hipStream_t st) {
     hipLaunchKernelGGL(probe_mfma_i8_kernel, dim3(blocks), dim3(256), 0, st, out, iters, operands);

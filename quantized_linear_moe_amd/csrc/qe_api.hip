@@ -24,7 +24,7 @@ int gemm_a16_ksplit(int T, int d_in, int d_out, int w_bits);
 hipError_t launch_gemm_a16(const void* x, int x_dtype, int T, int d_in, int d_out, int w_bits, const void* w_tiled,
                            int ksplit, float* part, const float* w_scale, const uint16_t* u, const uint16_t* bt_s,
                            int rs_pad, const uint16_t* v, const int32_t* expert, const uint16_t* bt_r, int rr_pad,
-                           int n_r, float* y, hipStream_t st);
+                           int n_r, float* y, bool y_bf16, hipStream_t st);
 }  // namespace qe
 
 using namespace qe;
@@ -64,6 +64,7 @@ int validate_linear(const qe_linear* lin) {
     } else {
         QE_CHECK(lin->r_routed == 0, QE_ERR_INVALID_ARG);
     }
+    QE_CHECK(lin->y_dtype == QE_F32 || lin->y_dtype == QE_BF16, QE_ERR_INVALID_ARG);
     QE_CHECK(lin->d_out % 16 == 0, QE_ERR_UNSUPPORTED);
     QE_CHECK(lin->d_in % 128 == 0, QE_ERR_UNSUPPORTED);
     // 16 * |acc| must stay below 2^31 on the int8 path: 16 * 127 * 7 * d_in
@@ -474,6 +475,7 @@ static int run_gemm(const qe_linear* lin, const int8_t* codes, const float* s_x,
     const uint16_t* bt_s = P.rs_pad > 0 ? at<const uint16_t>(lin->prep, P.bt_s) : nullptr;
     const uint16_t* bt_r = P.rr_pad > 0 ? at<const uint16_t>(lin->prep, P.bt_r) : nullptr;
     const float* w_scale = at<const float>(lin->prep, P.w_scale);
+    const bool y_bf16 = lin->y_dtype == QE_BF16;
     if (!bt_s) u = nullptr;
     if (!bt_r) v = nullptr;
     if (lin->a_bits == 16) {
@@ -484,20 +486,20 @@ static int run_gemm(const qe_linear* lin, const int8_t* codes, const float* s_x,
         if (T > kSkinnyMaxT) {  // every weight fragment used for 64 or 128 tokens
             QE_TRY_HIP(launch_gemm_a16(x, x_dtype, T, lin->d_in, lin->d_out, lin->w_bits,
                                        at<const void>(lin->prep, P.w_tiled), W.skinny_ksplit, part, w_scale, u, bt_s,
-                                       P.rs_pad, v, expert, bt_r, P.rr_pad, lin->n_routed, y, s));
+                                       P.rs_pad, v, expert, bt_r, P.rr_pad, lin->n_routed, y, y_bf16, s));
             return QE_OK;
         }
         // weight streaming, the tokens as one MFMA block
         QE_TRY_HIP(launch_skinny(x, x_dtype, T, lin->d_in, lin->d_out, lin->w_bits, at<const void>(lin->prep, P.w_tiled),
                                  W.skinny_ksplit, part, lin->d_out, s));
         QE_TRY_HIP(launch_skinny_finish(part, W.skinny_ksplit, T, lin->d_out, w_scale, u, bt_s, P.rs_pad, v, expert,
-                                        bt_r, P.rr_pad, y, s));
+                                        bt_r, P.rr_pad, y, y_bf16, s));
     } else {
         const WsLayout W = ws_layout(lin, T);
         const int ks = acc_debug ? 1 : W.gemm_ksplit;
         QE_TRY_HIP(launch_gemm_w4(codes, s_x, at<const uint8_t>(lin->prep, P.w_tiled), w_scale, T, lin->d_in,
                                   lin->d_out, u, bt_s, P.rs_pad, v, expert, bt_r, P.rr_pad, lin->n_routed, perm, y,
-                                  acc_debug, ks, ks > 1 ? at<int32_t>(ws, W.skinny) : nullptr, s));
+                                  acc_debug, ks, ks > 1 ? at<int32_t>(ws, W.skinny) : nullptr, y_bf16, s));
     }
     return QE_OK;
 }
@@ -528,6 +530,7 @@ int qe_routed_lora(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t
     if (st) return st;
     QE_CHECK(lin->n_routed > 0, QE_ERR_INVALID_ARG);
     QE_CHECK(T <= 65535, QE_ERR_UNSUPPORTED);
+    QE_CHECK(lin->y_dtype == QE_F32, QE_ERR_UNSUPPORTED);  // adds into y in place
     if (T == 0) return QE_OK;
     QE_CHECK(x && expert && offsets && perm && y, QE_ERR_INVALID_ARG);
     const PrepLayout P = prep_layout(lin);
@@ -633,7 +636,7 @@ int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int3
                                         lin->n_routed, lin->r_routed, P.rr_pad, P.col_router,
                                         P.rs_pad > 0 ? at<const uint16_t>(lin->prep, P.bt_s) : nullptr,
                                         P.rr_pad > 0 ? at<const uint16_t>(lin->prep, P.bt_r) : nullptr,
-                                        route ? expert : nullptr, y, s));
+                                        route ? expert : nullptr, y, lin->y_dtype == QE_BF16, s));
         return QE_OK;
     }
     int8_t* codes = lin->a_bits != 16 ? at<int8_t>(ws, W.codes) : nullptr;
@@ -760,6 +763,7 @@ int qe_linear_forward_top2(const qe_linear* lin, const void* x, int32_t x_dtype,
     const size_t need = qe_top2_workspace_bytes(lin, T);
     QE_CHECK(lin && lin->n_routed >= 2 && need > 0, QE_ERR_INVALID_ARG);
     QE_CHECK(T <= 65535, QE_ERR_UNSUPPORTED);
+    QE_CHECK(lin->y_dtype == QE_F32, QE_ERR_UNSUPPORTED);  // the second expert is added into y
     QE_CHECK(ws_bytes >= need, QE_ERR_WORKSPACE);
     const size_t base = qe_workspace_bytes(lin, T);
     if (T == 0) return validate_forward_common(lin, T, x_dtype, x, ws, ws_bytes);
@@ -999,6 +1003,16 @@ int qe_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
     return QE_OK;
 }
 
+size_t qe_probe_read_sink_bytes(void) { return probe_read_sink_words() * sizeof(uint32_t); }
+
+int qe_probe_read(const void* src, size_t bytes, uint32_t* sink, void* stream) {
+    QE_CHECK(src && sink && bytes % 16 == 0, QE_ERR_INVALID_ARG);
+    QE_CHECK(aligned16(src) && aligned16(sink), QE_ERR_ALIGNMENT);
+    if (bytes == 0) return QE_OK;
+    QE_TRY_HIP(launch_probe_read(src, bytes, sink, S(stream)));
+    return QE_OK;
+}
+
 // ------------------------------------------------------------------ cost
 int qe_linear_cost(const qe_linear* lin, int32_t T, int32_t n_distinct, int32_t xb, double* int_macs,
                    double* adapter_macs, double* alg_bytes) {
@@ -1012,7 +1026,7 @@ int qe_linear_cost(const qe_linear* lin, int32_t T, int32_t n_distinct, int32_t 
         double b = t * di * xb;                              // x read once
         b += di * dout * lin->w_bits / 8.0 + dout * 4.0;     // packed weights + scales
         if (lin->a_bits != 16) b += di * 4.0;                // smoothing vector
-        b += t * dout * 4.0;                                 // y written once (float32)
+        b += t * dout * (lin->y_dtype == QE_BF16 ? 2.0 : 4.0);  // y written once
         b += (di + dout) * rs * 2.0;                         // shared expert
         b += std::min<double>(n_distinct, nr) * (di + dout) * rr * 2.0;  // selected routed experts
         b += di * nr * 2.0;                                  // router

@@ -28,6 +28,13 @@ __device__ inline uint32_t f32_to_bf16_bits(float f) {
     uint32_t u = __float_as_uint(f);
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
+
+// One output element of y: float32, or bf16 (round to nearest even of the same float32 value)
+// when the linear writes bf16 outputs (y then points at uint16_t elements).
+__device__ inline void store_y(float* y, size_t idx, float v, bool y_bf16) {
+    if (y_bf16) reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)f32_to_bf16_bits(v);
+    else y[idx] = v;
+}
 __host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 // 16 four-bit weight codes of one int8-MFMA fragment (8 bytes of the tiled layout, byte b holding
@@ -128,12 +135,12 @@ hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* 
                           int T, int d_in, int d_out, const uint16_t* u, const uint16_t* bt_s, int rs_pad,
                           const uint16_t* v, const int32_t* expert, const uint16_t* bt_r, int rr_pad, int n_r,
                           const int32_t* perm, float* y, int32_t* acc_debug, int ksplit, int32_t* part,
-                          hipStream_t st);
+                          bool y_bf16, hipStream_t st);
 int gemm_ksplit(int T, int d_in, int d_out);
 hipError_t launch_gemm_split_finish(const int32_t* part, int ksplit, int T, int d_out, const float* s_x,
                                     const float* w_scale, const uint16_t* u, const uint16_t* bt_s, int rs_pad,
                                     const uint16_t* v, const int32_t* expert, int n_r, const uint16_t* bt_r,
-                                    int rr_pad, float* y, hipStream_t st);
+                                    int rr_pad, float* y, bool y_bf16, hipStream_t st);
 
 // weight streaming for few tokens: w_bits 3 / 4 read packed tiles, w_bits 16 reads bf16 rows
 // (the x-projection matrix); part[ks][t][c] with row stride out_ld
@@ -146,6 +153,8 @@ double probe_mfma_i8_ops(int blocks, int iters);
 hipError_t launch_probe_mfma_bf16(float* out, int blocks, int iters, int operands, hipStream_t st);
 double probe_mfma_bf16_flops(int blocks, int iters);
 hipError_t launch_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t st);
+hipError_t launch_probe_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t st);
+size_t probe_read_sink_words();
 
 // fused weight-only decode (T <= 16): one GEMV launch for the projection and the packed
 // weights, one finish launch
@@ -163,11 +172,12 @@ hipError_t launch_decode_finish(const float* part_m, const float* s_x, int ks_m,
                                 const float* w_scale, const float* part_p, int ks_p, int ncp, int col_se, int r_s,
                                 int rs_pad, int col_re, int n_r, int r_r, int rr_pad, int col_router,
                                 const uint16_t* bt_s, const uint16_t* bt_r, int32_t* expert_out, float* y,
-                                hipStream_t st);
+                                bool y_bf16, hipStream_t st);
 
 hipError_t launch_skinny_finish(const float* part, int ksplit, int T, int d_out, const float* w_scale,
                                 const uint16_t* u, const uint16_t* bt_s, int rs_pad, const uint16_t* v,
-                                const int32_t* expert, const uint16_t* bt_r, int rr_pad, float* y, hipStream_t st);
+                                const int32_t* expert, const uint16_t* bt_r, int rr_pad, float* y, bool y_bf16,
+                                hipStream_t st);
 
 hipError_t launch_routed_lora(const uint16_t* v, int rr_pad, const int32_t* offsets, const int32_t* perm, int n_r,
                               const uint16_t* bt_r, int T, int d_out, float* y, hipStream_t st);

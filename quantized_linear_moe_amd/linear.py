@@ -71,7 +71,8 @@ class QELinear:
                 ws: Optional[torch.Tensor] = None) -> torch.Tensor:
         T = x.shape[0]
         if y is None:
-            y = torch.empty(T, self.lin.d_out, dtype=torch.float32, device=self.device)
+            dt = torch.bfloat16 if self.lin.y_dtype == L.QE_BF16 else torch.float32
+            y = torch.empty(T, self.lin.d_out, dtype=dt, device=self.device)
         if ws is None:
             ws = self.workspace(T)
         L.qe_linear_forward(self.lin, x, y, expert_out, ws)

@@ -150,3 +150,13 @@ def test_buffer_sizes_for_every_configuration(L, kw, T):
     assert L.qe_workspace_bytes(lin, T) >= 0
     if T > 0:
         assert L.qe_workspace_bytes(lin, T) >= L.qe_workspace_bytes(lin, 1)
+
+
+def test_y_dtype_field_is_validated():
+    from quantized_linear_moe_amd import _libqe as L
+    lin = L.make_linear(256, 512, 4, 8, 8, 4, 8)
+    assert L.qe_workspace_bytes(lin, 64) > 0
+    lin.y_dtype = L.QE_BF16
+    assert L.qe_workspace_bytes(lin, 64) > 0
+    lin.y_dtype = 2  # not a dtype
+    assert L.qe_workspace_bytes(lin, 64) == 0
