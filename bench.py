@@ -338,7 +338,15 @@ def main():
             del params["W_f"]
         layers.append((spec, layer))
         log(f"prepared {spec.name} {spec.d_in}->{spec.d_out}")
-    ws = torch.empty(max(libqe.qe_workspace_bytes(l.lin, T) for _, l in layers), dtype=torch.uint8, device=dev)
+    # one workspace per linear: the linears that read the same input (q/k/v, gate/up) share one
+    # route pass, which leaves each linear's partial sums in that linear's workspace
+    wss = [torch.empty(libqe.qe_workspace_bytes(l.lin, T), dtype=torch.uint8, device=dev) for _, l in layers]
+    groups = []  # indices of consecutive linears that read the same activation stream
+    for i, (spec, _) in enumerate(layers):
+        if groups and layers[groups[-1][0]][0].stream == spec.stream:
+            groups[-1].append(i)
+        else:
+            groups.append([i])
     bufs = []
     for spec, layer in layers:
         bufs.append(dict(
@@ -359,16 +367,25 @@ def main():
     # under the GEMM was measured slower: the GEMM occupies every CU and the prologue
     # kernels only get the gaps.)
     def step(ev=None):
-        for i, (spec, layer) in enumerate(layers):
-            b = bufs[i]
-            libqe.qe_linear_prologue(layer.lin, xs[spec.stream], b["codes"], b["s_x"], b["u"], b["v"], b["e"], ws,
-                                     perm=b["perm"])
-            if ev is not None:
-                ev[i][0].record()
-            libqe.qe_wq_gemm(layer.lin, b["codes"], b["s_x"], None, T, b["u"], b["v"], b["e"], b["y"], None, ws,
-                             perm=b["perm"])
-            if ev is not None:
-                ev[i][1].record()
+        for g in groups:
+            x = xs[layers[g[0]][0].stream]
+            if len(g) == 1:
+                b = bufs[g[0]]
+                libqe.qe_linear_prologue(layers[g[0]][1].lin, x, b["codes"], b["s_x"], b["u"], b["v"], b["e"],
+                                         wss[g[0]], perm=b["perm"])
+            else:
+                bb = [bufs[i] for i in g]
+                libqe.qe_group_prologue([layers[i][1].lin for i in g], x, [b["codes"] for b in bb],
+                                        [b["s_x"] for b in bb], [b["u"] for b in bb], [b["v"] for b in bb],
+                                        [b["e"] for b in bb], [wss[i] for i in g], perm=[b["perm"] for b in bb])
+            for i in g:
+                b = bufs[i]
+                if ev is not None:
+                    ev[i][0].record()
+                libqe.qe_wq_gemm(layers[i][1].lin, b["codes"], b["s_x"], None, T, b["u"], b["v"], b["e"], b["y"],
+                                 None, wss[i], perm=b["perm"])
+                if ev is not None:
+                    ev[i][1].record()
 
     for _ in range(args.warmup):
         step()
@@ -403,16 +420,18 @@ def main():
         cold.append(a.elapsed_time(b))
     del flush
 
-    # the composite entry point on the same inputs (must match the split prologue + GEMM)
+    # the composite entry points on the same inputs (must match the split prologue + GEMM)
+    def composite():
+        for g in groups:
+            libqe.qe_group_forward([layers[i][1].lin for i in g], xs[layers[g[0]][0].stream],
+                                   [bufs[i]["y"] for i in g], [bufs[i]["e"] for i in g], [wss[i] for i in g])
     for _ in range(2):
-        for i, (spec, layer) in enumerate(layers):
-            layer.forward(xs[spec.stream], bufs[i]["y"], bufs[i]["e"], ws)
+        composite()
     torch.cuda.synchronize()
     s2, e2 = ev_t(), ev_t()
     s2.record()
     for _ in range(K):
-        for i, (spec, layer) in enumerate(layers):
-            layer.forward(xs[spec.stream], bufs[i]["y"], bufs[i]["e"], ws)
+        composite()
     e2.record()
     torch.cuda.synchronize()
     ms_step_fwd = s2.elapsed_time(e2) / K
@@ -566,13 +585,20 @@ def layer_throughput(torch, synth, qe, libqe, dev, name, steps=10):
         params = synth.gen_linear(cfg, spec)
         layers.append((spec, qe.QELinear.from_params(params, cfg.w_bits, cfg.a_bits, device=dev)))
         del params
-    ws = torch.empty(max(libqe.qe_workspace_bytes(l.lin, T) for _, l in layers), dtype=torch.uint8, device=dev)
+    wss = [torch.empty(max(libqe.qe_workspace_bytes(l.lin, T), 256), dtype=torch.uint8, device=dev) for _, l in layers]
     ys = [torch.empty(T, spec.d_out, dtype=torch.float32, device=dev) for spec, _ in layers]
     es = [torch.empty(T, dtype=torch.int32, device=dev) for _ in layers]
+    groups = []  # consecutive linears that read the same input share one route pass
+    for i, (spec, _) in enumerate(layers):
+        if groups and layers[groups[-1][0]][0].stream == spec.stream:
+            groups[-1].append(i)
+        else:
+            groups.append([i])
 
     def run():
-        for i, (spec, layer) in enumerate(layers):
-            libqe.qe_linear_forward(layer.lin, xs[spec.stream], ys[i], es[i], ws)
+        for g in groups:
+            libqe.qe_group_forward([layers[i][1].lin for i in g], xs[layers[g[0]][0].stream], [ys[i] for i in g],
+                                   [es[i] for i in g], [wss[i] for i in g])
 
     for _ in range(3):
         run()
@@ -590,7 +616,7 @@ def layer_throughput(torch, synth, qe, libqe, dev, name, steps=10):
         int_ops, adapter_flops, alg = int_ops + 2 * im, adapter_flops + 2 * am, alg + ab
     t_roof = max(int_ops / (PEAK_INT8_TOPS * 1e12) + adapter_flops / (PEAK_BF16_TFLOPS * 1e12),
                  alg / (PEAK_HBM_GBS * 1e9))
-    del layers, ws, xs, ys, es
+    del layers, wss, xs, ys, es
     torch.cuda.empty_cache()
     return {"linears": [f"{s.name} {s.d_in}->{s.d_out}" for s in cfg.linears], "T": T,
             "w_bits": cfg.w_bits, "a_bits": cfg.a_bits, "us_per_step": round(t * 1e6, 2),

@@ -233,6 +233,26 @@ int qe_linear_prologue(const qe_linear* lin, const void* x, int32_t x_dtype, int
 int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* y,
                       int32_t* expert_out, void* ws, size_t ws_bytes, void* stream);
 
+/* Linears that read the same input (q, k and v of an attention block; gate and up of an MLP):
+ * the QE linear of each (DeepRead summary, "Method"), with the input read once for all of their
+ * route passes.  lins[0..n_lin) (1 <= n_lin <= 3, equal d_in); x as for qe_linear_forward;
+ * every other pointer argument is an array of n_lin entries, entry i meaning what the same
+ * argument of qe_linear_prologue / qe_linear_forward means for lins[i]; ws[i] holds
+ * ws_bytes[i] >= qe_workspace_bytes(lins[i], T) bytes, one workspace per linear.  Results are
+ * identical, bit for bit, to calling qe_linear_prologue / qe_linear_forward on each linear in
+ * turn, which is what happens when the group cannot share the pass (fewer than 2 linears,
+ * float32 x, 16 tokens or fewer, weight-only linears, or more than 48 projected columns).
+ * Errors as for the single-linear calls; any invalid entry fails the whole call before any
+ * launch.
+ */
+int qe_group_prologue(const qe_linear* const* lins, int32_t n_lin, const void* x, int32_t x_dtype, int32_t T,
+                      int8_t* const* codes, float* const* s_x, uint16_t* const* u, uint16_t* const* v,
+                      int32_t* const* expert, int32_t* const* perm, void* const* ws, const size_t* ws_bytes,
+                      void* stream);
+int qe_group_forward(const qe_linear* const* lins, int32_t n_lin, const void* x, int32_t x_dtype, int32_t T,
+                     float* const* y, int32_t* const* expert_out, void* const* ws, const size_t* ws_bytes,
+                     void* stream);
+
 /* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): qe_linear_forward without a workspace argument.  It
  * computes exactly what qe_linear_forward computes (the same kernels), with its workspace in a

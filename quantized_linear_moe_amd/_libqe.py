@@ -66,6 +66,8 @@ def _load():
         "qe_routed_lora": (ctypes.c_int, [LP, P, I, I, P, P, P, P, P, Z, P]),
         "qe_linear_prologue": (ctypes.c_int, [LP, P, I, I, P, P, P, P, P, P, P, Z, P]),
         "qe_linear_forward": (ctypes.c_int, [LP, P, I, I, P, P, P, Z, P]),
+        "qe_group_prologue": (ctypes.c_int, [P, I, P, I, I, P, P, P, P, P, P, P, P, P]),
+        "qe_group_forward": (ctypes.c_int, [P, I, P, I, I, P, P, P, P, P]),
         "qe_noalloc_scratch_bytes": (Z, []),
         "qe_linear_forward_noalloc": (ctypes.c_int, [LP, P, I, I, P, P, P]),
         "qe_colmean_abs": (ctypes.c_int, [P, I, I, I, P, P]),
@@ -111,7 +113,8 @@ _lib = _load()
 EXPORTED = (
     "qe_status_string", "qe_last_hip_error", "qe_version", "qe_pack_weights", "qe_prepared_bytes", "qe_prepare",
     "qe_workspace_bytes", "qe_quant_act", "qe_route", "qe_adapter_inputs", "qe_wq_gemm", "qe_routed_lora",
-    "qe_linear_prologue", "qe_linear_forward", "qe_noalloc_scratch_bytes", "qe_linear_forward_noalloc", "qe_colmean_abs", "qe_channel_topk", "qe_linear_cost",
+    "qe_linear_prologue", "qe_linear_forward", "qe_noalloc_scratch_bytes", "qe_linear_forward_noalloc",
+    "qe_group_prologue", "qe_group_forward", "qe_colmean_abs", "qe_channel_topk", "qe_linear_cost",
     "qe_probe_mfma_i8", "qe_probe_mfma_bf16", "qe_probe_copy", "qe_probe_read_sink_bytes", "qe_probe_read", "qe_partition_channels", "qe_cooccur_workspace_bytes",
     "qe_cooccur", "qe_cluster_channels", "qe_top2_workspace_bytes", "qe_linear_forward_top2", "qe_quant_error", "qe_channel_rms_workspace_bytes", "qe_channel_rms",
     "qe_sub_lowrank", "qe_lowrank_workspace_bytes", "qe_lowrank_fit", "qe_build_experts_workspace_bytes",
@@ -238,6 +241,33 @@ def rank_pad(r: int) -> int:
 def qe_linear_forward(lin, x, y, expert_out, ws, stream=None):
     _check(_lib.qe_linear_forward(ctypes.byref(lin), _ptr(x), _dtype_code(x), x.shape[0], _ptr(y), _ptr(expert_out),
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)), "qe_linear_forward")
+
+
+def _ptr_array(items):
+    return (ctypes.c_void_p * len(items))(*[_ptr(t) for t in items])
+
+
+def _lin_array(lins):
+    return (ctypes.POINTER(qe_linear) * len(lins))(*[ctypes.pointer(l) for l in lins])
+
+
+def qe_group_prologue(lins, x, codes, s_x, u, v, expert, ws, perm=None, stream=None):
+    """Prologues of linears that read the same x (lists, one entry per linear; see include/qe.h)."""
+    n = len(lins)
+    perm = perm if perm is not None else [None] * n
+    wsb = (ctypes.c_size_t * n)(*[w.numel() * w.element_size() for w in ws])
+    _check(_lib.qe_group_prologue(_lin_array(lins), n, _ptr(x), _dtype_code(x), x.shape[0], _ptr_array(codes),
+                                  _ptr_array(s_x), _ptr_array(u), _ptr_array(v), _ptr_array(expert),
+                                  _ptr_array(perm), _ptr_array(ws), wsb, _stream(stream)), "qe_group_prologue")
+
+
+def qe_group_forward(lins, x, ys, expert_out, ws, stream=None):
+    """QE linears that read the same x (lists, one entry per linear; expert_out a list or None)."""
+    n = len(lins)
+    eo = _ptr_array(expert_out) if expert_out is not None else None
+    wsb = (ctypes.c_size_t * n)(*[w.numel() * w.element_size() for w in ws])
+    _check(_lib.qe_group_forward(_lin_array(lins), n, _ptr(x), _dtype_code(x), x.shape[0], _ptr_array(ys), eo,
+                                 _ptr_array(ws), wsb, _stream(stream)), "qe_group_forward")
 
 
 def qe_noalloc_scratch_bytes() -> int:

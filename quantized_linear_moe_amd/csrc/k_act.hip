@@ -645,6 +645,166 @@ hipError_t launch_route_pass(const uint16_t* x, int T, int d_in, const uint16_t*
     return hipGetLastError();
 }
 
+// ---- pass 1 for a group of linears that read the same input (q/k/v, gate/up)
+// The same tile as route_pass_kernel, for up to RG_MAX linears at once: x is read once per
+// 128-channel group and feeds every linear's projection MFMAs (its shared-expert and router
+// rows) and every linear's max |x / s_l| (each linear has its own smoothing).  Each linear's
+// projection rows and smoothing factors are staged in their own slice of the double-buffered
+// LDS; its partial sums go to its own buffers, laid out exactly as route_pass_kernel's.
+template <int NL, int NBK>
+__global__ __launch_bounds__(256, 2) void route_pass_group_kernel(const uint16_t* __restrict__ x, int T, int d_in,
+                                                               RouteGroup G, int ksplit) {
+    constexpr int MP = NBK;
+    constexpr int M_LDS = MP * 256 * 16;
+    constexpr int LBUF = M_LDS + 1024;  // one linear's rows and smoothing factors
+    constexpr int BUF = NL * LBUF;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF];
+    const int tok0 = blockIdx.x * RP_TOK, ks = blockIdx.y;
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int ngr = d_in / RP_KG;
+    const int g_beg = (int)((long)ks * ngr / ksplit), g_end = (int)((long)(ks + 1) * ngr / ksplit);
+    const int row = tok0 + wid * 16 + lr;
+    const bool rvalid = row < T;
+    const uint16_t* xrow = x + (size_t)min(row, T - 1) * d_in + lg * 32;  // rows past T repeat a valid row
+
+    v4f acc[NL][NBK];
+#pragma unroll
+    for (int l = 0; l < NL; ++l)
+#pragma unroll
+        for (int n = 0; n < NBK; ++n) acc[l][n] = v4f{0, 0, 0, 0};
+    float amax[NL];
+#pragma unroll
+    for (int l = 0; l < NL; ++l) amax[l] = 0.0f;
+
+    // x is double-buffered in registers (the next group's rows are requested before a group is
+    // processed); each linear's projection rows and smoothing factors are single-buffered: the
+    // next group's are requested right after the barrier that retires the current ones, so
+    // they are in flight during the current group's arithmetic
+    v4u m[NL][MP];
+    v4f sv[NL];
+    auto load_x = [&](v4u (&xr)[4], int g) {
+        const size_t k0 = (size_t)g * RP_KG;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xr[q] = *reinterpret_cast<const v4u*>(xrow + k0 + q * 8);
+    };
+    auto load_m = [&](int g) {
+        const size_t k0 = (size_t)g * RP_KG;
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+#pragma unroll
+            for (int p = 0; p < MP; ++p) {
+                const int idx = tid + 256 * p, r = idx >> 4, c = idx & 15;
+                m[l][p] = *reinterpret_cast<const v4u*>(G.mt[l] + (size_t)min(r, G.ncols[l] - 1) * d_in + k0 + c * 8);
+            }
+            sv[l] = *reinterpret_cast<const v4f*>(((tid & 32) ? G.inv_smooth[l] : G.smooth[l]) + k0 + (tid & 31) * 4);
+        }
+    };
+    auto process = [&](const v4u (&xr)[4], int g) {
+        uint8_t* buf = smem + (g & 1) * BUF;
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            uint8_t* lb = buf + l * LBUF;
+#pragma unroll
+            for (int p = 0; p < MP; ++p) {
+                const int idx = tid + 256 * p, r = idx >> 4, c = idx & 15;
+                if (r < G.ncols[l]) *reinterpret_cast<v4u*>(lb + r * 256 + ((c ^ (r & 15)) << 4)) = m[l][p];
+            }
+            if (tid < 64) *reinterpret_cast<v4f*>(lb + M_LDS + tid * 16) = sv[l];
+        }
+        QE_WAIT_LDS();
+        QE_WG_BARRIER();
+        load_m(min(g + 1, g_end - 1));  // past the range: a harmless repeat of the last group
+#pragma unroll
+        for (int l = 0; l < NL; ++l) {
+            const uint8_t* lb = buf + l * LBUF;
+            if (rvalid) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint8_t* sp = lb + M_LDS + (lg * 32 + q * 8) * 4;
+                    const v4f s0 = *reinterpret_cast<const v4f*>(sp), s1 = *reinterpret_cast<const v4f*>(sp + 16);
+                    const v4f i0 = *reinterpret_cast<const v4f*>(sp + 512), i1 = *reinterpret_cast<const v4f*>(sp + 528);
+                    float xs[8];
+                    smooth_div8(xr[q], s0, s1, i0, i1, xs);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) amax[l] = fmaxf(amax[l], __builtin_fabsf(xs[e]));
+                }
+            }
+            v8bf bv[4][NBK];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int n = 0; n < NBK; ++n) {
+                    const int rm = n * 16 + lr;
+                    bv[q][n] = *reinterpret_cast<const v8bf*>(lb + rm * 256 + (((lg * 4 + q) ^ (rm & 15)) << 4));
+                }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int n = 0; n < NBK; ++n)
+                    acc[l][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const v8bf*>(&xr[q]),
+                                                                        bv[q][n], acc[l][n], 0, 0, 0);
+        }
+    };
+    if (g_beg < g_end) {
+        v4u xa[4], xb[4];
+        load_x(xa, g_beg);
+        load_m(g_beg);
+        for (int g = g_beg; g < g_end; g += 2) {
+            load_x(xb, min(g + 1, g_end - 1));
+            process(xa, g);
+            load_x(xa, min(g + 2, g_end - 1));
+            if (g + 1 < g_end) process(xb, g + 1);
+        }
+    }
+
+#pragma unroll
+    for (int l = 0; l < NL; ++l) {
+        const int nc = G.ncols[l];
+        float* out = G.part[l] + (size_t)ks * T * nc;
+#pragma unroll
+        for (int n = 0; n < NBK; ++n) {
+            if (n * 16 >= nc) break;  // uniform
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int t = tok0 + wid * 16 + lg * 4 + r;
+                if (t < T) out[(size_t)t * nc + n * 16 + lr] = acc[l][n][r];
+            }
+        }
+        float m = amax[l];
+        m = fmaxf(m, __shfl_xor(m, 16, 64));
+        m = fmaxf(m, __shfl_xor(m, 32, 64));
+        if (lg == 0 && rvalid) G.amax[l][(size_t)ks * T + row] = m;
+    }
+}
+
+hipError_t launch_route_pass_group(const uint16_t* x, int T, int d_in, const RouteGroup& G, int n_lin, int ksplit,
+                                   hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (n_lin < 2 || n_lin > RG_MAX || d_in % RP_KG || ksplit < 1 || ksplit > d_in / RP_KG) return hipErrorInvalidValue;
+    int nbk = 0;
+    for (int l = 0; l < n_lin; ++l) {
+        if (G.ncols[l] < 16 || G.ncols[l] > RP_MAXN * 16 || G.ncols[l] % 16 || !G.smooth[l] || !G.inv_smooth[l] ||
+            !G.mt[l] || !G.part[l] || !G.amax[l])
+            return hipErrorInvalidValue;
+        nbk = std::max(nbk, G.ncols[l] / 16);
+    }
+    if (nbk > 3) return hipErrorInvalidValue;  // the grouped tile holds up to 48 projected columns per linear
+    const dim3 grid((T + RP_TOK - 1) / RP_TOK, ksplit);
+#define QE_RPG_LAUNCH(NLV, NB) \
+    hipLaunchKernelGGL((route_pass_group_kernel<NLV, NB>), grid, dim3(256), 0, st, x, T, d_in, G, ksplit)
+    if (n_lin == 2) {
+        if (nbk == 1) QE_RPG_LAUNCH(2, 1);
+        else if (nbk == 2) QE_RPG_LAUNCH(2, 2);
+        else QE_RPG_LAUNCH(2, 3);
+    } else {
+        if (nbk == 1) QE_RPG_LAUNCH(3, 1);
+        else if (nbk == 2) QE_RPG_LAUNCH(3, 2);
+        else QE_RPG_LAUNCH(3, 3);
+    }
+#undef QE_RPG_LAUNCH
+    return hipGetLastError();
+}
+
 // One wave per token: fixed-order split-K sums, router argmin (lowest index on ties),
 // u = bf16(shared projection), s_x = max |x/s| / qmax (a max is exact in any order).
 __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restrict__ part,

@@ -72,7 +72,23 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     constexpr int NS = MB == 4 ? 8 : G_NS;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
-    const int tm = blockIdx.x % n_tm, tn = blockIdx.x / n_tm;
+    // Tile order.  Workgroups are handed to the 8 XCDs in turn (block b to XCD b % 8), each
+    // XCD with its own L2: the block index is renumbered so that every XCD walks a contiguous
+    // range of logical tiles, and logical tiles run down groups of 8 token tiles across the
+    // channel tiles.  An XCD then touches 8 token tiles and a band of channel tiles, so every
+    // activation tile is fetched by about 2 XCDs and every weight tile by about 4 (the plain
+    // order made all 8 fetch every weight tile); the result does not depend on the order.
+    int tm, tn;
+    {
+        const int G = gridDim.x, n_tn = G / n_tm;
+        int L = blockIdx.x;
+        if ((G & 7) == 0) L = (L & 7) * (G >> 3) + (L >> 3);
+        constexpr int GM = 8;
+        const int per_group = GM * n_tn;
+        const int g = L / per_group, first = g * GM, gs = min(n_tm - first, GM), r = L - g * per_group;
+        tm = first + r % gs;
+        tn = r / gs;
+    }
     const int m0 = tm * BM;
     const int NB = d_out >> 4, KB = d_in / G_BK;
     // K steps of this workgroup: all of them, or split gridDim.y of `part`'s partial sums

@@ -545,6 +545,28 @@ int qe_routed_lora(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t
 }
 
 // ------------------------------------------------------------------ composite
+// The two-pass prologue after its route pass (whose partials are in ws): route finish, then the
+// expert-sorted quantization pass.
+static int run_prologue_rest(const qe_linear* lin, const void* x, int T, int8_t* codes, float* s_x, uint16_t* u,
+                             uint16_t* v, int32_t* expert, int32_t* perm, void* ws, hipStream_t s, bool keep_order) {
+    const PrepLayout P = prep_layout(lin);
+    const WsLayout W = ws_layout(lin, T);
+    const bool route = lin->n_routed > 0;
+    const float* smooth = at<const float>(lin->prep, P.smooth);
+    const float* inv_smooth = at<const float>(lin->prep, P.inv_smooth);
+    const uint16_t* mt = at<const uint16_t>(lin->prep, P.mt);
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
+    QE_TRY_HIP(launch_route_finish(at<const float>(ws, W.part), at<const float>(ws, W.amax), W.rp_ksplit, T,
+                                       P.n_lead, lin->r_shared, P.rs_pad, P.col_router, lin->n_routed, lin->a_bits,
+                                       route ? expert : nullptr, u, s_x, s));
+        QE_TRY_HIP(launch_expert_quant(xb, T, lin->d_in, smooth, inv_smooth, s_x, lin->a_bits,
+                                       route ? expert : nullptr, lin->n_routed,
+                                       route ? mt + (size_t)P.col_re * lin->d_in : nullptr, P.rr_pad, lin->r_routed,
+                                       W.eq_ksplit, route ? (perm ? perm : at<int32_t>(ws, W.perm)) : nullptr,
+                                       at<float>(ws, W.vpart), codes, route ? v : nullptr, keep_order, s));
+    return QE_OK;
+}
+
 // keep_order: few tokens may stay in token order in the two-pass prologue (perm is then not
 // written; the caller passes perm == NULL)
 static int run_prologue(const qe_linear* lin, const void* x, int x_dtype, int T, int8_t* codes, float* s_x,
@@ -554,21 +576,11 @@ static int run_prologue(const qe_linear* lin, const void* x, int x_dtype, int T,
     const WsLayout W = ws_layout(lin, T);
     const bool route = lin->n_routed > 0;
     if (two_pass_sized(lin, T) && x_dtype == QE_BF16) {
-        const float* smooth = at<const float>(lin->prep, P.smooth);
-        const float* inv_smooth = at<const float>(lin->prep, P.inv_smooth);
-        const uint16_t* mt = at<const uint16_t>(lin->prep, P.mt);
-        const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
-        QE_TRY_HIP(launch_route_pass(xb, T, lin->d_in, mt, P.n_lead, smooth, inv_smooth, W.rp_ksplit,
-                                     at<float>(ws, W.part), at<float>(ws, W.amax), s));
-        QE_TRY_HIP(launch_route_finish(at<const float>(ws, W.part), at<const float>(ws, W.amax), W.rp_ksplit, T,
-                                       P.n_lead, lin->r_shared, P.rs_pad, P.col_router, lin->n_routed, lin->a_bits,
-                                       route ? expert : nullptr, u, s_x, s));
-        QE_TRY_HIP(launch_expert_quant(xb, T, lin->d_in, smooth, inv_smooth, s_x, lin->a_bits,
-                                       route ? expert : nullptr, lin->n_routed,
-                                       route ? mt + (size_t)P.col_re * lin->d_in : nullptr, P.rr_pad, lin->r_routed,
-                                       W.eq_ksplit, route ? (perm ? perm : at<int32_t>(ws, W.perm)) : nullptr,
-                                       at<float>(ws, W.vpart), codes, route ? v : nullptr, keep_order, s));
-        return QE_OK;
+        QE_TRY_HIP(launch_route_pass(reinterpret_cast<const uint16_t*>(x), T, lin->d_in,
+                                     at<const uint16_t>(lin->prep, P.mt), P.n_lead, at<const float>(lin->prep, P.smooth),
+                                     at<const float>(lin->prep, P.inv_smooth), W.rp_ksplit, at<float>(ws, W.part),
+                                     at<float>(ws, W.amax), s));
+        return run_prologue_rest(lin, x, T, codes, s_x, u, v, expert, perm, ws, s, keep_order);
     }
     int st = run_xpass(lin, x, x_dtype, T, u != nullptr, route, route, nullptr, nullptr, route ? expert : nullptr, u,
                        v, ws, s);
@@ -649,6 +661,133 @@ int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int3
     st = run_prologue(lin, x, x_dtype, T, codes, s_x, u, v, expert, perm, ws, s, keep_order);
     if (st) return st;
     return run_gemm(lin, codes, s_x, x, x_dtype, T, u, v, expert, perm, y, nullptr, ws, s);
+}
+
+// ------------------------------------------------------------------ linears sharing one input
+// Whether a group of linears takes the grouped route pass: 2..3 linears on the same bf16 x, all
+// on the two-pass prefill prologue, with the same d_in and at most 48 projected columns each.
+static bool group_route_pass(const qe_linear* const* lins, int n, int x_dtype, int T) {
+    if (n < 2 || n > RG_MAX || x_dtype != QE_BF16) return false;
+    for (int i = 0; i < n; ++i) {
+        if (!two_pass_sized(lins[i], T) || lins[i]->d_in != lins[0]->d_in) return false;
+        const int nl = prep_layout(lins[i]).n_lead;
+        if (nl < 16 || nl > 48) return false;
+    }
+    return true;
+}
+
+static int validate_group(const qe_linear* const* lins, int32_t n, int32_t T, int32_t x_dtype, const void* x,
+                          void* const* ws, const size_t* ws_bytes) {
+    QE_CHECK(lins && n >= 1 && n <= RG_MAX && ws && ws_bytes, QE_ERR_INVALID_ARG);
+    for (int i = 0; i < n; ++i) {
+        int st = validate_forward_common(lins[i], T, x_dtype, x, ws[i], ws_bytes[i]);
+        if (st) return st;
+        QE_CHECK(lins[i]->d_in == lins[0]->d_in, QE_ERR_INVALID_ARG);
+    }
+    return QE_OK;
+}
+
+// One read of x for the route passes of the group: each linear's partials land where its own
+// route pass would put them (its workspace), then each linear's route finish and quantization.
+static int run_group_prologue(const qe_linear* const* lins, int n, const void* x, int x_dtype, int T,
+                              int8_t* const* codes, float* const* s_x, uint16_t* const* u, uint16_t* const* v,
+                              int32_t* const* expert, int32_t* const* perm, void* const* ws, hipStream_t s,
+                              const bool* keep_order) {
+    if (!group_route_pass(lins, n, x_dtype, T)) {
+        for (int i = 0; i < n; ++i) {
+            int st = run_prologue(lins[i], x, x_dtype, T, codes[i], s_x[i], u[i], v[i], expert[i], perm[i], ws[i], s,
+                                  keep_order ? keep_order[i] : false);
+            if (st) return st;
+        }
+        return QE_OK;
+    }
+    RouteGroup G{};
+    int ks = 0;
+    for (int i = 0; i < n; ++i) {
+        const PrepLayout P = prep_layout(lins[i]);
+        const WsLayout W = ws_layout(lins[i], T);
+        G.mt[i] = at<const uint16_t>(lins[i]->prep, P.mt);
+        G.smooth[i] = at<const float>(lins[i]->prep, P.smooth);
+        G.inv_smooth[i] = at<const float>(lins[i]->prep, P.inv_smooth);
+        G.part[i] = at<float>(ws[i], W.part);
+        G.amax[i] = at<float>(ws[i], W.amax);
+        G.ncols[i] = P.n_lead;
+        ks = W.rp_ksplit;  // depends on T and d_in only: the same for every linear of the group
+    }
+    QE_TRY_HIP(launch_route_pass_group(reinterpret_cast<const uint16_t*>(x), T, lins[0]->d_in, G, n, ks, s));
+    for (int i = 0; i < n; ++i) {
+        int st = run_prologue_rest(lins[i], x, T, codes[i], s_x[i], u[i], v[i], expert[i], perm[i], ws[i], s,
+                                   keep_order ? keep_order[i] : false);
+        if (st) return st;
+    }
+    return QE_OK;
+}
+
+int qe_group_prologue(const qe_linear* const* lins, int32_t n_lin, const void* x, int32_t x_dtype, int32_t T,
+                      int8_t* const* codes, float* const* s_x, uint16_t* const* u, uint16_t* const* v,
+                      int32_t* const* expert, int32_t* const* perm, void* const* ws, const size_t* ws_bytes,
+                      void* stream) {
+    int st = validate_group(lins, n_lin, T, x_dtype, x, ws, ws_bytes);
+    if (st) return st;
+    QE_CHECK(codes && s_x && u && v && expert && perm, QE_ERR_INVALID_ARG);
+    if (T == 0) return QE_OK;
+    QE_CHECK(x != nullptr, QE_ERR_INVALID_ARG);
+    for (int i = 0; i < n_lin; ++i) {
+        const qe_linear* lin = lins[i];
+        QE_CHECK(lin->a_bits == 16 ? (codes[i] == nullptr && s_x[i] == nullptr) : (codes[i] && s_x[i]),
+                 QE_ERR_INVALID_ARG);
+        QE_CHECK((lin->r_shared > 0) == (u[i] != nullptr), QE_ERR_INVALID_ARG);
+        QE_CHECK((lin->n_routed > 0) == (v[i] != nullptr) && (lin->n_routed > 0) == (expert[i] != nullptr),
+                 QE_ERR_INVALID_ARG);
+        QE_CHECK(!perm[i] || lin->n_routed > 0, QE_ERR_INVALID_ARG);
+        if (codes[i]) QE_CHECK(aligned16(codes[i]), QE_ERR_ALIGNMENT);
+    }
+    return run_group_prologue(lins, n_lin, x, x_dtype, T, codes, s_x, u, v, expert, perm, ws, S(stream), nullptr);
+}
+
+int qe_group_forward(const qe_linear* const* lins, int32_t n_lin, const void* x, int32_t x_dtype, int32_t T,
+                     float* const* y, int32_t* const* expert_out, void* const* ws, const size_t* ws_bytes,
+                     void* stream) {
+    int st = validate_group(lins, n_lin, T, x_dtype, x, ws, ws_bytes);
+    if (st) return st;
+    QE_CHECK(y, QE_ERR_INVALID_ARG);
+    if (T == 0) return QE_OK;
+    QE_CHECK(x != nullptr, QE_ERR_INVALID_ARG);
+    for (int i = 0; i < n_lin; ++i) QE_CHECK(y[i] && aligned16(y[i]), y[i] ? QE_ERR_ALIGNMENT : QE_ERR_INVALID_ARG);
+    if (!group_route_pass(lins, n_lin, x_dtype, T)) {  // the linears one by one
+        for (int i = 0; i < n_lin; ++i) {
+            st = qe_linear_forward(lins[i], x, x_dtype, T, y[i], expert_out ? expert_out[i] : nullptr, ws[i],
+                                   ws_bytes[i], stream);
+            if (st) return st;
+        }
+        return QE_OK;
+    }
+    hipStream_t s = S(stream);
+    int8_t* codes[RG_MAX];
+    float* s_x[RG_MAX];
+    uint16_t *u[RG_MAX], *v[RG_MAX];
+    int32_t *expert[RG_MAX], *perm[RG_MAX];
+    bool keep[RG_MAX];
+    for (int i = 0; i < n_lin; ++i) {  // the buffers qe_linear_forward takes from each workspace
+        const qe_linear* lin = lins[i];
+        const PrepLayout P = prep_layout(lin);
+        const WsLayout W = ws_layout(lin, T);
+        const bool route = lin->n_routed > 0;
+        expert[i] = route ? (expert_out && expert_out[i] ? expert_out[i] : at<int32_t>(ws[i], W.expert)) : nullptr;
+        u[i] = P.rs_pad > 0 ? at<uint16_t>(ws[i], W.u) : nullptr;
+        v[i] = route ? at<uint16_t>(ws[i], W.v) : nullptr;
+        codes[i] = at<int8_t>(ws[i], W.codes);
+        s_x[i] = at<float>(ws[i], W.s_x);
+        keep[i] = expert_quant_few(T) && W.gemm_ksplit > 1;
+        perm[i] = (route && !keep[i]) ? at<int32_t>(ws[i], W.perm) : nullptr;
+    }
+    st = run_group_prologue(lins, n_lin, x, x_dtype, T, codes, s_x, u, v, expert, perm, ws, s, keep);
+    if (st) return st;
+    for (int i = 0; i < n_lin; ++i) {
+        st = run_gemm(lins[i], codes[i], s_x[i], x, x_dtype, T, u[i], v[i], expert[i], perm[i], y[i], nullptr, ws[i], s);
+        if (st) return st;
+    }
+    return QE_OK;
 }
 
 size_t qe_noalloc_scratch_bytes(void) { return qe::kNoAllocScratchBytes; }

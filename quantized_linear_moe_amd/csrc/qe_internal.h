@@ -113,6 +113,20 @@ hipError_t launch_xproj_finish(const float* part, int ksplit, int T, int ncols_p
 hipError_t launch_route_pass(const uint16_t* x, int T, int d_in, const uint16_t* mt, int ncols, const float* smooth,
                              const float* inv_smooth, int ksplit, float* part, float* amax_part, hipStream_t st);
 int route_pass_ksplit(int T, int d_in);
+// the route pass of up to RG_MAX linears that read the same x (one read of x): per linear its
+// projection rows (Mt's leading ncols rows, ncols 16..48), smoothing factors and the partial
+// buffers the single-linear pass would write
+constexpr int RG_MAX = 3;
+struct RouteGroup {
+    const uint16_t* mt[RG_MAX];
+    const float* smooth[RG_MAX];
+    const float* inv_smooth[RG_MAX];
+    float* part[RG_MAX];
+    float* amax[RG_MAX];
+    int ncols[RG_MAX];
+};
+hipError_t launch_route_pass_group(const uint16_t* x, int T, int d_in, const RouteGroup& G, int n_lin, int ksplit,
+                                   hipStream_t st);
 hipError_t launch_route_finish(const float* part, const float* amax_part, int ksplit, int T, int ncols, int r_s,
                                int rs_pad, int router_col, int n_r, int a_bits, int32_t* expert, uint16_t* u,
                                float* s_x, hipStream_t st);
