@@ -12,9 +12,9 @@ int8-MFMA main GEMM with the dequantization and the shared/routed low-rank terms
 fused into its epilogue.  Inputs are resident in HBM before the timed region.
 
 Prints one JSON line.  `value` is tokens/s of the whole layer (T / step time).
-`roofline` is the dominant kernel, the 128-token-tile instantiation of the main GEMM
-(q, o, gate, up and down use it; the narrow k and v projections use 64-token tiles),
-timed with HIP events around each of its launches on the stream it is launched on.
+`roofline` is the dominant kernel, the main GEMM: one launch per group of linears that read
+the same input (q+k+v, o, gate+up, down; 128-token tiles), timed with HIP events around each
+of its launches on the stream it is launched on.
 
 `--copy-calibration` only times a 1 GiB device copy (the reference kernel for the
 HBM byte counters) and exits.
@@ -58,6 +58,9 @@ def parse():
                     help="time the int8 and bf16 MFMA ceilings of this part at the 72B layer's GEMM shapes: the "
                          "library's main GEMM, torch's int8 and bf16 matrix products (hipBLASLt) and the MFMA "
                          "probe loops; prints one JSON line and exits")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="run only the decode lines (Qwen2VL-72B up + down, T = 8, W3A16 and W4A6), print them "
+                         "as one JSON line and exit (the workload of the decode traffic counters)")
     ap.add_argument("--mfma-counters", metavar="DIR",
                     help="summarize a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_I8 "
                          "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE GRBM_COUNT --kernel-trace "
@@ -90,7 +93,7 @@ def load_traffic(per_launch_alg_bytes):
     return d.get("hbm_bytes_per_launch", {}).get("total")
 
 
-TRAFFIC_KERNEL = "gemm_w4_kernel<8, true>"
+TRAFFIC_KERNEL = "gemm_w4_group_kernel"
 
 
 def mfma_counters(d, n_simd=1024, n_xcd=8):
@@ -171,7 +174,8 @@ def write_traffic(d_bench_fetch, d_bench_write, d_copy_fetch, d_copy_write):
     bench_args = "--steps 2 --warmup 1 --no-cpu-baseline --no-extras"
     out = {
         "kernel": TRAFFIC_KERNEL,
-        "workload": "Qwen2VL-72B layer linears q, o, gate, up, down; W4A6; T=4096; averaged over their launches",
+        "workload": "Qwen2VL-72B layer linears, W4A6, T=4096: the grouped main-GEMM launches q+k+v, o, gate+up and "
+                    "down, averaged over them",
         "kernel_source_hash": gemm_source_hash(),
         "commands": [cmd.format(c="FETCH_SIZE", d=d_bench_fetch, a=bench_args),
                      cmd.format(c="WRITE_SIZE", d=d_bench_write, a=bench_args),
@@ -192,12 +196,6 @@ def write_traffic(d_bench_fetch, d_bench_write, d_copy_fetch, d_copy_write):
         json.dump(out, fh, indent=1)
         fh.write("\n")
     print(path, out["hbm_bytes_per_launch"])
-
-
-def uses_128_token_tiles(T, d_out):
-    """The GEMM launcher's tile choice: 128-token tiles unless that gives fewer than
-    512 workgroups."""
-    return ((T + 127) // 128) * ((d_out + 255) // 256) >= 512
 
 
 def copy_calibration():
@@ -307,6 +305,17 @@ def main():
     if args.mfma_counters:
         mfma_counters(args.mfma_counters)
         return
+    if args.decode_only:
+        import torch
+        import synth
+        import quantized_linear_moe_amd as qe
+        from quantized_linear_moe_amd import libqe
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        print(json.dumps({"decode_qwen2vl72b_up_down_w3a16_T8": decode_line(torch, synth, qe, libqe, dev, 3, 16),
+                          "decode_qwen2vl72b_up_down_w4a6_T8": decode_line(torch, synth, qe, libqe, dev, 4, 6)}),
+              flush=True)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures the QE linear on exactly one GPU; multi-GPU runs are not part of this "
@@ -347,6 +356,7 @@ def main():
             groups[-1].append(i)
         else:
             groups.append([i])
+    gi_of = {g[0]: k for k, g in enumerate(groups)}
     bufs = []
     for spec, layer in layers:
         bufs.append(dict(
@@ -378,14 +388,14 @@ def main():
                 libqe.qe_group_prologue([layers[i][1].lin for i in g], x, [b["codes"] for b in bb],
                                         [b["s_x"] for b in bb], [b["u"] for b in bb], [b["v"] for b in bb],
                                         [b["e"] for b in bb], [wss[i] for i in g], perm=[b["perm"] for b in bb])
-            for i in g:
-                b = bufs[i]
-                if ev is not None:
-                    ev[i][0].record()
-                libqe.qe_wq_gemm(layers[i][1].lin, b["codes"], b["s_x"], None, T, b["u"], b["v"], b["e"], b["y"],
-                                 None, wss[i], perm=b["perm"])
-                if ev is not None:
-                    ev[i][1].record()
+            bb = [bufs[i] for i in g]
+            if ev is not None:
+                ev[gi_of[g[0]]][0].record()
+            libqe.qe_group_gemm([layers[i][1].lin for i in g], [b["codes"] for b in bb], [b["s_x"] for b in bb], T,
+                                [b["u"] for b in bb], [b["v"] for b in bb], [b["e"] for b in bb],
+                                [b["y"] for b in bb], [wss[i] for i in g], perm=[b["perm"] for b in bb])
+            if ev is not None:
+                ev[gi_of[g[0]]][1].record()
 
     for _ in range(args.warmup):
         step()
@@ -393,7 +403,7 @@ def main():
 
     ev_t = lambda: torch.cuda.Event(enable_timing=True)
     K = args.steps
-    evs = [[(ev_t(), ev_t()) for _ in layers] for _ in range(K)]
+    evs = [[(ev_t(), ev_t()) for _ in groups] for _ in range(K)]
     marks = [ev_t() for _ in range(K + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -405,7 +415,7 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = marks[0].elapsed_time(marks[K]) / K
     step_ms = np.array([marks[k].elapsed_time(marks[k + 1]) for k in range(K)])
-    gemm_ms = np.array([[a.elapsed_time(b) for (a, b) in evs[k]] for k in range(K)])  # [K, 7]
+    gemm_ms = np.array([[a.elapsed_time(b) for (a, b) in evs[k]] for k in range(K)])  # [K, groups]
     gemm_ms_step = float(gemm_ms.sum(axis=1).mean())
 
     # cold steps: the Infinity Cache flushed before each (timed alone, not part of `value`)
@@ -438,8 +448,9 @@ def main():
 
     # ------------------------------------------------------------ accounting
     int_ops = adapter_flops = alg_bytes = 0.0
-    per_linear = []
+    per_linear, per_group = [], []
     gpu_routes = []
+    ops_lin = []
     for i, (spec, layer) in enumerate(layers):
         e_host = bufs[i]["e"].cpu().numpy()
         gpu_routes.append(e_host)
@@ -448,14 +459,19 @@ def main():
         int_ops += 2 * im
         adapter_flops += 2 * am
         alg_bytes += ab
+        ops_lin.append(2 * im)
         per_linear.append(dict(name=spec.name, d_in=spec.d_in, d_out=spec.d_out,
-                               gemm_us=round(float(gemm_ms[:, i].mean()) * 1e3, 2),
-                               gemm_tops=round(2 * im / (gemm_ms[:, i].mean() * 1e-3) / 1e12, 1),
                                expert_histogram=np.bincount(e_host, minlength=cfg.n_routed).tolist()))
-    big = [i for i, (spec, _) in enumerate(layers) if uses_128_token_tiles(T, spec.d_out)]
-    big_ops = sum(2 * libqe.qe_linear_cost(layers[i][1].lin, T, 1, 2)[0] for i in big)
-    big_ms = float(gemm_ms[:, big].sum(axis=1).mean())  # per step
+    for k, g in enumerate(groups):
+        ops = sum(ops_lin[i] for i in g)
+        per_group.append(dict(linears=",".join(layers[i][0].name for i in g),
+                              gemm_us=round(float(gemm_ms[:, k].mean()) * 1e3, 2),
+                              gemm_tops=round(ops / (gemm_ms[:, k].mean() * 1e-3) / 1e12, 1)))
+    # every group's main products run as one launch of the grouped GEMM kernel (128-token tiles)
+    big_ops = sum(ops_lin)
+    big_ms = float(gemm_ms.sum(axis=1).mean())  # per step
     achieved = big_ops / (big_ms * 1e-3) / 1e12
+    big = groups
     t_roof = max(int_ops / (PEAK_INT8_TOPS * 1e12) + adapter_flops / (PEAK_BF16_TFLOPS * 1e12),
                  alg_bytes / (PEAK_HBM_GBS * 1e9))
     traffic = load_traffic(None)
@@ -487,9 +503,9 @@ def main():
                             "step left the caches); cold: the Infinity Cache flushed by reading 1 GiB before each "
                             "step"},
         "roofline": {
-            "scope": "dominant kernel only: the main GEMM's 128-token-tile launches (q, o, gate, up, down); the "
-                     "whole step is in layer_roofline",
-            "kernel": "gemm_w4_kernel<8, true> (int8 MFMA main GEMM, 128-token tiles, fused dequant/SE/RE epilogue)",
+            "scope": "dominant kernel only: the main GEMM's launches (one per group of linears that read the same "
+                     "input: q+k+v, o, gate+up, down); the whole step is in layer_roofline",
+            "kernel": "gemm_w4_group_kernel (int8 MFMA main GEMM, 128-token tiles, fused dequant/SE/RE epilogue)",
             "bound": "mfma",
             "achieved": round(achieved, 1),
             "peak": PEAK_INT8_TOPS,
@@ -510,7 +526,7 @@ def main():
                       "prologue_ms_per_step": round(ms_step - gemm_ms_step, 4),
                       "ms_per_step_composite_entry": round(ms_step_fwd, 4),
                       "wall_s_timed_region": round(wall, 3),
-                      "per_linear": per_linear},
+                      "per_group": per_group, "per_linear": per_linear},
     }
 
     peaks = measured_peaks(torch, libqe, dev)
@@ -964,6 +980,25 @@ def extras(torch, synth, qe, libqe, dev, peaks):
         ex = libqe.qe_build_experts(W_f, s_d, cfg.w_bits, cr, dep, labels, n_r, r_s, r_r, omegas, q_it, bws)
         ts.append(time.perf_counter() - t1)
         tr.append(t1 - t0)
+    # the default construction: covariance whitening over the same calibration tokens (passes over E
+    # and over a float32 copy of x; test matrices [1 + N_r][T][k])
+    om_c = torch.randn(1 + n_r, cfg.T, k_sv, device=dev, generator=torch.Generator(device=dev).manual_seed(2))
+    cws = torch.empty(libqe.qe_build_experts_cov_workspace_bytes(spec.d_out, spec.d_in, cfg.T, k_sv, 32),
+                      dtype=torch.uint8, device=dev)
+    tc = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        exc = libqe.qe_build_experts_cov(W_f, s_d, cfg.w_bits, x, dep, labels, n_r, r_s, r_r, om_c, q_it, cws)
+        tc.append(time.perf_counter() - t0)
+    del cws, om_c
+    out["expert_build_cov_internvl2_8b_down"] = {
+        "d_in": spec.d_in, "d_out": spec.d_out, "calibration_tokens": cfg.T, "r_shared": r_s, "n_routed": n_r,
+        "r_routed": r_r, "k_columns": k_sv, "power_iters": q_it, "build_ms": round(float(np.median(tc)) * 1e3, 1),
+        "passes_per_fit": {"E": 2 * q_it + 2, "X": 2 * q_it + 2},
+        "sigma_shared_top": [round(float(v), 3) for v in exc["sigma_s"][:4]],
+        "note": "covariance whitening (the default reading): the SE and each RE minimize the residual times the "
+                "calibration tokens; randomized subspace iteration on E X^T by passes over E and a float32 copy of x"}
     # router: targets on the calibration tokens from the residual after the SE, then the ridge fit
     E1 = torch.empty(spec.d_out, spec.d_in, device=dev)
     libqe.qe_quant_error(W_f, s_d, cfg.w_bits, E1)

@@ -252,6 +252,16 @@ int qe_group_prologue(const qe_linear* const* lins, int32_t n_lin, const void* x
 int qe_group_forward(const qe_linear* const* lins, int32_t n_lin, const void* x, int32_t x_dtype, int32_t T,
                      float* const* y, int32_t* const* expert_out, void* const* ws, const size_t* ws_bytes,
                      void* stream);
+/* The main products of a group (qe_wq_gemm for each linear, a_bits 6/8 only): when every linear
+ * takes the 128-token-tile path (float32 y, ranks <= 32, no K split) and the combined tile grid
+ * is at least 512 workgroups, one launch runs all of them, so narrow projections (k, v) share
+ * the grid of a wide one (q) instead of running a grid of their own; else one product after the
+ * other.  Identical results either way.  Arrays of n_lin entries as for qe_group_prologue (its
+ * outputs are this call's inputs); qe_group_forward ends with this step.
+ */
+int qe_group_gemm(const qe_linear* const* lins, int32_t n_lin, const int8_t* const* codes, const float* const* s_x,
+                  int32_t T, const uint16_t* const* u, const uint16_t* const* v, const int32_t* const* expert,
+                  const int32_t* const* perm, float* const* y, void* const* ws, const size_t* ws_bytes, void* stream);
 
 /* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): qe_linear_forward without a workspace argument.  It

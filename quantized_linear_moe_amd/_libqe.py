@@ -68,6 +68,7 @@ def _load():
         "qe_linear_forward": (ctypes.c_int, [LP, P, I, I, P, P, P, Z, P]),
         "qe_group_prologue": (ctypes.c_int, [P, I, P, I, I, P, P, P, P, P, P, P, P, P]),
         "qe_group_forward": (ctypes.c_int, [P, I, P, I, I, P, P, P, P, P]),
+        "qe_group_gemm": (ctypes.c_int, [P, I, P, P, I, P, P, P, P, P, P, P, P]),
         "qe_noalloc_scratch_bytes": (Z, []),
         "qe_linear_forward_noalloc": (ctypes.c_int, [LP, P, I, I, P, P, P]),
         "qe_colmean_abs": (ctypes.c_int, [P, I, I, I, P, P]),
@@ -114,7 +115,7 @@ EXPORTED = (
     "qe_status_string", "qe_last_hip_error", "qe_version", "qe_pack_weights", "qe_prepared_bytes", "qe_prepare",
     "qe_workspace_bytes", "qe_quant_act", "qe_route", "qe_adapter_inputs", "qe_wq_gemm", "qe_routed_lora",
     "qe_linear_prologue", "qe_linear_forward", "qe_noalloc_scratch_bytes", "qe_linear_forward_noalloc",
-    "qe_group_prologue", "qe_group_forward", "qe_colmean_abs", "qe_channel_topk", "qe_linear_cost",
+    "qe_group_prologue", "qe_group_forward", "qe_group_gemm", "qe_colmean_abs", "qe_channel_topk", "qe_linear_cost",
     "qe_probe_mfma_i8", "qe_probe_mfma_bf16", "qe_probe_copy", "qe_probe_read_sink_bytes", "qe_probe_read", "qe_partition_channels", "qe_cooccur_workspace_bytes",
     "qe_cooccur", "qe_cluster_channels", "qe_top2_workspace_bytes", "qe_linear_forward_top2", "qe_quant_error", "qe_channel_rms_workspace_bytes", "qe_channel_rms",
     "qe_sub_lowrank", "qe_lowrank_workspace_bytes", "qe_lowrank_fit", "qe_build_experts_workspace_bytes",
@@ -268,6 +269,16 @@ def qe_group_forward(lins, x, ys, expert_out, ws, stream=None):
     wsb = (ctypes.c_size_t * n)(*[w.numel() * w.element_size() for w in ws])
     _check(_lib.qe_group_forward(_lin_array(lins), n, _ptr(x), _dtype_code(x), x.shape[0], _ptr_array(ys), eo,
                                  _ptr_array(ws), wsb, _stream(stream)), "qe_group_forward")
+
+
+def qe_group_gemm(lins, codes, s_x, T, u, v, expert, ys, ws, perm=None, stream=None):
+    """Main products of linears that read the same input (lists, one entry per linear)."""
+    n = len(lins)
+    perm = perm if perm is not None else [None] * n
+    wsb = (ctypes.c_size_t * n)(*[w.numel() * w.element_size() for w in ws])
+    _check(_lib.qe_group_gemm(_lin_array(lins), n, _ptr_array(codes), _ptr_array(s_x), T, _ptr_array(u),
+                              _ptr_array(v), _ptr_array(expert), _ptr_array(perm), _ptr_array(ys), _ptr_array(ws), wsb,
+                              _stream(stream)), "qe_group_gemm")
 
 
 def qe_noalloc_scratch_bytes() -> int:

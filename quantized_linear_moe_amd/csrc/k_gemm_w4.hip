@@ -54,13 +54,17 @@ __device__ inline int a_swz(int row) { return (row >> 1) & 3; }
 // tile meets few experts in the epilogue), else token order.
 // kFast: adapter ranks <= 32 and no accumulator dump; the epilogue then reads every
 // operand from LDS (see below).
+// One workgroup's tile: block `bid` of `nblk` (the tile grid of this linear) and K split `ky` of
+// `nky`; gemm_w4_kernel runs one linear's grid, gemm_w4_group_kernel the grids of several
+// linears in one launch.
 template <int MB, bool kFast>
-__global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
+__device__ __attribute__((always_inline)) inline void gemm_w4_tile(
     const int8_t* __restrict__ codes, const float* __restrict__ s_x, const uint8_t* __restrict__ w_tiled,
     const float* __restrict__ w_scale, int T, int d_in, int d_out, const uint16_t* __restrict__ u,
     const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v, const int32_t* __restrict__ expert,
     const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, const int32_t* __restrict__ perm, float* __restrict__ y,
-    int32_t* __restrict__ acc_debug, int n_tm, int32_t* __restrict__ part, bool y_bf16) {
+    int32_t* __restrict__ acc_debug, int n_tm, int32_t* __restrict__ part, bool y_bf16, int bid, int nblk, int ky,
+    int nky) {
     constexpr int BM = MB * 16;
     constexpr int A_STAGE = BM * G_BK;            // bytes of codes per stage
     constexpr int B_STAGE = 4 * G_NBW * 512;      // 4 waves x 4 N blocks x 512 B of packed weights
@@ -80,8 +84,8 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     // order made all 8 fetch every weight tile); the result does not depend on the order.
     int tm, tn;
     {
-        const int G = gridDim.x, n_tn = G / n_tm;
-        int L = blockIdx.x;
+        const int G = nblk, n_tn = G / n_tm;
+        int L = bid;
         if ((G & 7) == 0) L = (L & 7) * (G >> 3) + (L >> 3);
         constexpr int GM = 8;
         const int per_group = GM * n_tn;
@@ -91,8 +95,8 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     }
     const int m0 = tm * BM;
     const int NB = d_out >> 4, KB = d_in / G_BK;
-    // K steps of this workgroup: all of them, or split gridDim.y of `part`'s partial sums
-    const int kb_beg = (int)((long)blockIdx.y * KB / gridDim.y), nk = (int)((long)(blockIdx.y + 1) * KB / gridDim.y) - kb_beg;
+    // K steps of this workgroup: all of them, or split nky of `part`'s partial sums
+    const int kb_beg = (int)((long)ky * KB / nky), nk = (int)((long)(ky + 1) * KB / nky) - kb_beg;
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
     const int nb0 = tn * (G_BN / 16) + wid * G_NBW;
     const int lr = lane & 15, lg = lane >> 4;
@@ -214,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     QE_WAIT_VMCNT(0);
 
     if (part) {  // split K: this workgroup's exact partial sums, in token order
-        int32_t* pt = part + (size_t)blockIdx.y * T * d_out;
+        int32_t* pt = part + (size_t)ky * T * d_out;
 #pragma unroll
         for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -469,6 +473,33 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
     }
 }
 
+template <int MB, bool kFast>
+__global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
+    const int8_t* __restrict__ codes, const float* __restrict__ s_x, const uint8_t* __restrict__ w_tiled,
+    const float* __restrict__ w_scale, int T, int d_in, int d_out, const uint16_t* __restrict__ u,
+    const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v, const int32_t* __restrict__ expert,
+    const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, const int32_t* __restrict__ perm, float* __restrict__ y,
+    int32_t* __restrict__ acc_debug, int n_tm, int32_t* __restrict__ part, bool y_bf16) {
+    gemm_w4_tile<MB, kFast>(codes, s_x, w_tiled, w_scale, T, d_in, d_out, u, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r,
+                            perm, y, acc_debug, n_tm, part, y_bf16, blockIdx.x, gridDim.x, blockIdx.y, gridDim.y);
+}
+
+// Several linears' 128-token-tile grids in one launch (linears that read the same input: the
+// narrow k / v projections then run with q's tiles instead of a grid of their own that leaves
+// compute units idle).  Block b belongs to linear l with begin[l] <= b < begin[l + 1]; every
+// linear's grid starts at a multiple of 8, so its tiles keep their XCD assignment.
+__global__ __launch_bounds__(256, 2) void gemm_w4_group_kernel(GemmGroup G) {
+    int l = 0;
+#pragma unroll
+    for (int i = 1; i < GG_MAX; ++i)
+        if (i < G.n && (int)blockIdx.x >= G.begin[i]) l = i;
+    const GemmLinear& a = G.lin[l];
+    const int nblk = (l + 1 < G.n ? G.begin[l + 1] : (int)gridDim.x) - G.begin[l];
+    gemm_w4_tile<8, true>(a.codes, a.s_x, a.w_tiled, a.w_scale, G.T, a.d_in, a.d_out, a.u, a.bt_s, a.rs_pad, a.v,
+                          a.expert, a.bt_r, a.rr_pad, a.n_r, a.perm, a.y, nullptr, (G.T + 127) / 128, nullptr, false,
+                          (int)blockIdx.x - G.begin[l], nblk, 0, 1);
+}
+
 // K splits of the main product (fast epilogue only): 1 unless the 64-token-tile grid
 // leaves CUs idle.  The 64-token tiles hold one workgroup per CU (their LDS ring), so the
 // split grid is kept to one round of 256 workgroups; each split keeps at least 8 K steps,
@@ -514,6 +545,26 @@ hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* 
     const bool routed = v != nullptr && expert != nullptr && bt_r != nullptr && rr_pad > 0 && n_r > 0;
     return launch_gemm_split_finish(part, ks, T, d_out, s_x, w_scale, rs_pad > 0 ? u : nullptr, bt_s, rs_pad,
                                     routed ? v : nullptr, routed ? expert : nullptr, n_r, bt_r, rr_pad, y, y_bf16, st);
+}
+
+// The grouped launch is for linears on the 128-token-tile fast path: float32 y, ranks <= 32,
+// no accumulator dump, every linear's tile grid a multiple of 8.  Returns hipErrorInvalidValue
+// (nothing launched) otherwise, and the caller then launches the linears one by one.
+hipError_t launch_gemm_w4_group(const GemmGroup& G0, hipStream_t st) {
+    GemmGroup G = G0;
+    if (G.n < 1 || G.n > GG_MAX || G.T <= 0) return hipErrorInvalidValue;
+    const int n_tm = (G.T + 127) / 128;
+    int begin = 0;
+    for (int l = 0; l < G.n; ++l) {
+        const GemmLinear& a = G.lin[l];
+        if (a.rs_pad > 32 || a.rr_pad > 32 || a.d_out % 16 || a.d_in % G_BK) return hipErrorInvalidValue;
+        const int tiles = n_tm * ((a.d_out + G_BN - 1) / G_BN);
+        if (tiles % 8) return hipErrorInvalidValue;
+        G.begin[l] = begin;
+        begin += tiles;
+    }
+    hipLaunchKernelGGL(gemm_w4_group_kernel, dim3(begin), dim3(256), 0, st, G);
+    return hipGetLastError();
 }
 
 }  // namespace qe

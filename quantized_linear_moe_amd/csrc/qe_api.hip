@@ -723,6 +723,80 @@ static int run_group_prologue(const qe_linear* const* lins, int n, const void* x
     return QE_OK;
 }
 
+// The main products of a group in one launch when every linear takes the 128-token-tile fast
+// path (A6/A8, float32 y, ranks <= 32) and the combined grid fills the chip; false: nothing was
+// launched and the caller runs the linears' products one by one.
+static bool try_group_gemm(const qe_linear* const* lins, int n, int T, int8_t* const* codes, float* const* s_x,
+                           uint16_t* const* u, uint16_t* const* v, int32_t* const* expert, int32_t* const* perm,
+                           float* const* y, hipStream_t s, int* status) {
+    *status = QE_OK;
+    if (n < 1 || n > GG_MAX || T <= kSkinnyMaxT) return false;
+    GemmGroup G{};
+    G.n = n;
+    G.T = T;
+    long tiles = 0;
+    for (int i = 0; i < n; ++i) {
+        const qe_linear* lin = lins[i];
+        if (lin->a_bits == 16 || lin->y_dtype != QE_F32) return false;
+        const PrepLayout P = prep_layout(lin);
+        const WsLayout W = ws_layout(lin, T);
+        if (W.gemm_ksplit > 1 || P.rs_pad > 32 || P.rr_pad > 32) return false;
+        GemmLinear& a = G.lin[i];
+        a.codes = codes[i];
+        a.s_x = s_x[i];
+        a.w_tiled = at<const uint8_t>(lin->prep, P.w_tiled);
+        a.w_scale = at<const float>(lin->prep, P.w_scale);
+        a.u = (P.rs_pad > 0 && u[i]) ? u[i] : nullptr;
+        a.bt_s = a.u ? at<const uint16_t>(lin->prep, P.bt_s) : nullptr;
+        const bool routed = P.rr_pad > 0 && v[i] && expert[i];
+        a.v = routed ? v[i] : nullptr;
+        a.expert = routed ? expert[i] : nullptr;
+        a.bt_r = routed ? at<const uint16_t>(lin->prep, P.bt_r) : nullptr;
+        a.perm = perm[i];
+        a.y = y[i];
+        a.d_in = lin->d_in;
+        a.d_out = lin->d_out;
+        a.rs_pad = a.u ? P.rs_pad : 0;
+        a.rr_pad = routed ? P.rr_pad : 0;
+        a.n_r = routed ? lin->n_routed : 0;
+        tiles += (long)((T + 127) / 128) * ((lin->d_out + 255) / 256);
+    }
+    if (tiles < 512) return false;  // too few 128-token tiles: the per-linear launches pick smaller ones
+    const hipError_t e = launch_gemm_w4_group(G, s);
+    if (e == hipErrorInvalidValue) return false;  // a grid not a multiple of 8: nothing launched
+    *status = e == hipSuccess ? QE_OK : hip_fail(e);
+    return true;
+}
+
+int qe_group_gemm(const qe_linear* const* lins, int32_t n_lin, const int8_t* const* codes, const float* const* s_x,
+                  int32_t T, const uint16_t* const* u, const uint16_t* const* v, const int32_t* const* expert,
+                  const int32_t* const* perm, float* const* y, void* const* ws, const size_t* ws_bytes, void* stream) {
+    QE_CHECK(lins && n_lin >= 1 && n_lin <= RG_MAX && codes && s_x && u && v && expert && perm && y && ws && ws_bytes,
+             QE_ERR_INVALID_ARG);
+    for (int i = 0; i < n_lin; ++i) {
+        QE_CHECK(lins[i] && lins[i]->a_bits != 16, QE_ERR_INVALID_ARG);
+        int st = validate_forward_common(lins[i], T, QE_BF16, nullptr, ws[i], ws_bytes[i]);
+        if (st) return st;
+        if (T == 0) continue;
+        QE_CHECK(codes[i] && s_x[i] && y[i], QE_ERR_INVALID_ARG);
+        QE_CHECK(aligned16(codes[i]) && aligned16(y[i]), QE_ERR_ALIGNMENT);
+        QE_CHECK((v[i] == nullptr) == (expert[i] == nullptr), QE_ERR_INVALID_ARG);
+    }
+    if (T == 0) return QE_OK;
+    hipStream_t s = S(stream);
+    int st = QE_OK;
+    if (try_group_gemm(lins, n_lin, T, const_cast<int8_t* const*>(codes), const_cast<float* const*>(s_x),
+                       const_cast<uint16_t* const*>(u), const_cast<uint16_t* const*>(v),
+                       const_cast<int32_t* const*>(expert), const_cast<int32_t* const*>(perm), y, s, &st))
+        return st;
+    for (int i = 0; i < n_lin; ++i) {
+        st = run_gemm(lins[i], codes[i], s_x[i], nullptr, QE_BF16, T, u[i], v[i], expert[i], perm[i], y[i], nullptr,
+                      ws[i], s);
+        if (st) return st;
+    }
+    return QE_OK;
+}
+
 int qe_group_prologue(const qe_linear* const* lins, int32_t n_lin, const void* x, int32_t x_dtype, int32_t T,
                       int8_t* const* codes, float* const* s_x, uint16_t* const* u, uint16_t* const* v,
                       int32_t* const* expert, int32_t* const* perm, void* const* ws, const size_t* ws_bytes,
@@ -783,6 +857,7 @@ int qe_group_forward(const qe_linear* const* lins, int32_t n_lin, const void* x,
     }
     st = run_group_prologue(lins, n_lin, x, x_dtype, T, codes, s_x, u, v, expert, perm, ws, s, keep);
     if (st) return st;
+    if (try_group_gemm(lins, n_lin, T, codes, s_x, u, v, expert, perm, y, s, &st)) return st;
     for (int i = 0; i < n_lin; ++i) {
         st = run_gemm(lins[i], codes[i], s_x[i], x, x_dtype, T, u[i], v[i], expert[i], perm[i], y[i], nullptr, ws[i], s);
         if (st) return st;

@@ -151,6 +151,28 @@ hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* 
                           const int32_t* perm, float* y, int32_t* acc_debug, int ksplit, int32_t* part,
                           bool y_bf16, hipStream_t st);
 int gemm_ksplit(int T, int d_in, int d_out);
+// several linears' main products (128-token tiles, fast epilogue, float32 y) in one launch
+constexpr int GG_MAX = 3;
+struct GemmLinear {
+    const int8_t* codes;
+    const float* s_x;
+    const uint8_t* w_tiled;
+    const float* w_scale;
+    const uint16_t* u;
+    const uint16_t* bt_s;
+    const uint16_t* v;
+    const int32_t* expert;
+    const uint16_t* bt_r;
+    const int32_t* perm;
+    float* y;
+    int d_in, d_out, rs_pad, rr_pad, n_r;
+};
+struct GemmGroup {
+    GemmLinear lin[GG_MAX];
+    int begin[GG_MAX];
+    int n, T;
+};
+hipError_t launch_gemm_w4_group(const GemmGroup& G, hipStream_t st);
 hipError_t launch_gemm_split_finish(const int32_t* part, int ksplit, int T, int d_out, const float* s_x,
                                     const float* w_scale, const uint16_t* u, const uint16_t* bt_s, int rs_pad,
                                     const uint16_t* v, const int32_t* expert, int n_r, const uint16_t* bt_r,

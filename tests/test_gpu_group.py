@@ -106,3 +106,33 @@ def test_group_rejects_mismatched_inputs(Q):
     with pytest.raises(L.QEError) as ex:
         L.qe_group_forward([l.lin for l in layers], x, ys, None, [lay.workspace(T) for lay in layers])
     assert ex.value.status == L.QE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("cfg_name,names,T", [("qwen2vl_72b", ("q", "k", "v"), None), ("qwen2vl_72b", ("down",), None),
+                                              ("qwen2vl_2b", ("q", "k", "v"), 300)])
+def test_group_gemm_matches_single_gemms(Q, cfg_name, names, T):
+    # one launch over the group's 128-token tiles against each linear's own launch (whose narrow
+    # linears take 64-token tiles): identical bits
+    L = Q.libqe
+    cfg = synth.get_config(cfg_name)
+    specs, params, layers = _layers(Q, cfg, names)
+    x = synth.gen_activations(cfg, specs[0].stream, T=T).to(DEV)
+    T = x.shape[0]
+    wss = [lay.workspace(T) for lay in layers]
+    bb = [dict(codes=torch.empty(T, sp.d_in, dtype=torch.int8, device=DEV), s_x=torch.empty(T, device=DEV),
+               u=torch.empty(T, 32, dtype=torch.bfloat16, device=DEV), v=torch.empty(T, 32, dtype=torch.bfloat16, device=DEV),
+               e=torch.empty(T, dtype=torch.int32, device=DEV), perm=torch.empty(T, dtype=torch.int32, device=DEV))
+          for sp in specs]
+    L.qe_group_prologue([l.lin for l in layers], x, [b["codes"] for b in bb], [b["s_x"] for b in bb],
+                        [b["u"] for b in bb], [b["v"] for b in bb], [b["e"] for b in bb], wss,
+                        perm=[b["perm"] for b in bb])
+    ys1 = [torch.empty(T, sp.d_out, device=DEV) for sp in specs]
+    for lay, b, y, w in zip(layers, bb, ys1, wss):
+        L.qe_wq_gemm(lay.lin, b["codes"], b["s_x"], None, T, b["u"], b["v"], b["e"], y, None, w, perm=b["perm"])
+    ys2 = [torch.full((T, sp.d_out), float("nan"), device=DEV) for sp in specs]
+    L.qe_group_gemm([l.lin for l in layers], [b["codes"] for b in bb], [b["s_x"] for b in bb], T,
+                    [b["u"] for b in bb], [b["v"] for b in bb], [b["e"] for b in bb], ys2, wss,
+                    perm=[b["perm"] for b in bb])
+    torch.cuda.synchronize()
+    for name, a, b in zip(names, ys1, ys2):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"{name}: y differs"
