@@ -113,11 +113,16 @@ const char* qe_version(void);
 int qe_pack_weights(const float* W_f_host, const float* s_host, int32_t d_out, int32_t d_in,
                     int32_t w_bits, void* packed_host, float* w_scale_host);
 
-/* Bytes of the prepared parameter buffer for this linear (lin->prep ignored). */
+/* Bytes of the prepared parameter buffer for this linear (lin->prep ignored).  A sizing call
+ * for qe_prepare's load-time layout; no step of the method. */
 size_t qe_prepared_bytes(const qe_linear* lin);
 
 /* Lay out one linear's parameters for the kernels (load-time step, enqueued on
- * `stream`).  All inputs are device pointers in the canonical layouts:
+ * `stream`): the quantized weights of the listing's W4/W3 settings (thelatestinai.com listing,
+ * Tables 1-2) with the smoothing the DeepRead summary's "Method" applies before activation
+ * quantization, the shared and routed adapters and the router of the same section.  A layout
+ * change only; the values are those of the canonical inputs.  All inputs are device pointers in
+ * the canonical layouts:
  *   w_packed  W4/W3 packed codes as produced by qe_pack_weights
  *   w_scale   float32 [d_out]
  *   smooth    float32 [d_in], entries > 0, or NULL (identity); must be NULL when a_bits == 16
@@ -132,7 +137,8 @@ int qe_prepare(const qe_linear* lin, const void* w_packed, const float* w_scale,
                const uint16_t* R, void* prep, void* stream);
 
 /* Workspace bytes needed by qe_linear_forward / qe_route / qe_adapter_inputs /
- * qe_wq_gemm / qe_routed_lora for T tokens (the largest of them). */
+ * qe_wq_gemm / qe_routed_lora for T tokens (the largest of them).  A sizing call; no step of
+ * the method. */
 size_t qe_workspace_bytes(const qe_linear* lin, int32_t T);
 
 /* ------------------------------------------------------------ hot-path steps -- */
@@ -252,7 +258,9 @@ int qe_group_prologue(const qe_linear* const* lins, int32_t n_lin, const void* x
 int qe_group_forward(const qe_linear* const* lins, int32_t n_lin, const void* x, int32_t x_dtype, int32_t T,
                      float* const* y, int32_t* const* expert_out, void* const* ws, const size_t* ws_bytes,
                      void* stream);
-/* The main products of a group (qe_wq_gemm for each linear, a_bits 6/8 only): when every linear
+/* The main products of a group (qe_wq_gemm for each linear, a_bits 6/8 only; the quantized
+ * product with the fused adapter terms of the listing's Table 7 and the DeepRead summary's
+ * "Method", as for qe_wq_gemm): when every linear
  * takes the 128-token-tile path (float32 y, ranks <= 32, no K split) and the combined tile grid
  * is at least 512 workgroups, one launch runs all of them, so narrow projections (k, v) share
  * the grid of a wide one (q) instead of running a grid of their own; else one product after the
@@ -320,7 +328,9 @@ int qe_channel_topk(const void* x, int32_t x_dtype, const float* w, int32_t T, i
 int qe_partition_channels(const uint32_t* hist, int32_t d_in, int32_t k, int32_t n_r, int32_t* indep,
                           int32_t* dep, int32_t* slot);
 
-/* qe_cooccur (device): cooc[i][j] += #{t : topk[t] holds both dep[i] and dep[j]}, i.e.
+/* qe_cooccur (device; DeepRead summary, "Method", and the PaperDaily post "西交大提出Quant
+ * Experts：token级量化补偿", section "核心设计": the co-occurrence matrix of the token-dependent
+ * channels): cooc[i][j] += #{t : topk[t] holds both dep[i] and dep[j]}, i.e.
  *   cooc += O^T O with O[t][i] = 1 when token t selected the i-th token-dependent channel.
  *   The diagonal counts each channel's selections.  cooc is ACCUMULATED over calls (the
  *   caller zeroes it), so a calibration set can be fed in batches of tokens.
@@ -338,7 +348,9 @@ size_t qe_cooccur_workspace_bytes(int32_t T, int32_t n_dep);
 int qe_cooccur(const int32_t* topk, int32_t T, int32_t k, const int32_t* slot, int32_t d_in, int32_t n_dep,
                uint32_t* cooc, void* ws, size_t ws_bytes, void* stream);
 
-/* qe_cluster_channels (host, synchronous): from the co-occurrence counts of n_dep
+/* qe_cluster_channels (host, synchronous; DeepRead summary, "Method": NPMI similarity, spectral
+ *   clustering of the normalized Laplacian and K-Means into N_r clusters; PaperDaily post, section
+ *   "核心设计": p(i), p(i,j), the threshold): from the co-occurrence counts of n_dep
  *   token-dependent channels over T tokens,
  *     NPMI(i,j) = ln(p_ij / (p_i p_j)) / -ln p_ij,  p_ij = cooc[i][j] / T, p_i = cooc[i][i] / T,
  *     with -1 where p_ij = 0 and +1 where p_ij = 1;
