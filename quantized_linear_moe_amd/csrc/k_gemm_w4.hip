@@ -177,20 +177,96 @@ __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
 #pragma unroll
         for (int j = 0; j < G_NBW; ++j) acc[m][j] = v4i{0, 0, 0, 0};
 
+    // Operands of the fast epilogue (see below): the u and v rows of the tile, this wave's
+    // B_s fragments and the B_e fragments of up to NSLOT routed experts present, in the ring.
+    // 128-token tiles with at least NS K steps load them during their last NS-1 K steps,
+    // whose ring slots take no further K step: slot nk%NS the u and v rows, slot (nk+1)%NS
+    // the B_s fragments, slot (nk+2)%NS the first expert's B_e fragments (a second expert
+    // goes to the last K step's slot after the loop).  Other tiles load them all after the
+    // loop at fixed places.  Each tail step issues exactly OPS copies, as a K step does, so
+    // the ring's vmcnt waits keep their meaning (an operand the tile does not use is
+    // replaced by a copy of a valid code row that is never read).
+    const bool have_se = u != nullptr && bt_s != nullptr && rs_pad > 0;
+    constexpr int NSLOT = (NS * STAGE - 2 * MB * 1024 - 16384) / 16384;  // experts per round
+    static_assert(NSLOT >= 1, "LDS ring too small for the epilogue operands");
+    const bool pre = kFast && MB == 8 && part == nullptr && nk >= NS;
+    static_assert(MB != 8 || (2 * (MB / 4) == OPS && G_NBW == OPS), "tail steps must issue OPS copies");
+    int nbj[G_NBW];  // fragment sources; blocks past d_out repeat a valid block (never stored)
+#pragma unroll
+    for (int j = 0; j < G_NBW; ++j) nbj[j] = nb_ok[j] ? nb0 + j : 0;
+    int u_off = 0, bs_off = 2 * MB * 1024, br_off[NSLOT];
+#pragma unroll
+    for (int sl = 0; sl < NSLOT; ++sl) br_off[sl] = bs_off + 16384 * (sl + 1);
+    if (pre) {
+        u_off = (nk % NS) * STAGE;
+        bs_off = ((nk + 1) % NS) * STAGE;
+        br_off[0] = ((nk + 2) % NS) * STAGE;
+        br_off[NSLOT - 1] = ((nk + 3) % NS) * STAGE;
+    }
+    const int v_off = u_off + MB * 1024;
+    int es[NSLOT];  // experts of the current round (-1: none), taken in index order from `pend`
+    uint32_t pend = present;
+    auto pick_experts = [&]() {
+#pragma unroll
+        for (int sl = 0; sl < NSLOT; ++sl) {
+            es[sl] = -1;
+            if (pend) {
+                es[sl] = __builtin_ctz(pend);
+                pend &= pend - 1;
+            }
+        }
+    };
+    pick_experts();
+    float sw[G_NBW];
+#pragma unroll
+    for (int j = 0; j < G_NBW; ++j) sw[j] = nb_ok[j] ? w_scale[(nb0 + j) * 16 + lr] : 0.0f;
+    auto prefetch_epilogue = [&](int part_j) {  // tail step part_j = 0, 1, 2 (pre only)
+        const int8_t* dummy = a_src[0];
+        if (part_j == 0) {
+#pragma unroll
+            for (int p = 0; p < MB / 4; ++p) {
+                const int m = wid + 4 * p;
+                const void* src = have_se ? (const void*)(u + (size_t)s_tok[m * 16 + lr] * rs_pad + lg * 8) : dummy;
+                dma16(src, lds0 + u_off + m * 1024);
+            }
+#pragma unroll
+            for (int p = 0; p < MB / 4; ++p) {
+                const int m = wid + 4 * p;
+                const void* src = es[0] >= 0 ? (const void*)(v + (size_t)s_tok[m * 16 + lr] * rr_pad + lg * 8) : dummy;
+                dma16(src, lds0 + v_off + m * 1024);
+            }
+        } else if (part_j == 1) {
+#pragma unroll
+            for (int j = 0; j < G_NBW; ++j) {
+                const void* src = have_se ? (const void*)(bt_s + (size_t)(nbj[j] * 16 + lr) * rs_pad + lg * 8) : dummy;
+                dma16(src, lds0 + bs_off + (wid * G_NBW + j) * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < G_NBW; ++j) {
+                const void* src = es[0] >= 0 ? (const void*)(bt_r + ((size_t)es[0] * d_out + nbj[j] * 16 + lr) * rr_pad + lg * 8)
+                                             : dummy;
+                dma16(src, lds0 + br_off[0] + (wid * G_NBW + j) * 1024);
+            }
+        }
+    };
+
     // prologue: three stages in flight, then wait for the first
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st) issue(st, min(st, nk - 1));
     QE_WAIT_VMCNT_LDS((NS - 2) * OPS);
     QE_WG_BARRIER();
 
-    for (int kb = 0; kb < nk; ++kb) {
-        // refill the slot consumed in the previous step (past the end: a harmless repeat)
-        issue((kb + NS - 1) % NS, min(kb + NS - 1, nk - 1));
+    auto k_step = [&](int kb) {  // the MFMAs of K step kb (ring slot kb % NS)
         const uint8_t* st = smem + (kb % NS) * STAGE;
         v2u bp[G_NBW];
 #pragma unroll
         for (int j = 0; j < G_NBW; ++j)
             bp[j] = *reinterpret_cast<const v2u*>(st + A_STAGE + wid * 2048 + j * 512 + lane * 8);
+        // the weight fragments are requested first: their unpacking then overlaps the
+        // activation reads, and the first MFMAs wait for one activation row only (left to
+        // itself the compiler may issue them last, and every MFMA then waits for all reads)
+        __builtin_amdgcn_sched_barrier(0);
         v4i a[MB];
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
@@ -205,7 +281,7 @@ __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
 #pragma unroll
             for (int j = 0; j < G_NBW; ++j)
                 acc[m][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[m], bop[j], acc[m][j], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, MB + G_NBW, 0);  // LDS reads first
+        __builtin_amdgcn_sched_group_barrier(0x100, MB, 0);           // activation reads first
         __builtin_amdgcn_sched_group_barrier(0x002, 3 * G_NBW, 0);    // weight unpack
         __builtin_amdgcn_sched_group_barrier(0x008, MB * G_NBW, 0);   // then the MFMAs
         // nothing of this step may move below the barrier: the slot read here is the
@@ -214,6 +290,19 @@ __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
         __builtin_amdgcn_sched_barrier(0);
         QE_WAIT_VMCNT_LDS((NS - 2) * OPS);
         QE_WG_BARRIER();
+    };
+    // each step first refills the slot consumed in the previous one; past the end that is a
+    // harmless repeat, or (pre) the epilogue's operands, in a loop of its own so that their
+    // addresses are not held in registers through the main loop
+    const int nk_main = pre ? nk - (NS - 1) : nk;
+    int kb = 0;
+    for (; kb < nk_main; ++kb) {
+        issue((kb + NS - 1) % NS, min(kb + NS - 1, nk - 1));
+        k_step(kb);
+    }
+    for (; kb < nk; ++kb) {
+        prefetch_epilogue(kb + NS - 1 - nk);
+        k_step(kb);
     }
     QE_WAIT_VMCNT(0);
 
@@ -237,60 +326,49 @@ __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
     // lane holds column (nb*16 + lr) and rows (m*16 + lg*4 + r) of each block; the A
     // operands of the adapter MFMAs are rows (m*16 + lr).
     //
-    // Common case (kFast): the ring is free now, so the u and v rows of the tile, this
-    // wave's B_s fragments and the B_e fragments of up to NSLOT experts present arrive by
-    // DMA in one burst; each 16-row block is then dequantized, corrected and stored with
-    // every operand read from LDS.  A tile with more experts than the ring holds adds the
-    // rest in further rounds, reading back the y rows it stored.
-    const bool have_se = u != nullptr && bt_s != nullptr && rs_pad > 0;
+    // Common case (kFast): every operand is read from LDS (loaded into the ring as set out
+    // above); each 16-row block is dequantized, corrected and stored.  A tile with more
+    // experts than one round holds adds the rest in further rounds, reading back the y rows
+    // it stored.
     if constexpr (kFast) {
-        constexpr int U_OFF = 0, V_OFF = MB * 1024, BS_OFF = 2 * MB * 1024, BR_OFF = BS_OFF + 16384;
-        constexpr int NSLOT = (NS * STAGE - BR_OFF) / 16384;  // experts per round
-        static_assert(NSLOT >= 1, "LDS ring too small for the epilogue operands");
         QE_WAIT_VMCNT_LDS(0);
-        QE_WG_BARRIER();  // every wave is done with the ring
-        int nbj[G_NBW];   // fragment sources; blocks past d_out repeat a valid block (never stored)
-#pragma unroll
-        for (int j = 0; j < G_NBW; ++j) nbj[j] = nb_ok[j] ? nb0 + j : 0;
-        if (have_se) {
-#pragma unroll
-            for (int p = 0; p < MB / 4; ++p) {
-                const int m = wid + 4 * p;
-                dma16(u + (size_t)s_tok[m * 16 + lr] * rs_pad + lg * 8, lds0 + U_OFF + m * 1024);
-            }
-#pragma unroll
-            for (int j = 0; j < G_NBW; ++j)
-                dma16(bt_s + (size_t)(nbj[j] * 16 + lr) * rs_pad + lg * 8, lds0 + BS_OFF + (wid * G_NBW + j) * 1024);
-        }
-        if (present) {
-#pragma unroll
-            for (int p = 0; p < MB / 4; ++p) {
-                const int m = wid + 4 * p;
-                dma16(v + (size_t)s_tok[m * 16 + lr] * rr_pad + lg * 8, lds0 + V_OFF + m * 1024);
-            }
-        }
-        int es[NSLOT];
-        uint32_t pend = present;
-        auto stage_experts = [&]() {
+        QE_WG_BARRIER();  // every wave is done with the ring; the tail's copies have landed
+        auto stage_experts = [&](int first) {
 #pragma unroll
             for (int sl = 0; sl < NSLOT; ++sl) {
-                es[sl] = -1;
-                if (pend) {
-                    es[sl] = __builtin_ctz(pend);
-                    pend &= pend - 1;
+                if (sl < first || es[sl] < 0) continue;  // uniform
 #pragma unroll
-                    for (int j = 0; j < G_NBW; ++j)
-                        dma16(bt_r + ((size_t)es[sl] * d_out + nbj[j] * 16 + lr) * rr_pad + lg * 8,
-                              lds0 + BR_OFF + sl * 16384 + (wid * G_NBW + j) * 1024);
-                }
+                for (int j = 0; j < G_NBW; ++j)
+                    dma16(bt_r + ((size_t)es[sl] * d_out + nbj[j] * 16 + lr) * rr_pad + lg * 8,
+                          lds0 + br_off[sl] + (wid * G_NBW + j) * 1024);
             }
         };
-        stage_experts();
-        float sw[G_NBW];
+        if (!pre) {
+            if (have_se) {
 #pragma unroll
-        for (int j = 0; j < G_NBW; ++j) sw[j] = nb_ok[j] ? w_scale[(nb0 + j) * 16 + lr] : 0.0f;
-        QE_WAIT_VMCNT_LDS(0);
-        QE_WG_BARRIER();
+                for (int p = 0; p < MB / 4; ++p) {
+                    const int m = wid + 4 * p;
+                    dma16(u + (size_t)s_tok[m * 16 + lr] * rs_pad + lg * 8, lds0 + u_off + m * 1024);
+                }
+#pragma unroll
+                for (int j = 0; j < G_NBW; ++j)
+                    dma16(bt_s + (size_t)(nbj[j] * 16 + lr) * rs_pad + lg * 8, lds0 + bs_off + (wid * G_NBW + j) * 1024);
+            }
+            if (present) {
+#pragma unroll
+                for (int p = 0; p < MB / 4; ++p) {
+                    const int m = wid + 4 * p;
+                    dma16(v + (size_t)s_tok[m * 16 + lr] * rr_pad + lg * 8, lds0 + v_off + m * 1024);
+                }
+            }
+            stage_experts(0);
+        } else {
+            stage_experts(1);  // the first expert's fragments came with the tail
+        }
+        if (!pre || (NSLOT > 1 && es[1] >= 0)) {  // uniform
+            QE_WAIT_VMCNT_LDS(0);
+            QE_WG_BARRIER();
+        }
         auto routed = [&](int m, v4f (&yv)[G_NBW]) {  // y += (v masked to expert e's rows) . B_e
             const int exm = s_ex[m * 16 + lr];
 #pragma unroll
@@ -298,15 +376,15 @@ __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
                 if (es[sl] < 0) break;  // uniform
                 const bool mine = exm == es[sl];
                 if (__ballot(mine) == 0) continue;  // no row of this block uses the expert
-                const v8bf va = mine ? *reinterpret_cast<const v8bf*>(smem + V_OFF + m * 1024 + lane * 16) : v8bf{};
-                const uint8_t* lbr = smem + BR_OFF + sl * 16384 + wid * G_NBW * 1024 + lane * 16;
+                const v8bf va = mine ? *reinterpret_cast<const v8bf*>(smem + v_off + m * 1024 + lane * 16) : v8bf{};
+                const uint8_t* lbr = smem + br_off[sl] + wid * G_NBW * 1024 + lane * 16;
 #pragma unroll
                 for (int j = 0; j < G_NBW; ++j)
                     yv[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, *reinterpret_cast<const v8bf*>(lbr + j * 1024),
                                                                     yv[j], 0, 0, 0);
             }
         };
-        const uint8_t* lbs = smem + BS_OFF + wid * G_NBW * 1024 + lane * 16;
+        const uint8_t* lbs = smem + bs_off + wid * G_NBW * 1024 + lane * 16;
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
             const v4f sx = *reinterpret_cast<const v4f*>(&s_sx[m * 16 + lg * 4]);
@@ -316,7 +394,7 @@ __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) yv[j][r] = (float)(acc[m][j][r] >> 4) * sx[r] * sw[j];
             if (have_se) {  // y += u . B_s
-                const v8bf ua = *reinterpret_cast<const v8bf*>(smem + U_OFF + m * 1024 + lane * 16);
+                const v8bf ua = *reinterpret_cast<const v8bf*>(smem + u_off + m * 1024 + lane * 16);
 #pragma unroll
                 for (int j = 0; j < G_NBW; ++j)
                     yv[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, *reinterpret_cast<const v8bf*>(lbs + j * 1024),
@@ -337,7 +415,8 @@ __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
         while (pend) {  // more experts than one round holds (uniform; rare)
             QE_WAIT_VMCNT_LDS(0);
             QE_WG_BARRIER();
-            stage_experts();
+            pick_experts();
+            stage_experts(0);
             QE_WAIT_VMCNT_LDS(0);
             QE_WG_BARRIER();
             for (int m = 0; m < MB; ++m) {
@@ -377,10 +456,6 @@ __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
             bs[j] = nb_ok[j] ? *reinterpret_cast<const v8bf*>(bt_s + (size_t)((nb0 + j) * 16 + lr) * rs_pad + lg * 8)
                              : v8bf{};
     }
-    float sw[G_NBW];
-#pragma unroll
-    for (int j = 0; j < G_NBW; ++j) sw[j] = nb_ok[j] ? w_scale[(nb0 + j) * 16 + lr] : 0.0f;
-
     v4f yv[MB][G_NBW];
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
