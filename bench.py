@@ -813,7 +813,7 @@ def sweeps(torch, synth, qe, libqe, dev, reps=10):
         y = torch.empty(base.T, spec.d_out, dtype=torch.float32, device=dev)
         t = med_us(lambda: libqe.qe_linear_forward(layer.lin, x, y, None, ws))
         row = {"n_routed": n_r, "us": round(t, 2), "tokens_per_s": round(base.T / t * 1e6, 1)}
-        if n_r == 8:  # top-2 routing on the same linear: the second expert through the grouped path
+        if n_r == 8:  # top-2 routing on the same linear: both routed corrections in the GEMM epilogue
             ws2 = torch.empty(libqe.qe_top2_workspace_bytes(layer.lin, base.T), dtype=torch.uint8, device=dev)
             t2 = med_us(lambda: libqe.qe_linear_forward_top2(layer.lin, x, y, None, None, ws2))
             row.update(top2_us=round(t2, 2), top2_tokens_per_s=round(base.T / t2 * 1e6, 1))

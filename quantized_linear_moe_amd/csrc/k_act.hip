@@ -326,7 +326,8 @@ __global__ __launch_bounds__(1024) void xproj_finish_kernel(const float* __restr
                                                             int n_r, int r_r, int rr_pad, int router_col,
                                                             const int32_t* __restrict__ expert_in,
                                                             float* __restrict__ scores, int32_t* __restrict__ expert_out,
-                                                            uint16_t* __restrict__ u, uint16_t* __restrict__ v) {
+                                                            uint16_t* __restrict__ u, uint16_t* __restrict__ v,
+                                                            int32_t* __restrict__ expert2_out) {
     extern __shared__ float sums[];  // [nq][ncols_pad]: partial sums over split ranges, then the total in row 0
     __shared__ int s_e;
     const int t = blockIdx.x;
@@ -382,6 +383,16 @@ __global__ __launch_bounds__(1024) void xproj_finish_kernel(const float* __restr
                     e = j;
                 }
             if (expert_out) expert_out[t] = e;
+            if (expert2_out) {  // top-2 routing: the best of the others, lowest index on ties
+                int e2 = -1;
+                float b2 = 0.0f;
+                for (int j = 0; j < n_r; ++j)
+                    if (j != e && (e2 < 0 || sums[router_col + j] < b2)) {
+                        b2 = sums[router_col + j];
+                        e2 = j;
+                    }
+                expert2_out[t] = e2;
+            }
         } else if (expert_in) {
             e = min(max(expert_in[t], 0), max(n_r - 1, 0));
         }
@@ -403,8 +414,9 @@ __global__ __launch_bounds__(1024) void xproj_finish_kernel(const float* __restr
 hipError_t launch_xproj_finish(const float* part, int ksplit, int T, int ncols_pad, int col0, int se_col, int r_s,
                                int rs_pad, int re_col, int n_r, int r_r, int rr_pad, int router_col,
                                const int32_t* expert_in, float* scores, int32_t* expert_out, uint16_t* u,
-                               uint16_t* v, hipStream_t st) {
+                               uint16_t* v, hipStream_t st, int32_t* expert2_out) {
     if (T <= 0) return hipSuccess;
+    if (expert2_out && (router_col < 0 || n_r < 2)) return hipErrorInvalidValue;
     // columns are relative to the projected block that starts at col0
     auto rel = [&](int c) { return c < 0 ? -1 : c - col0; };
     // a call that reads only a few columns (router alone, or one known expert) takes one wave
@@ -413,7 +425,7 @@ hipError_t launch_xproj_finish(const float* part, int ksplit, int T, int ncols_p
     const int nq = few ? 1 : 4;
     hipLaunchKernelGGL(xproj_finish_kernel, dim3(T), dim3(256 * nq), nq * (size_t)ncols_pad * sizeof(float), st, part, ksplit, T,
                        ncols_pad, rel(se_col), r_s, rs_pad, rel(re_col), n_r, r_r, rr_pad, rel(router_col), expert_in,
-                       scores, expert_out, u, v);
+                       scores, expert_out, u, v, expert2_out);
     return hipGetLastError();
 }
 
@@ -812,7 +824,8 @@ __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restri
                                                            const float* __restrict__ amax_part, int ksplit, int T,
                                                            int ncols, int r_s, int rs_pad, int router_col, int n_r,
                                                            int qmax, int32_t* __restrict__ expert,
-                                                           uint16_t* __restrict__ u, float* __restrict__ s_x) {
+                                                           uint16_t* __restrict__ u, float* __restrict__ s_x,
+                                                           int32_t* __restrict__ expert2) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (t >= T) return;
     // columns lane and lane + 64 (ncols <= 80), and the activation maxima: the partials of up to
@@ -860,6 +873,28 @@ __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restri
             }
         }
         if (lane == 0) expert[t] = bi;
+        if (expert2) {  // top-2 routing: the best of the other experts, lowest index on ties
+            float b2 = __builtin_inff();
+            int i2 = 1 << 30;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int c = lane + 64 * j;
+                if (c >= router_col && c < router_col + n_r && c - router_col != bi && (sum[j] < b2 || i2 == 1 << 30)) {
+                    b2 = sum[j];
+                    i2 = c - router_col;
+                }
+            }
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1) {
+                const float ob = __shfl_xor(b2, off, 64);
+                const int oi = __shfl_xor(i2, off, 64);
+                if (ob < b2 || (ob == b2 && oi < i2)) {
+                    b2 = ob;
+                    i2 = oi;
+                }
+            }
+            if (lane == 0) expert2[t] = i2;
+        }
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -872,10 +907,11 @@ __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restri
 
 hipError_t launch_route_finish(const float* part, const float* amax_part, int ksplit, int T, int ncols, int r_s,
                                int rs_pad, int router_col, int n_r, int a_bits, int32_t* expert, uint16_t* u,
-                               float* s_x, hipStream_t st) {
+                               float* s_x, hipStream_t st, int32_t* expert2) {
     if (T <= 0) return hipSuccess;
+    if (expert2 && (!expert || router_col < 0 || n_r < 2)) return hipErrorInvalidValue;
     hipLaunchKernelGGL(route_finish_kernel, dim3((T + 3) / 4), dim3(256), 0, st, part, amax_part, ksplit, T, ncols,
-                       r_s, rs_pad, router_col, n_r, (1 << (a_bits - 1)) - 1, expert, u, s_x);
+                       r_s, rs_pad, router_col, n_r, (1 << (a_bits - 1)) - 1, expert, u, s_x, expert2);
     return hipGetLastError();
 }
 

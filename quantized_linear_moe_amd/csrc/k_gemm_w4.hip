@@ -57,14 +57,17 @@ __device__ inline int a_swz(int row) { return (row >> 1) & 3; }
 // One workgroup's tile: block `bid` of `nblk` (the tile grid of this linear) and K split `ky` of
 // `nky`; gemm_w4_kernel runs one linear's grid, gemm_w4_group_kernel the grids of several
 // linears in one launch.
-template <int MB, bool kFast>
+// kTop2: top-2 routing; every token also takes the correction of a second expert
+// (expert2, with its adapter input v2), added in the same epilogue rounds.
+template <int MB, bool kFast, bool kTop2 = false>
 __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
     const int8_t* __restrict__ codes, const float* __restrict__ s_x, const uint8_t* __restrict__ w_tiled,
     const float* __restrict__ w_scale, int T, int d_in, int d_out, const uint16_t* __restrict__ u,
     const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v, const int32_t* __restrict__ expert,
     const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, const int32_t* __restrict__ perm, float* __restrict__ y,
     int32_t* __restrict__ acc_debug, int n_tm, int32_t* __restrict__ part, bool y_bf16, int bid, int nblk, int ky,
-    int nky) {
+    int nky, const uint16_t* __restrict__ v2 = nullptr, const int32_t* __restrict__ expert2 = nullptr) {
+    static_assert(!kTop2 || (kFast && MB == 8), "top-2 routing takes the fast epilogue of 128-token tiles");
     constexpr int BM = MB * 16;
     constexpr int A_STAGE = BM * G_BK;            // bytes of codes per stage
     constexpr int B_STAGE = 4 * G_NBW * 512;      // 4 waves x 4 N blocks x 512 B of packed weights
@@ -74,7 +77,9 @@ __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
     // ring depth: 64-token tiles run few workgroups per CU with short K steps, so their loads
     // run further ahead to cover the memory latency
     constexpr int NS = MB == 4 ? 8 : G_NS;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+    // top-2: the second expert's v rows after the ring
+    constexpr int V2_OFF = NS * STAGE;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE + (kTop2 ? MB * 1024 : 0)];
 
     // Tile order.  Workgroups are handed to the 8 XCDs in turn (block b to XCD b % 8), each
     // XCD with its own L2: the block index is renumbered so that every XCD walks a contiguous
@@ -112,11 +117,12 @@ __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
     __shared__ int s_tok[BM];
     __shared__ __attribute__((aligned(16))) float s_sx[BM];
     __shared__ int s_ex[BM];
+    __shared__ int s_ex2[kTop2 ? BM : 1];
     const bool routed = v != nullptr && expert != nullptr && bt_r != nullptr && rr_pad > 0 && n_r > 0;
-    uint32_t present = 0;
+    uint32_t present = 0;  // experts of the tile's rows (first and, top-2, second)
     {
         constexpr int RPL = (BM + 63) / 64;  // rows per lane
-        int tk[RPL], ex[RPL];
+        int tk[RPL], ex[RPL], ex2[RPL];
         float sx[RPL];
 #pragma unroll
         for (int i = 0; i < RPL; ++i) tk[i] = perm ? perm[min(m0 + 64 * i + lane, T - 1)] : min(m0 + 64 * i + lane, T - 1);
@@ -124,22 +130,34 @@ __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
         for (int i = 0; i < RPL; ++i) {
             sx[i] = s_x[tk[i]];
             ex[i] = routed ? expert[tk[i]] : 0;
+            if constexpr (kTop2) ex2[i] = routed ? expert2[tk[i]] : 0;
         }
 #pragma unroll
         for (int i = 0; i < RPL; ++i) {
             const int r = 64 * i + lane;
             const int e = (routed && m0 + r < T) ? min(max(ex[i], 0), n_r - 1) : -1;
+            const int e2 = (kTop2 && routed && m0 + r < T) ? min(max(ex2[i], 0), n_r - 1) : -1;
             if (routed)
                 for (int q = 0; q < n_r; ++q)
-                    if (__ballot(e == q)) present |= 1u << q;
+                    if (__ballot(e == q || e2 == q)) present |= 1u << q;
             if (wid == 0) {
                 s_tok[r] = tk[i];
                 s_sx[r] = sx[i];
                 s_ex[r] = e;
+                if constexpr (kTop2) s_ex2[r] = e2;
             }
         }
     }
     __syncthreads();
+    if constexpr (kTop2) {  // the second expert's v rows, into LDS past the ring (landed by the ring's first wait)
+        if (present) {
+#pragma unroll
+            for (int p = 0; p < MB / 4; ++p) {
+                const int m = wid + 4 * p;
+                dma16(v2 + (size_t)s_tok[m * 16 + lr] * rr_pad + lg * 8, lds0 + V2_OFF + m * 1024);
+            }
+        }
+    }
 
 
     // DMA sources.  A: copy q = wid + 4p covers tile rows 16q..16q+15; lane i fetches the
@@ -371,12 +389,16 @@ __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
         }
         auto routed = [&](int m, v4f (&yv)[G_NBW]) {  // y += (v masked to expert e's rows) . B_e
             const int exm = s_ex[m * 16 + lr];
+            const int exm2 = kTop2 ? s_ex2[m * 16 + lr] : -1;
 #pragma unroll
             for (int sl = 0; sl < NSLOT; ++sl) {
                 if (es[sl] < 0) break;  // uniform
                 const bool mine = exm == es[sl];
-                if (__ballot(mine) == 0) continue;  // no row of this block uses the expert
-                const v8bf va = mine ? *reinterpret_cast<const v8bf*>(smem + v_off + m * 1024 + lane * 16) : v8bf{};
+                const bool mine2 = kTop2 && exm2 == es[sl];  // top-2: rows whose second expert it is
+                if (__ballot(mine || mine2) == 0) continue;  // no row of this block uses the expert
+                const v8bf va = mine    ? *reinterpret_cast<const v8bf*>(smem + v_off + m * 1024 + lane * 16)
+                                : mine2 ? *reinterpret_cast<const v8bf*>(smem + V2_OFF + m * 1024 + lane * 16)
+                                        : v8bf{};
                 const uint8_t* lbr = smem + br_off[sl] + wid * G_NBW * 1024 + lane * 16;
 #pragma unroll
                 for (int j = 0; j < G_NBW; ++j)
@@ -385,6 +407,49 @@ __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
             }
         };
         const uint8_t* lbs = smem + bs_off + wid * G_NBW * 1024 + lane * 16;
+        if constexpr (kTop2) {
+            // A tile meets most experts as second ones, so it takes several rounds: the whole
+            // tile stays in registers (the accumulators become y in place) and is stored once.
+            v4f yt[MB][G_NBW];
+#pragma unroll
+            for (int m = 0; m < MB; ++m) {
+                const v4f sx = *reinterpret_cast<const v4f*>(&s_sx[m * 16 + lg * 4]);
+#pragma unroll
+                for (int j = 0; j < G_NBW; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) yt[m][j][r] = (float)(acc[m][j][r] >> 4) * sx[r] * sw[j];
+                if (have_se) {  // y += u . B_s
+                    const v8bf ua = *reinterpret_cast<const v8bf*>(smem + u_off + m * 1024 + lane * 16);
+#pragma unroll
+                    for (int j = 0; j < G_NBW; ++j)
+                        yt[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            ua, *reinterpret_cast<const v8bf*>(lbs + j * 1024), yt[m][j], 0, 0, 0);
+                }
+                routed(m, yt[m]);
+            }
+            while (pend) {  // uniform
+                QE_WAIT_VMCNT_LDS(0);
+                QE_WG_BARRIER();
+                pick_experts();
+                stage_experts(0);
+                QE_WAIT_VMCNT_LDS(0);
+                QE_WG_BARRIER();
+#pragma unroll
+                for (int m = 0; m < MB; ++m) routed(m, yt[m]);
+            }
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = m * 16 + lg * 4 + r;
+                    if (m0 + row >= T) continue;
+                    float* yrow = y + (size_t)s_tok[row] * d_out;
+#pragma unroll
+                    for (int j = 0; j < G_NBW; ++j)
+                        if (nb_ok[j]) yrow[(nb0 + j) * 16 + lr] = yt[m][j][r];
+                }
+            return;
+        }
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
             const v4f sx = *reinterpret_cast<const v4f*>(&s_sx[m * 16 + lg * 4]);
@@ -563,6 +628,17 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_kernel(
 // narrow k / v projections then run with q's tiles instead of a grid of their own that leaves
 // compute units idle).  Block b belongs to linear l with begin[l] <= b < begin[l + 1]; every
 // linear's grid starts at a multiple of 8, so its tiles keep their XCD assignment.
+// top-2 routing: 128-token tiles, fast epilogue, both experts' corrections in it
+__global__ __launch_bounds__(256, 2) void gemm_w4_top2_kernel(
+    const int8_t* __restrict__ codes, const float* __restrict__ s_x, const uint8_t* __restrict__ w_tiled,
+    const float* __restrict__ w_scale, int T, int d_in, int d_out, const uint16_t* __restrict__ u,
+    const uint16_t* __restrict__ bt_s, int rs_pad, const uint16_t* __restrict__ v, const int32_t* __restrict__ expert,
+    const uint16_t* __restrict__ bt_r, int rr_pad, int n_r, const int32_t* __restrict__ perm, float* __restrict__ y,
+    int n_tm, const uint16_t* __restrict__ v2, const int32_t* __restrict__ expert2) {
+    gemm_w4_tile<8, true, true>(codes, s_x, w_tiled, w_scale, T, d_in, d_out, u, bt_s, rs_pad, v, expert, bt_r, rr_pad,
+                                n_r, perm, y, nullptr, n_tm, nullptr, false, blockIdx.x, gridDim.x, 0, 1, v2, expert2);
+}
+
 __global__ __launch_bounds__(256, 2) void gemm_w4_group_kernel(GemmGroup G) {
     int l = 0;
 #pragma unroll
@@ -620,6 +696,30 @@ hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* 
     const bool routed = v != nullptr && expert != nullptr && bt_r != nullptr && rr_pad > 0 && n_r > 0;
     return launch_gemm_split_finish(part, ks, T, d_out, s_x, w_scale, rs_pad > 0 ? u : nullptr, bt_s, rs_pad,
                                     routed ? v : nullptr, routed ? expert : nullptr, n_r, bt_r, rr_pad, y, y_bf16, st);
+}
+
+// Top-2 routing in the main product's epilogue: for the launches that take 128-token tiles with
+// the fast epilogue and no K split (float32 y, ranks <= 32); gemm_w4_top2_ok says which.
+bool gemm_w4_top2_ok(int T, int d_out, int rs_pad, int rr_pad, int ksplit, bool y_bf16) {
+    const int n_tn = (d_out + G_BN - 1) / G_BN;
+    const bool small = (long)((T + 127) / 128) * n_tn < 512;
+    return T > 0 && !small && ksplit <= 1 && !y_bf16 && rs_pad <= 32 && rr_pad > 0 && rr_pad <= 32;
+}
+
+hipError_t launch_gemm_w4_top2(const int8_t* codes, const float* s_x, const uint8_t* w_tiled, const float* w_scale,
+                               int T, int d_in, int d_out, const uint16_t* u, const uint16_t* bt_s, int rs_pad,
+                               const uint16_t* v, const int32_t* expert, const uint16_t* v2, const int32_t* expert2,
+                               const uint16_t* bt_r, int rr_pad, int n_r, const int32_t* perm, float* y,
+                               hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (!gemm_w4_top2_ok(T, d_out, rs_pad, rr_pad, 1, false) || !v || !expert || !v2 || !expert2 || !bt_r || n_r < 2 ||
+        d_in % G_BK)
+        return hipErrorInvalidValue;
+    const int n_tn = (d_out + G_BN - 1) / G_BN, n_tm = (T + 127) / 128;
+    hipLaunchKernelGGL(gemm_w4_top2_kernel, dim3(n_tm * n_tn), dim3(256), 0, st, codes, s_x, w_tiled, w_scale, T, d_in,
+                       d_out, rs_pad > 0 ? u : nullptr, bt_s, rs_pad, v, expert, bt_r, rr_pad, n_r, perm, y, n_tm, v2,
+                       expert2);
+    return hipGetLastError();
 }
 
 // The grouped launch is for linears on the 128-token-tile fast path: float32 y, ranks <= 32,

@@ -415,7 +415,7 @@ static int xpass_partials(const qe_linear* lin, const void* x, int x_dtype, int 
 
 static int run_xpass(const qe_linear* lin, const void* x, int x_dtype, int T, bool want_se, bool want_re,
                      bool do_route, const int32_t* expert_in, float* scores, int32_t* expert_out, uint16_t* u,
-                     uint16_t* v, void* ws, hipStream_t s) {
+                     uint16_t* v, void* ws, hipStream_t s, int32_t* expert2_out = nullptr) {
     const PrepLayout P = prep_layout(lin);
     const WsLayout W = ws_layout(lin, T);
     int c0 = P.n_cols, c1 = 0;
@@ -436,7 +436,7 @@ static int run_xpass(const qe_linear* lin, const void* x, int x_dtype, int T, bo
     QE_TRY_HIP(launch_xproj_finish(part, ks, T, nc_pad, c0, want_se ? P.col_se : -1, lin->r_shared, P.rs_pad,
                                    want_re ? P.col_re : -1, lin->n_routed, lin->r_routed, P.rr_pad,
                                    do_route ? P.col_router : -1, expert_in, scores, expert_out, want_se ? u : nullptr,
-                                   want_re ? v : nullptr, s));
+                                   want_re ? v : nullptr, s, do_route ? expert2_out : nullptr));
     return QE_OK;
 }
 
@@ -548,7 +548,8 @@ int qe_routed_lora(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t
 // The two-pass prologue after its route pass (whose partials are in ws): route finish, then the
 // expert-sorted quantization pass.
 static int run_prologue_rest(const qe_linear* lin, const void* x, int T, int8_t* codes, float* s_x, uint16_t* u,
-                             uint16_t* v, int32_t* expert, int32_t* perm, void* ws, hipStream_t s, bool keep_order) {
+                             uint16_t* v, int32_t* expert, int32_t* perm, void* ws, hipStream_t s, bool keep_order,
+                             int32_t* expert2 = nullptr) {
     const PrepLayout P = prep_layout(lin);
     const WsLayout W = ws_layout(lin, T);
     const bool route = lin->n_routed > 0;
@@ -558,7 +559,7 @@ static int run_prologue_rest(const qe_linear* lin, const void* x, int T, int8_t*
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(x);
     QE_TRY_HIP(launch_route_finish(at<const float>(ws, W.part), at<const float>(ws, W.amax), W.rp_ksplit, T,
                                        P.n_lead, lin->r_shared, P.rs_pad, P.col_router, lin->n_routed, lin->a_bits,
-                                       route ? expert : nullptr, u, s_x, s));
+                                       route ? expert : nullptr, u, s_x, s, route ? expert2 : nullptr));
         QE_TRY_HIP(launch_expert_quant(xb, T, lin->d_in, smooth, inv_smooth, s_x, lin->a_bits,
                                        route ? expert : nullptr, lin->n_routed,
                                        route ? mt + (size_t)P.col_re * lin->d_in : nullptr, P.rr_pad, lin->r_routed,
@@ -569,9 +570,10 @@ static int run_prologue_rest(const qe_linear* lin, const void* x, int T, int8_t*
 
 // keep_order: few tokens may stay in token order in the two-pass prologue (perm is then not
 // written; the caller passes perm == NULL)
+// expert2 (top-2 routing, optional): also the second expert of every token
 static int run_prologue(const qe_linear* lin, const void* x, int x_dtype, int T, int8_t* codes, float* s_x,
                         uint16_t* u, uint16_t* v, int32_t* expert, int32_t* perm, void* ws, hipStream_t s,
-                        bool keep_order = false) {
+                        bool keep_order = false, int32_t* expert2 = nullptr) {
     const PrepLayout P = prep_layout(lin);
     const WsLayout W = ws_layout(lin, T);
     const bool route = lin->n_routed > 0;
@@ -580,10 +582,10 @@ static int run_prologue(const qe_linear* lin, const void* x, int x_dtype, int T,
                                      at<const uint16_t>(lin->prep, P.mt), P.n_lead, at<const float>(lin->prep, P.smooth),
                                      at<const float>(lin->prep, P.inv_smooth), W.rp_ksplit, at<float>(ws, W.part),
                                      at<float>(ws, W.amax), s));
-        return run_prologue_rest(lin, x, T, codes, s_x, u, v, expert, perm, ws, s, keep_order);
+        return run_prologue_rest(lin, x, T, codes, s_x, u, v, expert, perm, ws, s, keep_order, expert2);
     }
     int st = run_xpass(lin, x, x_dtype, T, u != nullptr, route, route, nullptr, nullptr, route ? expert : nullptr, u,
-                       v, ws, s);
+                       v, ws, s, route ? expert2 : nullptr);
     if (st) return st;
     if (route && perm)  // tokens grouped by routed expert, for the GEMM's tile order
         QE_TRY_HIP(launch_bucket(expert, T, lin->n_routed, at<int32_t>(ws, W.counts), at<int32_t>(ws, W.offsets), perm, s));
@@ -968,8 +970,9 @@ size_t qe_top2_workspace_bytes(const qe_linear* lin, int32_t T) {
     const size_t base = qe_workspace_bytes(lin, T);
     if (base == 0 || lin->n_routed < 2 || T < 0) return 0;
     const size_t t4 = align256((size_t)std::max(T, 1) * 4);
+    const PrepLayout P = prep_layout(lin);
     return align256(base) + 4 * t4 + align256((size_t)std::max(T, 1) * lin->n_routed * 4) +
-           2 * align256(((size_t)lin->n_routed + 1) * 4);
+           2 * align256(((size_t)lin->n_routed + 1) * 4) + align256((size_t)std::max(T, 1) * P.rr_pad * 2);
 }
 
 int qe_linear_forward_top2(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* y,
@@ -991,11 +994,45 @@ int qe_linear_forward_top2(const qe_linear* lin, const void* x, int32_t x_dtype,
     char* q = p + 4 * t4 + align256((size_t)T * lin->n_routed * 4);
     int32_t* offsets = reinterpret_cast<int32_t*>(q);
     int32_t* counts = reinterpret_cast<int32_t*>(q + align256(((size_t)lin->n_routed + 1) * 4));
-    int st = qe_linear_forward(lin, x, x_dtype, T, y, e1, ws, base, stream);
-    if (st) return st;
+    uint16_t* v2 = reinterpret_cast<uint16_t*>(q + 2 * align256(((size_t)lin->n_routed + 1) * 4));
     const PrepLayout P = prep_layout(lin);
     const WsLayout W = ws_layout(lin, T);
     hipStream_t s = S(stream);
+    if (lin->a_bits != 16 && lin->w_bits == 4 && T > kSkinnyMaxT &&
+        gemm_w4_top2_ok(T, lin->d_out, P.rs_pad, P.rr_pad, W.gemm_ksplit, lin->y_dtype == QE_BF16)) {
+        // Both routed corrections in the main product's epilogue: the prologue also gives each
+        // token's second expert (from the same router scores), one more pass of x onto the routed
+        // experts' input columns gives its v2, and every output is stored once.
+        int st = validate_forward_common(lin, T, x_dtype, x, ws, ws_bytes);
+        if (st) return st;
+        QE_CHECK(x && y, QE_ERR_INVALID_ARG);
+        QE_CHECK(aligned16(y), QE_ERR_ALIGNMENT);
+        int8_t* codes = at<int8_t>(ws, W.codes);
+        float* s_x = at<float>(ws, W.s_x);
+        uint16_t* u = P.rs_pad > 0 ? at<uint16_t>(ws, W.u) : nullptr;
+        uint16_t* v = at<uint16_t>(ws, W.v);
+        int32_t* perm_g = at<int32_t>(ws, W.perm);
+        st = run_prologue(lin, x, x_dtype, T, codes, s_x, u, v, e1, perm_g, ws, s, false, e2);
+        if (st) return st;
+        const int nc = lin->n_routed * P.rr_pad, nc_pad = (nc + 15) / 16 * 16;
+        float* part = at<float>(ws, W.part);
+        int ks = 0;
+        st = xpass_partials(lin, x, x_dtype, T, P.col_re, nc, nc_pad, part, ws, s, &ks);
+        if (st) return st;
+        QE_TRY_HIP(launch_xproj_finish(part, ks, T, nc_pad, P.col_re, -1, lin->r_shared, P.rs_pad, P.col_re,
+                                       lin->n_routed, lin->r_routed, P.rr_pad, -1, e2, nullptr, nullptr, nullptr, v2,
+                                       s));
+        QE_TRY_HIP(launch_gemm_w4_top2(codes, s_x, at<const uint8_t>(lin->prep, P.w_tiled),
+                                       at<const float>(lin->prep, P.w_scale), T, lin->d_in, lin->d_out, u,
+                                       P.rs_pad > 0 ? at<const uint16_t>(lin->prep, P.bt_s) : nullptr, P.rs_pad, v, e1,
+                                       v2, e2, at<const uint16_t>(lin->prep, P.bt_r), P.rr_pad, lin->n_routed, perm_g,
+                                       y, s));
+        if (expert_out) QE_TRY_HIP(hipMemcpyAsync(expert_out, e1, (size_t)T * 4, hipMemcpyDeviceToDevice, s));
+        if (expert2_out) QE_TRY_HIP(hipMemcpyAsync(expert2_out, e2, (size_t)T * 4, hipMemcpyDeviceToDevice, s));
+        return QE_OK;
+    }
+    int st = qe_linear_forward(lin, x, x_dtype, T, y, e1, ws, base, stream);
+    if (st) return st;
     // one pass of x onto the router and every routed expert's input columns; the finish runs twice
     // on its partials: the scores first, then v of the second expert
     const int c0 = std::min(P.col_re, P.col_router);

@@ -107,7 +107,7 @@ hipError_t launch_xproj(const void* x, int x_dtype, int T, int d_in, const uint1
 hipError_t launch_xproj_finish(const float* part, int ksplit, int T, int ncols_pad, int col0, int se_col,
                                int r_s, int rs_pad, int re_col, int n_r, int r_r, int rr_pad, int router_col,
                                const int32_t* expert_in, float* scores, int32_t* expert_out, uint16_t* u,
-                               uint16_t* v, hipStream_t st);
+                               uint16_t* v, hipStream_t st, int32_t* expert2_out = nullptr);
 
 // two-pass prefill prologue
 hipError_t launch_route_pass(const uint16_t* x, int T, int d_in, const uint16_t* mt, int ncols, const float* smooth,
@@ -129,7 +129,7 @@ hipError_t launch_route_pass_group(const uint16_t* x, int T, int d_in, const Rou
                                    hipStream_t st);
 hipError_t launch_route_finish(const float* part, const float* amax_part, int ksplit, int T, int ncols, int r_s,
                                int rs_pad, int router_col, int n_r, int a_bits, int32_t* expert, uint16_t* u,
-                               float* s_x, hipStream_t st);
+                               float* s_x, hipStream_t st, int32_t* expert2 = nullptr);
 // Expert-sorted codes + selected-expert v; buckets the routes itself and writes perm
 // (needed when ksq > 1: the split-K finish scatters v through it)
 hipError_t launch_expert_quant(const uint16_t* x, int T, int d_in, const float* smooth, const float* inv_smooth,
@@ -151,6 +151,14 @@ hipError_t launch_gemm_w4(const int8_t* codes, const float* s_x, const uint8_t* 
                           const int32_t* perm, float* y, int32_t* acc_debug, int ksplit, int32_t* part,
                           bool y_bf16, hipStream_t st);
 int gemm_ksplit(int T, int d_in, int d_out);
+// top-2 routing: both routed corrections in the main product's epilogue (128-token tiles, fast
+// epilogue, no K split); gemm_w4_top2_ok says whether a launch of these sizes takes it
+bool gemm_w4_top2_ok(int T, int d_out, int rs_pad, int rr_pad, int ksplit, bool y_bf16);
+hipError_t launch_gemm_w4_top2(const int8_t* codes, const float* s_x, const uint8_t* w_tiled, const float* w_scale,
+                               int T, int d_in, int d_out, const uint16_t* u, const uint16_t* bt_s, int rs_pad,
+                               const uint16_t* v, const int32_t* expert, const uint16_t* v2, const int32_t* expert2,
+                               const uint16_t* bt_r, int rr_pad, int n_r, const int32_t* perm, float* y,
+                               hipStream_t st);
 // several linears' main products (128-token tiles, fast epilogue, float32 y) in one launch
 constexpr int GG_MAX = 3;
 struct GemmLinear {

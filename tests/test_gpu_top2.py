@@ -113,3 +113,21 @@ def test_top2_argument_errors(Q):
     assert Q.libqe.qe_top2_workspace_bytes(layer.lin, 4) == 0
     with pytest.raises(Q.libqe.QEError):
         Q.libqe.qe_linear_forward_top2(layer.lin, x, y, ws=torch.empty(1 << 20, dtype=torch.uint8, device=DEV))
+
+
+@pytest.mark.parametrize("T,x_f32", [(4096, False), (4000, False), (4096, True)])
+def test_top2_fused_epilogue_internvl2_8b_q(Q, T, x_f32):
+    """128-token tiles on the fast epilogue without a K split take both routed corrections in the
+    main product's epilogue (the tile grid of the 4096 x 4096 projection reaches 512 workgroups).
+    Expert-sorted tiles meet many second experts, so the epilogue's further rounds run too; a
+    ragged last tile (T = 4000), and float32 activations (general prologue) are covered."""
+    cfg = synth.get_config("internvl2_8b")
+    spec = next(l for l in cfg.linears if l.name == "q")
+    params = synth.gen_linear(cfg, spec)
+    x = synth.gen_activations(cfg, spec.stream)[:T]
+    if x_f32:
+        x = x.float()
+    rng = np.random.default_rng(T + int(x_f32))
+    toks = np.unique(np.concatenate([np.arange(0, 130), np.arange(T - 70, T), rng.choice(T, 150, replace=False)]))
+    err, agree = _check(Q, params, x, cfg.w_bits, cfg.a_bits, tokens=toks)
+    print(f"8B q top-2 (T {T}, float32 x {x_f32}): err {err:.2e}, pairs equal {agree:.3f}")
