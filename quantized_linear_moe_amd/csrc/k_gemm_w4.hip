@@ -639,6 +639,7 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_top2_kernel(
                                 n_r, perm, y, nullptr, n_tm, nullptr, false, blockIdx.x, gridDim.x, 0, 1, v2, expert2);
 }
 
+template <int MB>
 __global__ __launch_bounds__(256, 2) void gemm_w4_group_kernel(GemmGroup G) {
     int l = 0;
 #pragma unroll
@@ -646,9 +647,9 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_group_kernel(GemmGroup G) {
         if (i < G.n && (int)blockIdx.x >= G.begin[i]) l = i;
     const GemmLinear& a = G.lin[l];
     const int nblk = (l + 1 < G.n ? G.begin[l + 1] : (int)gridDim.x) - G.begin[l];
-    gemm_w4_tile<8, true>(a.codes, a.s_x, a.w_tiled, a.w_scale, G.T, a.d_in, a.d_out, a.u, a.bt_s, a.rs_pad, a.v,
-                          a.expert, a.bt_r, a.rr_pad, a.n_r, a.perm, a.y, nullptr, (G.T + 127) / 128, nullptr, false,
-                          (int)blockIdx.x - G.begin[l], nblk, 0, 1);
+    gemm_w4_tile<MB, true>(a.codes, a.s_x, a.w_tiled, a.w_scale, G.T, a.d_in, a.d_out, a.u, a.bt_s, a.rs_pad, a.v,
+                           a.expert, a.bt_r, a.rr_pad, a.n_r, a.perm, a.y, nullptr, (G.T + MB * 16 - 1) / (MB * 16),
+                           nullptr, false, (int)blockIdx.x - G.begin[l], nblk, 0, 1);
 }
 
 // K splits of the main product (fast epilogue only): 1 unless the 64-token-tile grid
@@ -722,13 +723,18 @@ hipError_t launch_gemm_w4_top2(const int8_t* codes, const float* s_x, const uint
     return hipGetLastError();
 }
 
-// The grouped launch is for linears on the 128-token-tile fast path: float32 y, ranks <= 32,
+// The grouped launch is for linears on the fast path without a K split: float32 y, ranks <= 32,
 // no accumulator dump, every linear's tile grid a multiple of 8.  Returns hipErrorInvalidValue
 // (nothing launched) otherwise, and the caller then launches the linears one by one.
 hipError_t launch_gemm_w4_group(const GemmGroup& G0, hipStream_t st) {
     GemmGroup G = G0;
     if (G.n < 1 || G.n > GG_MAX || G.T <= 0) return hipErrorInvalidValue;
-    const int n_tm = (G.T + 127) / 128;
+    // 128-token tiles unless the group's grid would leave the chip less than two workgroups per
+    // CU, as for one linear (launch_gemm_w4); then 64-token tiles
+    long tiles128 = 0;
+    for (int l = 0; l < G.n; ++l) tiles128 += (long)((G.T + 127) / 128) * ((G.lin[l].d_out + G_BN - 1) / G_BN);
+    const int bm = tiles128 < 512 ? 64 : 128;
+    const int n_tm = (G.T + bm - 1) / bm;
     int begin = 0;
     for (int l = 0; l < G.n; ++l) {
         const GemmLinear& a = G.lin[l];
@@ -738,7 +744,8 @@ hipError_t launch_gemm_w4_group(const GemmGroup& G0, hipStream_t st) {
         G.begin[l] = begin;
         begin += tiles;
     }
-    hipLaunchKernelGGL(gemm_w4_group_kernel, dim3(begin), dim3(256), 0, st, G);
+    if (bm == 128) hipLaunchKernelGGL(gemm_w4_group_kernel<8>, dim3(begin), dim3(256), 0, st, G);
+    else hipLaunchKernelGGL(gemm_w4_group_kernel<4>, dim3(begin), dim3(256), 0, st, G);
     return hipGetLastError();
 }
 

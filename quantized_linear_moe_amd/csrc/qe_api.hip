@@ -736,7 +736,6 @@ static bool try_group_gemm(const qe_linear* const* lins, int n, int T, int8_t* c
     GemmGroup G{};
     G.n = n;
     G.T = T;
-    long tiles = 0;
     for (int i = 0; i < n; ++i) {
         const qe_linear* lin = lins[i];
         if (lin->a_bits == 16 || lin->y_dtype != QE_F32) return false;
@@ -761,9 +760,7 @@ static bool try_group_gemm(const qe_linear* const* lins, int n, int T, int8_t* c
         a.rs_pad = a.u ? P.rs_pad : 0;
         a.rr_pad = routed ? P.rr_pad : 0;
         a.n_r = routed ? lin->n_routed : 0;
-        tiles += (long)((T + 127) / 128) * ((lin->d_out + 255) / 256);
     }
-    if (tiles < 512) return false;  // too few 128-token tiles: the per-linear launches pick smaller ones
     const hipError_t e = launch_gemm_w4_group(G, s);
     if (e == hipErrorInvalidValue) return false;  // a grid not a multiple of 8: nothing launched
     *status = e == hipSuccess ? QE_OK : hip_fail(e);

@@ -159,7 +159,7 @@ hipError_t launch_gemm_w4_top2(const int8_t* codes, const float* s_x, const uint
                                const uint16_t* v, const int32_t* expert, const uint16_t* v2, const int32_t* expert2,
                                const uint16_t* bt_r, int rr_pad, int n_r, const int32_t* perm, float* y,
                                hipStream_t st);
-// several linears' main products (128-token tiles, fast epilogue, float32 y) in one launch
+// several linears' main products (fast epilogue, float32 y, no K split) in one launch
 constexpr int GG_MAX = 3;
 struct GemmLinear {
     const int8_t* codes;
