@@ -820,13 +820,11 @@ hipError_t launch_route_pass_group(const uint16_t* x, int T, int d_in, const Rou
 
 // One wave per token: fixed-order split-K sums, router argmin (lowest index on ties),
 // u = bf16(shared projection), s_x = max |x/s| / qmax (a max is exact in any order).
-__global__ __launch_bounds__(256) void route_finish_kernel(const float* __restrict__ part,
-                                                           const float* __restrict__ amax_part, int ksplit, int T,
-                                                           int ncols, int r_s, int rs_pad, int router_col, int n_r,
-                                                           int qmax, int32_t* __restrict__ expert,
-                                                           uint16_t* __restrict__ u, float* __restrict__ s_x,
-                                                           int32_t* __restrict__ expert2) {
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+__device__ __forceinline__ void route_finish_token(const float* __restrict__ part, const float* __restrict__ amax_part,
+                                                   int ksplit, int T, int ncols, int r_s, int rs_pad, int router_col,
+                                                   int n_r, int qmax, int32_t* __restrict__ expert,
+                                                   uint16_t* __restrict__ u, float* __restrict__ s_x,
+                                                   int32_t* __restrict__ expert2, int t, int lane) {
     if (t >= T) return;
     // columns lane and lane + 64 (ncols <= 80), and the activation maxima: the partials of up to
     // 16 splits of both columns and the maxima are requested together, then added in split order
@@ -905,6 +903,30 @@ __global__ __launch_bounds__(256) void route_finish_kernel(const float* __restri
     if (lane == 0) s_x[t] = m / (float)qmax;
 }
 
+__global__ __launch_bounds__(256) void route_finish_kernel(const float* __restrict__ part,
+                                                           const float* __restrict__ amax_part, int ksplit, int T,
+                                                           int ncols, int r_s, int rs_pad, int router_col, int n_r,
+                                                           int qmax, int32_t* __restrict__ expert,
+                                                           uint16_t* __restrict__ u, float* __restrict__ s_x,
+                                                           int32_t* __restrict__ expert2) {
+    route_finish_token(part, amax_part, ksplit, T, ncols, r_s, rs_pad, router_col, n_r, qmax, expert, u, s_x, expert2,
+                       blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
+}
+
+// the route finishes of up to RG_MAX linears that read the same x: linear blockIdx.y
+__global__ __launch_bounds__(256) void route_finish_group_kernel(FinishGroup G, int ksplit, int T) {
+    const FinishLinear& a = G.lin[blockIdx.y];
+    route_finish_token(a.part, a.amax, ksplit, T, a.ncols, a.r_s, a.rs_pad, a.router_col, a.n_r, a.qmax, a.expert,
+                       a.u, a.s_x, nullptr, blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
+}
+
+hipError_t launch_route_finish_group(const FinishGroup& G, int n_lin, int ksplit, int T, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (n_lin < 1 || n_lin > RG_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(route_finish_group_kernel, dim3((T + 3) / 4, n_lin), dim3(256), 0, st, G, ksplit, T);
+    return hipGetLastError();
+}
+
 hipError_t launch_route_finish(const float* part, const float* amax_part, int ksplit, int T, int ncols, int r_s,
                                int rs_pad, int router_col, int n_r, int a_bits, int32_t* expert, uint16_t* u,
                                float* s_x, hipStream_t st, int32_t* expert2) {
@@ -943,11 +965,11 @@ constexpr int EQ_FEW_T = 256;       // token counts that take the few-token form
 // keeps the tokens in their order (no bucketing, no permutation written): for few tokens
 // whose main product is split over K, whose epilogue does not gain from grouped experts.
 template <int NBR, int ESL>
-__global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
+__device__ __forceinline__ void expert_quant_tile(
     const uint16_t* __restrict__ x, int T, int d_in, const float* __restrict__ smooth,
     const float* __restrict__ inv_smooth, const float* __restrict__ s_x, int qmax, const int32_t* __restrict__ expert,
     int n_r, const uint16_t* __restrict__ mt_re, int r_r, int ksq, int32_t* __restrict__ perm_out,
-    float* __restrict__ vpart, int8_t* __restrict__ codes, uint16_t* __restrict__ v, bool sort_rows) {
+    float* __restrict__ vpart, int8_t* __restrict__ codes, uint16_t* __restrict__ v, bool sort_rows, int tile, int kq) {
     constexpr int RR = NBR * 16;               // padded routed rank
     constexpr int NB1 = NBR ? NBR : 1;
     constexpr int ESLOTS = ESL > 0 ? ESL : NBR == 4 ? 1 : 2;  // experts per pass
@@ -962,7 +984,6 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
     __shared__ int s_cnt[EQ_W][kMaxRouted];
     __shared__ int s_tok[EQ_ROWS];
     const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-    const int tile = blockIdx.x, kq = blockIdx.y;
     const int pos0 = tile * EQ_ROWS;
     const bool routed = expert != nullptr && n_r > 0;
 
@@ -1192,6 +1213,25 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
     }
 }
 
+template <int NBR, int ESL>
+__global__ __launch_bounds__(64 * EQ_W) void expert_quant_kernel(
+    const uint16_t* __restrict__ x, int T, int d_in, const float* __restrict__ smooth,
+    const float* __restrict__ inv_smooth, const float* __restrict__ s_x, int qmax, const int32_t* __restrict__ expert,
+    int n_r, const uint16_t* __restrict__ mt_re, int r_r, int ksq, int32_t* __restrict__ perm_out,
+    float* __restrict__ vpart, int8_t* __restrict__ codes, uint16_t* __restrict__ v, bool sort_rows) {
+    expert_quant_tile<NBR, ESL>(x, T, d_in, smooth, inv_smooth, s_x, qmax, expert, n_r, mt_re, r_r, ksq, perm_out, vpart,
+                                codes, v, sort_rows, blockIdx.x, blockIdx.y);
+}
+
+// the expert-sorted passes of up to RG_MAX linears that read the same x: linear blockIdx.z
+template <int NBR, int ESL>
+__global__ __launch_bounds__(64 * EQ_W) void expert_quant_group_kernel(const uint16_t* __restrict__ x, int T, int d_in,
+                                                                       int ksq, bool sort_rows, EqGroup G) {
+    const EqLinear& a = G.lin[blockIdx.z];
+    expert_quant_tile<NBR, ESL>(x, T, d_in, a.smooth, a.inv_smooth, a.s_x, a.qmax, a.expert, a.n_r, a.mt_re, a.r_r, ksq,
+                                a.perm, a.vpart, a.codes, a.v, sort_rows, blockIdx.x, blockIdx.y);
+}
+
 // v[perm[pos]][c] = bf16(sum over q, in order, of vpart[q][pos][c])
 __global__ __launch_bounds__(256) void vpart_finish_kernel(const float* __restrict__ vpart, int ksq, int T, int rr_pad,
                                                            int r_r, const int32_t* __restrict__ perm,
@@ -1204,6 +1244,17 @@ __global__ __launch_bounds__(256) void vpart_finish_kernel(const float* __restri
     v[(size_t)tt * rr_pad + c] = c < r_r ? (uint16_t)f32_to_bf16_bits(a) : (uint16_t)0;
 }
 
+// the v finishes of a group: linear blockIdx.y
+__global__ __launch_bounds__(256) void vpart_finish_group_kernel(EqGroup G, int ksq, int T, int rr_pad) {
+    const EqLinear& a = G.lin[blockIdx.y];
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)T * rr_pad) return;
+    const int pos = (int)(idx / rr_pad), c = (int)(idx % rr_pad);
+    const int tt = a.perm ? a.perm[pos] : pos;
+    const float sum = sum_splits(a.vpart + idx, (size_t)T * rr_pad, ksq);
+    a.v[(size_t)tt * rr_pad + c] = c < a.r_r ? (uint16_t)f32_to_bf16_bits(sum) : (uint16_t)0;
+}
+
 // K splits: about 512 workgroups with at least two channel groups each; few tokens (one or two
 // row tiles) take one group per workgroup where at most 64 splits allow it, since each group
 // costs a memory latency that so few workgroups cannot hide
@@ -1214,6 +1265,40 @@ int expert_quant_ksplit(int T, int d_in) {
     const int ks = T <= EQ_FEW_T ? std::min(d_in / EQ_KG, 64)
                                  : std::min((512 + tiles - 1) / tiles, std::max(1, d_in / (2 * EQ_KG)));
     return std::max(ks, 1);
+}
+
+hipError_t launch_expert_quant_group(const uint16_t* x, int T, int d_in, const EqGroup& G0, int n_lin, int rr_pad,
+                                     int ksq, bool keep_order, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    const int nbr = rr_pad / 16;
+    if (n_lin < 1 || n_lin > RG_MAX || (nbr != 2 && nbr != 4) || d_in % EQ_KG || ksq < 1 || ksq > d_in / EQ_KG)
+        return hipErrorInvalidValue;
+    const bool few = expert_quant_few(T);
+    keep_order = keep_order && few;
+    EqGroup G = G0;
+    for (int l = 0; l < n_lin; ++l) {
+        EqLinear& a = G.lin[l];
+        if (!a.expert || !a.v || !a.smooth || !a.inv_smooth || a.n_r < 1 || a.n_r > kMaxRouted) return hipErrorInvalidValue;
+        if (ksq > 1 && (!a.vpart || (!a.perm && !keep_order))) return hipErrorInvalidValue;
+        if (keep_order) a.perm = nullptr;
+    }
+    const dim3 grid((T + EQ_ROWS - 1) / EQ_ROWS, ksq, n_lin);
+#define QE_EQG_LAUNCH(NB, ESLV) \
+    hipLaunchKernelGGL((expert_quant_group_kernel<NB, ESLV>), grid, dim3(64 * EQ_W), 0, st, x, T, d_in, ksq, !keep_order, G)
+    if (nbr == 2) {
+        if (few) QE_EQG_LAUNCH(2, 8);
+        else QE_EQG_LAUNCH(2, 0);
+    } else {
+        if (few) QE_EQG_LAUNCH(4, 4);
+        else QE_EQG_LAUNCH(4, 0);
+    }
+#undef QE_EQG_LAUNCH
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || ksq == 1) return err;
+    const size_t n = (size_t)T * rr_pad;
+    hipLaunchKernelGGL(vpart_finish_group_kernel, dim3((unsigned)((n + 255) / 256), n_lin), dim3(256), 0, st, G, ksq, T,
+                       rr_pad);
+    return hipGetLastError();
 }
 
 hipError_t launch_expert_quant(const uint16_t* x, int T, int d_in, const float* smooth, const float* inv_smooth,

@@ -717,11 +717,60 @@ static int run_group_prologue(const qe_linear* const* lins, int n, const void* x
         ks = W.rp_ksplit;  // depends on T and d_in only: the same for every linear of the group
     }
     QE_TRY_HIP(launch_route_pass_group(reinterpret_cast<const uint16_t*>(x), T, lins[0]->d_in, G, n, ks, s));
-    for (int i = 0; i < n; ++i) {
-        int st = run_prologue_rest(lins[i], x, T, codes[i], s_x[i], u[i], v[i], expert[i], perm[i], ws[i], s,
-                                   keep_order ? keep_order[i] : false);
-        if (st) return st;
+    // The rest as one launch per step for the whole group when every linear is routed with the
+    // same padded rank and token order rule; else linear by linear.
+    bool grouped = true;
+    const bool ko0 = keep_order ? keep_order[0] : false;
+    for (int i = 0; i < n; ++i)
+        grouped = grouped && lins[i]->n_routed > 0 && expert[i] && v[i] &&
+                  prep_layout(lins[i]).rr_pad == prep_layout(lins[0]).rr_pad &&
+                  (keep_order ? keep_order[i] : false) == ko0;
+    if (!grouped) {
+        for (int i = 0; i < n; ++i) {
+            int st = run_prologue_rest(lins[i], x, T, codes[i], s_x[i], u[i], v[i], expert[i], perm[i], ws[i], s,
+                                       keep_order ? keep_order[i] : false);
+            if (st) return st;
+        }
+        return QE_OK;
     }
+    FinishGroup F{};
+    EqGroup E{};
+    int ksq = 0;
+    for (int i = 0; i < n; ++i) {
+        const qe_linear* lin = lins[i];
+        const PrepLayout P = prep_layout(lin);
+        const WsLayout W = ws_layout(lin, T);
+        const int qmax = (1 << (lin->a_bits - 1)) - 1;
+        FinishLinear& f = F.lin[i];
+        f.part = at<const float>(ws[i], W.part);
+        f.amax = at<const float>(ws[i], W.amax);
+        f.ncols = P.n_lead;
+        f.r_s = lin->r_shared;
+        f.rs_pad = P.rs_pad;
+        f.router_col = P.col_router;
+        f.n_r = lin->n_routed;
+        f.qmax = qmax;
+        f.expert = expert[i];
+        f.u = u[i];
+        f.s_x = s_x[i];
+        EqLinear& e = E.lin[i];
+        e.smooth = at<const float>(lin->prep, P.smooth);
+        e.inv_smooth = at<const float>(lin->prep, P.inv_smooth);
+        e.s_x = s_x[i];
+        e.qmax = qmax;
+        e.expert = expert[i];
+        e.n_r = lin->n_routed;
+        e.mt_re = at<const uint16_t>(lin->prep, P.mt) + (size_t)P.col_re * lin->d_in;
+        e.r_r = lin->r_routed;
+        e.perm = perm[i] ? perm[i] : at<int32_t>(ws[i], W.perm);
+        e.vpart = at<float>(ws[i], W.vpart);
+        e.codes = codes[i];
+        e.v = v[i];
+        ksq = W.eq_ksplit;  // depends on T and d_in only
+    }
+    QE_TRY_HIP(launch_route_finish_group(F, n, ks, T, s));
+    QE_TRY_HIP(launch_expert_quant_group(reinterpret_cast<const uint16_t*>(x), T, lins[0]->d_in, E, n,
+                                         prep_layout(lins[0]).rr_pad, ksq, ko0, s));
     return QE_OK;
 }
 

@@ -127,6 +127,41 @@ struct RouteGroup {
 };
 hipError_t launch_route_pass_group(const uint16_t* x, int T, int d_in, const RouteGroup& G, int n_lin, int ksplit,
                                    hipStream_t st);
+// the rest of the two-pass prologue for the linears of a group, each step one launch for all
+// of them (route finishes; expert-sorted passes and v finishes); the same arithmetic as the
+// per-linear launches
+struct FinishLinear {
+    const float* part;
+    const float* amax;
+    int ncols, r_s, rs_pad, router_col, n_r, qmax;
+    int32_t* expert;
+    uint16_t* u;
+    float* s_x;
+};
+struct FinishGroup {
+    FinishLinear lin[RG_MAX];
+};
+hipError_t launch_route_finish_group(const FinishGroup& G, int n_lin, int ksplit, int T, hipStream_t st);
+struct EqLinear {
+    const float* smooth;
+    const float* inv_smooth;
+    const float* s_x;
+    int qmax;
+    const int32_t* expert;
+    int n_r;
+    const uint16_t* mt_re;
+    int r_r;
+    int32_t* perm;
+    float* vpart;
+    int8_t* codes;
+    uint16_t* v;
+};
+struct EqGroup {
+    EqLinear lin[RG_MAX];
+};
+// every linear routed, with the same padded rank rr_pad (32 or 64)
+hipError_t launch_expert_quant_group(const uint16_t* x, int T, int d_in, const EqGroup& G, int n_lin, int rr_pad,
+                                     int ksq, bool keep_order, hipStream_t st);
 hipError_t launch_route_finish(const float* part, const float* amax_part, int ksplit, int T, int ncols, int r_s,
                                int rs_pad, int router_col, int n_r, int a_bits, int32_t* expert, uint16_t* u,
                                float* s_x, hipStream_t st, int32_t* expert2 = nullptr);
