@@ -407,103 +407,62 @@ __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
             }
         };
         const uint8_t* lbs = smem + bs_off + wid * G_NBW * 1024 + lane * 16;
-        if constexpr (kTop2) {
-            // A tile meets most experts as second ones, so it takes several rounds: the whole
-            // tile stays in registers (the accumulators become y in place) and is stored once.
-            v4f yt[MB][G_NBW];
-#pragma unroll
-            for (int m = 0; m < MB; ++m) {
-                const v4f sx = *reinterpret_cast<const v4f*>(&s_sx[m * 16 + lg * 4]);
-#pragma unroll
-                for (int j = 0; j < G_NBW; ++j)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) yt[m][j][r] = (float)(acc[m][j][r] >> 4) * sx[r] * sw[j];
-                if (have_se) {  // y += u . B_s
-                    const v8bf ua = *reinterpret_cast<const v8bf*>(smem + u_off + m * 1024 + lane * 16);
-#pragma unroll
-                    for (int j = 0; j < G_NBW; ++j)
-                        yt[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            ua, *reinterpret_cast<const v8bf*>(lbs + j * 1024), yt[m][j], 0, 0, 0);
-                }
-                routed(m, yt[m]);
-            }
-            while (pend) {  // uniform
-                QE_WAIT_VMCNT_LDS(0);
-                QE_WG_BARRIER();
-                pick_experts();
-                stage_experts(0);
-                QE_WAIT_VMCNT_LDS(0);
-                QE_WG_BARRIER();
-#pragma unroll
-                for (int m = 0; m < MB; ++m) routed(m, yt[m]);
-            }
-#pragma unroll
-            for (int m = 0; m < MB; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = m * 16 + lg * 4 + r;
-                    if (m0 + row >= T) continue;
-                    float* yrow = y + (size_t)s_tok[row] * d_out;
-#pragma unroll
-                    for (int j = 0; j < G_NBW; ++j)
-                        if (nb_ok[j]) yrow[(nb0 + j) * 16 + lr] = yt[m][j][r];
-                }
-            return;
-        }
+        // The whole tile stays in registers through the expert rounds (the accumulators
+        // become y in place): a tile with more experts than one round holds (always, for
+        // top-2, whose tiles meet most experts as second ones) adds the rest in further rounds
+        // without reading back stored rows.
+        v4f yt[MB][G_NBW];
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
             const v4f sx = *reinterpret_cast<const v4f*>(&s_sx[m * 16 + lg * 4]);
-            v4f yv[G_NBW];
 #pragma unroll
             for (int j = 0; j < G_NBW; ++j)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) yv[j][r] = (float)(acc[m][j][r] >> 4) * sx[r] * sw[j];
+                for (int r = 0; r < 4; ++r) yt[m][j][r] = (float)(acc[m][j][r] >> 4) * sx[r] * sw[j];
             if (have_se) {  // y += u . B_s
                 const v8bf ua = *reinterpret_cast<const v8bf*>(smem + u_off + m * 1024 + lane * 16);
 #pragma unroll
                 for (int j = 0; j < G_NBW; ++j)
-                    yv[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, *reinterpret_cast<const v8bf*>(lbs + j * 1024),
-                                                                    yv[j], 0, 0, 0);
+                    yt[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        ua, *reinterpret_cast<const v8bf*>(lbs + j * 1024), yt[m][j], 0, 0, 0);
             }
-            routed(m, yv);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = m * 16 + lg * 4 + r;
-                if (m0 + row >= T) continue;
-                float* yrow = y + (size_t)s_tok[row] * d_out;
-#pragma unroll
-                for (int j = 0; j < G_NBW; ++j)
-                    if (nb_ok[j]) yrow[(nb0 + j) * 16 + lr] = yv[j][r];
-            }
-            __builtin_amdgcn_sched_barrier(0);  // one block at a time: keeps register pressure flat
+            routed(m, yt[m]);
         }
-        while (pend) {  // more experts than one round holds (uniform; rare)
+        while (pend) {  // uniform
             QE_WAIT_VMCNT_LDS(0);
             QE_WG_BARRIER();
             pick_experts();
             stage_experts(0);
             QE_WAIT_VMCNT_LDS(0);
             QE_WG_BARRIER();
-            for (int m = 0; m < MB; ++m) {
-                v4f yv[G_NBW];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {  // this lane's own stores of the first round
-                    const int row = m * 16 + lg * 4 + r;
-                    const float* yrow = y + (size_t)s_tok[row] * d_out;
+            for (int m = 0; m < MB; ++m) routed(m, yt[m]);
+        }
+        // Stores.  A lane holds 16 single columns of four rows; through a wave-private LDS
+        // buffer (16 rows x 64 columns, rows padded to 68 floats so a lane group's 16 writes hit
+        // distinct banks) each store instruction instead writes four rows x 256 contiguous bytes,
+        // whole 128-byte lines, marked non-temporal: y is not read again here, and full-line
+        // streaming stores keep the K loops' operands in the caches (partial lines written
+        // non-temporally cost more than they save).
+        QE_WAIT_LDS();
+        QE_WG_BARRIER();  // every wave is done with the operands in the ring
+        constexpr int YLD = 68;
+        static_assert(4 * 16 * YLD * 4 <= NS * STAGE, "store buffers must fit in the ring");
+        float* ybuf = reinterpret_cast<float*>(smem) + wid * 16 * YLD;
+        const int sr = lane >> 4, sc = (lane & 15) * 4;  // read-back: row sr + 4i, columns sc..sc+3
+        const bool col_ok = nb_ok[(lane & 15) >> 2];
 #pragma unroll
-                    for (int j = 0; j < G_NBW; ++j)
-                        yv[j][r] = (nb_ok[j] && m0 + row < T) ? yrow[(nb0 + j) * 16 + lr] : 0.0f;
-                }
-                routed(m, yv);
+        for (int m = 0; m < MB; ++m) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = m * 16 + lg * 4 + r;
-                    if (m0 + row >= T) continue;
-                    float* yrow = y + (size_t)s_tok[row] * d_out;
+            for (int j = 0; j < G_NBW; ++j)
 #pragma unroll
-                    for (int j = 0; j < G_NBW; ++j)
-                        if (nb_ok[j]) yrow[(nb0 + j) * 16 + lr] = yv[j][r];
-                }
+                for (int r = 0; r < 4; ++r) ybuf[(lg * 4 + r) * YLD + j * 16 + lr] = yt[m][j][r];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = m * 16 + sr + 4 * i;
+                const v4f val = *reinterpret_cast<const v4f*>(&ybuf[(sr + 4 * i) * YLD + sc]);
+                if (col_ok && m0 + row < T)
+                    __builtin_nontemporal_store(val, reinterpret_cast<v4f*>(y + (size_t)s_tok[row] * d_out + nb0 * 16 + sc));
             }
         }
         return;
