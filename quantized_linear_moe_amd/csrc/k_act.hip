@@ -196,8 +196,8 @@ hipError_t launch_quant_act(const void* x, int x_dtype, const float* smooth, con
 // lane) straight into registers, one K step ahead of the MFMAs.
 constexpr int XP_TOK = 128;      // tokens per workgroup
 constexpr int XP_MB = XP_TOK / 16;
-constexpr int XP_NBW = 5;        // 16-column blocks per wave
-constexpr int XP_COLS = 4 * XP_NBW * 16;
+// 16-column blocks per wave: 5 (320 columns per workgroup), or 4 for column counts that are a
+// multiple of 256 (the routed experts' 8 x 32 input columns), which 5 would pad by a quarter
 constexpr int XP_KC = 64;        // K chunk staged in LDS
 constexpr int XP_LDS_LD = XP_KC * 2 + 16;  // bytes per LDS row (padded against bank conflicts)
 
@@ -213,9 +213,11 @@ __device__ inline v4u load_x8_bf16(const void* x, int x_dtype, size_t idx) {
     return val;
 }
 
+template <int XP_NBW>
 __global__ __launch_bounds__(256, 2) void xproj_kernel(const void* __restrict__ x, int x_dtype, int T, int d_in,
                                                        const uint16_t* __restrict__ mt, int col0, int ncols,
                                                        int ncols_pad, int ksplit, float* __restrict__ part) {
+    constexpr int XP_COLS = 4 * XP_NBW * 16;
     __shared__ __attribute__((aligned(16))) uint8_t xs[2][XP_TOK * XP_LDS_LD];
     const int tile = blockIdx.x, ks = blockIdx.y, cgrp = blockIdx.z;
     const int tok0 = tile * XP_TOK;
@@ -311,9 +313,15 @@ __global__ __launch_bounds__(256, 2) void xproj_kernel(const void* __restrict__ 
 hipError_t launch_xproj(const void* x, int x_dtype, int T, int d_in, const uint16_t* mt, int col0, int ncols,
                         int ncols_pad, int ksplit, float* part, hipStream_t st) {
     if (T <= 0) return hipSuccess;
-    dim3 grid((T + XP_TOK - 1) / XP_TOK, ksplit, (ncols_pad + XP_COLS - 1) / XP_COLS);
-    hipLaunchKernelGGL(xproj_kernel, grid, dim3(256), 0, st, x, x_dtype, T, d_in, mt, col0, ncols, ncols_pad, ksplit,
-                       part);
+    if (ncols_pad % 256 == 0) {
+        dim3 grid((T + XP_TOK - 1) / XP_TOK, ksplit, ncols_pad / 256);
+        hipLaunchKernelGGL(xproj_kernel<4>, grid, dim3(256), 0, st, x, x_dtype, T, d_in, mt, col0, ncols, ncols_pad,
+                           ksplit, part);
+    } else {
+        dim3 grid((T + XP_TOK - 1) / XP_TOK, ksplit, (ncols_pad + 319) / 320);
+        hipLaunchKernelGGL(xproj_kernel<5>, grid, dim3(256), 0, st, x, x_dtype, T, d_in, mt, col0, ncols, ncols_pad,
+                           ksplit, part);
+    }
     return hipGetLastError();
 }
 

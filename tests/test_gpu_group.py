@@ -30,8 +30,11 @@ def _layers(Q, cfg, names):
     return specs, params, layers
 
 
+# the grouped route pass, then the grouped route finish / expert-sorted pass / v finish (every
+# linear routed with the same rank); ragged token counts (2000, 300: the few-token form)
 CASES = [("qwen2vl_72b", ("q", "k", "v"), None), ("qwen2vl_72b", ("gate", "up"), None),
-         ("qwen2vl_2b", ("q", "k", "v"), None), ("internvl2_8b", ("gate", "up"), 300), ("tiny", ("lin",), None)]
+         ("qwen2vl_2b", ("q", "k", "v"), None), ("qwen2vl_2b", ("q", "k", "v"), 2000),
+         ("internvl2_8b", ("gate", "up"), 300), ("tiny", ("lin",), None)]
 
 
 @pytest.mark.parametrize("cfg_name,names,T", CASES)
@@ -109,12 +112,13 @@ def test_group_rejects_mismatched_inputs(Q):
 
 
 @pytest.mark.parametrize("cfg_name,names,T", [("qwen2vl_72b", ("q", "k", "v"), None), ("qwen2vl_72b", ("down",), None),
-                                              ("qwen2vl_2b", ("q", "k", "v"), None), ("qwen2vl_2b", ("q", "k", "v"), 300)])
+                                              ("qwen2vl_2b", ("q", "k", "v"), None), ("qwen2vl_2b", ("q", "k", "v"), 2000),
+                                              ("qwen2vl_2b", ("q", "k", "v"), 300)])
 def test_group_gemm_matches_single_gemms(Q, cfg_name, names, T):
     # one launch over the group's tiles against each linear's own launch: identical bits.  72B
     # q/k/v: 128-token tiles (the narrow k and v alone take 64-token tiles); 2B q/k/v at 2048
-    # tokens: 64-token tiles for the whole group (fewer than 512 128-token tiles); at 300
-    # tokens the K split keeps the per-linear launches
+    # and 2000 tokens (a ragged last tile): 64-token tiles for the whole group (fewer than 512
+    # 128-token tiles); at 300 tokens the K split keeps the per-linear launches
     L = Q.libqe
     cfg = synth.get_config(cfg_name)
     specs, params, layers = _layers(Q, cfg, names)
