@@ -241,7 +241,8 @@ int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int3
 
 /* Linears that read the same input (q, k and v of an attention block; gate and up of an MLP):
  * the QE linear of each (DeepRead summary, "Method"), with the input read once for all of their
- * route passes.  lins[0..n_lin) (1 <= n_lin <= 3, equal d_in); x as for qe_linear_forward;
+ * route passes (and, when every linear is routed with the same rank, one launch per step for the
+ * rest of their prologues).  lins[0..n_lin) (1 <= n_lin <= 3, equal d_in); x as for qe_linear_forward;
  * every other pointer argument is an array of n_lin entries, entry i meaning what the same
  * argument of qe_linear_prologue / qe_linear_forward means for lins[i]; ws[i] holds
  * ws_bytes[i] >= qe_workspace_bytes(lins[i], T) bytes, one workspace per linear.  Results are
@@ -260,11 +261,12 @@ int qe_group_forward(const qe_linear* const* lins, int32_t n_lin, const void* x,
                      void* stream);
 /* The main products of a group (qe_wq_gemm for each linear, a_bits 6/8 only; the quantized
  * product with the fused adapter terms of the listing's Table 7 and the DeepRead summary's
- * "Method", as for qe_wq_gemm): when every linear
- * takes the 128-token-tile path (float32 y, ranks <= 32, no K split) and the combined tile grid
- * is at least 512 workgroups, one launch runs all of them, so narrow projections (k, v) share
- * the grid of a wide one (q) instead of running a grid of their own; else one product after the
- * other.  Identical results either way.  Arrays of n_lin entries as for qe_group_prologue (its
+ * "Method", as for qe_wq_gemm): when every linear takes the fast path without a K split
+ * (float32 y, ranks <= 32) and every linear's tile grid is a multiple of 8 workgroups, one
+ * launch runs all of them, so narrow projections (k, v) share the grid of a wide one (q) instead
+ * of running a grid of their own: 128-token tiles when the combined grid of those is at least
+ * 512 workgroups, else 64-token tiles; otherwise one product after the other.  Identical results
+ * either way.  Arrays of n_lin entries as for qe_group_prologue (its
  * outputs are this call's inputs); qe_group_forward ends with this step.
  */
 int qe_group_gemm(const qe_linear* const* lins, int32_t n_lin, const int8_t* const* codes, const float* const* s_x,
@@ -390,10 +392,12 @@ int qe_linear_cost(const qe_linear* lin, int32_t T, int32_t n_distinct_experts, 
  * corrections are added: each routed expert is fitted to the error of its own cluster of
  * channels, so the two corrections are complementary (the pages give no combining rule).
  * qe_linear_forward_top2: y as qe_linear_forward plus (x A_e2) B_e2 for the second expert e2 =
- *   the smallest score among the experts other than the forward's first expert.  Requires
- *   n_routed >= 2, T <= 65535.  expert_out / expert2_out: optional device int32 [T].  ws:
- *   qe_top2_workspace_bytes(lin, T) bytes (qe_workspace_bytes' layout plus the scores and the
- *   second expert's grouping).  Enqueued; errors as qe_linear_forward.
+ *   the smallest score among the experts other than the forward's first expert (both taken
+ *   from the same router scores where the main product runs unsplit on 128-token tiles, which
+ *   then adds both corrections in its epilogue).  Requires n_routed >= 2, T <= 65535.
+ *   expert_out / expert2_out: optional device int32 [T].  ws: qe_top2_workspace_bytes(lin, T)
+ *   bytes (qe_workspace_bytes' layout plus the routes, scores, the second expert's grouping
+ *   and its adapter input).  Enqueued; errors as qe_linear_forward.
  */
 size_t qe_top2_workspace_bytes(const qe_linear* lin, int32_t T);
 int qe_linear_forward_top2(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, float* y,
