@@ -131,3 +131,24 @@ def test_top2_fused_epilogue_internvl2_8b_q(Q, T, x_f32):
     toks = np.unique(np.concatenate([np.arange(0, 130), np.arange(T - 70, T), rng.choice(T, 150, replace=False)]))
     err, agree = _check(Q, params, x, cfg.w_bits, cfg.a_bits, tokens=toks)
     print(f"8B q top-2 (T {T}, float32 x {x_f32}): err {err:.2e}, pairs equal {agree:.3f}")
+
+
+@pytest.mark.parametrize("r_s,n_r,r_r", [(0, 8, 32), (8, 16, 16), (32, 2, 32)])
+def test_top2_fused_epilogue_adapter_layouts(Q, r_s, n_r, r_r):
+    """The fused top-2 path over adapter layouts: no shared expert, the most experts (16, so
+    the epilogue takes eight rounds of two) with a rank padded from 16 to 32, and two experts
+    (every token takes both).  4096 tokens x 4096 channels: 512 tiles of 128 tokens."""
+    rng = np.random.default_rng(11 + r_s + n_r)
+    d_in, d_out, T = 1024, 4096, 4096
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    params = dict(W_f=(rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32),
+                  s=rng.uniform(0.5, 2, d_in).astype(np.float32),
+                  A_s=bf(rng.standard_normal((d_in, r_s)) * 0.02) if r_s else None,
+                  B_s=bf(rng.standard_normal((r_s, d_out)) * 0.02) if r_s else None,
+                  A_r=bf(rng.standard_normal((n_r, d_in, r_r)) * 0.02),
+                  B_r=bf(rng.standard_normal((n_r, r_r, d_out)) * 0.02),
+                  R=bf(rng.standard_normal((d_in, n_r)) * 0.02))
+    x = torch.from_numpy((rng.standard_normal((T, d_in)) * 2).astype(np.float32)).to(torch.bfloat16)
+    toks = np.unique(np.concatenate([np.arange(0, 64), np.arange(T - 64, T), rng.choice(T, 120, replace=False)]))
+    err, agree = _check(Q, params, x, 4, 8, tokens=toks)
+    print(f"top-2 fused r_s {r_s} N_r {n_r} r_r {r_r}: err {err:.2e}, pairs equal {agree:.3f}")
