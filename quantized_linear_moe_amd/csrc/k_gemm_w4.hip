@@ -28,7 +28,10 @@
 //     experts instead of all of them.
 //   * Epilogue: int32 -> float, scale by s_x and s_w, then bf16 MFMA
 //     16x16x32 steps accumulate u.B_s and, for every routed expert present in
-//     the tile, (v masked to that expert's tokens).B_e on top of it.
+//     the tile, (v masked to that expert's tokens).B_e on top of it; the tile
+//     stays in registers through the expert rounds and leaves as whole 128-byte
+//     lines (a wave-private LDS transpose) with non-temporal stores.  Top-2
+//     routing adds each token's second expert in the same rounds.
 //   * Few tokens (a grid far below the CU count): the K steps are split over
 //     gridDim.y workgroups that store their exact int32 partial sums; a finish
 //     kernel adds them in split order (still exact) and applies the epilogue.
@@ -345,9 +348,8 @@ __device__ __attribute__((always_inline)) inline void gemm_w4_tile(
     // operands of the adapter MFMAs are rows (m*16 + lr).
     //
     // Common case (kFast): every operand is read from LDS (loaded into the ring as set out
-    // above); each 16-row block is dequantized, corrected and stored.  A tile with more
-    // experts than one round holds adds the rest in further rounds, reading back the y rows
-    // it stored.
+    // above); the tile is dequantized and corrected in registers, round by round of experts,
+    // then stored.
     if constexpr (kFast) {
         QE_WAIT_VMCNT_LDS(0);
         QE_WG_BARRIER();  // every wave is done with the ring; the tail's copies have landed
