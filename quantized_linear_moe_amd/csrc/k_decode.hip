@@ -320,35 +320,55 @@ hipError_t launch_decode_gemv(const void* x, int x_dtype, const int8_t* codes, i
     return hipGetLastError();
 }
 
-// Finish of the fused decode.  Every workgroup first turns the projection partials into the
-// routed expert of each token (argmin of the router scores, lowest index on ties) and the bf16
-// adapter inputs u (shared expert) and v (the token's routed expert), then writes, for its 64
-// channels and all tokens (wave w handles tokens w and w + 8),
+// Finish of the fused decode.  Every workgroup turns the projection partials into the routed
+// expert of each token (argmin of the router scores, lowest index on ties) and the bf16 adapter
+// inputs u (shared expert) and v (the token's routed expert), then writes, for its CH channels
+// and all tokens (thread (c, ts) takes channel c of the group and tokens ts, ts + 512/CH, ...),
 //   y[t][i] = s_w[i] * sum_ks part_m[ks][t][i] + u[t].Bt_s[i] + v[t].Bt_r[e_t][i]
 // or, with quantized activations (s_x != NULL, int32 main partials),
 //   y[t][i] = (float)(sum_ks part_m[ks][t][i]) * s_x[t] * s_w[i] + (the same adapter terms).
-// Partials are summed in split order; their loads are issued in independent batches of 16 (a
-// dependent chain of loads would cost one memory latency per split), and the phases are
-// ordered so that about three memory latencies are exposed.
-constexpr int DF_CH = 64;
+// Partials are summed in split order.  Two memory rounds are exposed: first everything that
+// needs no route (the thread's main partials and shared-expert row, kept in registers, and the
+// router and u partials, summed into LDS), then, after one barrier, each thread takes the routes
+// of its tokens from the scores in LDS and requests their routed-expert rows together with the
+// v partials (measured no faster than the three rounds of loading each phase's operands
+// after the previous barrier).  CH is 64 or 32 so that narrower outputs still give every
+// compute unit a workgroup.
 constexpr int DF_THREADS = 512;
 
-__global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
+// CH channels per workgroup; KR = 4 or 8: adapter ranks up to 32 or 64 (the register rows' size)
+template <int CH, int KR>
+__global__ __launch_bounds__(DF_THREADS, KR == 4 ? 4 : 2) void decode_finish_kernel(
     const float* __restrict__ part_m, const float* __restrict__ s_x, int ks_m, int T, int d_out,
     const float* __restrict__ w_scale,
     const float* __restrict__ part_p, int ks_p, int ncp, int col_se, int r_s, int rs_pad, int col_re, int n_r,
     int r_r, int rr_pad, int col_router, const uint16_t* __restrict__ bt_s, const uint16_t* __restrict__ bt_r,
     int32_t* __restrict__ expert_out, float* __restrict__ y, bool y_bf16) {
+    constexpr int TS = DF_THREADS / CH;  // token slots
+    constexpr int NH = (16 + TS - 1) / TS;  // tokens per thread at T = 16
+    constexpr int MP = NH == 1 ? 16 : 4;     // main partials per output requested ahead (the rest after)
     __shared__ float s_sc[16][kMaxRouted];
-    __shared__ int s_e[16];
     __shared__ float s_u[16][kMaxRank];
     __shared__ float s_v[16][kMaxRank];
     const int tid = threadIdx.x;
-    const int c = tid & (DF_CH - 1), t = tid >> 6;  // wave t: tokens t and t + 8
-    const int i = min(blockIdx.x * DF_CH + c, d_out - 1);
-    const size_t pstride = (size_t)T * ncp;
+    const int c = tid % CH, ts = tid / CH;
+    const int i = min(blockIdx.x * CH + c, d_out - 1);
+    const size_t pstride = (size_t)T * ncp, mstride = (size_t)T * d_out;
 
-    // 1. router scores and u (independent of each other)
+    // 1. no route needed: main partials and the shared-expert row (registers), then the router
+    //    scores and u (LDS)
+    float pm[NH][MP];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+        const int tt = min(ts + TS * h, T - 1);
+#pragma unroll
+        for (int q = 0; q < MP; ++q)
+            pm[h][q] = (ts + TS * h < T && q < ks_m) ? part_m[(size_t)q * mstride + (size_t)tt * d_out + i] : 0.0f;
+    }
+    v4u bs[KR];
+#pragma unroll
+    for (int q = 0; q < KR; ++q)
+        bs[q] = 8 * q < rs_pad ? *reinterpret_cast<const v4u*>(bt_s + (size_t)i * rs_pad + 8 * q) : v4u{0, 0, 0, 0};
     const int nsc = T * n_r, nu = T * rs_pad;
     for (int it = tid; it < nsc + nu; it += DF_THREADS) {
         if (it < nsc) {
@@ -361,59 +381,66 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
         }
     }
     __syncthreads();
-    // 2. the routed expert of each token
-    if (n_r > 0 && tid < T) {
+
+    // 2. routes from the scores (strict <: the lowest index wins ties), the routed rows of the
+    //    thread's tokens (registers) and v of every token's expert (LDS)
+    auto route = [&](int tt) {
         int e = 0;
-        float best = s_sc[tid][0];
+        float best = s_sc[tt][0];
         for (int j = 1; j < n_r; ++j)
-            if (s_sc[tid][j] < best) {  // strict: the lowest index wins ties
-                best = s_sc[tid][j];
+            if (s_sc[tt][j] < best) {
+                best = s_sc[tt][j];
                 e = j;
             }
-        s_e[tid] = e;
-        if (expert_out && blockIdx.x == 0) expert_out[tid] = e;
-    }
-    __syncthreads();
-    // 3. v of the selected experts, the shared-expert row and the main-weight sum
-    for (int it = tid; it < T * rr_pad; it += DF_THREADS) {
-        const int tt = it / rr_pad, m = it % rr_pad;
-        const float a =
-            m < r_r ? sum_splits(part_p + (size_t)tt * ncp + col_re + s_e[tt] * rr_pad + m, pstride, ks_p) : 0.0f;
-        s_v[tt][m] = __uint_as_float(f32_to_bf16_bits(a) << 16);
-    }
-    v4u bs[kMaxRank / 8];
+        return e;
+    };
+    int eh[NH];
+    v4u br[NH][KR];
 #pragma unroll
-    for (int q = 0; q < kMaxRank / 8; ++q)
-        bs[q] = 8 * q < rs_pad ? *reinterpret_cast<const v4u*>(bt_s + (size_t)i * rs_pad + 8 * q) : v4u{0, 0, 0, 0};
-    float out[2];
+    for (int h = 0; h < NH; ++h) {
+        const int tt = ts + TS * h;
+        eh[h] = (n_r > 0 && tt < T) ? route(tt) : -1;
+        const uint16_t* row = bt_r + ((size_t)max(eh[h], 0) * d_out + i) * rr_pad;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int tt = t + 8 * h;
-        if (tt >= T) {
-            out[h] = 0.0f;
-        } else if (s_x) {
-            const int32_t acc =
-                sum_splits_i32(reinterpret_cast<const int32_t*>(part_m) + (size_t)tt * d_out + i, (size_t)T * d_out, ks_m);
-            out[h] = (float)acc * s_x[tt] * w_scale[i];
-        } else {
-            out[h] = sum_splits(part_m + (size_t)tt * d_out + i, (size_t)T * d_out, ks_m) * w_scale[i];
+        for (int q = 0; q < KR; ++q)
+            br[h][q] = (eh[h] >= 0 && 8 * q < rr_pad) ? *reinterpret_cast<const v4u*>(row + 8 * q) : v4u{0, 0, 0, 0};
+    }
+    if (n_r > 0 && expert_out && blockIdx.x == 0 && tid < T) expert_out[tid] = route(tid);
+    if (n_r > 0) {
+        for (int it = tid; it < T * rr_pad; it += DF_THREADS) {
+            const int tt = it / rr_pad, m = it % rr_pad;
+            const float a =
+                m < r_r ? sum_splits(part_p + (size_t)tt * ncp + col_re + route(tt) * rr_pad + m, pstride, ks_p) : 0.0f;
+            s_v[tt][m] = __uint_as_float(f32_to_bf16_bits(a) << 16);
         }
     }
     __syncthreads();
-    // 4. the routed expert's row, then the two dot products
+
+    // 3. the main term (split order), the two dot products, the output
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int tt = t + 8 * h;
-        if (tt >= T) break;  // wave-uniform; no barrier follows
-        const int e = n_r > 0 ? s_e[tt] : -1;
-        v4u br[kMaxRank / 8];
-        const uint16_t* row = bt_r + ((size_t)max(e, 0) * d_out + i) * rr_pad;
+    for (int h = 0; h < NH; ++h) {
+        const int tt = ts + TS * h;
+        if (tt >= T) break;  // no barrier follows
+        float main;
+        if (s_x) {
+            int32_t acc = 0;
 #pragma unroll
-        for (int q = 0; q < kMaxRank / 8; ++q)
-            br[q] = (e >= 0 && 8 * q < rr_pad) ? *reinterpret_cast<const v4u*>(row + 8 * q) : v4u{0, 0, 0, 0};
+            for (int q = 0; q < MP; ++q) acc += __float_as_int(pm[h][q]);
+            if (ks_m > MP)
+                acc += sum_splits_i32(reinterpret_cast<const int32_t*>(part_m) + MP * mstride + (size_t)tt * d_out + i,
+                                      mstride, ks_m - MP);
+            main = (float)acc * s_x[tt] * w_scale[i];
+        } else {
+            float sum = 0.0f;
+#pragma unroll
+            for (int q = 0; q < MP; ++q)
+                if (q < ks_m) sum += pm[h][q];
+            for (int q = MP; q < ks_m; ++q) sum += part_m[(size_t)q * mstride + (size_t)tt * d_out + i];
+            main = sum * w_scale[i];
+        }
         float du = 0.0f, dv = 0.0f;
 #pragma unroll
-        for (int q = 0; q < kMaxRank / 8; ++q) {
+        for (int q = 0; q < KR; ++q) {
             if (8 * q >= rs_pad) break;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -421,20 +448,25 @@ __global__ __launch_bounds__(DF_THREADS) void decode_finish_kernel(
                 du = __builtin_fmaf(s_u[tt][8 * q + 2 * k + 1], __uint_as_float(bs[q][k] & 0xFFFF0000u), du);
             }
         }
-        if (e >= 0) {
+        if (eh[h] >= 0) {
 #pragma unroll
-            for (int q = 0; q < kMaxRank / 8; ++q) {
+            for (int q = 0; q < KR; ++q) {
                 if (8 * q >= rr_pad) break;
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
-                    dv = __builtin_fmaf(s_v[tt][8 * q + 2 * k], __uint_as_float(br[q][k] << 16), dv);
-                    dv = __builtin_fmaf(s_v[tt][8 * q + 2 * k + 1], __uint_as_float(br[q][k] & 0xFFFF0000u), dv);
+                    dv = __builtin_fmaf(s_v[tt][8 * q + 2 * k], __uint_as_float(br[h][q][k] << 16), dv);
+                    dv = __builtin_fmaf(s_v[tt][8 * q + 2 * k + 1], __uint_as_float(br[h][q][k] & 0xFFFF0000u), dv);
                 }
             }
         }
-        if (blockIdx.x * DF_CH + c < d_out) store_y(y, (size_t)tt * d_out + i, (out[h] + du) + dv, y_bf16);
+        if (blockIdx.x * CH + c < d_out) store_y(y, (size_t)tt * d_out + i, (main + du) + dv, y_bf16);
     }
 }
+
+// channels per workgroup: 64, or 32 when 64 would leave compute units without a workgroup
+// (the 8192-wide outputs: 256 workgroups instead of 128, measured 1.4 us faster per call;
+// 32 for the 29568-wide outputs doubles the grid past one round and is slower)
+int decode_finish_channels(int d_out) { return (d_out + 63) / 64 >= 256 ? 64 : 32; }
 
 hipError_t launch_decode_finish(const float* part_m, const float* s_x, int ks_m, int T, int d_out,
                                 const float* w_scale, const float* part_p, int ks_p, int ncp, int col_se, int r_s,
@@ -443,9 +475,20 @@ hipError_t launch_decode_finish(const float* part_m, const float* s_x, int ks_m,
                                 bool y_bf16, hipStream_t st) {
     if (T <= 0) return hipSuccess;
     if (T > 16 || n_r > kMaxRouted || rs_pad > kMaxRank || rr_pad > kMaxRank) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(decode_finish_kernel, dim3((d_out + DF_CH - 1) / DF_CH), dim3(DF_THREADS), 0, st, part_m, s_x,
-                       ks_m, T, d_out, w_scale, part_p, ks_p, ncp, col_se, r_s, rs_pad, col_re, n_r, r_r, rr_pad, col_router,
-                       bt_s, bt_r, expert_out, y, y_bf16);
+    const int ch = decode_finish_channels(d_out);
+    const bool wide = rs_pad > 32 || rr_pad > 32;
+#define QE_DF_LAUNCH(CHV, KRV)                                                                                     \
+    hipLaunchKernelGGL((decode_finish_kernel<CHV, KRV>), dim3((d_out + CHV - 1) / CHV), dim3(DF_THREADS), 0, st,   \
+                       part_m, s_x, ks_m, T, d_out, w_scale, part_p, ks_p, ncp, col_se, r_s, rs_pad, col_re, n_r,  \
+                       r_r, rr_pad, col_router, bt_s, bt_r, expert_out, y, y_bf16)
+    if (ch == 64) {
+        if (wide) QE_DF_LAUNCH(64, 8);
+        else QE_DF_LAUNCH(64, 4);
+    } else {
+        if (wide) QE_DF_LAUNCH(32, 8);
+        else QE_DF_LAUNCH(32, 4);
+    }
+#undef QE_DF_LAUNCH
     return hipGetLastError();
 }
 
