@@ -1,8 +1,9 @@
 """GPU parity of the decode path (T <= 16: one launch streams the projection matrix and the packed
 weights, one finish launch routes and adds the adapter terms) over every adapter layout the
 finish takes: no adapters at all, shared only, routed only, the largest ranks and expert count at
-16 tokens, quantized activations (int32 partials), a partial last channel group, and long K
-(many K splits per channel group)."""
+16 tokens, quantized activations (int32 partials), a partial last channel group, long K
+(many K splits per channel group), and outputs wide enough for the finish's 64-channel
+workgroups."""
 
 import numpy as np
 import pytest
@@ -40,6 +41,12 @@ CASES = [  # w_bits, a_bits, T, r_s, n_r, r_r, d_in, d_out
     (4, 6, 5, 64, 16, 64, 1024, 784),     # quantized activations (int32 partials)
     (4, 8, 16, 8, 2, 8, 2048, 1024),
     (3, 16, 3, 8, 4, 8, 29568, 256),      # long K: many main K splits per channel group
+    # outputs of 16384 channels and more: the finish's 64-channel workgroups (two token slots per
+    # thread past 8 tokens, main partials past the four requested ahead, rank-64 register rows)
+    (3, 16, 16, 32, 8, 32, 1024, 16384),
+    (4, 16, 11, 64, 16, 64, 1024, 16400),  # ragged last channel group, rank 64
+    (4, 6, 16, 32, 8, 32, 4096, 16384),    # int32 partials
+    (3, 16, 13, 0, 8, 32, 4096, 18944),    # routed experts only
 ]
 
 
