@@ -945,6 +945,247 @@ hipError_t launch_route_finish(const float* part, const float* amax_part, int ks
     return hipGetLastError();
 }
 
+// ---- few-token prologue
+// For up to 128 tokens (256 without a shared expert) the two passes above run a few dozen
+// workgroups each, and their four launches (route pass, route finish, expert-sorted pass, v
+// finish) cost more than the work.  Here one launch does it all, one workgroup per token (plus
+// one more for u when there is a shared expert), with no partials leaving the workgroup:
+//   blockIdx.y == 0: x' = x / s and max |x'| (one 8-channel chunk per thread), s_x and the
+//     codes; the router scores x.R and their argmin (lowest index on ties); then v = x.A_e
+//     for the chosen expert;
+//   blockIdx.y == 1: u = x.A_s.
+// The token's row is staged in LDS once.  The projections run on bf16 MFMA with the token as
+// row 0 of A (the other rows zero): wave w takes the 128-channel groups w, w + 16, ..., lane
+// (column l%16, g = l/16) channels 32g .. 32g+31 of each group, 8 per step (any order A and B
+// share), so a lane reads 64 contiguous bytes of a projection row per group; the waves' sums
+// are added in wave order.  The router's (and u's first) weight fragments are requested with
+// the row, before the barrier that publishes it, so two memory rounds are exposed: the row
+// with the router weights, then the chosen expert's weights.  Each workgroup streams the
+// projection rows it needs once (16 + 32 rows of d_in bf16 values for 8 experts of rank 32),
+// which bounds d_in.
+constexpr int RW_THREADS = 1024;
+constexpr int RW_WAVES = RW_THREADS / 64;
+constexpr int RW_MAX_WG = 256;                      // workgroups of one launch (one round)
+constexpr int RW_MAX_DIN = RW_THREADS * 8;          // one chunk of 8 channels per thread
+constexpr int RW_GPW = RW_MAX_DIN / 128 / RW_WAVES;  // channel groups per wave at the widest
+
+// weight fragments of NG of this wave's groups (its groups i0 .. i0 + NG - 1; a group past the
+// range repeats the last one and is not used): NB blocks of 16 rows
+template <int NB, int NG>
+__device__ __forceinline__ void row_load_b(const uint16_t* __restrict__ rows, int d_in, int wid, int lane, int i0,
+                                           v4u (&b)[NG][NB][4]) {
+    const int lr = lane & 15, lg = lane >> 4, ngr = d_in >> 7;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        const size_t k0 = (size_t)min(wid + RW_WAVES * (i0 + i), ngr - 1) * 128 + lg * 32;
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                b[i][n][s] = *reinterpret_cast<const v4u*>(rows + (size_t)(n * 16 + lr) * d_in + k0 + 8 * s);
+    }
+}
+
+// acc[n] += the token row (LDS) . those fragments, for the groups that exist
+template <int NB, int NG>
+__device__ __forceinline__ void row_mma(const uint16_t* xl, int d_in, int wid, int lane, int i0,
+                                        const v4u (&b)[NG][NB][4], v4f (&acc)[NB]) {
+    const int lr = lane & 15, lg = lane >> 4, ngr = d_in >> 7;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+        const int g = wid + RW_WAVES * (i0 + i);
+        if (g >= ngr) break;  // uniform in the wave
+        const uint16_t* xp = xl + g * 128 + lg * 32;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const v4u w = *reinterpret_cast<const v4u*>(xp + 8 * s);
+            const v4u a = lr == 0 ? w : v4u{0, 0, 0, 0};
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+                acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const v8bf*>(&a),
+                                                                 *reinterpret_cast<const v8bf*>(&b[i][n][s]), acc[n], 0,
+                                                                 0, 0);
+        }
+    }
+}
+
+// this wave's share of the projection onto NB*16 rows, NG groups' fragments in flight at a time
+// (the first batch may already be in b)
+template <int NB, int NG>
+__device__ __forceinline__ void row_project(const uint16_t* __restrict__ rows, const uint16_t* xl, int d_in, int wid,
+                                            int lane, v4u (&b)[NG][NB][4], bool first_loaded, v4f (&acc)[NB]) {
+    const int ngr = d_in >> 7;
+    const int my = wid < ngr ? (ngr - 1 - wid) / RW_WAVES + 1 : 0;  // this wave's groups
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] = v4f{0, 0, 0, 0};
+    for (int i0 = 0; i0 < my; i0 += NG) {
+        if (i0 > 0 || !first_loaded) row_load_b<NB, NG>(rows, d_in, wid, lane, i0, b);
+        row_mma<NB, NG>(xl, d_in, wid, lane, i0, b, acc);
+    }
+}
+
+// NBS, NBR: 16-column blocks of u (rs_pad / 16) and of v (rr_pad / 16)
+template <int NBS, int NBR>
+__global__ __launch_bounds__(RW_THREADS) void row_prologue_kernel(
+    const uint16_t* __restrict__ x, int d_in, const float* __restrict__ smooth, const float* __restrict__ inv_smooth,
+    int qmax, const uint16_t* __restrict__ mt, int r_s, int col_router, int n_r, int col_re, int r_r,
+    int8_t* __restrict__ codes, float* __restrict__ s_x, uint16_t* __restrict__ u, int32_t* __restrict__ expert,
+    uint16_t* __restrict__ v) {
+    __shared__ __attribute__((aligned(16))) uint16_t xl[RW_MAX_DIN];
+    __shared__ float s_part[RW_WAVES][64];
+    __shared__ float s_vpart[RW_WAVES][64];
+    __shared__ float s_max[RW_WAVES];
+    __shared__ float s_sc[16];
+    const int t = blockIdx.x;
+    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const uint16_t* xrow = x + (size_t)t * d_in;
+    const int nch = d_in >> 3;
+    const int c = min(tid, nch - 1);  // threads past the row repeat its last chunk (not used)
+    const v4u w = *reinterpret_cast<const v4u*>(xrow + (size_t)c * 8);
+
+    if (blockIdx.y == 1) {  // the shared expert's input
+        if constexpr (NBS > 0) {
+            constexpr int NG = NBS == 2 ? 2 : 1;
+            v4u b[NG][NBS][4];
+            row_load_b<NBS, NG>(mt, d_in, wid, lane, 0, b);
+            if (tid < nch) *reinterpret_cast<v4u*>(xl + tid * 8) = w;
+            QE_WAIT_LDS();
+            QE_WG_BARRIER();
+            v4f acc[NBS];
+            row_project<NBS, NG>(mt, xl, d_in, wid, lane, b, true, acc);
+            if (lg == 0) {
+#pragma unroll
+                for (int n = 0; n < NBS; ++n) s_part[wid][n * 16 + lr] = acc[n][0];
+            }
+            QE_WAIT_LDS();
+            QE_WG_BARRIER();
+            if (tid < NBS * 16) {
+                float a = 0.0f;
+#pragma unroll
+                for (int q = 0; q < RW_WAVES; ++q) a += s_part[q][tid];
+                u[(size_t)t * (NBS * 16) + tid] = tid < r_s ? (uint16_t)f32_to_bf16_bits(a) : (uint16_t)0;
+            }
+        }
+        return;
+    }
+
+    // the row's chunk and smoothing factors, and the router's weight fragments, in one round
+    const v4f s0 = *reinterpret_cast<const v4f*>(smooth + c * 8), s1 = *reinterpret_cast<const v4f*>(smooth + c * 8 + 4);
+    const v4f i0 = *reinterpret_cast<const v4f*>(inv_smooth + c * 8),
+              i1 = *reinterpret_cast<const v4f*>(inv_smooth + c * 8 + 4);
+    v4u rb[RW_GPW][1][4];
+    if constexpr (NBR > 0) row_load_b<1, RW_GPW>(mt + (size_t)col_router * d_in, d_in, wid, lane, 0, rb);
+    if (tid < nch) *reinterpret_cast<v4u*>(xl + tid * 8) = w;
+    float xs[8];
+    smooth_div8(w, s0, s1, i0, i1, xs);
+    float amax = 0.0f;
+    if (tid < nch) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, __builtin_fabsf(xs[e]));
+    }
+    amax = wave_max(amax);
+    if (lane == 0) s_max[wid] = amax;
+    QE_WAIT_LDS();
+    QE_WG_BARRIER();  // the row and the maxima are in LDS; the router's fragments stay in flight
+
+    if constexpr (NBR > 0) {  // router scores (the router block is 16 rows)
+        v4f racc[1];
+        row_project<1, RW_GPW>(mt + (size_t)col_router * d_in, xl, d_in, wid, lane, rb, true, racc);
+        if (lg == 0) s_part[wid][lr] = racc[0][0];
+    }
+    // s_x = max |x'| / qmax (a max is exact in any order), then the codes
+    float m = s_max[0];
+#pragma unroll
+    for (int q = 1; q < RW_WAVES; ++q) m = fmaxf(m, s_max[q]);
+    const float sx = m / (float)qmax;
+    if (tid == 0) s_x[t] = sx;
+    const float inv_sx = sx != 0.0f ? 1.0f / sx : 0.0f;
+    const bool fast = (sx >= 0x1p-90f && sx <= 0x1p90f) || sx == 0.0f;
+    const v2u cw = codes8(xs, sx, inv_sx, fast, (float)qmax);
+    if (tid < nch) *reinterpret_cast<v2u*>(codes + (size_t)t * d_in + (size_t)tid * 8) = cw;
+
+    if constexpr (NBR > 0) {
+        // scores summed in wave order by one thread each; then every thread takes the argmin
+        // (strict <: the lowest index wins ties).  The barriers order LDS only: the codes'
+        // stores need not have landed.
+        QE_WAIT_LDS();
+        QE_WG_BARRIER();
+        if (tid < n_r) {
+            float a = 0.0f;
+#pragma unroll
+            for (int q = 0; q < RW_WAVES; ++q) a += s_part[q][tid];
+            s_sc[tid] = a;
+        }
+        QE_WAIT_LDS();
+        QE_WG_BARRIER();
+        int e = 0;
+        float best = s_sc[0];
+        for (int j = 1; j < n_r; ++j) {
+            const float sc = s_sc[j];
+            if (sc < best) {
+                best = sc;
+                e = j;
+            }
+        }
+        if (tid == 0) expert[t] = e;
+        constexpr int NG = NBR == 2 ? 2 : 1;
+        v4u b[NG][NBR][4];
+        v4f vacc[NBR];
+        row_project<NBR, NG>(mt + (size_t)(col_re + e * NBR * 16) * d_in, xl, d_in, wid, lane, b, false, vacc);
+        if (lg == 0) {
+#pragma unroll
+            for (int n = 0; n < NBR; ++n) s_vpart[wid][n * 16 + lr] = vacc[n][0];
+        }
+        QE_WAIT_LDS();
+        QE_WG_BARRIER();
+        if (tid < NBR * 16) {
+            float a = 0.0f;
+#pragma unroll
+            for (int q = 0; q < RW_WAVES; ++q) a += s_vpart[q][tid];
+            v[(size_t)t * (NBR * 16) + tid] = tid < r_r ? (uint16_t)f32_to_bf16_bits(a) : (uint16_t)0;
+        }
+    }
+}
+
+// Shapes it takes: every workgroup resident at once (one 1024-thread workgroup per compute unit
+// at its register count: a second round of workgroups was measured slower than the two passes)
+bool row_prologue_ok(int T, int d_in, int rs_pad, int n_r, int rr_pad) {
+    const bool rs_ok = rs_pad == 0 || rs_pad == 32 || rs_pad == 64;
+    const bool re_ok = n_r == 0 ? rr_pad == 0 : (n_r <= 16 && (rr_pad == 32 || rr_pad == 64));
+    return T > 0 && T * (rs_pad > 0 ? 2 : 1) <= RW_MAX_WG && d_in > 0 && d_in % 128 == 0 && d_in <= RW_MAX_DIN &&
+           rs_ok && re_ok;
+}
+
+hipError_t launch_row_prologue(const uint16_t* x, int T, int d_in, const float* smooth, const float* inv_smooth,
+                               int a_bits, const uint16_t* mt, int r_s, int rs_pad, int col_router, int n_r, int col_re,
+                               int r_r, int rr_pad, int8_t* codes, float* s_x, uint16_t* u, int32_t* expert,
+                               uint16_t* v, hipStream_t st) {
+    if (T <= 0) return hipSuccess;
+    if (!row_prologue_ok(T, d_in, rs_pad, n_r, rr_pad) || !x || !smooth || !inv_smooth || !mt || !codes || !s_x ||
+        (rs_pad > 0 && !u) || (n_r > 0 && (!expert || !v || col_router < 0 || col_re < 0)) || a_bits < 2 ||
+        a_bits > 8)
+        return hipErrorInvalidValue;
+    const dim3 grid(T, rs_pad > 0 ? 2 : 1);
+    const int qmax = (1 << (a_bits - 1)) - 1;
+#define QE_RW_LAUNCH(S, R)                                                                                       \
+    hipLaunchKernelGGL((row_prologue_kernel<S, R>), grid, dim3(RW_THREADS), 0, st, x, d_in, smooth, inv_smooth, \
+                       qmax, mt, r_s, col_router, n_r, col_re, r_r, codes, s_x, u, expert, v)
+#define QE_RW_BY_R(S)                      \
+    if (rr_pad == 0) QE_RW_LAUNCH(S, 0);   \
+    else if (rr_pad == 32) QE_RW_LAUNCH(S, 2); \
+    else QE_RW_LAUNCH(S, 4);
+    if (rs_pad == 0) {
+        QE_RW_BY_R(0)
+    } else if (rs_pad == 32) {
+        QE_RW_BY_R(2)
+    } else {
+        QE_RW_BY_R(4)
+    }
+#undef QE_RW_BY_R
+#undef QE_RW_LAUNCH
+    return hipGetLastError();
+}
+
 // ---- pass 2
 // A workgroup takes 128 token rows of the expert-sorted order, one 16-row block per
 // wave, and a K range walked in groups of 128 channels (four 32-wide

@@ -124,6 +124,12 @@ int noalloc_scratch(void** out);
 // Prefill prologue in two reads of x (route pass, then expert-sorted quantization), for
 // bf16 activations; the workspace is sized for it whatever the activation type
 bool two_pass_sized(const qe_linear* lin, int T) { return lin->a_bits != 16 && T > kSkinnyMaxT; }
+// few-token prefill with bf16 x: the one-launch prologue where its shape limits allow
+bool row_prologue(const qe_linear* lin, int T, int x_dtype) {
+    return two_pass_sized(lin, T) && x_dtype == QE_BF16 &&
+           row_prologue_ok(T, lin->d_in, rank_pad(lin->r_shared), lin->n_routed,
+                           lin->n_routed > 0 ? rank_pad(lin->r_routed) : 0);
+}
 }  // namespace qe
 
 namespace qe {
@@ -577,6 +583,19 @@ static int run_prologue(const qe_linear* lin, const void* x, int x_dtype, int T,
     const PrepLayout P = prep_layout(lin);
     const WsLayout W = ws_layout(lin, T);
     const bool route = lin->n_routed > 0;
+    if (row_prologue(lin, T, x_dtype) && !expert2) {
+        // few tokens: one launch, everything in token order; the expert order the GEMM's tiles
+        // walk (when it is asked for) comes from the bucketing kernel
+        QE_TRY_HIP(launch_row_prologue(reinterpret_cast<const uint16_t*>(x), T, lin->d_in,
+                                       at<const float>(lin->prep, P.smooth), at<const float>(lin->prep, P.inv_smooth),
+                                       lin->a_bits, at<const uint16_t>(lin->prep, P.mt), lin->r_shared, P.rs_pad,
+                                       P.col_router, lin->n_routed, P.col_re, lin->r_routed, P.rr_pad, codes, s_x,
+                                       P.rs_pad > 0 ? u : nullptr, route ? expert : nullptr, route ? v : nullptr, s));
+        if (route && perm)
+            QE_TRY_HIP(launch_bucket(expert, T, lin->n_routed, at<int32_t>(ws, W.counts), at<int32_t>(ws, W.offsets),
+                                     perm, s));
+        return QE_OK;
+    }
     if (two_pass_sized(lin, T) && x_dtype == QE_BF16) {
         QE_TRY_HIP(launch_route_pass(reinterpret_cast<const uint16_t*>(x), T, lin->d_in,
                                      at<const uint16_t>(lin->prep, P.mt), P.n_lead, at<const float>(lin->prep, P.smooth),
@@ -671,7 +690,9 @@ int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int3
 static bool group_route_pass(const qe_linear* const* lins, int n, int x_dtype, int T) {
     if (n < 2 || n > RG_MAX || x_dtype != QE_BF16) return false;
     for (int i = 0; i < n; ++i) {
-        if (!two_pass_sized(lins[i], T) || lins[i]->d_in != lins[0]->d_in) return false;
+        // few tokens: each linear's one-launch prologue (bit-identical to a linear's own call)
+        if (!two_pass_sized(lins[i], T) || row_prologue(lins[i], T, x_dtype) || lins[i]->d_in != lins[0]->d_in)
+            return false;
         const int nl = prep_layout(lins[i]).n_lead;
         if (nl < 16 || nl > 48) return false;
     }

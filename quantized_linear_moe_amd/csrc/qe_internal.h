@@ -142,6 +142,13 @@ struct FinishGroup {
     FinishLinear lin[RG_MAX];
 };
 hipError_t launch_route_finish_group(const FinishGroup& G, int n_lin, int ksplit, int T, hipStream_t st);
+// Few-token prologue in one launch (one workgroup per token, one more for u): codes, s_x, u,
+// routes and v, all in token order; row_prologue_ok says which shapes it takes
+bool row_prologue_ok(int T, int d_in, int rs_pad, int n_r, int rr_pad);
+hipError_t launch_row_prologue(const uint16_t* x, int T, int d_in, const float* smooth, const float* inv_smooth,
+                               int a_bits, const uint16_t* mt, int r_s, int rs_pad, int col_router, int n_r, int col_re,
+                               int r_r, int rr_pad, int8_t* codes, float* s_x, uint16_t* u, int32_t* expert,
+                               uint16_t* v, hipStream_t st);
 struct EqLinear {
     const float* smooth;
     const float* inv_smooth;

@@ -34,7 +34,8 @@ def _layers(Q, cfg, names):
 # linear routed with the same rank); ragged token counts (2000, 300: the few-token form)
 CASES = [("qwen2vl_72b", ("q", "k", "v"), None), ("qwen2vl_72b", ("gate", "up"), None),
          ("qwen2vl_2b", ("q", "k", "v"), None), ("qwen2vl_2b", ("q", "k", "v"), 2000),
-         ("internvl2_8b", ("gate", "up"), 300), ("tiny", ("lin",), None)]
+         ("internvl2_8b", ("gate", "up"), 300), ("tiny", ("lin",), None),
+         ("qwen2vl_2b", ("q", "k", "v"), 200)]  # few tokens: each linear's one-launch prologue
 
 
 @pytest.mark.parametrize("cfg_name,names,T", CASES)
@@ -69,7 +70,8 @@ def test_group_prologue_matches_single_prologues(Q, cfg_name, names, T):
 @pytest.mark.parametrize("cfg_name,names,T,dtype", [("qwen2vl_72b", ("q", "k", "v"), None, None),
                                                     ("qwen2vl_72b", ("gate", "up"), 1024, None),
                                                     ("internvl2_8b", ("q", "k", "v"), 12, None),
-                                                    ("qwen2vl_2b", ("gate", "up"), 200, torch.float32)])
+                                                    ("qwen2vl_2b", ("gate", "up"), 200, torch.float32),
+                                                    ("internvl2_8b", ("q", "k", "v"), 160, None)])
 def test_group_forward_matches_single_forwards(Q, cfg_name, names, T, dtype):
     L = Q.libqe
     cfg = synth.get_config(cfg_name)

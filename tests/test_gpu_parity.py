@@ -377,6 +377,31 @@ def test_prologue_shapes(Q, T, r_s, n_r, r_r, x_dtype):
     _check_prologue(Q, layer, params, x, 6, n_r, r_s, r_r)
 
 
+# few-token prologue in one launch (bf16 x, d_in <= 8192, up to 128 tokens, or 256 without a shared
+# expert): widths from one channel group to the limit, A6/A8, ranks up to 64; and just past the token and
+# width limits, where the two passes take over
+@pytest.mark.parametrize("T,d_in,a_bits,r_s,n_r,r_r", [(128, 3584, 6, 32, 8, 32), (128, 8192, 8, 32, 8, 32),
+                                                       (33, 128, 8, 64, 16, 64), (97, 1024, 6, 0, 2, 8),
+                                                       (256, 3584, 8, 0, 8, 32), (256, 640, 8, 8, 0, 0),
+                                                       (129, 3584, 6, 32, 8, 32), (64, 8320, 6, 32, 8, 32)])
+def test_prologue_few_tokens(Q, T, d_in, a_bits, r_s, n_r, r_r):
+    rng = np.random.default_rng(T + d_in)
+    d_out = 256
+    bf = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16)
+    params = dict(W_f=(rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32),
+                  s=rng.uniform(0.5, 2, d_in).astype(np.float32),
+                  A_s=bf(rng.standard_normal((d_in, r_s)) * 0.02) if r_s else None,
+                  B_s=bf(rng.standard_normal((r_s, d_out)) * 0.02) if r_s else None,
+                  A_r=bf(rng.standard_normal((n_r, d_in, r_r)) * 0.02) if n_r else None,
+                  B_r=bf(rng.standard_normal((n_r, r_r, d_out)) * 0.02) if n_r else None,
+                  R=bf(rng.standard_normal((d_in, n_r)) * 0.02) if n_r else None)
+    x = rng.standard_normal((T, d_in)).astype(np.float32) * 2
+    x[:, rng.choice(d_in, 3, replace=False)] *= 25.0
+    x = torch.from_numpy(x).to(torch.bfloat16)
+    layer = Q.QELinear.from_params(params, 4, a_bits, device=DEV)
+    _check_prologue(Q, layer, params, x, a_bits, n_r, r_s, r_r)
+
+
 # ------------------------------------------------------------ a8 top-k
 @pytest.mark.parametrize("cfg_name,lin_name", [("tiny", "lin"), ("internvl2_8b", "q"), ("internvl2_8b", "down")])
 def test_channel_topk_bit_exact(Q, cfg_name, lin_name):
