@@ -224,7 +224,11 @@ int qe_routed_lora(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t
  * read of x for all projections.  Outputs (device, caller-owned): codes int8 [T][d_in] and
  * s_x float32 [T] (a_bits 6/8; both NULL for a_bits 16), u and v as for
  * qe_adapter_inputs (padded rows), expert int32 [T], and perm int32 [T] or NULL (tokens
- * sorted by (expert, token), as qe_route's).  Feed them to qe_wq_gemm.
+ * sorted by (expert, token), as qe_route's).  Feed them to qe_wq_gemm.  With bf16 x and more
+ * than 16 tokens it runs as two reads of x (scores, u and max |x/s|; then codes and v), or,
+ * for up to 128 tokens (256 without a shared expert) and d_in <= 8192, as one launch with a
+ * workgroup per token.  Codes and s_x do not depend on the form; the float32 sums behind the
+ * scores, u and v are added in another order (routes can differ only at near-ties).
  */
 int qe_linear_prologue(const qe_linear* lin, const void* x, int32_t x_dtype, int32_t T, int8_t* codes,
                        float* s_x, uint16_t* u, uint16_t* v, int32_t* expert, int32_t* perm,
@@ -248,7 +252,8 @@ int qe_linear_forward(const qe_linear* lin, const void* x, int32_t x_dtype, int3
  * ws_bytes[i] >= qe_workspace_bytes(lins[i], T) bytes, one workspace per linear.  Results are
  * identical, bit for bit, to calling qe_linear_prologue / qe_linear_forward on each linear in
  * turn, which is what happens when the group cannot share the pass (fewer than 2 linears,
- * float32 x, 16 tokens or fewer, weight-only linears, or more than 48 projected columns).
+ * float32 x, 16 tokens or fewer, weight-only linears, more than 48 projected columns, or few
+ * enough tokens for each linear's one-launch prologue: see qe_linear_prologue).
  * Errors as for the single-linear calls; any invalid entry fails the whole call before any
  * launch.
  */
