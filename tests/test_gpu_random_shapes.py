@@ -6,7 +6,9 @@ four K steps), 64-token tiles, K-split grids with their finish, the general epil
 adapters, A6/A8, bf16 and float32 activations, ragged token and channel counts.  A second sweep
 draws groups of linears that read one input (one launch over the group's tiles, the grouped
 prologue when every linear is routed with one rank, the per-linear fallback otherwise): each
-linear's y must match its own forward bit for bit and the oracle on sampled tokens."""
+linear's y must match its own forward bit for bit and the oracle on sampled tokens.  A third sweep
+draws few-token shapes (1 to 256 tokens, widths around the one-launch prologue's limit), checked on
+every token."""
 
 import numpy as np
 import pytest
@@ -135,3 +137,35 @@ def test_random_group_forward(Q, seed):
         ref = oracle_for(p, x, 4, a_bits, tokens=tok)
         err = check_y(b.cpu().numpy()[tok], ref, p, xs, 4, a_bits, gpu_expert=eb.cpu().numpy()[tok] if r else None)
         print(f"  linear {i}: max rel err {err:.2e}")
+
+
+def _few_case(seed):
+    rng = np.random.default_rng(3000 + seed)
+    # decode sizes, up to 128 tokens, 129 to 256 tokens in turn
+    T = int(rng.integers(*((1, 17), (17, 129), (129, 257))[seed % 3]))
+    d_in = int(rng.choice([128, 384, 1024, 2048, 3584, 4096, 8192, 8320]))
+    d_out = int(rng.integers(1, 64)) * 16
+    r_s, n_r, r_r = _adapters(rng)
+    a_bits = int(rng.choice([6, 8]))
+    return dict(T=T, d_in=d_in, d_out=d_out, r_s=r_s, n_r=n_r, r_r=r_r, a_bits=a_bits, rng=rng)
+
+
+# few tokens: the one-launch prologue (up to 128 tokens, or 256 without a shared expert, d_in <= 8192), the
+# two passes past those limits, and the fused decode at 16 tokens or fewer; bf16 x
+@pytest.mark.parametrize("seed", range(24))
+def test_random_few_token_forward(Q, seed):
+    c = _few_case(seed)
+    rng = c["rng"]
+    T, d_in, d_out, r_s, n_r, r_r = c["T"], c["d_in"], c["d_out"], c["r_s"], c["n_r"], c["r_r"]
+    print(f"few seed {seed}: T {T} d_in {d_in} d_out {d_out} r_s {r_s} N_r {n_r} r_r {r_r} A{c['a_bits']}", flush=True)
+    params = _params(rng, d_in, d_out, r_s, n_r, r_r)
+    x = _x(rng, T, d_in, torch.bfloat16)
+    layer = Q.QELinear.from_params(params, 4, c["a_bits"], device=DEV)
+    y = torch.full((T, d_out), float("nan"), dtype=torch.float32, device=DEV)
+    e = torch.empty(T, dtype=torch.int32, device=DEV)
+    Q.libqe.qe_linear_forward(layer.lin, x.to(DEV), y, e if n_r else None, layer.workspace(T))
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all(), "an output was not written"
+    ref = oracle_for(params, x, 4, c["a_bits"])
+    err = check_y(y.cpu().numpy(), ref, params, x, 4, c["a_bits"], gpu_expert=e.cpu().numpy() if n_r else None)
+    print(f"  max rel err {err:.2e}")
