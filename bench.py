@@ -446,6 +446,20 @@ def main():
     torch.cuda.synchronize()
     ms_step_fwd = s2.elapsed_time(e2) / K
 
+    # the same composite step captured once in a HIP graph and replayed K times (a serving loop's
+    # form: one launch of the whole step); every replay must reproduce the eager outputs bit for bit
+    ref_y = [bufs[i]["y"].clone() for i in range(len(layers))]
+    g_step = graph_of(torch, composite)
+    s3, e3 = ev_t(), ev_t()
+    s3.record()
+    for _ in range(K):
+        g_step.replay()
+    e3.record()
+    torch.cuda.synchronize()
+    ms_step_graph = s3.elapsed_time(e3) / K
+    graph_equal = all(torch.equal(bufs[i]["y"], ref_y[i]) for i in range(len(layers)))
+    del g_step, ref_y
+
     # ------------------------------------------------------------ accounting
     int_ops = adapter_flops = alg_bytes = 0.0
     per_linear, per_group = [], []
@@ -525,6 +539,8 @@ def main():
         "breakdown": {"gemm_ms_per_step": round(gemm_ms_step, 4),
                       "prologue_ms_per_step": round(ms_step - gemm_ms_step, 4),
                       "ms_per_step_composite_entry": round(ms_step_fwd, 4),
+                      "ms_per_step_composite_graph": round(ms_step_graph, 4),
+                      "graph_replays_bit_equal": bool(graph_equal),
                       "wall_s_timed_region": round(wall, 3),
                       "per_group": per_group, "per_linear": per_linear},
     }
@@ -590,6 +606,23 @@ def measured_peaks(torch, libqe, dev):
                       "(1 GiB read + 1 GiB write), median of 5"}
 
 
+def graph_of(torch, fn):
+    """fn (launches only: no allocation, copy or synchronization inside) captured once in a HIP
+    graph after warm-up calls on a side stream; returns the graph, replayed by the caller."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
 def layer_throughput(torch, synth, qe, libqe, dev, name, steps=10):
     """The composite entry point over every linear of a configuration, one stream, inputs resident:
     tokens/s, the int8 rate of the whole step and its fraction of the spec roofline."""
@@ -626,6 +659,16 @@ def layer_throughput(torch, synth, qe, libqe, dev, name, steps=10):
     b.record()
     torch.cuda.synchronize()
     t = a.elapsed_time(b) / steps * 1e-3
+    ref_y = [y.clone() for y in ys]
+    g = graph_of(torch, run)  # the same step as one HIP graph, replayed
+    a.record()
+    for _ in range(steps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    t_graph = a.elapsed_time(b) / steps * 1e-3
+    graph_equal = all(torch.equal(y, r) for y, r in zip(ys, ref_y))
+    del g, ref_y
     int_ops = adapter_flops = alg = 0.0
     for i, (spec, layer) in enumerate(layers):
         im, am, ab = libqe.qe_linear_cost(layer.lin, T, int(torch.unique(es[i]).numel()), 2)
@@ -636,6 +679,7 @@ def layer_throughput(torch, synth, qe, libqe, dev, name, steps=10):
     torch.cuda.empty_cache()
     return {"linears": [f"{s.name} {s.d_in}->{s.d_out}" for s in cfg.linears], "T": T,
             "w_bits": cfg.w_bits, "a_bits": cfg.a_bits, "us_per_step": round(t * 1e6, 2),
+            "us_per_step_graph": round(t_graph * 1e6, 2), "graph_replays_bit_equal": bool(graph_equal),
             "tokens_per_s": round(T / t, 1), "int8_tops": round(int_ops / t / 1e12, 1),
             "layer_roofline_frac": round(t_roof / t, 4)}
 
