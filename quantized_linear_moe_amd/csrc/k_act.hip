@@ -826,112 +826,103 @@ hipError_t launch_route_pass_group(const uint16_t* x, int T, int d_in, const Rou
     return hipGetLastError();
 }
 
-// One wave per token: fixed-order split-K sums, router argmin (lowest index on ties),
-// u = bf16(shared projection), s_x = max |x/s| / qmax (a max is exact in any order).
-__device__ __forceinline__ void route_finish_token(const float* __restrict__ part, const float* __restrict__ amax_part,
+// The route finish of RF_TOK consecutive tokens t0 .. t0 + RF_TOK - 1 per workgroup: the
+// partial sums of each split are one contiguous block of RF_TOK * ncols floats, read as 16-byte
+// vectors, one per thread and split, every split's load in flight together; each thread adds
+// its vector's splits in split order starting from zero (the same float32 sums, bit for bit, as
+// a sequential sum over the splits), then the sums go through LDS to the per-token steps:
+// router argmin (lowest index on ties; for top-2 also the best of the others), u = bf16 of the
+// shared projection, s_x = max |x/s| / qmax (a max is exact in any order).
+constexpr int RF_TOK = 16;
+constexpr int RF_THREADS = 256;
+
+__device__ __forceinline__ void route_finish_block(const float* __restrict__ part, const float* __restrict__ amax_part,
                                                    int ksplit, int T, int ncols, int r_s, int rs_pad, int router_col,
                                                    int n_r, int qmax, int32_t* __restrict__ expert,
                                                    uint16_t* __restrict__ u, float* __restrict__ s_x,
-                                                   int32_t* __restrict__ expert2, int t, int lane) {
-    if (t >= T) return;
-    // columns lane and lane + 64 (ncols <= 80), and the activation maxima: the partials of up to
-    // 16 splits of both columns and the maxima are requested together, then added in split order
-    float sum[2] = {0.0f, 0.0f};
-    const size_t stride = (size_t)T * ncols;
-    constexpr int KB16 = 16;
-    float vals[2][KB16];
+                                                   int32_t* __restrict__ expert2, int t0) {
+    __shared__ __attribute__((aligned(16))) float s_sum[RF_TOK * RP_MAXN * 16];
+    const int tid = threadIdx.x;
+    const int nt = min(RF_TOK, T - t0);
+    if (nt <= 0) return;  // uniform
+    const int nvec = nt * ncols / 4;  // ncols is a multiple of 16
+    const size_t stride = (size_t)T * ncols / 4;  // one split, in 16-byte vectors
+    const v4f* blk = reinterpret_cast<const v4f*>(part + (size_t)t0 * ncols);
+    constexpr int B = 16;
+    for (int i = tid; i < nvec; i += RF_THREADS) {
+        v4f sum = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int k0 = 0; k0 < ksplit; k0 += B) {
+            v4f a[B];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int c = min(lane + 64 * j, max(ncols - 1, 0));  // a column past ncols reads a valid one, unused
-        const float* p = part + (size_t)t * ncols + c;
+            for (int q = 0; q < B; ++q) a[q] = k0 + q < ksplit ? blk[(size_t)(k0 + q) * stride + i] : v4f{0, 0, 0, 0};
 #pragma unroll
-        for (int q = 0; q < KB16; ++q) vals[j][q] = (q < ksplit && ncols > 0) ? p[(size_t)q * stride] : 0.0f;
+            for (int q = 0; q < B; ++q)
+                if (k0 + q < ksplit) sum += a[q];
+        }
+        *reinterpret_cast<v4f*>(s_sum + 4 * i) = sum;
     }
     float m = 0.0f;
-    for (int k = lane; k < ksplit; k += 64) m = fmaxf(m, amax_part[(size_t)k * T + t]);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-        for (int q = 0; q < KB16; ++q)
-            if (q < ksplit) sum[j] += vals[j][q];
-        const float* p = part + (size_t)t * ncols + min(lane + 64 * j, max(ncols - 1, 0));
-        if (ncols > 0)
-            for (int k = KB16; k < ksplit; ++k) sum[j] += p[(size_t)k * stride];  // more than 16 splits: rare
-    }
-    if (router_col >= 0) {
-        float best = __builtin_inff();
-        int bi = 1 << 30;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {  // lane's own candidates, lower column first
-            const int c = lane + 64 * j;
-            if (c >= router_col && c < router_col + n_r && (sum[j] < best || bi == 1 << 30)) {
-                best = sum[j];
-                bi = c - router_col;
-            }
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ob = __shfl_xor(best, off, 64);
-            const int oi = __shfl_xor(bi, off, 64);
-            if (ob < best || (ob == best && oi < bi)) {
-                best = ob;
-                bi = oi;
-            }
-        }
-        if (lane == 0) expert[t] = bi;
-        if (expert2) {  // top-2 routing: the best of the other experts, lowest index on ties
-            float b2 = __builtin_inff();
-            int i2 = 1 << 30;
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int c = lane + 64 * j;
-                if (c >= router_col && c < router_col + n_r && c - router_col != bi && (sum[j] < b2 || i2 == 1 << 30)) {
-                    b2 = sum[j];
-                    i2 = c - router_col;
+    if (tid < nt)
+        for (int k = 0; k < ksplit; ++k) m = fmaxf(m, amax_part[(size_t)k * T + t0 + tid]);
+    __syncthreads();
+    if (tid < nt) {
+        const int t = t0 + tid;
+        const float* sc = s_sum + tid * ncols;
+        if (router_col >= 0) {
+            int e = 0;
+            float best = sc[router_col];
+            for (int j = 1; j < n_r; ++j)
+                if (sc[router_col + j] < best) {
+                    best = sc[router_col + j];
+                    e = j;
                 }
+            expert[t] = e;
+            if (expert2) {  // top-2 routing: the best of the other experts, lowest index on ties
+                int e2 = -1;
+                float b2 = 0.0f;
+                for (int j = 0; j < n_r; ++j)
+                    if (j != e && (e2 < 0 || sc[router_col + j] < b2)) {
+                        b2 = sc[router_col + j];
+                        e2 = j;
+                    }
+                expert2[t] = e2;
             }
-#pragma unroll
-            for (int off = 32; off > 0; off >>= 1) {
-                const float ob = __shfl_xor(b2, off, 64);
-                const int oi = __shfl_xor(i2, off, 64);
-                if (ob < b2 || (ob == b2 && oi < i2)) {
-                    b2 = ob;
-                    i2 = oi;
-                }
-            }
-            if (lane == 0) expert2[t] = i2;
+        }
+        s_x[t] = m / (float)qmax;
+    }
+    if (u) {
+        for (int i = tid; i < nt * rs_pad; i += RF_THREADS) {
+            const int tt = i / rs_pad, c = i - tt * rs_pad;
+            u[(size_t)(t0 + tt) * rs_pad + c] = c < r_s ? (uint16_t)f32_to_bf16_bits(s_sum[tt * ncols + c]) : (uint16_t)0;
         }
     }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int c = lane + 64 * j;
-        if (u && c < rs_pad) u[(size_t)t * rs_pad + c] = c < r_s ? (uint16_t)f32_to_bf16_bits(sum[j]) : (uint16_t)0;
-    }
-    m = wave_max(m);
-    if (lane == 0) s_x[t] = m / (float)qmax;
 }
 
-__global__ __launch_bounds__(256) void route_finish_kernel(const float* __restrict__ part,
-                                                           const float* __restrict__ amax_part, int ksplit, int T,
-                                                           int ncols, int r_s, int rs_pad, int router_col, int n_r,
-                                                           int qmax, int32_t* __restrict__ expert,
-                                                           uint16_t* __restrict__ u, float* __restrict__ s_x,
-                                                           int32_t* __restrict__ expert2) {
-    route_finish_token(part, amax_part, ksplit, T, ncols, r_s, rs_pad, router_col, n_r, qmax, expert, u, s_x, expert2,
-                       blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
+__global__ __launch_bounds__(RF_THREADS) void route_finish_kernel(const float* __restrict__ part,
+                                                                  const float* __restrict__ amax_part, int ksplit,
+                                                                  int T, int ncols, int r_s, int rs_pad,
+                                                                  int router_col, int n_r, int qmax,
+                                                                  int32_t* __restrict__ expert,
+                                                                  uint16_t* __restrict__ u, float* __restrict__ s_x,
+                                                                  int32_t* __restrict__ expert2) {
+    route_finish_block(part, amax_part, ksplit, T, ncols, r_s, rs_pad, router_col, n_r, qmax, expert, u, s_x, expert2,
+                       blockIdx.x * RF_TOK);
 }
 
 // the route finishes of up to RG_MAX linears that read the same x: linear blockIdx.y
-__global__ __launch_bounds__(256) void route_finish_group_kernel(FinishGroup G, int ksplit, int T) {
+__global__ __launch_bounds__(RF_THREADS) void route_finish_group_kernel(FinishGroup G, int ksplit, int T) {
     const FinishLinear& a = G.lin[blockIdx.y];
-    route_finish_token(a.part, a.amax, ksplit, T, a.ncols, a.r_s, a.rs_pad, a.router_col, a.n_r, a.qmax, a.expert,
-                       a.u, a.s_x, nullptr, blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
+    route_finish_block(a.part, a.amax, ksplit, T, a.ncols, a.r_s, a.rs_pad, a.router_col, a.n_r, a.qmax, a.expert,
+                       a.u, a.s_x, nullptr, blockIdx.x * RF_TOK);
 }
 
 hipError_t launch_route_finish_group(const FinishGroup& G, int n_lin, int ksplit, int T, hipStream_t st) {
     if (T <= 0) return hipSuccess;
     if (n_lin < 1 || n_lin > RG_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(route_finish_group_kernel, dim3((T + 3) / 4, n_lin), dim3(256), 0, st, G, ksplit, T);
+    for (int l = 0; l < n_lin; ++l)
+        if (G.lin[l].ncols < 0 || G.lin[l].ncols > RP_MAXN * 16 || G.lin[l].ncols % 16) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(route_finish_group_kernel, dim3((T + RF_TOK - 1) / RF_TOK, n_lin), dim3(RF_THREADS), 0, st, G,
+                       ksplit, T);
     return hipGetLastError();
 }
 
@@ -940,7 +931,8 @@ hipError_t launch_route_finish(const float* part, const float* amax_part, int ks
                                float* s_x, hipStream_t st, int32_t* expert2) {
     if (T <= 0) return hipSuccess;
     if (expert2 && (!expert || router_col < 0 || n_r < 2)) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(route_finish_kernel, dim3((T + 3) / 4), dim3(256), 0, st, part, amax_part, ksplit, T, ncols,
+    if (ncols < 0 || ncols > RP_MAXN * 16 || ncols % 16 || ksplit < 1) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(route_finish_kernel, dim3((T + RF_TOK - 1) / RF_TOK), dim3(RF_THREADS), 0, st, part, amax_part, ksplit, T, ncols,
                        r_s, rs_pad, router_col, n_r, (1 << (a_bits - 1)) - 1, expert, u, s_x, expert2);
     return hipGetLastError();
 }
