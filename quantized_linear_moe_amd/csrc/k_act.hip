@@ -963,9 +963,11 @@ constexpr int RW_GPW = RW_MAX_DIN / 128 / RW_WAVES;  // channel groups per wave 
 
 // weight fragments of NG of this wave's groups (its groups i0 .. i0 + NG - 1; a group past the
 // range repeats the last one and is not used): NB blocks of 16 rows
+// (rows at or past nrows repeat row nrows - 1: the same addresses as a lane that needs them, so
+// they add no memory traffic; their columns are not used)
 template <int NB, int NG>
 __device__ __forceinline__ void row_load_b(const uint16_t* __restrict__ rows, int d_in, int wid, int lane, int i0,
-                                           v4u (&b)[NG][NB][4]) {
+                                           v4u (&b)[NG][NB][4], int nrows = NB * 16) {
     const int lr = lane & 15, lg = lane >> 4, ngr = d_in >> 7;
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
@@ -974,7 +976,7 @@ __device__ __forceinline__ void row_load_b(const uint16_t* __restrict__ rows, in
         for (int n = 0; n < NB; ++n)
 #pragma unroll
             for (int s = 0; s < 4; ++s)
-                b[i][n][s] = *reinterpret_cast<const v4u*>(rows + (size_t)(n * 16 + lr) * d_in + k0 + 8 * s);
+                b[i][n][s] = *reinterpret_cast<const v4u*>(rows + (size_t)min(n * 16 + lr, nrows - 1) * d_in + k0 + 8 * s);
     }
 }
 
@@ -1016,8 +1018,9 @@ __device__ __forceinline__ void row_project(const uint16_t* __restrict__ rows, c
     }
 }
 
-// NBS, NBR: 16-column blocks of u (rs_pad / 16) and of v (rr_pad / 16)
-template <int NBS, int NBR>
+// NBS, NBR: 16-column blocks of u (rs_pad / 16) and of v (rr_pad / 16); GPW: channel groups per
+// wave the router's fragments are requested for (2 when d_in <= 4096, else RW_GPW)
+template <int NBS, int NBR, int GPW>
 __global__ __launch_bounds__(RW_THREADS) void row_prologue_kernel(
     const uint16_t* __restrict__ x, int d_in, const float* __restrict__ smooth, const float* __restrict__ inv_smooth,
     int qmax, const uint16_t* __restrict__ mt, int r_s, int col_router, int n_r, int col_re, int r_r,
@@ -1065,8 +1068,8 @@ __global__ __launch_bounds__(RW_THREADS) void row_prologue_kernel(
     const v4f s0 = *reinterpret_cast<const v4f*>(smooth + c * 8), s1 = *reinterpret_cast<const v4f*>(smooth + c * 8 + 4);
     const v4f i0 = *reinterpret_cast<const v4f*>(inv_smooth + c * 8),
               i1 = *reinterpret_cast<const v4f*>(inv_smooth + c * 8 + 4);
-    v4u rb[RW_GPW][1][4];
-    if constexpr (NBR > 0) row_load_b<1, RW_GPW>(mt + (size_t)col_router * d_in, d_in, wid, lane, 0, rb);
+    v4u rb[GPW][1][4];
+    if constexpr (NBR > 0) row_load_b<1, GPW>(mt + (size_t)col_router * d_in, d_in, wid, lane, 0, rb, n_r);
     if (tid < nch) *reinterpret_cast<v4u*>(xl + tid * 8) = w;
     float xs[8];
     smooth_div8(w, s0, s1, i0, i1, xs);
@@ -1082,7 +1085,7 @@ __global__ __launch_bounds__(RW_THREADS) void row_prologue_kernel(
 
     if constexpr (NBR > 0) {  // router scores (the router block is 16 rows)
         v4f racc[1];
-        row_project<1, RW_GPW>(mt + (size_t)col_router * d_in, xl, d_in, wid, lane, rb, true, racc);
+        row_project<1, GPW>(mt + (size_t)col_router * d_in, xl, d_in, wid, lane, rb, true, racc);
         if (lg == 0) s_part[wid][lr] = racc[0][0];
     }
     // s_x = max |x'| / qmax (a max is exact in any order), then the codes
@@ -1159,13 +1162,22 @@ hipError_t launch_row_prologue(const uint16_t* x, int T, int d_in, const float* 
         return hipErrorInvalidValue;
     const dim3 grid(T, rs_pad > 0 ? 2 : 1);
     const int qmax = (1 << (a_bits - 1)) - 1;
-#define QE_RW_LAUNCH(S, R)                                                                                       \
-    hipLaunchKernelGGL((row_prologue_kernel<S, R>), grid, dim3(RW_THREADS), 0, st, x, d_in, smooth, inv_smooth, \
-                       qmax, mt, r_s, col_router, n_r, col_re, r_r, codes, s_x, u, expert, v)
-#define QE_RW_BY_R(S)                      \
-    if (rr_pad == 0) QE_RW_LAUNCH(S, 0);   \
-    else if (rr_pad == 32) QE_RW_LAUNCH(S, 2); \
-    else QE_RW_LAUNCH(S, 4);
+    const bool narrow = d_in <= RW_WAVES * 128 * 2;  // at most two channel groups per wave
+#define QE_RW_LAUNCH(S, R)                                                                                          \
+    if (narrow)                                                                                                     \
+        hipLaunchKernelGGL((row_prologue_kernel<S, R, 2>), grid, dim3(RW_THREADS), 0, st, x, d_in, smooth,          \
+                           inv_smooth, qmax, mt, r_s, col_router, n_r, col_re, r_r, codes, s_x, u, expert, v);     \
+    else                                                                                                            \
+        hipLaunchKernelGGL((row_prologue_kernel<S, R, RW_GPW>), grid, dim3(RW_THREADS), 0, st, x, d_in, smooth,     \
+                           inv_smooth, qmax, mt, r_s, col_router, n_r, col_re, r_r, codes, s_x, u, expert, v)
+#define QE_RW_BY_R(S)                          \
+    if (rr_pad == 0) {                         \
+        QE_RW_LAUNCH(S, 0);                    \
+    } else if (rr_pad == 32) {                 \
+        QE_RW_LAUNCH(S, 2);                    \
+    } else {                                   \
+        QE_RW_LAUNCH(S, 4);                    \
+    }
     if (rs_pad == 0) {
         QE_RW_BY_R(0)
     } else if (rs_pad == 32) {
