@@ -1485,39 +1485,69 @@ __global__ __launch_bounds__(64 * EQ_W) void expert_quant_group_kernel(const uin
                                 a.perm, a.vpart, a.codes, a.v, sort_rows, blockIdx.x, blockIdx.y);
 }
 
-// v[perm[pos]][c] = bf16(sum over q, in order, of vpart[q][pos][c])
+// v[perm[pos]][c] = bf16 of the sum over the splits q of vpart[q][pos][c]: added in split order
+// when there are at most VF_SERIAL splits (one thread per entry); with more splits (few tokens
+// and wide inputs, one channel group per split) each of a workgroup's four waves adds a quarter
+// of the splits in order for 64 entries and the quarters are added in order, so each thread
+// waits for one batch of loads instead of a chain of them
+constexpr int VF_SERIAL = 64;
+
+__device__ __forceinline__ void vpart_finish_entries(const float* __restrict__ vpart, int ksq, int T, int rr_pad,
+                                                     int r_r, const int32_t* __restrict__ perm,
+                                                     uint16_t* __restrict__ v, bool quarters) {
+    const size_t n = (size_t)T * rr_pad, stride = n;
+    if (!quarters) {
+        const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+        if (idx >= n) return;
+        const int pos = (int)(idx / rr_pad), c = (int)(idx % rr_pad);
+        const int tt = perm ? perm[pos] : pos;
+        const float a = sum_splits(vpart + idx, stride, ksq);
+        v[(size_t)tt * rr_pad + c] = c < r_r ? (uint16_t)f32_to_bf16_bits(a) : (uint16_t)0;
+        return;
+    }
+    __shared__ float s_q[4][64];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const size_t idx = (size_t)blockIdx.x * 64 + lane;
+    const bool ok = idx < n;
+    const int k0 = (int)((long)w * ksq / 4), k1 = (int)((long)(w + 1) * ksq / 4);
+    s_q[w][lane] = ok ? sum_splits<VF_SERIAL>(vpart + (size_t)k0 * stride + idx, stride, k1 - k0) : 0.0f;
+    __syncthreads();
+    if (w == 0 && ok) {
+        const float a = ((s_q[0][lane] + s_q[1][lane]) + s_q[2][lane]) + s_q[3][lane];
+        const int pos = (int)(idx / rr_pad), c = (int)(idx % rr_pad);
+        const int tt = perm ? perm[pos] : pos;
+        v[(size_t)tt * rr_pad + c] = c < r_r ? (uint16_t)f32_to_bf16_bits(a) : (uint16_t)0;
+    }
+}
+
 __global__ __launch_bounds__(256) void vpart_finish_kernel(const float* __restrict__ vpart, int ksq, int T, int rr_pad,
                                                            int r_r, const int32_t* __restrict__ perm,
                                                            uint16_t* __restrict__ v) {
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (size_t)T * rr_pad) return;
-    const int pos = (int)(idx / rr_pad), c = (int)(idx % rr_pad);
-    const int tt = perm ? perm[pos] : pos;
-    const float a = sum_splits(vpart + idx, (size_t)T * rr_pad, ksq);
-    v[(size_t)tt * rr_pad + c] = c < r_r ? (uint16_t)f32_to_bf16_bits(a) : (uint16_t)0;
+    vpart_finish_entries(vpart, ksq, T, rr_pad, r_r, perm, v, ksq > VF_SERIAL);
 }
 
 // the v finishes of a group: linear blockIdx.y
 __global__ __launch_bounds__(256) void vpart_finish_group_kernel(EqGroup G, int ksq, int T, int rr_pad) {
     const EqLinear& a = G.lin[blockIdx.y];
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (size_t)T * rr_pad) return;
-    const int pos = (int)(idx / rr_pad), c = (int)(idx % rr_pad);
-    const int tt = a.perm ? a.perm[pos] : pos;
-    const float sum = sum_splits(a.vpart + idx, (size_t)T * rr_pad, ksq);
-    a.v[(size_t)tt * rr_pad + c] = c < a.r_r ? (uint16_t)f32_to_bf16_bits(sum) : (uint16_t)0;
+    vpart_finish_entries(a.vpart, ksq, T, rr_pad, a.r_r, a.perm, a.v, ksq > VF_SERIAL);
+}
+
+// workgroups of a v finish over n entries
+static unsigned vpart_finish_blocks(size_t n, int ksq) {
+    return (unsigned)(ksq > VF_SERIAL ? (n + 63) / 64 : (n + 255) / 256);
 }
 
 // K splits: about 256 workgroups with at least two channel groups each (measured against 384 and
 // 512: the 8B-shaped layer 1.7 % faster than with 512, the 2B-shaped 1 %, the 72B-shaped the same;
 // fewer splits also mean fewer v partials to add); few tokens (one or two row tiles) take one
-// group per workgroup where at most 64 splits allow it, since each group costs a memory latency
-// that so few workgroups cannot hide
+// group per workgroup up to 256 splits (every input here), since each group costs a memory
+// latency that so few workgroups cannot hide (the v finish then adds up to 256 partials, 64
+// requested at a time)
 bool expert_quant_few(int T) { return T <= EQ_FEW_T; }
 
 int expert_quant_ksplit(int T, int d_in) {
     const int tiles = (T + EQ_ROWS - 1) / EQ_ROWS;
-    const int ks = T <= EQ_FEW_T ? std::min(d_in / EQ_KG, 64)
+    const int ks = T <= EQ_FEW_T ? std::min(d_in / EQ_KG, 256)
                                  : std::min((256 + tiles - 1) / tiles, std::max(1, d_in / (2 * EQ_KG)));
     return std::max(ks, 1);
 }
@@ -1551,7 +1581,7 @@ hipError_t launch_expert_quant_group(const uint16_t* x, int T, int d_in, const E
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || ksq == 1) return err;
     const size_t n = (size_t)T * rr_pad;
-    hipLaunchKernelGGL(vpart_finish_group_kernel, dim3((unsigned)((n + 255) / 256), n_lin), dim3(256), 0, st, G, ksq, T,
+    hipLaunchKernelGGL(vpart_finish_group_kernel, dim3(vpart_finish_blocks(n, ksq), n_lin), dim3(256), 0, st, G, ksq, T,
                        rr_pad);
     return hipGetLastError();
 }
@@ -1587,7 +1617,7 @@ hipError_t launch_expert_quant(const uint16_t* x, int T, int d_in, const float* 
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || ksq == 1 || !nbr) return err;
     const size_t n = (size_t)T * rr_pad;
-    hipLaunchKernelGGL(vpart_finish_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, vpart, ksq, T, rr_pad,
+    hipLaunchKernelGGL(vpart_finish_kernel, dim3(vpart_finish_blocks(n, ksq)), dim3(256), 0, st, vpart, ksq, T, rr_pad,
                        r_r, keep_order ? nullptr : perm, v);
     return hipGetLastError();
 }

@@ -8,9 +8,10 @@
 namespace qe {
 
 // sum_k p[k * stride] for k = 0 .. n-1, added in order; the loads are issued in independent
-// batches of 16 (a chain of dependent loads would cost one memory latency per term)
+// batches of B (a chain of dependent loads would cost one memory latency per term, a batch one
+// latency for B terms)
+template <int B = 16>
 __device__ inline float sum_splits(const float* __restrict__ p, size_t stride, int n) {
-    constexpr int B = 16;
     float sum = 0.0f;
     for (int k = 0; k < n; k += B) {
         float a[B];
