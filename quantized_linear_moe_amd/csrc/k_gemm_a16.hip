@@ -78,6 +78,49 @@ __device__ __attribute__((always_inline)) inline void a16_epilogue(
         nbc[j] = nb_ok[j] ? nb0 + j : 0;
         sw[j] = w_scale[nbc[j] * 16 + lr];
     }
+    if constexpr (MB == 1 && NBW == 1) {
+        // the finish kernels' 16 x 16 blocks: with rank-32 adapters and at most 8 routed experts,
+        // the shared fragments, the v row and every present expert's fragments are requested
+        // together (one memory latency instead of one per expert present), then the MFMAs run in
+        // the order of the general form below (shared expert, then the experts by index), so the
+        // result is bit for bit the same
+        if (routed && rr_pad == 32 && n_r <= 8 && (!shared || rs_pad == 32)) {
+            const int ar = min(m0 + lr, T - 1);
+            const int ex = m0 + lr < T ? min(max(expert[ar], 0), n_r - 1) : -1;
+            int el[8];
+            int np = 0;
+            for (int q = 0; q < n_r; ++q)
+                if (__ballot(ex == q)) el[np++] = q;  // wave-uniform
+            v8bf ua = v8bf{}, bs = v8bf{};
+            if (shared) {
+                ua = *reinterpret_cast<const v8bf*>(u + (size_t)ar * rs_pad + lg * 8);
+                bs = *reinterpret_cast<const v8bf*>(bt_s + (size_t)(nbc[0] * 16 + lr) * rs_pad + lg * 8);
+            }
+            const v8bf vrow = *reinterpret_cast<const v8bf*>(v + (size_t)ar * rr_pad + lg * 8);
+            v8bf br[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int e = np > 0 ? el[min(i, np - 1)] : 0;  // slots past np repeat a present expert (unused)
+                br[i] = *reinterpret_cast<const v8bf*>(bt_r + ((size_t)e * d_out + nbc[0] * 16 + lr) * rr_pad + lg * 8);
+            }
+            v4f ad = v4f{0, 0, 0, 0};
+            if (shared) ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ua, bs, ad, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i >= np) break;  // uniform
+                const v8bf va = ex == el[i] ? vrow : v8bf{};
+                ad = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, br[i], ad, 0, 0, 0);
+            }
+            if (nb_ok[0]) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int t = m0 + lg * 4 + r;
+                    if (t < T) store_y(y, (size_t)t * d_out + nb0 * 16 + lr, acc[0][0][r] * sw[0] + ad[r], y_bf16);
+                }
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
         const int ar = min(m0 + m * 16 + lr, T - 1);
